@@ -1,0 +1,304 @@
+"""Pins of the oracle's attention forward/backward (CPU only).
+
+Each test checks the oracle against something other than itself: pure-Python
+brute force, torch's scaled_dot_product_attention, closed forms, invariants or
+central finite differences. Negative controls plant a mistake in a copy of the
+oracle and require the pins to catch it.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import scfa_oracle as so
+from io_aware_attention_head_amd.inputs import make_inputs, small
+
+
+def _np64(t):
+    return t.to(torch.float64).numpy()
+
+
+def _case(mode, T, H=2, D=16, seed=0, keep_p=0.6, nb=4, B=1):
+    w = small(mode, B, H, T, D, dtype="bf16", keep_p=keep_p, nb=nb, seed=seed)
+    x = make_inputs(w)
+    q, k, v = _np64(x["q"]), _np64(x["k"]), _np64(x["v"])
+    kq, kk = x["keep_q"].numpy(), x["keep_k"].numpy()
+    bq = bk = None
+    if mode == "hash":
+        bq = oracle.hash_bucket(q, x["R"].double().numpy(), nb)
+        bk = oracle.hash_bucket(k, x["R"].double().numpy(), nb)
+    return w, x, q, k, v, kq, kk, bq, bk
+
+
+def _brute_fwd(mode, q, k, v, kq, kk, bq, bk):
+    """Pairwise enumeration with Python scalars and math.exp."""
+    B, T, H, D = q.shape
+    tau = 1.0 / math.sqrt(D)
+    O = np.zeros_like(q)
+    L = np.full((B, H, T), -math.inf)
+    for b in range(B):
+        for h in range(H):
+            for i in range(T):
+                vis = []
+                for j in range(i + 1):
+                    if mode == "qk" and not (kq[b, i, h] and kk[b, j, h]):
+                        continue
+                    if mode == "hash" and bq[b, h, i] != bk[b, h, j]:
+                        continue
+                    vis.append(j)
+                if not vis:
+                    continue
+                s = [tau * sum(float(q[b, i, h, d]) * float(k[b, j, h, d]) for d in range(D)) for j in vis]
+                m = max(s)
+                lse = m + math.log(sum(math.exp(x - m) for x in s))
+                L[b, h, i] = lse
+                for jj, j in enumerate(vis):
+                    w = math.exp(s[jj] - lse)
+                    O[b, i, h] += w * v[b, j, h]
+    return O, L
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash"])
+@pytest.mark.parametrize("T,seed", [(1, 0), (7, 1), (33, 2), (64, 3)])
+def test_fwd_matches_pairwise_brute_force(mode, T, seed):
+    _, _, q, k, v, kq, kk, bq, bk = _case(mode, T, seed=seed)
+    O, L = oracle.attention_fwd(mode, q, k, v, kq, kk, bq, bk)
+    Ob, Lb = _brute_fwd(mode, q, k, v, kq, kk, bq, bk)
+    np.testing.assert_allclose(O, Ob, atol=1e-12, rtol=0)
+    assert np.array_equal(np.isinf(L), np.isinf(Lb))
+    fin = np.isfinite(Lb)
+    np.testing.assert_allclose(L[fin], Lb[fin], atol=1e-12, rtol=0)
+
+
+def test_fwd_brute_force_full_head_dim():
+    _, _, q, k, v, kq, kk, bq, bk = _case("hash", 24, H=1, D=64, seed=9, nb=2)
+    O, L = oracle.attention_fwd("hash", q, k, v, kq, kk, bq, bk)
+    Ob, Lb = _brute_fwd("hash", q, k, v, kq, kk, bq, bk)
+    np.testing.assert_allclose(O, Ob, atol=1e-12, rtol=0)
+
+
+def _sdpa_causal(q, k, v):
+    # (B,T,H,D) -> (B,H,T,D); float64 on CPU.
+    qt, kt, vt = (torch.from_numpy(a).permute(0, 2, 1, 3).contiguous() for a in (q, k, v))
+    return qt, kt, vt
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk"])
+def test_dense_and_all_keep_equal_causal_sdpa(mode):
+    _, _, q, k, v, kq, kk, _, _ = _case(mode, 96, H=3, D=64, seed=4, keep_p=1.0)
+    assert kq.all() and kk.all()
+    O, _ = oracle.attention_fwd(mode, q, k, v, kq, kk)
+    qt, kt, vt = _sdpa_causal(q, k, v)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    np.testing.assert_allclose(O, ref.permute(0, 2, 1, 3).numpy(), atol=1e-12, rtol=0)
+
+
+def test_bwd_dense_equals_sdpa_autograd():
+    _, x, q, k, v, kq, kk, _, _ = _case("dense", 80, H=2, D=64, seed=5)
+    dO = _np64(x["dO"])
+    dQ, dK, dV = oracle.attention_bwd("dense", q, k, v, dO)
+    qt, kt, vt = (t.requires_grad_(True) for t in _sdpa_causal(q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    g = torch.autograd.grad((out * torch.from_numpy(dO).permute(0, 2, 1, 3)).sum(), (qt, kt, vt))
+    for mine, ref in zip((dQ, dK, dV), g):
+        np.testing.assert_allclose(mine, ref.permute(0, 2, 1, 3).numpy(), atol=1e-11, rtol=0)
+
+
+def test_single_bucket_equals_causal():
+    # R = 0 makes every projection +-0, so the first-index tie-break puts every
+    # token in bucket 0 and hash-sparse attention is plain causal attention.
+    _, x, q, k, v, *_ = _case("hash", 50, H=2, D=64, seed=6)
+    R0 = np.zeros((2, 64, 8))
+    bq = oracle.hash_bucket(q, R0, 16)
+    bk = oracle.hash_bucket(k, R0, 16)
+    assert (bq == 0).all() and (bk == 0).all()
+    O, L = oracle.attention_fwd("hash", q, k, v, bkt_q=bq, bkt_k=bk)
+    Od, Ld = oracle.attention_fwd("dense", q, k, v)
+    np.testing.assert_allclose(O, Od, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(L, Ld, atol=1e-13, rtol=0)
+
+
+def test_bucket_relabelling_invariance():
+    _, _, q, k, v, kq, kk, bq, bk = _case("hash", 64, H=2, D=16, seed=7, nb=8)
+    sigma = np.random.default_rng(0).permutation(8)
+    O, L = oracle.attention_fwd("hash", q, k, v, bkt_q=bq, bkt_k=bk)
+    O2, L2 = oracle.attention_fwd("hash", q, k, v, bkt_q=sigma[bq], bkt_k=sigma[bk])
+    np.testing.assert_array_equal(O, O2)
+    np.testing.assert_array_equal(L, L2)
+
+
+def test_sorted_domain_and_within_bucket_permutation_invariance():
+    """Attention over rows sorted by (bucket, position), each row carrying its
+    position and bucket, scattered back to original order, equals the
+    original-order result; so does any within-bucket or global reordering."""
+    _, _, q, k, v, _, _, bq, bk = _case("hash", 64, H=2, D=16, seed=8, nb=4)
+    O, L = oracle.attention_fwd("hash", q, k, v, bkt_q=bq, bkt_k=bk)
+    qp, _, _ = oracle.hash_sort(bq, 4)
+    kp, _, _ = oracle.hash_sort(bk, 4)
+    rng = np.random.default_rng(1)
+    for h in range(2):
+        orders = [(qp[0, h], kp[0, h])]
+        # within-bucket shuffles of the sorted order
+        qs, ks = qp[0, h].copy(), kp[0, h].copy()
+        for arr, bb in ((qs, bq[0, h]), (ks, bk[0, h])):
+            for val in np.unique(bb):
+                sel = np.flatnonzero(bb[arr] == val)
+                arr[sel] = arr[sel][rng.permutation(len(sel))]
+        orders.append((qs, ks))
+        orders.append((rng.permutation(64), rng.permutation(64)))
+        for qo, ko in orders:
+            Or, Lr = oracle.attention_rows(q[0, qo, h], k[0, ko, h], v[0, ko, h], qo, ko, bq[0, h, qo], bk[0, h, ko])
+            back = np.zeros_like(Or)
+            back[qo] = Or
+            lb = np.zeros_like(Lr)
+            lb[qo] = Lr
+            np.testing.assert_allclose(back, O[0, :, h], atol=1e-13, rtol=0)
+            np.testing.assert_array_equal(np.isinf(lb), np.isinf(L[0, h]))
+
+
+def test_compacted_domain_equals_original_order():
+    _, x, q, k, v, kq, kk, _, _ = _case("qk", 64, H=2, D=16, seed=10, keep_p=0.5)
+    O, L = oracle.attention_fwd("qk", q, k, v, kq, kk)
+    Tc = 64
+    qc, qi = oracle.qk_compact(q, kq, Tc, oracle.Q_PAD)
+    kc, ki = oracle.qk_compact(k, kk, Tc, oracle.K_PAD)
+    vc, _ = oracle.qk_compact(v, kk, Tc, oracle.K_PAD)
+    for h in range(2):
+        Or, Lr = oracle.attention_rows(qc[0, h], kc[0, h], vc[0, h], qi[0, h], ki[0, h])
+        real = qi[0, h] >= 0
+        np.testing.assert_allclose(Or[real], O[0, qi[0, h][real], h], atol=1e-13, rtol=0)
+        assert np.isinf(Lr[~real]).all()
+        dropped = kq[0, :, h] == 0
+        assert (O[0, dropped, h] == 0).all() and np.isinf(L[0, h, dropped]).all()
+
+
+def test_closed_forms():
+    _, x, q, k, v, kq, kk, _, _ = _case("qk", 40, H=2, D=16, seed=11, keep_p=0.6)
+    B, T, H, D = q.shape
+    # Q = 0: uniform weights -> mean of visible values, LSE = ln n.
+    O, L = oracle.attention_fwd("qk", np.zeros_like(q), k, v, kq, kk)
+    for h in range(H):
+        for i in range(T):
+            vis = [j for j in range(i + 1) if kq[0, i, h] and kk[0, j, h]]
+            if vis:
+                np.testing.assert_allclose(O[0, i, h], v[0, vis, h].mean(axis=0), atol=1e-13)
+                assert abs(L[0, h, i] - math.log(len(vis))) < 1e-13
+            else:
+                assert (O[0, i, h] == 0).all() and L[0, h, i] == -math.inf
+    # V constant -> O = c on rows with a visible key.
+    c = np.broadcast_to(np.arange(D, dtype=np.float64) - 3.5, v.shape)
+    O, L = oracle.attention_fwd("qk", q, k, c, kq, kk)
+    fin = np.isfinite(L).transpose(0, 2, 1)
+    np.testing.assert_allclose(O[fin], c[fin], atol=1e-13)
+    # Key shift by a constant vector: O unchanged, LSE shifts by tau q.c.
+    shift = np.linspace(-1, 1, D)
+    O1, L1 = oracle.attention_fwd("qk", q, k, v, kq, kk)
+    O2, L2 = oracle.attention_fwd("qk", q, k + shift, v, kq, kk)
+    np.testing.assert_allclose(O1, O2, atol=1e-12)
+    fin = np.isfinite(L1)
+    expect = L1 + (q @ shift / math.sqrt(D)).transpose(0, 2, 1)
+    np.testing.assert_allclose(L2[fin], expect[fin], atol=1e-12)
+
+
+def test_single_visible_key_closed_form():
+    # Only key j = 0 kept: every kept query sees exactly that key.
+    _, _, q, k, v, kq, _, _, _ = _case("qk", 20, H=1, D=16, seed=12)
+    kk = np.zeros_like(kq)
+    kk[0, 0, 0] = 1
+    O, L = oracle.attention_fwd("qk", q, k, v, kq, kk)
+    for i in range(20):
+        if kq[0, i, 0]:
+            np.testing.assert_allclose(O[0, i, 0], v[0, 0, 0], atol=1e-14)
+            assert abs(L[0, 0, i] - q[0, i, 0] @ k[0, 0, 0] / 4.0) < 1e-13
+
+
+def test_hand_worked_qk_example():
+    """T = 4, Q = 0: hand-derived from the uniform-softmax closed form.
+    keep_q = [1,1,0,1], keep_k = [0,1,1,1]; query 0 sees no kept key at or
+    before it, query 2 is dropped, query 1 sees key 1, query 3 sees keys 1..3."""
+    v = np.array([[1, 2], [3, -1], [5, 7], [-2, 4]], dtype=np.float64).reshape(1, 4, 1, 2)
+    q = np.zeros_like(v)
+    k = np.ones_like(v)
+    kq = np.array([1, 1, 0, 1], dtype=np.uint8).reshape(1, 4, 1)
+    kk = np.array([0, 1, 1, 1], dtype=np.uint8).reshape(1, 4, 1)
+    O, L = oracle.attention_fwd("qk", q, k, v, kq, kk)
+    np.testing.assert_allclose(O[0, :, 0], [[0, 0], [3, -1], [0, 0], [2, 10 / 3]], atol=1e-15)
+    assert L[0, 0, 0] == -math.inf and L[0, 0, 2] == -math.inf
+    assert L[0, 0, 1] == 0.0 and abs(L[0, 0, 3] - math.log(3)) < 1e-15
+
+
+def _loss(mode, q, k, v, dO, kq, kk, bq, bk):
+    O, _ = oracle.attention_fwd(mode, q, k, v, kq, kk, bq, bk)
+    return float((O * dO).sum())
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash"])
+def test_bwd_central_finite_differences(mode):
+    _, x, q, k, v, kq, kk, bq, bk = _case(mode, 10, H=1, D=4, seed=13, keep_p=0.6, nb=2)
+    dO = _np64(x["dO"])
+    grads = oracle.attention_bwd(mode, q, k, v, dO, kq, kk, bq, bk)
+    eps = 1e-6
+    for which, g in zip(range(3), grads):
+        args = [q.copy(), k.copy(), v.copy()]
+        num = np.zeros_like(g)
+        for idx in np.ndindex(*g.shape):
+            a = [t.copy() for t in args]
+            a[which][idx] += eps
+            lp = _loss(mode, a[0], a[1], a[2], dO, kq, kk, bq, bk)
+            a[which][idx] -= 2 * eps
+            lm = _loss(mode, a[0], a[1], a[2], dO, kq, kk, bq, bk)
+            num[idx] = (lp - lm) / (2 * eps)
+        scale = max(1.0, np.abs(num).max())
+        assert np.abs(num - g).max() <= 1e-6 * scale, (which, np.abs(num - g).max())
+
+
+def test_gradient_identities():
+    _, x, q, k, v, kq, kk, _, _ = _case("qk", 48, H=2, D=16, seed=14, keep_p=0.6)
+    dO = _np64(x["dO"])
+    dQ, dK, dV = oracle.attention_bwd("qk", q, k, v, dO, kq, kk)
+    _, L = oracle.attention_fwd("qk", q, k, v, kq, kk)
+    for h in range(2):
+        # rows of dS sum to zero -> sum_j dK_j = 0
+        np.testing.assert_allclose(dK[0, :, h].sum(axis=0), 0, atol=1e-12)
+        has = np.isfinite(L[0, h])
+        np.testing.assert_allclose(dV[0, :, h].sum(axis=0), dO[0, has, h].sum(axis=0), atol=1e-12)
+        # zero gradients at dropped / stranded tokens
+        assert (dQ[0, ~has, h] == 0).all()
+        assert (dK[0, kk[0, :, h] == 0, h] == 0).all() and (dV[0, kk[0, :, h] == 0, h] == 0).all()
+
+
+# ---- negative controls: plant a mistake in a copy of the oracle ----------
+
+def test_negative_control_strict_mask_is_caught(monkeypatch):
+    _, _, q, k, v, kq, kk, bq, bk = _case("qk", 33, seed=15)
+    orig = so._vis_rows
+
+    def strict(mode, rows, T, kq_, kk_, bq_, bk_):
+        vis = orig(mode, rows, T, kq_, kk_, bq_, bk_)
+        return vis & (np.arange(T)[None, :] < rows[:, None])  # '>' instead of '>='
+
+    monkeypatch.setattr(so, "_vis_rows", strict)
+    O, _ = so.attention_fwd("qk", q, k, v, kq, kk)
+    Ob, _ = _brute_fwd("qk", q, k, v, kq, kk, None, None)
+    assert np.abs(O - Ob).max() > 1e-3
+
+
+def test_negative_control_missing_scale_is_caught():
+    _, _, q, k, v, kq, kk, bq, bk = _case("dense", 33, seed=16)
+    O, _ = oracle.attention_fwd("dense", q, k, v, scale=1.0)
+    Ob, _ = _brute_fwd("dense", q, k, v, kq, kk, None, None)
+    assert np.abs(O - Ob).max() > 1e-3
+
+
+def test_negative_control_flipped_keep_bit_changes_row():
+    _, _, q, k, v, kq, kk, _, _ = _case("qk", 30, H=1, seed=17, keep_p=0.99)
+    kq[:] = 1
+    kk[:] = 1
+    O, _ = oracle.attention_fwd("qk", q, k, v, kq, kk)
+    kk2 = kk.copy()
+    kk2[0, 3, 0] = 0
+    O2, _ = oracle.attention_fwd("qk", q, k, v, kq, kk2)
+    assert np.abs(O2[0, 3:, 0] - O[0, 3:, 0]).max(axis=1).min() > 0
+    np.testing.assert_array_equal(O2[0, :3, 0], O[0, :3, 0])

@@ -1,0 +1,143 @@
+"""Pins of the oracle's tile range / skip tables (CPU only).
+
+Brute force: a tile pair must be processed whenever it holds at least one
+visible (query, key) pair (100% coverage); in QK and dense mode the processed
+set is exactly the set of tiles holding a visible pair; the backward ranges
+traverse the same set as the forward ranges; dense mode reproduces the plain
+causal schedule (key tiles 0..i for query tile i).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from io_aware_attention_head_amd.inputs import make_inputs, small
+
+
+def _sorted_domain(mode, T, seed, keep_p=0.6, nb=16, B=1, H=2, Tc=None):
+    w = small(mode, B, H, T, 16, keep_p=keep_p, nb=nb, seed=seed)
+    x = make_inputs(w)
+    if mode == "qk":
+        kq, kk = x["keep_q"].numpy(), x["keep_k"].numpy()
+        if Tc is None:
+            Tc = T
+        _, qi = oracle.qk_compact(None, kq, Tc, oracle.Q_PAD)
+        _, ki = oracle.qk_compact(None, kk, Tc, oracle.K_PAD)
+        return qi, ki, None, None
+    if mode == "dense":
+        a = np.broadcast_to(np.arange(T, dtype=np.int32), (B, H, T)).copy()
+        return a, a.copy(), None, None
+    R = x["R"].double().numpy()
+    bq = oracle.hash_bucket(x["q"].double().numpy(), R, nb)
+    bk = oracle.hash_bucket(x["k"].double().numpy(), R, nb)
+    qp, qb, _ = oracle.hash_sort(bq, nb)
+    kp, kb, _ = oracle.hash_sort(bk, nb)
+    return qp, kp, qb, kb
+
+
+def _tiles_with_visible_pair(qi, ki, qb, kb, Bm, Bn):
+    B, H, Tq = qi.shape
+    Tk = ki.shape[-1]
+    nQt, nKt = -(-Tq // Bm), -(-Tk // Bn)
+    out = np.zeros((B, H, nQt, nKt), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            vis = (ki[b, h][None, :] <= qi[b, h][:, None]) & (qi[b, h][:, None] >= 0)
+            if qb is not None:
+                vis &= qb[b, h][:, None] == kb[b, h][None, :]
+            for i in range(nQt):
+                for j in range(nKt):
+                    out[b, h, i, j] = vis[i * Bm:(i + 1) * Bm, j * Bn:(j + 1) * Bn].any()
+    return out
+
+
+@pytest.mark.parametrize("Bm,Bn", [(64, 64), (64, 128), (128, 64), (128, 128), (16, 32)])
+@pytest.mark.parametrize("mode,T,seed", [("dense", 300, 0), ("qk", 512, 1), ("qk", 333, 2), ("hash", 700, 3),
+                                         ("hash", 129, 4)])
+def test_coverage_and_exactness(mode, T, seed, Bm, Bn):
+    qi, ki, qb, kb = _sorted_domain(mode, T, seed)
+    tab = oracle.range_tables(mode, qi, ki, qb, kb, Bm, Bn)
+    need = _tiles_with_visible_pair(qi, ki, qb, kb, Bm, Bn)
+    P = tab["P"]
+    assert not (need & ~P).any(), "a tile holding a visible pair is skipped"
+    if mode in ("qk", "dense"):
+        assert (need == P).all(), "QK/dense processed set must be exact"
+    assert (tab["tiles"] == P.sum(axis=(2, 3))).all()
+    # forward ranges: every processed j is inside [start, end)
+    B, H, nQt, nKt = P.shape
+    for b in range(B):
+        for h in range(H):
+            for i in range(nQt):
+                s, e = tab["fwd"][b, h, i]
+                js = np.flatnonzero(P[b, h, i])
+                if len(js):
+                    assert s <= js[0] and js[-1] < e and e == js[-1] + 1
+                else:
+                    assert s == e
+            # backward ranges traverse the same set
+            for j in range(nKt):
+                s, e = tab["bwd"][b, h, j]
+                ii = np.flatnonzero(P[b, h, :, j])
+                if len(ii):
+                    assert s == ii[0] and e == ii[-1] + 1
+                else:
+                    assert s == e == 0
+
+
+def test_dense_reduces_to_causal_schedule():
+    # Backward compatibility: with idx = arange, query tile i processes key
+    # tiles 0..i (start 0, stop i + 1) when the tiles are square.
+    T = 1024
+    a = np.broadcast_to(np.arange(T, dtype=np.int32), (1, 1, T)).copy()
+    for Bm in (64, 128):
+        tab = oracle.range_tables("qk", a, a, None, None, Bm, Bm)
+        n = T // Bm
+        assert (tab["fwd"][0, 0, :, 0] == 0).all()
+        assert list(tab["fwd"][0, 0, :, 1]) == list(range(1, n + 1))
+        assert tab["tiles"][0, 0] == n * (n + 1) // 2
+
+
+def test_qk_tables_hand_example():
+    # Tc = 6, tiles of 2. q_idx = [0,3 | 5,6 | -1,-1], k_idx = [1,2 | 6,1e9 | 1e9,1e9]
+    # query tile maxima 3, 6, -1; key tile minima 1, 6, 1e9
+    # -> ends 1, 2, 0; processed (0,0), (1,0), (1,1).
+    qi = np.array([0, 3, 5, 6, -1, -1], dtype=np.int32).reshape(1, 1, 6)
+    K = oracle.K_PAD
+    ki = np.array([1, 2, 6, K, K, K], dtype=np.int32).reshape(1, 1, 6)
+    tab = oracle.range_tables("qk", qi, ki, None, None, 2, 2)
+    assert tab["fwd"][0, 0].tolist() == [[0, 1], [0, 2], [0, 0]]
+    assert tab["bwd"][0, 0].tolist() == [[0, 2], [1, 2], [0, 0]]
+    assert tab["tiles"][0, 0] == 3
+    assert tab["qstats"][0, 0, :, :2].tolist() == [[0, 3], [5, 6], [-1, -1]]
+    assert tab["kstats"][0, 0, :, :2].tolist() == [[1, 2], [6, K], [K, K]]
+
+
+def test_hash_tables_hand_example():
+    # Sorted query rows (bucket, pos): (0,1) (0,4) | (1,2) (2,0);
+    # sorted key rows:                 (0,0) (0,5) | (1,1) (1,3) | (2,6)
+    # query tile 0: buckets [0,0], max pos 4 -> start 0 (key tile 0 max bucket 0),
+    #   provisional stop 1 (key tile 1 min bucket 1 > 0), causal: tile0 min pos 0 <= 4 -> end 1
+    # query tile 1: buckets [1,2], max pos 2 -> start 1, provisional stop 3,
+    #   causal: tile1 min pos 1 <= 2 ok, tile2 min pos 6 > 2 -> end 2
+    qi = np.array([1, 4, 2, 0], dtype=np.int32).reshape(1, 1, 4)
+    qb = np.array([0, 0, 1, 2], dtype=np.int32).reshape(1, 1, 4)
+    ki = np.array([0, 5, 1, 3, 6], dtype=np.int32).reshape(1, 1, 5)
+    kb = np.array([0, 0, 1, 1, 2], dtype=np.int32).reshape(1, 1, 5)
+    tab = oracle.range_tables("hash", qi, ki, qb, kb, 2, 2)
+    assert tab["fwd"][0, 0].tolist() == [[0, 1], [1, 2]]
+    assert tab["bwd"][0, 0].tolist() == [[0, 1], [1, 2], [0, 0]]
+    assert tab["tiles"][0, 0] == 2
+
+
+def test_qk_end_is_a_prefix_and_pad_tiles_are_empty():
+    qi, ki, _, _ = _sorted_domain("qk", 600, 5, keep_p=0.3, Tc=640)
+    tab = oracle.range_tables("qk", qi, ki, None, None, 128, 64)
+    ks = tab["kstats"]
+    for b in range(qi.shape[0]):
+        for h in range(qi.shape[1]):
+            for i in range(tab["fwd"].shape[2]):
+                s, e = tab["fwd"][b, h, i]
+                qmax = tab["qstats"][b, h, i, 1]
+                assert s == 0
+                assert (ks[b, h, :e, 0] <= qmax).all() and (ks[b, h, e:, 0] > qmax).all()
+                if qmax < 0:
+                    assert e == 0
