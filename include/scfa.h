@@ -1,0 +1,232 @@
+/*
+ * scfa.h -- C ABI of libscfa.so: sparse causal flash attention (SCFA) on
+ * AMD MI355X (gfx950).
+ *
+ * The operations follow the explainer page "Faster Causal Attention Over
+ * Large Sequences Through Sparse Flash Attention" (arXiv 2306.01160),
+ * cited below as "SCFA explainer" with its section names.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All pointers are DEVICE pointers unless stated otherwise; the caller
+ *    owns and allocates all memory. The library never allocates, frees or
+ *    synchronises, and keeps no pointer after returning.
+ *  - Every call only enqueues work on `stream` (may be NULL = default
+ *    stream) and returns; results are ready when the stream is.
+ *  - Return value: SCFA_OK, or a negative status. Argument errors that the
+ *    host can see (NULL pointer, bad size, unsupported dtype/mode) return
+ *    SCFA_ERR_INVALID / SCFA_ERR_UNSUPPORTED before anything is enqueued.
+ *    A failed kernel launch returns SCFA_ERR_HIP.
+ *  - Data-dependent errors that only the device can see (a kept count above
+ *    the compacted length, a bucket id outside [0, nb)) OR a bit into the
+ *    caller's `dev_err` word (may be NULL) without a host sync; the affected
+ *    outputs are then unspecified, but no access leaves its buffer.
+ *  - Layouts: user tensors are (B, T, H, D) row-major ("3.2 Big-Picture
+ *    Architecture", items 2 and 4); per-head index arrays are (B, H, n);
+ *    compacted / sorted tensors are head-major.
+ *  - Row buffers of compacted / sorted tensors hold Tpad = SCFA_PAD(n) rows,
+ *    n = valid rows (Tc for QK compaction, T for hash sorting). Rows
+ *    beyond n are zero; their index entries are the pads (-1 query,
+ *    1000000000 key).
+ *  - Supported: D = 64; dtype bf16 or fp32 (all operands of one call share
+ *    the input dtype). The library is stateless and thread-safe.
+ */
+#ifndef SCFA_H_
+#define SCFA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define SCFA_OK 0
+#define SCFA_ERR_INVALID (-1)     /* bad argument (NULL, size, range)          */
+#define SCFA_ERR_UNSUPPORTED (-2) /* valid but not built (e.g. D != 64)        */
+#define SCFA_ERR_HIP (-3)         /* a HIP launch/runtime call failed          */
+
+/* ---- device error bits (OR-ed into *dev_err) -------------------------- */
+#define SCFA_DEVERR_COUNT_EXCEEDS_TC 1 /* a head keeps more tokens than Tc     */
+#define SCFA_DEVERR_BUCKET_RANGE 2     /* a bucket id outside [0, nb)           */
+
+/* ---- enums ------------------------------------------------------------- */
+#define SCFA_BF16 0 /* bfloat16 storage, fp32 accumulation */
+#define SCFA_F32 1  /* float32 storage and accumulation     */
+
+#define SCFA_DENSE 0 /* causal attention, positions 0..T-1 */
+#define SCFA_QK 1    /* QK-drop: compacted keys/queries      */
+#define SCFA_HASH 2  /* hash-sparse: bucket-sorted           */
+
+#define SCFA_ROWS 0 /* (B, H, Tpad, D): one row per token           */
+#define SCFA_COLS 1 /* (B, H, D, Tpad): transposed, one row per dim */
+
+/* Sentinel indices for padded rows (SCFA explainer, 3.4, QK-Sparse
+ * Attention, compaction step; Hyperparameters and Implementation Constants). */
+#define SCFA_Q_PAD (-1)
+#define SCFA_K_PAD 1000000000
+
+/* Row padding of compacted/sorted buffers and the tile sizes of the
+ * attention kernels (query tile SCFA_TILE_M rows, key tile SCFA_TILE_N). */
+#define SCFA_ROW_ALIGN 128
+#define SCFA_PAD(n) ((((n) + SCFA_ROW_ALIGN - 1) / SCFA_ROW_ALIGN) * SCFA_ROW_ALIGN)
+#define SCFA_TILE_M 128
+#define SCFA_TILE_N 64
+#define SCFA_COUNT_CHUNK 64 /* positions per chunk of scfa_qk_count */
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* scfa_status_string(int status);
+
+/* Library ABI version (major*100 + minor). */
+int scfa_version(void);
+
+/* ------------------------------------------------------------------------
+ * QK-drop preprocessing.
+ * SCFA explainer, 3.4 "QK-Sparse Attention: Compaction and Index-Guided
+ * Tiling", compaction step: per head the kept tokens are counted, kept in
+ * position order (stable), gathered to the front and the index is padded.
+ * ---------------------------------------------------------------------- */
+
+/* Count kept tokens per head.
+ *  keep          (B, T, H) uint8, nonzero = kept.
+ *  count         out (B, H) int32: kept tokens of head (b, h).
+ *  max_count     out (1) int32: max over all heads (read it back to size Tc).
+ *  chunk_offsets out (B, H, ceil(T/64)) int32: kept tokens of head (b, h)
+ *                before chunk c (positions [64c, 64c+64)) -- an exclusive
+ *                prefix sum; input of scfa_qk_compact.                     */
+int scfa_qk_count(const uint8_t* keep, int B, int T, int H, int32_t* count, int32_t* max_count,
+                  int32_t* chunk_offsets, hipStream_t stream);
+
+/* Compact one tensor. For r < count[b,h]: idx_c[b,h,r] = position of the
+ * r-th kept token, x_c row r = x[b, idx_c[b,h,r], h, :] bit for bit. For
+ * count <= r < Tc: idx_c = pad_idx and the row is zero.
+ *  dtype         SCFA_BF16 / SCFA_F32 (element size of x and x_c).
+ *  x             (B, T, H, D); may be NULL only if x_c is NULL.
+ *  keep, count, chunk_offsets   as produced by scfa_qk_count on this keep.
+ *  Tc            compacted length, a multiple of SCFA_ROW_ALIGN, >= max count
+ *                (a head with more kept tokens sets COUNT_EXCEEDS_TC).
+ *  pad_idx       SCFA_Q_PAD for queries, SCFA_K_PAD for keys.
+ *  x_c           out (B, H, Tc, D) or NULL (index only).
+ *  idx_c         out (B, H, Tc) int32.                                     */
+int scfa_qk_compact(int dtype, const void* x, const uint8_t* keep, const int32_t* count,
+                    const int32_t* chunk_offsets, int B, int T, int H, int D, int Tc, int32_t pad_idx,
+                    void* x_c, int32_t* idx_c, int32_t* dev_err, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Hash-sparse preprocessing.
+ * SCFA explainer, 3.4 "Hash-Sparse Attention: Sorting by Bucket and
+ * Two-Dimensional Tiling": Reformer-style angular LSH buckets, a stable
+ * per-head sort by bucket, and a gather into the sorted order.
+ * ---------------------------------------------------------------------- */
+
+/* LSH bucket of every token: c_j = sum_d x[b,t,h,d] * R[h,d,j] for
+ * j < nb/2, accumulated in float64 in the order d = 0..D-1; bucket = the
+ * first index of the maximum of [c ; -c].
+ *  x       (B, T, H, D) bf16/fp32;  R (H, D, nb/2) fp32;  nb even, 2..64.
+ *  bucket  out (B, H, T) int32 in [0, nb).                                  */
+int scfa_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb,
+                     int32_t* bucket, hipStream_t stream);
+
+/* Bytes of device workspace scfa_hash_sort needs. */
+size_t scfa_hash_sort_workspace_bytes(int B, int H, int T, int nb);
+
+/* Stable counting sort of each head's tokens by bucket.
+ *  bucket        (B, H, T) int32 in [0, nb).
+ *  perm          out (B, H, SCFA_PAD(T)): original positions ordered by
+ *                (bucket, position); entries >= T hold pad_idx.
+ *  bucket_sorted out (B, H, SCFA_PAD(T)): bucket[perm]; entries >= T hold -1.
+ *  offsets       out (B, H, nb+1): offsets[v] = tokens with bucket < v.
+ *  pad_idx       SCFA_Q_PAD when sorting queries, SCFA_K_PAD for keys.
+ *  workspace     device scratch of scfa_hash_sort_workspace_bytes() bytes.  */
+int scfa_hash_sort(const int32_t* bucket, int B, int H, int T, int nb, int32_t pad_idx, int32_t* perm,
+                   int32_t* bucket_sorted, int32_t* offsets, void* workspace, size_t workspace_bytes,
+                   int32_t* dev_err, hipStream_t stream);
+
+/* Gather rows into head-major order: out row r of head (b, h) is
+ * x[b, idx[b,h,r], h, :] when 0 <= idx < T, else zero.
+ *  layout  SCFA_ROWS -> x_p (B, H, Tp, D);  SCFA_COLS -> x_p (B, H, D, Tp).
+ *  idx     (B, H, Tp) int32; Tp a multiple of SCFA_ROW_ALIGN.               */
+int scfa_gather(int dtype, int layout, const void* x, const int32_t* idx, int B, int T, int H, int D, int Tp,
+                void* x_p, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Tile range / skip table.
+ * SCFA explainer, 3.4: "Kernel tiling logic (Algorithm 1)" (QK: key tiles
+ * [0, end), end = number of key tiles whose smallest position is <= the
+ * query tile's largest position); "Kernel tiling logic for Hash-sparse
+ * (Algorithm 2)" (start skips key tiles whose largest bucket is below the
+ * query tile's smallest bucket; the stop is the first tile whose smallest
+ * bucket exceeds the query tile's largest, refined to one past the last tile
+ * passing the causal extremum test); "Backward Pass Design" (per key tile,
+ * the range of query tiles); "Design Choices" item 4 (dense = QK rule on
+ * positions 0..T-1).
+ *
+ * A tile pair (i, j) is PROCESSED iff j is in fwd range of i and
+ * kstats[j].minpos <= qstats[i].maxpos. bwd range of j = [min, max+1) of
+ * the processed i (or [0, 0)).
+ *  mode          SCFA_DENSE (q_idx, k_idx ignored, may be NULL), SCFA_QK,
+ *                SCFA_HASH (q_bkt, k_bkt required).
+ *  q_idx, q_bkt  (B, H, SCFA_PAD(Tq)); k_idx, k_bkt (B, H, SCFA_PAD(Tk)).
+ *  Tq, Tk        valid rows (extrema are taken over rows < Tq / < Tk).
+ *  Bm, Bn        tile sizes, each 16, 32, 64 or 128. The attention kernels
+ *                require Bm = SCFA_TILE_M, Bn = SCFA_TILE_N.
+ *  qstats out (B, H, nQt, 4), nQt = SCFA_PAD(Tq)/Bm:
+ *                [min pos, max pos, min bucket, max bucket] (buckets 0 unless
+ *                hash).
+ *  kstats out (B, H, nKt, 4), nKt = SCFA_PAD(Tk)/Bn; a tile with no valid
+ *                row holds [K_PAD, K_PAD, INT32_MAX, INT32_MAX].
+ *  fwd_tab out (B, H, nQt, 2) [start, end);  bwd_tab out (B, H, nKt, 2).
+ *  tiles   out (B, H) int32: number of processed tile pairs.               */
+int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt,
+                     const int32_t* k_bkt, int B, int H, int Tq, int Tk, int Bm, int Bn, int32_t* qstats,
+                     int32_t* kstats, int32_t* fwd_tab, int32_t* bwd_tab, int32_t* tiles, hipStream_t stream);
+
+/* Exact number of visible (query, key) pairs per head, from the sorted /
+ * compacted index arrays (a query row r < Tq with position p >= 0 sees the
+ * key rows s < Tk with k_idx[s] <= p, and equal bucket in hash mode).
+ *  pairs out (B, H) int64.                                                  */
+int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt,
+                       const int32_t* k_bkt, int B, int H, int Tq, int Tk, int64_t* pairs, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Forward attention.
+ * SCFA explainer, 3.4 "Kernel tiling logic (Algorithm 1)" / "(Algorithm 2)"
+ * and "Softmax Statistics Accumulation with NaN Safety" (Algorithm 3);
+ * "3.2 Big-Picture Architecture" item 4 (outputs scattered back to original
+ * positions, dropped queries get a zero vector).
+ *
+ * For every query the output is softmax-weighted V over the VISIBLE keys:
+ * key visible iff k_pos <= q_pos (QK), and same bucket (hash); scores are
+ * scale * q.k. A query with no visible key -- and, in QK mode, a dropped
+ * query -- gets O = 0 and LSE = -inf.
+ *  dtype_in      SCFA_BF16 / SCFA_F32 of q, k, v_t.
+ *  dtype_out     SCFA_F32 / SCFA_BF16 of O.
+ *  q, k          (B, H, Tpad, D) SCFA_ROWS compacted/sorted rows.
+ *  v_t           (B, H, D, Tpad) SCFA_COLS compacted/sorted values.
+ *  q_idx, k_idx  (B, H, Tpad) original positions with pads.
+ *  q_bkt, k_bkt  (B, H, Tpad) sorted bucket ids (hash only).
+ *  qstats, kstats, fwd_tab   from scfa_range_table with Bm = SCFA_TILE_M,
+ *                Bn = SCFA_TILE_N, same mode and arrays.
+ *  T             original sequence length (rows of O and LSE).
+ *  Tc            QK: compacted length (multiple of 128); Tpad = Tc.
+ *  scale         score scale, normally 1/sqrt(D).
+ *  O             out (B, T, H, D), every row written.
+ *  lse           out (B, H, T) fp32 natural-log normaliser, every entry
+ *                written (-inf for rows without a visible key).           */
+int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v_t,
+                       const int32_t* q_idx, const int32_t* k_idx, const int32_t* qstats, const int32_t* kstats,
+                       const int32_t* fwd_tab, int B, int H, int T, int Tc, int D, float scale, void* O,
+                       float* lse, hipStream_t stream);
+
+int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v_t,
+                         const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
+                         const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, int B, int H,
+                         int T, int D, float scale, void* O, float* lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCFA_H_ */

@@ -1,0 +1,680 @@
+// Index / bucket preprocessing and tile tables for sparse causal flash
+// attention on gfx950.
+//
+// Operations (see the explainer "Faster Causal Attention Over Large Sequences
+// Through Sparse Flash Attention", section 3.4):
+//   * QK-drop compaction: per-head keep counts, exclusive prefix sums,
+//     stable scatter of the kept rows to the front, sentinel padding.
+//   * Hash-sparse: angular LSH bucket (argmax over [xR ; -xR]), stable
+//     counting sort by bucket, gather into the sorted order.
+//   * Tile extrema and the per-query-tile / per-key-tile range tables of
+//     Algorithms 1 and 2 and of the backward pass.
+// All of these are HBM-bandwidth or latency bound: they use 16-byte
+// coalesced accesses, wave64 ballots for the prefix sums, and no MFMA.
+
+#include <limits.h>
+
+#include "scfa_internal.h"
+
+namespace scfa {
+namespace {
+
+// ---------------------------------------------------------------------------
+// QK-drop: counts per 64-position chunk, then an exclusive scan per head.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_qk_chunk_counts(const uint8_t* __restrict__ keep, int T, int H, int nC,
+                                                         int32_t* __restrict__ chunk, int32_t* __restrict__ max_count) {
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (c == 0 && b == 0 && threadIdx.x == 0) *max_count = 0;
+  const int t = c * SCFA_COUNT_CHUNK + lane;
+  for (int h = w; h < H; h += 4) {
+    const bool f = t < T && keep[(static_cast<size_t>(b) * T + t) * H + h] != 0;
+    const uint64_t m = __ballot(f);
+    if (lane == 0) chunk[(static_cast<size_t>(b) * H + h) * nC + c] = __popcll(m);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_qk_scan(int32_t* __restrict__ chunk, int nC, int32_t* __restrict__ count,
+                                                 int32_t* __restrict__ max_count) {
+  __shared__ int32_t wsum[4];
+  const int bh = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int32_t* p = chunk + static_cast<size_t>(bh) * nC;
+  int carry = 0;
+  for (int base = 0; base < nC; base += 256) {
+    const int i = base + threadIdx.x;
+    const int v = i < nC ? p[i] : 0;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int pre = 0;
+    for (int k = 0; k < w; ++k) pre += wsum[k];
+    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (i < nC) p[i] = carry + pre + x - v;
+    carry += total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    count[bh] = carry;
+    atomicMax(max_count, carry);
+  }
+}
+
+// One workgroup per (64-position chunk, batch), all heads: the keep bytes and
+// the input rows of the chunk are one contiguous block of memory.
+template <int ESZ>
+__global__ __launch_bounds__(256) void k_qk_compact(const uint8_t* __restrict__ x, const uint8_t* __restrict__ keep,
+                                                    const int32_t* __restrict__ count,
+                                                    const int32_t* __restrict__ chunk_off, int T, int H, int D, int Tc,
+                                                    int nC, int32_t pad, uint8_t* __restrict__ xc,
+                                                    int32_t* __restrict__ idx, int32_t* dev_err) {
+  extern __shared__ int32_t rank[];  // [H][64]
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int h = w; h < H; h += 4) {
+    const int bh = b * H + h;
+    int r = -1;
+    if (c < nC) {
+      const int t = c * SCFA_COUNT_CHUNK + lane;
+      const bool f = t < T && keep[(static_cast<size_t>(b) * T + t) * H + h] != 0;
+      const uint64_t m = __ballot(f);
+      if (f) {
+        r = chunk_off[static_cast<size_t>(bh) * nC + c] + lanes_below(m);
+        if (r < Tc) {
+          idx[static_cast<size_t>(bh) * Tc + r] = t;
+        } else {
+          set_dev_err(dev_err, SCFA_DEVERR_COUNT_EXCEEDS_TC);
+          r = -1;
+        }
+      }
+    }
+    rank[h * 64 + lane] = r;
+    const int pr = count[bh] + c * SCFA_COUNT_CHUNK + lane;
+    if (pr >= 0 && pr < Tc) idx[static_cast<size_t>(bh) * Tc + pr] = pad;
+  }
+  __syncthreads();
+  if (xc == nullptr) return;
+  const int U = D * ESZ / 16;  // 16-byte units per row
+  if (c < nC) {
+    const int npos = min(SCFA_COUNT_CHUNK, T - c * SCFA_COUNT_CHUNK);
+    const int nunits = npos * H * U;
+    const uint8_t* src0 = x + (static_cast<size_t>(b) * T + static_cast<size_t>(c) * SCFA_COUNT_CHUNK) * H * D * ESZ;
+    for (int u = threadIdx.x; u < nunits; u += 256) {
+      const int l = u / (H * U);
+      const int rem = u - l * H * U;
+      const int h = rem / U;
+      const int kk = rem - h * U;
+      const int r = rank[h * 64 + l];
+      if (r >= 0) {
+        const uint4 val = reinterpret_cast<const uint4*>(src0)[u];
+        uint8_t* dst = xc + ((static_cast<size_t>(b) * H + h) * Tc + r) * D * ESZ;
+        reinterpret_cast<uint4*>(dst)[kk] = val;
+      }
+    }
+  }
+  // zero the pad rows [count + 64c, count + 64c + 64) of every head
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  for (int u = threadIdx.x; u < SCFA_COUNT_CHUNK * H * U; u += 256) {
+    const int l = u / (H * U);
+    const int rem = u - l * H * U;
+    const int h = rem / U;
+    const int kk = rem - h * U;
+    const int bh = b * H + h;
+    const int pr = count[bh] + c * SCFA_COUNT_CHUNK + l;
+    if (pr >= 0 && pr < Tc) {
+      uint8_t* dst = xc + (static_cast<size_t>(bh) * Tc + pr) * D * ESZ;
+      reinterpret_cast<uint4*>(dst)[kk] = z;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LSH bucket. One thread per token, one workgroup per (256 tokens, head):
+// R of the head sits in LDS as float64. Products of a bf16/fp32 input and an
+// fp32 rotation are exact in float64, so the accumulation below rounds only
+// at the sums, in the order d = 0..63.
+// ---------------------------------------------------------------------------
+
+template <typename TIN>
+__device__ inline float load_elem(const TIN* p, int i);
+
+template <>
+__device__ inline float load_elem<float>(const float* p, int i) {
+  return p[i];
+}
+
+template <>
+__device__ inline float load_elem<uint16_t>(const uint16_t* p, int i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+
+template <typename TIN, int HALF>
+__global__ __launch_bounds__(256) void k_hash_bucket(const TIN* __restrict__ x, const float* __restrict__ R, int T,
+                                                     int H, int32_t* __restrict__ bucket) {
+#pragma clang fp contract(off)
+  constexpr int D = 64;
+  __shared__ double Rs[D * HALF];
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  for (int i = threadIdx.x; i < D * HALF; i += 256) Rs[i] = static_cast<double>(R[static_cast<size_t>(h) * D * HALF + i]);
+  __syncthreads();
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  const TIN* row = x + ((static_cast<size_t>(b) * T + t) * H + h) * D;
+  double c[HALF];
+#pragma unroll
+  for (int j = 0; j < HALF; ++j) c[j] = 0.0;
+#pragma unroll 8
+  for (int d = 0; d < D; ++d) {
+    const double xd = static_cast<double>(load_elem<TIN>(row, d));
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+      const double prod = xd * Rs[d * HALF + j];
+      c[j] = c[j] + prod;
+    }
+  }
+  // argmax over [c ; -c], first index on ties: the positive half comes first.
+  int bp = 0, bn = 0;
+  double vp = c[0], vn = -c[0];
+#pragma unroll
+  for (int j = 1; j < HALF; ++j) {
+    if (c[j] > vp) { vp = c[j]; bp = j; }
+    if (-c[j] > vn) { vn = -c[j]; bn = j; }
+  }
+  bucket[static_cast<size_t>(bh) * T + t] = (vn > vp) ? HALF + bn : bp;
+}
+
+// ---------------------------------------------------------------------------
+// Stable counting sort by bucket: per-chunk histograms, per-head scan, then a
+// stable scatter whose in-chunk ranks come from wave64 ballots.
+// ---------------------------------------------------------------------------
+
+constexpr int kSortChunk = 256;
+
+__global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ bucket, int T, int nb, int nC,
+                                                   int32_t* __restrict__ hist, int32_t* dev_err) {
+  __shared__ int32_t hs[64];
+  const int c = blockIdx.x, bh = blockIdx.y;
+  if (threadIdx.x < 64) hs[threadIdx.x] = 0;
+  __syncthreads();
+  const int t = c * kSortChunk + threadIdx.x;
+  if (t < T) {
+    const int v = bucket[static_cast<size_t>(bh) * T + t];
+    if (v >= 0 && v < nb) {
+      atomicAdd(&hs[v], 1);
+    } else {
+      set_dev_err(dev_err, SCFA_DEVERR_BUCKET_RANGE);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < nb) hist[(static_cast<size_t>(bh) * nC + c) * nb + threadIdx.x] = hs[threadIdx.x];
+}
+
+// One wave per head: lane v owns bucket v. hist[c][v] becomes the sorted
+// position of the first chunk-c token of bucket v.
+__global__ __launch_bounds__(64) void k_sort_scan(int32_t* __restrict__ hist, int nb, int nC,
+                                                  int32_t* __restrict__ offsets) {
+  const int bh = blockIdx.x;
+  const int v = threadIdx.x;
+  int32_t* hp = hist + static_cast<size_t>(bh) * nC * nb;
+  int total = 0;
+  if (v < nb)
+    for (int c = 0; c < nC; ++c) total += hp[c * nb + v];
+  // exclusive scan of the totals over v
+  int x = total;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (v >= o) x += y;
+  }
+  const int off = x - total;
+  if (v < nb) {
+    offsets[static_cast<size_t>(bh) * (nb + 1) + v] = off;
+    int run = off;
+    for (int c = 0; c < nC; ++c) {
+      const int n = hp[c * nb + v];
+      hp[c * nb + v] = run;
+      run += n;
+    }
+  }
+  if (v == nb - 1) offsets[static_cast<size_t>(bh) * (nb + 1) + nb] = off + total;
+}
+
+__global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict__ bucket, int T, int Tp, int nb, int nC,
+                                                      const int32_t* __restrict__ base, int32_t pad,
+                                                      int32_t* __restrict__ perm, int32_t* __restrict__ bsorted) {
+  __shared__ int32_t wcnt[4][64];
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = c * kSortChunk + threadIdx.x;
+  for (int i = threadIdx.x; i < 4 * 64; i += 256) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  int v = -1;
+  if (t < T) v = bucket[static_cast<size_t>(bh) * T + t];
+  const bool valid = t < T && v >= 0 && v < nb;
+  int my_rank = 0;
+  uint64_t remaining = __ballot(valid);
+  while (remaining) {
+    const int leader = __ffsll(static_cast<long long>(remaining)) - 1;
+    const int lv = __shfl(v, leader);
+    const bool mine = valid && v == lv;
+    const uint64_t m = __ballot(mine);
+    if (mine) my_rank = lanes_below(m);
+    if (lane == 0) wcnt[w][lv] = __popcll(m);
+    remaining &= ~m;
+  }
+  __syncthreads();
+  int32_t* pp = perm + static_cast<size_t>(bh) * Tp;
+  int32_t* bp = bsorted + static_cast<size_t>(bh) * Tp;
+  if (valid && c < nC) {
+    int pos = base[(static_cast<size_t>(bh) * nC + c) * nb + v] + my_rank;
+    for (int k = 0; k < w; ++k) pos += wcnt[k][v];
+    pp[pos] = t;
+    bp[pos] = v;
+  }
+  if (t >= T && t < Tp) {
+    pp[t] = pad;
+    bp[t] = -1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gather into head-major order (rows or transposed columns).
+// ---------------------------------------------------------------------------
+
+template <int ESZ>
+__global__ __launch_bounds__(256) void k_gather_rows(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
+                                                     int T, int H, int D, int Tp, uint8_t* __restrict__ out) {
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int U = D * ESZ / 16;
+  const long long u = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (u >= static_cast<long long>(Tp) * U) return;
+  const int r = static_cast<int>(u / U);
+  const int kk = static_cast<int>(u - static_cast<long long>(r) * U);
+  const int src = idx[static_cast<size_t>(bh) * Tp + r];
+  uint4 val = make_uint4(0, 0, 0, 0);
+  if (src >= 0 && src < T)
+    val = reinterpret_cast<const uint4*>(x + ((static_cast<size_t>(b) * T + src) * H + h) * D * ESZ)[kk];
+  reinterpret_cast<uint4*>(out + (static_cast<size_t>(bh) * Tp + r) * D * ESZ)[kk] = val;
+}
+
+// 64 rows per workgroup staged in LDS, then written as D rows of 64 columns.
+template <typename E>
+__global__ __launch_bounds__(256) void k_gather_cols(const E* __restrict__ x, const int32_t* __restrict__ idx, int T,
+                                                     int H, int Tp, E* __restrict__ out) {
+  constexpr int D = 64;
+  constexpr int LD = D + (sizeof(E) == 2 ? 2 : 1);  // odd word stride: conflict-free column reads
+  __shared__ E tile[64 * LD];
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int r0 = blockIdx.x * 64;
+  for (int e = threadIdx.x; e < 64 * D; e += 256) {
+    const int rr = e / D, d = e - rr * D;
+    const int src = idx[static_cast<size_t>(bh) * Tp + r0 + rr];
+    E val = E(0);
+    if (src >= 0 && src < T) val = x[((static_cast<size_t>(b) * T + src) * H + h) * D + d];
+    tile[rr * LD + d] = val;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * D; e += 256) {
+    const int d = e / 64, rr = e - d * 64;
+    out[(static_cast<size_t>(bh) * D + d) * Tp + r0 + rr] = tile[rr * LD + d];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tile extrema and range tables.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(64) void k_tile_stats(int mode, const int32_t* __restrict__ q_idx,
+                                                   const int32_t* __restrict__ k_idx, const int32_t* __restrict__ q_bkt,
+                                                   const int32_t* __restrict__ k_bkt, int Tq, int Tk, int TqP, int TkP,
+                                                   int Bm, int Bn, int nQt, int nKt, int32_t* __restrict__ qstats,
+                                                   int32_t* __restrict__ kstats, int32_t* __restrict__ tiles) {
+  const int bh = blockIdx.y;
+  const int x = blockIdx.x;
+  const int lane = threadIdx.x;
+  const bool isq = x < nQt;
+  const int tile = isq ? x : x - nQt;
+  const int bs = isq ? Bm : Bn;
+  const int Tv = isq ? Tq : Tk;
+  const int32_t* ip = isq ? q_idx + static_cast<size_t>(bh) * TqP : k_idx + static_cast<size_t>(bh) * TkP;
+  const int32_t* bp = nullptr;
+  if (mode == SCFA_HASH) bp = isq ? q_bkt + static_cast<size_t>(bh) * TqP : k_bkt + static_cast<size_t>(bh) * TkP;
+  const int r0 = tile * bs, r1 = min(r0 + bs, Tv);
+  int mn = kInt32Max, mx = kInt32Min, mnb = kInt32Max, mxb = kInt32Min;
+  for (int r = r0 + lane; r < r1; r += 64) {
+    const int p = (mode == SCFA_DENSE) ? r : ip[r];
+    mn = min(mn, p);
+    mx = max(mx, p);
+    if (bp) {
+      const int v = bp[r];
+      mnb = min(mnb, v);
+      mxb = max(mxb, v);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, __shfl_xor(mn, o));
+    mx = max(mx, __shfl_xor(mx, o));
+    mnb = min(mnb, __shfl_xor(mnb, o));
+    mxb = max(mxb, __shfl_xor(mxb, o));
+  }
+  if (lane == 0) {
+    int4 s;
+    if (r1 <= r0) {
+      s = isq ? make_int4(SCFA_Q_PAD, SCFA_Q_PAD, kInt32Max, kInt32Min)
+              : make_int4(SCFA_K_PAD, SCFA_K_PAD, kInt32Max, kInt32Max);
+    } else if (bp) {
+      s = make_int4(mn, mx, mnb, mxb);
+    } else {
+      s = make_int4(mn, mx, 0, 0);
+    }
+    int32_t* out = isq ? qstats + (static_cast<size_t>(bh) * nQt + tile) * 4 : kstats + (static_cast<size_t>(bh) * nKt + tile) * 4;
+    *reinterpret_cast<int4*>(out) = s;
+    if (x == 0) tiles[bh] = 0;
+  }
+}
+
+__global__ __launch_bounds__(64) void k_fwd_table(int mode, const int32_t* __restrict__ qstats,
+                                                  const int32_t* __restrict__ kstats, int nQt, int nKt,
+                                                  int32_t* __restrict__ fwd, int32_t* __restrict__ tiles) {
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= nQt) return;
+  const int4 qs = reinterpret_cast<const int4*>(qstats)[static_cast<size_t>(bh) * nQt + i];
+  const int4* ks = reinterpret_cast<const int4*>(kstats) + static_cast<size_t>(bh) * nKt;
+  int start = 0, end = 0, cnt = 0;
+  if (mode != SCFA_HASH) {
+    for (int j = 0; j < nKt; ++j) cnt += ks[j].x <= qs.y;
+    end = cnt;
+  } else {
+    for (int j = 0; j < nKt; ++j) start += ks[j].w < qs.z;
+    int eh = start;
+    while (eh < nKt && !(ks[eh].z > qs.w)) ++eh;
+    end = start;
+    for (int j = start; j < eh; ++j) {
+      if (ks[j].x <= qs.y) {
+        end = j + 1;
+        ++cnt;
+      }
+    }
+  }
+  reinterpret_cast<int2*>(fwd)[static_cast<size_t>(bh) * nQt + i] = make_int2(start, end);
+  if (cnt) atomicAdd(&tiles[bh], cnt);
+}
+
+__global__ __launch_bounds__(64) void k_bwd_table(const int32_t* __restrict__ qstats, const int32_t* __restrict__ kstats,
+                                                  const int32_t* __restrict__ fwd, int nQt, int nKt,
+                                                  int32_t* __restrict__ bwd) {
+  const int bh = blockIdx.y;
+  const int j = blockIdx.x * 64 + threadIdx.x;
+  if (j >= nKt) return;
+  const int kmin = reinterpret_cast<const int4*>(kstats)[static_cast<size_t>(bh) * nKt + j].x;
+  const int4* qs = reinterpret_cast<const int4*>(qstats) + static_cast<size_t>(bh) * nQt;
+  const int2* ft = reinterpret_cast<const int2*>(fwd) + static_cast<size_t>(bh) * nQt;
+  int first = -1, last = -1;
+  for (int i = 0; i < nQt; ++i) {
+    const int2 r = ft[i];
+    if (j >= r.x && j < r.y && kmin <= qs[i].y) {
+      if (first < 0) first = i;
+      last = i;
+    }
+  }
+  reinterpret_cast<int2*>(bwd)[static_cast<size_t>(bh) * nKt + j] = first < 0 ? make_int2(0, 0) : make_int2(first, last + 1);
+}
+
+// ---------------------------------------------------------------------------
+// Exact visible-pair count (binary searches in the sorted key arrays).
+// ---------------------------------------------------------------------------
+
+__global__ void k_zero_i64(int64_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_count_visible(int mode, const int32_t* __restrict__ q_idx,
+                                                       const int32_t* __restrict__ k_idx,
+                                                       const int32_t* __restrict__ q_bkt,
+                                                       const int32_t* __restrict__ k_bkt, int Tq, int Tk, int TqP,
+                                                       int TkP, int64_t* __restrict__ pairs) {
+  __shared__ long long part[4];
+  const int bh = blockIdx.y;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  long long n = 0;
+  if (r < Tq) {
+    if (mode == SCFA_DENSE) {
+      n = min(r + 1, Tk);
+    } else {
+      const int p = q_idx[static_cast<size_t>(bh) * TqP + r];
+      const int32_t* kp = k_idx + static_cast<size_t>(bh) * TkP;
+      if (p >= 0) {
+        if (mode == SCFA_QK) {
+          int lo = 0, hi = Tk;  // first s with kp[s] > p
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (kp[mid] <= p) lo = mid + 1; else hi = mid;
+          }
+          n = lo;
+        } else {
+          const int qb = q_bkt[static_cast<size_t>(bh) * TqP + r];
+          const int32_t* kb = k_bkt + static_cast<size_t>(bh) * TkP;
+          int lo = 0, hi = Tk;  // first s with (kb, kp) > (qb, p)
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (kb[mid] < qb || (kb[mid] == qb && kp[mid] <= p)) lo = mid + 1; else hi = mid;
+          }
+          const int up = lo;
+          lo = 0;
+          hi = Tk;  // first s with kb >= qb
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (kb[mid] < qb) lo = mid + 1; else hi = mid;
+          }
+          n = up - lo;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const long long s = part[0] + part[1] + part[2] + part[3];
+    if (s) atomicAdd(reinterpret_cast<unsigned long long*>(pairs + bh), static_cast<unsigned long long>(s));
+  }
+}
+
+}  // namespace
+}  // namespace scfa
+
+using namespace scfa;
+
+extern "C" {
+
+const char* scfa_status_string(int status) {
+  switch (status) {
+    case SCFA_OK: return "SCFA_OK";
+    case SCFA_ERR_INVALID: return "SCFA_ERR_INVALID: invalid argument";
+    case SCFA_ERR_UNSUPPORTED: return "SCFA_ERR_UNSUPPORTED: configuration not built";
+    case SCFA_ERR_HIP: return "SCFA_ERR_HIP: HIP launch or runtime error";
+    default: return "SCFA: unknown status";
+  }
+}
+
+int scfa_version(void) { return 100; }
+
+int scfa_qk_count(const uint8_t* keep, int B, int T, int H, int32_t* count, int32_t* max_count,
+                  int32_t* chunk_offsets, hipStream_t stream) {
+  if (!keep || !count || !max_count || !chunk_offsets) return SCFA_ERR_INVALID;
+  if (B < 1 || T < 1 || H < 1) return SCFA_ERR_INVALID;
+  const int nC = ceil_div(T, SCFA_COUNT_CHUNK);
+  hipLaunchKernelGGL(k_qk_chunk_counts, dim3(nC, B), dim3(256), 0, stream, keep, T, H, nC, chunk_offsets, max_count);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  hipLaunchKernelGGL(k_qk_scan, dim3(B * H), dim3(256), 0, stream, chunk_offsets, nC, count, max_count);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+int scfa_qk_compact(int dtype, const void* x, const uint8_t* keep, const int32_t* count, const int32_t* chunk_offsets,
+                    int B, int T, int H, int D, int Tc, int32_t pad_idx, void* x_c, int32_t* idx_c, int32_t* dev_err,
+                    hipStream_t stream) {
+  if (!keep || !count || !chunk_offsets || !idx_c) return SCFA_ERR_INVALID;
+  if (x_c && !x) return SCFA_ERR_INVALID;
+  if (B < 1 || T < 1 || H < 1 || H > 128 || Tc < SCFA_ROW_ALIGN || Tc % SCFA_ROW_ALIGN) return SCFA_ERR_INVALID;
+  if (!dtype_ok(dtype)) return SCFA_ERR_INVALID;
+  if (x_c && D != 64) return SCFA_ERR_UNSUPPORTED;
+  const int nC = ceil_div(T, SCFA_COUNT_CHUNK);
+  const int nCx = ceil_div(T > Tc ? T : Tc, SCFA_COUNT_CHUNK);
+  const size_t lds = static_cast<size_t>(H) * 64 * sizeof(int32_t);
+  if (dtype == SCFA_BF16)
+    hipLaunchKernelGGL(k_qk_compact<2>, dim3(nCx, B), dim3(256), lds, stream, static_cast<const uint8_t*>(x), keep,
+                       count, chunk_offsets, T, H, D, Tc, nC, pad_idx, static_cast<uint8_t*>(x_c), idx_c, dev_err);
+  else
+    hipLaunchKernelGGL(k_qk_compact<4>, dim3(nCx, B), dim3(256), lds, stream, static_cast<const uint8_t*>(x), keep,
+                       count, chunk_offsets, T, H, D, Tc, nC, pad_idx, static_cast<uint8_t*>(x_c), idx_c, dev_err);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+int scfa_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb, int32_t* bucket,
+                     hipStream_t stream) {
+  if (!x || !R || !bucket) return SCFA_ERR_INVALID;
+  if (B < 1 || T < 1 || H < 1 || nb < 2 || nb % 2) return SCFA_ERR_INVALID;
+  if (!dtype_ok(dtype)) return SCFA_ERR_INVALID;
+  if (D != 64 || nb > 64) return SCFA_ERR_UNSUPPORTED;
+  const dim3 grid(ceil_div(T, 256), B * H);
+  const int half = nb / 2;
+#define SCFA_BUCKET_CASE(HALF)                                                                                  \
+  case HALF:                                                                                                    \
+    if (dtype == SCFA_BF16)                                                                                     \
+      hipLaunchKernelGGL((k_hash_bucket<uint16_t, HALF>), grid, dim3(256), 0, stream,                          \
+                         static_cast<const uint16_t*>(x), R, T, H, bucket);                                    \
+    else                                                                                                        \
+      hipLaunchKernelGGL((k_hash_bucket<float, HALF>), grid, dim3(256), 0, stream, static_cast<const float*>(x), \
+                         R, T, H, bucket);                                                                      \
+    break;
+  switch (half) {
+    SCFA_BUCKET_CASE(1)
+    SCFA_BUCKET_CASE(2)
+    SCFA_BUCKET_CASE(3)
+    SCFA_BUCKET_CASE(4)
+    SCFA_BUCKET_CASE(5)
+    SCFA_BUCKET_CASE(6)
+    SCFA_BUCKET_CASE(7)
+    SCFA_BUCKET_CASE(8)
+    SCFA_BUCKET_CASE(12)
+    SCFA_BUCKET_CASE(16)
+    SCFA_BUCKET_CASE(24)
+    SCFA_BUCKET_CASE(32)
+    default:
+      return SCFA_ERR_UNSUPPORTED;
+  }
+#undef SCFA_BUCKET_CASE
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+size_t scfa_hash_sort_workspace_bytes(int B, int H, int T, int nb) {
+  if (B < 1 || H < 1 || T < 1 || nb < 1) return 0;
+  return static_cast<size_t>(B) * H * ceil_div(T, kSortChunk) * nb * sizeof(int32_t);
+}
+
+int scfa_hash_sort(const int32_t* bucket, int B, int H, int T, int nb, int32_t pad_idx, int32_t* perm,
+                   int32_t* bucket_sorted, int32_t* offsets, void* workspace, size_t workspace_bytes,
+                   int32_t* dev_err, hipStream_t stream) {
+  if (!bucket || !perm || !bucket_sorted || !offsets || !workspace) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || T < 1 || nb < 1) return SCFA_ERR_INVALID;
+  if (nb > 64) return SCFA_ERR_UNSUPPORTED;
+  if (workspace_bytes < scfa_hash_sort_workspace_bytes(B, H, T, nb)) return SCFA_ERR_INVALID;
+  const int nC = ceil_div(T, kSortChunk);
+  const int Tp = pad_rows(T);
+  const int nCx = ceil_div(Tp, kSortChunk);
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  hipLaunchKernelGGL(k_sort_hist, dim3(nC, B * H), dim3(256), 0, stream, bucket, T, nb, nC, hist, dev_err);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  hipLaunchKernelGGL(k_sort_scan, dim3(B * H), dim3(64), 0, stream, hist, nb, nC, offsets);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  hipLaunchKernelGGL(k_sort_scatter, dim3(nCx, B * H), dim3(256), 0, stream, bucket, T, Tp, nb, nC, hist, pad_idx,
+                     perm, bucket_sorted);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+int scfa_gather(int dtype, int layout, const void* x, const int32_t* idx, int B, int T, int H, int D, int Tp,
+                void* x_p, hipStream_t stream) {
+  if (!x || !idx || !x_p) return SCFA_ERR_INVALID;
+  if (B < 1 || T < 1 || H < 1 || Tp < SCFA_ROW_ALIGN || Tp % SCFA_ROW_ALIGN) return SCFA_ERR_INVALID;
+  if (!dtype_ok(dtype) || (layout != SCFA_ROWS && layout != SCFA_COLS)) return SCFA_ERR_INVALID;
+  if (D != 64) return SCFA_ERR_UNSUPPORTED;
+  if (layout == SCFA_ROWS) {
+    const int U = D * dtype_size(dtype) / 16;
+    const dim3 grid(ceil_div(Tp * U, 256), B * H);
+    if (dtype == SCFA_BF16)
+      hipLaunchKernelGGL(k_gather_rows<2>, grid, dim3(256), 0, stream, static_cast<const uint8_t*>(x), idx, T, H, D,
+                         Tp, static_cast<uint8_t*>(x_p));
+    else
+      hipLaunchKernelGGL(k_gather_rows<4>, grid, dim3(256), 0, stream, static_cast<const uint8_t*>(x), idx, T, H, D,
+                         Tp, static_cast<uint8_t*>(x_p));
+  } else {
+    const dim3 grid(Tp / 64, B * H);
+    if (dtype == SCFA_BF16)
+      hipLaunchKernelGGL(k_gather_cols<uint16_t>, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x), idx, T,
+                         H, Tp, static_cast<uint16_t*>(x_p));
+    else
+      hipLaunchKernelGGL(k_gather_cols<float>, grid, dim3(256), 0, stream, static_cast<const float*>(x), idx, T, H,
+                         Tp, static_cast<float*>(x_p));
+  }
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
+                     int B, int H, int Tq, int Tk, int Bm, int Bn, int32_t* qstats, int32_t* kstats, int32_t* fwd_tab,
+                     int32_t* bwd_tab, int32_t* tiles, hipStream_t stream) {
+  if (mode != SCFA_DENSE && mode != SCFA_QK && mode != SCFA_HASH) return SCFA_ERR_INVALID;
+  if (!qstats || !kstats || !fwd_tab || !bwd_tab || !tiles) return SCFA_ERR_INVALID;
+  if (mode != SCFA_DENSE && (!q_idx || !k_idx)) return SCFA_ERR_INVALID;
+  if (mode == SCFA_HASH && (!q_bkt || !k_bkt)) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || Tq < 1 || Tk < 1) return SCFA_ERR_INVALID;
+  auto tile_ok = [](int t) { return t == 16 || t == 32 || t == 64 || t == 128; };
+  if (!tile_ok(Bm) || !tile_ok(Bn)) return SCFA_ERR_INVALID;
+  const int TqP = pad_rows(Tq), TkP = pad_rows(Tk);
+  const int nQt = TqP / Bm, nKt = TkP / Bn;
+  hipLaunchKernelGGL(k_tile_stats, dim3(nQt + nKt, B * H), dim3(64), 0, stream, mode, q_idx, k_idx, q_bkt, k_bkt, Tq,
+                     Tk, TqP, TkP, Bm, Bn, nQt, nKt, qstats, kstats, tiles);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  hipLaunchKernelGGL(k_fwd_table, dim3(ceil_div(nQt, 64), B * H), dim3(64), 0, stream, mode, qstats, kstats, nQt, nKt,
+                     fwd_tab, tiles);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  hipLaunchKernelGGL(k_bwd_table, dim3(ceil_div(nKt, 64), B * H), dim3(64), 0, stream, qstats, kstats, fwd_tab, nQt, nKt,
+                     bwd_tab);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
+                       int B, int H, int Tq, int Tk, int64_t* pairs, hipStream_t stream) {
+  if (mode != SCFA_DENSE && mode != SCFA_QK && mode != SCFA_HASH) return SCFA_ERR_INVALID;
+  if (!pairs) return SCFA_ERR_INVALID;
+  if (mode != SCFA_DENSE && (!q_idx || !k_idx)) return SCFA_ERR_INVALID;
+  if (mode == SCFA_HASH && (!q_bkt || !k_bkt)) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || Tq < 1 || Tk < 1) return SCFA_ERR_INVALID;
+  hipLaunchKernelGGL(k_zero_i64, dim3(ceil_div(B * H, 256)), dim3(256), 0, stream, pairs, B * H);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  hipLaunchKernelGGL(k_count_visible, dim3(ceil_div(Tq, 256), B * H), dim3(256), 0, stream, mode, q_idx, k_idx, q_bkt,
+                     k_bkt, Tq, Tk, pad_rows(Tq), pad_rows(Tk), pairs);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+}  // extern "C"

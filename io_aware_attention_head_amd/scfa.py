@@ -1,0 +1,363 @@
+"""Python binding of libscfa.so (ctypes).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libscfa.so. torch is used for device memory and streams. The
+low-level functions carry the C names and take torch CUDA tensors; sizes are
+read from the tensor shapes. The pipeline helpers at the bottom allocate the
+intermediate buffers and chain the C calls for the three modes.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libscfa.so")
+
+SCFA_OK, SCFA_ERR_INVALID, SCFA_ERR_UNSUPPORTED, SCFA_ERR_HIP = 0, -1, -2, -3
+SCFA_DEVERR_COUNT_EXCEEDS_TC, SCFA_DEVERR_BUCKET_RANGE = 1, 2
+SCFA_BF16, SCFA_F32 = 0, 1
+SCFA_DENSE, SCFA_QK, SCFA_HASH = 0, 1, 2
+SCFA_ROWS, SCFA_COLS = 0, 1
+SCFA_Q_PAD, SCFA_K_PAD = -1, 1_000_000_000
+SCFA_ROW_ALIGN = 128
+SCFA_TILE_M, SCFA_TILE_N = 128, 64
+SCFA_COUNT_CHUNK = 64
+
+MODE_IDS = {"dense": SCFA_DENSE, "qk": SCFA_QK, "hash": SCFA_HASH}
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "scfa_status_string": (ctypes.c_char_p, [_i]),
+    "scfa_version": (_i, []),
+    "scfa_qk_count": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "scfa_qk_compact": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_int32, _vp, _vp, _vp, _vp]),
+    "scfa_hash_bucket": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
+    "scfa_hash_sort_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "scfa_hash_sort": (_i, [_vp, _i, _i, _i, _i, ctypes.c_int32, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "scfa_gather": (_i, [_i, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
+    "scfa_range_table": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "scfa_count_visible": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "scfa_qk_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp,
+                                _vp]),
+    "scfa_hash_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp,
+                                  _vp, _vp]),
+    "scfa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "scfa_bwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
+                      _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
+}
+
+_LIB = None
+
+
+class ScfaError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libscfa.so (built in-tree by __graft_entry__.build()). Fails loudly
+    when the library is missing: there is no fallback path."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ScfaError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name, None)
+            if fn is None:
+                continue
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def exported_symbols():
+    L = lib()
+    return [n for n in _SIGS if getattr(L, n, None) is not None]
+
+
+def _check(status: int, name: str):
+    if status != SCFA_OK:
+        msg = lib().scfa_status_string(status).decode()
+        raise ScfaError(f"{name} failed: {msg}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ScfaError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ScfaError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, ref: Optional[torch.Tensor] = None):
+    if stream is None:
+        dev = ref.device if ref is not None else torch.device("cuda")
+        stream = torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SCFA_BF16
+    if t.dtype == torch.float32:
+        return SCFA_F32
+    raise ScfaError(f"unsupported dtype {t.dtype}")
+
+
+def pad_rows(n: int) -> int:
+    return ((n + SCFA_ROW_ALIGN - 1) // SCFA_ROW_ALIGN) * SCFA_ROW_ALIGN
+
+
+# ---------------------------------------------------------------------------
+# Low-level calls (same names as the C ABI).
+# ---------------------------------------------------------------------------
+
+def scfa_status_string(status: int) -> str:
+    return lib().scfa_status_string(status).decode()
+
+
+def scfa_version() -> int:
+    return lib().scfa_version()
+
+
+def scfa_qk_count(keep, count, max_count, chunk_offsets, stream=None):
+    B, T, H = keep.shape
+    _check(lib().scfa_qk_count(_p(keep), B, T, H, _p(count), _p(max_count), _p(chunk_offsets), _stream(stream, keep)),
+           "scfa_qk_count")
+
+
+def scfa_qk_compact(x, keep, count, chunk_offsets, Tc, pad_idx, x_c, idx_c, dev_err=None, stream=None):
+    B, T, H = keep.shape
+    D = x.shape[-1] if x is not None else 64
+    dt = _dt(x) if x is not None else SCFA_BF16
+    _check(lib().scfa_qk_compact(dt, _p(x), _p(keep), _p(count), _p(chunk_offsets), B, T, H, D, Tc, pad_idx, _p(x_c),
+                                 _p(idx_c), _p(dev_err), _stream(stream, keep)), "scfa_qk_compact")
+
+
+def scfa_hash_bucket(x, R, nb, bucket, stream=None):
+    B, T, H, D = x.shape
+    _check(lib().scfa_hash_bucket(_dt(x), _p(x), _p(R), B, T, H, D, nb, _p(bucket), _stream(stream, x)),
+           "scfa_hash_bucket")
+
+
+def scfa_hash_sort_workspace_bytes(B, H, T, nb) -> int:
+    return lib().scfa_hash_sort_workspace_bytes(B, H, T, nb)
+
+
+def scfa_hash_sort(bucket, nb, pad_idx, perm, bucket_sorted, offsets, workspace, dev_err=None, stream=None):
+    B, H, T = bucket.shape
+    _check(lib().scfa_hash_sort(_p(bucket), B, H, T, nb, pad_idx, _p(perm), _p(bucket_sorted), _p(offsets),
+                                _p(workspace), workspace.numel() * workspace.element_size(), _p(dev_err),
+                                _stream(stream, bucket)), "scfa_hash_sort")
+
+
+def scfa_gather(x, idx, layout, x_p, stream=None):
+    B, T, H, D = x.shape
+    Tp = idx.shape[-1]
+    _check(lib().scfa_gather(_dt(x), layout, _p(x), _p(idx), B, T, H, D, Tp, _p(x_p), _stream(stream, x)),
+           "scfa_gather")
+
+
+def scfa_range_table(mode, q_idx, k_idx, q_bkt, k_bkt, B, H, Tq, Tk, Bm, Bn, qstats, kstats, fwd_tab, bwd_tab, tiles,
+                     stream=None):
+    _check(lib().scfa_range_table(mode, _p(q_idx), _p(k_idx), _p(q_bkt), _p(k_bkt), B, H, Tq, Tk, Bm, Bn, _p(qstats),
+                                  _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(tiles), _stream(stream, qstats)),
+           "scfa_range_table")
+
+
+def scfa_count_visible(mode, q_idx, k_idx, q_bkt, k_bkt, B, H, Tq, Tk, pairs, stream=None):
+    _check(lib().scfa_count_visible(mode, _p(q_idx), _p(k_idx), _p(q_bkt), _p(k_bkt), B, H, Tq, Tk, _p(pairs),
+                                    _stream(stream, pairs)), "scfa_count_visible")
+
+
+def scfa_qk_sparse_fwd(q_c, k_c, v_t, q_idx, k_idx, qstats, kstats, fwd_tab, T, O, lse, scale=None, stream=None):
+    B, H, Tc, D = q_c.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(lib().scfa_qk_sparse_fwd(_dt(q_c), _dt(O), _p(q_c), _p(k_c), _p(v_t), _p(q_idx), _p(k_idx), _p(qstats),
+                                    _p(kstats), _p(fwd_tab), B, H, T, Tc, D, scale, _p(O), _p(lse),
+                                    _stream(stream, q_c)), "scfa_qk_sparse_fwd")
+
+
+def scfa_hash_sparse_fwd(q_s, k_s, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, T, O, lse, scale=None,
+                         stream=None):
+    B, H, Tp, D = q_s.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(lib().scfa_hash_sparse_fwd(_dt(q_s), _dt(O), _p(q_s), _p(k_s), _p(v_t), _p(q_idx), _p(k_idx), _p(q_bkt),
+                                      _p(k_bkt), _p(qstats), _p(kstats), _p(fwd_tab), B, H, T, D, scale, _p(O),
+                                      _p(lse), _stream(stream, q_s)), "scfa_hash_sparse_fwd")
+
+
+# ---------------------------------------------------------------------------
+# Pipelines: allocate intermediates and chain the calls.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Prepared:
+    """Compacted / sorted operands of one attention call (head-major)."""
+    mode: str
+    B: int
+    H: int
+    T: int
+    D: int
+    Tq: int          # valid rows (Tc for QK, T otherwise)
+    Tpad: int        # rows of the buffers
+    q: torch.Tensor  # (B,H,Tpad,D) rows
+    k: torch.Tensor  # (B,H,Tpad,D) rows
+    v_t: torch.Tensor  # (B,H,D,Tpad) transposed
+    q_idx: torch.Tensor
+    k_idx: torch.Tensor
+    q_bkt: Optional[torch.Tensor] = None
+    k_bkt: Optional[torch.Tensor] = None
+    extra: dict = dataclasses.field(default_factory=dict)
+
+
+@dataclasses.dataclass
+class Tables:
+    qstats: torch.Tensor
+    kstats: torch.Tensor
+    fwd: torch.Tensor
+    bwd: torch.Tensor
+    tiles: torch.Tensor
+    Bm: int
+    Bn: int
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, stream=None) -> Prepared:
+    """QK-drop preprocessing: counts, compaction of Q and K (rows) and the
+    transposed gather of V by the compacted key positions. Reads the max kept
+    count back to the host once (to size Tc) unless Tc is given."""
+    B, T, H, D = q.shape
+    dev = q
+    i32 = torch.int32
+    nC = (T + SCFA_COUNT_CHUNK - 1) // SCFA_COUNT_CHUNK
+    cq, ck = _empty((B, H), i32, dev), _empty((B, H), i32, dev)
+    mq, mk = _empty((1,), i32, dev), _empty((1,), i32, dev)
+    oq, ok = _empty((B, H, nC), i32, dev), _empty((B, H, nC), i32, dev)
+    scfa_qk_count(keep_q, cq, mq, oq, stream)
+    scfa_qk_count(keep_k, ck, mk, ok, stream)
+    if Tc is None:
+        Tc = pad_rows(max(1, int(torch.maximum(mq, mk).item())))
+    dev_err = torch.zeros((1,), dtype=i32, device=q.device)
+    q_c, k_c = _empty((B, H, Tc, D), q.dtype, dev), _empty((B, H, Tc, D), k.dtype, dev)
+    q_idx, k_idx = _empty((B, H, Tc), i32, dev), _empty((B, H, Tc), i32, dev)
+    scfa_qk_compact(q, keep_q, cq, oq, Tc, SCFA_Q_PAD, q_c, q_idx, dev_err, stream)
+    scfa_qk_compact(k, keep_k, ck, ok, Tc, SCFA_K_PAD, k_c, k_idx, dev_err, stream)
+    v_t = _empty((B, H, D, Tc), v.dtype, dev)
+    scfa_gather(v, k_idx, SCFA_COLS, v_t, stream)
+    return Prepared("qk", B, H, T, D, Tc, Tc, q_c, k_c, v_t, q_idx, k_idx,
+                    extra={"count_q": cq, "count_k": ck, "max_q": mq, "max_k": mk, "dev_err": dev_err})
+
+
+def prepare_hash(q, k, v, R, nb: int, stream=None) -> Prepared:
+    """Hash-sparse preprocessing: LSH buckets of Q and K, stable counting sort
+    per head, gathers of Q, K (rows) and V (transposed) into sorted order."""
+    B, T, H, D = q.shape
+    dev = q
+    i32 = torch.int32
+    Tp = pad_rows(T)
+    bq, bk = _empty((B, H, T), i32, dev), _empty((B, H, T), i32, dev)
+    scfa_hash_bucket(q, R, nb, bq, stream)
+    scfa_hash_bucket(k, R, nb, bk, stream)
+    ws = _empty((max(1, scfa_hash_sort_workspace_bytes(B, H, T, nb)),), torch.uint8, dev)
+    dev_err = torch.zeros((1,), dtype=i32, device=q.device)
+    q_idx, k_idx = _empty((B, H, Tp), i32, dev), _empty((B, H, Tp), i32, dev)
+    q_bs, k_bs = _empty((B, H, Tp), i32, dev), _empty((B, H, Tp), i32, dev)
+    offq, offk = _empty((B, H, nb + 1), i32, dev), _empty((B, H, nb + 1), i32, dev)
+    scfa_hash_sort(bq, nb, SCFA_Q_PAD, q_idx, q_bs, offq, ws, dev_err, stream)
+    scfa_hash_sort(bk, nb, SCFA_K_PAD, k_idx, k_bs, offk, ws, dev_err, stream)
+    q_s, k_s = _empty((B, H, Tp, D), q.dtype, dev), _empty((B, H, Tp, D), k.dtype, dev)
+    v_t = _empty((B, H, D, Tp), v.dtype, dev)
+    scfa_gather(q, q_idx, SCFA_ROWS, q_s, stream)
+    scfa_gather(k, k_idx, SCFA_ROWS, k_s, stream)
+    scfa_gather(v, k_idx, SCFA_COLS, v_t, stream)
+    return Prepared("hash", B, H, T, D, T, Tp, q_s, k_s, v_t, q_idx, k_idx, q_bs, k_bs,
+                    extra={"bucket_q": bq, "bucket_k": bk, "offsets_q": offq, "offsets_k": offk, "dev_err": dev_err,
+                           "workspace": ws})
+
+
+def prepare_dense(q, k, v, stream=None) -> Prepared:
+    """Dense causal attention on the same kernel: positions 0..T-1 for both
+    queries and keys (the QK path with nothing dropped), head-major gathers."""
+    B, T, H, D = q.shape
+    Tp = pad_rows(T)
+    ar = torch.arange(Tp, dtype=torch.int32, device=q.device)
+    q_idx = torch.where(ar < T, ar, torch.full_like(ar, SCFA_Q_PAD)).expand(B, H, Tp).contiguous()
+    k_idx = torch.where(ar < T, ar, torch.full_like(ar, SCFA_K_PAD)).expand(B, H, Tp).contiguous()
+    q_s, k_s = _empty((B, H, Tp, D), q.dtype, q), _empty((B, H, Tp, D), k.dtype, q)
+    v_t = _empty((B, H, D, Tp), v.dtype, q)
+    scfa_gather(q, q_idx, SCFA_ROWS, q_s, stream)
+    scfa_gather(k, k_idx, SCFA_ROWS, k_s, stream)
+    scfa_gather(v, k_idx, SCFA_COLS, v_t, stream)
+    return Prepared("dense", B, H, T, D, Tp, Tp, q_s, k_s, v_t, q_idx, k_idx)
+
+
+def build_tables(pre: Prepared, Bm: int = SCFA_TILE_M, Bn: int = SCFA_TILE_N, stream=None) -> Tables:
+    """Tile extrema and range tables. Dense inputs use the QK rule on their
+    arange positions (identical to the dense rule, and it keeps the ragged
+    tail's pads out of the causal ranges)."""
+    B, H = pre.B, pre.H
+    nQt, nKt = pre.Tpad // Bm, pre.Tpad // Bn
+    mode = SCFA_HASH if pre.mode == "hash" else SCFA_QK
+    i32 = torch.int32
+    t = Tables(_empty((B, H, nQt, 4), i32, pre.q), _empty((B, H, nKt, 4), i32, pre.q), _empty((B, H, nQt, 2), i32, pre.q),
+               _empty((B, H, nKt, 2), i32, pre.q), _empty((B, H), i32, pre.q), Bm, Bn)
+    scfa_range_table(mode, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, B, H, pre.Tq, pre.Tq, Bm, Bn, t.qstats, t.kstats,
+                     t.fwd, t.bwd, t.tiles, stream)
+    return t
+
+
+def count_visible(pre: Prepared, stream=None) -> torch.Tensor:
+    pairs = _empty((pre.B, pre.H), torch.int64, pre.q)
+    mode = SCFA_HASH if pre.mode == "hash" else SCFA_QK
+    scfa_count_visible(mode, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, pre.B, pre.H, pre.Tq, pre.Tq, pairs, stream)
+    return pairs
+
+
+def forward(pre: Prepared, tab: Tables, out_dtype=torch.float32, scale=None, O=None, lse=None, stream=None):
+    """Attention forward on prepared operands. Returns O (B,T,H,D) in original
+    order and LSE (B,H,T) float32."""
+    B, H, T, D = pre.B, pre.H, pre.T, pre.D
+    if O is None:
+        O = _empty((B, T, H, D), out_dtype, pre.q)
+    if lse is None:
+        lse = _empty((B, H, T), torch.float32, pre.q)
+    if pre.mode == "hash":
+        scfa_hash_sparse_fwd(pre.q, pre.k, pre.v_t, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats,
+                             tab.fwd, T, O, lse, scale, stream)
+    else:
+        scfa_qk_sparse_fwd(pre.q, pre.k, pre.v_t, pre.q_idx, pre.k_idx, tab.qstats, tab.kstats, tab.fwd, T, O, lse,
+                           scale, stream)
+    return O, lse
+
+
+def qk_sparse_attention(q, k, v, keep_q, keep_k, out_dtype=torch.float32, scale=None):
+    pre = prepare_qk(q, k, v, keep_q, keep_k)
+    return forward(pre, build_tables(pre), out_dtype, scale)
+
+
+def hash_sparse_attention(q, k, v, R, nb, out_dtype=torch.float32, scale=None):
+    pre = prepare_hash(q, k, v, R, nb)
+    return forward(pre, build_tables(pre), out_dtype, scale)
+
+
+def dense_causal_attention(q, k, v, out_dtype=torch.float32, scale=None):
+    pre = prepare_dense(q, k, v)
+    return forward(pre, build_tables(pre), out_dtype, scale)

@@ -1,0 +1,95 @@
+"""The C-ABI library loads without a GPU, exports every symbol the header
+declares, and rejects host-visible argument errors before enqueueing anything
+(no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import io_aware_attention_head_amd.scfa as scfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "scfa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(scfa.LIB_PATH), reason="libscfa.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(scfa_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_symbols_exported():
+    L = scfa.lib()
+    names = _declared()
+    assert "scfa_qk_sparse_fwd" in names and "scfa_hash_sparse_fwd" in names
+    missing = [n for n in names if getattr(L, n, None) is None]
+    assert not missing, missing
+    # every declared symbol has a binding signature
+    assert not [n for n in names if n not in scfa._SIGS]
+
+
+def test_status_strings_and_version():
+    assert scfa.scfa_status_string(0) == "SCFA_OK"
+    for s in (-1, -2, -3):
+        assert scfa.scfa_status_string(s).startswith("SCFA_ERR")
+    assert scfa.scfa_version() >= 100
+
+
+def test_invalid_arguments_rejected_without_gpu():
+    L = scfa.lib()
+    null = None
+    dummy = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    # NULL pointers
+    assert L.scfa_qk_count(null, 1, 8, 1, dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    # bad sizes
+    assert L.scfa_qk_count(dummy, 0, 8, 1, dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    # Tc not a multiple of 128
+    assert L.scfa_qk_compact(0, dummy, dummy, dummy, dummy, 1, 8, 1, 64, 100, -1, dummy, dummy, null,
+                             null) == scfa.SCFA_ERR_INVALID
+    # D != 64
+    assert L.scfa_qk_compact(0, dummy, dummy, dummy, dummy, 1, 8, 1, 32, 128, -1, dummy, dummy, null,
+                             null) == scfa.SCFA_ERR_UNSUPPORTED
+    # odd nb / unsupported nb
+    assert L.scfa_hash_bucket(0, dummy, dummy, 1, 8, 1, 64, 15, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_bucket(0, dummy, dummy, 1, 8, 1, 64, 128, dummy, null) == scfa.SCFA_ERR_UNSUPPORTED
+    # bad dtype
+    assert L.scfa_gather(7, 0, dummy, dummy, 1, 8, 1, 64, 128, dummy, null) == scfa.SCFA_ERR_INVALID
+    # bad layout
+    assert L.scfa_gather(0, 5, dummy, dummy, 1, 8, 1, 64, 128, dummy, null) == scfa.SCFA_ERR_INVALID
+    # workspace too small
+    assert L.scfa_hash_sort(dummy, 1, 1, 1000, 16, -1, dummy, dummy, dummy, dummy, 4, null,
+                            null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_sort_workspace_bytes(1, 1, 1000, 16) == 4 * 16 * 4
+    # tile sizes
+    assert L.scfa_range_table(1, dummy, dummy, null, null, 1, 1, 8, 8, 48, 64, dummy, dummy, dummy, dummy, dummy,
+                              null) == scfa.SCFA_ERR_INVALID
+    # hash mode needs buckets
+    assert L.scfa_range_table(2, dummy, dummy, null, null, 1, 1, 8, 8, 128, 64, dummy, dummy, dummy, dummy, dummy,
+                              null) == scfa.SCFA_ERR_INVALID
+    # forward: bad scale, D, Tc
+    args = [0, 1] + [dummy] * 8
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 64, ctypes.c_float(0.0), dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 128, ctypes.c_float(0.125), dummy, dummy,
+                                null) == scfa.SCFA_ERR_UNSUPPORTED
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 120, 64, ctypes.c_float(0.125), dummy, dummy,
+                                null) == scfa.SCFA_ERR_INVALID
+    hargs = [0, 1] + [dummy] * 10
+    assert L.scfa_hash_sparse_fwd(*hargs[:-1], null, 1, 1, 8, 64, ctypes.c_float(0.125), dummy, dummy,
+                                  null) == scfa.SCFA_ERR_INVALID
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 8, 1, 64)
+    with pytest.raises(scfa.ScfaError):
+        scfa.scfa_gather(x, torch.zeros(1, 1, 128, dtype=torch.int32), scfa.SCFA_ROWS, torch.zeros(1, 1, 128, 64))
+
+
+def test_header_constants_match_binding():
+    txt = open(HEADER).read()
+    for name in ("SCFA_TILE_M", "SCFA_TILE_N", "SCFA_ROW_ALIGN", "SCFA_COUNT_CHUNK", "SCFA_K_PAD"):
+        m = re.search(rf"#define {name} \(?(-?\d+)\)?", txt)
+        assert m and int(m.group(1)) == getattr(scfa, name), name

@@ -1,0 +1,202 @@
+"""GPU parity of the forward attention against the float64 oracle (calls go
+through the C ABI): small cases compared element by element over all of O and
+LSE, full-size workloads on sampled rows of every head plus properties that
+hold at any size, and the edge cases of the method."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import io_aware_attention_head_amd.scfa as scfa
+from io_aware_attention_head_amd.inputs import WORKLOADS, make_inputs, small
+from gpu_util import announce, check_fwd, f64, need_gpu, oracle_buckets, oracle_fwd, run_pipeline, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    WORKLOADS["qk_f32_t256"],
+    small("qk", 2, 3, 777, keep_p=0.6, seed=51),
+    small("qk", 1, 2, 1000, dtype="f32", keep_p=0.5, seed=52),
+    small("hash", 2, 3, 1000, nb=16, seed=53),
+    small("hash", 1, 2, 513, dtype="f32", nb=4, seed=54),
+    small("hash", 1, 3, 2048, nb=64, seed=55),
+    small("dense", 1, 2, 333, seed=56),
+    small("dense", 2, 2, 1024, dtype="f32", seed=57),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_fwd_small_all_outputs(w):
+    need_gpu()
+    announce(f"fwd {w.name}")
+    x = make_inputs(w)
+    _, pre, tab, O, lse = run_pipeline(w, x)
+    Or, Lr = oracle_fwd(w, x)
+    err, lerr = check_fwd(w, O, lse, Or, Lr)
+    print(f"{w.name}: max-abs {err:.2e}  lse {lerr:.2e}")
+
+
+def test_fwd_bf16_output_small():
+    need_gpu()
+    w = small("hash", 1, 2, 600, nb=8, seed=58)
+    announce("fwd bf16 output")
+    x = make_inputs(w)
+    _, pre, tab, O, lse = run_pipeline(w, x, out_dtype=torch.bfloat16)
+    assert O.dtype == torch.bfloat16
+    Or, Lr = oracle_fwd(w, x)
+    check_fwd(w, O, lse, Or, Lr)
+
+
+def test_dense_equals_qk_all_kept_and_single_bucket():
+    """Dense mode, QK with every token kept and hash with one bucket (R = 0)
+    run different preprocessing but must give the same attention."""
+    need_gpu()
+    announce("mode equivalences")
+    w = small("dense", 1, 2, 700, seed=59)
+    x = make_inputs(w)
+    g = to_dev(x)
+    Od, Ld = scfa.dense_causal_attention(g["q"], g["k"], g["v"])
+    ones = torch.ones_like(g["keep_q"])
+    Oq, Lq = scfa.qk_sparse_attention(g["q"], g["k"], g["v"], ones, ones)
+    Oh, Lh = scfa.hash_sparse_attention(g["q"], g["k"], g["v"], torch.zeros_like(g["R"]), 16)
+    torch.cuda.synchronize()
+    Or, Lr = oracle_fwd(w, x)
+    for O, L in ((Od, Ld), (Oq, Lq), (Oh, Lh)):
+        check_fwd(w, O, L, Or, Lr)
+    assert torch.equal(Od, Oq)  # same kernel, same operands
+
+
+EDGE = {
+    "all_keys_dropped": dict(keep_k=0.0, keep_q=0.7),
+    "all_queries_dropped": dict(keep_k=0.7, keep_q=0.0),
+    "one_token_kept": dict(one=True),
+    "T1": dict(T=1),
+    "BH1": dict(B=1, H=1),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE))
+def test_qk_edge_cases(case):
+    need_gpu()
+    announce(f"qk edge {case}")
+    spec = EDGE[case]
+    w = small("qk", spec.get("B", 2), spec.get("H", 2), spec.get("T", 300), keep_p=0.7, seed=60)
+    x = make_inputs(w)
+    if "keep_k" in spec:
+        x["keep_k"] = (torch.rand(x["keep_k"].shape, generator=torch.Generator().manual_seed(1)) < spec["keep_k"]).to(torch.uint8)
+        x["keep_q"] = (torch.rand(x["keep_q"].shape, generator=torch.Generator().manual_seed(2)) < spec["keep_q"]).to(torch.uint8)
+    if spec.get("one"):
+        x["keep_q"].zero_()
+        x["keep_k"].zero_()
+        x["keep_q"][:, 150] = 1
+        x["keep_k"][:, 100] = 1
+    _, pre, tab, O, lse = run_pipeline(w, x)
+    Or, Lr = oracle_fwd(w, x)
+    check_fwd(w, O, lse, Or, Lr)
+    if case == "all_keys_dropped" or case == "all_queries_dropped":
+        assert (O == 0).all() and torch.isneginf(lse).all()
+
+
+def test_qk_compacted_length_larger_than_needed():
+    """Extra all-pad tiles (Tc well above the kept count) change nothing."""
+    need_gpu()
+    announce("qk oversized Tc")
+    w = small("qk", 1, 2, 500, keep_p=0.5, seed=61)
+    x = make_inputs(w)
+    g = to_dev(x)
+    pre = scfa.prepare_qk(g["q"], g["k"], g["v"], g["keep_q"], g["keep_k"], Tc=768)
+    O, lse = scfa.forward(pre, scfa.build_tables(pre))
+    torch.cuda.synchronize()
+    Or, Lr = oracle_fwd(w, x)
+    check_fwd(w, O, lse, Or, Lr)
+
+
+@pytest.mark.parametrize("case", ["single_bucket", "last_bucket_only", "T1", "skewed"])
+def test_hash_edge_cases(case):
+    need_gpu()
+    announce(f"hash edge {case}")
+    T = 1 if case == "T1" else 900
+    w = small("hash", 1, 3, T, nb=16, seed=62)
+    x = make_inputs(w)
+    if case == "single_bucket":
+        x["R"].zero_()
+    elif case == "last_bucket_only":
+        # all projections negative and equal-magnitude-free: bucket = nb/2 + argmax(-c)
+        x["R"].zero_()
+        x["R"][:, :, 7] = 1.0
+        x["q"] = -x["q"].abs() - 0.01
+        x["k"] = -x["k"].abs() - 0.01
+        x["q"] = x["q"].to(torch.bfloat16)
+        x["k"] = x["k"].to(torch.bfloat16)
+    elif case == "skewed":
+        x["R"][:, :, 0] += 3.0  # most tokens land in bucket 0 or 8
+    _, pre, tab, O, lse = run_pipeline(w, x)
+    bq, bk = oracle_buckets(w, x)
+    if case == "last_bucket_only":
+        assert (bq == 15).all() and (bk == 15).all()
+    Or, Lr = oracle_fwd(w, x, buckets=(bq, bk))
+    check_fwd(w, O, lse, Or, Lr)
+
+
+def _sampled_rows(T, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.choice(T, n, replace=False), [0, 1, T - 1], np.arange(T - 64, T)]))
+    return rows
+
+
+@pytest.mark.parametrize("name", ["dense_bf16_t2048", "qk_bf16_t8192_keep0.7", "qk_bf16_t8192_keep0.5",
+                                  "hash_bf16_t16384_nb16"])
+def test_fwd_full_size(name):
+    """The benchmark workloads at full size, in the benchmark's launch
+    configuration: sampled rows of EVERY head against the oracle, and over all
+    rows: finite outputs, LSE = -inf exactly for rows without a visible key,
+    zero rows there."""
+    need_gpu()
+    w = WORKLOADS[name]
+    announce(f"full-size fwd {name}")
+    x = make_inputs(w)
+    _, pre, tab, O, lse = run_pipeline(w, x)
+    rows = np.arange(w.T) if w.T <= 2048 else _sampled_rows(w.T, 192, 7)
+    buckets = oracle_buckets(w, x) if w.mode == "hash" else None
+    Or, Lr = oracle_fwd(w, x, rows=rows, buckets=buckets)
+    err, lerr = check_fwd(w, O, lse, Or, Lr, rows=rows)
+    print(f"{name}: sampled max-abs {err:.2e}  lse {lerr:.2e}")
+    # properties over all rows
+    Og = O.cpu()
+    assert torch.isfinite(Og).all()
+    L = lse.cpu().numpy()
+    if w.mode == "qk":
+        kq, kk = x["keep_q"].numpy(), x["keep_k"].numpy()
+        nvis = np.cumsum(kk, axis=1) * kq  # (B,T,H) visible keys per query
+    elif w.mode == "hash":
+        bq, bk = buckets
+        onehot = np.zeros((w.B, w.H, w.T, w.nb), dtype=np.int32)
+        np.put_along_axis(onehot, bk[..., None], 1, axis=-1)
+        cum = np.cumsum(onehot, axis=2)
+        nvis = np.take_along_axis(cum, bq[..., None], axis=-1)[..., 0].transpose(0, 2, 1)
+    else:
+        nvis = np.broadcast_to(np.arange(1, w.T + 1)[None, :, None], (w.B, w.T, w.H))
+    empty = nvis.transpose(0, 2, 1) == 0
+    assert np.array_equal(np.isneginf(L), empty)
+    assert (Og.numpy()[empty.transpose(0, 2, 1)] == 0).all()
+    # visible-pair count of the GPU equals the oracle's
+    pairs = scfa.count_visible(pre).cpu().numpy()
+    if w.mode == "hash":
+        ref = oracle.visible_pairs("hash", w.T, w.B, w.H, bkt_q=bq, bkt_k=bk)
+    elif w.mode == "qk":
+        ref = oracle.visible_pairs("qk", w.T, w.B, w.H, kq, kk)
+    else:
+        ref = oracle.visible_pairs("dense", w.T, w.B, w.H)
+    assert np.array_equal(pairs, ref)
+    assert int(nvis.sum()) == int(ref.sum())
+
+
+def test_fwd_deterministic():
+    need_gpu()
+    announce("fwd determinism")
+    w = small("hash", 1, 4, 3000, nb=16, seed=63)
+    x = make_inputs(w)
+    _, pre, tab, O1, l1 = run_pipeline(w, x)
+    O2, l2 = scfa.forward(pre, tab)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(l1, l2)

@@ -1,0 +1,200 @@
+"""GPU parity of the integer steps: compaction, LSH bucket, counting sort,
+gathers, tile tables and visible-pair counts must equal the oracle BIT FOR
+BIT (calls go through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import io_aware_attention_head_amd.scfa as scfa
+from io_aware_attention_head_amd.inputs import WORKLOADS, make_inputs, small
+from gpu_util import announce, f64, need_gpu, np_bits, oracle_buckets, to_dev
+
+pytestmark = pytest.mark.gpu
+
+QK_CASES = [small("qk", 2, 3, 777, keep_p=0.6, seed=21), small("qk", 1, 2, 256, dtype="f32", keep_p=0.7, seed=1),
+            small("qk", 1, 1, 1, keep_p=1.0, seed=22), small("qk", 2, 2, 300, keep_p=0.0, seed=23),
+            small("qk", 1, 12, 2048, keep_p=0.5, seed=24)]
+HASH_CASES = [small("hash", 2, 3, 1000, nb=16, seed=31), small("hash", 1, 2, 1, nb=16, seed=32),
+              small("hash", 1, 2, 333, dtype="f32", nb=8, seed=33), small("hash", 1, 4, 4096, nb=64, seed=34),
+              small("hash", 2, 2, 700, nb=2, seed=35)]
+
+
+def _tables_match(mode, pre, tab, Tq, Bm, Bn, q_bkt=None, k_bkt=None):
+    qi = pre.q_idx.cpu().numpy()[:, :, :Tq]
+    ki = pre.k_idx.cpu().numpy()[:, :, :Tq]
+    qb = None if q_bkt is None else q_bkt.cpu().numpy()[:, :, :Tq]
+    kb = None if k_bkt is None else k_bkt.cpu().numpy()[:, :, :Tq]
+    ref = oracle.range_tables(mode, qi, ki, qb, kb, Bm, Bn)
+    nQ, nK = ref["fwd"].shape[2], ref["bwd"].shape[2]
+    qs, ks = tab.qstats.cpu().numpy(), tab.kstats.cpu().numpy()
+    fwd, bwd = tab.fwd.cpu().numpy(), tab.bwd.cpu().numpy()
+    assert np.array_equal(qs[:, :, :nQ], ref["qstats"])
+    assert np.array_equal(ks[:, :, :nK], ref["kstats"])
+    assert np.array_equal(fwd[:, :, :nQ], ref["fwd"])
+    assert np.array_equal(bwd[:, :, :nK], ref["bwd"])
+    assert np.array_equal(tab.tiles.cpu().numpy(), ref["tiles"])
+    # tiles beyond the valid rows are empty and never processed
+    assert (fwd[:, :, nQ:, 0] == fwd[:, :, nQ:, 1]).all()
+    assert (bwd[:, :, nK:] == 0).all()
+    assert (ks[:, :, nK:, 0] == scfa.SCFA_K_PAD).all()
+    return ref
+
+
+@pytest.mark.parametrize("w", QK_CASES, ids=lambda w: w.name)
+def test_qk_compaction_bitexact(w):
+    need_gpu()
+    announce(f"qk compaction {w.name}")
+    x = make_inputs(w)
+    g = to_dev(x)
+    pre = scfa.prepare_qk(g["q"], g["k"], g["v"], g["keep_q"], g["keep_k"])
+    torch.cuda.synchronize()
+    assert int(pre.extra["dev_err"].item()) == 0
+    kq, kk = x["keep_q"].numpy(), x["keep_k"].numpy()
+    cq, ck = oracle.qk_count(kq), oracle.qk_count(kk)
+    assert np.array_equal(pre.extra["count_q"].cpu().numpy(), cq)
+    assert np.array_equal(pre.extra["count_k"].cpu().numpy(), ck)
+    assert int(pre.extra["max_q"].item()) == cq.max() and int(pre.extra["max_k"].item()) == ck.max()
+    Tc = pre.Tq
+    assert Tc == scfa.pad_rows(max(1, int(max(cq.max(), ck.max()))))
+    qc, qi = oracle.qk_compact(np_bits(x["q"]), kq, Tc, oracle.Q_PAD)
+    kc, ki = oracle.qk_compact(np_bits(x["k"]), kk, Tc, oracle.K_PAD)
+    assert np.array_equal(pre.q_idx.cpu().numpy(), qi)
+    assert np.array_equal(pre.k_idx.cpu().numpy(), ki)
+    assert np.array_equal(np_bits(pre.q), qc)
+    assert np.array_equal(np_bits(pre.k), kc)
+    vref = oracle.gather_rows(np_bits(x["v"]), ki)
+    assert np.array_equal(np_bits(pre.v_t), vref.transpose(0, 1, 3, 2))
+    tab = scfa.build_tables(pre)
+    torch.cuda.synchronize()
+    _tables_match("qk", pre, tab, Tc, scfa.SCFA_TILE_M, scfa.SCFA_TILE_N)
+    pairs = scfa.count_visible(pre).cpu().numpy()
+    assert np.array_equal(pairs, oracle.visible_pairs("qk", w.T, w.B, w.H, kq, kk))
+
+
+@pytest.mark.parametrize("w", HASH_CASES, ids=lambda w: w.name)
+def test_hash_bucket_sort_gather_bitexact(w):
+    need_gpu()
+    announce(f"hash preprocessing {w.name}")
+    x = make_inputs(w)
+    g = to_dev(x)
+    pre = scfa.prepare_hash(g["q"], g["k"], g["v"], g["R"], w.nb)
+    torch.cuda.synchronize()
+    assert int(pre.extra["dev_err"].item()) == 0
+    bq, bk = oracle_buckets(w, x)
+    assert np.array_equal(pre.extra["bucket_q"].cpu().numpy(), bq)
+    assert np.array_equal(pre.extra["bucket_k"].cpu().numpy(), bk)
+    T, Tp = w.T, pre.Tpad
+    for b_, pre_idx, pre_bs, off, pad in ((bq, pre.q_idx, pre.q_bkt, pre.extra["offsets_q"], oracle.Q_PAD),
+                                          (bk, pre.k_idx, pre.k_bkt, pre.extra["offsets_k"], oracle.K_PAD)):
+        perm, bs, offs = oracle.hash_sort(b_, w.nb)
+        gi, gb = pre_idx.cpu().numpy(), pre_bs.cpu().numpy()
+        assert np.array_equal(gi[:, :, :T], perm)
+        assert (gi[:, :, T:] == pad).all()
+        assert np.array_equal(gb[:, :, :T], bs)
+        assert (gb[:, :, T:] == -1).all()
+        assert np.array_equal(off.cpu().numpy(), offs)
+    qi, ki = pre.q_idx.cpu().numpy(), pre.k_idx.cpu().numpy()
+    assert np.array_equal(np_bits(pre.q), oracle.gather_rows(np_bits(x["q"]), qi))
+    assert np.array_equal(np_bits(pre.k), oracle.gather_rows(np_bits(x["k"]), ki))
+    assert np.array_equal(np_bits(pre.v_t), oracle.gather_rows(np_bits(x["v"]), ki).transpose(0, 1, 3, 2))
+    tab = scfa.build_tables(pre)
+    torch.cuda.synchronize()
+    _tables_match("hash", pre, tab, T, scfa.SCFA_TILE_M, scfa.SCFA_TILE_N, pre.q_bkt, pre.k_bkt)
+    pairs = scfa.count_visible(pre).cpu().numpy()
+    assert np.array_equal(pairs, oracle.visible_pairs("hash", T, w.B, w.H, bkt_q=bq, bkt_k=bk))
+
+
+@pytest.mark.parametrize("Bm,Bn", [(16, 16), (32, 64), (64, 128), (128, 32), (128, 128)])
+def test_tables_any_tile_size(Bm, Bn):
+    """Tile-size invariance of the table rules: the GPU tables equal the
+    oracle's for every supported tile shape, in all three modes."""
+    need_gpu()
+    announce(f"tables Bm={Bm} Bn={Bn}")
+    for w in (small("hash", 1, 2, 900, nb=8, seed=41), small("qk", 1, 2, 900, keep_p=0.5, seed=42)):
+        x = make_inputs(w)
+        g = to_dev(x)
+        pre = (scfa.prepare_hash(g["q"], g["k"], g["v"], g["R"], w.nb) if w.mode == "hash"
+               else scfa.prepare_qk(g["q"], g["k"], g["v"], g["keep_q"], g["keep_k"]))
+        tab = scfa.build_tables(pre, Bm, Bn)
+        torch.cuda.synchronize()
+        ref = _tables_match(w.mode, pre, tab, pre.Tq, Bm, Bn, pre.q_bkt, pre.k_bkt)
+        assert ref["tiles"].sum() > 0
+    # dense mode of the table call (positions = row numbers, no index arrays)
+    T = 1000
+    B, H = 1, 2
+    nQt, nKt = scfa.pad_rows(T) // Bm, scfa.pad_rows(T) // Bn
+    i32 = torch.int32
+    d = torch.device("cuda:0")
+    t = [torch.empty(s, dtype=i32, device=d) for s in ((B, H, nQt, 4), (B, H, nKt, 4), (B, H, nQt, 2), (B, H, nKt, 2),
+                                                      (B, H))]
+    scfa.scfa_range_table(scfa.SCFA_DENSE, None, None, None, None, B, H, T, T, Bm, Bn, *t)
+    torch.cuda.synchronize()
+    a = np.broadcast_to(np.arange(T, dtype=np.int32), (B, H, T)).copy()
+    ref = oracle.range_tables("dense", a, a, None, None, Bm, Bn)
+    nQ, nK = ref["fwd"].shape[2], ref["bwd"].shape[2]
+    assert np.array_equal(t[2].cpu().numpy()[:, :, :nQ], ref["fwd"])
+    assert np.array_equal(t[3].cpu().numpy()[:, :, :nK], ref["bwd"])
+    assert np.array_equal(t[4].cpu().numpy(), ref["tiles"])
+
+
+def test_device_error_flags():
+    """Data errors only the device sees set dev_err (no host sync needed)."""
+    need_gpu()
+    announce("device error flags")
+    d = torch.device("cuda:0")
+    # a bucket id outside [0, nb)
+    B, H, T, nb = 1, 1, 300, 8
+    bucket = torch.randint(0, nb, (B, H, T), dtype=torch.int32, device=d)
+    bucket[0, 0, 17] = nb + 3
+    ws = torch.empty(scfa.scfa_hash_sort_workspace_bytes(B, H, T, nb), dtype=torch.uint8, device=d)
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+    Tp = scfa.pad_rows(T)
+    perm = torch.empty((B, H, Tp), dtype=torch.int32, device=d)
+    bs = torch.empty_like(perm)
+    off = torch.empty((B, H, nb + 1), dtype=torch.int32, device=d)
+    scfa.scfa_hash_sort(bucket, nb, -1, perm, bs, off, ws, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & scfa.SCFA_DEVERR_BUCKET_RANGE
+    # a kept count above the compacted length
+    keep = torch.ones((1, 200, 1), dtype=torch.uint8, device=d)
+    x = torch.zeros((1, 200, 1, 64), dtype=torch.bfloat16, device=d)
+    cnt = torch.empty((1, 1), dtype=torch.int32, device=d)
+    mx = torch.empty((1,), dtype=torch.int32, device=d)
+    co = torch.empty((1, 1, 4), dtype=torch.int32, device=d)
+    scfa.scfa_qk_count(keep, cnt, mx, co)
+    err.zero_()
+    xc = torch.empty((1, 1, 128, 64), dtype=torch.bfloat16, device=d)
+    idx = torch.empty((1, 1, 128), dtype=torch.int32, device=d)
+    scfa.scfa_qk_compact(x, keep, cnt, co, 128, -1, xc, idx, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & scfa.SCFA_DEVERR_COUNT_EXCEEDS_TC
+    assert idx.cpu().numpy().tolist()[0][0] == list(range(128))
+
+
+@pytest.mark.parametrize("name", ["qk_bf16_t8192_keep0.7", "qk_bf16_t8192_keep0.5", "hash_bf16_t16384_nb16"])
+def test_full_size_preprocessing_bitexact(name):
+    """Full-size workloads: every integer output bit-exact against the oracle."""
+    need_gpu()
+    w = WORKLOADS[name]
+    announce(f"full-size preprocessing {name}")
+    x = make_inputs(w)
+    g = to_dev(x)
+    if w.mode == "hash":
+        pre = scfa.prepare_hash(g["q"], g["k"], g["v"], g["R"], w.nb)
+        torch.cuda.synchronize()
+        bq, bk = oracle_buckets(w, x)
+        assert np.array_equal(pre.extra["bucket_q"].cpu().numpy(), bq)
+        assert np.array_equal(pre.extra["bucket_k"].cpu().numpy(), bk)
+        perm, bs, _ = oracle.hash_sort(bk, w.nb)
+        assert np.array_equal(pre.k_idx.cpu().numpy()[:, :, :w.T], perm)
+        mode = "hash"
+    else:
+        pre = scfa.prepare_qk(g["q"], g["k"], g["v"], g["keep_q"], g["keep_k"])
+        torch.cuda.synchronize()
+        _, ki = oracle.qk_compact(None, x["keep_k"].numpy(), pre.Tq, oracle.K_PAD)
+        assert np.array_equal(pre.k_idx.cpu().numpy(), ki)
+        mode = "qk"
+    tab = scfa.build_tables(pre)
+    torch.cuda.synchronize()
+    _tables_match(mode, pre, tab, pre.Tq, scfa.SCFA_TILE_M, scfa.SCFA_TILE_N, pre.q_bkt, pre.k_bkt)
