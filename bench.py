@@ -1,0 +1,253 @@
+#!/usr/bin/env python
+"""Benchmark of the sparse causal flash attention hot path on one MI355X.
+
+One step = the whole hash-sparse forward path over one batch of resident
+synthetic inputs: LSH buckets of Q and K, stable sort by bucket, gathers into
+sorted order, tile range tables, attention forward (output scattered back to
+original positions). Workload: B=2, H=12, T=16384, D=64, nb=16, bf16 inputs,
+N(0,1) values (the language-model shapes of the explainer of arXiv
+2306.01160: 12 heads of 64 dimensions, 16 buckets).
+
+Prints ONE JSON line. `value` = visible-pair TFLOP/s of the whole step
+(4*D FLOPs per visible (query, key) pair / step time). Extra keys give the
+forward kernel alone (TFLOP/s, fraction of the bf16 MFMA peak), its speedup
+over the same kernel run dense-causal on the same shape, per-stage times and
+achieved GB/s of the preprocessing, the roofline of the forward kernel, and
+the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+FWD_SOURCE = os.path.join(ROOT, "io_aware_attention_head_amd", "csrc", "scfa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_hash_bf16_t16384_nb16.json")
+
+
+def _src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="hash_bf16_t16384_nb16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (HBM counter calibration) and exit")
+    ap.add_argument("--fwd-only", action="store_true", help="only launch the forward kernel in the timed loop "
+                                                            "(for counter collection)")
+    return ap.parse_args()
+
+
+def _copy_calibration():
+    import torch
+    n = 512 * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}))
+
+
+def _cpu_baseline(w, x):
+    """The float64 oracle, untuned, on one (b, h) head of the workload: LSH
+    bucket + stable sort of that head's queries and keys and the explicit
+    masked-softmax forward over all of its rows."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    b, h = 0, 0
+    sl = slice(h, h + 1)
+    q = x["q"][b:b + 1, :, sl].double().numpy()
+    k = x["k"][b:b + 1, :, sl].double().numpy()
+    v = x["v"][b:b + 1, :, sl].double().numpy()
+    R = x["R"][sl].double().numpy()
+    t0 = time.perf_counter()
+    bq = oracle.hash_bucket(q, R, w.nb)
+    bk = oracle.hash_bucket(k, R, w.nb)
+    oracle.hash_sort(bq, w.nb)
+    oracle.hash_sort(bk, w.nb)
+    oracle.attention_fwd("hash", q, k, v, bkt_q=bq, bkt_k=bk)
+    dt = time.perf_counter() - t0
+    pairs = int(oracle.visible_pairs("hash", w.T, 1, 1, bkt_q=bq, bkt_k=bk).sum())
+    return {"value": 4 * w.D * pairs / dt / 1e12, "unit": "visible-pair TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"1 of {w.B * w.H} heads (b=0,h=0) of {w.name}: float64 LSH bucket + stable sort of its "
+                      f"queries and keys, explicit masked-softmax forward over all {w.T} rows ({pairs} visible pairs)"}
+
+
+def main():
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); the hot path "
+              f"needs no communication and shards per head; no multi-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        _copy_calibration()
+        return
+    import io_aware_attention_head_amd.scfa as scfa
+    from io_aware_attention_head_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    if w.mode != "hash" or w.grad:
+        raise SystemExit("bench.py times the hash-sparse forward workload")
+    dev = torch.device("cuda:0")
+    x_cpu = make_inputs(w)
+    x = {k: v.to(dev) for k, v in x_cpu.items()}
+    dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    plan = scfa.Plan("hash", w.B, w.H, w.T, w.D, dtype, nb=w.nb)
+    dense = scfa.Plan("dense", w.B, w.H, w.T, w.D, dtype)
+
+    # warm-up (also builds the operands the dense twin uses)
+    for _ in range(max(1, args.warmup)):
+        plan.run(x)
+        dense.run(x)
+    torch.cuda.synchronize()
+    pairs = int(plan.count_visible().sum().item())
+    dense_pairs = int(dense.count_visible().sum().item())
+    tiles = int(plan.tab.tiles.sum().item())
+    dense_tiles = int(dense.tab.tiles.sum().item())
+    assert int(plan.dev_err.item()) == 0, "device error flag set"
+    assert torch.isfinite(plan.O).all().item(), "non-finite output"
+    assert pairs > 0
+
+    stages = ["bucket", "sort", "gather", "tables", "forward"]
+    fns = {"bucket": lambda: plan.bucket(x["q"], x["k"], x["R"]), "sort": plan.sort,
+           "gather": lambda: plan.gather(x["q"], x["k"], x["v"]), "tables": plan.tables, "forward": plan.forward}
+    if args.fwd_only:
+        stages = ["forward"]
+    K = args.steps
+    ev = {s: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+          for s in stages}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    # ---- timed region --------------------------------------------------------
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        for s in stages:
+            ev[s][i][0].record()
+            fns[s]()
+            ev[s][i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / K
+    stage_ms = {s: sum(a.elapsed_time(b) for a, b in ev[s]) / K for s in stages}
+
+    # ---- dense-causal twin: same kernel, same shape, positions 0..T-1 ------
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for a, b in dev_ev:
+        a.record()
+        dense.forward()
+        b.record()
+    torch.cuda.synchronize()
+    dense_fwd_ms = sum(a.elapsed_time(b) for a, b in dev_ev) / K
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(K):
+        dense.gather(x["q"], x["k"], x["v"])
+        dense.tables()
+        dense.forward()
+    d1.record()
+    torch.cuda.synchronize()
+    dense_step_ms = d0.elapsed_time(d1) / K
+
+    fwd_ms = stage_ms["forward"]
+    flops = 4 * w.D * pairs
+    fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
+    step_tflops = flops / (ms_step * 1e-3) / 1e12
+    nQt, nKt = plan.Tpad // scfa.SCFA_TILE_M, plan.Tpad // scfa.SCFA_TILE_N
+    esz = 2 if dtype == torch.bfloat16 else 4
+    out_esz = 4
+    BHT = w.B * w.H * w.T
+    # algorithmic bytes: each stage reads its inputs once and writes its outputs once
+    alg_bytes = {
+        "bucket": 2 * BHT * w.D * esz + 2 * BHT * 4,
+        "sort": 2 * (BHT * 4 + 2 * BHT * 4),
+        "gather": 3 * 2 * BHT * w.D * esz + 3 * BHT * 4,
+        "forward": 3 * BHT * w.D * esz + BHT * w.D * out_esz + BHT * 4,
+    }
+    prep_gbs = {s: alg_bytes[s] / (stage_ms[s] * 1e-3) / 1e9 for s in ("bucket", "sort", "gather") if s in stage_ms}
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            t = json.load(open(TRAFFIC_FILE))
+            if t.get("fwd_source_sha256_16") == _src_hash(FWD_SOURCE):
+                traffic = t.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    props = torch.cuda.get_device_properties(dev)
+    out = {
+        "metric": "visible-pair TFLOP/s + % bf16 MFMA peak + speedup vs dense causal, T=8k/16k",
+        "value": round(step_tflops, 3),
+        "unit": "visible-pair TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dtype == torch.bfloat16 else "f32",
+        "data": "synthetic: seeded N(0,1) Q/K/V and rotations (no dataset needed)",
+        "config": {"workload": w.name, "mode": "hash", "B": w.B, "H": w.H, "T": w.T, "D": w.D, "nb": w.nb,
+                   "seed": w.seed, "out_dtype": "f32", "tile_m": scfa.SCFA_TILE_M, "tile_n": scfa.SCFA_TILE_N,
+                   "parallelism": "single GPU"},
+        "step": "LSH bucket + stable sort + gathers + range tables + attention forward (inputs resident in HBM)",
+        "visible_pairs": pairs,
+        "fwd_kernel_ms": round(fwd_ms, 5),
+        "fwd_kernel_tflops": round(fwd_tflops, 2),
+        "pct_bf16_peak_fwd": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "dense_causal_fwd_ms": round(dense_fwd_ms, 5),
+        "dense_causal_fwd_tflops": round(4 * w.D * dense_pairs / (dense_fwd_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense_causal_fwd": round(dense_fwd_ms / fwd_ms, 3),
+        "dense_causal_step_ms": round(dense_step_ms, 5),
+        "speedup_vs_dense_causal_step": round(dense_step_ms / ms_step, 3),
+        "stage_ms": {s: round(v, 5) for s, v in stage_ms.items()},
+        "preproc_gbs": {s: round(v, 1) for s, v in prep_gbs.items()},
+        "tiles_processed": tiles,
+        "tiles_total": nQt * nKt * w.B * w.H,
+        "tiles_skipped_frac": round(1 - tiles / (nQt * nKt * w.B * w.H), 4),
+        "dense_tiles_processed": dense_tiles,
+        "visible_density": round(pairs / (tiles * scfa.SCFA_TILE_M * scfa.SCFA_TILE_N), 4),
+        "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "k_fwd<hash,bf16>", "alg_flops_per_launch": flops,
+                     "alg_bytes_per_launch": alg_bytes["forward"]},
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "torch": torch.__version__, "hip": torch.version.hip},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(w, x_cpu)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,6 +14,12 @@ LIB = os.path.join(PKG, "libscfa.so")
 
 SOURCES = ["scfa_preprocess.hip", "scfa_fwd.hip", "scfa_bwd.hip"]
 
+# Attention kernels: MFMA accumulators in VGPRs (no AGPR copies for the
+# softmax), and no NaN canonicalisation around max (infinities are still
+# honoured: masked scores are -inf).
+ATTN_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]
+PER_FILE_FLAGS = {"scfa_fwd.hip": ATTN_FLAGS, "scfa_bwd.hip": ATTN_FLAGS}
+
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 VALU ops anywhere in the device code
@@ -40,7 +46,8 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in srcs]
-    cmds = [[_hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(srcs, objs)]
+    cmds = [[_hipcc(), *HIPCC_FLAGS, *PER_FILE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(srcs, objs)]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         outs = list(ex.map(_run, cmds))
     if verbose:

@@ -40,6 +40,7 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = SCFA_TILE_M;  // 128 query rows per workgroup
 constexpr int BN = SCFA_TILE_N;  // 64 keys per tile
@@ -119,14 +120,75 @@ struct Tr<true> {  // fp32
   static constexpr int NBUF = 1;
 };
 
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+// Calls f(IntC<0>), ..., f(IntC<N-1>): compile-time indices for register arrays.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<0, N>(f);
+}
+
+// Registers holding the next key tile while the current one is computed.
+template <int LOADS>
+struct TileRegs {
+  u32x4 k[LOADS];
+  u32x4 v[LOADS];
+  int idx;
+};
+
+// Global -> registers: the K tile (64 contiguous rows) and the V^T tile
+// (64 d-rows of 64 keys), 16 bytes per load, plus the tile's key positions
+// (threads 0..63) and buckets (threads 64..127).
+template <bool HASH, int ESZ, int CH, int LOADS>
+__device__ __forceinline__ void tile_load(TileRegs<LOADS>& r, const uint8_t* kg, const uint8_t* vg, const int32_t* kig,
+                                          const int32_t* kbg, int Tpad, int j, int tid) {
+  constexpr int TILE_BYTES = BN * HD * ESZ;
+  static_for<LOADS>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    const int u = tid + 256 * i;
+    r.k[i] = reinterpret_cast<const u32x4*>(kg + static_cast<size_t>(j) * TILE_BYTES)[u];
+    const int d = u / CH, ch = u - d * CH;
+    r.v[i] = *reinterpret_cast<const u32x4*>(vg + (static_cast<size_t>(d) * Tpad + j * BN) * ESZ + ch * 16);
+  });
+  if (tid < BN) r.idx = kig[j * BN + tid];
+  else if (HASH && tid < 2 * BN) r.idx = kbg[j * BN + tid - BN];
+}
+
+// Registers -> LDS with 16-byte XOR swizzles (K rows: swz_k, V^T rows: d & 7).
+template <bool HASH, int ESZ, int CH, int LOADS>
+__device__ __forceinline__ void tile_store(const TileRegs<LOADS>& r, uint8_t* ks, uint8_t* vs, int32_t* kp, int32_t* kb,
+                                           int tid) {
+  static_for<LOADS>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    const int u = tid + 256 * i;
+    const int row = u / CH, ch = u - row * CH;
+    *reinterpret_cast<u32x4*>(ks + row * HD * ESZ + ((ch ^ swz_k(row)) * 16)) = r.k[i];
+    *reinterpret_cast<u32x4*>(vs + row * BN * ESZ + ((ch ^ (row & 7)) * 16)) = r.v[i];
+  });
+  if (tid < BN) kp[tid] = r.idx;
+  else if (HASH && tid < 2 * BN) kb[tid - BN] = r.idx;
+}
+
 template <bool HASH, bool F32, bool ZERO_DROPPED, typename TOUT>
 __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
   using TR = Tr<F32>;
   constexpr int ESZ = TR::ESZ, CH = TR::CH, NBUF = TR::NBUF;
   constexpr int TILE_BYTES = BN * HD * ESZ;        // K tile and V^T tile, bytes each
   constexpr int LOADS = TILE_BYTES / 16 / 256;     // 16-byte loads per thread per tile
-  __shared__ __align__(16) uint8_t Ks[NBUF][TILE_BYTES];
-  __shared__ __align__(16) uint8_t Vs[NBUF][TILE_BYTES];
+  // K and V^T tiles; after the loop the same bytes stage the output tile.
+  __shared__ __align__(16) uint8_t smem[2 * NBUF * TILE_BYTES];
+  uint8_t(*Ks)[TILE_BYTES] = reinterpret_cast<uint8_t(*)[TILE_BYTES]>(smem);
+  uint8_t(*Vs)[TILE_BYTES] = reinterpret_cast<uint8_t(*)[TILE_BYTES]>(smem + NBUF * TILE_BYTES);
+  static_assert(2 * NBUF * TILE_BYTES >= BM * HD * sizeof(TOUT), "output staging does not fit");
   __shared__ __align__(16) int32_t Kp[NBUF][BN];
   __shared__ __align__(16) int32_t Kb[NBUF][BN];
   __shared__ int32_t Qi[BM];
@@ -153,6 +215,7 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
   const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
+  if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];  // visible after the first barrier
 
   // ---- queries of this wave: B operand, positions, buckets --------------
   const int q0 = qt * BM + w * 32;
@@ -197,46 +260,25 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
   // ---- tile pipeline ------------------------------------------------------
   const uint8_t* kg = static_cast<const uint8_t*>(p.k) + rowbase * HD * ESZ;
   const uint8_t* vg = static_cast<const uint8_t*>(p.vt) + static_cast<size_t>(bh) * HD * p.Tpad * ESZ;
-  uint4 kr[LOADS], vr[LOADS];
-  int kpr = 0;
+  const int32_t* kig = p.k_idx + rowbase;
+  const int32_t* kbg = HASH ? p.k_bkt + rowbase : nullptr;
+  TileRegs<LOADS> tr;
 
   auto next_tile = [&](int j) {
     while (j < rng.y && kst[j].x > qs.y) ++j;  // causal extremum test (hash ranges)
     return j;
   };
-  auto load_regs = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int u = tid + 256 * i;
-      kr[i] = reinterpret_cast<const uint4*>(kg + static_cast<size_t>(j) * TILE_BYTES)[u];
-      const int d = u / CH, ch = u - d * CH;
-      vr[i] = *reinterpret_cast<const uint4*>(vg + (static_cast<size_t>(d) * p.Tpad + j * BN) * ESZ + ch * 16);
-    }
-    if (tid < BN) kpr = p.k_idx[rowbase + j * BN + tid];
-    else if (HASH && tid < 2 * BN) kpr = p.k_bkt[rowbase + j * BN + tid - BN];
-  };
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int u = tid + 256 * i;
-      const int row = u / CH, ch = u - row * CH;
-      *reinterpret_cast<uint4*>(&Ks[buf][row * HD * ESZ + ((ch ^ swz_k(row)) * 16)]) = kr[i];
-      *reinterpret_cast<uint4*>(&Vs[buf][row * BN * ESZ + ((ch ^ (row & 7)) * 16)]) = vr[i];
-    }
-    if (tid < BN) Kp[buf][tid] = kpr;
-    else if (HASH && tid < 2 * BN) Kb[buf][tid - BN] = kpr;
-  };
 
   int j = next_tile(rng.x);
   if (j < rng.y) {
-    load_regs(j);
-    store_lds(0);
+    tile_load<HASH, ESZ, CH, LOADS>(tr, kg, vg, kig, kbg, p.Tpad, j, tid);
+    tile_store<HASH, ESZ, CH, LOADS>(tr, Ks[0], Vs[0], Kp[0], Kb[0], tid);
   }
   __syncthreads();
   int buf = 0;
   while (j < rng.y) {
     const int jn = next_tile(j + 1);
-    if (jn < rng.y) load_regs(jn);
+    if (jn < rng.y) tile_load<HASH, ESZ, CH, LOADS>(tr, kg, vg, kig, kbg, p.Tpad, jn, tid);
 
     // -- S^T = K Q^T --------------------------------------------------------
     f32x4 S[4][2];
@@ -298,10 +340,11 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
     // -- online softmax (base 2, scale folded into the exponent) -----------
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
+      float mx = fmaxf(S[0][qb][0], S[0][qb][1]);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        mx = fmaxf(fmaxf(mx, fmaxf(S[kb][qb][0], S[kb][qb][1])), fmaxf(S[kb][qb][2], S[kb][qb][3]));
+#pragma unroll
+        for (int e = (kb == 0 ? 2 : 0); e < 4; e += 2) mx = fmaxf(mx, fmaxf(S[kb][qb][e], S[kb][qb][e + 1]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mnew = fmaxf(m[qb], mx * p.c);
@@ -318,8 +361,10 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
           ls += pv;
         }
       l[qb] = l[qb] * alpha + ls;
+      if (__ballot(alpha != 1.f)) {  // the running max moved for some query of this wave
 #pragma unroll
-      for (int db = 0; db < 4; ++db) Oacc[db][qb] *= alpha;
+        for (int db = 0; db < 4; ++db) Oacc[db][qb] *= alpha;
+      }
     }
 
     // -- O^T += V^T P^T -----------------------------------------------------
@@ -359,19 +404,21 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
     }
 
     if constexpr (NBUF == 2) {
-      if (jn < rng.y) store_lds(buf ^ 1);
+      if (jn < rng.y) tile_store<HASH, ESZ, CH, LOADS>(tr, Ks[buf ^ 1], Vs[buf ^ 1], Kp[buf ^ 1], Kb[buf ^ 1], tid);
       __syncthreads();
       buf ^= 1;
     } else {
       __syncthreads();
-      if (jn < rng.y) store_lds(0);
+      if (jn < rng.y) tile_store<HASH, ESZ, CH, LOADS>(tr, Ks[0], Vs[0], Kp[0], Kb[0], tid);
       __syncthreads();
     }
     j = jn;
   }
 
-  // ---- epilogue: normalise, scatter to original positions ----------------
-  TOUT* O = static_cast<TOUT*>(p.O);
+  // ---- epilogue: normalise, stage the tile in LDS, write whole rows --------
+  // Output units of 4 elements (16 B fp32 / 8 B bf16), 16 per row, XOR
+  // swizzled by row so the column-wise staging writes are conflict-free.
+  TOUT* ost = reinterpret_cast<TOUT*>(smem);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     float lt = l[qb] + __shfl_xor(l[qb], 16);
@@ -379,12 +426,25 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float muse = (m[qb] == -INFINITY) ? 0.f : m[qb];
     const float lse = lt > 0.f ? (muse + log2f(lt)) * kLn2 : -INFINITY;
+    const int row = w * 32 + qb * 16 + r16;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) store4<TOUT>(ost + row * HD + (((4 * db + g) ^ (row & 15)) * 4), Oacc[db][qb] * inv);
     const int qp = qpos[qb];
+    if (g == 0 && qp >= 0 && qp < p.T) p.lse[static_cast<size_t>(bh) * p.T + qp] = lse;
+  }
+  __syncthreads();
+  TOUT* O = static_cast<TOUT*>(p.O);
+#pragma unroll
+  for (int it = 0; it < BM / 16; ++it) {
+    const int row = it * 16 + (tid >> 4), u = tid & 15;
+    const int qp = Qi[row];
     if (qp >= 0 && qp < p.T) {
       TOUT* orow = O + ((static_cast<size_t>(b) * p.T + qp) * p.H + h) * HD;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) store4<TOUT>(orow + db * 16 + 4 * g, Oacc[db][qb] * inv);
-      if (g == 0) p.lse[static_cast<size_t>(bh) * p.T + qp] = lse;
+      const TOUT* src = ost + row * HD + ((u ^ (row & 15)) * 4);
+      if constexpr (sizeof(TOUT) == 4)
+        *reinterpret_cast<uint4*>(orow + u * 4) = *reinterpret_cast<const uint4*>(src);
+      else
+        *reinterpret_cast<uint2*>(orow + u * 4) = *reinterpret_cast<const uint2*>(src);
     }
   }
 
@@ -395,7 +455,6 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
   // the whole sequence). Positions in that range that are not among the
   // tile's queries were dropped: O = 0, LSE = -inf.
   if constexpr (ZERO_DROPPED) {
-    if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];
     const int nreal = __syncthreads_count(tid < BM && Qi[tid] >= 0);
     int lo = 0, hi = -1;
     if (nreal > 0) {

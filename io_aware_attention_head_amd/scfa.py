@@ -361,3 +361,127 @@ def hash_sparse_attention(q, k, v, R, nb, out_dtype=torch.float32, scale=None):
 def dense_causal_attention(q, k, v, out_dtype=torch.float32, scale=None):
     pre = prepare_dense(q, k, v)
     return forward(pre, build_tables(pre), out_dtype, scale)
+
+
+# ---------------------------------------------------------------------------
+# Plans: every buffer allocated once, run() only launches kernels (no host
+# synchronisation, no allocation), so a plan can be timed or graph-captured.
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """Preallocated pipeline for one shape and mode.
+
+    mode "hash": bucket -> sort -> gathers -> tables -> forward.
+    mode "qk":   count -> compact -> gather -> tables -> forward, with a fixed
+                 compacted length Tc (default: pad_rows(T), which always fits).
+    mode "dense": gathers -> tables -> forward on positions 0..T-1.
+    Each stage is a separate method so it can be timed on its own.
+    """
+
+    def __init__(self, mode, B, H, T, D=64, dtype=torch.bfloat16, nb=16, Tc=None, out_dtype=torch.float32,
+                 device="cuda", scale=None):
+        if mode not in MODE_IDS:
+            raise ScfaError(f"unknown mode {mode}")
+        self.mode, self.B, self.H, self.T, self.D, self.nb = mode, B, H, T, D, nb
+        self.dtype, self.out_dtype = dtype, out_dtype
+        self.scale = 1.0 / math.sqrt(D) if scale is None else scale
+        d = torch.device(device)
+        i32 = torch.int32
+        e = lambda shape, dt=i32: torch.empty(shape, dtype=dt, device=d)  # noqa: E731
+        if mode == "qk":
+            self.Tpad = Tc if Tc is not None else pad_rows(T)
+            if self.Tpad % SCFA_ROW_ALIGN:
+                raise ScfaError("Tc must be a multiple of 128")
+            self.Tq = self.Tpad
+            nC = (T + SCFA_COUNT_CHUNK - 1) // SCFA_COUNT_CHUNK
+            self.cnt = [e((B, H)), e((B, H))]
+            self.mx = [e((1,)), e((1,))]
+            self.choff = [e((B, H, nC)), e((B, H, nC))]
+        else:
+            self.Tpad = pad_rows(T)
+            self.Tq = T if mode == "hash" else self.Tpad
+        Tp = self.Tpad
+        self.q_s, self.k_s = e((B, H, Tp, D), dtype), e((B, H, Tp, D), dtype)
+        self.v_t = e((B, H, D, Tp), dtype)
+        self.q_idx, self.k_idx = e((B, H, Tp)), e((B, H, Tp))
+        self.q_bkt = self.k_bkt = None
+        self.dev_err = torch.zeros((1,), dtype=i32, device=d)
+        if mode == "hash":
+            self.bq, self.bk = e((B, H, T)), e((B, H, T))
+            self.q_bkt, self.k_bkt = e((B, H, Tp)), e((B, H, Tp))
+            self.offq, self.offk = e((B, H, nb + 1)), e((B, H, nb + 1))
+            self.ws = e((max(1, scfa_hash_sort_workspace_bytes(B, H, T, nb)),), torch.uint8)
+        if mode == "dense":
+            ar = torch.arange(Tp, dtype=i32, device=d)
+            self.q_idx.copy_(torch.where(ar < T, ar, torch.full_like(ar, SCFA_Q_PAD)).expand(B, H, Tp))
+            self.k_idx.copy_(torch.where(ar < T, ar, torch.full_like(ar, SCFA_K_PAD)).expand(B, H, Tp))
+        Bm, Bn = SCFA_TILE_M, SCFA_TILE_N
+        nQt, nKt = Tp // Bm, Tp // Bn
+        self.tab = Tables(e((B, H, nQt, 4)), e((B, H, nKt, 4)), e((B, H, nQt, 2)), e((B, H, nKt, 2)), e((B, H)), Bm, Bn)
+        self.O = e((B, T, H, D), out_dtype)
+        self.lse = e((B, H, T), torch.float32)
+        self.pairs = e((B, H), torch.int64)
+
+    # -- stages ---------------------------------------------------------------
+    def bucket(self, q, k, R, stream=None):
+        scfa_hash_bucket(q, R, self.nb, self.bq, stream)
+        scfa_hash_bucket(k, R, self.nb, self.bk, stream)
+
+    def sort(self, stream=None):
+        scfa_hash_sort(self.bq, self.nb, SCFA_Q_PAD, self.q_idx, self.q_bkt, self.offq, self.ws, self.dev_err, stream)
+        scfa_hash_sort(self.bk, self.nb, SCFA_K_PAD, self.k_idx, self.k_bkt, self.offk, self.ws, self.dev_err, stream)
+
+    def compact(self, q, k, keep_q, keep_k, stream=None):
+        scfa_qk_count(keep_q, self.cnt[0], self.mx[0], self.choff[0], stream)
+        scfa_qk_count(keep_k, self.cnt[1], self.mx[1], self.choff[1], stream)
+        scfa_qk_compact(q, keep_q, self.cnt[0], self.choff[0], self.Tpad, SCFA_Q_PAD, self.q_s, self.q_idx,
+                        self.dev_err, stream)
+        scfa_qk_compact(k, keep_k, self.cnt[1], self.choff[1], self.Tpad, SCFA_K_PAD, self.k_s, self.k_idx,
+                        self.dev_err, stream)
+
+    def gather(self, q, k, v, stream=None):
+        if self.mode != "qk":
+            scfa_gather(q, self.q_idx, SCFA_ROWS, self.q_s, stream)
+            scfa_gather(k, self.k_idx, SCFA_ROWS, self.k_s, stream)
+        scfa_gather(v, self.k_idx, SCFA_COLS, self.v_t, stream)
+
+    def tables(self, stream=None):
+        mode = SCFA_HASH if self.mode == "hash" else SCFA_QK
+        t = self.tab
+        scfa_range_table(mode, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H, self.Tq, self.Tq, t.Bm,
+                         t.Bn, t.qstats, t.kstats, t.fwd, t.bwd, t.tiles, stream)
+
+    def forward(self, stream=None):
+        t = self.tab
+        if self.mode == "hash":
+            scfa_hash_sparse_fwd(self.q_s, self.k_s, self.v_t, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, t.qstats,
+                                 t.kstats, t.fwd, self.T, self.O, self.lse, self.scale, stream)
+        else:
+            scfa_qk_sparse_fwd(self.q_s, self.k_s, self.v_t, self.q_idx, self.k_idx, t.qstats, t.kstats, t.fwd, self.T,
+                               self.O, self.lse, self.scale, stream)
+
+    def count_visible(self, stream=None):
+        mode = SCFA_HASH if self.mode == "hash" else SCFA_QK
+        scfa_count_visible(mode, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H, self.Tq, self.Tq,
+                           self.pairs, stream)
+        return self.pairs
+
+    def prepare(self, x: dict, stream=None):
+        """All preprocessing stages for inputs x (q, k, v, keep_q, keep_k, R)."""
+        if self.mode == "hash":
+            self.bucket(x["q"], x["k"], x["R"], stream)
+            self.sort(stream)
+        elif self.mode == "qk":
+            self.compact(x["q"], x["k"], x["keep_q"], x["keep_k"], stream)
+        self.gather(x["q"], x["k"], x["v"], stream)
+        self.tables(stream)
+
+    def run(self, x: dict, stream=None):
+        """Whole forward path: preprocessing, tables, attention."""
+        self.prepare(x, stream)
+        self.forward(stream)
+        return self.O, self.lse
+
+    def prepared(self) -> Prepared:
+        return Prepared(self.mode, self.B, self.H, self.T, self.D, self.Tq, self.Tpad, self.q_s, self.k_s, self.v_t,
+                        self.q_idx, self.k_idx, self.q_bkt, self.k_bkt)
