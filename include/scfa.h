@@ -225,6 +225,39 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
                          const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, int B, int H,
                          int T, int D, float scale, void* O, float* lse, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Backward attention (recomputation from the saved LSE).
+ * SCFA explainer, 3.4 "Backward Pass Design": score tiles are recomputed
+ * with the same index-guided tile ranges and local masks (queries and keys
+ * swapped for dK/dV), and the same -inf guard as the forward: a query with
+ * LSE = -inf contributes nothing. With P = exp(scale q.k - LSE) on visible
+ * pairs: dV = P^T dO, dS = P (dO V^T - rowsum(dO * O)), dQ = scale dS K,
+ * dK = scale dS^T Q. Keep masks and buckets are constants.
+ *
+ *  mode          SCFA_QK (also dense: QK rule on positions 0..T-1) or
+ *                SCFA_HASH.
+ *  dtype_in      SCFA_BF16 (the only backward build; fp32 returns
+ *                SCFA_ERR_UNSUPPORTED).
+ *  q, k, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab
+ *                exactly the operands and tables of the forward call.
+ *  O             (B, T, H, D) fp32 forward output;  lse (B, H, T) fp32.
+ *  dO            (B, T, H, D) upstream gradient, dtype_in.
+ *  T             original sequence length; Tq valid rows (Tc for QK,
+ *                T for hash).
+ *  dQ, dK, dV    out (B, T, H, D) fp32 in original order, every row
+ *                written (zero for dropped tokens and tokens without any
+ *                visible pair).
+ *  workspace     device scratch of scfa_bwd_workspace_bytes() bytes (the
+ *                transposed / re-laid-out operands, Delta and log2 LSE).
+ * Launches 7 kernels on `stream`; no atomics, results are deterministic.  */
+size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int D);
+
+int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v_t, const int32_t* q_idx,
+             const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
+             const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
+             const void* dO, int B, int H, int T, int Tq, int D, float scale, float* dQ, float* dK, float* dV,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,14 +33,10 @@
 
 #include <math.h>
 
-#include "scfa_internal.h"
+#include "scfa_mfma.h"
 
 namespace scfa {
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = SCFA_TILE_M;  // 128 query rows per workgroup
 constexpr int BN = SCFA_TILE_N;  // 64 keys per tile
@@ -66,25 +62,6 @@ struct FwdParams {
   int nQt, nKt;
   float c;  // scale * log2(e)
 };
-
-// Key row of MFMA A-operand row r (0..15) for 16-key block kb of a 64-key
-// tile: blocks 2kc and 2kc+1 interleave in groups of 4 so that accumulator
-// element e of lane group g in block kb is key 32kc + 8g + 4(kb&1) + e.
-__device__ inline int key_row(int kb, int r) { return 32 * (kb >> 1) + 8 * (r >> 2) + 4 * (kb & 1) + (r & 3); }
-__device__ inline int swz_k(int row) { return (row & 3) | ((row >> 1) & 4); }
-
-__device__ inline bf16x8 pack_bf16x8(const f32x4& a, const f32x4& b) {
-  bf16x8 r;
-  r[0] = static_cast<__bf16>(a[0]);
-  r[1] = static_cast<__bf16>(a[1]);
-  r[2] = static_cast<__bf16>(a[2]);
-  r[3] = static_cast<__bf16>(a[3]);
-  r[4] = static_cast<__bf16>(b[0]);
-  r[5] = static_cast<__bf16>(b[1]);
-  r[6] = static_cast<__bf16>(b[2]);
-  r[7] = static_cast<__bf16>(b[3]);
-  return r;
-}
 
 template <typename TOUT>
 __device__ inline void store4(TOUT* p, const f32x4& v);
@@ -119,23 +96,6 @@ struct Tr<true> {  // fp32
   static constexpr int CH = HD * ESZ / 16;  // 16
   static constexpr int NBUF = 1;
 };
-
-template <int N>
-struct IntC {
-  static constexpr int value = N;
-};
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for_impl(F&& f) {
-  if constexpr (I < N) {
-    f(IntC<I>{});
-    static_for_impl<I + 1, N>(f);
-  }
-}
-// Calls f(IntC<0>), ..., f(IntC<N-1>): compile-time indices for register arrays.
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl<0, N>(f);
-}
 
 // Registers holding the next key tile while the current one is computed.
 template <int LOADS>

@@ -53,8 +53,8 @@ _SIGS = {
     "scfa_hash_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp,
                                   _vp, _vp]),
     "scfa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
-    "scfa_bwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
-                      _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "scfa_bwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                      _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 _LIB = None
@@ -199,6 +199,20 @@ def scfa_hash_sparse_fwd(q_s, k_s, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, ksta
     _check(lib().scfa_hash_sparse_fwd(_dt(q_s), _dt(O), _p(q_s), _p(k_s), _p(v_t), _p(q_idx), _p(k_idx), _p(q_bkt),
                                       _p(k_bkt), _p(qstats), _p(kstats), _p(fwd_tab), B, H, T, D, scale, _p(O),
                                       _p(lse), _stream(stream, q_s)), "scfa_hash_sparse_fwd")
+
+
+def scfa_bwd_workspace_bytes(mode, B, H, Tq, D=64) -> int:
+    return lib().scfa_bwd_workspace_bytes(mode, B, H, Tq, D)
+
+
+def scfa_bwd(mode, q, k, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, T, Tq, dQ, dK,
+             dV, workspace, scale=None, stream=None):
+    B, H, Tp, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(lib().scfa_bwd(mode, _dt(q), _p(q), _p(k), _p(v_t), _p(q_idx), _p(k_idx), _p(q_bkt), _p(k_bkt), _p(qstats),
+                          _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(O), _p(lse), _p(dO), B, H, T, Tq, D, scale, _p(dQ),
+                          _p(dK), _p(dV), _p(workspace), workspace.numel() * workspace.element_size(),
+                          _stream(stream, q)), "scfa_bwd")
 
 
 # ---------------------------------------------------------------------------
@@ -348,6 +362,20 @@ def forward(pre: Prepared, tab: Tables, out_dtype=torch.float32, scale=None, O=N
     return O, lse
 
 
+def backward(pre: Prepared, tab: Tables, O, lse, dO, scale=None, grads=None, workspace=None, stream=None):
+    """Gradients w.r.t. the original-order q, k, v (fp32, (B,T,H,D))."""
+    B, H, T, D = pre.B, pre.H, pre.T, pre.D
+    mode = SCFA_HASH if pre.mode == "hash" else SCFA_QK
+    if grads is None:
+        grads = tuple(_empty((B, T, H, D), torch.float32, pre.q) for _ in range(3))
+    if workspace is None:
+        workspace = _empty((scfa_bwd_workspace_bytes(mode, B, H, pre.Tq, D),), torch.uint8, pre.q)
+    dQ, dK, dV = grads
+    scfa_bwd(mode, pre.q, pre.k, pre.v_t, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats, tab.fwd,
+             tab.bwd, O, lse, dO, T, pre.Tq, dQ, dK, dV, workspace, scale, stream)
+    return dQ, dK, dV
+
+
 def qk_sparse_attention(q, k, v, keep_q, keep_k, out_dtype=torch.float32, scale=None):
     pre = prepare_qk(q, k, v, keep_q, keep_k)
     return forward(pre, build_tables(pre), out_dtype, scale)
@@ -421,6 +449,8 @@ class Plan:
         self.O = e((B, T, H, D), out_dtype)
         self.lse = e((B, H, T), torch.float32)
         self.pairs = e((B, H), torch.int64)
+        self._grads = None
+        self._bws = None
 
     # -- stages ---------------------------------------------------------------
     def bucket(self, q, k, R, stream=None):
@@ -459,6 +489,19 @@ class Plan:
         else:
             scfa_qk_sparse_fwd(self.q_s, self.k_s, self.v_t, self.q_idx, self.k_idx, t.qstats, t.kstats, t.fwd, self.T,
                                self.O, self.lse, self.scale, stream)
+
+    def backward(self, dO, stream=None):
+        """Gradients of the last forward() w.r.t. q, k, v (fp32, original order)."""
+        if self._grads is None:
+            d = self.q_s.device
+            mode = SCFA_HASH if self.mode == "hash" else SCFA_QK
+            self._grads = tuple(torch.empty((self.B, self.T, self.H, self.D), dtype=torch.float32, device=d)
+                                for _ in range(3))
+            self._bws = torch.empty((scfa_bwd_workspace_bytes(mode, self.B, self.H, self.Tq, self.D),),
+                                    dtype=torch.uint8, device=d)
+        if self.out_dtype != torch.float32:
+            raise ScfaError("backward needs the fp32 forward output")
+        return backward(self.prepared(), self.tab, self.O, self.lse, dO, self.scale, self._grads, self._bws, stream)
 
     def count_visible(self, stream=None):
         mode = SCFA_HASH if self.mode == "hash" else SCFA_QK
