@@ -183,6 +183,23 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
                      const int32_t* k_bkt, int B, int H, int Tq, int Tk, int Bm, int Bn, int32_t* qstats,
                      int32_t* kstats, int32_t* fwd_tab, int32_t* bwd_tab, int32_t* tiles, hipStream_t stream);
 
+/* Launch order of the attention workgroups for one range table (the
+ * forward table for the forward and dQ kernels, the backward table for the
+ * dK/dV kernel): the B*H*ntiles items (item = (b*H + h)*ntiles + tile) sorted
+ * by range length (end - start), longest first, so that the longest tiles
+ * start first and the short ones fill the tail. When B*H is a multiple of 8
+ * the items are sorted within 8 groups of heads (head bh in group bh % 8)
+ * and interleaved, order[slot*8 + g]: workgroup x runs on XCD x % 8, so each
+ * XCD keeps to its own heads and their K/V tiles stay in its L2. Items of
+ * equal length come in an unspecified order.
+ *  tab     (B, H, ntiles, 2) [start, end) range table.
+ *  ntiles  >= 1, tiles per head the table describes.
+ *  span    1..16383, tiles per head its ranges index (key tiles for the
+ *          forward table, query tiles for the backward table); lengths
+ *          are clamped to [0, span].
+ *  order   out (B*H*ntiles) int32, a permutation of the items.             */
+int scfa_work_order(const int32_t* tab, int B, int H, int ntiles, int span, int32_t* order, hipStream_t stream);
+
 /* Exact number of visible (query, key) pairs per head, from the sorted /
  * compacted index arrays (a query row r < Tq with position p >= 0 sees the
  * key rows s < Tk with k_idx[s] <= p, and equal bucket in hash mode).
@@ -209,6 +226,9 @@ int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, con
  *  q_bkt, k_bkt  (B, H, Tpad) sorted bucket ids (hash only).
  *  qstats, kstats, fwd_tab   from scfa_range_table with Bm = SCFA_TILE_M,
  *                Bn = SCFA_TILE_N, same mode and arrays.
+ *  order         (B*H*nQt) launch order from scfa_work_order on fwd_tab, or
+ *                NULL (then query tiles run in descending index order). Any
+ *                permutation gives the same results; only the schedule moves.
  *  T             original sequence length (rows of O and LSE).
  *  Tc            QK: compacted length (multiple of 128); Tpad = Tc.
  *  scale         score scale, normally 1/sqrt(D).
@@ -217,13 +237,13 @@ int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, con
  *                written (-inf for rows without a visible key).           */
 int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v_t,
                        const int32_t* q_idx, const int32_t* k_idx, const int32_t* qstats, const int32_t* kstats,
-                       const int32_t* fwd_tab, int B, int H, int T, int Tc, int D, float scale, void* O,
-                       float* lse, hipStream_t stream);
+                       const int32_t* fwd_tab, const int32_t* order, int B, int H, int T, int Tc, int D, float scale,
+                       void* O, float* lse, hipStream_t stream);
 
 int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v_t,
                          const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
-                         const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, int B, int H,
-                         int T, int D, float scale, void* O, float* lse, hipStream_t stream);
+                         const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, const int32_t* order,
+                         int B, int H, int T, int D, float scale, void* O, float* lse, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Backward attention (recomputation from the saved LSE).

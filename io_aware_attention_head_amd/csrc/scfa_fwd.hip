@@ -54,6 +54,7 @@ struct FwdParams {
   const int4* qstats;
   const int4* kstats;
   const int2* fwd_tab;
+  const int32_t* order;  // launch order of (head, query tile) items, or null
   void* O;
   float* lse;
   int B, H, T;
@@ -159,7 +160,11 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
 
   // ---- work item: (head, query tile), longest first, XCD-aware ----------
   int qt, bh;
-  {
+  if (p.order) {
+    const int it = p.order[blockIdx.x];
+    bh = it / p.nQt;
+    qt = it - bh * p.nQt;
+  } else {
     const int x = blockIdx.x;
     if ((BH & 7) == 0) {
       const int hpx = BH >> 3, xcd = x & 7, slot = x >> 3;
@@ -185,6 +190,27 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
     const int row = q0 + qb * 16 + r16;
     qpos[qb] = p.q_idx[rowbase + row];
     qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
+  }
+  // extrema of this wave's real query rows (pad rows: position -1, their
+  // results are never stored): a key tile is skipped by the whole wave when
+  // it holds no pair visible to any of them, and unmasked when every pair is
+  // visible to all of them.
+  int wmin = kInt32Max, wmax = -1, wbmin = kInt32Max, wbmax = kInt32Min;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    if (qpos[qb] >= 0) {
+      wmin = min(wmin, qpos[qb]);
+      wmax = max(wmax, qpos[qb]);
+      wbmin = min(wbmin, qbkt[qb]);
+      wbmax = max(wbmax, qbkt[qb]);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    wmin = min(wmin, __shfl_xor(wmin, o));
+    wmax = max(wmax, __shfl_xor(wmax, o));
+    wbmin = min(wbmin, __shfl_xor(wbmin, o));
+    wbmax = max(wbmax, __shfl_xor(wbmax, o));
   }
   bf16x8 Qb[2][2];   // bf16: [qb][ds]
   float Qf[2][16];   // fp32: [qb][t], d = 16g + t
@@ -239,6 +265,9 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
   while (j < rng.y) {
     const int jn = next_tile(j + 1);
     if (jn < rng.y) tile_load<HASH, ESZ, CH, LOADS>(tr, kg, vg, kig, kbg, p.Tpad, jn, tid);
+    const int4 ks = kst[j];
+    const bool wave_empty = ks.x > wmax || (HASH && (ks.w < wbmin || ks.z > wbmax));
+    if (!wave_empty) {
 
     // -- S^T = K Q^T --------------------------------------------------------
     f32x4 S[4][2];
@@ -276,9 +305,8 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
     }
 
     // -- mask on tiles that are not fully visible ---------------------------
-    const int4 ks = kst[j];
-    bool full = ks.y <= qs.x && (j + 1) * BN <= p.Tk;
-    if (HASH) full = full && ks.z == ks.w && qs.z == qs.w && ks.z == qs.z;
+    bool full = ks.y <= wmin && (j + 1) * BN <= p.Tk;
+    if (HASH) full = full && ks.z == ks.w && wbmin == wbmax && ks.z == wbmin;
     if (!full) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -362,6 +390,8 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
         }
       }
     }
+
+    }  // !wave_empty
 
     if constexpr (NBUF == 2) {
       if (jn < rng.y) tile_store<HASH, ESZ, CH, LOADS>(tr, Ks[buf ^ 1], Vs[buf ^ 1], Kp[buf ^ 1], Kb[buf ^ 1], tid);
@@ -481,8 +511,8 @@ extern "C" {
 
 int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v_t,
                        const int32_t* q_idx, const int32_t* k_idx, const int32_t* qstats, const int32_t* kstats,
-                       const int32_t* fwd_tab, int B, int H, int T, int Tc, int D, float scale, void* O, float* lse,
-                       hipStream_t stream) {
+                       const int32_t* fwd_tab, const int32_t* order, int B, int H, int T, int Tc, int D, float scale,
+                       void* O, float* lse, hipStream_t stream) {
   if (!q || !k || !v_t || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !O || !lse) return SCFA_ERR_INVALID;
   const int st = check_common(dtype_in, dtype_out, B, H, T, D, scale);
   if (st != SCFA_OK) return st;
@@ -498,6 +528,7 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
   p.qstats = reinterpret_cast<const int4*>(qstats);
   p.kstats = reinterpret_cast<const int4*>(kstats);
   p.fwd_tab = reinterpret_cast<const int2*>(fwd_tab);
+  p.order = order;
   p.O = O;
   p.lse = lse;
   p.B = B;
@@ -513,8 +544,8 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
 
 int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v_t,
                          const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
-                         const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, int B, int H, int T,
-                         int D, float scale, void* O, float* lse, hipStream_t stream) {
+                         const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, const int32_t* order,
+                         int B, int H, int T, int D, float scale, void* O, float* lse, hipStream_t stream) {
   if (!q || !k || !v_t || !q_idx || !k_idx || !q_bkt || !k_bkt || !qstats || !kstats || !fwd_tab || !O || !lse)
     return SCFA_ERR_INVALID;
   const int st = check_common(dtype_in, dtype_out, B, H, T, D, scale);
@@ -531,6 +562,7 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
   p.qstats = reinterpret_cast<const int4*>(qstats);
   p.kstats = reinterpret_cast<const int4*>(kstats);
   p.fwd_tab = reinterpret_cast<const int2*>(fwd_tab);
+  p.order = order;
   p.O = O;
   p.lse = lse;
   p.B = B;

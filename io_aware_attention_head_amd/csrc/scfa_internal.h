@@ -13,6 +13,8 @@
 
 namespace scfa {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kWave = 64;
 constexpr int kInt32Max = 2147483647;
 constexpr int kInt32Min = -2147483647 - 1;

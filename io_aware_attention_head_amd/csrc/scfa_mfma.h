@@ -14,7 +14,6 @@ namespace scfa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 
 constexpr float kLog2e = 1.44269504088896340736f;

@@ -137,29 +137,34 @@ __global__ __launch_bounds__(256) void k_qk_compact(const uint8_t* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // LSH bucket. One thread per token, one workgroup per (256 tokens, head):
-// R of the head sits in LDS as float64. Products of a bf16/fp32 input and an
-// fp32 rotation are exact in float64, so the accumulation below rounds only
-// at the sums, in the order d = 0..63.
+// R of the head sits in LDS as float64 and is read as a wave-wide broadcast.
+// Each thread reads its token's row with 16-byte loads. A product of a
+// bf16/fp32 input and an fp32 rotation is exact in float64, so a fused
+// multiply-add rounds exactly where a separate multiply and add would (only
+// at the sum): the accumulation matches the sequential definition
+// c_j = ((0 + x_0 R_0j) + x_1 R_1j) + ... bit for bit.
 // ---------------------------------------------------------------------------
 
 template <typename TIN>
-__device__ inline float load_elem(const TIN* p, int i);
+__device__ inline float unit_elem(const u32x4& u, int e);
 
 template <>
-__device__ inline float load_elem<float>(const float* p, int i) {
-  return p[i];
+__device__ inline float unit_elem<float>(const u32x4& u, int e) {
+  return __uint_as_float(u[e]);
 }
 
 template <>
-__device__ inline float load_elem<uint16_t>(const uint16_t* p, int i) {
-  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+__device__ inline float unit_elem<uint16_t>(const u32x4& u, int e) {
+  const uint32_t w = u[e >> 1];
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
 template <typename TIN, int HALF>
 __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* __restrict__ x, const float* __restrict__ R, int T,
                                                      int H, int32_t* __restrict__ bucket) {
-#pragma clang fp contract(off)
   constexpr int D = 64;
+  constexpr int EPU = 16 / sizeof(TIN);  // elements per 16-byte unit
+  constexpr int NU = D / EPU;            // units per row
   __shared__ double Rs[D * HALF];
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
@@ -167,17 +172,21 @@ __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* __restrict__ x, 
   __syncthreads();
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
-  const TIN* row = x + ((static_cast<size_t>(b) * T + t) * H + h) * D;
+  const u32x4* row = reinterpret_cast<const u32x4*>(x + ((static_cast<size_t>(b) * T + t) * H + h) * D);
+  u32x4 u[NU];
+#pragma unroll
+  for (int i = 0; i < NU; ++i) u[i] = row[i];
   double c[HALF];
 #pragma unroll
   for (int j = 0; j < HALF; ++j) c[j] = 0.0;
-#pragma unroll 8
-  for (int d = 0; d < D; ++d) {
-    const double xd = static_cast<double>(load_elem<TIN>(row, d));
 #pragma unroll
-    for (int j = 0; j < HALF; ++j) {
-      const double prod = xd * Rs[d * HALF + j];
-      c[j] = c[j] + prod;
+  for (int i = 0; i < NU; ++i) {
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) {
+      const int d = i * EPU + e;
+      const double xd = static_cast<double>(unit_elem<TIN>(u[i], e));
+#pragma unroll
+      for (int j = 0; j < HALF; ++j) c[j] = fma(xd, Rs[d * HALF + j], c[j]);
     }
   }
   // argmax over [c ; -c], first index on ties: the positive half comes first.
@@ -192,11 +201,14 @@ __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* __restrict__ x, 
 }
 
 // ---------------------------------------------------------------------------
-// Stable counting sort by bucket: per-chunk histograms, per-head scan, then a
-// stable scatter whose in-chunk ranks come from wave64 ballots.
+// Stable counting sort by bucket: per-chunk histograms, then a scatter whose
+// workgroups each derive their own base from all chunk histograms of the
+// head (4 KB of L2 reads at nb = 16, 64 chunks) and whose in-chunk ranks
+// come from wave64 ballots.
 // ---------------------------------------------------------------------------
 
 constexpr int kSortChunk = 256;
+constexpr int kMaxOrderSpan = 16383;  // length bins of k_work_order fit in 64 KB of LDS
 
 __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ bucket, int T, int nb, int nC,
                                                    int32_t* __restrict__ hist, int32_t* dev_err) {
@@ -217,45 +229,61 @@ __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ b
   if (threadIdx.x < nb) hist[(static_cast<size_t>(bh) * nC + c) * nb + threadIdx.x] = hs[threadIdx.x];
 }
 
-// One wave per head: lane v owns bucket v. hist[c][v] becomes the sorted
-// position of the first chunk-c token of bucket v.
-__global__ __launch_bounds__(64) void k_sort_scan(int32_t* __restrict__ hist, int nb, int nC,
-                                                  int32_t* __restrict__ offsets) {
-  const int bh = blockIdx.x;
-  const int v = threadIdx.x;
-  int32_t* hp = hist + static_cast<size_t>(bh) * nC * nb;
-  int total = 0;
-  if (v < nb)
-    for (int c = 0; c < nC; ++c) total += hp[c * nb + v];
-  // exclusive scan of the totals over v
-  int x = total;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (v >= o) x += y;
-  }
-  const int off = x - total;
-  if (v < nb) {
-    offsets[static_cast<size_t>(bh) * (nb + 1) + v] = off;
-    int run = off;
-    for (int c = 0; c < nC; ++c) {
-      const int n = hp[c * nb + v];
-      hp[c * nb + v] = run;
-      run += n;
-    }
-  }
-  if (v == nb - 1) offsets[static_cast<size_t>(bh) * (nb + 1) + nb] = off + total;
-}
-
+// Workgroup (chunk c, head bh). base[v] = (tokens of the head with bucket
+// < v) + (tokens of bucket v in chunks before c); the chunk-0 workgroup also
+// writes offsets. Chunks at or beyond nC only write the pad entries.
 __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict__ bucket, int T, int Tp, int nb, int nC,
-                                                      const int32_t* __restrict__ base, int32_t pad,
-                                                      int32_t* __restrict__ perm, int32_t* __restrict__ bsorted) {
+                                                      const int32_t* __restrict__ hist, int32_t pad,
+                                                      int32_t* __restrict__ perm, int32_t* __restrict__ bsorted,
+                                                      int32_t* __restrict__ offsets) {
+  __shared__ int32_t part_tot[4][64];
+  __shared__ int32_t part_bef[4][64];
+  __shared__ int32_t base_s[64];
   __shared__ int32_t wcnt[4][64];
   const int c = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int32_t* pp = perm + static_cast<size_t>(bh) * Tp;
+  int32_t* bp = bsorted + static_cast<size_t>(bh) * Tp;
   const int t = c * kSortChunk + threadIdx.x;
-  for (int i = threadIdx.x; i < 4 * 64; i += 256) (&wcnt[0][0])[i] = 0;
+  if (c >= nC) {  // pad-only chunk: no token of this chunk exists
+    if (t >= T && t < Tp) {
+      pp[t] = pad;
+      bp[t] = -1;
+    }
+    return;
+  }
+  // per-bucket totals and the count before this chunk, lane = bucket
+  {
+    int tot = 0, bef = 0;
+    if (lane < nb) {
+      const int32_t* hp = hist + static_cast<size_t>(bh) * nC * nb + lane;
+      for (int cc = w; cc < nC; cc += 4) {
+        const int n = hp[static_cast<size_t>(cc) * nb];
+        tot += n;
+        bef += cc < c ? n : 0;
+      }
+    }
+    part_tot[w][lane] = tot;
+    part_bef[w][lane] = bef;
+    wcnt[w][lane] = 0;
+  }
   __syncthreads();
+  if (w == 0) {
+    const int tot = part_tot[0][lane] + part_tot[1][lane] + part_tot[2][lane] + part_tot[3][lane];
+    const int bef = part_bef[0][lane] + part_bef[1][lane] + part_bef[2][lane] + part_bef[3][lane];
+    int x = tot;  // inclusive scan over buckets
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    const int off = x - tot;
+    base_s[lane] = off + bef;
+    if (c == 0) {
+      if (lane < nb) offsets[static_cast<size_t>(bh) * (nb + 1) + lane] = off;
+      if (lane == 63) offsets[static_cast<size_t>(bh) * (nb + 1) + nb] = x;  // all tokens
+    }
+  }
   int v = -1;
   if (t < T) v = bucket[static_cast<size_t>(bh) * T + t];
   const bool valid = t < T && v >= 0 && v < nb;
@@ -271,10 +299,8 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
     remaining &= ~m;
   }
   __syncthreads();
-  int32_t* pp = perm + static_cast<size_t>(bh) * Tp;
-  int32_t* bp = bsorted + static_cast<size_t>(bh) * Tp;
-  if (valid && c < nC) {
-    int pos = base[(static_cast<size_t>(bh) * nC + c) * nb + v] + my_rank;
+  if (valid) {
+    int pos = base_s[v] + my_rank;
     for (int k = 0; k < w; ++k) pos += wcnt[k][v];
     pp[pos] = t;
     bp[pos] = v;
@@ -306,27 +332,46 @@ __global__ __launch_bounds__(256) void k_gather_rows(const uint8_t* __restrict__
   reinterpret_cast<uint4*>(out + (static_cast<size_t>(bh) * Tp + r) * D * ESZ)[kk] = val;
 }
 
-// 64 rows per workgroup staged in LDS, then written as D rows of 64 columns.
+// 64 rows per workgroup: read with 16-byte loads into an LDS tile, then
+// written as D rows of 64 consecutive columns (16-byte stores).
 template <typename E>
 __global__ __launch_bounds__(256) void k_gather_cols(const E* __restrict__ x, const int32_t* __restrict__ idx, int T,
                                                      int H, int Tp, E* __restrict__ out) {
   constexpr int D = 64;
-  constexpr int LD = D + (sizeof(E) == 2 ? 2 : 1);  // odd word stride: conflict-free column reads
-  __shared__ E tile[64 * LD];
+  constexpr int EPU = 16 / sizeof(E);  // elements per 16-byte unit
+  constexpr int UPR = D / EPU;         // units per input row
+  constexpr int LD = D + EPU;          // LDS row stride: 16-byte aligned, rows shifted by 4 banks
+  __shared__ __align__(16) E tile[64 * LD];
+  __shared__ int32_t src_s[64];
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
   const int r0 = blockIdx.x * 64;
-  for (int e = threadIdx.x; e < 64 * D; e += 256) {
-    const int rr = e / D, d = e - rr * D;
-    const int src = idx[static_cast<size_t>(bh) * Tp + r0 + rr];
-    E val = E(0);
-    if (src >= 0 && src < T) val = x[((static_cast<size_t>(b) * T + src) * H + h) * D + d];
-    tile[rr * LD + d] = val;
+  if (threadIdx.x < 64) src_s[threadIdx.x] = idx[static_cast<size_t>(bh) * Tp + r0 + threadIdx.x];
+  __syncthreads();
+  for (int u = threadIdx.x; u < 64 * UPR; u += 256) {
+    const int rr = u / UPR, k = u - rr * UPR;
+    const int src = src_s[rr];
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (src >= 0 && src < T)
+      val = *reinterpret_cast<const u32x4*>(x + ((static_cast<size_t>(b) * T + src) * H + h) * D + k * EPU);
+    *reinterpret_cast<u32x4*>(&tile[rr * LD + k * EPU]) = val;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < 64 * D; e += 256) {
-    const int d = e / 64, rr = e - d * 64;
-    out[(static_cast<size_t>(bh) * D + d) * Tp + r0 + rr] = tile[rr * LD + d];
+  constexpr int UPO = 64 / EPU;  // units per output row (64 columns)
+  for (int u = threadIdx.x; u < D * UPO; u += 256) {
+    const int d = u / UPO, k = u - d * UPO;
+    u32x4 val;
+    if constexpr (sizeof(E) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = tile[(k * 8 + 2 * e) * LD + d], hi = tile[(k * 8 + 2 * e + 1) * LD + d];
+        val[e] = lo | (hi << 16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = __float_as_uint(tile[(k * 4 + e) * LD + d]);
+    }
+    *reinterpret_cast<u32x4*>(out + (static_cast<size_t>(bh) * D + d) * Tp + r0 + k * EPU) = val;
   }
 }
 
@@ -384,52 +429,147 @@ __global__ __launch_bounds__(64) void k_tile_stats(int mode, const int32_t* __re
   }
 }
 
-__global__ __launch_bounds__(64) void k_fwd_table(int mode, const int32_t* __restrict__ qstats,
-                                                  const int32_t* __restrict__ kstats, int nQt, int nKt,
-                                                  int32_t* __restrict__ fwd, int32_t* __restrict__ tiles) {
+// One wave per query tile; lanes scan the key tiles 64 at a time.
+// QK / dense (Algorithm 1): end = number of key tiles whose smallest
+// position is <= the query tile's largest position (a prefix, since key
+// positions ascend). Hash (Algorithm 2): start = key tiles whose largest
+// bucket is below the query tile's smallest bucket; provisional stop = first
+// tile at/after start whose smallest bucket exceeds the query tile's largest;
+// end = one past the last tile in [start, stop) passing the causal test.
+__global__ __launch_bounds__(256) void k_fwd_table(int mode, const int32_t* __restrict__ qstats,
+                                                   const int32_t* __restrict__ kstats, int nQt, int nKt,
+                                                   int32_t* __restrict__ fwd, int32_t* __restrict__ tiles) {
   const int bh = blockIdx.y;
-  const int i = blockIdx.x * 64 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= nQt) return;
   const int4 qs = reinterpret_cast<const int4*>(qstats)[static_cast<size_t>(bh) * nQt + i];
   const int4* ks = reinterpret_cast<const int4*>(kstats) + static_cast<size_t>(bh) * nKt;
   int start = 0, end = 0, cnt = 0;
   if (mode != SCFA_HASH) {
-    for (int j = 0; j < nKt; ++j) cnt += ks[j].x <= qs.y;
+    for (int j0 = 0; j0 < nKt; j0 += 64) {
+      const int j = j0 + lane;
+      cnt += __popcll(__ballot(j < nKt && ks[j].x <= qs.y));
+    }
     end = cnt;
   } else {
-    for (int j = 0; j < nKt; ++j) start += ks[j].w < qs.z;
-    int eh = start;
-    while (eh < nKt && !(ks[eh].z > qs.w)) ++eh;
+    // start: tiles entirely below the query tile's smallest bucket
+    for (int j0 = 0; j0 < nKt; j0 += 64) {
+      const int j = j0 + lane;
+      start += __popcll(__ballot(j < nKt && ks[j].w < qs.z));
+    }
+    // provisional stop: first tile >= start with smallest bucket > largest query bucket
+    int eh = nKt;
+    for (int j0 = start & ~63; j0 < nKt; j0 += 64) {
+      const int j = j0 + lane;
+      const uint64_t m = __ballot(j >= start && j < nKt && ks[j].z > qs.w);
+      if (m) {
+        eh = j0 + __ffsll(static_cast<long long>(m)) - 1;
+        break;
+      }
+    }
+    // refined stop and processed count: tiles in [start, eh) passing the causal test
     end = start;
-    for (int j = start; j < eh; ++j) {
-      if (ks[j].x <= qs.y) {
-        end = j + 1;
-        ++cnt;
+    for (int j0 = start & ~63; j0 < eh; j0 += 64) {
+      const int j = j0 + lane;
+      const uint64_t m = __ballot(j >= start && j < eh && ks[j].x <= qs.y);
+      if (m) {
+        end = j0 + 64 - __clzll(static_cast<long long>(m));
+        cnt += __popcll(m);
       }
     }
   }
-  reinterpret_cast<int2*>(fwd)[static_cast<size_t>(bh) * nQt + i] = make_int2(start, end);
-  if (cnt) atomicAdd(&tiles[bh], cnt);
+  if (lane == 0) {
+    reinterpret_cast<int2*>(fwd)[static_cast<size_t>(bh) * nQt + i] = make_int2(start, end);
+    if (cnt) atomicAdd(&tiles[bh], cnt);
+  }
 }
 
-__global__ __launch_bounds__(64) void k_bwd_table(const int32_t* __restrict__ qstats, const int32_t* __restrict__ kstats,
-                                                  const int32_t* __restrict__ fwd, int nQt, int nKt,
-                                                  int32_t* __restrict__ bwd) {
+// One wave per key tile: first and last query tile that processes it.
+__global__ __launch_bounds__(256) void k_bwd_table(const int32_t* __restrict__ qstats, const int32_t* __restrict__ kstats,
+                                                   const int32_t* __restrict__ fwd, int nQt, int nKt,
+                                                   int32_t* __restrict__ bwd) {
   const int bh = blockIdx.y;
-  const int j = blockIdx.x * 64 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (j >= nKt) return;
   const int kmin = reinterpret_cast<const int4*>(kstats)[static_cast<size_t>(bh) * nKt + j].x;
   const int4* qs = reinterpret_cast<const int4*>(qstats) + static_cast<size_t>(bh) * nQt;
   const int2* ft = reinterpret_cast<const int2*>(fwd) + static_cast<size_t>(bh) * nQt;
   int first = -1, last = -1;
-  for (int i = 0; i < nQt; ++i) {
-    const int2 r = ft[i];
-    if (j >= r.x && j < r.y && kmin <= qs[i].y) {
-      if (first < 0) first = i;
-      last = i;
+  for (int i0 = 0; i0 < nQt; i0 += 64) {
+    const int i = i0 + lane;
+    bool hit = false;
+    if (i < nQt) {
+      const int2 r = ft[i];
+      hit = j >= r.x && j < r.y && kmin <= qs[i].y;
+    }
+    const uint64_t m = __ballot(hit);
+    if (m) {
+      if (first < 0) first = i0 + __ffsll(static_cast<long long>(m)) - 1;
+      last = i0 + 63 - __clzll(static_cast<long long>(m));
     }
   }
-  reinterpret_cast<int2*>(bwd)[static_cast<size_t>(bh) * nKt + j] = first < 0 ? make_int2(0, 0) : make_int2(first, last + 1);
+  if (lane == 0)
+    reinterpret_cast<int2*>(bwd)[static_cast<size_t>(bh) * nKt + j] =
+        first < 0 ? make_int2(0, 0) : make_int2(first, last + 1);
+}
+
+// ---------------------------------------------------------------------------
+// Launch order of the attention workgroups: tiles sorted by range length,
+// longest first (a longest-processing-time-first schedule), within G groups
+// of heads. Workgroup x of an attention launch takes order[x]; the hardware
+// hands workgroup x to XCD x % 8, so with G = 8 each XCD works on its own
+// heads (their K/V stay in that XCD's L2). One workgroup per group:
+// counting sort over the length bins in LDS. Items of equal length may come
+// in any order; every order gives the same attention results.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_work_order(const int2* __restrict__ tab, int BH, int nT, int span, int G,
+                                                     int32_t* __restrict__ order) {
+  extern __shared__ int32_t bins[];  // span + 1 bins: bin span - len
+  __shared__ int32_t wsum[16];
+  const int g = blockIdx.x;
+  const int hpg = BH / G;
+  const int n = hpg * nT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nbins = span + 1;
+  for (int i = tid; i < nbins; i += 1024) bins[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) {
+    const int bh = g + (i / nT) * G, t = i % nT;
+    const int2 r = tab[static_cast<size_t>(bh) * nT + t];
+    const int len = min(max(r.y - r.x, 0), span);
+    atomicAdd(&bins[span - len], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the bins: each thread owns a contiguous run of bins
+  const int per = (nbins + 1023) / 1024;
+  const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
+  int s = 0;
+  for (int k = b0; k < b1; ++k) s += bins[k];
+  int x = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int pre = x - s;
+  for (int k = 0; k < w; ++k) pre += wsum[k];
+  for (int k = b0; k < b1; ++k) {
+    const int c = bins[k];
+    bins[k] = pre;
+    pre += c;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) {
+    const int bh = g + (i / nT) * G, t = i % nT;
+    const int2 r = tab[static_cast<size_t>(bh) * nT + t];
+    const int len = min(max(r.y - r.x, 0), span);
+    const int slot = atomicAdd(&bins[span - len], 1);
+    order[static_cast<size_t>(slot) * G + g] = bh * nT + t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -602,10 +742,8 @@ int scfa_hash_sort(const int32_t* bucket, int B, int H, int T, int nb, int32_t p
   int32_t* hist = static_cast<int32_t*>(workspace);
   hipLaunchKernelGGL(k_sort_hist, dim3(nC, B * H), dim3(256), 0, stream, bucket, T, nb, nC, hist, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_sort_scan, dim3(B * H), dim3(64), 0, stream, hist, nb, nC, offsets);
-  SCFA_RETURN_IF_LAUNCH_FAILED();
   hipLaunchKernelGGL(k_sort_scatter, dim3(nCx, B * H), dim3(256), 0, stream, bucket, T, Tp, nb, nC, hist, pad_idx,
-                     perm, bucket_sorted);
+                     perm, bucket_sorted, offsets);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }
@@ -653,11 +791,23 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
   hipLaunchKernelGGL(k_tile_stats, dim3(nQt + nKt, B * H), dim3(64), 0, stream, mode, q_idx, k_idx, q_bkt, k_bkt, Tq,
                      Tk, TqP, TkP, Bm, Bn, nQt, nKt, qstats, kstats, tiles);
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_fwd_table, dim3(ceil_div(nQt, 64), B * H), dim3(64), 0, stream, mode, qstats, kstats, nQt, nKt,
+  hipLaunchKernelGGL(k_fwd_table, dim3(ceil_div(nQt, 4), B * H), dim3(256), 0, stream, mode, qstats, kstats, nQt, nKt,
                      fwd_tab, tiles);
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_bwd_table, dim3(ceil_div(nKt, 64), B * H), dim3(64), 0, stream, qstats, kstats, fwd_tab, nQt, nKt,
-                     bwd_tab);
+  hipLaunchKernelGGL(k_bwd_table, dim3(ceil_div(nKt, 4), B * H), dim3(256), 0, stream, qstats, kstats, fwd_tab, nQt,
+                     nKt, bwd_tab);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+int scfa_work_order(const int32_t* tab, int B, int H, int ntiles, int span, int32_t* order, hipStream_t stream) {
+  if (!tab || !order) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || ntiles < 1 || span < 1 || span > kMaxOrderSpan) return SCFA_ERR_INVALID;
+  const int BH = B * H;
+  const int G = (BH % 8 == 0) ? 8 : 1;
+  const size_t lds = static_cast<size_t>(span + 1) * sizeof(int32_t);
+  hipLaunchKernelGGL(k_work_order, dim3(G), dim3(1024), lds, stream, reinterpret_cast<const int2*>(tab), BH, ntiles,
+                     span, G, order);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }

@@ -48,10 +48,11 @@ _SIGS = {
     "scfa_gather": (_i, [_i, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "scfa_range_table": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_count_visible": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
-    "scfa_qk_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp,
-                                _vp]),
-    "scfa_hash_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _vp,
-                                  _vp, _vp]),
+    "scfa_work_order": (_i, [_vp, _i, _i, _i, _i, _vp, _vp]),
+    "scfa_qk_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp,
+                                _vp, _vp]),
+    "scfa_hash_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f,
+                                  _vp, _vp, _vp]),
     "scfa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "scfa_bwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                       _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -184,21 +185,27 @@ def scfa_count_visible(mode, q_idx, k_idx, q_bkt, k_bkt, B, H, Tq, Tk, pairs, st
                                     _stream(stream, pairs)), "scfa_count_visible")
 
 
-def scfa_qk_sparse_fwd(q_c, k_c, v_t, q_idx, k_idx, qstats, kstats, fwd_tab, T, O, lse, scale=None, stream=None):
+def scfa_work_order(tab, span, order, stream=None):
+    B, H, n, _ = tab.shape
+    _check(lib().scfa_work_order(_p(tab), B, H, n, span, _p(order), _stream(stream, tab)), "scfa_work_order")
+
+
+def scfa_qk_sparse_fwd(q_c, k_c, v_t, q_idx, k_idx, qstats, kstats, fwd_tab, T, O, lse, scale=None, stream=None,
+                       order=None):
     B, H, Tc, D = q_c.shape
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(lib().scfa_qk_sparse_fwd(_dt(q_c), _dt(O), _p(q_c), _p(k_c), _p(v_t), _p(q_idx), _p(k_idx), _p(qstats),
-                                    _p(kstats), _p(fwd_tab), B, H, T, Tc, D, scale, _p(O), _p(lse),
+                                    _p(kstats), _p(fwd_tab), _p(order), B, H, T, Tc, D, scale, _p(O), _p(lse),
                                     _stream(stream, q_c)), "scfa_qk_sparse_fwd")
 
 
 def scfa_hash_sparse_fwd(q_s, k_s, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, T, O, lse, scale=None,
-                         stream=None):
+                         stream=None, order=None):
     B, H, Tp, D = q_s.shape
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(lib().scfa_hash_sparse_fwd(_dt(q_s), _dt(O), _p(q_s), _p(k_s), _p(v_t), _p(q_idx), _p(k_idx), _p(q_bkt),
-                                      _p(k_bkt), _p(qstats), _p(kstats), _p(fwd_tab), B, H, T, D, scale, _p(O),
-                                      _p(lse), _stream(stream, q_s)), "scfa_hash_sparse_fwd")
+                                      _p(k_bkt), _p(qstats), _p(kstats), _p(fwd_tab), _p(order), B, H, T, D, scale,
+                                      _p(O), _p(lse), _stream(stream, q_s)), "scfa_hash_sparse_fwd")
 
 
 def scfa_bwd_workspace_bytes(mode, B, H, Tq, D=64) -> int:
@@ -248,6 +255,7 @@ class Tables:
     tiles: torch.Tensor
     Bm: int
     Bn: int
+    fwd_order: Optional[torch.Tensor] = None  # launch order of the forward / dQ workgroups
 
 
 def _empty(shape, dtype, like):
@@ -335,6 +343,8 @@ def build_tables(pre: Prepared, Bm: int = SCFA_TILE_M, Bn: int = SCFA_TILE_N, st
                _empty((B, H, nKt, 2), i32, pre.q), _empty((B, H), i32, pre.q), Bm, Bn)
     scfa_range_table(mode, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, B, H, pre.Tq, pre.Tq, Bm, Bn, t.qstats, t.kstats,
                      t.fwd, t.bwd, t.tiles, stream)
+    t.fwd_order = _empty((B * H * nQt,), i32, pre.q)
+    scfa_work_order(t.fwd, nKt, t.fwd_order, stream)
     return t
 
 
@@ -355,10 +365,10 @@ def forward(pre: Prepared, tab: Tables, out_dtype=torch.float32, scale=None, O=N
         lse = _empty((B, H, T), torch.float32, pre.q)
     if pre.mode == "hash":
         scfa_hash_sparse_fwd(pre.q, pre.k, pre.v_t, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats,
-                             tab.fwd, T, O, lse, scale, stream)
+                             tab.fwd, T, O, lse, scale, stream, order=tab.fwd_order)
     else:
         scfa_qk_sparse_fwd(pre.q, pre.k, pre.v_t, pre.q_idx, pre.k_idx, tab.qstats, tab.kstats, tab.fwd, T, O, lse,
-                           scale, stream)
+                           scale, stream, order=tab.fwd_order)
     return O, lse
 
 
@@ -445,7 +455,8 @@ class Plan:
             self.k_idx.copy_(torch.where(ar < T, ar, torch.full_like(ar, SCFA_K_PAD)).expand(B, H, Tp))
         Bm, Bn = SCFA_TILE_M, SCFA_TILE_N
         nQt, nKt = Tp // Bm, Tp // Bn
-        self.tab = Tables(e((B, H, nQt, 4)), e((B, H, nKt, 4)), e((B, H, nQt, 2)), e((B, H, nKt, 2)), e((B, H)), Bm, Bn)
+        self.tab = Tables(e((B, H, nQt, 4)), e((B, H, nKt, 4)), e((B, H, nQt, 2)), e((B, H, nKt, 2)), e((B, H)), Bm, Bn,
+                          e((B * H * nQt,)))
         self.O = e((B, T, H, D), out_dtype)
         self.lse = e((B, H, T), torch.float32)
         self.pairs = e((B, H), torch.int64)
@@ -480,15 +491,16 @@ class Plan:
         t = self.tab
         scfa_range_table(mode, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H, self.Tq, self.Tq, t.Bm,
                          t.Bn, t.qstats, t.kstats, t.fwd, t.bwd, t.tiles, stream)
+        scfa_work_order(t.fwd, t.kstats.shape[2], t.fwd_order, stream)
 
     def forward(self, stream=None):
         t = self.tab
         if self.mode == "hash":
             scfa_hash_sparse_fwd(self.q_s, self.k_s, self.v_t, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, t.qstats,
-                                 t.kstats, t.fwd, self.T, self.O, self.lse, self.scale, stream)
+                                 t.kstats, t.fwd, self.T, self.O, self.lse, self.scale, stream, order=t.fwd_order)
         else:
             scfa_qk_sparse_fwd(self.q_s, self.k_s, self.v_t, self.q_idx, self.k_idx, t.qstats, t.kstats, t.fwd, self.T,
-                               self.O, self.lse, self.scale, stream)
+                               self.O, self.lse, self.scale, stream, order=t.fwd_order)
 
     def backward(self, dO, stream=None):
         """Gradients of the last forward() w.r.t. q, k, v (fp32, original order)."""

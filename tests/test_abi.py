@@ -69,16 +69,21 @@ def test_invalid_arguments_rejected_without_gpu():
     # hash mode needs buckets
     assert L.scfa_range_table(2, dummy, dummy, null, null, 1, 1, 8, 8, 128, 64, dummy, dummy, dummy, dummy, dummy,
                               null) == scfa.SCFA_ERR_INVALID
-    # forward: bad scale, D, Tc
-    args = [0, 1] + [dummy] * 8
+    # forward: bad scale, D, Tc (the launch order may be NULL)
+    args = [0, 1] + [dummy] * 8 + [null]
     assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 64, ctypes.c_float(0.0), dummy, dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 128, ctypes.c_float(0.125), dummy, dummy,
                                 null) == scfa.SCFA_ERR_UNSUPPORTED
     assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 120, 64, ctypes.c_float(0.125), dummy, dummy,
                                 null) == scfa.SCFA_ERR_INVALID
     hargs = [0, 1] + [dummy] * 10
-    assert L.scfa_hash_sparse_fwd(*hargs[:-1], null, 1, 1, 8, 64, ctypes.c_float(0.125), dummy, dummy,
+    # hash forward: a NULL table is rejected
+    assert L.scfa_hash_sparse_fwd(*hargs[:-1], null, null, 1, 1, 8, 64, ctypes.c_float(0.125), dummy, dummy,
                                   null) == scfa.SCFA_ERR_INVALID
+    # work order: bad sizes, NULL pointers
+    assert L.scfa_work_order(dummy, 1, 1, 0, 8, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_work_order(dummy, 1, 1, 8, 16384, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_work_order(null, 1, 1, 8, 8, dummy, null) == scfa.SCFA_ERR_INVALID
 
 
 def test_python_binding_rejects_host_tensors():

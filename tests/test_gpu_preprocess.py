@@ -38,7 +38,26 @@ def _tables_match(mode, pre, tab, Tq, Bm, Bn, q_bkt=None, k_bkt=None):
     assert (fwd[:, :, nQ:, 0] == fwd[:, :, nQ:, 1]).all()
     assert (bwd[:, :, nK:] == 0).all()
     assert (ks[:, :, nK:, 0] == scfa.SCFA_K_PAD).all()
+    if tab.fwd_order is not None:
+        check_order(tab.fwd_order.cpu().numpy(), fwd)
     return ref
+
+
+def check_order(order, tab):
+    """A launch order is a permutation of the (head, tile) items; within each
+    group of heads (bh % 8 when B*H is a multiple of 8) the range lengths do
+    not increase along the group's slots, and slot s of group g sits at
+    s*8 + g (workgroup x runs on XCD x % 8)."""
+    B, H, n, _ = tab.shape
+    BH = B * H
+    assert sorted(order.tolist()) == list(range(BH * n))
+    G = 8 if BH % 8 == 0 else 1
+    lens = (tab[..., 1] - tab[..., 0]).reshape(BH * n)
+    for g in range(G):
+        items = order[g::G]
+        assert ((items // n) % G == g).all()
+        ls = lens[items]
+        assert (np.diff(ls) <= 0).all()
 
 
 @pytest.mark.parametrize("w", QK_CASES, ids=lambda w: w.name)
