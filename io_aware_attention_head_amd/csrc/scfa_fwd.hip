@@ -17,19 +17,29 @@
 //  * Scores are computed TRANSPOSED, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_bf16: the accumulator then gives every lane one
 //    query column and 4 keys per 16x16 block, so the row max needs one
-//    in-lane pass plus two cross-lane steps, the row sum stays per lane until
-//    the epilogue, and the output rescale is lane-local.
+//    in-lane pass plus two cross-lane steps and the output rescale is
+//    lane-local.
 //  * O^T = V^T P^T reuses the S^T accumulator as the B operand after a cvt
 //    to bf16; K rows are permuted when loaded as the A operand so that each
 //    lane's 8 probabilities cover 8 CONSECUTIVE keys, which makes the V^T
 //    operand one 16-byte LDS read (V is stored transposed by the gather).
-//  * K rows and V^T rows are double-buffered in LDS (16 B XOR-swizzled
-//    chunks), the next tile's global loads are in flight during the MFMAs.
-//  * Fully visible tiles (decided from the tile extrema) skip the mask.
-//  * Work order: longest query tiles first, and when B*H is a multiple of 8
-//    each XCD owns whole heads so K/V tiles are reused from its own L2.
-//  * float32 inputs use v_mfma_f32_16x16x4_f32 with the same data flow
-//    (single-buffered LDS).
+//  * Software pipeline (bf16): while the exponentials of tile j run on the
+//    VALU, the MFMAs of S for tile j+1 are in flight; while P V of tile j
+//    runs on the MFMA unit, tile j+1 is masked and its row max taken. K/V^T
+//    tiles rotate through three LDS stages (one barrier per tile) and the
+//    global loads of tile j+2 are in flight during tile j.
+//  * The reference max moves only when a row's tile max exceeds it by more
+//    than 2^8 (lazy rescaling): probabilities stay <= 256 and the O rescale
+//    is rare. O is normalised by the sum of the bf16-rounded probabilities
+//    (an MFMA against a ones operand, consistent with the P V product); the
+//    LSE uses the fp32 row sum.
+//  * Per-wave tile tests from the extrema: a key tile holding no pair visible
+//    to any of the wave's 32 queries is skipped by that wave, and one whose
+//    pairs are all visible skips the mask.
+//  * Work order: a launch order (longest query tiles first, XCD-aware) from
+//    scfa_work_order, or descending query-tile index.
+//  * float32 inputs use v_mfma_f32_16x16x4_f32 in a single-buffered kernel
+//    with the same data layout.
 
 #include <math.h>
 
@@ -42,6 +52,7 @@ constexpr int BM = SCFA_TILE_M;  // 128 query rows per workgroup
 constexpr int BN = SCFA_TILE_N;  // 64 keys per tile
 constexpr int HD = 64;           // head dimension
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLazy = 8.0f;  // log2 headroom before the reference max moves
 
 struct FwdParams {
   const void* q;
@@ -81,22 +92,6 @@ __device__ inline void store4<uint16_t>(uint16_t* p, const f32x4& v) {
   u.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h2)) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h3)) << 16);
   *reinterpret_cast<uint2*>(p) = u;
 }
-
-// Element type traits of the input path.
-template <bool F32>
-struct Tr;
-template <>
-struct Tr<false> {  // bf16
-  static constexpr int ESZ = 2;
-  static constexpr int CH = HD * ESZ / 16;  // 16-byte chunks per 64-element row = 8
-  static constexpr int NBUF = 2;
-};
-template <>
-struct Tr<true> {  // fp32
-  static constexpr int ESZ = 4;
-  static constexpr int CH = HD * ESZ / 16;  // 16
-  static constexpr int NBUF = 1;
-};
 
 // Registers holding the next key tile while the current one is computed.
 template <int LOADS>
@@ -139,27 +134,9 @@ __device__ __forceinline__ void tile_store(const TileRegs<LOADS>& r, uint8_t* ks
   else if (HASH && tid < 2 * BN) kb[tid - BN] = r.idx;
 }
 
-template <bool HASH, bool F32, bool ZERO_DROPPED, typename TOUT>
-__global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
-  using TR = Tr<F32>;
-  constexpr int ESZ = TR::ESZ, CH = TR::CH, NBUF = TR::NBUF;
-  constexpr int TILE_BYTES = BN * HD * ESZ;        // K tile and V^T tile, bytes each
-  constexpr int LOADS = TILE_BYTES / 16 / 256;     // 16-byte loads per thread per tile
-  // K and V^T tiles; after the loop the same bytes stage the output tile.
-  __shared__ __align__(16) uint8_t smem[2 * NBUF * TILE_BYTES];
-  uint8_t(*Ks)[TILE_BYTES] = reinterpret_cast<uint8_t(*)[TILE_BYTES]>(smem);
-  uint8_t(*Vs)[TILE_BYTES] = reinterpret_cast<uint8_t(*)[TILE_BYTES]>(smem + NBUF * TILE_BYTES);
-  static_assert(2 * NBUF * TILE_BYTES >= BM * HD * sizeof(TOUT), "output staging does not fit");
-  __shared__ __align__(16) int32_t Kp[NBUF][BN];
-  __shared__ __align__(16) int32_t Kb[NBUF][BN];
-  __shared__ int32_t Qi[BM];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+// Work item of this workgroup: (head, query tile).
+__device__ inline void pick_work(const FwdParams& p, int& qt, int& bh) {
   const int BH = p.B * p.H;
-
-  // ---- work item: (head, query tile), longest first, XCD-aware ----------
-  int qt, bh;
   if (p.order) {
     const int it = p.order[blockIdx.x];
     bh = it / p.nQt;
@@ -175,252 +152,109 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
       bh = x % BH;
     }
   }
-  const int b = bh / p.H, h = bh - b * p.H;
-  const size_t rowbase = static_cast<size_t>(bh) * p.Tpad;
-  const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
-  const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
-  const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
-  if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];  // visible after the first barrier
+}
 
-  // ---- queries of this wave: B operand, positions, buckets --------------
-  const int q0 = qt * BM + w * 32;
-  int qpos[2], qbkt[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = q0 + qb * 16 + r16;
-    qpos[qb] = p.q_idx[rowbase + row];
-    qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
-  }
-  // extrema of this wave's real query rows (pad rows: position -1, their
-  // results are never stored): a key tile is skipped by the whole wave when
-  // it holds no pair visible to any of them, and unmasked when every pair is
-  // visible to all of them.
-  int wmin = kInt32Max, wmax = -1, wbmin = kInt32Max, wbmax = kInt32Min;
+// Extrema of this wave's real query rows (pad rows: position -1, their
+// results are never stored): a key tile is skipped by the whole wave when it
+// holds no pair visible to any of them, and unmasked when every pair is
+// visible to all of them. All 4 lane groups hold the same 2 x 16 rows.
+struct WaveRows {
+  int minpos, maxpos, minb, maxb;
+};
+
+__device__ inline WaveRows wave_rows(const int (&qpos)[2], const int (&qbkt)[2]) {
+  WaveRows s{kInt32Max, -1, kInt32Max, kInt32Min};
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     if (qpos[qb] >= 0) {
-      wmin = min(wmin, qpos[qb]);
-      wmax = max(wmax, qpos[qb]);
-      wbmin = min(wbmin, qbkt[qb]);
-      wbmax = max(wbmax, qbkt[qb]);
+      s.minpos = min(s.minpos, qpos[qb]);
+      s.maxpos = max(s.maxpos, qpos[qb]);
+      s.minb = min(s.minb, qbkt[qb]);
+      s.maxb = max(s.maxb, qbkt[qb]);
     }
   }
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) {
-    wmin = min(wmin, __shfl_xor(wmin, o));
-    wmax = max(wmax, __shfl_xor(wmax, o));
-    wbmin = min(wbmin, __shfl_xor(wbmin, o));
-    wbmax = max(wbmax, __shfl_xor(wbmax, o));
+    s.minpos = min(s.minpos, __shfl_xor(s.minpos, o));
+    s.maxpos = max(s.maxpos, __shfl_xor(s.maxpos, o));
+    s.minb = min(s.minb, __shfl_xor(s.minb, o));
+    s.maxb = max(s.maxb, __shfl_xor(s.maxb, o));
   }
-  bf16x8 Qb[2][2];   // bf16: [qb][ds]
-  float Qf[2][16];   // fp32: [qb][t], d = 16g + t
-  if constexpr (!F32) {
-    const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (rowbase + q0) * HD;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int ds = 0; ds < 2; ++ds)
-        Qb[qb][ds] = *reinterpret_cast<const bf16x8*>(qg + (qb * 16 + r16) * HD + ds * 32 + g * 8);
-  } else {
-    const float* qg = static_cast<const float*>(p.q) + (rowbase + q0) * HD;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const float4 v = *reinterpret_cast<const float4*>(qg + (qb * 16 + r16) * HD + 16 * g + 4 * t4);
-        Qf[qb][4 * t4 + 0] = v.x;
-        Qf[qb][4 * t4 + 1] = v.y;
-        Qf[qb][4 * t4 + 2] = v.z;
-        Qf[qb][4 * t4 + 3] = v.w;
-      }
-  }
+  // wave-uniform from here on: tile tests become scalar branches
+  s.minpos = __builtin_amdgcn_readfirstlane(s.minpos);
+  s.maxpos = __builtin_amdgcn_readfirstlane(s.maxpos);
+  s.minb = __builtin_amdgcn_readfirstlane(s.minb);
+  s.maxb = __builtin_amdgcn_readfirstlane(s.maxb);
+  return s;
+}
 
-  f32x4 Oacc[4][2];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) Oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
+template <bool HASH>
+__device__ inline bool tile_empty_for(const int4& ks, const WaveRows& wr) {
+  return ks.x > wr.maxpos || (HASH && (ks.w < wr.minb || ks.z > wr.maxb));
+}
 
-  // ---- tile pipeline ------------------------------------------------------
-  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + rowbase * HD * ESZ;
-  const uint8_t* vg = static_cast<const uint8_t*>(p.vt) + static_cast<size_t>(bh) * HD * p.Tpad * ESZ;
-  const int32_t* kig = p.k_idx + rowbase;
-  const int32_t* kbg = HASH ? p.k_bkt + rowbase : nullptr;
-  TileRegs<LOADS> tr;
+template <bool HASH>
+__device__ inline bool tile_full_for(const int4& ks, const WaveRows& wr, int j, int Tk) {
+  bool full = ks.y <= wr.minpos && (j + 1) * BN <= Tk;
+  if (HASH) full = full && ks.z == ks.w && wr.minb == wr.maxb && ks.z == wr.minb;
+  return full;
+}
 
-  auto next_tile = [&](int j) {
-    while (j < rng.y && kst[j].x > qs.y) ++j;  // causal extremum test (hash ranges)
-    return j;
-  };
-
-  int j = next_tile(rng.x);
-  if (j < rng.y) {
-    tile_load<HASH, ESZ, CH, LOADS>(tr, kg, vg, kig, kbg, p.Tpad, j, tid);
-    tile_store<HASH, ESZ, CH, LOADS>(tr, Ks[0], Vs[0], Kp[0], Kb[0], tid);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (j < rng.y) {
-    const int jn = next_tile(j + 1);
-    if (jn < rng.y) tile_load<HASH, ESZ, CH, LOADS>(tr, kg, vg, kig, kbg, p.Tpad, jn, tid);
-    const int4 ks = kst[j];
-    const bool wave_empty = ks.x > wmax || (HASH && (ks.w < wbmin || ks.z > wbmax));
-    if (!wave_empty) {
-
-    // -- S^T = K Q^T --------------------------------------------------------
-    f32x4 S[4][2];
+// Scores of keys that are not visible to the lane's query become -inf.
+// Accumulator element e of block kb in lane group g is key
+// 32 (kb >> 1) + 8 g + 4 (kb & 1) + e of the tile.
+template <bool HASH>
+__device__ inline void apply_mask(f32x4 (&S)[4][2], const int32_t* kp, const int32_t* kbk, const int (&qpos)[2],
+                                  const int (&qbkt)[2], int g) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (!F32) {
-#pragma unroll
-      for (int ds = 0; ds < 2; ++ds)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int row = key_row(kb, r16);
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[buf][row * HD * 2 + (((ds * 4 + g) ^ swz_k(row)) * 16)]);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Qb[qb][ds], S[kb][qb], 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int row = key_row(kb, r16);
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-          const float4 a = *reinterpret_cast<const float4*>(&Ks[buf][row * HD * 4 + (((4 * g + t4) ^ swz_k(row)) * 16)]);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, Qf[qb][4 * t4 + 0], S[kb][qb], 0, 0, 0);
-            S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, Qf[qb][4 * t4 + 1], S[kb][qb], 0, 0, 0);
-            S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, Qf[qb][4 * t4 + 2], S[kb][qb], 0, 0, 0);
-            S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, Qf[qb][4 * t4 + 3], S[kb][qb], 0, 0, 0);
-          }
-        }
-      }
-    }
-
-    // -- mask on tiles that are not fully visible ---------------------------
-    bool full = ks.y <= wmin && (j + 1) * BN <= p.Tk;
-    if (HASH) full = full && ks.z == ks.w && wbmin == wbmax && ks.z == wbmin;
-    if (!full) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int kbase = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1);
-        const int4 kp4 = *reinterpret_cast<const int4*>(&Kp[buf][kbase]);
-        int4 kb4 = make_int4(0, 0, 0, 0);
-        if (HASH) kb4 = *reinterpret_cast<const int4*>(&Kb[buf][kbase]);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int qp = qpos[qb], qh = qbkt[qb];
-          if (!(kp4.x <= qp && (!HASH || kb4.x == qh))) S[kb][qb][0] = -INFINITY;
-          if (!(kp4.y <= qp && (!HASH || kb4.y == qh))) S[kb][qb][1] = -INFINITY;
-          if (!(kp4.z <= qp && (!HASH || kb4.z == qh))) S[kb][qb][2] = -INFINITY;
-          if (!(kp4.w <= qp && (!HASH || kb4.w == qh))) S[kb][qb][3] = -INFINITY;
-        }
-      }
-    }
-
-    // -- online softmax (base 2, scale folded into the exponent) -----------
+  for (int kb = 0; kb < 4; ++kb) {
+    const int kbase = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1);
+    const int4 kp4 = *reinterpret_cast<const int4*>(&kp[kbase]);
+    int4 kb4 = make_int4(0, 0, 0, 0);
+    if (HASH) kb4 = *reinterpret_cast<const int4*>(&kbk[kbase]);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float mx = fmaxf(S[0][qb][0], S[0][qb][1]);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = (kb == 0 ? 2 : 0); e < 4; e += 2) mx = fmaxf(mx, fmaxf(S[kb][qb][e], S[kb][qb][e + 1]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[qb], mx * p.c);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - muse);
-      m[qb] = mnew;
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][e], p.c, -muse));
-          S[kb][qb][e] = pv;
-          ls += pv;
-        }
-      l[qb] = l[qb] * alpha + ls;
-      if (__ballot(alpha != 1.f)) {  // the running max moved for some query of this wave
-#pragma unroll
-        for (int db = 0; db < 4; ++db) Oacc[db][qb] *= alpha;
-      }
+      const int qp = qpos[qb], qh = qbkt[qb];
+      if (!(kp4.x <= qp && (!HASH || kb4.x == qh))) S[kb][qb][0] = -INFINITY;
+      if (!(kp4.y <= qp && (!HASH || kb4.y == qh))) S[kb][qb][1] = -INFINITY;
+      if (!(kp4.z <= qp && (!HASH || kb4.z == qh))) S[kb][qb][2] = -INFINITY;
+      if (!(kp4.w <= qp && (!HASH || kb4.w == qh))) S[kb][qb][3] = -INFINITY;
     }
-
-    // -- O^T += V^T P^T -----------------------------------------------------
-    if constexpr (!F32) {
-      bf16x8 P[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) P[qb][kc] = pack_bf16x8(S[2 * kc][qb], S[2 * kc + 1][qb]);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const int d = db * 16 + r16;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vs[buf][d * BN * 2 + (((kc * 4 + g) ^ (d & 7)) * 16)]);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, P[qb][kc], Oacc[db][qb], 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = db * 16 + r16;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int ch = 8 * (kb >> 1) + 2 * g + (kb & 1);  // keys 32kc + 8g + 4hb + 0..3
-          const float4 a = *reinterpret_cast<const float4*>(&Vs[buf][d * BN * 4 + ((ch ^ (d & 7)) * 16)]);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, S[kb][qb][0], Oacc[db][qb], 0, 0, 0);
-            Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, S[kb][qb][1], Oacc[db][qb], 0, 0, 0);
-            Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, S[kb][qb][2], Oacc[db][qb], 0, 0, 0);
-            Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, S[kb][qb][3], Oacc[db][qb], 0, 0, 0);
-          }
-        }
-      }
-    }
-
-    }  // !wave_empty
-
-    if constexpr (NBUF == 2) {
-      if (jn < rng.y) tile_store<HASH, ESZ, CH, LOADS>(tr, Ks[buf ^ 1], Vs[buf ^ 1], Kp[buf ^ 1], Kb[buf ^ 1], tid);
-      __syncthreads();
-      buf ^= 1;
-    } else {
-      __syncthreads();
-      if (jn < rng.y) tile_store<HASH, ESZ, CH, LOADS>(tr, Ks[0], Vs[0], Kp[0], Kb[0], tid);
-      __syncthreads();
-    }
-    j = jn;
   }
+}
 
-  // ---- epilogue: normalise, stage the tile in LDS, write whole rows --------
+// Row max (log2 units) of a score tile: 16 in-lane values per query column
+// (max3 chains), then across the 4 lane groups.
+__device__ inline float row_max_scaled(const f32x4 (&S)[4][2], int qb, float c) {
+  float mx = fmaxf(S[0][qb][0], fmaxf(S[0][qb][1], S[0][qb][2]));
+#pragma unroll
+  for (int i = 3; i < 15; i += 2)
+    mx = fmaxf(mx, fmaxf(S[i >> 2][qb][i & 3], S[(i + 1) >> 2][qb][(i + 1) & 3]));
+  mx = fmaxf(mx, S[3][qb][3]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  return mx * c;
+}
+
+// Epilogue: normalise, stage the tile in LDS, write whole rows at the
+// original positions, LSE; in QK-drop mode zero the dropped queries the tile
+// owns. `ost` must hold BM * HD * sizeof(TOUT) bytes of LDS.
+template <bool ZERO_DROPPED, typename TOUT>
+__device__ inline void fwd_epilogue(const FwdParams& p, TOUT* ost, const int32_t* Qi, const f32x4 (&Oacc)[4][2],
+                                    const float (&inv)[2], const float (&lse)[2], const int (&qpos)[2], int qt, int bh,
+                                    size_t rowbase) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int b = bh / p.H, h = bh - b * p.H;
   // Output units of 4 elements (16 B fp32 / 8 B bf16), 16 per row, XOR
   // swizzled by row so the column-wise staging writes are conflict-free.
-  TOUT* ost = reinterpret_cast<TOUT*>(smem);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float lt = l[qb] + __shfl_xor(l[qb], 16);
-    lt = lt + __shfl_xor(lt, 32);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float muse = (m[qb] == -INFINITY) ? 0.f : m[qb];
-    const float lse = lt > 0.f ? (muse + log2f(lt)) * kLn2 : -INFINITY;
     const int row = w * 32 + qb * 16 + r16;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) store4<TOUT>(ost + row * HD + (((4 * db + g) ^ (row & 15)) * 4), Oacc[db][qb] * inv);
+    for (int db = 0; db < 4; ++db) store4<TOUT>(ost + row * HD + (((4 * db + g) ^ (row & 15)) * 4), Oacc[db][qb] * inv[qb]);
     const int qp = qpos[qb];
-    if (g == 0 && qp >= 0 && qp < p.T) p.lse[static_cast<size_t>(bh) * p.T + qp] = lse;
+    if (g == 0 && qp >= 0 && qp < p.T) p.lse[static_cast<size_t>(bh) * p.T + qp] = lse[qb];
   }
   __syncthreads();
   TOUT* O = static_cast<TOUT*>(p.O);
@@ -438,11 +272,10 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
     }
   }
 
-  // ---- QK-drop: zero the dropped queries this tile owns ------------------
-  // Tile qt owns the original positions after the previous tile's last kept
-  // query up to its own last kept query (the last tile holding kept queries
-  // also owns everything after it; with no kept query at all, tile 0 owns
-  // the whole sequence). Positions in that range that are not among the
+  // QK-drop: tile qt owns the original positions after the previous tile's
+  // last kept query up to its own last kept query (the last tile holding kept
+  // queries also owns everything after it; with no kept query at all, tile 0
+  // owns the whole sequence). Positions in that range that are not among the
   // tile's queries were dropped: O = 0, LSE = -inf.
   if constexpr (ZERO_DROPPED) {
     const int nreal = __syncthreads_count(tid < BM && Qi[tid] >= 0);
@@ -476,22 +309,385 @@ __global__ __launch_bounds__(256) void k_fwd(FwdParams p) {
   }
 }
 
-template <bool HASH, bool F32, bool ZD, typename TOUT>
-int launch_fwd(const FwdParams& p, hipStream_t stream) {
-  const int grid = p.nQt * p.B * p.H;
-  hipLaunchKernelGGL((k_fwd<HASH, F32, ZD, TOUT>), dim3(grid), dim3(256), 0, stream, p);
-  SCFA_RETURN_IF_LAUNCH_FAILED();
-  return SCFA_OK;
+// ---------------------------------------------------------------------------
+// bf16 inputs.
+// ---------------------------------------------------------------------------
+
+// Global -> LDS DMA without registers: each lane's 16 (or 4) bytes land at
+// consecutive LDS addresses from the wave-uniform byte address `lds`; the
+// source is a wave-uniform base plus a per-lane 32-bit offset. Issued as
+// inline assembly so that the compiler does not order the LDS reads of the
+// other stage behind it; completion is awaited with dma_wait() before the
+// barrier that publishes the stage.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt not waited on), as a builtin so that
+// the compiler knows every earlier vector-memory load has completed.
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0xF70); }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  const __attribute__((address_space(3))) void* lp = (const __attribute__((address_space(3))) void*)p;
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lp);
+}
+
+template <bool HASH, bool ZERO_DROPPED, typename TOUT>
+__global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
+  constexpr int TB = BN * HD * 2;  // K tile and V^T tile, bytes each (8 KB)
+  // Two stages of (K, V^T); after the loop the same bytes stage the output.
+  __shared__ __align__(16) uint8_t smem[4 * TB];
+  static_assert(4 * TB >= BM * HD * sizeof(TOUT), "output staging does not fit");
+  __shared__ __align__(16) int32_t Kp[2][BN];
+  __shared__ __align__(16) int32_t Kb[2][BN];
+  __shared__ int32_t Qi[BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int ws = __builtin_amdgcn_readfirstlane(w);
+  int qt, bh;
+  pick_work(p, qt, bh);
+  const size_t rowbase = static_cast<size_t>(bh) * p.Tpad;
+  const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
+  const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
+  const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
+  if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];  // visible after the first barrier
+
+  // ---- queries of this wave: B operand, positions, buckets --------------
+  const int q0 = qt * BM + w * 32;
+  int qpos[2], qbkt[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = q0 + qb * 16 + r16;
+    qpos[qb] = p.q_idx[rowbase + row];
+    qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
+  }
+  const WaveRows wr = wave_rows(qpos, qbkt);
+  bf16x8 Qb[2][2];  // [qb][ds]
+  {
+    const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (rowbase + q0) * HD;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int ds = 0; ds < 2; ++ds)
+        Qb[qb][ds] = *reinterpret_cast<const bf16x8*>(qg + (qb * 16 + r16) * HD + ds * 32 + g * 8);
+  }
+
+  f32x4 Oacc[4][2];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) Oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};
+  float l[2] = {0.f, 0.f};  // fp32 row sums (per lane: its 16 keys of each tile), for the LSE
+  f32x4 Lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};  // sums of the bf16 weights
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = static_cast<__bf16>(1.0f);
+
+  // ---- DMA addressing: uniform tile bases, per-lane constant offsets ------
+  // Wave w stages K rows and V^T rows 16w .. 16w+15 of a tile, 8 rows (1 KB)
+  // per instruction, XOR-swizzled by choosing each lane's source chunk.
+  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + rowbase * HD * 2;
+  const uint8_t* vg = static_cast<const uint8_t*>(p.vt) + static_cast<size_t>(bh) * HD * p.Tpad * 2;
+  const int32_t* kig = p.k_idx + rowbase;
+  const int32_t* kbg = HASH ? p.k_bkt + rowbase : nullptr;
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * w + 8 * i + (lane >> 3), cp = lane & 7;
+    koff[i] = row * 128 + ((cp ^ swz_k(row)) * 16);
+    voff[i] = row * p.Tpad * 2 + ((cp ^ (row & 7)) * 16);
+  }
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t ldsp = lds_addr(&Kp[0][0]), ldsb = lds_addr(&Kb[0][0]);
+  auto stage_tile = [&](int j, int s) {
+    const uint8_t* kt = kg + static_cast<size_t>(j) * TB;
+    const uint8_t* vt = vg + static_cast<size_t>(j) * BN * 2;
+    const uint32_t ks = lds0 + s * TB + ws * 2048, vs = lds0 + (2 + s) * TB + ws * 2048;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      dma16(kt, koff[i], ks + i * 1024);
+      dma16(vt, voff[i], vs + i * 1024);
+    }
+    if (ws == 0) dma4(kig + j * BN, lane * 4, ldsp + s * BN * 4);
+    else if (HASH && ws == 1) dma4(kbg + j * BN, lane * 4, ldsb + s * BN * 4);
+  };
+
+  auto next_tile = [&](int j) {
+    while (j < rng.y && kst[j].x > qs.y) ++j;  // causal extremum test (hash ranges)
+    return j;
+  };
+
+  int j = next_tile(rng.x);
+  if (j < rng.y) {
+    stage_tile(j, 0);
+    dma_wait();
+  }
+  __syncthreads();
+  int s = 0;
+  int4 ks_cur = kst[min(j, p.nKt - 1)];
+  while (j < rng.y) {
+    const int jn = next_tile(j + 1);
+    // the next tile's statistics are loaded before its DMA is issued, so
+    // that waiting for them never waits for the DMA
+    const int4 ks = ks_cur;
+    ks_cur = kst[min(jn, p.nKt - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    if (jn < rng.y) stage_tile(jn, s ^ 1);
+
+    if (!tile_empty_for<HASH>(ks, wr)) {
+      const uint8_t* Ks = smem + s * TB;
+      const uint8_t* Vs = smem + (2 + s) * TB;
+      // -- S^T = K Q^T ------------------------------------------------------
+      f32x4 S[4][2];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int row = key_row(kb, r16);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[row * HD * 2 + (((ds * 4 + g) ^ swz_k(row)) * 16)]);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Qb[qb][ds], S[kb][qb], 0, 0, 0);
+        }
+      if (!tile_full_for<HASH>(ks, wr, j, p.Tk)) apply_mask<HASH>(S, Kp[s], Kb[s], qpos, qbkt, g);
+
+      // -- online softmax, lazy reference max ---------------------------------
+      float mxs[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) mxs[qb] = row_max_scaled(S, qb, p.c);
+      if (__ballot(mxs[0] > m[0] + kLazy || mxs[1] > m[1] + kLazy)) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float mnew = fmaxf(m[qb], mxs[qb]);
+          const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+          const float alpha = __builtin_amdgcn_exp2f(m[qb] - muse);  // 1 when unchanged, 0 from -inf
+          m[qb] = mnew;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) Oacc[db][qb] *= alpha;
+          Lacc[qb] *= alpha;
+          l[qb] *= alpha;
+        }
+      }
+      bf16x8 P[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float muse = (m[qb] == -INFINITY) ? 0.f : m[qb];
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][e], p.c, -muse));
+            S[kb][qb][e] = pv;
+            ls += pv;
+          }
+        l[qb] += ls;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) P[qb][kc] = pack_bf16x8(S[2 * kc][qb], S[2 * kc + 1][qb]);
+      }
+
+      // -- O^T += V^T P^T; row sums of the rounded weights ---------------------
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const int d = db * 16 + r16;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vs[d * BN * 2 + (((kc * 4 + g) ^ (d & 7)) * 16)]);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, P[qb][kc], Oacc[db][qb], 0, 0, 0);
+        }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          Lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, P[qb][kc], Lacc[qb], 0, 0, 0);
+    }
+
+    dma_wait();
+    __syncthreads();
+    s ^= 1;
+    j = jn;
+  }
+
+  // ---- epilogue --------------------------------------------------------------
+  float inv[2], lse[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float lt = l[qb] + __shfl_xor(l[qb], 16);
+    lt = lt + __shfl_xor(lt, 32);
+    const float lo = Lacc[qb][0];  // every row of the ones product holds the full sum
+    inv[qb] = lo > 0.f ? 1.f / lo : 0.f;
+    const float muse = (m[qb] == -INFINITY) ? 0.f : m[qb];
+    lse[qb] = lt > 0.f ? (muse + log2f(lt)) * kLn2 : -INFINITY;
+  }
+  fwd_epilogue<ZERO_DROPPED, TOUT>(p, reinterpret_cast<TOUT*>(smem), Qi, Oacc, inv, lse, qpos, qt, bh, rowbase);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs: v_mfma_f32_16x16x4_f32, single-buffered LDS, same layout.
+// ---------------------------------------------------------------------------
+template <bool HASH, bool ZERO_DROPPED, typename TOUT>
+__global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
+  constexpr int ESZ = 4, CH = 16;
+  constexpr int TB = BN * HD * ESZ;     // 16 KB
+  constexpr int LOADS = TB / 16 / 256;  // 4
+  __shared__ __align__(16) uint8_t smem[2 * TB];
+  uint8_t* Ks = smem;
+  uint8_t* Vs = smem + TB;
+  static_assert(2 * TB >= BM * HD * sizeof(TOUT), "output staging does not fit");
+  __shared__ __align__(16) int32_t Kp[BN];
+  __shared__ __align__(16) int32_t Kb[BN];
+  __shared__ int32_t Qi[BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  int qt, bh;
+  pick_work(p, qt, bh);
+  const size_t rowbase = static_cast<size_t>(bh) * p.Tpad;
+  const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
+  const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
+  const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
+  if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];
+
+  const int q0 = qt * BM + w * 32;
+  int qpos[2], qbkt[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = q0 + qb * 16 + r16;
+    qpos[qb] = p.q_idx[rowbase + row];
+    qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
+  }
+  const WaveRows wr = wave_rows(qpos, qbkt);
+  float Qf[2][16];  // [qb][t], d = 16g + t
+  {
+    const float* qg = static_cast<const float*>(p.q) + (rowbase + q0) * HD;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const float4 v = *reinterpret_cast<const float4*>(qg + (qb * 16 + r16) * HD + 16 * g + 4 * t4);
+        Qf[qb][4 * t4 + 0] = v.x;
+        Qf[qb][4 * t4 + 1] = v.y;
+        Qf[qb][4 * t4 + 2] = v.z;
+        Qf[qb][4 * t4 + 3] = v.w;
+      }
+  }
+
+  f32x4 Oacc[4][2];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) Oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};
+  float l[2] = {0.f, 0.f};
+
+  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + rowbase * HD * ESZ;
+  const uint8_t* vg = static_cast<const uint8_t*>(p.vt) + static_cast<size_t>(bh) * HD * p.Tpad * ESZ;
+  const int32_t* kig = p.k_idx + rowbase;
+  const int32_t* kbg = HASH ? p.k_bkt + rowbase : nullptr;
+  TileRegs<LOADS> tr;
+
+  for (int j = rng.x; j < rng.y; ++j) {
+    if (kst[j].x > qs.y) continue;  // causal extremum test (uniform)
+    tile_load<HASH, ESZ, CH, LOADS>(tr, kg, vg, kig, kbg, p.Tpad, j, tid);
+    __syncthreads();  // previous tile no longer read
+    tile_store<HASH, ESZ, CH, LOADS>(tr, Ks, Vs, Kp, Kb, tid);
+    __syncthreads();
+    if (tile_empty_for<HASH>(kst[j], wr)) continue;
+
+    f32x4 S[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int row = key_row(kb, r16);
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const float4 a = *reinterpret_cast<const float4*>(&Ks[row * HD * 4 + (((4 * g + t4) ^ swz_k(row)) * 16)]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, Qf[qb][4 * t4 + 0], S[kb][qb], 0, 0, 0);
+          S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, Qf[qb][4 * t4 + 1], S[kb][qb], 0, 0, 0);
+          S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, Qf[qb][4 * t4 + 2], S[kb][qb], 0, 0, 0);
+          S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, Qf[qb][4 * t4 + 3], S[kb][qb], 0, 0, 0);
+        }
+      }
+    }
+    if (!tile_full_for<HASH>(kst[j], wr, j, p.Tk)) apply_mask<HASH>(S, Kp, Kb, qpos, qbkt, g);
+
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mnew = fmaxf(m[qb], row_max_scaled(S, qb, p.c));
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(m[qb] - muse);
+      m[qb] = mnew;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][e], p.c, -muse));
+          S[kb][qb][e] = pv;
+          ls += pv;
+        }
+      l[qb] = l[qb] * alpha + ls;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) Oacc[db][qb] *= alpha;
+    }
+
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = db * 16 + r16;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int ch = 8 * (kb >> 1) + 2 * g + (kb & 1);  // keys 32kc + 8g + 4hb + 0..3
+        const float4 a = *reinterpret_cast<const float4*>(&Vs[d * BN * 4 + ((ch ^ (d & 7)) * 16)]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, S[kb][qb][0], Oacc[db][qb], 0, 0, 0);
+          Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, S[kb][qb][1], Oacc[db][qb], 0, 0, 0);
+          Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, S[kb][qb][2], Oacc[db][qb], 0, 0, 0);
+          Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, S[kb][qb][3], Oacc[db][qb], 0, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();  // LDS tiles no longer read: the epilogue reuses them
+
+  float inv[2], lse[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float lt = l[qb] + __shfl_xor(l[qb], 16);
+    lt = lt + __shfl_xor(lt, 32);
+    inv[qb] = lt > 0.f ? 1.f / lt : 0.f;
+    const float muse = (m[qb] == -INFINITY) ? 0.f : m[qb];
+    lse[qb] = lt > 0.f ? (muse + log2f(lt)) * kLn2 : -INFINITY;
+  }
+  fwd_epilogue<ZERO_DROPPED, TOUT>(p, reinterpret_cast<TOUT*>(smem), Qi, Oacc, inv, lse, qpos, qt, bh, rowbase);
 }
 
 template <bool HASH, bool ZD>
 int dispatch_fwd(int dtype_in, int dtype_out, const FwdParams& p, hipStream_t stream) {
+  const dim3 grid(p.nQt * p.B * p.H), block(256);
   if (dtype_in == SCFA_BF16) {
-    if (dtype_out == SCFA_F32) return launch_fwd<HASH, false, ZD, float>(p, stream);
-    return launch_fwd<HASH, false, ZD, uint16_t>(p, stream);
+    if (dtype_out == SCFA_F32) hipLaunchKernelGGL((k_fwd_bf16<HASH, ZD, float>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((k_fwd_bf16<HASH, ZD, uint16_t>), grid, block, 0, stream, p);
+  } else {
+    if (dtype_out == SCFA_F32) hipLaunchKernelGGL((k_fwd_f32<HASH, ZD, float>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((k_fwd_f32<HASH, ZD, uint16_t>), grid, block, 0, stream, p);
   }
-  if (dtype_out == SCFA_F32) return launch_fwd<HASH, true, ZD, float>(p, stream);
-  return launch_fwd<HASH, true, ZD, uint16_t>(p, stream);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
 }
 
 int check_common(int dtype_in, int dtype_out, int B, int H, int T, int D, float scale) {

@@ -136,12 +136,14 @@ __global__ __launch_bounds__(256) void k_qk_compact(const uint8_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// LSH bucket. One thread per token, one workgroup per (256 tokens, head):
-// R of the head sits in LDS as float64 and is read as a wave-wide broadcast.
-// Each thread reads its token's row with 16-byte loads. A product of a
-// bf16/fp32 input and an fp32 rotation is exact in float64, so a fused
-// multiply-add rounds exactly where a separate multiply and add would (only
-// at the sum): the accumulation matches the sequential definition
+// LSH bucket. One workgroup per (256 tokens, head), one wave per 64 tokens.
+// A wave first copies its 64 rows into LDS with coalesced 16-byte loads
+// (consecutive lanes read consecutive 16 bytes of a row), then each lane
+// accumulates its own token's projections; R of the head sits in LDS as
+// float64 and is read as a wave-wide broadcast. A product of a bf16/fp32
+// input and an fp32 rotation is exact in float64, so a fused multiply-add
+// rounds exactly where a separate multiply and add would (only at the sum):
+// the accumulation matches the sequential definition
 // c_j = ((0 + x_0 R_0j) + x_1 R_1j) + ... bit for bit.
 // ---------------------------------------------------------------------------
 
@@ -164,31 +166,40 @@ __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* __restrict__ x, 
                                                      int H, int32_t* __restrict__ bucket) {
   constexpr int D = 64;
   constexpr int EPU = 16 / sizeof(TIN);  // elements per 16-byte unit
-  constexpr int NU = D / EPU;            // units per row
+  constexpr int NU = D / EPU;            // units per row (8 bf16, 16 fp32)
+  constexpr int RPI = 64 / NU;           // rows per wave-wide load
+  constexpr int LDW = NU * 4 + 4;        // LDS row stride in 32-bit words (+16 bytes)
   __shared__ double Rs[D * HALF];
+  __shared__ __align__(16) uint32_t xs[4][64 * LDW];
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < D * HALF; i += 256) Rs[i] = static_cast<double>(R[static_cast<size_t>(h) * D * HALF + i]);
-  __syncthreads();
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= T) return;
-  const u32x4* row = reinterpret_cast<const u32x4*>(x + ((static_cast<size_t>(b) * T + t) * H + h) * D);
-  u32x4 u[NU];
+  const int tw = blockIdx.x * 256 + w * 64;  // first token of this wave
 #pragma unroll
-  for (int i = 0; i < NU; ++i) u[i] = row[i];
+  for (int k = 0; k < 64 / RPI; ++k) {
+    const int row = k * RPI + lane / NU, unit = lane % NU;
+    const int t = min(tw + row, T - 1);
+    const u32x4 v = reinterpret_cast<const u32x4*>(x + ((static_cast<size_t>(b) * T + t) * H + h) * D)[unit];
+    *reinterpret_cast<u32x4*>(&xs[w][row * LDW + unit * 4]) = v;
+  }
+  __syncthreads();
   double c[HALF];
 #pragma unroll
   for (int j = 0; j < HALF; ++j) c[j] = 0.0;
-#pragma unroll
+#pragma unroll 2
   for (int i = 0; i < NU; ++i) {
+    const u32x4 u = *reinterpret_cast<const u32x4*>(&xs[w][lane * LDW + i * 4]);
 #pragma unroll
     for (int e = 0; e < EPU; ++e) {
       const int d = i * EPU + e;
-      const double xd = static_cast<double>(unit_elem<TIN>(u[i], e));
+      const double xd = static_cast<double>(unit_elem<TIN>(u, e));
 #pragma unroll
       for (int j = 0; j < HALF; ++j) c[j] = fma(xd, Rs[d * HALF + j], c[j]);
     }
   }
+  const int t = tw + lane;
+  if (t >= T) return;
   // argmax over [c ; -c], first index on ties: the positive half comes first.
   int bp = 0, bn = 0;
   double vp = c[0], vn = -c[0];
@@ -429,63 +440,133 @@ __global__ __launch_bounds__(64) void k_tile_stats(int mode, const int32_t* __re
   }
 }
 
-// One wave per query tile; lanes scan the key tiles 64 at a time.
+// One wave per query tile; lane l holds key tiles l, l+64, ... in registers
+// (all loads issued up front), the scans are wave ballots.
 // QK / dense (Algorithm 1): end = number of key tiles whose smallest
 // position is <= the query tile's largest position (a prefix, since key
 // positions ascend). Hash (Algorithm 2): start = key tiles whose largest
 // bucket is below the query tile's smallest bucket; provisional stop = first
 // tile at/after start whose smallest bucket exceeds the query tile's largest;
 // end = one past the last tile in [start, stop) passing the causal test.
-__global__ __launch_bounds__(256) void k_fwd_table(int mode, const int32_t* __restrict__ qstats,
-                                                   const int32_t* __restrict__ kstats, int nQt, int nKt,
-                                                   int32_t* __restrict__ fwd, int32_t* __restrict__ tiles) {
-  const int bh = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (i >= nQt) return;
+constexpr int kTabRegChunks = 8;  // register path for up to 512 tiles
+
+// One query tile's range [start, end) and processed-tile count (one wave).
+__device__ void fwd_table_row(int mode, const int32_t* __restrict__ qstats, const int32_t* __restrict__ kstats,
+                              int nQt, int nKt, int32_t* __restrict__ fwd, int bh, int i, int lane,
+                              int32_t& cnt_out) {
   const int4 qs = reinterpret_cast<const int4*>(qstats)[static_cast<size_t>(bh) * nQt + i];
   const int4* ks = reinterpret_cast<const int4*>(kstats) + static_cast<size_t>(bh) * nKt;
+  const int nch = (nKt + 63) / 64;
+  // per chunk: a = tile below the query buckets, e = tile above them, c = causal test passes
+  uint64_t A[kTabRegChunks], E[kTabRegChunks], C[kTabRegChunks];
+  auto chunk_masks = [&](int ch, uint64_t& a, uint64_t& e, uint64_t& c) {
+    const int j = ch * 64 + lane;
+    int4 k = make_int4(kInt32Max, kInt32Max, kInt32Max, kInt32Max);
+    if (j < nKt) k = ks[j];
+    a = __ballot(j < nKt && k.w < qs.z);
+    e = __ballot(j < nKt && k.z > qs.w);
+    c = __ballot(j < nKt && k.x <= qs.y);
+  };
   int start = 0, end = 0, cnt = 0;
-  if (mode != SCFA_HASH) {
-    for (int j0 = 0; j0 < nKt; j0 += 64) {
-      const int j = j0 + lane;
-      cnt += __popcll(__ballot(j < nKt && ks[j].x <= qs.y));
-    }
-    end = cnt;
-  } else {
-    // start: tiles entirely below the query tile's smallest bucket
-    for (int j0 = 0; j0 < nKt; j0 += 64) {
-      const int j = j0 + lane;
-      start += __popcll(__ballot(j < nKt && ks[j].w < qs.z));
-    }
-    // provisional stop: first tile >= start with smallest bucket > largest query bucket
-    int eh = nKt;
-    for (int j0 = start & ~63; j0 < nKt; j0 += 64) {
-      const int j = j0 + lane;
-      const uint64_t m = __ballot(j >= start && j < nKt && ks[j].z > qs.w);
-      if (m) {
-        eh = j0 + __ffsll(static_cast<long long>(m)) - 1;
-        break;
+  if (nch <= kTabRegChunks) {
+#pragma unroll
+    for (int ch = 0; ch < kTabRegChunks; ++ch)
+      if (ch < nch) chunk_masks(ch, A[ch], E[ch], C[ch]);
+    if (mode != SCFA_HASH) {
+#pragma unroll
+      for (int ch = 0; ch < kTabRegChunks; ++ch)
+        if (ch < nch) cnt += __popcll(C[ch]);
+      end = cnt;
+    } else {
+#pragma unroll
+      for (int ch = 0; ch < kTabRegChunks; ++ch)
+        if (ch < nch) start += __popcll(A[ch]);
+      // bits of the tiles j >= start / j < stop within chunk ch
+      auto from = [](int s, int j0) {
+        return s <= j0 ? ~0ull : (s >= j0 + 64 ? 0ull : (~0ull << (s - j0)));
+      };
+      int eh = nKt;
+#pragma unroll
+      for (int ch = 0; ch < kTabRegChunks; ++ch) {
+        const uint64_t m = E[ch] & from(start, ch * 64);
+        if (ch < nch && eh == nKt && m) eh = ch * 64 + __ffsll(static_cast<long long>(m)) - 1;
+      }
+      end = start;
+#pragma unroll
+      for (int ch = 0; ch < kTabRegChunks; ++ch) {
+        if (ch < nch) {
+          const int j0 = ch * 64;
+          // tiles j in [start, eh) of this chunk
+          const uint64_t m = C[ch] & from(start, j0) & ~from(eh, j0);
+          if (m) {
+            end = j0 + 64 - __clzll(static_cast<long long>(m));
+            cnt += __popcll(m);
+          }
+        }
       }
     }
-    // refined stop and processed count: tiles in [start, eh) passing the causal test
-    end = start;
-    for (int j0 = start & ~63; j0 < eh; j0 += 64) {
-      const int j = j0 + lane;
-      const uint64_t m = __ballot(j >= start && j < eh && ks[j].x <= qs.y);
-      if (m) {
-        end = j0 + 64 - __clzll(static_cast<long long>(m));
-        cnt += __popcll(m);
+  } else {
+    // long sequences: the same scans, one chunk of 64 tiles at a time
+    for (int ch = 0; ch < nch; ++ch) {
+      uint64_t a, e, c;
+      chunk_masks(ch, a, e, c);
+      start += __popcll(a);
+      if (mode != SCFA_HASH) cnt += __popcll(c);
+    }
+    if (mode != SCFA_HASH) {
+      start = 0;
+      end = cnt;
+    } else {
+      int eh = nKt;
+      for (int j0 = start & ~63; j0 < nKt; j0 += 64) {
+        const int j = j0 + lane;
+        const uint64_t m = __ballot(j >= start && j < nKt && ks[j].z > qs.w);
+        if (m) {
+          eh = j0 + __ffsll(static_cast<long long>(m)) - 1;
+          break;
+        }
+      }
+      end = start;
+      for (int j0 = start & ~63; j0 < eh; j0 += 64) {
+        const int j = j0 + lane;
+        const uint64_t m = __ballot(j >= start && j < eh && ks[j].x <= qs.y);
+        if (m) {
+          end = j0 + 64 - __clzll(static_cast<long long>(m));
+          cnt += __popcll(m);
+        }
       }
     }
   }
   if (lane == 0) {
     reinterpret_cast<int2*>(fwd)[static_cast<size_t>(bh) * nQt + i] = make_int2(start, end);
-    if (cnt) atomicAdd(&tiles[bh], cnt);
+    cnt_out = cnt;
   }
 }
 
-// One wave per key tile: first and last query tile that processes it.
+// 16 waves per workgroup; their processed-tile counts are summed in LDS and
+// added to the head's total with one atomic per workgroup.
+constexpr int kTabWaves = 16;
+
+__global__ __launch_bounds__(64 * kTabWaves) void k_fwd_table(int mode, const int32_t* __restrict__ qstats,
+                                                              const int32_t* __restrict__ kstats, int nQt, int nKt,
+                                                              int32_t* __restrict__ fwd, int32_t* __restrict__ tiles) {
+  __shared__ int32_t wcnt[kTabWaves];
+  const int bh = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = blockIdx.x * kTabWaves + w;
+  if (lane == 0) wcnt[w] = 0;
+  if (i < nQt) fwd_table_row(mode, qstats, kstats, nQt, nKt, fwd, bh, i, lane, wcnt[w]);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < kTabWaves; ++k) sum += wcnt[k];
+    if (sum) atomicAdd(&tiles[bh], sum);
+  }
+}
+
+// One wave per key tile: first and last query tile that processes it. Lane l
+// holds query tiles l, l+64, ... (loads issued up front).
 __global__ __launch_bounds__(256) void k_bwd_table(const int32_t* __restrict__ qstats, const int32_t* __restrict__ kstats,
                                                    const int32_t* __restrict__ fwd, int nQt, int nKt,
                                                    int32_t* __restrict__ bwd) {
@@ -496,19 +577,33 @@ __global__ __launch_bounds__(256) void k_bwd_table(const int32_t* __restrict__ q
   const int kmin = reinterpret_cast<const int4*>(kstats)[static_cast<size_t>(bh) * nKt + j].x;
   const int4* qs = reinterpret_cast<const int4*>(qstats) + static_cast<size_t>(bh) * nQt;
   const int2* ft = reinterpret_cast<const int2*>(fwd) + static_cast<size_t>(bh) * nQt;
-  int first = -1, last = -1;
-  for (int i0 = 0; i0 < nQt; i0 += 64) {
-    const int i = i0 + lane;
+  const int nch = (nQt + 63) / 64;
+  auto hit_mask = [&](int ch) {
+    const int i = ch * 64 + lane;
     bool hit = false;
     if (i < nQt) {
       const int2 r = ft[i];
       hit = j >= r.x && j < r.y && kmin <= qs[i].y;
     }
-    const uint64_t m = __ballot(hit);
+    return __ballot(hit);
+  };
+  int first = -1, last = -1;
+  auto take = [&](int ch, uint64_t m) {
     if (m) {
-      if (first < 0) first = i0 + __ffsll(static_cast<long long>(m)) - 1;
-      last = i0 + 63 - __clzll(static_cast<long long>(m));
+      if (first < 0) first = ch * 64 + __ffsll(static_cast<long long>(m)) - 1;
+      last = ch * 64 + 63 - __clzll(static_cast<long long>(m));
     }
+  };
+  if (nch <= kTabRegChunks) {
+    uint64_t M[kTabRegChunks];
+#pragma unroll
+    for (int ch = 0; ch < kTabRegChunks; ++ch)
+      if (ch < nch) M[ch] = hit_mask(ch);
+#pragma unroll
+    for (int ch = 0; ch < kTabRegChunks; ++ch)
+      if (ch < nch) take(ch, M[ch]);
+  } else {
+    for (int ch = 0; ch < nch; ++ch) take(ch, hit_mask(ch));
   }
   if (lane == 0)
     reinterpret_cast<int2*>(bwd)[static_cast<size_t>(bh) * nKt + j] =
@@ -791,8 +886,8 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
   hipLaunchKernelGGL(k_tile_stats, dim3(nQt + nKt, B * H), dim3(64), 0, stream, mode, q_idx, k_idx, q_bkt, k_bkt, Tq,
                      Tk, TqP, TkP, Bm, Bn, nQt, nKt, qstats, kstats, tiles);
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_fwd_table, dim3(ceil_div(nQt, 4), B * H), dim3(256), 0, stream, mode, qstats, kstats, nQt, nKt,
-                     fwd_tab, tiles);
+  hipLaunchKernelGGL(k_fwd_table, dim3(ceil_div(nQt, kTabWaves), B * H), dim3(64 * kTabWaves), 0, stream, mode, qstats,
+                     kstats, nQt, nKt, fwd_tab, tiles);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   hipLaunchKernelGGL(k_bwd_table, dim3(ceil_div(nKt, 4), B * H), dim3(256), 0, stream, qstats, kstats, fwd_tab, nQt,
                      nKt, bwd_tab);

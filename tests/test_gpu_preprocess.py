@@ -157,6 +157,25 @@ def test_tables_any_tile_size(Bm, Bn):
     assert np.array_equal(t[4].cpu().numpy(), ref["tiles"])
 
 
+@pytest.mark.parametrize("mode", ["hash", "qk"])
+def test_tables_more_than_512_tiles(mode):
+    """More than 512 tiles per head on both sides: the table kernels' chunked
+    loop (instead of the register path) against the oracle, plus the launch
+    order."""
+    need_gpu()
+    announce(f"tables >512 tiles {mode}")
+    w = small(mode, 1, 2, 9000, nb=16, keep_p=0.95, seed=43)
+    x = make_inputs(w)
+    g = to_dev(x)
+    pre = (scfa.prepare_hash(g["q"], g["k"], g["v"], g["R"], w.nb) if mode == "hash"
+           else scfa.prepare_qk(g["q"], g["k"], g["v"], g["keep_q"], g["keep_k"]))
+    tab = scfa.build_tables(pre, 16, 16)
+    torch.cuda.synchronize()
+    assert tab.fwd.shape[2] > 512 and tab.bwd.shape[2] > 512
+    ref = _tables_match(mode, pre, tab, pre.Tq, 16, 16, pre.q_bkt, pre.k_bkt)
+    assert ref["tiles"].sum() > 0
+
+
 def test_device_error_flags():
     """Data errors only the device sees set dev_err (no host sync needed)."""
     need_gpu()
