@@ -180,7 +180,7 @@ def main():
     flops = 4 * w.D * pairs
     fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
     step_tflops = flops / (ms_step * 1e-3) / 1e12
-    nQt, nKt = plan.Tpad // scfa.SCFA_TILE_M, plan.Tpad // scfa.SCFA_TILE_N
+    nQt, nKt = plan.tab.fwd.shape[2], plan.tab.bwd.shape[2]
     esz = 2 if dtype == torch.bfloat16 else 4
     out_esz = 4
     BHT = w.B * w.H * w.T

@@ -51,6 +51,7 @@ extern "C" {
 /* ---- device error bits (OR-ed into *dev_err) -------------------------- */
 #define SCFA_DEVERR_COUNT_EXCEEDS_TC 1 /* a head keeps more tokens than Tc     */
 #define SCFA_DEVERR_BUCKET_RANGE 2     /* a bucket id outside [0, nb)           */
+#define SCFA_DEVERR_SEGMENT_OVERFLOW 4 /* a bucket-aligned layout exceeds Tseg  */
 
 /* ---- enums ------------------------------------------------------------- */
 #define SCFA_BF16 0 /* bfloat16 storage, fp32 accumulation */
@@ -143,6 +144,30 @@ size_t scfa_hash_sort_workspace_bytes(int B, int H, int T, int nb);
 int scfa_hash_sort(const int32_t* bucket, int B, int H, int T, int nb, int32_t pad_idx, int32_t* perm,
                    int32_t* bucket_sorted, int32_t* offsets, void* workspace, size_t workspace_bytes,
                    int32_t* dev_err, hipStream_t stream);
+
+/* Bucket-aligned layout of a sorted head. Same rows in the same order as
+ * the stable sort, with pad rows inserted so that every bucket starts at a
+ * multiple of `align`: tiles of `align` rows (the attention tiles) never hold
+ * two buckets. This is a storage layout of the sorted order of "Hash-Sparse
+ * Attention: Sorting by Bucket and Two-Dimensional Tiling" (SCFA explainer,
+ * 3.4); it changes no result.
+ *  perm, offsets  from scfa_hash_sort (perm has SCFA_PAD(T) rows per head).
+ *  align          16, 32, 64 or 128.
+ *  Tseg           rows per head of the outputs, a multiple of SCFA_ROW_ALIGN;
+ *                 scfa_hash_segment_rows(T, nb, align) always suffices (a
+ *                 smaller Tseg that a head overflows sets SEGMENT_OVERFLOW).
+ *  idx_seg out (B, H, Tseg): bucket v's rows start at A_v = sum over u < v of
+ *                 ceil(n_u / align) * align and hold perm[offsets[v] + r];
+ *                 the rest of each segment holds pad_idx; rows from A_nb on
+ *                 hold pad_idx.
+ *  bkt_seg out (B, H, Tseg): v on the rows of segment v (pads included), nb
+ *                 on the rows from A_nb on.
+ *  seg_offsets out (B, H, nb+1) int32: A.                                    */
+int scfa_hash_segment_rows(int T, int nb, int align);
+
+int scfa_hash_segments(const int32_t* perm, const int32_t* offsets, int B, int H, int T, int nb, int align,
+                       int32_t pad_idx, int Tseg, int32_t* idx_seg, int32_t* bkt_seg, int32_t* seg_offsets,
+                       int32_t* dev_err, hipStream_t stream);
 
 /* Gather rows into head-major order: out row r of head (b, h) is
  * x[b, idx[b,h,r], h, :] when 0 <= idx < T, else zero.
@@ -240,10 +265,16 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
                        const int32_t* fwd_tab, const int32_t* order, int B, int H, int T, int Tc, int D, float scale,
                        void* O, float* lse, hipStream_t stream);
 
+/* Hash-sparse: as above, with the sorted (or bucket-aligned) operands and
+ *  q_bkt, k_bkt  sorted bucket ids of the rows;
+ *  Tq, Tk        query / key rows as passed to scfa_range_table (T for the
+ *                sorted order, Tseg for the bucket-aligned layout); the
+ *                buffers hold SCFA_PAD(Tq) / SCFA_PAD(Tk) rows per head.       */
 int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v_t,
                          const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
                          const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, const int32_t* order,
-                         int B, int H, int T, int D, float scale, void* O, float* lse, hipStream_t stream);
+                         int B, int H, int T, int Tq, int Tk, int D, float scale, void* O, float* lse,
+                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Backward attention (recomputation from the saved LSE).
@@ -262,20 +293,22 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
  *                exactly the operands and tables of the forward call.
  *  O             (B, T, H, D) fp32 forward output;  lse (B, H, T) fp32.
  *  dO            (B, T, H, D) upstream gradient, dtype_in.
- *  T             original sequence length; Tq valid rows (Tc for QK,
- *                T for hash).
+ *  T             original sequence length; Tq, Tk query / key rows as
+ *                passed to scfa_range_table (Tc and Tc for QK; T and T for the
+ *                sorted hash order, Tseg_q and Tseg_k for the bucket-aligned
+ *                layout); the buffers hold SCFA_PAD(Tq) / SCFA_PAD(Tk) rows.
  *  dQ, dK, dV    out (B, T, H, D) fp32 in original order, every row
  *                written (zero for dropped tokens and tokens without any
  *                visible pair).
  *  workspace     device scratch of scfa_bwd_workspace_bytes() bytes (the
  *                transposed / re-laid-out operands, Delta and log2 LSE).
  * Launches 7 kernels on `stream`; no atomics, results are deterministic.  */
-size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int D);
+size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D);
 
 int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v_t, const int32_t* q_idx,
              const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
              const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
-             const void* dO, int B, int H, int T, int Tq, int D, float scale, float* dQ, float* dK, float* dV,
+             const void* dO, int B, int H, int T, int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV,
              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -64,8 +64,8 @@ struct BwdParams {
   float* dK;
   float* dV;
   int B, H, T;
-  int Tq;    // valid rows
-  int Tpad;  // rows of the sorted / compacted buffers
+  int Tq, Tk;    // valid query / key rows (as passed to the range table)
+  int TqP, TkP;  // rows per head of the query-side / key-side buffers
   int nQt, nKt;
   float c;      // scale * log2(e)
   float scale;  // score scale
@@ -276,18 +276,19 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
   int kt, bh;
   map_work(blockIdx.x, BH, p.nKt, kt, bh, false);  // early key tiles see the most queries
   const int b = bh / p.H, h = bh - b * p.H;
-  const size_t rowbase = static_cast<size_t>(bh) * p.Tpad;
-  const size_t colbase = static_cast<size_t>(bh) * HD * p.Tpad;
+  const size_t rowbase = static_cast<size_t>(bh) * p.TqP;        // query side
+  const size_t colbase = static_cast<size_t>(bh) * HD * p.TqP;
+  const size_t kbase = static_cast<size_t>(bh) * p.TkP;          // key side
 
-  if (tid < BN) Ki[tid] = p.k_idx[rowbase + kt * BN + tid];
+  if (tid < BN) Ki[tid] = p.k_idx[kbase + kt * BN + tid];
   const int krow = kt * BN + w * 16 + r16;  // this lane's key
-  const int kpos = p.k_idx[rowbase + krow];
-  const int kbkt = HASH ? p.k_bkt[rowbase + krow] : 0;
+  const int kpos = p.k_idx[kbase + krow];
+  const int kbkt = HASH ? p.k_bkt[kbase + krow] : 0;
   bf16x8 Kb[2], Vb[2];
 #pragma unroll
   for (int ds = 0; ds < 2; ++ds) {
-    Kb[ds] = *reinterpret_cast<const bf16x8*>(p.k_s + (rowbase + krow) * HD + ds * 32 + g * 8);
-    Vb[ds] = *reinterpret_cast<const bf16x8*>(p.v_s + (rowbase + krow) * HD + ds * 32 + g * 8);
+    Kb[ds] = *reinterpret_cast<const bf16x8*>(p.k_s + (kbase + krow) * HD + ds * 32 + g * 8);
+    Vb[ds] = *reinterpret_cast<const bf16x8*>(p.v_s + (kbase + krow) * HD + ds * 32 + g * 8);
   }
   f32x4 dVa[4], dKa[4];
 #pragma unroll
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
   const int2 rng = p.bwd_tab[static_cast<size_t>(bh) * p.nKt + kt];
   const int4 ks = p.kstats[static_cast<size_t>(bh) * p.nKt + kt];
   const int4* qst = p.qstats + static_cast<size_t>(bh) * p.nQt;
-  const bool kfull = (kt + 1) * BN <= p.Tq;
+  const bool kfull = (kt + 1) * BN <= p.Tk;
 
   // chunk ci = 2 * query tile + half; skip tiles failing the causal test
   auto next_chunk = [&](int ci) {
@@ -311,9 +312,9 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
   auto load = [&](int ci) {
     const int q0 = ci * QC;
     rq = load_rows_tile(p.q_s + (rowbase + q0) * HD, tid);
-    rqt = load_cols_tile(p.q_t + colbase + q0, p.Tpad, tid);
+    rqt = load_cols_tile(p.q_t + colbase + q0, p.TqP, tid);
     rdo = load_rows_tile(p.do_s + (rowbase + q0) * HD, tid);
-    rdot = load_cols_tile(p.do_t + colbase + q0, p.Tpad, tid);
+    rdot = load_cols_tile(p.do_t + colbase + q0, p.TqP, tid);
     const int which = tid >> 6, r = tid & 63;
     if (which == 0) rsi = p.q_idx[rowbase + q0 + r];
     else if (which == 1) rsi = HASH ? p.q_bkt[rowbase + q0 + r] : 0;
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
   __syncthreads();
   write_rows(tk, Ki, BN, p.dK, p.T, p.H, b, h);
   write_rows(tv, Ki, BN, p.dV, p.T, p.H, b, h);
-  if constexpr (ZD) zero_unheld<BN>(p.k_idx + rowbase, Ki, kt, p.Tpad, p.T, p.H, b, h, p.dK, p.dV);
+  if constexpr (ZD) zero_unheld<BN>(p.k_idx + kbase, Ki, kt, p.TkP, p.T, p.H, b, h, p.dK, p.dV);
 }
 
 // ---------------------------------------------------------------------------
@@ -438,8 +439,9 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   int qt, bh;
   map_work(blockIdx.x, BH, p.nQt, qt, bh, true);
   const int b = bh / p.H, h = bh - b * p.H;
-  const size_t rowbase = static_cast<size_t>(bh) * p.Tpad;
-  const size_t colbase = static_cast<size_t>(bh) * HD * p.Tpad;
+  const size_t rowbase = static_cast<size_t>(bh) * p.TqP;        // query side
+  const size_t kbase = static_cast<size_t>(bh) * p.TkP;          // key side
+  const size_t kcolbase = static_cast<size_t>(bh) * HD * p.TkP;
   if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];
 
   const int q0 = qt * BM + w * 32;
@@ -476,11 +478,11 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   Tile2 rk, rv, rkt;
   int ri = 0;
   auto load = [&](int j) {
-    rk = load_rows_tile(p.k_s + (rowbase + j * BN) * HD, tid);
-    rv = load_rows_tile(p.v_s + (rowbase + j * BN) * HD, tid);
-    rkt = load_cols_tile(p.k_t + colbase + j * BN, p.Tpad, tid);
-    if (tid < BN) ri = p.k_idx[rowbase + j * BN + tid];
-    else if (HASH && tid < 2 * BN) ri = p.k_bkt[rowbase + j * BN + tid - BN];
+    rk = load_rows_tile(p.k_s + (kbase + j * BN) * HD, tid);
+    rv = load_rows_tile(p.v_s + (kbase + j * BN) * HD, tid);
+    rkt = load_cols_tile(p.k_t + kcolbase + j * BN, p.TkP, tid);
+    if (tid < BN) ri = p.k_idx[kbase + j * BN + tid];
+    else if (HASH && tid < 2 * BN) ri = p.k_bkt[kbase + j * BN + tid - BN];
   };
   auto store = [&](int s) {
     store_rows_tile(stage[s], rk, tid);
@@ -526,7 +528,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
         }
       }
     const int4 ks = kst[j];
-    bool full = qfull && ks.y <= qs.x && (j + 1) * BN <= p.Tq;
+    bool full = qfull && ks.y <= qs.x && (j + 1) * BN <= p.Tk;
     if (HASH) full = full && ks.z == ks.w && qs.z == qs.w && ks.z == qs.z;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -574,15 +576,19 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   }
   __syncthreads();
   write_rows(tq, Qi, BM, p.dQ, p.T, p.H, b, h);
-  if constexpr (ZD) zero_unheld<BM>(p.q_idx + rowbase, Qi, qt, p.Tpad, p.T, p.H, b, h, p.dQ, nullptr);
+  if constexpr (ZD) zero_unheld<BM>(p.q_idx + rowbase, Qi, qt, p.TqP, p.T, p.H, b, h, p.dQ, nullptr);
 }
 
-size_t ws_layout(int B, int H, int Tp, size_t off[8]) {
-  const size_t bf = static_cast<size_t>(B) * H * Tp * HD * 2;  // one bf16 (BH, Tp, D) tensor
-  const size_t f = static_cast<size_t>(B) * H * Tp * 4;
+// Workspace: v_s and k_t on the key side, q_t, do_s, do_t, lse2 and delta on
+// the query side.
+size_t ws_layout(int B, int H, int TqP, int TkP, size_t off[8]) {
+  const size_t bfq = static_cast<size_t>(B) * H * TqP * HD * 2;  // one bf16 (BH, TqP, D) tensor
+  const size_t bfk = static_cast<size_t>(B) * H * TkP * HD * 2;
+  const size_t f = static_cast<size_t>(B) * H * TqP * 4;
   size_t o = 0;
   for (int i = 0; i < 5; ++i) {  // v_s, q_t, k_t, do_s, do_t
     off[i] = o;
+    const size_t bf = (i == 0 || i == 2) ? bfk : bfq;
     o += (bf + 255) & ~size_t(255);
   }
   off[5] = o;  // lse2
@@ -609,29 +615,29 @@ using namespace scfa;
 
 extern "C" {
 
-size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int D) {
-  if ((mode != SCFA_QK && mode != SCFA_HASH) || B < 1 || H < 1 || Tq < 1 || D != HD) return 0;
+size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D) {
+  if ((mode != SCFA_QK && mode != SCFA_HASH) || B < 1 || H < 1 || Tq < 1 || Tk < 1 || D != HD) return 0;
   size_t off[8];
-  return ws_layout(B, H, pad_rows(Tq), off);
+  return ws_layout(B, H, pad_rows(Tq), pad_rows(Tk), off);
 }
 
 int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v_t, const int32_t* q_idx,
              const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
              const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
-             const void* dO, int B, int H, int T, int Tq, int D, float scale, float* dQ, float* dK, float* dV,
+             const void* dO, int B, int H, int T, int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV,
              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (mode != SCFA_QK && mode != SCFA_HASH) return SCFA_ERR_INVALID;
   if (!q || !k || !v_t || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !bwd_tab || !O || !lse || !dO ||
       !dQ || !dK || !dV || !workspace)
     return SCFA_ERR_INVALID;
   if (mode == SCFA_HASH && (!q_bkt || !k_bkt)) return SCFA_ERR_INVALID;
-  if (B < 1 || H < 1 || T < 1 || Tq < 1 || !(scale > 0.f) || !isfinite(scale)) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || T < 1 || Tq < 1 || Tk < 1 || !(scale > 0.f) || !isfinite(scale)) return SCFA_ERR_INVALID;
   if (!dtype_ok(dtype_in)) return SCFA_ERR_INVALID;
   if (D != HD || dtype_in != SCFA_BF16) return SCFA_ERR_UNSUPPORTED;
-  if (mode == SCFA_QK && Tq % SCFA_ROW_ALIGN) return SCFA_ERR_INVALID;
-  const int Tp = pad_rows(Tq);
+  if (mode == SCFA_QK && (Tq % SCFA_ROW_ALIGN || Tk != Tq)) return SCFA_ERR_INVALID;
+  const int TqP = pad_rows(Tq), TkP = pad_rows(Tk);
   size_t off[8];
-  if (workspace_bytes < ws_layout(B, H, Tp, off)) return SCFA_ERR_INVALID;
+  if (workspace_bytes < ws_layout(B, H, TqP, TkP, off)) return SCFA_ERR_INVALID;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   BwdParams p{};
   p.q_s = static_cast<const uint16_t*>(q);
@@ -658,25 +664,30 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
   p.H = H;
   p.T = T;
   p.Tq = Tq;
-  p.Tpad = Tp;
-  p.nQt = Tp / BM;
-  p.nKt = Tp / BN;
+  p.Tk = Tk;
+  p.TqP = TqP;
+  p.TkP = TkP;
+  p.nQt = TqP / BM;
+  p.nKt = TkP / BN;
   p.c = scale * kLog2e;
   p.scale = scale;
   const int BH = B * H;
   // preparation: transposes / row copies of the sorted operands, dO, Delta, LSE
-  hipLaunchKernelGGL(k_transpose<false>, dim3(Tp / 64, BH), dim3(256), 0, stream, static_cast<const uint16_t*>(v_t),
-                     const_cast<uint16_t*>(p.v_s), Tp);
+  hipLaunchKernelGGL(k_transpose<false>, dim3(TkP / 64, BH), dim3(256), 0, stream, static_cast<const uint16_t*>(v_t),
+                     const_cast<uint16_t*>(p.v_s), TkP);
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_transpose<true>, dim3(Tp / 64, BH), dim3(256), 0, stream, p.q_s, const_cast<uint16_t*>(p.q_t), Tp);
+  hipLaunchKernelGGL(k_transpose<true>, dim3(TqP / 64, BH), dim3(256), 0, stream, p.q_s, const_cast<uint16_t*>(p.q_t),
+                     TqP);
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_transpose<true>, dim3(Tp / 64, BH), dim3(256), 0, stream, p.k_s, const_cast<uint16_t*>(p.k_t), Tp);
+  hipLaunchKernelGGL(k_transpose<true>, dim3(TkP / 64, BH), dim3(256), 0, stream, p.k_s, const_cast<uint16_t*>(p.k_t),
+                     TkP);
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_bwd_prep, dim3(Tp / 32, BH), dim3(256), 0, stream, static_cast<const uint16_t*>(dO), O, lse, q_idx,
-                     H, T, Tp, const_cast<uint16_t*>(p.do_s), const_cast<float*>(p.lse2), const_cast<float*>(p.delta));
+  hipLaunchKernelGGL(k_bwd_prep, dim3(TqP / 32, BH), dim3(256), 0, stream, static_cast<const uint16_t*>(dO), O, lse,
+                     q_idx, H, T, TqP, const_cast<uint16_t*>(p.do_s), const_cast<float*>(p.lse2),
+                     const_cast<float*>(p.delta));
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_transpose<true>, dim3(Tp / 64, BH), dim3(256), 0, stream, p.do_s, const_cast<uint16_t*>(p.do_t),
-                     Tp);
+  hipLaunchKernelGGL(k_transpose<true>, dim3(TqP / 64, BH), dim3(256), 0, stream, p.do_s, const_cast<uint16_t*>(p.do_t),
+                     TqP);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   if (mode == SCFA_HASH) return launch_bwd<true, false>(p, stream);
   return launch_bwd<false, true>(p, stream);

@@ -70,7 +70,8 @@ struct FwdParams {
   float* lse;
   int B, H, T;
   int Tk;    // valid key rows (extrema/ragged test)
-  int Tpad;  // rows of the compacted / sorted buffers
+  int TqPad;  // rows per head of the query-side buffers (q, q_idx, q_bkt)
+  int TkPad;  // rows per head of the key-side buffers (k, v_t columns, k_idx, k_bkt)
   int nQt, nKt;
   float c;  // scale * log2(e)
 };
@@ -282,7 +283,7 @@ __device__ inline void fwd_epilogue(const FwdParams& p, TOUT* ost, const int32_t
     int lo = 0, hi = -1;
     if (nreal > 0) {
       lo = qt == 0 ? 0 : max(0, p.q_idx[rowbase + qt * BM - 1] + 1);
-      const bool next_real = (qt + 1) * BM < p.Tpad && p.q_idx[rowbase + (qt + 1) * BM] >= 0;
+      const bool next_real = (qt + 1) * BM < p.TqPad && p.q_idx[rowbase + (qt + 1) * BM] >= 0;
       hi = next_real ? min(Qi[nreal - 1], p.T - 1) : p.T - 1;
     } else if (qt == 0) {
       lo = 0;
@@ -348,7 +349,8 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
   const int ws = __builtin_amdgcn_readfirstlane(w);
   int qt, bh;
   pick_work(p, qt, bh);
-  const size_t rowbase = static_cast<size_t>(bh) * p.Tpad;
+  const size_t rowbase = static_cast<size_t>(bh) * p.TqPad;  // query side
+  const size_t kbase = static_cast<size_t>(bh) * p.TkPad;    // key side
   const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
@@ -389,16 +391,16 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
   // ---- DMA addressing: uniform tile bases, per-lane constant offsets ------
   // Wave w stages K rows and V^T rows 16w .. 16w+15 of a tile, 8 rows (1 KB)
   // per instruction, XOR-swizzled by choosing each lane's source chunk.
-  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + rowbase * HD * 2;
-  const uint8_t* vg = static_cast<const uint8_t*>(p.vt) + static_cast<size_t>(bh) * HD * p.Tpad * 2;
-  const int32_t* kig = p.k_idx + rowbase;
-  const int32_t* kbg = HASH ? p.k_bkt + rowbase : nullptr;
+  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + kbase * HD * 2;
+  const uint8_t* vg = static_cast<const uint8_t*>(p.vt) + kbase * HD * 2;
+  const int32_t* kig = p.k_idx + kbase;
+  const int32_t* kbg = HASH ? p.k_bkt + kbase : nullptr;
   uint32_t koff[2], voff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 16 * w + 8 * i + (lane >> 3), cp = lane & 7;
     koff[i] = row * 128 + ((cp ^ swz_k(row)) * 16);
-    voff[i] = row * p.Tpad * 2 + ((cp ^ (row & 7)) * 16);
+    voff[i] = row * p.TkPad * 2 + ((cp ^ (row & 7)) * 16);
   }
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t ldsp = lds_addr(&Kp[0][0]), ldsb = lds_addr(&Kb[0][0]);
@@ -551,7 +553,8 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
   int qt, bh;
   pick_work(p, qt, bh);
-  const size_t rowbase = static_cast<size_t>(bh) * p.Tpad;
+  const size_t rowbase = static_cast<size_t>(bh) * p.TqPad;  // query side
+  const size_t kbase = static_cast<size_t>(bh) * p.TkPad;    // key side
   const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
@@ -589,15 +592,15 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
   float m[2] = {-INFINITY, -INFINITY};
   float l[2] = {0.f, 0.f};
 
-  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + rowbase * HD * ESZ;
-  const uint8_t* vg = static_cast<const uint8_t*>(p.vt) + static_cast<size_t>(bh) * HD * p.Tpad * ESZ;
-  const int32_t* kig = p.k_idx + rowbase;
-  const int32_t* kbg = HASH ? p.k_bkt + rowbase : nullptr;
+  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + kbase * HD * ESZ;
+  const uint8_t* vg = static_cast<const uint8_t*>(p.vt) + kbase * HD * ESZ;
+  const int32_t* kig = p.k_idx + kbase;
+  const int32_t* kbg = HASH ? p.k_bkt + kbase : nullptr;
   TileRegs<LOADS> tr;
 
   for (int j = rng.x; j < rng.y; ++j) {
     if (kst[j].x > qs.y) continue;  // causal extremum test (uniform)
-    tile_load<HASH, ESZ, CH, LOADS>(tr, kg, vg, kig, kbg, p.Tpad, j, tid);
+    tile_load<HASH, ESZ, CH, LOADS>(tr, kg, vg, kig, kbg, p.TkPad, j, tid);
     __syncthreads();  // previous tile no longer read
     tile_store<HASH, ESZ, CH, LOADS>(tr, Ks, Vs, Kp, Kb, tid);
     __syncthreads();
@@ -731,7 +734,8 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
   p.H = H;
   p.T = T;
   p.Tk = Tc;
-  p.Tpad = Tc;
+  p.TqPad = Tc;
+  p.TkPad = Tc;
   p.nQt = Tc / BM;
   p.nKt = Tc / BN;
   p.c = scale * 1.44269504088896340736f;
@@ -741,12 +745,13 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
 int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v_t,
                          const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
                          const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, const int32_t* order,
-                         int B, int H, int T, int D, float scale, void* O, float* lse, hipStream_t stream) {
+                         int B, int H, int T, int Tq, int Tk, int D, float scale, void* O, float* lse,
+                         hipStream_t stream) {
   if (!q || !k || !v_t || !q_idx || !k_idx || !q_bkt || !k_bkt || !qstats || !kstats || !fwd_tab || !O || !lse)
     return SCFA_ERR_INVALID;
   const int st = check_common(dtype_in, dtype_out, B, H, T, D, scale);
   if (st != SCFA_OK) return st;
-  const int Tp = pad_rows(T);
+  if (Tq < 1 || Tk < 1) return SCFA_ERR_INVALID;
   FwdParams p{};
   p.q = q;
   p.k = k;
@@ -764,10 +769,11 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
   p.B = B;
   p.H = H;
   p.T = T;
-  p.Tk = T;
-  p.Tpad = Tp;
-  p.nQt = Tp / BM;
-  p.nKt = Tp / BN;
+  p.Tk = Tk;
+  p.TqPad = pad_rows(Tq);
+  p.TkPad = pad_rows(Tk);
+  p.nQt = p.TqPad / BM;
+  p.nKt = p.TkPad / BN;
   p.c = scale * 1.44269504088896340736f;
   return dispatch_fwd<true, false>(dtype_in, dtype_out, p, stream);
 }

@@ -323,6 +323,63 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Bucket-aligned layout of a sorted head: bucket v starts at row
+// A_v = sum_{u<v} ceil(n_u / align) * align; its rows keep the sorted order,
+// the rest of its segment holds pad rows (bucket v), rows from A_nb on hold
+// pads with bucket nb. One thread per output row; wave 0 of each workgroup
+// derives A from the bucket offsets.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_hash_segments(const int32_t* __restrict__ perm,
+                                                       const int32_t* __restrict__ offsets, int Tp, int nb, int align,
+                                                       int32_t pad, int Tseg, int32_t* __restrict__ idx_seg,
+                                                       int32_t* __restrict__ bkt_seg, int32_t* __restrict__ seg_off,
+                                                       int32_t* dev_err) {
+  __shared__ int32_t off_s[65], aoff_s[65];
+  const int bh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {  // lane v < nb: bucket v (nb <= 64)
+    const int32_t* op = offsets + static_cast<size_t>(bh) * (nb + 1);
+    const int lo = lane < nb ? op[lane] : 0;
+    const int hi = lane < nb ? op[lane + 1] : lo;
+    const int m = ((hi - lo + align - 1) / align) * align;  // aligned rows of bucket `lane`
+    int x = m;  // inclusive scan over buckets
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    int32_t* so = seg_off + static_cast<size_t>(bh) * (nb + 1);
+    if (lane < nb) {
+      off_s[lane] = lo;
+      aoff_s[lane] = x - m;
+      if (blockIdx.x == 0) so[lane] = x - m;
+    }
+    if (lane == nb - 1) {  // end of the last bucket
+      off_s[nb] = hi;
+      aoff_s[nb] = x;
+      if (blockIdx.x == 0) so[nb] = x;
+      if (x > Tseg) set_dev_err(dev_err, SCFA_DEVERR_SEGMENT_OVERFLOW);
+    }
+  }
+  __syncthreads();
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= Tseg) return;
+  // bucket of row r: the last v with A_v <= r (empty buckets share a start)
+  int a = 0, z = nb;  // search v in [0, nb]
+  while (a < z) {
+    const int mid = (a + z + 1) >> 1;
+    if (aoff_s[mid] <= r) a = mid; else z = mid - 1;
+  }
+  int idx = pad, bkt = a;
+  if (a < nb) {
+    const int k = r - aoff_s[a];
+    if (k < off_s[a + 1] - off_s[a]) idx = perm[static_cast<size_t>(bh) * Tp + off_s[a] + k];
+  }
+  idx_seg[static_cast<size_t>(bh) * Tseg + r] = idx;
+  bkt_seg[static_cast<size_t>(bh) * Tseg + r] = bkt;
+}
+
+// ---------------------------------------------------------------------------
 // Gather into head-major order (rows or transposed columns).
 // ---------------------------------------------------------------------------
 
@@ -839,6 +896,27 @@ int scfa_hash_sort(const int32_t* bucket, int B, int H, int T, int nb, int32_t p
   SCFA_RETURN_IF_LAUNCH_FAILED();
   hipLaunchKernelGGL(k_sort_scatter, dim3(nCx, B * H), dim3(256), 0, stream, bucket, T, Tp, nb, nC, hist, pad_idx,
                      perm, bucket_sorted, offsets);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+int scfa_hash_segment_rows(int T, int nb, int align) {
+  if (T < 1 || nb < 1 || nb > 64 || !(align == 16 || align == 32 || align == 64 || align == 128)) return 0;
+  const long long n = static_cast<long long>(T) + static_cast<long long>(nb) * (align - 1);
+  if (n > (1ll << 30)) return 0;
+  return pad_rows(static_cast<int>(n));
+}
+
+int scfa_hash_segments(const int32_t* perm, const int32_t* offsets, int B, int H, int T, int nb, int align,
+                       int32_t pad_idx, int Tseg, int32_t* idx_seg, int32_t* bkt_seg, int32_t* seg_offsets,
+                       int32_t* dev_err, hipStream_t stream) {
+  if (!perm || !offsets || !idx_seg || !bkt_seg || !seg_offsets) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || T < 1 || nb < 1) return SCFA_ERR_INVALID;
+  if (nb > 64) return SCFA_ERR_UNSUPPORTED;
+  if (!(align == 16 || align == 32 || align == 64 || align == 128)) return SCFA_ERR_INVALID;
+  if (Tseg < SCFA_ROW_ALIGN || Tseg % SCFA_ROW_ALIGN || Tseg < T) return SCFA_ERR_INVALID;
+  hipLaunchKernelGGL(k_hash_segments, dim3(ceil_div(Tseg, 256), B * H), dim3(256), 0, stream, perm, offsets,
+                     pad_rows(T), nb, align, pad_idx, Tseg, idx_seg, bkt_seg, seg_offsets, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libscfa.so")
 
 SCFA_OK, SCFA_ERR_INVALID, SCFA_ERR_UNSUPPORTED, SCFA_ERR_HIP = 0, -1, -2, -3
-SCFA_DEVERR_COUNT_EXCEEDS_TC, SCFA_DEVERR_BUCKET_RANGE = 1, 2
+SCFA_DEVERR_COUNT_EXCEEDS_TC, SCFA_DEVERR_BUCKET_RANGE, SCFA_DEVERR_SEGMENT_OVERFLOW = 1, 2, 4
 SCFA_BF16, SCFA_F32 = 0, 1
 SCFA_DENSE, SCFA_QK, SCFA_HASH = 0, 1, 2
 SCFA_ROWS, SCFA_COLS = 0, 1
@@ -45,17 +45,19 @@ _SIGS = {
     "scfa_hash_bucket": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "scfa_hash_sort_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "scfa_hash_sort": (_i, [_vp, _i, _i, _i, _i, ctypes.c_int32, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "scfa_hash_segment_rows": (_i, [_i, _i, _i]),
+    "scfa_hash_segments": (_i, [_vp, _vp, _i, _i, _i, _i, _i, ctypes.c_int32, _i, _vp, _vp, _vp, _vp, _vp]),
     "scfa_gather": (_i, [_i, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "scfa_range_table": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_count_visible": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_work_order": (_i, [_vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_qk_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp,
                                 _vp, _vp]),
-    "scfa_hash_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f,
-                                  _vp, _vp, _vp]),
-    "scfa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "scfa_hash_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                  _i, _f, _vp, _vp, _vp]),
+    "scfa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "scfa_bwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
-                      _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
+                      _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 _LIB = None
@@ -166,6 +168,18 @@ def scfa_hash_sort(bucket, nb, pad_idx, perm, bucket_sorted, offsets, workspace,
                                 _stream(stream, bucket)), "scfa_hash_sort")
 
 
+def scfa_hash_segment_rows(T, nb, align) -> int:
+    return lib().scfa_hash_segment_rows(T, nb, align)
+
+
+def scfa_hash_segments(perm, offsets, T, nb, align, pad_idx, idx_seg, bkt_seg, seg_offsets, dev_err=None,
+                       stream=None):
+    B, H, Tseg = idx_seg.shape
+    _check(lib().scfa_hash_segments(_p(perm), _p(offsets), B, H, T, nb, align, pad_idx, Tseg, _p(idx_seg),
+                                    _p(bkt_seg), _p(seg_offsets), _p(dev_err), _stream(stream, perm)),
+           "scfa_hash_segments")
+
+
 def scfa_gather(x, idx, layout, x_p, stream=None):
     B, T, H, D = x.shape
     Tp = idx.shape[-1]
@@ -200,25 +214,28 @@ def scfa_qk_sparse_fwd(q_c, k_c, v_t, q_idx, k_idx, qstats, kstats, fwd_tab, T, 
 
 
 def scfa_hash_sparse_fwd(q_s, k_s, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, T, O, lse, scale=None,
-                         stream=None, order=None):
+                         stream=None, order=None, Tq=None, Tk=None):
+    """Tq / Tk: query / key rows as passed to the range table (default: T)."""
     B, H, Tp, D = q_s.shape
     scale = 1.0 / math.sqrt(D) if scale is None else scale
+    Tq = T if Tq is None else Tq
+    Tk = T if Tk is None else Tk
     _check(lib().scfa_hash_sparse_fwd(_dt(q_s), _dt(O), _p(q_s), _p(k_s), _p(v_t), _p(q_idx), _p(k_idx), _p(q_bkt),
-                                      _p(k_bkt), _p(qstats), _p(kstats), _p(fwd_tab), _p(order), B, H, T, D, scale,
-                                      _p(O), _p(lse), _stream(stream, q_s)), "scfa_hash_sparse_fwd")
+                                      _p(k_bkt), _p(qstats), _p(kstats), _p(fwd_tab), _p(order), B, H, T, Tq, Tk, D,
+                                      scale, _p(O), _p(lse), _stream(stream, q_s)), "scfa_hash_sparse_fwd")
 
 
-def scfa_bwd_workspace_bytes(mode, B, H, Tq, D=64) -> int:
-    return lib().scfa_bwd_workspace_bytes(mode, B, H, Tq, D)
+def scfa_bwd_workspace_bytes(mode, B, H, Tq, Tk, D=64) -> int:
+    return lib().scfa_bwd_workspace_bytes(mode, B, H, Tq, Tk, D)
 
 
-def scfa_bwd(mode, q, k, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, T, Tq, dQ, dK,
-             dV, workspace, scale=None, stream=None):
+def scfa_bwd(mode, q, k, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, T, Tq, Tk, dQ,
+             dK, dV, workspace, scale=None, stream=None):
     B, H, Tp, D = q.shape
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(lib().scfa_bwd(mode, _dt(q), _p(q), _p(k), _p(v_t), _p(q_idx), _p(k_idx), _p(q_bkt), _p(k_bkt), _p(qstats),
-                          _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(O), _p(lse), _p(dO), B, H, T, Tq, D, scale, _p(dQ),
-                          _p(dK), _p(dV), _p(workspace), workspace.numel() * workspace.element_size(),
+                          _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(O), _p(lse), _p(dO), B, H, T, Tq, Tk, D, scale,
+                          _p(dQ), _p(dK), _p(dV), _p(workspace), workspace.numel() * workspace.element_size(),
                           _stream(stream, q)), "scfa_bwd")
 
 
@@ -228,17 +245,20 @@ def scfa_bwd(mode, q, k, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_ta
 
 @dataclasses.dataclass
 class Prepared:
-    """Compacted / sorted operands of one attention call (head-major)."""
+    """Compacted / sorted operands of one attention call (head-major).
+
+    Tq, Tk are the query / key rows as passed to the range table; the buffers
+    hold pad_rows(Tq) / pad_rows(Tk) rows per head."""
     mode: str
     B: int
     H: int
     T: int
     D: int
-    Tq: int          # valid rows (Tc for QK, T otherwise)
-    Tpad: int        # rows of the buffers
-    q: torch.Tensor  # (B,H,Tpad,D) rows
-    k: torch.Tensor  # (B,H,Tpad,D) rows
-    v_t: torch.Tensor  # (B,H,D,Tpad) transposed
+    Tq: int
+    Tk: int
+    q: torch.Tensor  # (B,H,pad(Tq),D) rows
+    k: torch.Tensor  # (B,H,pad(Tk),D) rows
+    v_t: torch.Tensor  # (B,H,D,pad(Tk)) transposed
     q_idx: torch.Tensor
     k_idx: torch.Tensor
     q_bkt: Optional[torch.Tensor] = None
@@ -288,9 +308,11 @@ def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, stream=None) -
                     extra={"count_q": cq, "count_k": ck, "max_q": mq, "max_k": mk, "dev_err": dev_err})
 
 
-def prepare_hash(q, k, v, R, nb: int, stream=None) -> Prepared:
+def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None) -> Prepared:
     """Hash-sparse preprocessing: LSH buckets of Q and K, stable counting sort
-    per head, gathers of Q, K (rows) and V (transposed) into sorted order."""
+    per head, then (aligned=True) the bucket-aligned layout (query buckets
+    start at multiples of the query tile, key buckets at multiples of the key
+    tile), gathers of Q, K (rows) and V (transposed) into that order."""
     B, T, H, D = q.shape
     dev = q
     i32 = torch.int32
@@ -300,19 +322,31 @@ def prepare_hash(q, k, v, R, nb: int, stream=None) -> Prepared:
     scfa_hash_bucket(k, R, nb, bk, stream)
     ws = _empty((max(1, scfa_hash_sort_workspace_bytes(B, H, T, nb)),), torch.uint8, dev)
     dev_err = torch.zeros((1,), dtype=i32, device=q.device)
-    q_idx, k_idx = _empty((B, H, Tp), i32, dev), _empty((B, H, Tp), i32, dev)
-    q_bs, k_bs = _empty((B, H, Tp), i32, dev), _empty((B, H, Tp), i32, dev)
+    perm_q, perm_k = _empty((B, H, Tp), i32, dev), _empty((B, H, Tp), i32, dev)
+    bs_q, bs_k = _empty((B, H, Tp), i32, dev), _empty((B, H, Tp), i32, dev)
     offq, offk = _empty((B, H, nb + 1), i32, dev), _empty((B, H, nb + 1), i32, dev)
-    scfa_hash_sort(bq, nb, SCFA_Q_PAD, q_idx, q_bs, offq, ws, dev_err, stream)
-    scfa_hash_sort(bk, nb, SCFA_K_PAD, k_idx, k_bs, offk, ws, dev_err, stream)
-    q_s, k_s = _empty((B, H, Tp, D), q.dtype, dev), _empty((B, H, Tp, D), k.dtype, dev)
-    v_t = _empty((B, H, D, Tp), v.dtype, dev)
+    scfa_hash_sort(bq, nb, SCFA_Q_PAD, perm_q, bs_q, offq, ws, dev_err, stream)
+    scfa_hash_sort(bk, nb, SCFA_K_PAD, perm_k, bs_k, offk, ws, dev_err, stream)
+    extra = {"bucket_q": bq, "bucket_k": bk, "perm_q": perm_q, "perm_k": perm_k, "sorted_bkt_q": bs_q,
+             "sorted_bkt_k": bs_k, "offsets_q": offq, "offsets_k": offk, "dev_err": dev_err, "workspace": ws}
+    if aligned:
+        Tq = scfa_hash_segment_rows(T, nb, SCFA_TILE_M)
+        Tk = scfa_hash_segment_rows(T, nb, SCFA_TILE_N)
+        q_idx, q_bkt = _empty((B, H, Tq), i32, dev), _empty((B, H, Tq), i32, dev)
+        k_idx, k_bkt = _empty((B, H, Tk), i32, dev), _empty((B, H, Tk), i32, dev)
+        sq, sk = _empty((B, H, nb + 1), i32, dev), _empty((B, H, nb + 1), i32, dev)
+        scfa_hash_segments(perm_q, offq, T, nb, SCFA_TILE_M, SCFA_Q_PAD, q_idx, q_bkt, sq, dev_err, stream)
+        scfa_hash_segments(perm_k, offk, T, nb, SCFA_TILE_N, SCFA_K_PAD, k_idx, k_bkt, sk, dev_err, stream)
+        extra.update(seg_offsets_q=sq, seg_offsets_k=sk)
+    else:
+        Tq = Tk = T
+        q_idx, k_idx, q_bkt, k_bkt = perm_q, perm_k, bs_q, bs_k
+    q_s, k_s = _empty((B, H, pad_rows(Tq), D), q.dtype, dev), _empty((B, H, pad_rows(Tk), D), k.dtype, dev)
+    v_t = _empty((B, H, D, pad_rows(Tk)), v.dtype, dev)
     scfa_gather(q, q_idx, SCFA_ROWS, q_s, stream)
     scfa_gather(k, k_idx, SCFA_ROWS, k_s, stream)
     scfa_gather(v, k_idx, SCFA_COLS, v_t, stream)
-    return Prepared("hash", B, H, T, D, T, Tp, q_s, k_s, v_t, q_idx, k_idx, q_bs, k_bs,
-                    extra={"bucket_q": bq, "bucket_k": bk, "offsets_q": offq, "offsets_k": offk, "dev_err": dev_err,
-                           "workspace": ws})
+    return Prepared("hash", B, H, T, D, Tq, Tk, q_s, k_s, v_t, q_idx, k_idx, q_bkt, k_bkt, extra=extra)
 
 
 def prepare_dense(q, k, v, stream=None) -> Prepared:
@@ -331,18 +365,21 @@ def prepare_dense(q, k, v, stream=None) -> Prepared:
     return Prepared("dense", B, H, T, D, Tp, Tp, q_s, k_s, v_t, q_idx, k_idx)
 
 
+def _table_mode(mode: str) -> int:
+    return SCFA_HASH if mode == "hash" else SCFA_QK
+
+
 def build_tables(pre: Prepared, Bm: int = SCFA_TILE_M, Bn: int = SCFA_TILE_N, stream=None) -> Tables:
-    """Tile extrema and range tables. Dense inputs use the QK rule on their
-    arange positions (identical to the dense rule, and it keeps the ragged
-    tail's pads out of the causal ranges)."""
+    """Tile extrema, range tables and the forward launch order. Dense inputs
+    use the QK rule on their arange positions (identical to the dense rule,
+    and it keeps the ragged tail's pads out of the causal ranges)."""
     B, H = pre.B, pre.H
-    nQt, nKt = pre.Tpad // Bm, pre.Tpad // Bn
-    mode = SCFA_HASH if pre.mode == "hash" else SCFA_QK
+    nQt, nKt = pad_rows(pre.Tq) // Bm, pad_rows(pre.Tk) // Bn
     i32 = torch.int32
     t = Tables(_empty((B, H, nQt, 4), i32, pre.q), _empty((B, H, nKt, 4), i32, pre.q), _empty((B, H, nQt, 2), i32, pre.q),
                _empty((B, H, nKt, 2), i32, pre.q), _empty((B, H), i32, pre.q), Bm, Bn)
-    scfa_range_table(mode, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, B, H, pre.Tq, pre.Tq, Bm, Bn, t.qstats, t.kstats,
-                     t.fwd, t.bwd, t.tiles, stream)
+    scfa_range_table(_table_mode(pre.mode), pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, B, H, pre.Tq, pre.Tk, Bm, Bn,
+                     t.qstats, t.kstats, t.fwd, t.bwd, t.tiles, stream)
     t.fwd_order = _empty((B * H * nQt,), i32, pre.q)
     scfa_work_order(t.fwd, nKt, t.fwd_order, stream)
     return t
@@ -350,8 +387,8 @@ def build_tables(pre: Prepared, Bm: int = SCFA_TILE_M, Bn: int = SCFA_TILE_N, st
 
 def count_visible(pre: Prepared, stream=None) -> torch.Tensor:
     pairs = _empty((pre.B, pre.H), torch.int64, pre.q)
-    mode = SCFA_HASH if pre.mode == "hash" else SCFA_QK
-    scfa_count_visible(mode, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, pre.B, pre.H, pre.Tq, pre.Tq, pairs, stream)
+    scfa_count_visible(_table_mode(pre.mode), pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, pre.B, pre.H, pre.Tq, pre.Tk,
+                       pairs, stream)
     return pairs
 
 
@@ -365,7 +402,7 @@ def forward(pre: Prepared, tab: Tables, out_dtype=torch.float32, scale=None, O=N
         lse = _empty((B, H, T), torch.float32, pre.q)
     if pre.mode == "hash":
         scfa_hash_sparse_fwd(pre.q, pre.k, pre.v_t, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats,
-                             tab.fwd, T, O, lse, scale, stream, order=tab.fwd_order)
+                             tab.fwd, T, O, lse, scale, stream, order=tab.fwd_order, Tq=pre.Tq, Tk=pre.Tk)
     else:
         scfa_qk_sparse_fwd(pre.q, pre.k, pre.v_t, pre.q_idx, pre.k_idx, tab.qstats, tab.kstats, tab.fwd, T, O, lse,
                            scale, stream, order=tab.fwd_order)
@@ -375,14 +412,14 @@ def forward(pre: Prepared, tab: Tables, out_dtype=torch.float32, scale=None, O=N
 def backward(pre: Prepared, tab: Tables, O, lse, dO, scale=None, grads=None, workspace=None, stream=None):
     """Gradients w.r.t. the original-order q, k, v (fp32, (B,T,H,D))."""
     B, H, T, D = pre.B, pre.H, pre.T, pre.D
-    mode = SCFA_HASH if pre.mode == "hash" else SCFA_QK
+    mode = _table_mode(pre.mode)
     if grads is None:
         grads = tuple(_empty((B, T, H, D), torch.float32, pre.q) for _ in range(3))
     if workspace is None:
-        workspace = _empty((scfa_bwd_workspace_bytes(mode, B, H, pre.Tq, D),), torch.uint8, pre.q)
+        workspace = _empty((scfa_bwd_workspace_bytes(mode, B, H, pre.Tq, pre.Tk, D),), torch.uint8, pre.q)
     dQ, dK, dV = grads
     scfa_bwd(mode, pre.q, pre.k, pre.v_t, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats, tab.fwd,
-             tab.bwd, O, lse, dO, T, pre.Tq, dQ, dK, dV, workspace, scale, stream)
+             tab.bwd, O, lse, dO, T, pre.Tq, pre.Tk, dQ, dK, dV, workspace, scale, stream)
     return dQ, dK, dV
 
 
@@ -409,7 +446,8 @@ def dense_causal_attention(q, k, v, out_dtype=torch.float32, scale=None):
 class Plan:
     """Preallocated pipeline for one shape and mode.
 
-    mode "hash": bucket -> sort -> gathers -> tables -> forward.
+    mode "hash": bucket -> sort -> bucket-aligned layout -> gathers -> tables
+                 -> forward.
     mode "qk":   count -> compact -> gather -> tables -> forward, with a fixed
                  compacted length Tc (default: pad_rows(T), which always fits).
     mode "dense": gathers -> tables -> forward on positions 0..T-1.
@@ -427,34 +465,40 @@ class Plan:
         i32 = torch.int32
         e = lambda shape, dt=i32: torch.empty(shape, dtype=dt, device=d)  # noqa: E731
         if mode == "qk":
-            self.Tpad = Tc if Tc is not None else pad_rows(T)
-            if self.Tpad % SCFA_ROW_ALIGN:
+            Tc = Tc if Tc is not None else pad_rows(T)
+            if Tc % SCFA_ROW_ALIGN:
                 raise ScfaError("Tc must be a multiple of 128")
-            self.Tq = self.Tpad
+            self.Tq = self.Tk = Tc
             nC = (T + SCFA_COUNT_CHUNK - 1) // SCFA_COUNT_CHUNK
             self.cnt = [e((B, H)), e((B, H))]
             self.mx = [e((1,)), e((1,))]
             self.choff = [e((B, H, nC)), e((B, H, nC))]
+        elif mode == "hash":
+            self.Tq = scfa_hash_segment_rows(T, nb, SCFA_TILE_M)
+            self.Tk = scfa_hash_segment_rows(T, nb, SCFA_TILE_N)
         else:
-            self.Tpad = pad_rows(T)
-            self.Tq = T if mode == "hash" else self.Tpad
-        Tp = self.Tpad
-        self.q_s, self.k_s = e((B, H, Tp, D), dtype), e((B, H, Tp, D), dtype)
-        self.v_t = e((B, H, D, Tp), dtype)
-        self.q_idx, self.k_idx = e((B, H, Tp)), e((B, H, Tp))
+            self.Tq = self.Tk = pad_rows(T)
+        TqP, TkP = pad_rows(self.Tq), pad_rows(self.Tk)
+        self.q_s, self.k_s = e((B, H, TqP, D), dtype), e((B, H, TkP, D), dtype)
+        self.v_t = e((B, H, D, TkP), dtype)
+        self.q_idx, self.k_idx = e((B, H, TqP)), e((B, H, TkP))
         self.q_bkt = self.k_bkt = None
         self.dev_err = torch.zeros((1,), dtype=i32, device=d)
         if mode == "hash":
+            Tp = pad_rows(T)
             self.bq, self.bk = e((B, H, T)), e((B, H, T))
-            self.q_bkt, self.k_bkt = e((B, H, Tp)), e((B, H, Tp))
+            self.perm_q, self.perm_k = e((B, H, Tp)), e((B, H, Tp))
+            self.bs_q, self.bs_k = e((B, H, Tp)), e((B, H, Tp))
             self.offq, self.offk = e((B, H, nb + 1)), e((B, H, nb + 1))
+            self.segq, self.segk = e((B, H, nb + 1)), e((B, H, nb + 1))
+            self.q_bkt, self.k_bkt = e((B, H, TqP)), e((B, H, TkP))
             self.ws = e((max(1, scfa_hash_sort_workspace_bytes(B, H, T, nb)),), torch.uint8)
         if mode == "dense":
-            ar = torch.arange(Tp, dtype=i32, device=d)
-            self.q_idx.copy_(torch.where(ar < T, ar, torch.full_like(ar, SCFA_Q_PAD)).expand(B, H, Tp))
-            self.k_idx.copy_(torch.where(ar < T, ar, torch.full_like(ar, SCFA_K_PAD)).expand(B, H, Tp))
+            ar = torch.arange(TqP, dtype=i32, device=d)
+            self.q_idx.copy_(torch.where(ar < T, ar, torch.full_like(ar, SCFA_Q_PAD)).expand(B, H, TqP))
+            self.k_idx.copy_(torch.where(ar < T, ar, torch.full_like(ar, SCFA_K_PAD)).expand(B, H, TkP))
         Bm, Bn = SCFA_TILE_M, SCFA_TILE_N
-        nQt, nKt = Tp // Bm, Tp // Bn
+        nQt, nKt = TqP // Bm, TkP // Bn
         self.tab = Tables(e((B, H, nQt, 4)), e((B, H, nKt, 4)), e((B, H, nQt, 2)), e((B, H, nKt, 2)), e((B, H)), Bm, Bn,
                           e((B * H * nQt,)))
         self.O = e((B, T, H, D), out_dtype)
@@ -469,15 +513,20 @@ class Plan:
         scfa_hash_bucket(k, R, self.nb, self.bk, stream)
 
     def sort(self, stream=None):
-        scfa_hash_sort(self.bq, self.nb, SCFA_Q_PAD, self.q_idx, self.q_bkt, self.offq, self.ws, self.dev_err, stream)
-        scfa_hash_sort(self.bk, self.nb, SCFA_K_PAD, self.k_idx, self.k_bkt, self.offk, self.ws, self.dev_err, stream)
+        """Stable sort by bucket, then the bucket-aligned layout."""
+        scfa_hash_sort(self.bq, self.nb, SCFA_Q_PAD, self.perm_q, self.bs_q, self.offq, self.ws, self.dev_err, stream)
+        scfa_hash_sort(self.bk, self.nb, SCFA_K_PAD, self.perm_k, self.bs_k, self.offk, self.ws, self.dev_err, stream)
+        scfa_hash_segments(self.perm_q, self.offq, self.T, self.nb, SCFA_TILE_M, SCFA_Q_PAD, self.q_idx, self.q_bkt,
+                           self.segq, self.dev_err, stream)
+        scfa_hash_segments(self.perm_k, self.offk, self.T, self.nb, SCFA_TILE_N, SCFA_K_PAD, self.k_idx, self.k_bkt,
+                           self.segk, self.dev_err, stream)
 
     def compact(self, q, k, keep_q, keep_k, stream=None):
         scfa_qk_count(keep_q, self.cnt[0], self.mx[0], self.choff[0], stream)
         scfa_qk_count(keep_k, self.cnt[1], self.mx[1], self.choff[1], stream)
-        scfa_qk_compact(q, keep_q, self.cnt[0], self.choff[0], self.Tpad, SCFA_Q_PAD, self.q_s, self.q_idx,
+        scfa_qk_compact(q, keep_q, self.cnt[0], self.choff[0], self.Tq, SCFA_Q_PAD, self.q_s, self.q_idx,
                         self.dev_err, stream)
-        scfa_qk_compact(k, keep_k, self.cnt[1], self.choff[1], self.Tpad, SCFA_K_PAD, self.k_s, self.k_idx,
+        scfa_qk_compact(k, keep_k, self.cnt[1], self.choff[1], self.Tk, SCFA_K_PAD, self.k_s, self.k_idx,
                         self.dev_err, stream)
 
     def gather(self, q, k, v, stream=None):
@@ -487,38 +536,29 @@ class Plan:
         scfa_gather(v, self.k_idx, SCFA_COLS, self.v_t, stream)
 
     def tables(self, stream=None):
-        mode = SCFA_HASH if self.mode == "hash" else SCFA_QK
         t = self.tab
-        scfa_range_table(mode, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H, self.Tq, self.Tq, t.Bm,
-                         t.Bn, t.qstats, t.kstats, t.fwd, t.bwd, t.tiles, stream)
+        scfa_range_table(_table_mode(self.mode), self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H, self.Tq,
+                         self.Tk, t.Bm, t.Bn, t.qstats, t.kstats, t.fwd, t.bwd, t.tiles, stream)
         scfa_work_order(t.fwd, t.kstats.shape[2], t.fwd_order, stream)
 
     def forward(self, stream=None):
-        t = self.tab
-        if self.mode == "hash":
-            scfa_hash_sparse_fwd(self.q_s, self.k_s, self.v_t, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, t.qstats,
-                                 t.kstats, t.fwd, self.T, self.O, self.lse, self.scale, stream, order=t.fwd_order)
-        else:
-            scfa_qk_sparse_fwd(self.q_s, self.k_s, self.v_t, self.q_idx, self.k_idx, t.qstats, t.kstats, t.fwd, self.T,
-                               self.O, self.lse, self.scale, stream, order=t.fwd_order)
+        forward(self.prepared(), self.tab, self.out_dtype, self.scale, self.O, self.lse, stream)
 
     def backward(self, dO, stream=None):
         """Gradients of the last forward() w.r.t. q, k, v (fp32, original order)."""
         if self._grads is None:
             d = self.q_s.device
-            mode = SCFA_HASH if self.mode == "hash" else SCFA_QK
             self._grads = tuple(torch.empty((self.B, self.T, self.H, self.D), dtype=torch.float32, device=d)
                                 for _ in range(3))
-            self._bws = torch.empty((scfa_bwd_workspace_bytes(mode, self.B, self.H, self.Tq, self.D),),
-                                    dtype=torch.uint8, device=d)
+            self._bws = torch.empty((scfa_bwd_workspace_bytes(_table_mode(self.mode), self.B, self.H, self.Tq, self.Tk,
+                                                              self.D),), dtype=torch.uint8, device=d)
         if self.out_dtype != torch.float32:
             raise ScfaError("backward needs the fp32 forward output")
         return backward(self.prepared(), self.tab, self.O, self.lse, dO, self.scale, self._grads, self._bws, stream)
 
     def count_visible(self, stream=None):
-        mode = SCFA_HASH if self.mode == "hash" else SCFA_QK
-        scfa_count_visible(mode, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H, self.Tq, self.Tq,
-                           self.pairs, stream)
+        scfa_count_visible(_table_mode(self.mode), self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H,
+                           self.Tq, self.Tk, self.pairs, stream)
         return self.pairs
 
     def prepare(self, x: dict, stream=None):
@@ -538,5 +578,5 @@ class Plan:
         return self.O, self.lse
 
     def prepared(self) -> Prepared:
-        return Prepared(self.mode, self.B, self.H, self.T, self.D, self.Tq, self.Tpad, self.q_s, self.k_s, self.v_t,
+        return Prepared(self.mode, self.B, self.H, self.T, self.D, self.Tq, self.Tk, self.q_s, self.k_s, self.v_t,
                         self.q_idx, self.k_idx, self.q_bkt, self.k_bkt)

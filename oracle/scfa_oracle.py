@@ -128,6 +128,49 @@ def hash_sort(bucket: np.ndarray, nb: int):
     return perm, bsorted, offsets
 
 
+def segment_rows(T: int, nb: int, align: int) -> int:
+    """Rows of a bucket-aligned layout that any head of length T fits in:
+    T real rows plus at most align - 1 pad rows per bucket, rounded up to a
+    multiple of 128."""
+    n = T + nb * (align - 1)
+    return -(-n // 128) * 128
+
+
+def hash_segments(perm: np.ndarray, offsets: np.ndarray, nb: int, align: int, pad: int, Tseg: int):
+    """Bucket-aligned layout of a sorted head (a layout of the sorted order of
+    the SCFA explainer, 3.4 "Hash-Sparse Attention: Sorting by Bucket and
+    Two-Dimensional Tiling": it keeps every bucket's rows in sorted order and
+    only inserts pad rows, so tiles of `align` rows never hold two buckets).
+
+    perm: (B, H, >=T) sorted positions; offsets: (B, H, nb+1) from hash_sort.
+    Bucket v starts at row A_v = sum_{u<v} ceil(n_u / align) * align, where
+    n_u = offsets[u+1] - offsets[u]. Row A_v + r, r < n_v, holds
+    perm[offsets[v] + r] with bucket v; rows A_v + n_v .. A_{v+1} - 1 hold
+    `pad` with bucket v; rows A_nb .. Tseg - 1 hold `pad` with bucket nb.
+    Returns idx (B, H, Tseg) int32, bkt (B, H, Tseg) int32, seg_off
+    (B, H, nb+1) int32 = A.
+    """
+    B, H = offsets.shape[:2]
+    idx = np.full((B, H, Tseg), pad, dtype=np.int32)
+    bkt = np.full((B, H, Tseg), nb, dtype=np.int32)
+    seg = np.zeros((B, H, nb + 1), dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            a = 0
+            for v in range(nb):
+                lo, hi = int(offsets[b, h, v]), int(offsets[b, h, v + 1])
+                n = hi - lo
+                m = -(-n // align) * align
+                if a + m > Tseg:
+                    raise ValueError("Tseg too small")
+                seg[b, h, v] = a
+                idx[b, h, a:a + n] = perm[b, h, lo:hi]
+                bkt[b, h, a:a + m] = v
+                a += m
+            seg[b, h, nb] = a
+    return idx, bkt, seg
+
+
 def gather_rows(x: np.ndarray, perm: np.ndarray) -> np.ndarray:
     """x: (B, T, H, D) any dtype; perm: (B, H, Tp). Row r of head (b,h) is
     x[b, perm[r], h] when 0 <= perm[r] < T, else a zero row. -> (B, H, Tp, D)."""

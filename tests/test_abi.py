@@ -78,8 +78,15 @@ def test_invalid_arguments_rejected_without_gpu():
                                 null) == scfa.SCFA_ERR_INVALID
     hargs = [0, 1] + [dummy] * 10
     # hash forward: a NULL table is rejected
-    assert L.scfa_hash_sparse_fwd(*hargs[:-1], null, null, 1, 1, 8, 64, ctypes.c_float(0.125), dummy, dummy,
+    assert L.scfa_hash_sparse_fwd(*hargs[:-1], null, null, 1, 1, 8, 8, 8, 64, ctypes.c_float(0.125), dummy, dummy,
                                   null) == scfa.SCFA_ERR_INVALID
+    # bucket-aligned layout: bad alignment, rows below T, size helper
+    assert L.scfa_hash_segments(dummy, dummy, 1, 1, 100, 16, 48, -1, 128, dummy, dummy, dummy, null,
+                                null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_segments(dummy, dummy, 1, 1, 300, 16, 64, -1, 256, dummy, dummy, dummy, null,
+                                null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_segment_rows(16384, 16, 128) == 18432
+    assert L.scfa_hash_segment_rows(16384, 16, 48) == 0
     # work order: bad sizes, NULL pointers
     assert L.scfa_work_order(dummy, 1, 1, 0, 8, dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_work_order(dummy, 1, 1, 8, 16384, dummy, null) == scfa.SCFA_ERR_INVALID

@@ -47,6 +47,23 @@ def test_fwd_bf16_output_small():
     check_fwd(w, O, lse, Or, Lr)
 
 
+def test_hash_sorted_order_without_alignment():
+    """The forward on the plain sorted order (buckets not aligned to tiles, so
+    tiles straddle buckets and the bucket mask is exercised) gives the same
+    attention as the oracle."""
+    need_gpu()
+    announce("hash fwd, unaligned sorted order")
+    w = small("hash", 2, 2, 1100, nb=16, seed=64)
+    x = make_inputs(w)
+    g = to_dev(x)
+    pre = scfa.prepare_hash(g["q"], g["k"], g["v"], g["R"], w.nb, aligned=False)
+    assert pre.Tq == pre.Tk == w.T
+    O, lse = scfa.forward(pre, scfa.build_tables(pre))
+    torch.cuda.synchronize()
+    Or, Lr = oracle_fwd(w, x)
+    check_fwd(w, O, lse, Or, Lr)
+
+
 def test_dense_equals_qk_all_kept_and_single_bucket():
     """Dense mode, QK with every token kept and hash with one bucket (R = 0)
     run different preprocessing but must give the same attention."""

@@ -20,11 +20,12 @@ HASH_CASES = [small("hash", 2, 3, 1000, nb=16, seed=31), small("hash", 1, 2, 1, 
               small("hash", 2, 2, 700, nb=2, seed=35)]
 
 
-def _tables_match(mode, pre, tab, Tq, Bm, Bn, q_bkt=None, k_bkt=None):
+def _tables_match(mode, pre, tab, Tq, Bm, Bn, q_bkt=None, k_bkt=None, Tk=None):
+    Tk = Tq if Tk is None else Tk
     qi = pre.q_idx.cpu().numpy()[:, :, :Tq]
-    ki = pre.k_idx.cpu().numpy()[:, :, :Tq]
+    ki = pre.k_idx.cpu().numpy()[:, :, :Tk]
     qb = None if q_bkt is None else q_bkt.cpu().numpy()[:, :, :Tq]
-    kb = None if k_bkt is None else k_bkt.cpu().numpy()[:, :, :Tq]
+    kb = None if k_bkt is None else k_bkt.cpu().numpy()[:, :, :Tk]
     ref = oracle.range_tables(mode, qi, ki, qb, kb, Bm, Bn)
     nQ, nK = ref["fwd"].shape[2], ref["bwd"].shape[2]
     qs, ks = tab.qstats.cpu().numpy(), tab.kstats.cpu().numpy()
@@ -103,23 +104,33 @@ def test_hash_bucket_sort_gather_bitexact(w):
     bq, bk = oracle_buckets(w, x)
     assert np.array_equal(pre.extra["bucket_q"].cpu().numpy(), bq)
     assert np.array_equal(pre.extra["bucket_k"].cpu().numpy(), bk)
-    T, Tp = w.T, pre.Tpad
-    for b_, pre_idx, pre_bs, off, pad in ((bq, pre.q_idx, pre.q_bkt, pre.extra["offsets_q"], oracle.Q_PAD),
-                                          (bk, pre.k_idx, pre.k_bkt, pre.extra["offsets_k"], oracle.K_PAD)):
+    T = w.T
+    ex = pre.extra
+    sides = ((bq, ex["perm_q"], ex["sorted_bkt_q"], ex["offsets_q"], oracle.Q_PAD, pre.q_idx, pre.q_bkt,
+              ex["seg_offsets_q"], scfa.SCFA_TILE_M, pre.Tq),
+             (bk, ex["perm_k"], ex["sorted_bkt_k"], ex["offsets_k"], oracle.K_PAD, pre.k_idx, pre.k_bkt,
+              ex["seg_offsets_k"], scfa.SCFA_TILE_N, pre.Tk))
+    for b_, pperm, pbs, off, pad, sidx, sbkt, soff, align, Tseg in sides:
         perm, bs, offs = oracle.hash_sort(b_, w.nb)
-        gi, gb = pre_idx.cpu().numpy(), pre_bs.cpu().numpy()
+        gi, gb = pperm.cpu().numpy(), pbs.cpu().numpy()
         assert np.array_equal(gi[:, :, :T], perm)
         assert (gi[:, :, T:] == pad).all()
         assert np.array_equal(gb[:, :, :T], bs)
         assert (gb[:, :, T:] == -1).all()
         assert np.array_equal(off.cpu().numpy(), offs)
+        # bucket-aligned layout
+        assert Tseg == oracle.segment_rows(T, w.nb, align)
+        ri, rb, ro = oracle.hash_segments(perm, offs, w.nb, align, pad, Tseg)
+        assert np.array_equal(sidx.cpu().numpy(), ri)
+        assert np.array_equal(sbkt.cpu().numpy(), rb)
+        assert np.array_equal(soff.cpu().numpy(), ro)
     qi, ki = pre.q_idx.cpu().numpy(), pre.k_idx.cpu().numpy()
     assert np.array_equal(np_bits(pre.q), oracle.gather_rows(np_bits(x["q"]), qi))
     assert np.array_equal(np_bits(pre.k), oracle.gather_rows(np_bits(x["k"]), ki))
     assert np.array_equal(np_bits(pre.v_t), oracle.gather_rows(np_bits(x["v"]), ki).transpose(0, 1, 3, 2))
     tab = scfa.build_tables(pre)
     torch.cuda.synchronize()
-    _tables_match("hash", pre, tab, T, scfa.SCFA_TILE_M, scfa.SCFA_TILE_N, pre.q_bkt, pre.k_bkt)
+    _tables_match("hash", pre, tab, pre.Tq, scfa.SCFA_TILE_M, scfa.SCFA_TILE_N, pre.q_bkt, pre.k_bkt, pre.Tk)
     pairs = scfa.count_visible(pre).cpu().numpy()
     assert np.array_equal(pairs, oracle.visible_pairs("hash", T, w.B, w.H, bkt_q=bq, bkt_k=bk))
 
@@ -137,7 +148,7 @@ def test_tables_any_tile_size(Bm, Bn):
                else scfa.prepare_qk(g["q"], g["k"], g["v"], g["keep_q"], g["keep_k"]))
         tab = scfa.build_tables(pre, Bm, Bn)
         torch.cuda.synchronize()
-        ref = _tables_match(w.mode, pre, tab, pre.Tq, Bm, Bn, pre.q_bkt, pre.k_bkt)
+        ref = _tables_match(w.mode, pre, tab, pre.Tq, Bm, Bn, pre.q_bkt, pre.k_bkt, pre.Tk)
         assert ref["tiles"].sum() > 0
     # dense mode of the table call (positions = row numbers, no index arrays)
     T = 1000
@@ -172,7 +183,7 @@ def test_tables_more_than_512_tiles(mode):
     tab = scfa.build_tables(pre, 16, 16)
     torch.cuda.synchronize()
     assert tab.fwd.shape[2] > 512 and tab.bwd.shape[2] > 512
-    ref = _tables_match(mode, pre, tab, pre.Tq, 16, 16, pre.q_bkt, pre.k_bkt)
+    ref = _tables_match(mode, pre, tab, pre.Tq, 16, 16, pre.q_bkt, pre.k_bkt, pre.Tk)
     assert ref["tiles"].sum() > 0
 
 
@@ -194,6 +205,19 @@ def test_device_error_flags():
     scfa.scfa_hash_sort(bucket, nb, -1, perm, bs, off, ws, err)
     torch.cuda.synchronize()
     assert int(err.item()) & scfa.SCFA_DEVERR_BUCKET_RANGE
+    # a bucket-aligned layout that does not fit the given number of rows: 16
+    # buckets of about 19 tokens each need 16 x 128 rows, 256 are given
+    bucket = (torch.arange(300, dtype=torch.int32, device=d) % 16).reshape(1, 1, 300).contiguous()
+    ws16 = torch.empty(scfa.scfa_hash_sort_workspace_bytes(1, 1, 300, 16), dtype=torch.uint8, device=d)
+    off16 = torch.empty((1, 1, 17), dtype=torch.int32, device=d)
+    err.zero_()
+    scfa.scfa_hash_sort(bucket, 16, -1, perm, bs, off16, ws16, err)
+    seg_i = torch.empty((1, 1, 384), dtype=torch.int32, device=d)
+    seg_b, seg_o = torch.empty_like(seg_i), torch.empty((1, 1, 17), dtype=torch.int32, device=d)
+    scfa.scfa_hash_segments(perm, off16, 300, 16, 128, -1, seg_i, seg_b, seg_o, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == scfa.SCFA_DEVERR_SEGMENT_OVERFLOW
+    assert seg_o.cpu().numpy()[0, 0, 16] == 16 * 128
     # a kept count above the compacted length
     keep = torch.ones((1, 200, 1), dtype=torch.uint8, device=d)
     x = torch.zeros((1, 200, 1, 64), dtype=torch.bfloat16, device=d)
@@ -224,8 +248,11 @@ def test_full_size_preprocessing_bitexact(name):
         bq, bk = oracle_buckets(w, x)
         assert np.array_equal(pre.extra["bucket_q"].cpu().numpy(), bq)
         assert np.array_equal(pre.extra["bucket_k"].cpu().numpy(), bk)
-        perm, bs, _ = oracle.hash_sort(bk, w.nb)
-        assert np.array_equal(pre.k_idx.cpu().numpy()[:, :, :w.T], perm)
+        perm, bs, offs = oracle.hash_sort(bk, w.nb)
+        assert np.array_equal(pre.extra["perm_k"].cpu().numpy()[:, :, :w.T], perm)
+        ri, rb, _ = oracle.hash_segments(perm, offs, w.nb, scfa.SCFA_TILE_N, oracle.K_PAD, pre.Tk)
+        assert np.array_equal(pre.k_idx.cpu().numpy(), ri)
+        assert np.array_equal(pre.k_bkt.cpu().numpy(), rb)
         mode = "hash"
     else:
         pre = scfa.prepare_qk(g["q"], g["k"], g["v"], g["keep_q"], g["keep_k"])
@@ -235,4 +262,4 @@ def test_full_size_preprocessing_bitexact(name):
         mode = "qk"
     tab = scfa.build_tables(pre)
     torch.cuda.synchronize()
-    _tables_match(mode, pre, tab, pre.Tq, scfa.SCFA_TILE_M, scfa.SCFA_TILE_N, pre.q_bkt, pre.k_bkt)
+    _tables_match(mode, pre, tab, pre.Tq, scfa.SCFA_TILE_M, scfa.SCFA_TILE_N, pre.q_bkt, pre.k_bkt, pre.Tk)

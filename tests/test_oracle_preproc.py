@@ -126,6 +126,44 @@ def test_hash_sort_hand_example():
     assert list(off[0, 0]) == [0, 2, 3, 3, 5]
 
 
+def test_hash_segments_hand_example():
+    """Buckets of sizes 2, 1, 0, 2 (nb = 4) with align 2: bucket 0 at row 0,
+    bucket 1 at row 2 (one pad), bucket 2 empty, bucket 3 at row 4."""
+    bucket = np.array([3, 0, 3, 0, 1], dtype=np.int32).reshape(1, 1, 5)
+    perm, _, off = oracle.hash_sort(bucket, 4)
+    idx, bkt, seg = oracle.hash_segments(perm, off, 4, 2, -1, 8)
+    assert list(idx[0, 0]) == [1, 3, 4, -1, 0, 2, -1, -1]
+    assert list(bkt[0, 0]) == [0, 0, 1, 1, 3, 3, 4, 4]
+    assert list(seg[0, 0]) == [0, 2, 4, 4, 6]
+
+
+@pytest.mark.parametrize("align", [1, 16, 64, 128])
+def test_hash_segments_invariants(align):
+    """Removing the pad rows gives back the sorted order; every bucket starts
+    at a multiple of align and fits the segment_rows bound; buckets never
+    decrease along the rows; no tile of align rows holds two buckets."""
+    rng = np.random.default_rng(align)
+    nb, T = 8, 300
+    bucket = rng.integers(0, nb, size=(2, 2, T)).astype(np.int32)
+    bucket[1, 1] = 5  # one bucket holds everything
+    perm, bs, off = oracle.hash_sort(bucket, nb)
+    Tseg = oracle.segment_rows(T, nb, align)
+    assert Tseg % 128 == 0 and Tseg >= T + nb * (align - 1)
+    idx, bkt, seg = oracle.hash_segments(perm, off, nb, align, 1_000_000_000, Tseg)
+    for b in range(2):
+        for h in range(2):
+            real = idx[b, h] != 1_000_000_000
+            assert list(idx[b, h][real]) == list(perm[b, h])
+            assert list(bkt[b, h][real]) == list(bs[b, h])
+            assert (seg[b, h] % align == 0).all()
+            assert (np.diff(bkt[b, h]) >= 0).all()
+            tiles = bkt[b, h].reshape(-1, align) if Tseg % align == 0 else None
+            if tiles is not None:
+                assert (tiles.min(axis=1) == tiles.max(axis=1)).all()
+            n = np.diff(off[b, h])
+            assert list(np.diff(seg[b, h])) == [-(-int(c) // align) * align for c in n]
+
+
 def test_gather_rows():
     x = np.arange(2 * 5 * 3 * 4, dtype=np.int16).reshape(2, 5, 3, 4)
     perm = np.array([[[4, 0, -1], [1, 1, 1000000000], [2, 3, 4]]] * 2, dtype=np.int32)

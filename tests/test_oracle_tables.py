@@ -83,6 +83,33 @@ def test_coverage_and_exactness(mode, T, seed, Bm, Bn):
                     assert s == e == 0
 
 
+@pytest.mark.parametrize("Bm,Bn", [(128, 64), (64, 64), (32, 32)])
+def test_coverage_on_bucket_aligned_layout(Bm, Bn):
+    """The hash table rule on the bucket-aligned layout (query buckets start
+    at multiples of Bm, key buckets at multiples of Bn, pad rows inside):
+    every tile holding a visible pair is processed, every processed tile
+    lies inside one bucket on both sides, and the ranges match the set."""
+    T, nb = 700, 8
+    w = small("hash", 1, 2, T, 16, nb=nb, seed=9)
+    x = make_inputs(w)
+    R = x["R"].double().numpy()
+    bq = oracle.hash_bucket(x["q"].double().numpy(), R, nb)
+    bk = oracle.hash_bucket(x["k"].double().numpy(), R, nb)
+    qp, _, qo = oracle.hash_sort(bq, nb)
+    kp, _, ko = oracle.hash_sort(bk, nb)
+    qi, qb, _ = oracle.hash_segments(qp, qo, nb, Bm, oracle.Q_PAD, oracle.segment_rows(T, nb, Bm))
+    ki, kb, _ = oracle.hash_segments(kp, ko, nb, Bn, oracle.K_PAD, oracle.segment_rows(T, nb, Bn))
+    tab = oracle.range_tables("hash", qi, ki, qb, kb, Bm, Bn)
+    need = _tiles_with_visible_pair(qi, ki, qb, kb, Bm, Bn)
+    P = tab["P"]
+    assert need.any()
+    assert not (need & ~P).any()
+    assert (tab["qstats"][..., 2] == tab["qstats"][..., 3]).all()
+    assert (tab["kstats"][..., 2] == tab["kstats"][..., 3]).all()
+    same = tab["qstats"][..., 2][..., :, None] == tab["kstats"][..., 2][..., None, :]
+    assert not (P & ~same).any()
+
+
 def test_dense_reduces_to_causal_schedule():
     # Backward compatibility: with idx = arange, query tile i processes key
     # tiles 0..i (start 0, stop i + 1) when the tiles are square.
