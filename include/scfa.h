@@ -243,10 +243,13 @@ int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, con
  * key visible iff k_pos <= q_pos (QK), and same bucket (hash); scores are
  * scale * q.k. A query with no visible key -- and, in QK mode, a dropped
  * query -- gets O = 0 and LSE = -inf.
- *  dtype_in      SCFA_BF16 / SCFA_F32 of q, k, v_t.
+ *  dtype_in      SCFA_BF16 / SCFA_F32 of q, k, v.
  *  dtype_out     SCFA_F32 / SCFA_BF16 of O.
- *  q, k          (B, H, Tpad, D) SCFA_ROWS compacted/sorted rows.
- *  v_t           (B, H, D, Tpad) SCFA_COLS compacted/sorted values.
+ *  q, k, v       (B, T, H, D) the ORIGINAL, unpermuted tensors (D = 64).
+ *                The gather of the preprocessing is fused into the loads:
+ *                row r of a head reads token q_idx[r] (k_idx[r] for k and
+ *                v); pad entries (any index outside [0, T)) read token 0,
+ *                whose values must be finite.
  *  q_idx, k_idx  (B, H, Tpad) original positions with pads.
  *  q_bkt, k_bkt  (B, H, Tpad) sorted bucket ids (hash only).
  *  qstats, kstats, fwd_tab   from scfa_range_table with Bm = SCFA_TILE_M,
@@ -260,17 +263,18 @@ int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, con
  *  O             out (B, T, H, D), every row written.
  *  lse           out (B, H, T) fp32 natural-log normaliser, every entry
  *                written (-inf for rows without a visible key).           */
-int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v_t,
+int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v,
                        const int32_t* q_idx, const int32_t* k_idx, const int32_t* qstats, const int32_t* kstats,
                        const int32_t* fwd_tab, const int32_t* order, int B, int H, int T, int Tc, int D, float scale,
                        void* O, float* lse, hipStream_t stream);
 
-/* Hash-sparse: as above, with the sorted (or bucket-aligned) operands and
+/* Hash-sparse: as above, with the sorted (or bucket-aligned) index arrays
+ * and
  *  q_bkt, k_bkt  sorted bucket ids of the rows;
  *  Tq, Tk        query / key rows as passed to scfa_range_table (T for the
  *                sorted order, Tseg for the bucket-aligned layout); the
- *                buffers hold SCFA_PAD(Tq) / SCFA_PAD(Tk) rows per head.       */
-int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v_t,
+ *                index arrays hold SCFA_PAD(Tq) / SCFA_PAD(Tk) rows per head. */
+int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v,
                          const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
                          const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, const int32_t* order,
                          int B, int H, int T, int Tq, int Tk, int D, float scale, void* O, float* lse,
@@ -289,8 +293,11 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
  *                SCFA_HASH.
  *  dtype_in      SCFA_BF16 (the only backward build; fp32 returns
  *                SCFA_ERR_UNSUPPORTED).
- *  q, k, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab
- *                exactly the operands and tables of the forward call.
+ *  q, k          (B, H, Tpad, D) SCFA_ROWS gathered rows and
+ *  v_t           (B, H, D, Tpad) SCFA_COLS gathered values (scfa_gather of
+ *                the forward's original tensors through q_idx / k_idx).
+ *  q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab
+ *                exactly the index arrays and tables of the forward call.
  *  O             (B, T, H, D) fp32 forward output;  lse (B, H, T) fp32.
  *  dO            (B, T, H, D) upstream gradient, dtype_in.
  *  T             original sequence length; Tq, Tk query / key rows as

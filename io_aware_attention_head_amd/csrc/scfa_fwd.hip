@@ -12,6 +12,12 @@
 // Architecture", item 4) together with the natural-log LSE.
 //
 // MI355X design:
+//  * The gather of the explainer's preprocessing ("Gather: Reordering Q, K,
+//    V according to the sorted indices") is fused into the loads: query rows
+//    and the key/value rows of each tile are read from the original
+//    (B, T, H, D) tensors through q_idx / k_idx. Rows of pad entries read
+//    token 0 instead (finite values; pad queries are never stored and pad
+//    keys are always masked).
 //  * One workgroup = 4 wave64s = one 128-row query tile; each wave owns 32
 //    queries as two 16-query MFMA column blocks.
 //  * Scores are computed TRANSPOSED, S^T = K Q^T, with
@@ -21,13 +27,14 @@
 //    lane-local.
 //  * O^T = V^T P^T reuses the S^T accumulator as the B operand after a cvt
 //    to bf16; K rows are permuted when loaded as the A operand so that each
-//    lane's 8 probabilities cover 8 CONSECUTIVE keys, which makes the V^T
-//    operand one 16-byte LDS read (V is stored transposed by the gather).
-//  * Software pipeline (bf16): while the exponentials of tile j run on the
-//    VALU, the MFMAs of S for tile j+1 are in flight; while P V of tile j
-//    runs on the MFMA unit, tile j+1 is masked and its row max taken. K/V^T
-//    tiles rotate through three LDS stages (one barrier per tile) and the
-//    global loads of tile j+2 are in flight during tile j.
+//    lane's 8 probabilities cover 8 CONSECUTIVE keys. The V^T operand is
+//    read from the row-major V tile with the LDS transpose read
+//    (ds_read_b64_tr_b16: 16 lanes exchange a 16 x 4 block of 16-bit values)
+//    from a layout whose 16-byte chunks are XOR-swizzled by row so that these
+//    reads are free of bank conflicts.
+//  * K and V tiles are staged by global-to-LDS DMA (no registers), double
+//    buffered; the key positions of the tile after next are prefetched into
+//    registers one tile ahead, so DMA addresses never wait on a load.
 //  * The reference max moves only when a row's tile max exceeds it by more
 //    than 2^8 (lazy rescaling): probabilities stay <= 256 and the O rescale
 //    is rare. O is normalised by the sum of the bf16-rounded probabilities
@@ -39,7 +46,7 @@
 //  * Work order: a launch order (longest query tiles first, XCD-aware) from
 //    scfa_work_order, or descending query-tile index.
 //  * float32 inputs use v_mfma_f32_16x16x4_f32 in a single-buffered kernel
-//    with the same data layout.
+//    with the same data flow.
 
 #include <math.h>
 
@@ -55,9 +62,9 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLazy = 8.0f;  // log2 headroom before the reference max moves
 
 struct FwdParams {
-  const void* q;
+  const void* q;  // (B, T, H, D) original order, as are k and v
   const void* k;
-  const void* vt;
+  const void* v;
   const int32_t* q_idx;
   const int32_t* k_idx;
   const int32_t* q_bkt;
@@ -70,8 +77,8 @@ struct FwdParams {
   float* lse;
   int B, H, T;
   int Tk;    // valid key rows (extrema/ragged test)
-  int TqPad;  // rows per head of the query-side buffers (q, q_idx, q_bkt)
-  int TkPad;  // rows per head of the key-side buffers (k, v_t columns, k_idx, k_bkt)
+  int TqPad;  // rows per head of the query-side index arrays (q_idx, q_bkt)
+  int TkPad;  // rows per head of the key-side index arrays (k_idx, k_bkt)
   int nQt, nKt;
   float c;  // scale * log2(e)
 };
@@ -92,47 +99,6 @@ __device__ inline void store4<uint16_t>(uint16_t* p, const f32x4& v) {
   u.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
   u.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h2)) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h3)) << 16);
   *reinterpret_cast<uint2*>(p) = u;
-}
-
-// Registers holding the next key tile while the current one is computed.
-template <int LOADS>
-struct TileRegs {
-  u32x4 k[LOADS];
-  u32x4 v[LOADS];
-  int idx;
-};
-
-// Global -> registers: the K tile (64 contiguous rows) and the V^T tile
-// (64 d-rows of 64 keys), 16 bytes per load, plus the tile's key positions
-// (threads 0..63) and buckets (threads 64..127).
-template <bool HASH, int ESZ, int CH, int LOADS>
-__device__ __forceinline__ void tile_load(TileRegs<LOADS>& r, const uint8_t* kg, const uint8_t* vg, const int32_t* kig,
-                                          const int32_t* kbg, int Tpad, int j, int tid) {
-  constexpr int TILE_BYTES = BN * HD * ESZ;
-  static_for<LOADS>([&](auto I) {
-    constexpr int i = decltype(I)::value;
-    const int u = tid + 256 * i;
-    r.k[i] = reinterpret_cast<const u32x4*>(kg + static_cast<size_t>(j) * TILE_BYTES)[u];
-    const int d = u / CH, ch = u - d * CH;
-    r.v[i] = *reinterpret_cast<const u32x4*>(vg + (static_cast<size_t>(d) * Tpad + j * BN) * ESZ + ch * 16);
-  });
-  if (tid < BN) r.idx = kig[j * BN + tid];
-  else if (HASH && tid < 2 * BN) r.idx = kbg[j * BN + tid - BN];
-}
-
-// Registers -> LDS with 16-byte XOR swizzles (K rows: swz_k, V^T rows: d & 7).
-template <bool HASH, int ESZ, int CH, int LOADS>
-__device__ __forceinline__ void tile_store(const TileRegs<LOADS>& r, uint8_t* ks, uint8_t* vs, int32_t* kp, int32_t* kb,
-                                           int tid) {
-  static_for<LOADS>([&](auto I) {
-    constexpr int i = decltype(I)::value;
-    const int u = tid + 256 * i;
-    const int row = u / CH, ch = u - row * CH;
-    *reinterpret_cast<u32x4*>(ks + row * HD * ESZ + ((ch ^ swz_k(row)) * 16)) = r.k[i];
-    *reinterpret_cast<u32x4*>(vs + row * BN * ESZ + ((ch ^ (row & 7)) * 16)) = r.v[i];
-  });
-  if (tid < BN) kp[tid] = r.idx;
-  else if (HASH && tid < 2 * BN) kb[tid - BN] = r.idx;
 }
 
 // Work item of this workgroup: (head, query tile).
@@ -334,10 +300,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lp);
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Row of the original (B, T, H, D) tensors for an index entry: pads (and any
+// entry outside [0, T)) read token 0, whose values are finite.
+__device__ inline int src_row(int pos, int T) { return (pos >= 0 && pos < T) ? pos : 0; }
+
+// 16-byte chunk of row r of a staged V tile that holds chunk c: swizzled so
+// that the transposed operand reads (4 rows x 32 bytes per 16 lanes) use all
+// banks.
+__device__ inline int swz_v(int r, int c) { return c ^ (2 * (r & 3)); }
+
 template <bool HASH, bool ZERO_DROPPED, typename TOUT>
 __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
-  constexpr int TB = BN * HD * 2;  // K tile and V^T tile, bytes each (8 KB)
-  // Two stages of (K, V^T); after the loop the same bytes stage the output.
+  constexpr int TB = BN * HD * 2;  // K tile and V tile, bytes each (8 KB)
+  // Two stages of (K, V); after the loop the same bytes stage the output.
   __shared__ __align__(16) uint8_t smem[4 * TB];
   static_assert(4 * TB >= BM * HD * sizeof(TOUT), "output staging does not fit");
   __shared__ __align__(16) int32_t Kp[2][BN];
@@ -349,12 +326,15 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
   const int ws = __builtin_amdgcn_readfirstlane(w);
   int qt, bh;
   pick_work(p, qt, bh);
+  const int b = bh / p.H, h = bh - b * p.H;
   const size_t rowbase = static_cast<size_t>(bh) * p.TqPad;  // query side
   const size_t kbase = static_cast<size_t>(bh) * p.TkPad;    // key side
   const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
   if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];  // visible after the first barrier
+  const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
+  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;  // token 0 of this head
 
   // ---- queries of this wave: B operand, positions, buckets --------------
   const int q0 = qt * BM + w * 32;
@@ -367,13 +347,12 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
   }
   const WaveRows wr = wave_rows(qpos, qbkt);
   bf16x8 Qb[2][2];  // [qb][ds]
-  {
-    const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (rowbase + q0) * HD;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < 2; ++qb) {
+    const uint8_t* qrow = static_cast<const uint8_t*>(p.q) + head0 +
+                          static_cast<size_t>(src_row(qpos[qb], p.T)) * rstride;
 #pragma unroll
-      for (int ds = 0; ds < 2; ++ds)
-        Qb[qb][ds] = *reinterpret_cast<const bf16x8*>(qg + (qb * 16 + r16) * HD + ds * 32 + g * 8);
+    for (int ds = 0; ds < 2; ++ds) Qb[qb][ds] = *reinterpret_cast<const bf16x8*>(qrow + (ds * 32 + g * 8) * 2);
   }
 
   f32x4 Oacc[4][2];
@@ -388,30 +367,35 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = static_cast<__bf16>(1.0f);
 
-  // ---- DMA addressing: uniform tile bases, per-lane constant offsets ------
-  // Wave w stages K rows and V^T rows 16w .. 16w+15 of a tile, 8 rows (1 KB)
-  // per instruction, XOR-swizzled by choosing each lane's source chunk.
-  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + kbase * HD * 2;
-  const uint8_t* vg = static_cast<const uint8_t*>(p.vt) + kbase * HD * 2;
+  // ---- DMA staging of a key tile -----------------------------------------
+  // Wave w stages rows 16w .. 16w+15 of the K and V tiles, 8 rows (1 KB) per
+  // instruction: lane l writes chunk position l % 8 of row 16w + 8i + l / 8
+  // and reads the chunk of that row's token that the swizzle puts there.
+  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + head0;
+  const uint8_t* vg = static_cast<const uint8_t*>(p.v) + head0;
   const int32_t* kig = p.k_idx + kbase;
   const int32_t* kbg = HASH ? p.k_bkt + kbase : nullptr;
-  uint32_t koff[2], voff[2];
+  uint32_t kch[2], vch[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 16 * w + 8 * i + (lane >> 3), cp = lane & 7;
-    koff[i] = row * 128 + ((cp ^ swz_k(row)) * 16);
-    voff[i] = row * p.TkPad * 2 + ((cp ^ (row & 7)) * 16);
+    kch[i] = (cp ^ swz_k(row)) * 16;
+    vch[i] = swz_v(row, cp) * 16;  // swz_v is its own inverse
   }
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t ldsp = lds_addr(&Kp[0][0]), ldsb = lds_addr(&Kb[0][0]);
-  auto stage_tile = [&](int j, int s) {
-    const uint8_t* kt = kg + static_cast<size_t>(j) * TB;
-    const uint8_t* vt = vg + static_cast<size_t>(j) * BN * 2;
+  // positions of the rows this lane stages for key tile j
+  auto tile_rows = [&](int j, int (&pos)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pos[i] = kig[min(j, p.nKt - 1) * BN + 16 * w + 8 * i + (lane >> 3)];
+  };
+  auto stage_tile = [&](int j, int s, const int (&pos)[2]) {
     const uint32_t ks = lds0 + s * TB + ws * 2048, vs = lds0 + (2 + s) * TB + ws * 2048;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      dma16(kt, koff[i], ks + i * 1024);
-      dma16(vt, voff[i], vs + i * 1024);
+      const uint32_t off = static_cast<uint32_t>(src_row(pos[i], p.T)) * rstride;
+      dma16(kg, off + kch[i], ks + i * 1024);
+      dma16(vg, off + vch[i], vs + i * 1024);
     }
     if (ws == 0) dma4(kig + j * BN, lane * 4, ldsp + s * BN * 4);
     else if (HASH && ws == 1) dma4(kbg + j * BN, lane * 4, ldsb + s * BN * 4);
@@ -423,21 +407,27 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
   };
 
   int j = next_tile(rng.x);
+  int jn = j < rng.y ? next_tile(j + 1) : rng.y;
+  int pos[2];
   if (j < rng.y) {
-    stage_tile(j, 0);
-    dma_wait();
+    tile_rows(j, pos);
+    stage_tile(j, 0, pos);
   }
+  tile_rows(jn, pos);  // rows of the next tile, used by the first iteration
+  dma_wait();
   __syncthreads();
   int s = 0;
   int4 ks_cur = kst[min(j, p.nKt - 1)];
   while (j < rng.y) {
-    const int jn = next_tile(j + 1);
-    // the next tile's statistics are loaded before its DMA is issued, so
-    // that waiting for them never waits for the DMA
+    const int jnn = jn < rng.y ? next_tile(jn + 1) : rng.y;
+    // small loads (statistics, and the rows of the tile after next) are
+    // issued before the DMA, so that waiting for them never waits for it
     const int4 ks = ks_cur;
     ks_cur = kst[min(jn, p.nKt - 1)];
+    int pos_nn[2];
+    tile_rows(jnn, pos_nn);
     __builtin_amdgcn_sched_barrier(0);
-    if (jn < rng.y) stage_tile(jn, s ^ 1);
+    if (jn < rng.y) stage_tile(jn, s ^ 1, pos);
 
     if (!tile_empty_for<HASH>(ks, wr)) {
       const uint8_t* Ks = smem + s * TB;
@@ -496,12 +486,23 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
       }
 
       // -- O^T += V^T P^T; row sums of the rounded weights ---------------------
+      // V^T operand of (db, kc): dims 16db + r16, keys 32kc + 8g + 0..7, as
+      // two transposed reads of 4 keys; source lane r16 of group g reads
+      // 4 dims of key 32kc + 8g + 4hh + r16 / 4.
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-          const int d = db * 16 + r16;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vs[d * BN * 2 + (((kc * 4 + g) ^ (d & 7)) * 16)]);
+          v4i16 t[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int r = 32 * kc + 8 * g + 4 * hh + (r16 >> 2);
+            const int col = 16 * db + 4 * (r16 & 3);  // first of the 4 dims
+            const uint8_t* src = Vs + r * 128 + swz_v(r, col >> 3) * 16 + (col & 7) * 2;
+            t[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(__attribute__((address_space(3))) void*)src);
+          }
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
             Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, P[qb][kc], Oacc[db][qb], 0, 0, 0);
@@ -517,6 +518,9 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
     __syncthreads();
     s ^= 1;
     j = jn;
+    jn = jnn;
+    pos[0] = pos_nn[0];
+    pos[1] = pos_nn[1];
   }
 
   // ---- epilogue --------------------------------------------------------------
@@ -538,9 +542,7 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
 // ---------------------------------------------------------------------------
 template <bool HASH, bool ZERO_DROPPED, typename TOUT>
 __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
-  constexpr int ESZ = 4, CH = 16;
-  constexpr int TB = BN * HD * ESZ;     // 16 KB
-  constexpr int LOADS = TB / 16 / 256;  // 4
+  constexpr int TB = BN * HD * 4;  // 16 KB
   __shared__ __align__(16) uint8_t smem[2 * TB];
   uint8_t* Ks = smem;
   uint8_t* Vs = smem + TB;
@@ -553,12 +555,15 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
   int qt, bh;
   pick_work(p, qt, bh);
+  const int b = bh / p.H, h = bh - b * p.H;
   const size_t rowbase = static_cast<size_t>(bh) * p.TqPad;  // query side
   const size_t kbase = static_cast<size_t>(bh) * p.TkPad;    // key side
   const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
   if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];
+  const size_t rstride = static_cast<size_t>(p.H) * HD;                 // floats between token rows
+  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD;  // token 0 of this head
 
   const int q0 = qt * BM + w * 32;
   int qpos[2], qbkt[2];
@@ -570,18 +575,17 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
   }
   const WaveRows wr = wave_rows(qpos, qbkt);
   float Qf[2][16];  // [qb][t], d = 16g + t
-  {
-    const float* qg = static_cast<const float*>(p.q) + (rowbase + q0) * HD;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < 2; ++qb) {
+    const float* qrow = static_cast<const float*>(p.q) + head0 + src_row(qpos[qb], p.T) * rstride;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const float4 v = *reinterpret_cast<const float4*>(qg + (qb * 16 + r16) * HD + 16 * g + 4 * t4);
-        Qf[qb][4 * t4 + 0] = v.x;
-        Qf[qb][4 * t4 + 1] = v.y;
-        Qf[qb][4 * t4 + 2] = v.z;
-        Qf[qb][4 * t4 + 3] = v.w;
-      }
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const float4 v = *reinterpret_cast<const float4*>(qrow + 16 * g + 4 * t4);
+      Qf[qb][4 * t4 + 0] = v.x;
+      Qf[qb][4 * t4 + 1] = v.y;
+      Qf[qb][4 * t4 + 2] = v.z;
+      Qf[qb][4 * t4 + 3] = v.w;
+    }
   }
 
   f32x4 Oacc[4][2];
@@ -592,17 +596,26 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
   float m[2] = {-INFINITY, -INFINITY};
   float l[2] = {0.f, 0.f};
 
-  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + kbase * HD * ESZ;
-  const uint8_t* vg = static_cast<const uint8_t*>(p.vt) + kbase * HD * ESZ;
+  const float* kg = static_cast<const float*>(p.k) + head0;
+  const float* vg = static_cast<const float*>(p.v) + head0;
   const int32_t* kig = p.k_idx + kbase;
   const int32_t* kbg = HASH ? p.k_bkt + kbase : nullptr;
-  TileRegs<LOADS> tr;
 
   for (int j = rng.x; j < rng.y; ++j) {
     if (kst[j].x > qs.y) continue;  // causal extremum test (uniform)
-    tile_load<HASH, ESZ, CH, LOADS>(tr, kg, vg, kig, kbg, p.TkPad, j, tid);
     __syncthreads();  // previous tile no longer read
-    tile_store<HASH, ESZ, CH, LOADS>(tr, Ks, Vs, Kp, Kb, tid);
+    // K and V rows of the tile (16 chunks of 16 bytes per row), through k_idx
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i, row = u >> 4, ch = u & 15;
+      const size_t off = src_row(kig[j * BN + row], p.T) * rstride + ch * 4;
+      const float4 kr = *reinterpret_cast<const float4*>(kg + off);
+      const float4 vr = *reinterpret_cast<const float4*>(vg + off);
+      *reinterpret_cast<float4*>(Ks + row * HD * 4 + ((ch ^ swz_k(row)) * 16)) = kr;
+      *reinterpret_cast<float4*>(Vs + row * HD * 4 + ch * 16) = vr;
+    }
+    if (tid < BN) Kp[tid] = kig[j * BN + tid];
+    else if (HASH && tid < 2 * BN) Kb[tid - BN] = kbg[j * BN + tid - BN];
     __syncthreads();
     if (tile_empty_for<HASH>(kst[j], wr)) continue;
 
@@ -648,19 +661,22 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
       for (int db = 0; db < 4; ++db) Oacc[db][qb] *= alpha;
     }
 
+    // O^T += V^T P^T: the A operand of block kb, element e is V[key][d] for
+    // key 32 (kb >> 1) + 8 g + 4 (kb & 1) + e, d = 16 db + r16.
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int d = db * 16 + r16;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const int ch = 8 * (kb >> 1) + 2 * g + (kb & 1);  // keys 32kc + 8g + 4hb + 0..3
-        const float4 a = *reinterpret_cast<const float4*>(&Vs[d * BN * 4 + ((ch ^ (d & 7)) * 16)]);
+        const int key0 = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1);
+        const float* vcol = reinterpret_cast<const float*>(Vs) + key0 * HD + d;
+        const float a0 = vcol[0], a1 = vcol[HD], a2 = vcol[2 * HD], a3 = vcol[3 * HD];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, S[kb][qb][0], Oacc[db][qb], 0, 0, 0);
-          Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, S[kb][qb][1], Oacc[db][qb], 0, 0, 0);
-          Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, S[kb][qb][2], Oacc[db][qb], 0, 0, 0);
-          Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, S[kb][qb][3], Oacc[db][qb], 0, 0, 0);
+          Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, S[kb][qb][0], Oacc[db][qb], 0, 0, 0);
+          Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, S[kb][qb][1], Oacc[db][qb], 0, 0, 0);
+          Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, S[kb][qb][2], Oacc[db][qb], 0, 0, 0);
+          Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a3, S[kb][qb][3], Oacc[db][qb], 0, 0, 0);
         }
       }
     }
@@ -708,18 +724,18 @@ using namespace scfa;
 
 extern "C" {
 
-int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v_t,
+int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v,
                        const int32_t* q_idx, const int32_t* k_idx, const int32_t* qstats, const int32_t* kstats,
                        const int32_t* fwd_tab, const int32_t* order, int B, int H, int T, int Tc, int D, float scale,
                        void* O, float* lse, hipStream_t stream) {
-  if (!q || !k || !v_t || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !O || !lse) return SCFA_ERR_INVALID;
+  if (!q || !k || !v || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !O || !lse) return SCFA_ERR_INVALID;
   const int st = check_common(dtype_in, dtype_out, B, H, T, D, scale);
   if (st != SCFA_OK) return st;
   if (Tc < SCFA_ROW_ALIGN || Tc % SCFA_ROW_ALIGN) return SCFA_ERR_INVALID;
   FwdParams p{};
   p.q = q;
   p.k = k;
-  p.vt = v_t;
+  p.v = v;
   p.q_idx = q_idx;
   p.k_idx = k_idx;
   p.q_bkt = nullptr;
@@ -742,12 +758,12 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
   return dispatch_fwd<false, true>(dtype_in, dtype_out, p, stream);
 }
 
-int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v_t,
+int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v,
                          const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
                          const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, const int32_t* order,
                          int B, int H, int T, int Tq, int Tk, int D, float scale, void* O, float* lse,
                          hipStream_t stream) {
-  if (!q || !k || !v_t || !q_idx || !k_idx || !q_bkt || !k_bkt || !qstats || !kstats || !fwd_tab || !O || !lse)
+  if (!q || !k || !v || !q_idx || !k_idx || !q_bkt || !k_bkt || !qstats || !kstats || !fwd_tab || !O || !lse)
     return SCFA_ERR_INVALID;
   const int st = check_common(dtype_in, dtype_out, B, H, T, D, scale);
   if (st != SCFA_OK) return st;
@@ -755,7 +771,7 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
   FwdParams p{};
   p.q = q;
   p.k = k;
-  p.vt = v_t;
+  p.v = v;
   p.q_idx = q_idx;
   p.k_idx = k_idx;
   p.q_bkt = q_bkt;

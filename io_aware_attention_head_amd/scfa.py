@@ -204,25 +204,32 @@ def scfa_work_order(tab, span, order, stream=None):
     _check(lib().scfa_work_order(_p(tab), B, H, n, span, _p(order), _stream(stream, tab)), "scfa_work_order")
 
 
-def scfa_qk_sparse_fwd(q_c, k_c, v_t, q_idx, k_idx, qstats, kstats, fwd_tab, T, O, lse, scale=None, stream=None,
+def scfa_qk_sparse_fwd(q, k, v, q_idx, k_idx, qstats, kstats, fwd_tab, T, O, lse, scale=None, stream=None,
                        order=None):
-    B, H, Tc, D = q_c.shape
+    """q, k, v: original (B,T,H,D) tensors; q_idx, k_idx (B,H,Tc) compacted."""
+    B, Tq_, H, D = q.shape
+    if Tq_ != T:
+        raise ScfaError("q must be the original (B,T,H,D) tensor")
+    Tc = q_idx.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None else scale
-    _check(lib().scfa_qk_sparse_fwd(_dt(q_c), _dt(O), _p(q_c), _p(k_c), _p(v_t), _p(q_idx), _p(k_idx), _p(qstats),
+    _check(lib().scfa_qk_sparse_fwd(_dt(q), _dt(O), _p(q), _p(k), _p(v), _p(q_idx), _p(k_idx), _p(qstats),
                                     _p(kstats), _p(fwd_tab), _p(order), B, H, T, Tc, D, scale, _p(O), _p(lse),
-                                    _stream(stream, q_c)), "scfa_qk_sparse_fwd")
+                                    _stream(stream, q)), "scfa_qk_sparse_fwd")
 
 
-def scfa_hash_sparse_fwd(q_s, k_s, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, T, O, lse, scale=None,
+def scfa_hash_sparse_fwd(q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, T, O, lse, scale=None,
                          stream=None, order=None, Tq=None, Tk=None):
-    """Tq / Tk: query / key rows as passed to the range table (default: T)."""
-    B, H, Tp, D = q_s.shape
+    """q, k, v: original (B,T,H,D) tensors. Tq / Tk: query / key rows as
+    passed to the range table (default: T)."""
+    B, Tq_, H, D = q.shape
+    if Tq_ != T:
+        raise ScfaError("q must be the original (B,T,H,D) tensor")
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     Tq = T if Tq is None else Tq
     Tk = T if Tk is None else Tk
-    _check(lib().scfa_hash_sparse_fwd(_dt(q_s), _dt(O), _p(q_s), _p(k_s), _p(v_t), _p(q_idx), _p(k_idx), _p(q_bkt),
+    _check(lib().scfa_hash_sparse_fwd(_dt(q), _dt(O), _p(q), _p(k), _p(v), _p(q_idx), _p(k_idx), _p(q_bkt),
                                       _p(k_bkt), _p(qstats), _p(kstats), _p(fwd_tab), _p(order), B, H, T, Tq, Tk, D,
-                                      scale, _p(O), _p(lse), _stream(stream, q_s)), "scfa_hash_sparse_fwd")
+                                      scale, _p(O), _p(lse), _stream(stream, q)), "scfa_hash_sparse_fwd")
 
 
 def scfa_bwd_workspace_bytes(mode, B, H, Tq, Tk, D=64) -> int:
@@ -245,10 +252,13 @@ def scfa_bwd(mode, q, k, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_ta
 
 @dataclasses.dataclass
 class Prepared:
-    """Compacted / sorted operands of one attention call (head-major).
+    """Index arrays of one attention call (head-major) and its operands.
 
-    Tq, Tk are the query / key rows as passed to the range table; the buffers
-    hold pad_rows(Tq) / pad_rows(Tk) rows per head."""
+    The forward reads q_in, k_in, v_in (original (B,T,H,D) order) through
+    q_idx / k_idx. The backward reads gathered head-major copies q, k (rows)
+    and v_t (transposed), which gather_operands() fills on first use.
+    Tq, Tk are the query / key rows as passed to the range table; the index
+    arrays hold pad_rows(Tq) / pad_rows(Tk) rows per head."""
     mode: str
     B: int
     H: int
@@ -256,14 +266,34 @@ class Prepared:
     D: int
     Tq: int
     Tk: int
-    q: torch.Tensor  # (B,H,pad(Tq),D) rows
-    k: torch.Tensor  # (B,H,pad(Tk),D) rows
-    v_t: torch.Tensor  # (B,H,D,pad(Tk)) transposed
+    q_in: torch.Tensor
+    k_in: torch.Tensor
+    v_in: torch.Tensor
     q_idx: torch.Tensor
     k_idx: torch.Tensor
     q_bkt: Optional[torch.Tensor] = None
     k_bkt: Optional[torch.Tensor] = None
+    q: Optional[torch.Tensor] = None  # (B,H,pad(Tq),D) rows
+    k: Optional[torch.Tensor] = None  # (B,H,pad(Tk),D) rows
+    v_t: Optional[torch.Tensor] = None  # (B,H,D,pad(Tk)) transposed
     extra: dict = dataclasses.field(default_factory=dict)
+
+
+def gather_operands(pre: Prepared, stream=None) -> Prepared:
+    """Head-major copies of the operands in index order (pad rows zero), as
+    the backward kernels read them; a no-op for the ones already present."""
+    B, H, D = pre.B, pre.H, pre.D
+    TqP, TkP = pad_rows(pre.Tq), pad_rows(pre.Tk)
+    if pre.q is None:
+        pre.q = _empty((B, H, TqP, D), pre.q_in.dtype, pre.q_in)
+        scfa_gather(pre.q_in, pre.q_idx, SCFA_ROWS, pre.q, stream)
+    if pre.k is None:
+        pre.k = _empty((B, H, TkP, D), pre.k_in.dtype, pre.k_in)
+        scfa_gather(pre.k_in, pre.k_idx, SCFA_ROWS, pre.k, stream)
+    if pre.v_t is None:
+        pre.v_t = _empty((B, H, D, TkP), pre.v_in.dtype, pre.v_in)
+        scfa_gather(pre.v_in, pre.k_idx, SCFA_COLS, pre.v_t, stream)
+    return pre
 
 
 @dataclasses.dataclass
@@ -282,10 +312,10 @@ def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
-def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, stream=None) -> Prepared:
-    """QK-drop preprocessing: counts, compaction of Q and K (rows) and the
-    transposed gather of V by the compacted key positions. Reads the max kept
-    count back to the host once (to size Tc) unless Tc is given."""
+def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, rows: bool = False, stream=None) -> Prepared:
+    """QK-drop preprocessing: counts and the compacted index arrays (with
+    rows=True also the compacted Q and K rows). Reads the max kept count back
+    to the host once (to size Tc) unless Tc is given."""
     B, T, H, D = q.shape
     dev = q
     i32 = torch.int32
@@ -298,13 +328,12 @@ def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, stream=None) -
     if Tc is None:
         Tc = pad_rows(max(1, int(torch.maximum(mq, mk).item())))
     dev_err = torch.zeros((1,), dtype=i32, device=q.device)
-    q_c, k_c = _empty((B, H, Tc, D), q.dtype, dev), _empty((B, H, Tc, D), k.dtype, dev)
+    q_c = _empty((B, H, Tc, D), q.dtype, dev) if rows else None
+    k_c = _empty((B, H, Tc, D), k.dtype, dev) if rows else None
     q_idx, k_idx = _empty((B, H, Tc), i32, dev), _empty((B, H, Tc), i32, dev)
     scfa_qk_compact(q, keep_q, cq, oq, Tc, SCFA_Q_PAD, q_c, q_idx, dev_err, stream)
     scfa_qk_compact(k, keep_k, ck, ok, Tc, SCFA_K_PAD, k_c, k_idx, dev_err, stream)
-    v_t = _empty((B, H, D, Tc), v.dtype, dev)
-    scfa_gather(v, k_idx, SCFA_COLS, v_t, stream)
-    return Prepared("qk", B, H, T, D, Tc, Tc, q_c, k_c, v_t, q_idx, k_idx,
+    return Prepared("qk", B, H, T, D, Tc, Tc, q, k, v, q_idx, k_idx, q=q_c, k=k_c,
                     extra={"count_q": cq, "count_k": ck, "max_q": mq, "max_k": mk, "dev_err": dev_err})
 
 
@@ -312,7 +341,7 @@ def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None) -> Prep
     """Hash-sparse preprocessing: LSH buckets of Q and K, stable counting sort
     per head, then (aligned=True) the bucket-aligned layout (query buckets
     start at multiples of the query tile, key buckets at multiples of the key
-    tile), gathers of Q, K (rows) and V (transposed) into that order."""
+    tile). The operands stay in original order (gathered on load)."""
     B, T, H, D = q.shape
     dev = q
     i32 = torch.int32
@@ -341,28 +370,18 @@ def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None) -> Prep
     else:
         Tq = Tk = T
         q_idx, k_idx, q_bkt, k_bkt = perm_q, perm_k, bs_q, bs_k
-    q_s, k_s = _empty((B, H, pad_rows(Tq), D), q.dtype, dev), _empty((B, H, pad_rows(Tk), D), k.dtype, dev)
-    v_t = _empty((B, H, D, pad_rows(Tk)), v.dtype, dev)
-    scfa_gather(q, q_idx, SCFA_ROWS, q_s, stream)
-    scfa_gather(k, k_idx, SCFA_ROWS, k_s, stream)
-    scfa_gather(v, k_idx, SCFA_COLS, v_t, stream)
-    return Prepared("hash", B, H, T, D, Tq, Tk, q_s, k_s, v_t, q_idx, k_idx, q_bkt, k_bkt, extra=extra)
+    return Prepared("hash", B, H, T, D, Tq, Tk, q, k, v, q_idx, k_idx, q_bkt, k_bkt, extra=extra)
 
 
 def prepare_dense(q, k, v, stream=None) -> Prepared:
     """Dense causal attention on the same kernel: positions 0..T-1 for both
-    queries and keys (the QK path with nothing dropped), head-major gathers."""
+    queries and keys (the QK path with nothing dropped)."""
     B, T, H, D = q.shape
     Tp = pad_rows(T)
     ar = torch.arange(Tp, dtype=torch.int32, device=q.device)
     q_idx = torch.where(ar < T, ar, torch.full_like(ar, SCFA_Q_PAD)).expand(B, H, Tp).contiguous()
     k_idx = torch.where(ar < T, ar, torch.full_like(ar, SCFA_K_PAD)).expand(B, H, Tp).contiguous()
-    q_s, k_s = _empty((B, H, Tp, D), q.dtype, q), _empty((B, H, Tp, D), k.dtype, q)
-    v_t = _empty((B, H, D, Tp), v.dtype, q)
-    scfa_gather(q, q_idx, SCFA_ROWS, q_s, stream)
-    scfa_gather(k, k_idx, SCFA_ROWS, k_s, stream)
-    scfa_gather(v, k_idx, SCFA_COLS, v_t, stream)
-    return Prepared("dense", B, H, T, D, Tp, Tp, q_s, k_s, v_t, q_idx, k_idx)
+    return Prepared("dense", B, H, T, D, Tp, Tp, q, k, v, q_idx, k_idx)
 
 
 def _table_mode(mode: str) -> int:
@@ -376,43 +395,46 @@ def build_tables(pre: Prepared, Bm: int = SCFA_TILE_M, Bn: int = SCFA_TILE_N, st
     B, H = pre.B, pre.H
     nQt, nKt = pad_rows(pre.Tq) // Bm, pad_rows(pre.Tk) // Bn
     i32 = torch.int32
-    t = Tables(_empty((B, H, nQt, 4), i32, pre.q), _empty((B, H, nKt, 4), i32, pre.q), _empty((B, H, nQt, 2), i32, pre.q),
-               _empty((B, H, nKt, 2), i32, pre.q), _empty((B, H), i32, pre.q), Bm, Bn)
+    d = pre.q_idx
+    t = Tables(_empty((B, H, nQt, 4), i32, d), _empty((B, H, nKt, 4), i32, d), _empty((B, H, nQt, 2), i32, d),
+               _empty((B, H, nKt, 2), i32, d), _empty((B, H), i32, d), Bm, Bn)
     scfa_range_table(_table_mode(pre.mode), pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, B, H, pre.Tq, pre.Tk, Bm, Bn,
                      t.qstats, t.kstats, t.fwd, t.bwd, t.tiles, stream)
-    t.fwd_order = _empty((B * H * nQt,), i32, pre.q)
+    t.fwd_order = _empty((B * H * nQt,), i32, d)
     scfa_work_order(t.fwd, nKt, t.fwd_order, stream)
     return t
 
 
 def count_visible(pre: Prepared, stream=None) -> torch.Tensor:
-    pairs = _empty((pre.B, pre.H), torch.int64, pre.q)
+    pairs = _empty((pre.B, pre.H), torch.int64, pre.q_idx)
     scfa_count_visible(_table_mode(pre.mode), pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, pre.B, pre.H, pre.Tq, pre.Tk,
                        pairs, stream)
     return pairs
 
 
 def forward(pre: Prepared, tab: Tables, out_dtype=torch.float32, scale=None, O=None, lse=None, stream=None):
-    """Attention forward on prepared operands. Returns O (B,T,H,D) in original
-    order and LSE (B,H,T) float32."""
+    """Attention forward on the original operands through the prepared index
+    arrays. Returns O (B,T,H,D) in original order and LSE (B,H,T) float32."""
     B, H, T, D = pre.B, pre.H, pre.T, pre.D
     if O is None:
-        O = _empty((B, T, H, D), out_dtype, pre.q)
+        O = _empty((B, T, H, D), out_dtype, pre.q_in)
     if lse is None:
-        lse = _empty((B, H, T), torch.float32, pre.q)
+        lse = _empty((B, H, T), torch.float32, pre.q_in)
     if pre.mode == "hash":
-        scfa_hash_sparse_fwd(pre.q, pre.k, pre.v_t, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats,
+        scfa_hash_sparse_fwd(pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats,
                              tab.fwd, T, O, lse, scale, stream, order=tab.fwd_order, Tq=pre.Tq, Tk=pre.Tk)
     else:
-        scfa_qk_sparse_fwd(pre.q, pre.k, pre.v_t, pre.q_idx, pre.k_idx, tab.qstats, tab.kstats, tab.fwd, T, O, lse,
+        scfa_qk_sparse_fwd(pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx, tab.qstats, tab.kstats, tab.fwd, T, O, lse,
                            scale, stream, order=tab.fwd_order)
     return O, lse
 
 
 def backward(pre: Prepared, tab: Tables, O, lse, dO, scale=None, grads=None, workspace=None, stream=None):
-    """Gradients w.r.t. the original-order q, k, v (fp32, (B,T,H,D))."""
+    """Gradients w.r.t. the original-order q, k, v (fp32, (B,T,H,D)). Gathers
+    the head-major operands first if they are not there yet."""
     B, H, T, D = pre.B, pre.H, pre.T, pre.D
     mode = _table_mode(pre.mode)
+    gather_operands(pre, stream)
     if grads is None:
         grads = tuple(_empty((B, T, H, D), torch.float32, pre.q) for _ in range(3))
     if workspace is None:
@@ -446,12 +468,14 @@ def dense_causal_attention(q, k, v, out_dtype=torch.float32, scale=None):
 class Plan:
     """Preallocated pipeline for one shape and mode.
 
-    mode "hash": bucket -> sort -> bucket-aligned layout -> gathers -> tables
-                 -> forward.
-    mode "qk":   count -> compact -> gather -> tables -> forward, with a fixed
-                 compacted length Tc (default: pad_rows(T), which always fits).
-    mode "dense": gathers -> tables -> forward on positions 0..T-1.
-    Each stage is a separate method so it can be timed on its own.
+    mode "hash": bucket -> sort -> bucket-aligned layout -> tables -> forward.
+    mode "qk":   count -> compact (index arrays) -> tables -> forward, with a
+                 fixed compacted length Tc (default: pad_rows(T), which always
+                 fits).
+    mode "dense": tables -> forward on positions 0..T-1.
+    The forward gathers on load; backward() first gathers head-major copies
+    (gather stage). Each stage is a separate method so it can be timed on its
+    own.
     """
 
     def __init__(self, mode, B, H, T, D=64, dtype=torch.bfloat16, nb=16, Tc=None, out_dtype=torch.float32,
@@ -479,8 +503,9 @@ class Plan:
         else:
             self.Tq = self.Tk = pad_rows(T)
         TqP, TkP = pad_rows(self.Tq), pad_rows(self.Tk)
-        self.q_s, self.k_s = e((B, H, TqP, D), dtype), e((B, H, TkP, D), dtype)
-        self.v_t = e((B, H, D, TkP), dtype)
+        self.q_s = self.k_s = self.v_t = None  # gathered copies, allocated by gather()
+        self.x = None  # operands of the last prepare()
+        self.device = d
         self.q_idx, self.k_idx = e((B, H, TqP)), e((B, H, TkP))
         self.q_bkt = self.k_bkt = None
         self.dev_err = torch.zeros((1,), dtype=i32, device=d)
@@ -524,15 +549,20 @@ class Plan:
     def compact(self, q, k, keep_q, keep_k, stream=None):
         scfa_qk_count(keep_q, self.cnt[0], self.mx[0], self.choff[0], stream)
         scfa_qk_count(keep_k, self.cnt[1], self.mx[1], self.choff[1], stream)
-        scfa_qk_compact(q, keep_q, self.cnt[0], self.choff[0], self.Tq, SCFA_Q_PAD, self.q_s, self.q_idx,
+        scfa_qk_compact(q, keep_q, self.cnt[0], self.choff[0], self.Tq, SCFA_Q_PAD, None, self.q_idx,
                         self.dev_err, stream)
-        scfa_qk_compact(k, keep_k, self.cnt[1], self.choff[1], self.Tk, SCFA_K_PAD, self.k_s, self.k_idx,
+        scfa_qk_compact(k, keep_k, self.cnt[1], self.choff[1], self.Tk, SCFA_K_PAD, None, self.k_idx,
                         self.dev_err, stream)
 
     def gather(self, q, k, v, stream=None):
-        if self.mode != "qk":
-            scfa_gather(q, self.q_idx, SCFA_ROWS, self.q_s, stream)
-            scfa_gather(k, self.k_idx, SCFA_ROWS, self.k_s, stream)
+        """Head-major copies in index order, for the backward."""
+        if self.q_s is None:
+            B, H, D = self.B, self.H, self.D
+            TqP, TkP = pad_rows(self.Tq), pad_rows(self.Tk)
+            e = lambda shape: torch.empty(shape, dtype=self.dtype, device=self.device)  # noqa: E731
+            self.q_s, self.k_s, self.v_t = e((B, H, TqP, D)), e((B, H, TkP, D)), e((B, H, D, TkP))
+        scfa_gather(q, self.q_idx, SCFA_ROWS, self.q_s, stream)
+        scfa_gather(k, self.k_idx, SCFA_ROWS, self.k_s, stream)
         scfa_gather(v, self.k_idx, SCFA_COLS, self.v_t, stream)
 
     def tables(self, stream=None):
@@ -545,9 +575,13 @@ class Plan:
         forward(self.prepared(), self.tab, self.out_dtype, self.scale, self.O, self.lse, stream)
 
     def backward(self, dO, stream=None):
-        """Gradients of the last forward() w.r.t. q, k, v (fp32, original order)."""
+        """Gradients of the last forward() w.r.t. q, k, v (fp32, original order):
+        gathers, then the backward kernels."""
+        if self.x is None:
+            raise ScfaError("backward needs a prepared forward")
+        self.gather(self.x["q"], self.x["k"], self.x["v"], stream)
         if self._grads is None:
-            d = self.q_s.device
+            d = self.device
             self._grads = tuple(torch.empty((self.B, self.T, self.H, self.D), dtype=torch.float32, device=d)
                                 for _ in range(3))
             self._bws = torch.empty((scfa_bwd_workspace_bytes(_table_mode(self.mode), self.B, self.H, self.Tq, self.Tk,
@@ -568,7 +602,7 @@ class Plan:
             self.sort(stream)
         elif self.mode == "qk":
             self.compact(x["q"], x["k"], x["keep_q"], x["keep_k"], stream)
-        self.gather(x["q"], x["k"], x["v"], stream)
+        self.x = x
         self.tables(stream)
 
     def run(self, x: dict, stream=None):
@@ -578,5 +612,8 @@ class Plan:
         return self.O, self.lse
 
     def prepared(self) -> Prepared:
-        return Prepared(self.mode, self.B, self.H, self.T, self.D, self.Tq, self.Tk, self.q_s, self.k_s, self.v_t,
-                        self.q_idx, self.k_idx, self.q_bkt, self.k_bkt)
+        if self.x is None:
+            raise ScfaError("call prepare() first")
+        x = self.x
+        return Prepared(self.mode, self.B, self.H, self.T, self.D, self.Tq, self.Tk, x["q"], x["k"], x["v"],
+                        self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.q_s, self.k_s, self.v_t)

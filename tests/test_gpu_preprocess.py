@@ -67,7 +67,8 @@ def test_qk_compaction_bitexact(w):
     announce(f"qk compaction {w.name}")
     x = make_inputs(w)
     g = to_dev(x)
-    pre = scfa.prepare_qk(g["q"], g["k"], g["v"], g["keep_q"], g["keep_k"])
+    pre = scfa.prepare_qk(g["q"], g["k"], g["v"], g["keep_q"], g["keep_k"], rows=True)
+    scfa.gather_operands(pre)  # v_t only: compaction wrote the q and k rows
     torch.cuda.synchronize()
     assert int(pre.extra["dev_err"].item()) == 0
     kq, kk = x["keep_q"].numpy(), x["keep_k"].numpy()
@@ -85,6 +86,11 @@ def test_qk_compaction_bitexact(w):
     assert np.array_equal(np_bits(pre.k), kc)
     vref = oracle.gather_rows(np_bits(x["v"]), ki)
     assert np.array_equal(np_bits(pre.v_t), vref.transpose(0, 1, 3, 2))
+    # the same rows through the plain gather (pads zero, as compaction writes them)
+    pre2 = scfa.gather_operands(scfa.prepare_qk(g["q"], g["k"], g["v"], g["keep_q"], g["keep_k"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(np_bits(pre2.q), qc)
+    assert np.array_equal(np_bits(pre2.k), kc)
     tab = scfa.build_tables(pre)
     torch.cuda.synchronize()
     _tables_match("qk", pre, tab, Tc, scfa.SCFA_TILE_M, scfa.SCFA_TILE_N)
@@ -124,6 +130,7 @@ def test_hash_bucket_sort_gather_bitexact(w):
         assert np.array_equal(sidx.cpu().numpy(), ri)
         assert np.array_equal(sbkt.cpu().numpy(), rb)
         assert np.array_equal(soff.cpu().numpy(), ro)
+    scfa.gather_operands(pre)
     qi, ki = pre.q_idx.cpu().numpy(), pre.k_idx.cpu().numpy()
     assert np.array_equal(np_bits(pre.q), oracle.gather_rows(np_bits(x["q"]), qi))
     assert np.array_equal(np_bits(pre.k), oracle.gather_rows(np_bits(x["k"]), ki))
