@@ -167,27 +167,71 @@ __device__ inline bool tile_full_for(const int4& ks, const WaveRows& wr, int j, 
   return full;
 }
 
-// Scores of keys that are not visible to the lane's query become -inf.
-// Accumulator element e of block kb in lane group g is key
-// 32 (kb >> 1) + 8 g + 4 (kb & 1) + e of the tile.
-template <bool HASH>
-__device__ inline void apply_mask(f32x4 (&S)[4][2], const int32_t* kp, const int32_t* kbk, const int (&qpos)[2],
-                                  const int (&qbkt)[2], int g) {
+// The compares below go to VCC and are consumed at once, so a masked tile
+// holds no per-element lane masks in scalar registers (-inf comes from a
+// VGPR: VCC already takes the one scalar operand slot).
+// 0 if a >= b, else -inf.
+__device__ __forceinline__ float bias_if_ge(int a, int b) {
+  float r;
+  asm("v_cmp_ge_i32_e32 vcc, %1, %2\n\tv_cndmask_b32_e64 %0, %3, 0, vcc"
+      : "=v"(r)
+      : "v"(a), "v"(b), "v"(0xff800000u)
+      : "vcc");
+  return r;
+}
+// x if a == b, else -inf.
+__device__ __forceinline__ float keep_if_eq(float x, int a, int b) {
+  asm("v_cmp_eq_i32_e32 vcc, %1, %2\n\tv_cndmask_b32_e32 %0, %3, %0, vcc"
+      : "+v"(x)
+      : "v"(a), "v"(b), "v"(0xff800000u)
+      : "vcc");
+  return x;
+}
+
+// Mask bias of a tile: element e of block kb in lane group g (key
+// 32 (kb >> 1) + 8 g + 4 (kb & 1) + e of the tile) is 0 if that key is
+// visible to the lane's query, else -inf. BUCKETS: also compare buckets (not
+// needed when the tile and the wave's queries are all in one bucket: a tile
+// that is not skipped then has the queries' bucket).
+template <bool BUCKETS>
+__device__ inline void bias_tile(f32x4 (&C)[4][2], const int32_t* kp, const int32_t* kbk, const int (&qpos)[2],
+                                 const int (&qbkt)[2], int g) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const int kbase = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1);
     const int4 kp4 = *reinterpret_cast<const int4*>(&kp[kbase]);
     int4 kb4 = make_int4(0, 0, 0, 0);
-    if (HASH) kb4 = *reinterpret_cast<const int4*>(&kbk[kbase]);
+    if (BUCKETS) kb4 = *reinterpret_cast<const int4*>(&kbk[kbase]);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int qp = qpos[qb], qh = qbkt[qb];
-      if (!(kp4.x <= qp && (!HASH || kb4.x == qh))) S[kb][qb][0] = -INFINITY;
-      if (!(kp4.y <= qp && (!HASH || kb4.y == qh))) S[kb][qb][1] = -INFINITY;
-      if (!(kp4.z <= qp && (!HASH || kb4.z == qh))) S[kb][qb][2] = -INFINITY;
-      if (!(kp4.w <= qp && (!HASH || kb4.w == qh))) S[kb][qb][3] = -INFINITY;
+      const int qp = qpos[qb];
+      f32x4 c;
+      c[0] = bias_if_ge(qp, kp4.x);
+      c[1] = bias_if_ge(qp, kp4.y);
+      c[2] = bias_if_ge(qp, kp4.z);
+      c[3] = bias_if_ge(qp, kp4.w);
+      if (BUCKETS) {
+        const int qh = qbkt[qb];
+        c[0] = keep_if_eq(c[0], qh, kb4.x);
+        c[1] = keep_if_eq(c[1], qh, kb4.y);
+        c[2] = keep_if_eq(c[2], qh, kb4.z);
+        c[3] = keep_if_eq(c[3], qh, kb4.w);
+      }
+      C[kb][qb] = c;
     }
   }
+}
+
+// Mask bias of a tile that is not fully visible: positions only when the
+// tile's keys and the wave's real queries share one bucket (always so in QK
+// mode and in the bucket-aligned layout), positions and buckets otherwise.
+template <bool HASH>
+__device__ inline void mask_bias(f32x4 (&C)[4][2], const int4& ks, const WaveRows& wr, const int32_t* kp,
+                                 const int32_t* kbk, const int (&qpos)[2], const int (&qbkt)[2], int g) {
+  if (!HASH || (ks.z == ks.w && wr.minb == wr.maxb))
+    bias_tile<false>(C, kp, kbk, qpos, qbkt, g);
+  else
+    bias_tile<true>(C, kp, kbk, qpos, qbkt, g);
 }
 
 // Row max (log2 units) of a score tile: 16 in-lane values per query column
@@ -311,8 +355,25 @@ __device__ inline int src_row(int pos, int T) { return (pos >= 0 && pos < T) ? p
 // banks.
 __device__ inline int swz_v(int r, int c) { return c ^ (2 * (r & 3)); }
 
+// S^T += K Q^T for one staged key tile: 2 x 4 x 2 MFMAs over the two
+// 32-wide halves of D. K rows are read permuted (key_row) so that each
+// lane's accumulator elements are consecutive keys.
+__device__ __forceinline__ void scores_bf16(f32x4 (&S)[4][2], const uint8_t* Ks, const bf16x8 (&Qb)[2][2], int r16,
+                                            int g) {
+#pragma unroll
+  for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int row = key_row(kb, r16);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[row * HD * 2 + (((ds * 4 + g) ^ swz_k(row)) * 16)]);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Qb[qb][ds], S[kb][qb], 0, 0, 0);
+    }
+}
+
 template <bool HASH, bool ZERO_DROPPED, typename TOUT>
-__global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_fwd_bf16(FwdParams p) {
   constexpr int TB = BN * HD * 2;  // K tile and V tile, bytes each (8 KB)
   // Two stages of (K, V); after the loop the same bytes stage the output.
   __shared__ __align__(16) uint8_t smem[4 * TB];
@@ -320,6 +381,10 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
   __shared__ __align__(16) int32_t Kp[2][BN];
   __shared__ __align__(16) int32_t Kb[2][BN];
   __shared__ int32_t Qi[BM];
+  // statistics of the key tiles of this workgroup's range (ranges longer
+  // than kKstCap read them from global memory instead)
+  constexpr int kKstCap = 512;
+  __shared__ __align__(16) int4 Kst[kKstCap];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
@@ -333,6 +398,16 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
   if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];  // visible after the first barrier
+  const bool kst_lds = rng.y - rng.x <= kKstCap;
+  if (kst_lds)
+    for (int i = tid; i < rng.y - rng.x; i += 256) Kst[i] = kst[rng.x + i];
+  __syncthreads();
+  // statistics of key tile j, rng.x <= j < rng.y
+  auto kstat = [&](int j) -> int4 {
+    const int4 v = kst_lds ? Kst[j - rng.x] : kst[j];
+    return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                     __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
+  };
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
   const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;  // token 0 of this head
 
@@ -401,8 +476,11 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
     else if (HASH && ws == 1) dma4(kbg + j * BN, lane * 4, ldsb + s * BN * 4);
   };
 
+  // first tile from j on that passes the causal extremum test (hash ranges;
+  // every tile of a QK range passes it)
   auto next_tile = [&](int j) {
-    while (j < rng.y && kst[j].x > qs.y) ++j;  // causal extremum test (hash ranges)
+    if (HASH)
+      while (j < rng.y && kstat(j).x > qs.y) ++j;
     return j;
   };
 
@@ -417,13 +495,13 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
   dma_wait();
   __syncthreads();
   int s = 0;
-  int4 ks_cur = kst[min(j, p.nKt - 1)];
+  int4 ks_cur = j < rng.y ? kstat(j) : make_int4(0, 0, 0, 0);
   while (j < rng.y) {
     const int jnn = jn < rng.y ? next_tile(jn + 1) : rng.y;
     // small loads (statistics, and the rows of the tile after next) are
     // issued before the DMA, so that waiting for them never waits for it
     const int4 ks = ks_cur;
-    ks_cur = kst[min(jn, p.nKt - 1)];
+    if (jn < rng.y) ks_cur = kstat(jn);
     int pos_nn[2];
     tile_rows(jnn, pos_nn);
     __builtin_amdgcn_sched_barrier(0);
@@ -433,22 +511,20 @@ __global__ __launch_bounds__(256) void k_fwd_bf16(FwdParams p) {
       const uint8_t* Ks = smem + s * TB;
       const uint8_t* Vs = smem + (2 + s) * TB;
       // -- S^T = K Q^T ------------------------------------------------------
+      // A tile that is not fully visible starts the accumulators at the
+      // mask bias (0 or -inf), so masked scores come out of the MFMAs as
+      // -inf; both branches define S afresh.
       f32x4 S[4][2];
+      if (tile_full_for<HASH>(ks, wr, j, p.Tk)) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < 2; ++ds)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int row = key_row(kb, r16);
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[row * HD * 2 + (((ds * 4 + g) ^ swz_k(row)) * 16)]);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Qb[qb][ds], S[kb][qb], 0, 0, 0);
-        }
-      if (!tile_full_for<HASH>(ks, wr, j, p.Tk)) apply_mask<HASH>(S, Kp[s], Kb[s], qpos, qbkt, g);
+          for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        scores_bf16(S, Ks, Qb, r16, g);
+      } else {
+        mask_bias<HASH>(S, ks, wr, Kp[s], Kb[s], qpos, qbkt, g);
+        scores_bf16(S, Ks, Qb, r16, g);
+      }
 
       // -- online softmax, lazy reference max ---------------------------------
       float mxs[2];
@@ -619,11 +695,15 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
     __syncthreads();
     if (tile_empty_for<HASH>(kst[j], wr)) continue;
 
-    f32x4 S[4][2];
+    f32x4 S[4][2];  // starts at the mask bias (0 or -inf) unless all pairs are visible
+    if (tile_full_for<HASH>(kst[j], wr, j, p.Tk)) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+      mask_bias<HASH>(S, kst[j], wr, Kp, Kb, qpos, qbkt, g);
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int row = key_row(kb, r16);
@@ -639,7 +719,6 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
         }
       }
     }
-    if (!tile_full_for<HASH>(kst[j], wr, j, p.Tk)) apply_mask<HASH>(S, Kp, Kb, qpos, qbkt, g);
 
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
