@@ -234,17 +234,26 @@ __device__ inline void mask_bias(f32x4 (&C)[4][2], const int4& ks, const WaveRow
     bias_tile<true>(C, kp, kbk, qpos, qbkt, g);
 }
 
-// Row max (log2 units) of a score tile: 16 in-lane values per query column
-// (max3 chains), then across the 4 lane groups.
-__device__ inline float row_max_scaled(const f32x4 (&S)[4][2], int qb, float c) {
+// Max (log2 units) of the 16 scores a lane holds for query column qb
+// (max3 chains).
+__device__ inline float lane_max_scaled(const f32x4 (&S)[4][2], int qb, float c) {
   float mx = fmaxf(S[0][qb][0], fmaxf(S[0][qb][1], S[0][qb][2]));
 #pragma unroll
   for (int i = 3; i < 15; i += 2)
     mx = fmaxf(mx, fmaxf(S[i >> 2][qb][i & 3], S[(i + 1) >> 2][qb][(i + 1) & 3]));
   mx = fmaxf(mx, S[3][qb][3]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
   return mx * c;
+}
+
+// Max over the 4 lane groups that hold the same query column.
+__device__ inline float group_max(float mx) {
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  return fmaxf(mx, __shfl_xor(mx, 32));
+}
+
+// Row max (log2 units) of a score tile.
+__device__ inline float row_max_scaled(const f32x4 (&S)[4][2], int qb, float c) {
+  return group_max(lane_max_scaled(S, qb, c));
 }
 
 // Epilogue: normalise, stage the tile in LDS, write whole rows at the
@@ -527,13 +536,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       }
 
       // -- online softmax, lazy reference max ---------------------------------
-      float mxs[2];
+      // Each lane tests its own 16 scores per query against the shared
+      // reference; only when some lane is more than 2^kLazy above it is the
+      // row max taken across the lane groups and the reference moved.
+      float lmx[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) mxs[qb] = row_max_scaled(S, qb, p.c);
-      if (__ballot(mxs[0] > m[0] + kLazy || mxs[1] > m[1] + kLazy)) {
+      for (int qb = 0; qb < 2; ++qb) lmx[qb] = lane_max_scaled(S, qb, p.c);
+      if (__ballot(lmx[0] > m[0] + kLazy || lmx[1] > m[1] + kLazy)) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const float mnew = fmaxf(m[qb], mxs[qb]);
+          const float mnew = fmaxf(m[qb], group_max(lmx[qb]));
           const float muse = (mnew == -INFINITY) ? 0.f : mnew;
           const float alpha = __builtin_amdgcn_exp2f(m[qb] - muse);  // 1 when unchanged, 0 from -inf
           m[qb] = mnew;
