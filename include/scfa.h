@@ -130,6 +130,13 @@ int scfa_qk_compact(int dtype, const void* x, const uint8_t* keep, const int32_t
 int scfa_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb,
                      int32_t* bucket, hipStream_t stream);
 
+/* scfa_hash_bucket plus the chunk histogram of the stable sort:
+ *  chunk_counts  out (B, H, ceil(T / 256), nb) int32, the number of tokens
+ *                of each bucket among positions [256 c, 256 c + 256) of each
+ *                head (input of scfa_hash_layout).                          */
+int scfa_hash_bucket_counts(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb,
+                            int32_t* bucket, int32_t* chunk_counts, hipStream_t stream);
+
 /* Bytes of device workspace scfa_hash_sort needs. */
 size_t scfa_hash_sort_workspace_bytes(int B, int H, int T, int nb);
 
@@ -168,6 +175,22 @@ int scfa_hash_segment_rows(int T, int nb, int align);
 int scfa_hash_segments(const int32_t* perm, const int32_t* offsets, int B, int H, int T, int nb, int align,
                        int32_t pad_idx, int Tseg, int32_t* idx_seg, int32_t* bkt_seg, int32_t* seg_offsets,
                        int32_t* dev_err, hipStream_t stream);
+
+/* Sort and bucket-aligned layout in one launch, from the chunk counts of
+ * scfa_hash_bucket_counts: the outputs of scfa_hash_sort followed by
+ * scfa_hash_segments (same definitions, same bits). The explainer's hash
+ * preprocessing (3.4, "Hash-Sparse Attention: Sorting by Bucket and
+ * Two-Dimensional Tiling").
+ *  bucket, nb, pad_idx, perm, bucket_sorted, offsets   as scfa_hash_sort.
+ *  chunk_counts   (B, H, ceil(T / 256), nb): tokens of each bucket among
+ *                 positions [256 c, 256 c + 256) of each head.
+ *  align          0 (sort only: idx_seg, bkt_seg, seg_offsets unused and may
+ *                 be NULL) or 16, 32, 64, 128 (as scfa_hash_segments).
+ *  Tseg, idx_seg, bkt_seg, seg_offsets                 as scfa_hash_segments.
+ * Data errors: BUCKET_RANGE (such tokens are left out), SEGMENT_OVERFLOW.  */
+int scfa_hash_layout(const int32_t* bucket, const int32_t* chunk_counts, int B, int H, int T, int nb, int align,
+                     int32_t pad_idx, int Tseg, int32_t* perm, int32_t* bucket_sorted, int32_t* offsets,
+                     int32_t* idx_seg, int32_t* bkt_seg, int32_t* seg_offsets, int32_t* dev_err, hipStream_t stream);
 
 /* Gather rows into head-major order: out row r of head (b, h) is
  * x[b, idx[b,h,r], h, :] when 0 <= idx < T, else zero.

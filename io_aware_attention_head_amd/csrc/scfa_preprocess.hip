@@ -163,7 +163,7 @@ __device__ inline float unit_elem<uint16_t>(const u32x4& u, int e) {
 
 template <typename TIN, int HALF>
 __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* __restrict__ x, const float* __restrict__ R, int T,
-                                                     int H, int32_t* __restrict__ bucket) {
+                                                     int H, int32_t* __restrict__ bucket, int32_t* __restrict__ counts) {
   constexpr int D = 64;
   constexpr int EPU = 16 / sizeof(TIN);  // elements per 16-byte unit
   constexpr int NU = D / EPU;            // units per row (8 bf16, 16 fp32)
@@ -171,7 +171,9 @@ __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* __restrict__ x, 
   constexpr int LDW = NU * 4 + 4;        // LDS row stride in 32-bit words (+16 bytes)
   __shared__ double Rs[D * HALF];
   __shared__ __align__(16) uint32_t xs[4][64 * LDW];
+  __shared__ int32_t hs[2 * HALF];  // bucket counts of this workgroup's 256 tokens
   const int bh = blockIdx.y;
+  if (counts && threadIdx.x < 2 * HALF) hs[threadIdx.x] = 0;
   const int b = bh / H, h = bh - b * H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < D * HALF; i += 256) Rs[i] = static_cast<double>(R[static_cast<size_t>(h) * D * HALF + i]);
@@ -199,7 +201,6 @@ __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* __restrict__ x, 
     }
   }
   const int t = tw + lane;
-  if (t >= T) return;
   // argmax over [c ; -c], first index on ties: the positive half comes first.
   int bp = 0, bn = 0;
   double vp = c[0], vn = -c[0];
@@ -208,7 +209,14 @@ __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* __restrict__ x, 
     if (c[j] > vp) { vp = c[j]; bp = j; }
     if (-c[j] > vn) { vn = -c[j]; bn = j; }
   }
-  bucket[static_cast<size_t>(bh) * T + t] = (vn > vp) ? HALF + bn : bp;
+  const int v = (vn > vp) ? HALF + bn : bp;
+  if (t < T) bucket[static_cast<size_t>(bh) * T + t] = v;
+  if (counts) {  // the chunk histogram of the stable sort (chunk = this workgroup)
+    if (t < T) atomicAdd(&hs[v], 1);
+    __syncthreads();
+    if (threadIdx.x < 2 * HALF)
+      counts[(static_cast<size_t>(bh) * gridDim.x + blockIdx.x) * (2 * HALF) + threadIdx.x] = hs[threadIdx.x];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -242,27 +250,26 @@ __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ b
 
 // Workgroup (chunk c, head bh). base[v] = (tokens of the head with bucket
 // < v) + (tokens of bucket v in chunks before c); the chunk-0 workgroup also
-// writes offsets. Chunks at or beyond nC only write the pad entries.
+// writes offsets. With align > 0 the same workgroup also places its tokens
+// in the bucket-aligned layout (bucket v's rows start at A_v) and writes the
+// pad rows of that layout that fall in rows [256 c, 256 c + 256). Chunks at or
+// beyond nC only write pad entries.
 __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict__ bucket, int T, int Tp, int nb, int nC,
                                                       const int32_t* __restrict__ hist, int32_t pad,
                                                       int32_t* __restrict__ perm, int32_t* __restrict__ bsorted,
-                                                      int32_t* __restrict__ offsets) {
+                                                      int32_t* __restrict__ offsets, int align, int Tseg,
+                                                      int32_t* __restrict__ idx_seg, int32_t* __restrict__ bkt_seg,
+                                                      int32_t* __restrict__ seg_off, int32_t* dev_err) {
   __shared__ int32_t part_tot[4][64];
   __shared__ int32_t part_bef[4][64];
   __shared__ int32_t base_s[64];
   __shared__ int32_t wcnt[4][64];
+  __shared__ int32_t tot_s[64], off_s[65], aoff_s[65];
   const int c = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int32_t* pp = perm + static_cast<size_t>(bh) * Tp;
   int32_t* bp = bsorted + static_cast<size_t>(bh) * Tp;
   const int t = c * kSortChunk + threadIdx.x;
-  if (c >= nC) {  // pad-only chunk: no token of this chunk exists
-    if (t >= T && t < Tp) {
-      pp[t] = pad;
-      bp[t] = -1;
-    }
-    return;
-  }
   // per-bucket totals and the count before this chunk, lane = bucket
   {
     int tot = 0, bef = 0;
@@ -290,14 +297,39 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
     }
     const int off = x - tot;
     base_s[lane] = off + bef;
+    tot_s[lane] = tot;
+    off_s[lane] = off;
+    if (lane == 63) off_s[64] = x;
     if (c == 0) {
       if (lane < nb) offsets[static_cast<size_t>(bh) * (nb + 1) + lane] = off;
       if (lane == 63) offsets[static_cast<size_t>(bh) * (nb + 1) + nb] = x;  // all tokens
     }
+    if (align > 0) {
+      const int a = ((tot + align - 1) / align) * align;  // aligned rows of bucket `lane`
+      int y = a;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int z = __shfl_up(y, o);
+        if (lane >= o) y += z;
+      }
+      aoff_s[lane] = y - a;
+      if (lane == 63) aoff_s[64] = y;
+      if (c == 0) {
+        int32_t* so = seg_off + static_cast<size_t>(bh) * (nb + 1);
+        if (lane < nb) so[lane] = y - a;
+        if (lane == nb - 1) {
+          so[nb] = y;
+          if (y > Tseg) set_dev_err(dev_err, SCFA_DEVERR_SEGMENT_OVERFLOW);
+        }
+      }
+    }
   }
+  int32_t* ip = align > 0 ? idx_seg + static_cast<size_t>(bh) * Tseg : nullptr;
+  int32_t* kp = align > 0 ? bkt_seg + static_cast<size_t>(bh) * Tseg : nullptr;
   int v = -1;
-  if (t < T) v = bucket[static_cast<size_t>(bh) * T + t];
-  const bool valid = t < T && v >= 0 && v < nb;
+  if (c < nC && t < T) v = bucket[static_cast<size_t>(bh) * T + t];
+  const bool valid = c < nC && t < T && v >= 0 && v < nb;
+  if (c < nC && t < T && !valid) set_dev_err(dev_err, SCFA_DEVERR_BUCKET_RANGE);
   int my_rank = 0;
   uint64_t remaining = __ballot(valid);
   while (remaining) {
@@ -315,10 +347,28 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
     for (int k = 0; k < w; ++k) pos += wcnt[k][v];
     pp[pos] = t;
     bp[pos] = v;
+    if (align > 0) {
+      const int r = aoff_s[v] + (pos - off_s[v]);
+      if (r < Tseg) {
+        ip[r] = t;
+        kp[r] = v;
+      }
+    }
   }
   if (t >= T && t < Tp) {
     pp[t] = pad;
     bp[t] = -1;
+  }
+  if (align > 0 && t < Tseg) {  // pad rows of the aligned layout among rows [256 c, 256 c + 256)
+    int a = 0, z = nb;          // the last bucket v in [0, nb] with A_v <= t
+    while (a < z) {
+      const int mid = (a + z + 1) >> 1;
+      if (aoff_s[mid] <= t) a = mid; else z = mid - 1;
+    }
+    if (a == nb || t - aoff_s[a] >= tot_s[a]) {
+      ip[t] = pad;
+      kp[t] = a;
+    }
   }
 }
 
@@ -838,8 +888,8 @@ int scfa_qk_compact(int dtype, const void* x, const uint8_t* keep, const int32_t
   return SCFA_OK;
 }
 
-int scfa_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb, int32_t* bucket,
-                     hipStream_t stream) {
+static int launch_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb,
+                              int32_t* bucket, int32_t* counts, hipStream_t stream) {
   if (!x || !R || !bucket) return SCFA_ERR_INVALID;
   if (B < 1 || T < 1 || H < 1 || nb < 2 || nb % 2) return SCFA_ERR_INVALID;
   if (!dtype_ok(dtype)) return SCFA_ERR_INVALID;
@@ -850,10 +900,10 @@ int scfa_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int
   case HALF:                                                                                                    \
     if (dtype == SCFA_BF16)                                                                                     \
       hipLaunchKernelGGL((k_hash_bucket<uint16_t, HALF>), grid, dim3(256), 0, stream,                          \
-                         static_cast<const uint16_t*>(x), R, T, H, bucket);                                    \
+                         static_cast<const uint16_t*>(x), R, T, H, bucket, counts);                            \
     else                                                                                                        \
       hipLaunchKernelGGL((k_hash_bucket<float, HALF>), grid, dim3(256), 0, stream, static_cast<const float*>(x), \
-                         R, T, H, bucket);                                                                      \
+                         R, T, H, bucket, counts);                                                              \
     break;
   switch (half) {
     SCFA_BUCKET_CASE(1)
@@ -876,6 +926,17 @@ int scfa_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int
   return SCFA_OK;
 }
 
+int scfa_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb, int32_t* bucket,
+                     hipStream_t stream) {
+  return launch_hash_bucket(dtype, x, R, B, T, H, D, nb, bucket, nullptr, stream);
+}
+
+int scfa_hash_bucket_counts(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb,
+                            int32_t* bucket, int32_t* chunk_counts, hipStream_t stream) {
+  if (!chunk_counts) return SCFA_ERR_INVALID;
+  return launch_hash_bucket(dtype, x, R, B, T, H, D, nb, bucket, chunk_counts, stream);
+}
+
 size_t scfa_hash_sort_workspace_bytes(int B, int H, int T, int nb) {
   if (B < 1 || H < 1 || T < 1 || nb < 1) return 0;
   return static_cast<size_t>(B) * H * ceil_div(T, kSortChunk) * nb * sizeof(int32_t);
@@ -895,7 +956,7 @@ int scfa_hash_sort(const int32_t* bucket, int B, int H, int T, int nb, int32_t p
   hipLaunchKernelGGL(k_sort_hist, dim3(nC, B * H), dim3(256), 0, stream, bucket, T, nb, nC, hist, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   hipLaunchKernelGGL(k_sort_scatter, dim3(nCx, B * H), dim3(256), 0, stream, bucket, T, Tp, nb, nC, hist, pad_idx,
-                     perm, bucket_sorted, offsets);
+                     perm, bucket_sorted, offsets, 0, 0, nullptr, nullptr, nullptr, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }
@@ -917,6 +978,26 @@ int scfa_hash_segments(const int32_t* perm, const int32_t* offsets, int B, int H
   if (Tseg < SCFA_ROW_ALIGN || Tseg % SCFA_ROW_ALIGN || Tseg < T) return SCFA_ERR_INVALID;
   hipLaunchKernelGGL(k_hash_segments, dim3(ceil_div(Tseg, 256), B * H), dim3(256), 0, stream, perm, offsets,
                      pad_rows(T), nb, align, pad_idx, Tseg, idx_seg, bkt_seg, seg_offsets, dev_err);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+int scfa_hash_layout(const int32_t* bucket, const int32_t* chunk_counts, int B, int H, int T, int nb, int align,
+                     int32_t pad_idx, int Tseg, int32_t* perm, int32_t* bucket_sorted, int32_t* offsets,
+                     int32_t* idx_seg, int32_t* bkt_seg, int32_t* seg_offsets, int32_t* dev_err, hipStream_t stream) {
+  if (!bucket || !chunk_counts || !perm || !bucket_sorted || !offsets) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || T < 1 || nb < 1) return SCFA_ERR_INVALID;
+  if (nb > 64) return SCFA_ERR_UNSUPPORTED;
+  if (align != 0) {
+    if (!(align == 16 || align == 32 || align == 64 || align == 128)) return SCFA_ERR_INVALID;
+    if (!idx_seg || !bkt_seg || !seg_offsets) return SCFA_ERR_INVALID;
+    if (Tseg < SCFA_ROW_ALIGN || Tseg % SCFA_ROW_ALIGN || Tseg < T) return SCFA_ERR_INVALID;
+  }
+  const int nC = ceil_div(T, kSortChunk);
+  const int Tp = pad_rows(T);
+  const int nW = ceil_div(align != 0 ? max(Tp, Tseg) : Tp, kSortChunk);
+  hipLaunchKernelGGL(k_sort_scatter, dim3(nW, B * H), dim3(256), 0, stream, bucket, T, Tp, nb, nC, chunk_counts,
+                     pad_idx, perm, bucket_sorted, offsets, align, Tseg, idx_seg, bkt_seg, seg_offsets, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }

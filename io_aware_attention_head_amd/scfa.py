@@ -47,6 +47,8 @@ _SIGS = {
     "scfa_hash_sort": (_i, [_vp, _i, _i, _i, _i, ctypes.c_int32, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "scfa_hash_segment_rows": (_i, [_i, _i, _i]),
     "scfa_hash_segments": (_i, [_vp, _vp, _i, _i, _i, _i, _i, ctypes.c_int32, _i, _vp, _vp, _vp, _vp, _vp]),
+    "scfa_hash_layout": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "scfa_hash_bucket_counts": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "scfa_gather": (_i, [_i, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "scfa_range_table": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_count_visible": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
@@ -157,6 +159,12 @@ def scfa_hash_bucket(x, R, nb, bucket, stream=None):
            "scfa_hash_bucket")
 
 
+def scfa_hash_bucket_counts(x, R, nb, bucket, chunk_counts, stream=None):
+    B, T, H, D = x.shape
+    _check(lib().scfa_hash_bucket_counts(_dt(x), _p(x), _p(R), B, T, H, D, nb, _p(bucket), _p(chunk_counts),
+                                         _stream(stream, x)), "scfa_hash_bucket_counts")
+
+
 def scfa_hash_sort_workspace_bytes(B, H, T, nb) -> int:
     return lib().scfa_hash_sort_workspace_bytes(B, H, T, nb)
 
@@ -178,6 +186,22 @@ def scfa_hash_segments(perm, offsets, T, nb, align, pad_idx, idx_seg, bkt_seg, s
     _check(lib().scfa_hash_segments(_p(perm), _p(offsets), B, H, T, nb, align, pad_idx, Tseg, _p(idx_seg),
                                     _p(bkt_seg), _p(seg_offsets), _p(dev_err), _stream(stream, perm)),
            "scfa_hash_segments")
+
+
+def scfa_hash_layout(bucket, chunk_counts, nb, align, pad_idx, perm, bucket_sorted, offsets, idx_seg=None,
+                     bkt_seg=None, seg_offsets=None, dev_err=None, stream=None):
+    """Sort by bucket and (align > 0) the bucket-aligned layout in one launch,
+    from the chunk counts of scfa_hash_bucket_counts."""
+    B, H, T = bucket.shape
+    Tseg = idx_seg.shape[-1] if idx_seg is not None else 0
+    _check(lib().scfa_hash_layout(_p(bucket), _p(chunk_counts), B, H, T, nb, align, pad_idx, Tseg, _p(perm),
+                                  _p(bucket_sorted), _p(offsets), _p(idx_seg), _p(bkt_seg), _p(seg_offsets),
+                                  _p(dev_err), _stream(stream, bucket)), "scfa_hash_layout")
+
+
+def chunk_count_shape(B, H, T, nb):
+    """Shape of the chunk counts of scfa_hash_bucket_counts."""
+    return (B, H, (T + 255) // 256, nb)
 
 
 def scfa_gather(x, idx, layout, x_p, stream=None):
@@ -339,7 +363,8 @@ def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, rows: bool = F
 
 def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None) -> Prepared:
     """Hash-sparse preprocessing: LSH buckets of Q and K, stable counting sort
-    per head, then (aligned=True) the bucket-aligned layout (query buckets
+    per head and (aligned=True) the bucket-aligned layout in one launch per
+    side (query buckets
     start at multiples of the query tile, key buckets at multiples of the key
     tile). The operands stay in original order (gathered on load)."""
     B, T, H, D = q.shape
@@ -347,27 +372,27 @@ def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None) -> Prep
     i32 = torch.int32
     Tp = pad_rows(T)
     bq, bk = _empty((B, H, T), i32, dev), _empty((B, H, T), i32, dev)
-    scfa_hash_bucket(q, R, nb, bq, stream)
-    scfa_hash_bucket(k, R, nb, bk, stream)
-    ws = _empty((max(1, scfa_hash_sort_workspace_bytes(B, H, T, nb)),), torch.uint8, dev)
+    cq, ck = _empty(chunk_count_shape(B, H, T, nb), i32, dev), _empty(chunk_count_shape(B, H, T, nb), i32, dev)
+    scfa_hash_bucket_counts(q, R, nb, bq, cq, stream)
+    scfa_hash_bucket_counts(k, R, nb, bk, ck, stream)
     dev_err = torch.zeros((1,), dtype=i32, device=q.device)
     perm_q, perm_k = _empty((B, H, Tp), i32, dev), _empty((B, H, Tp), i32, dev)
     bs_q, bs_k = _empty((B, H, Tp), i32, dev), _empty((B, H, Tp), i32, dev)
     offq, offk = _empty((B, H, nb + 1), i32, dev), _empty((B, H, nb + 1), i32, dev)
-    scfa_hash_sort(bq, nb, SCFA_Q_PAD, perm_q, bs_q, offq, ws, dev_err, stream)
-    scfa_hash_sort(bk, nb, SCFA_K_PAD, perm_k, bs_k, offk, ws, dev_err, stream)
-    extra = {"bucket_q": bq, "bucket_k": bk, "perm_q": perm_q, "perm_k": perm_k, "sorted_bkt_q": bs_q,
-             "sorted_bkt_k": bs_k, "offsets_q": offq, "offsets_k": offk, "dev_err": dev_err, "workspace": ws}
+    extra = {"bucket_q": bq, "bucket_k": bk, "chunk_counts_q": cq, "chunk_counts_k": ck, "perm_q": perm_q, "perm_k": perm_k, "sorted_bkt_q": bs_q,
+             "sorted_bkt_k": bs_k, "offsets_q": offq, "offsets_k": offk, "dev_err": dev_err}
     if aligned:
         Tq = scfa_hash_segment_rows(T, nb, SCFA_TILE_M)
         Tk = scfa_hash_segment_rows(T, nb, SCFA_TILE_N)
         q_idx, q_bkt = _empty((B, H, Tq), i32, dev), _empty((B, H, Tq), i32, dev)
         k_idx, k_bkt = _empty((B, H, Tk), i32, dev), _empty((B, H, Tk), i32, dev)
         sq, sk = _empty((B, H, nb + 1), i32, dev), _empty((B, H, nb + 1), i32, dev)
-        scfa_hash_segments(perm_q, offq, T, nb, SCFA_TILE_M, SCFA_Q_PAD, q_idx, q_bkt, sq, dev_err, stream)
-        scfa_hash_segments(perm_k, offk, T, nb, SCFA_TILE_N, SCFA_K_PAD, k_idx, k_bkt, sk, dev_err, stream)
+        scfa_hash_layout(bq, cq, nb, SCFA_TILE_M, SCFA_Q_PAD, perm_q, bs_q, offq, q_idx, q_bkt, sq, dev_err, stream)
+        scfa_hash_layout(bk, ck, nb, SCFA_TILE_N, SCFA_K_PAD, perm_k, bs_k, offk, k_idx, k_bkt, sk, dev_err, stream)
         extra.update(seg_offsets_q=sq, seg_offsets_k=sk)
     else:
+        scfa_hash_layout(bq, cq, nb, 0, SCFA_Q_PAD, perm_q, bs_q, offq, dev_err=dev_err, stream=stream)
+        scfa_hash_layout(bk, ck, nb, 0, SCFA_K_PAD, perm_k, bs_k, offk, dev_err=dev_err, stream=stream)
         Tq = Tk = T
         q_idx, k_idx, q_bkt, k_bkt = perm_q, perm_k, bs_q, bs_k
     return Prepared("hash", B, H, T, D, Tq, Tk, q, k, v, q_idx, k_idx, q_bkt, k_bkt, extra=extra)
@@ -517,7 +542,7 @@ class Plan:
             self.offq, self.offk = e((B, H, nb + 1)), e((B, H, nb + 1))
             self.segq, self.segk = e((B, H, nb + 1)), e((B, H, nb + 1))
             self.q_bkt, self.k_bkt = e((B, H, TqP)), e((B, H, TkP))
-            self.ws = e((max(1, scfa_hash_sort_workspace_bytes(B, H, T, nb)),), torch.uint8)
+            self.cq, self.ck = e(chunk_count_shape(B, H, T, nb)), e(chunk_count_shape(B, H, T, nb))
         if mode == "dense":
             ar = torch.arange(TqP, dtype=i32, device=d)
             self.q_idx.copy_(torch.where(ar < T, ar, torch.full_like(ar, SCFA_Q_PAD)).expand(B, H, TqP))
@@ -534,17 +559,16 @@ class Plan:
 
     # -- stages ---------------------------------------------------------------
     def bucket(self, q, k, R, stream=None):
-        scfa_hash_bucket(q, R, self.nb, self.bq, stream)
-        scfa_hash_bucket(k, R, self.nb, self.bk, stream)
+        """LSH buckets and the chunk counts of the sort."""
+        scfa_hash_bucket_counts(q, R, self.nb, self.bq, self.cq, stream)
+        scfa_hash_bucket_counts(k, R, self.nb, self.bk, self.ck, stream)
 
     def sort(self, stream=None):
-        """Stable sort by bucket, then the bucket-aligned layout."""
-        scfa_hash_sort(self.bq, self.nb, SCFA_Q_PAD, self.perm_q, self.bs_q, self.offq, self.ws, self.dev_err, stream)
-        scfa_hash_sort(self.bk, self.nb, SCFA_K_PAD, self.perm_k, self.bs_k, self.offk, self.ws, self.dev_err, stream)
-        scfa_hash_segments(self.perm_q, self.offq, self.T, self.nb, SCFA_TILE_M, SCFA_Q_PAD, self.q_idx, self.q_bkt,
-                           self.segq, self.dev_err, stream)
-        scfa_hash_segments(self.perm_k, self.offk, self.T, self.nb, SCFA_TILE_N, SCFA_K_PAD, self.k_idx, self.k_bkt,
-                           self.segk, self.dev_err, stream)
+        """Stable sort by bucket and the bucket-aligned layout (one launch per side)."""
+        scfa_hash_layout(self.bq, self.cq, self.nb, SCFA_TILE_M, SCFA_Q_PAD, self.perm_q, self.bs_q, self.offq,
+                         self.q_idx, self.q_bkt, self.segq, self.dev_err, stream)
+        scfa_hash_layout(self.bk, self.ck, self.nb, SCFA_TILE_N, SCFA_K_PAD, self.perm_k, self.bs_k, self.offk,
+                         self.k_idx, self.k_bkt, self.segk, self.dev_err, stream)
 
     def compact(self, q, k, keep_q, keep_k, stream=None):
         scfa_qk_count(keep_q, self.cnt[0], self.mx[0], self.choff[0], stream)

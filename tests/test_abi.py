@@ -85,6 +85,18 @@ def test_invalid_arguments_rejected_without_gpu():
                                 null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_hash_segments(dummy, dummy, 1, 1, 300, 16, 64, -1, 256, dummy, dummy, dummy, null,
                                 null) == scfa.SCFA_ERR_INVALID
+    # one-launch sort and layout: bad alignment, rows below T, missing counts or layout outputs, nb above 64
+    assert L.scfa_hash_layout(dummy, dummy, 1, 1, 100, 16, 48, -1, 128, dummy, dummy, dummy, dummy, dummy, dummy,
+                              null, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_layout(dummy, dummy, 1, 1, 300, 16, 64, -1, 256, dummy, dummy, dummy, dummy, dummy, dummy,
+                              null, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_layout(dummy, dummy, 1, 1, 300, 16, 64, -1, 512, dummy, dummy, dummy, null, dummy, dummy,
+                              null, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_layout(dummy, null, 1, 1, 300, 16, 0, -1, 0, dummy, dummy, dummy, null, null, null, null,
+                              null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_layout(dummy, dummy, 1, 1, 300, 65, 0, -1, 0, dummy, dummy, dummy, null, null, null, null,
+                              null) == scfa.SCFA_ERR_UNSUPPORTED
+    assert L.scfa_hash_bucket_counts(0, dummy, dummy, 1, 8, 1, 64, 16, dummy, null, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_hash_segment_rows(16384, 16, 128) == 18432
     assert L.scfa_hash_segment_rows(16384, 16, 48) == 0
     # work order: bad sizes, NULL pointers

@@ -110,6 +110,8 @@ def test_hash_bucket_sort_gather_bitexact(w):
     bq, bk = oracle_buckets(w, x)
     assert np.array_equal(pre.extra["bucket_q"].cpu().numpy(), bq)
     assert np.array_equal(pre.extra["bucket_k"].cpu().numpy(), bk)
+    assert np.array_equal(pre.extra["chunk_counts_q"].cpu().numpy(), chunk_counts_np(bq, w.nb))
+    assert np.array_equal(pre.extra["chunk_counts_k"].cpu().numpy(), chunk_counts_np(bk, w.nb))
     T = w.T
     ex = pre.extra
     sides = ((bq, ex["perm_q"], ex["sorted_bkt_q"], ex["offsets_q"], oracle.Q_PAD, pre.q_idx, pre.q_bkt,
@@ -192,6 +194,108 @@ def test_tables_more_than_512_tiles(mode):
     assert tab.fwd.shape[2] > 512 and tab.bwd.shape[2] > 512
     ref = _tables_match(mode, pre, tab, pre.Tq, 16, 16, pre.q_bkt, pre.k_bkt, pre.Tk)
     assert ref["tiles"].sum() > 0
+
+
+def chunk_counts_np(b_np, nb):
+    """Tokens of each bucket among positions [256 c, 256 c + 256) of each head."""
+    B, H, T = b_np.shape
+    nC = (T + 255) // 256
+    out = np.zeros((B, H, nC, nb), dtype=np.int32)
+    for c in range(nC):
+        blk = b_np[:, :, 256 * c:256 * (c + 1)]
+        for v in range(nb):
+            out[:, :, c, v] = (blk == v).sum(-1)
+    return out
+
+
+@pytest.mark.parametrize("T,nb,align,dist", [(1, 1, 0, "uniform"), (63, 3, 16, "uniform"), (300, 16, 128, "uniform"),
+                                              (1000, 64, 64, "uniform"), (4100, 16, 64, "skewed"),
+                                              (16384, 16, 128, "uniform"), (777, 8, 32, "one"),
+                                              (2049, 5, 0, "skewed"), (40000, 16, 64, "uniform")])
+def test_hash_layout_bitexact(T, nb, align, dist):
+    """The one-launch sort and layout against the oracle's sort and
+    bucket-aligned layout, and against the two-stage entry points
+    (scfa_hash_sort then scfa_hash_segments) on the same buckets: ragged
+    lengths, empty buckets, one bucket holding everything, nb up to 64."""
+    need_gpu()
+    announce(f"hash layout T={T} nb={nb} align={align} {dist}")
+    d = torch.device("cuda:0")
+    B, H = 2, 3
+    rng = np.random.default_rng(T * 131 + nb)
+    if dist == "uniform":
+        b_np = rng.integers(0, nb, (B, H, T)).astype(np.int32)
+    elif dist == "skewed":  # most tokens in bucket 0, a few elsewhere, some buckets empty
+        b_np = np.where(rng.random((B, H, T)) < 0.9, 0, rng.integers(0, nb, (B, H, T))).astype(np.int32)
+    else:
+        b_np = np.full((B, H, T), nb - 1, dtype=np.int32)
+    bucket = torch.from_numpy(b_np).to(d)
+    counts = torch.from_numpy(chunk_counts_np(b_np, nb)).to(d)
+    Tp = scfa.pad_rows(T)
+    i32 = torch.int32
+    out = {k: torch.full(shape, -7, dtype=i32, device=d) for k, shape in
+           (("perm", (B, H, Tp)), ("bs", (B, H, Tp)), ("off", (B, H, nb + 1)))}
+    err = torch.zeros(1, dtype=i32, device=d)
+    pad = oracle.K_PAD
+    perm, bs, offs = oracle.hash_sort(b_np, nb)
+    if align:
+        Tseg = scfa.scfa_hash_segment_rows(T, nb, align)
+        seg = {k: torch.full(shape, -7, dtype=i32, device=d) for k, shape in
+               (("idx", (B, H, Tseg)), ("bkt", (B, H, Tseg)), ("so", (B, H, nb + 1)))}
+        scfa.scfa_hash_layout(bucket, counts, nb, align, pad, out["perm"], out["bs"], out["off"], seg["idx"],
+                              seg["bkt"], seg["so"], err)
+    else:
+        scfa.scfa_hash_layout(bucket, counts, nb, 0, pad, out["perm"], out["bs"], out["off"], dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    gp, gb = out["perm"].cpu().numpy(), out["bs"].cpu().numpy()
+    assert np.array_equal(gp[:, :, :T], perm) and (gp[:, :, T:] == pad).all()
+    assert np.array_equal(gb[:, :, :T], bs) and (gb[:, :, T:] == -1).all()
+    assert np.array_equal(out["off"].cpu().numpy(), offs)
+    # the two-stage entry points give the same bits
+    ws = torch.empty(max(1, scfa.scfa_hash_sort_workspace_bytes(B, H, T, nb)), dtype=torch.uint8, device=d)
+    p2, b2, o2 = torch.empty_like(out["perm"]), torch.empty_like(out["bs"]), torch.empty_like(out["off"])
+    scfa.scfa_hash_sort(bucket, nb, pad, p2, b2, o2, ws, err)
+    if align:
+        ri, rb, ro = oracle.hash_segments(perm, offs, nb, align, pad, Tseg)
+        i2, k2, s2 = torch.empty_like(seg["idx"]), torch.empty_like(seg["bkt"]), torch.empty_like(seg["so"])
+        scfa.scfa_hash_segments(p2, o2, T, nb, align, pad, i2, k2, s2, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(p2, out["perm"]) and torch.equal(b2, out["bs"]) and torch.equal(o2, out["off"])
+    if align:
+        assert np.array_equal(seg["idx"].cpu().numpy(), ri)
+        assert np.array_equal(seg["bkt"].cpu().numpy(), rb)
+        assert np.array_equal(seg["so"].cpu().numpy(), ro)
+        assert torch.equal(i2, seg["idx"]) and torch.equal(k2, seg["bkt"]) and torch.equal(s2, seg["so"])
+
+
+def test_hash_layout_device_errors():
+    """scfa_hash_layout flags a bucket outside [0, nb) and a layout that
+    overflows the given rows."""
+    need_gpu()
+    announce("hash layout device errors")
+    d = torch.device("cuda:0")
+    i32 = torch.int32
+    T, nb = 300, 16
+    Tp = scfa.pad_rows(T)
+    perm, bs = torch.empty((1, 1, Tp), dtype=i32, device=d), torch.empty((1, 1, Tp), dtype=i32, device=d)
+    off = torch.empty((1, 1, nb + 1), dtype=i32, device=d)
+    err = torch.zeros(1, dtype=i32, device=d)
+    bucket = (torch.arange(T, dtype=i32, device=d) % nb).reshape(1, 1, T).contiguous()
+    bucket[0, 0, 5] = -2
+    counts = torch.from_numpy(chunk_counts_np(bucket.cpu().numpy(), nb)).to(d)
+    scfa.scfa_hash_layout(bucket, counts, nb, 0, -1, perm, bs, off, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == scfa.SCFA_DEVERR_BUCKET_RANGE
+    bucket[0, 0, 5] = 5
+    counts = torch.from_numpy(chunk_counts_np(bucket.cpu().numpy(), nb)).to(d)
+    seg_i = torch.empty((1, 1, 384), dtype=i32, device=d)
+    seg_b, seg_o = torch.empty_like(seg_i), torch.empty((1, 1, nb + 1), dtype=i32, device=d)
+    err.zero_()
+    scfa.scfa_hash_layout(bucket, counts, nb, 128, -1, perm, bs, off, seg_i, seg_b, seg_o, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == scfa.SCFA_DEVERR_SEGMENT_OVERFLOW
+    assert seg_o.cpu().numpy()[0, 0, nb] == nb * 128
 
 
 def test_device_error_flags():
