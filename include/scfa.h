@@ -225,11 +225,18 @@ int scfa_gather(int dtype, int layout, const void* x, const int32_t* idx, int B,
  *                hash).
  *  kstats out (B, H, nKt, 4), nKt = SCFA_PAD(Tk)/Bn; a tile with no valid
  *                row holds [K_PAD, K_PAD, INT32_MAX, INT32_MAX].
- *  fwd_tab out (B, H, nQt, 2) [start, end);  bwd_tab out (B, H, nKt, 2).
+ *  fwd_tab out (B, H, nQt, 2) [start, end).
+ *  bwd_tab out (B, H, nKt, 2), or NULL to skip it (a forward-only call;
+ *                scfa_bwd_table builds it later from the same statistics).
  *  tiles   out (B, H) int32: number of processed tile pairs.               */
 int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt,
                      const int32_t* k_bkt, int B, int H, int Tq, int Tk, int Bm, int Bn, int32_t* qstats,
                      int32_t* kstats, int32_t* fwd_tab, int32_t* bwd_tab, int32_t* tiles, hipStream_t stream);
+
+/* The backward table alone, from the statistics and forward table of a
+ * scfa_range_table call (nQt, nKt as there): the same bwd_tab.              */
+int scfa_bwd_table(const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, int B, int H, int nQt, int nKt,
+                   int32_t* bwd_tab, hipStream_t stream);
 
 /* Launch order of the attention workgroups for one range table (the
  * forward table for the forward and dQ kernels, the backward table for the

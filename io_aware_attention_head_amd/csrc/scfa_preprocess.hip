@@ -497,22 +497,10 @@ __global__ __launch_bounds__(256) void k_gather_cols(const E* __restrict__ x, co
 // Tile extrema and range tables.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(64) void k_tile_stats(int mode, const int32_t* __restrict__ q_idx,
-                                                   const int32_t* __restrict__ k_idx, const int32_t* __restrict__ q_bkt,
-                                                   const int32_t* __restrict__ k_bkt, int Tq, int Tk, int TqP, int TkP,
-                                                   int Bm, int Bn, int nQt, int nKt, int32_t* __restrict__ qstats,
-                                                   int32_t* __restrict__ kstats, int32_t* __restrict__ tiles) {
-  const int bh = blockIdx.y;
-  const int x = blockIdx.x;
-  const int lane = threadIdx.x;
-  const bool isq = x < nQt;
-  const int tile = isq ? x : x - nQt;
-  const int bs = isq ? Bm : Bn;
-  const int Tv = isq ? Tq : Tk;
-  const int32_t* ip = isq ? q_idx + static_cast<size_t>(bh) * TqP : k_idx + static_cast<size_t>(bh) * TkP;
-  const int32_t* bp = nullptr;
-  if (mode == SCFA_HASH) bp = isq ? q_bkt + static_cast<size_t>(bh) * TqP : k_bkt + static_cast<size_t>(bh) * TkP;
-  const int r0 = tile * bs, r1 = min(r0 + bs, Tv);
+// [min pos, max pos, min bucket, max bucket] of rows [r0, r1) (one wave; all
+// lanes return it). An empty row range gives the sentinel statistics.
+__device__ inline int4 tile_stats_wave(int mode, const int32_t* ip, const int32_t* bp, int r0, int r1, bool isq,
+                                       int lane) {
   int mn = kInt32Max, mx = kInt32Min, mnb = kInt32Max, mxb = kInt32Min;
   for (int r = r0 + lane; r < r1; r += 64) {
     const int p = (mode == SCFA_DENSE) ? r : ip[r];
@@ -531,16 +519,29 @@ __global__ __launch_bounds__(64) void k_tile_stats(int mode, const int32_t* __re
     mnb = min(mnb, __shfl_xor(mnb, o));
     mxb = max(mxb, __shfl_xor(mxb, o));
   }
+  if (r1 <= r0)
+    return isq ? make_int4(SCFA_Q_PAD, SCFA_Q_PAD, kInt32Max, kInt32Min)
+               : make_int4(SCFA_K_PAD, SCFA_K_PAD, kInt32Max, kInt32Max);
+  return bp ? make_int4(mn, mx, mnb, mxb) : make_int4(mn, mx, 0, 0);
+}
+
+__global__ __launch_bounds__(64) void k_tile_stats(int mode, const int32_t* __restrict__ q_idx,
+                                                   const int32_t* __restrict__ k_idx, const int32_t* __restrict__ q_bkt,
+                                                   const int32_t* __restrict__ k_bkt, int Tq, int Tk, int TqP, int TkP,
+                                                   int Bm, int Bn, int nQt, int nKt, int32_t* __restrict__ qstats,
+                                                   int32_t* __restrict__ kstats, int32_t* __restrict__ tiles) {
+  const int bh = blockIdx.y;
+  const int x = blockIdx.x;
+  const int lane = threadIdx.x;
+  const bool isq = x < nQt;
+  const int tile = isq ? x : x - nQt;
+  const int bs = isq ? Bm : Bn;
+  const int Tv = isq ? Tq : Tk;
+  const int32_t* ip = isq ? q_idx + static_cast<size_t>(bh) * TqP : k_idx + static_cast<size_t>(bh) * TkP;
+  const int32_t* bp = nullptr;
+  if (mode == SCFA_HASH) bp = isq ? q_bkt + static_cast<size_t>(bh) * TqP : k_bkt + static_cast<size_t>(bh) * TkP;
+  const int4 s = tile_stats_wave(mode, ip, bp, tile * bs, min(tile * bs + bs, Tv), isq, lane);
   if (lane == 0) {
-    int4 s;
-    if (r1 <= r0) {
-      s = isq ? make_int4(SCFA_Q_PAD, SCFA_Q_PAD, kInt32Max, kInt32Min)
-              : make_int4(SCFA_K_PAD, SCFA_K_PAD, kInt32Max, kInt32Max);
-    } else if (bp) {
-      s = make_int4(mn, mx, mnb, mxb);
-    } else {
-      s = make_int4(mn, mx, 0, 0);
-    }
     int32_t* out = isq ? qstats + (static_cast<size_t>(bh) * nQt + tile) * 4 : kstats + (static_cast<size_t>(bh) * nKt + tile) * 4;
     *reinterpret_cast<int4*>(out) = s;
     if (x == 0) tiles[bh] = 0;
@@ -558,11 +559,9 @@ __global__ __launch_bounds__(64) void k_tile_stats(int mode, const int32_t* __re
 constexpr int kTabRegChunks = 8;  // register path for up to 512 tiles
 
 // One query tile's range [start, end) and processed-tile count (one wave).
-__device__ void fwd_table_row(int mode, const int32_t* __restrict__ qstats, const int32_t* __restrict__ kstats,
-                              int nQt, int nKt, int32_t* __restrict__ fwd, int bh, int i, int lane,
+// ks: the head's key-tile statistics (global memory or LDS).
+__device__ void fwd_table_row(int mode, const int4 qs, const int4* ks, int nKt, int2* __restrict__ fwd_row, int lane,
                               int32_t& cnt_out) {
-  const int4 qs = reinterpret_cast<const int4*>(qstats)[static_cast<size_t>(bh) * nQt + i];
-  const int4* ks = reinterpret_cast<const int4*>(kstats) + static_cast<size_t>(bh) * nKt;
   const int nch = (nKt + 63) / 64;
   // per chunk: a = tile below the query buckets, e = tile above them, c = causal test passes
   uint64_t A[kTabRegChunks], E[kTabRegChunks], C[kTabRegChunks];
@@ -645,7 +644,7 @@ __device__ void fwd_table_row(int mode, const int32_t* __restrict__ qstats, cons
     }
   }
   if (lane == 0) {
-    reinterpret_cast<int2*>(fwd)[static_cast<size_t>(bh) * nQt + i] = make_int2(start, end);
+    *fwd_row = make_int2(start, end);
     cnt_out = cnt;
   }
 }
@@ -662,7 +661,10 @@ __global__ __launch_bounds__(64 * kTabWaves) void k_fwd_table(int mode, const in
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = blockIdx.x * kTabWaves + w;
   if (lane == 0) wcnt[w] = 0;
-  if (i < nQt) fwd_table_row(mode, qstats, kstats, nQt, nKt, fwd, bh, i, lane, wcnt[w]);
+  if (i < nQt)
+    fwd_table_row(mode, reinterpret_cast<const int4*>(qstats)[static_cast<size_t>(bh) * nQt + i],
+                  reinterpret_cast<const int4*>(kstats) + static_cast<size_t>(bh) * nKt, nKt,
+                  reinterpret_cast<int2*>(fwd) + static_cast<size_t>(bh) * nQt + i, lane, wcnt[w]);
   __syncthreads();
   if (threadIdx.x == 0) {
     int sum = 0;
@@ -1034,7 +1036,7 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
                      int B, int H, int Tq, int Tk, int Bm, int Bn, int32_t* qstats, int32_t* kstats, int32_t* fwd_tab,
                      int32_t* bwd_tab, int32_t* tiles, hipStream_t stream) {
   if (mode != SCFA_DENSE && mode != SCFA_QK && mode != SCFA_HASH) return SCFA_ERR_INVALID;
-  if (!qstats || !kstats || !fwd_tab || !bwd_tab || !tiles) return SCFA_ERR_INVALID;
+  if (!qstats || !kstats || !fwd_tab || !tiles) return SCFA_ERR_INVALID;
   if (mode != SCFA_DENSE && (!q_idx || !k_idx)) return SCFA_ERR_INVALID;
   if (mode == SCFA_HASH && (!q_bkt || !k_bkt)) return SCFA_ERR_INVALID;
   if (B < 1 || H < 1 || Tq < 1 || Tk < 1) return SCFA_ERR_INVALID;
@@ -1048,8 +1050,20 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
   hipLaunchKernelGGL(k_fwd_table, dim3(ceil_div(nQt, kTabWaves), B * H), dim3(64 * kTabWaves), 0, stream, mode, qstats,
                      kstats, nQt, nKt, fwd_tab, tiles);
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_bwd_table, dim3(ceil_div(nKt, 4), B * H), dim3(256), 0, stream, qstats, kstats, fwd_tab, nQt,
-                     nKt, bwd_tab);
+  if (bwd_tab) {
+    hipLaunchKernelGGL(k_bwd_table, dim3(ceil_div(nKt, 4), B * H), dim3(256), 0, stream, qstats, kstats, fwd_tab, nQt,
+                       nKt, bwd_tab);
+    SCFA_RETURN_IF_LAUNCH_FAILED();
+  }
+  return SCFA_OK;
+}
+
+int scfa_bwd_table(const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, int B, int H, int nQt, int nKt,
+                   int32_t* bwd_tab, hipStream_t stream) {
+  if (!qstats || !kstats || !fwd_tab || !bwd_tab) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || nQt < 1 || nKt < 1) return SCFA_ERR_INVALID;
+  hipLaunchKernelGGL(k_bwd_table, dim3(ceil_div(nKt, 4), B * H), dim3(256), 0, stream, qstats, kstats, fwd_tab, nQt, nKt,
+                     bwd_tab);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }

@@ -49,6 +49,7 @@ _SIGS = {
     "scfa_hash_segments": (_i, [_vp, _vp, _i, _i, _i, _i, _i, ctypes.c_int32, _i, _vp, _vp, _vp, _vp, _vp]),
     "scfa_hash_layout": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_hash_bucket_counts": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "scfa_bwd_table": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_gather": (_i, [_i, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "scfa_range_table": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_count_visible": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
@@ -216,6 +217,13 @@ def scfa_range_table(mode, q_idx, k_idx, q_bkt, k_bkt, B, H, Tq, Tk, Bm, Bn, qst
     _check(lib().scfa_range_table(mode, _p(q_idx), _p(k_idx), _p(q_bkt), _p(k_bkt), B, H, Tq, Tk, Bm, Bn, _p(qstats),
                                   _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(tiles), _stream(stream, qstats)),
            "scfa_range_table")
+
+
+def scfa_bwd_table(qstats, kstats, fwd_tab, bwd_tab, stream=None):
+    B, H, nQt = fwd_tab.shape[:3]
+    nKt = bwd_tab.shape[2]
+    _check(lib().scfa_bwd_table(_p(qstats), _p(kstats), _p(fwd_tab), B, H, nQt, nKt, _p(bwd_tab),
+                                _stream(stream, fwd_tab)), "scfa_bwd_table")
 
 
 def scfa_count_visible(mode, q_idx, k_idx, q_bkt, k_bkt, B, H, Tq, Tk, pairs, stream=None):
@@ -590,9 +598,11 @@ class Plan:
         scfa_gather(v, self.k_idx, SCFA_COLS, self.v_t, stream)
 
     def tables(self, stream=None):
+        """Tile statistics, forward ranges and the launch order (the backward
+        table is built by backward())."""
         t = self.tab
         scfa_range_table(_table_mode(self.mode), self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H, self.Tq,
-                         self.Tk, t.Bm, t.Bn, t.qstats, t.kstats, t.fwd, t.bwd, t.tiles, stream)
+                         self.Tk, t.Bm, t.Bn, t.qstats, t.kstats, t.fwd, None, t.tiles, stream)
         scfa_work_order(t.fwd, t.kstats.shape[2], t.fwd_order, stream)
 
     def forward(self, stream=None):
@@ -604,6 +614,7 @@ class Plan:
         if self.x is None:
             raise ScfaError("backward needs a prepared forward")
         self.gather(self.x["q"], self.x["k"], self.x["v"], stream)
+        scfa_bwd_table(self.tab.qstats, self.tab.kstats, self.tab.fwd, self.tab.bwd, stream)
         if self._grads is None:
             d = self.device
             self._grads = tuple(torch.empty((self.B, self.T, self.H, self.D), dtype=torch.float32, device=d)

@@ -177,14 +177,35 @@ def test_tables_any_tile_size(Bm, Bn):
     assert np.array_equal(t[4].cpu().numpy(), ref["tiles"])
 
 
-@pytest.mark.parametrize("mode", ["hash", "qk"])
-def test_tables_more_than_512_tiles(mode):
+def test_backward_table_separately():
+    """A forward-only table call (no backward table) followed by
+    scfa_bwd_table gives the backward table of the full call."""
+    need_gpu()
+    announce("backward table separately")
+    w = small("hash", 1, 2, 3000, nb=8, seed=44)
+    x = make_inputs(w)
+    g = to_dev(x)
+    pre = scfa.prepare_hash(g["q"], g["k"], g["v"], g["R"], w.nb)
+    tab = scfa.build_tables(pre)
+    t2 = [torch.full_like(a, -5) for a in (tab.qstats, tab.kstats, tab.fwd, tab.bwd, tab.tiles)]
+    scfa.scfa_range_table(scfa.SCFA_HASH, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, w.B, w.H, pre.Tq, pre.Tk,
+                          tab.Bm, tab.Bn, t2[0], t2[1], t2[2], None, t2[4])
+    torch.cuda.synchronize()
+    assert (t2[3] == -5).all()  # not written
+    scfa.scfa_bwd_table(t2[0], t2[1], t2[2], t2[3])
+    torch.cuda.synchronize()
+    for a, b in zip((tab.qstats, tab.kstats, tab.fwd, tab.bwd, tab.tiles), t2):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("mode,T", [("hash", 9000), ("qk", 9000), ("hash", 17000)])
+def test_tables_more_than_512_tiles(mode, T):
     """More than 512 tiles per head on both sides: the table kernels' chunked
     loop (instead of the register path) against the oracle, plus the launch
     order."""
     need_gpu()
-    announce(f"tables >512 tiles {mode}")
-    w = small(mode, 1, 2, 9000, nb=16, keep_p=0.95, seed=43)
+    announce(f"tables >512 tiles {mode} T={T}")
+    w = small(mode, 1, 2, T, nb=16, keep_p=0.95, seed=43)
     x = make_inputs(w)
     g = to_dev(x)
     pre = (scfa.prepare_hash(g["q"], g["k"], g["v"], g["R"], w.nb) if mode == "hash"
