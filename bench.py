@@ -143,9 +143,8 @@ def main():
           for s in stages}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    # ---- timed region --------------------------------------------------------
+    # ---- per-stage times, eager launches ---------------------------------------
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     start.record()
     for i in range(K):
         for s in stages:
@@ -154,9 +153,31 @@ def main():
             ev[s][i][1].record()
     end.record()
     torch.cuda.synchronize()
+    ms_step_eager = start.elapsed_time(end) / K
+    stage_ms = {s: sum(a.elapsed_time(b) for a, b in ev[s]) / K for s in stages}
+    O_eager = plan.O.clone()
+
+    # ---- timed region: the step as one HIP graph replay ------------------------
+    graph = None
+    if not args.fwd_only:
+        graph = plan.capture(x)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.O, O_eager), "graph replay differs from the eager step"
+        for _ in range(max(1, args.warmup)):
+            graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        if graph is not None:
+            graph.replay()
+        else:
+            plan.forward()
+    end.record()
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / K
-    stage_ms = {s: sum(a.elapsed_time(b) for a, b in ev[s]) / K for s in stages}
 
     # ---- dense-causal twin: same kernel, same shape, positions 0..T-1 ------
     dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
@@ -168,10 +189,15 @@ def main():
     torch.cuda.synchronize()
     dense_fwd_ms = sum(a.elapsed_time(b) for a, b in dev_ev) / K
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dense_graph = dense.capture(x) if graph is not None else None
+    torch.cuda.synchronize()
     d0.record()
     for _ in range(K):
-        dense.tables()
-        dense.forward()
+        if dense_graph is not None:
+            dense_graph.replay()
+        else:
+            dense.tables()
+            dense.forward()
     d1.record()
     torch.cuda.synchronize()
     dense_step_ms = d0.elapsed_time(d1) / K
@@ -219,7 +245,8 @@ def main():
                    "seed": w.seed, "out_dtype": "f32", "tile_m": scfa.SCFA_TILE_M, "tile_n": scfa.SCFA_TILE_N,
                    "parallelism": "single GPU"},
         "step": "LSH bucket + stable sort + bucket-aligned layout + range tables + attention forward with the gather "
-                "fused into its loads (inputs resident in HBM)",
+                "fused into its loads (inputs resident in HBM), launched as one HIP graph",
+        "ms_per_step_eager_launches": round(ms_step_eager, 5),
         "visible_pairs": pairs,
         "fwd_kernel_ms": round(fwd_ms, 5),
         "fwd_kernel_tflops": round(fwd_tflops, 2),

@@ -646,6 +646,20 @@ class Plan:
         self.forward(stream)
         return self.O, self.lse
 
+    def capture(self, x: dict):
+        """A HIP graph of run(x) (all stages launch on the capturing stream;
+        none allocates, synchronises or records a memset). Replay it with
+        graph.replay(); the inputs must stay at the same addresses."""
+        s = torch.cuda.Stream(device=self.device)
+        s.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(s):  # warm-up launch on the capture stream
+            self.run(x)
+        torch.cuda.current_stream(self.device).wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run(x)
+        return graph
+
     def prepared(self) -> Prepared:
         if self.x is None:
             raise ScfaError("call prepare() first")

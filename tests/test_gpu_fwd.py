@@ -217,3 +217,29 @@ def test_fwd_deterministic():
     O2, l2 = scfa.forward(pre, tab)
     torch.cuda.synchronize()
     assert torch.equal(O1, O2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("mode", ["hash", "qk"])
+def test_graph_replay_matches_eager(mode):
+    """The whole forward path of a Plan captured in a HIP graph: every replay,
+    with eager work and synchronisations between replays, gives the eager
+    result bit for bit (no memset nodes, no host synchronisation inside)."""
+    need_gpu()
+    announce(f"graph replay {mode}")
+    w = small(mode, 2, 3, 2500, nb=16, keep_p=0.6, seed=64)
+    x = to_dev(make_inputs(w))
+    plan = scfa.Plan(mode, w.B, w.H, w.T, w.D, torch.bfloat16, nb=w.nb)
+    plan.run(x)
+    torch.cuda.synchronize()
+    O_ref, l_ref = plan.O.clone(), plan.lse.clone()
+    graph = plan.capture(x)
+    for rep in range(3):
+        plan.O.fill_(float("nan"))
+        plan.lse.fill_(0.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.O, O_ref) and torch.equal(plan.lse, l_ref), f"replay {rep}"
+        plan.run(x)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(plan.O, O_ref)
