@@ -51,6 +51,7 @@ def _parse():
                     help="only run a plain 512 MiB device copy (HBM counter calibration) and exit")
     ap.add_argument("--fwd-only", action="store_true", help="only launch the forward kernel in the timed loop "
                                                             "(for counter collection)")
+    ap.add_argument("--no-train", action="store_true", help="skip the backward (training) figures")
     return ap.parse_args()
 
 
@@ -94,6 +95,45 @@ def _cpu_baseline(w, x):
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"1 of {w.B * w.H} heads (b=0,h=0) of {w.name}: float64 LSH bucket + stable sort of its "
                       f"queries and keys, explicit masked-softmax forward over all {w.T} rows ({pairs} visible pairs)"}
+
+
+def _train_figures(K):
+    """Backward of the hash-sparse training workload (B=1, H=12, T=16384,
+    nb=16): the recomputation backward (gathers for the backward operands,
+    backward table, Delta / dK,dV / dQ kernels) after a forward, timed on its
+    own with HIP events, against the same kernels run dense-causal."""
+    import torch
+    import io_aware_attention_head_amd.scfa as scfa
+    from io_aware_attention_head_amd.inputs import WORKLOADS, make_inputs
+
+    wt = WORKLOADS["train_hash_bf16_t16384_nb16"]
+    xt = {k: v.to("cuda:0") for k, v in make_inputs(wt).items()}
+    res = {"workload": wt.name, "B": wt.B, "H": wt.H, "T": wt.T, "D": wt.D, "nb": wt.nb}
+    for mode in ("hash", "dense"):
+        plan = scfa.Plan(mode, wt.B, wt.H, wt.T, wt.D, torch.bfloat16, nb=wt.nb)
+        plan.run(xt)
+        for _ in range(2):
+            plan.backward(xt["dO"])
+        torch.cuda.synchronize()
+        dQ = plan._grads[0]
+        assert torch.isfinite(dQ).all().item(), "non-finite gradient"
+        pairs = int(plan.count_visible().sum().item())
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(K):
+            plan.backward(xt["dO"])
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / K
+        tf = 10 * wt.D * pairs / (ms * 1e-3) / 1e12
+        res[mode] = {"bwd_ms": round(ms, 5), "bwd_tflops": round(tf, 2),
+                     "pct_bf16_peak_bwd": round(100 * tf / PEAK_BF16_TFLOPS, 2), "visible_pairs": pairs}
+        del plan
+        torch.cuda.empty_cache()
+    res["speedup_vs_dense_causal_bwd"] = round(res["dense"]["bwd_ms"] / res["hash"]["bwd_ms"], 3)
+    res["flop_convention"] = "10*D per visible pair (dV, dP, dQ, dK products and the recomputed scores)"
+    return res
 
 
 def main():
@@ -271,6 +311,8 @@ def main():
                    "torch": torch.__version__, "hip": torch.version.hip},
         "wall_s_timed": round(wall, 3),
     }
+    if not args.no_train and not args.fwd_only:
+        out["train"] = _train_figures(args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(w, x_cpu)
     print(json.dumps(out), flush=True)
