@@ -323,11 +323,13 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
  *                SCFA_HASH.
  *  dtype_in      SCFA_BF16 (the only backward build; fp32 returns
  *                SCFA_ERR_UNSUPPORTED).
- *  q, k          (B, H, Tpad, D) SCFA_ROWS gathered rows and
- *  v_t           (B, H, D, Tpad) SCFA_COLS gathered values (scfa_gather of
- *                the forward's original tensors through q_idx / k_idx).
- *  q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab
+ *  q, k, v       (B, T, H, D) the original tensors of the forward call,
+ *                read through q_idx / k_idx like the forward (pad entries
+ *                read token 0).
+ *  q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab
  *                exactly the index arrays and tables of the forward call.
+ *  bwd_tab       the backward table of the same call (scfa_range_table or
+ *                scfa_bwd_table).
  *  O             (B, T, H, D) fp32 forward output;  lse (B, H, T) fp32.
  *  dO            (B, T, H, D) upstream gradient, dtype_in.
  *  T             original sequence length; Tq, Tk query / key rows as
@@ -337,12 +339,12 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
  *  dQ, dK, dV    out (B, T, H, D) fp32 in original order, every row
  *                written (zero for dropped tokens and tokens without any
  *                visible pair).
- *  workspace     device scratch of scfa_bwd_workspace_bytes() bytes (the
- *                transposed / re-laid-out operands, Delta and log2 LSE).
- * Launches 7 kernels on `stream`; no atomics, results are deterministic.  */
+ *  workspace     device scratch of scfa_bwd_workspace_bytes() bytes (Delta
+ *                and log2 LSE per sorted query row).
+ * Launches 3 kernels on `stream`; no atomics, results are deterministic.  */
 size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D);
 
-int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v_t, const int32_t* q_idx,
+int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
              const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
              const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
              const void* dO, int B, int H, int T, int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV,

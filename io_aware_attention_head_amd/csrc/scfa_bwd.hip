@@ -14,24 +14,32 @@
 // NaN-safe softmax carried to the backward).
 //
 // MI355X design:
-//  * Three kernels, no atomics (deterministic): a preparation kernel (dO in
-//    sorted order, Delta, log2 LSE), dK/dV per 64-key tile (4 waves x 16
-//    keys, query chunks of 64 double-buffered in LDS), dQ per 128-query tile
-//    (4 waves x 32 queries, key tiles of 64 double-buffered in LDS).
+//  * Three kernels, no atomics (deterministic): a preparation kernel (Delta
+//    and log2 LSE per sorted query row), dK/dV per 64-key tile (4 waves x 16
+//    keys, query chunks of 64), dQ per 128-query tile (4 waves x 32 queries,
+//    key tiles of 64).
+//  * Operands are read from the original (B, T, H, D) tensors through the
+//    index arrays (gather fused into the loads, as in the forward): each
+//    lane's own rows straight into registers, the shared tiles by
+//    global-to-LDS DMA, double buffered. A tile needed both as row operand
+//    and transposed (Q and dO for dK/dV, K for dQ) is staged twice, once in
+//    the row layout and once in the layout of the transposed reads
+//    (ds_read_b64_tr_b16); no transposed copy exists in memory.
 //  * All six products are v_mfma_f32_16x16x32_bf16. The score-like tiles
 //    (S, dP) are laid out so that each lane owns one column (a key in dK/dV,
 //    a query in dQ) and 4 rows per 16x16 block; their A-operand rows are
 //    permuted so a lane's 8 probabilities cover 8 consecutive rows, which
-//    lets P and dS feed the next MFMA directly as B operands against a
-//    transposed operand read with one 16-byte LDS load.
-//  * Operands needed transposed (Q^T, dO^T for dK/dV; K^T for dQ) are
-//    produced once by a tiled transpose into the workspace.
+//    lets P and dS feed the next MFMA directly as B operands.
+//  * Masks are accumulator biases (0 / -inf) built with VCC-only selects;
+//    tiles proven fully visible by the extrema skip them, and each wave
+//    skips chunks holding no pair visible to its rows. The tile statistics
+//    of a workgroup's range are staged in LDS once.
 //  * Gradients are staged in LDS and written as whole rows at the original
 //    token positions; QK-drop zeroes the rows of dropped tokens.
 
 #include <math.h>
 
-#include "scfa_mfma.h"
+#include "scfa_stage.h"
 
 namespace scfa {
 namespace {
@@ -41,17 +49,15 @@ constexpr int BN = SCFA_TILE_N;  // 64: dK/dV workgroup keys, table granularity
 constexpr int QC = 64;           // query chunk of the dK/dV loop
 constexpr int HD = 64;
 constexpr int TB = 64 * HD * 2;  // bytes of one 64 x 64 bf16 tile
+constexpr int kStatCap = 256;    // tile statistics of a range held in LDS
 
 struct BwdParams {
-  const uint16_t* q_s;   // (BH, Tp, D) rows
-  const uint16_t* k_s;   // (BH, Tp, D) rows
-  const uint16_t* v_s;   // (BH, Tp, D) rows
-  const uint16_t* q_t;   // (BH, D, Tp)
-  const uint16_t* k_t;   // (BH, D, Tp)
-  const uint16_t* do_s;  // (BH, Tp, D) rows
-  const uint16_t* do_t;  // (BH, D, Tp)
-  const float* lse2;     // (BH, Tp) log2-domain LSE, +inf when no visible key / pad row
-  const float* delta;    // (BH, Tp)
+  const void* q;   // (B, T, H, D) bf16, original order, as are k, v, dO
+  const void* k;
+  const void* v;
+  const void* dO;
+  const float* lse2;   // (BH, TqP) sorted query rows: log2 LSE, +inf when no visible key / pad row
+  const float* delta;  // (BH, TqP)
   const int32_t* q_idx;
   const int32_t* k_idx;
   const int32_t* q_bkt;
@@ -65,31 +71,30 @@ struct BwdParams {
   float* dV;
   int B, H, T;
   int Tq, Tk;    // valid query / key rows (as passed to the range table)
-  int TqP, TkP;  // rows per head of the query-side / key-side buffers
+  int TqP, TkP;  // rows per head of the query-side / key-side index arrays
   int nQt, nKt;
   float c;      // scale * log2(e)
   float scale;  // score scale
 };
 
 // ---------------------------------------------------------------------------
-// Preparation: dO gathered to sorted order, Delta = dO . O, log2 LSE.
+// Preparation: Delta = dO . O and log2 LSE per sorted query row.
 // 8 threads per row (8 dims each), 32 rows per workgroup.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_bwd_prep(const uint16_t* __restrict__ dO, const float* __restrict__ O,
                                                   const float* __restrict__ lse, const int32_t* __restrict__ q_idx,
-                                                  int H, int T, int Tp, uint16_t* __restrict__ do_s,
-                                                  float* __restrict__ lse2, float* __restrict__ delta) {
+                                                  int H, int T, int Tp, float* __restrict__ lse2,
+                                                  float* __restrict__ delta) {
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
   const int r = blockIdx.x * 32 + (threadIdx.x >> 3);
   const int part = threadIdx.x & 7;
   const int qp = q_idx[static_cast<size_t>(bh) * Tp + r];
   const bool valid = qp >= 0 && qp < T;
-  u32x4 dv = {0u, 0u, 0u, 0u};
   float s = 0.f;
   if (valid) {
     const size_t row = (static_cast<size_t>(b) * T + qp) * H + h;
-    dv = *reinterpret_cast<const u32x4*>(dO + row * HD + part * 8);
+    const u32x4 dv = *reinterpret_cast<const u32x4*>(dO + row * HD + part * 8);
     const f32x4 o0 = *reinterpret_cast<const f32x4*>(O + row * HD + part * 8);
     const f32x4 o1 = *reinterpret_cast<const f32x4*>(O + row * HD + part * 8 + 4);
 #pragma unroll
@@ -101,50 +106,11 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const uint16_t* __restrict__ d
   s += __shfl_xor(s, 1);
   s += __shfl_xor(s, 2);
   s += __shfl_xor(s, 4);
-  *reinterpret_cast<u32x4*>(do_s + (static_cast<size_t>(bh) * Tp + r) * HD + part * 8) = dv;
   if (part == 0) {
     const size_t o = static_cast<size_t>(bh) * Tp + r;
     delta[o] = valid ? s : 0.f;
     const float l = valid ? lse[static_cast<size_t>(bh) * T + qp] : -INFINITY;
     lse2[o] = (l == -INFINITY) ? INFINITY : l * kLog2e;
-  }
-}
-
-// (BH, Tp, 64) rows <-> (BH, 64, Tp) columns, one 64 x 64 tile per workgroup.
-template <bool TO_COLS>
-__global__ __launch_bounds__(256) void k_transpose(const uint16_t* __restrict__ in, uint16_t* __restrict__ out, int Tp) {
-  __shared__ uint16_t t[64][66];
-  const int bh = blockIdx.y;
-  const int r0 = blockIdx.x * 64;
-  const size_t base = static_cast<size_t>(bh) * Tp * HD;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int u = threadIdx.x + 256 * i;  // 512 units of 8 elements
-    const int a = u >> 3, c8 = (u & 7) * 8;
-    u32x4 v;
-    if (TO_COLS)
-      v = *reinterpret_cast<const u32x4*>(in + base + static_cast<size_t>(r0 + a) * HD + c8);  // row a
-    else
-      v = *reinterpret_cast<const u32x4*>(in + base + static_cast<size_t>(a) * Tp + r0 + c8);  // dim a
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      t[a][c8 + 2 * e] = static_cast<uint16_t>(v[e] & 0xffffu);
-      t[a][c8 + 2 * e + 1] = static_cast<uint16_t>(v[e] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    const int a = u >> 3, c8 = (u & 7) * 8;  // output line a, 8 consecutive elements
-    u32x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v[e] = static_cast<uint32_t>(t[c8 + 2 * e][a]) | (static_cast<uint32_t>(t[c8 + 2 * e + 1][a]) << 16);
-    if (TO_COLS)
-      *reinterpret_cast<u32x4*>(out + base + static_cast<size_t>(a) * Tp + r0 + c8) = v;
-    else
-      *reinterpret_cast<u32x4*>(out + base + static_cast<size_t>(r0 + a) * HD + c8) = v;
   }
 }
 
@@ -209,42 +175,6 @@ __device__ inline void write_rows(const float* tile, const int32_t* pos, int nro
   }
 }
 
-// 64 x 64 bf16 tile loads: rows (64 rows x 128 B contiguous) and transposed
-// (64 lines of 128 B at a stride of Tpad elements), 2 x 16 B per thread.
-struct Tile2 {
-  u32x4 a, b;
-};
-__device__ __forceinline__ Tile2 load_rows_tile(const uint16_t* base, int tid) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(base);
-  return Tile2{p[tid], p[tid + 256]};
-}
-__device__ __forceinline__ Tile2 load_cols_tile(const uint16_t* base, int Tpad, int tid) {
-  const int u0 = tid, u1 = tid + 256;
-  return Tile2{*reinterpret_cast<const u32x4*>(base + static_cast<size_t>(u0 >> 3) * Tpad + (u0 & 7) * 8),
-               *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(u1 >> 3) * Tpad + (u1 & 7) * 8)};
-}
-// Rows are read as A operands with permuted rows (swz_k); transposed tiles
-// are read line by line (swizzle line & 7).
-__device__ __forceinline__ void store_rows_tile(uint8_t* lds, const Tile2& t, int tid) {
-  const int u0 = tid, u1 = tid + 256;
-  *reinterpret_cast<u32x4*>(lds + (u0 >> 3) * 128 + (((u0 & 7) ^ swz_k(u0 >> 3)) * 16)) = t.a;
-  *reinterpret_cast<u32x4*>(lds + (u1 >> 3) * 128 + (((u1 & 7) ^ swz_k(u1 >> 3)) * 16)) = t.b;
-}
-__device__ __forceinline__ void store_cols_tile(uint8_t* lds, const Tile2& t, int tid) {
-  const int u0 = tid, u1 = tid + 256;
-  *reinterpret_cast<u32x4*>(lds + (u0 >> 3) * 128 + (((u0 & 7) ^ ((u0 >> 3) & 7)) * 16)) = t.a;
-  *reinterpret_cast<u32x4*>(lds + (u1 >> 3) * 128 + (((u1 & 7) ^ ((u1 >> 3) & 7)) * 16)) = t.b;
-}
-// A operand of a permuted-row tile: block blk, lane row r16, k-chunk ch.
-__device__ __forceinline__ bf16x8 read_rows_op(const uint8_t* lds, int blk, int r16, int ch) {
-  const int row = key_row(blk, r16);
-  return *reinterpret_cast<const bf16x8*>(lds + row * 128 + ((ch ^ swz_k(row)) * 16));
-}
-// A operand of a transposed tile: line d, 8 consecutive entries at chunk ch.
-__device__ __forceinline__ bf16x8 read_cols_op(const uint8_t* lds, int d, int ch) {
-  return *reinterpret_cast<const bf16x8*>(lds + d * 128 + ((ch ^ (d & 7)) * 16));
-}
-
 __device__ inline void map_work(int x, int BH, int ntiles, int& tile, int& bh, bool reverse) {
   int t;
   if ((BH & 7) == 0) {
@@ -258,37 +188,92 @@ __device__ inline void map_work(int x, int BH, int ntiles, int& tile, int& bh, b
   tile = reverse ? ntiles - 1 - t : t;
 }
 
+__device__ __forceinline__ int4 uniform4(const int4& v) {
+  return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                   __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
+}
+
+// Extrema of this wave's 16 keys (lane column r16; the 4 lane groups hold the
+// same keys), over the real ones (0 <= position < T); `all` = no pad key.
+struct WaveKeys {
+  int minpos, maxpos, minb, maxb;
+  bool any, all;
+};
+
+__device__ inline WaveKeys wave_keys(int kpos, int kbkt, int T) {
+  const bool real = kpos >= 0 && kpos < T;
+  int mn = real ? kpos : kInt32Max, mx = real ? kpos : kInt32Min;
+  int mnb = real ? kbkt : kInt32Max, mxb = real ? kbkt : kInt32Min;
+  int nreal = real ? 1 : 0;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    mn = min(mn, __shfl_xor(mn, o));
+    mx = max(mx, __shfl_xor(mx, o));
+    mnb = min(mnb, __shfl_xor(mnb, o));
+    mxb = max(mxb, __shfl_xor(mxb, o));
+    nreal += __shfl_xor(nreal, o);
+  }
+  WaveKeys k;
+  k.minpos = __builtin_amdgcn_readfirstlane(mn);
+  k.maxpos = __builtin_amdgcn_readfirstlane(mx);
+  k.minb = __builtin_amdgcn_readfirstlane(mnb);
+  k.maxb = __builtin_amdgcn_readfirstlane(mxb);
+  nreal = __builtin_amdgcn_readfirstlane(nreal);
+  k.any = nreal > 0;
+  k.all = nreal == 16;
+  return k;
+}
+
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per 64-key tile.
+// dK, dV: one workgroup per 64-key tile; wave w owns keys 16w .. 16w+15
+// (its K and V rows in registers, one key per lane column). Query chunks of
+// 64 rows are staged by DMA: Q and dO each in the row layout (A operands of
+// S = Q K^T and dP = dO V^T) and in the transposed-read layout (A operands of
+// dK^T += Q^T dS and dV^T += dO^T P), with their positions, buckets, log2
+// LSE and Delta.
 // ---------------------------------------------------------------------------
 template <bool HASH, bool ZD>
 __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
-  __shared__ __align__(16) uint8_t stage[2][4 * TB];  // Q rows, Q^T, dO rows, dO^T
+  __shared__ __align__(16) uint8_t smem[2 * 4 * TB];  // 2 stages x (Q rows, Q tr, dO rows, dO tr); epilogue staging
   __shared__ __align__(16) int32_t qpos_s[2][QC];
   __shared__ __align__(16) int32_t qbkt_s[2][QC];
   __shared__ __align__(16) float lse_s[2][QC];
   __shared__ __align__(16) float del_s[2][QC];
+  __shared__ __align__(16) int4 Qst[kStatCap];
   __shared__ int32_t Ki[BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int ws = __builtin_amdgcn_readfirstlane(w);
   const int BH = p.B * p.H;
   int kt, bh;
   map_work(blockIdx.x, BH, p.nKt, kt, bh, false);  // early key tiles see the most queries
   const int b = bh / p.H, h = bh - b * p.H;
-  const size_t rowbase = static_cast<size_t>(bh) * p.TqP;        // query side
-  const size_t colbase = static_cast<size_t>(bh) * HD * p.TqP;
-  const size_t kbase = static_cast<size_t>(bh) * p.TkP;          // key side
-
+  const size_t rowbase = static_cast<size_t>(bh) * p.TqP;  // query side
+  const size_t kbase = static_cast<size_t>(bh) * p.TkP;    // key side
+  const int2 rng = p.bwd_tab[static_cast<size_t>(bh) * p.nKt + kt];
+  const int4* qst = p.qstats + static_cast<size_t>(bh) * p.nQt;
+  const bool qst_lds = rng.y - rng.x <= kStatCap;
+  if (qst_lds)
+    for (int i = tid; i < rng.y - rng.x; i += 256) Qst[i] = qst[rng.x + i];
   if (tid < BN) Ki[tid] = p.k_idx[kbase + kt * BN + tid];
+  __syncthreads();
+  auto qstat = [&](int i) { return uniform4(qst_lds ? Qst[i - rng.x] : qst[i]); };
+
+  const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
+  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;
   const int krow = kt * BN + w * 16 + r16;  // this lane's key
   const int kpos = p.k_idx[kbase + krow];
   const int kbkt = HASH ? p.k_bkt[kbase + krow] : 0;
+  const WaveKeys wk = wave_keys(kpos, kbkt, p.T);
   bf16x8 Kb[2], Vb[2];
+  {
+    const size_t off = head0 + static_cast<size_t>(src_row(kpos, p.T)) * rstride;
 #pragma unroll
-  for (int ds = 0; ds < 2; ++ds) {
-    Kb[ds] = *reinterpret_cast<const bf16x8*>(p.k_s + (kbase + krow) * HD + ds * 32 + g * 8);
-    Vb[ds] = *reinterpret_cast<const bf16x8*>(p.v_s + (kbase + krow) * HD + ds * 32 + g * 8);
+    for (int ds = 0; ds < 2; ++ds) {
+      Kb[ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.k) + off + (ds * 32 + g * 8) * 2);
+      Vb[ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.v) + off + (ds * 32 + g * 8) * 2);
+    }
   }
   f32x4 dVa[4], dKa[4];
 #pragma unroll
@@ -296,123 +281,158 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
     dVa[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     dKa[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int2 rng = p.bwd_tab[static_cast<size_t>(bh) * p.nKt + kt];
-  const int4 ks = p.kstats[static_cast<size_t>(bh) * p.nKt + kt];
-  const int4* qst = p.qstats + static_cast<size_t>(bh) * p.nQt;
-  const bool kfull = (kt + 1) * BN <= p.Tk;
 
+  // ---- DMA staging of a query chunk: wave w stages rows 16w .. 16w+15 ------
+  const uint8_t* qg = static_cast<const uint8_t*>(p.q) + head0;
+  const uint8_t* dg = static_cast<const uint8_t*>(p.dO) + head0;
+  uint32_t rch[2], tch[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * w + 8 * i + (lane >> 3), cp = lane & 7;
+    rch[i] = (cp ^ swz_k(row)) * 16;  // row layout
+    tch[i] = swz_v(row, cp) * 16;     // transposed-read layout
+  }
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t lds_small = ws == 0 ? lds_addr(&qpos_s[0][0])
+                             : ws == 1 ? lds_addr(&qbkt_s[0][0])
+                             : ws == 2 ? lds_addr(&lse_s[0][0])
+                                       : lds_addr(&del_s[0][0]);
+  const void* small_src = ws == 0 ? static_cast<const void*>(p.q_idx + rowbase)
+                          : ws == 1 ? static_cast<const void*>(HASH ? p.q_bkt + rowbase : p.q_idx + rowbase)
+                          : ws == 2 ? static_cast<const void*>(p.lse2 + rowbase)
+                                    : static_cast<const void*>(p.delta + rowbase);
+  const int nch = 2 * p.nQt;
+  auto chunk_rows = [&](int ci, int (&pos)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pos[i] = p.q_idx[rowbase + min(ci, nch - 1) * QC + 16 * w + 8 * i + (lane >> 3)];
+  };
+  auto stage = [&](int ci, int s, const int (&pos)[2]) {
+    const uint32_t base = lds0 + s * 4 * TB + ws * 2048;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t off = static_cast<uint32_t>(src_row(pos[i], p.T)) * rstride;
+      dma16(qg, off + rch[i], base + i * 1024);
+      dma16(qg, off + tch[i], base + TB + i * 1024);
+      dma16(dg, off + rch[i], base + 2 * TB + i * 1024);
+      dma16(dg, off + tch[i], base + 3 * TB + i * 1024);
+    }
+    dma4(static_cast<const uint8_t*>(small_src) + ci * QC * 4, lane * 4, lds_small + s * QC * 4);
+  };
   // chunk ci = 2 * query tile + half; skip tiles failing the causal test
+  const int4 ks = p.kstats[static_cast<size_t>(bh) * p.nKt + kt];
+  const int cend = 2 * rng.y;
   auto next_chunk = [&](int ci) {
-    while (ci < 2 * rng.y && qst[ci >> 1].y < ks.x) ci = (ci | 1) + 1;
+    while (ci < cend && qstat(ci >> 1).y < ks.x) ci = (ci | 1) + 1;
     return ci;
-  };
-  Tile2 rq, rqt, rdo, rdot;
-  float rsc = 0.f;
-  int rsi = 0;
-  auto load = [&](int ci) {
-    const int q0 = ci * QC;
-    rq = load_rows_tile(p.q_s + (rowbase + q0) * HD, tid);
-    rqt = load_cols_tile(p.q_t + colbase + q0, p.TqP, tid);
-    rdo = load_rows_tile(p.do_s + (rowbase + q0) * HD, tid);
-    rdot = load_cols_tile(p.do_t + colbase + q0, p.TqP, tid);
-    const int which = tid >> 6, r = tid & 63;
-    if (which == 0) rsi = p.q_idx[rowbase + q0 + r];
-    else if (which == 1) rsi = HASH ? p.q_bkt[rowbase + q0 + r] : 0;
-    else if (which == 2) rsc = p.lse2[rowbase + q0 + r];
-    else rsc = p.delta[rowbase + q0 + r];
-  };
-  auto store = [&](int s) {
-    store_rows_tile(stage[s], rq, tid);
-    store_cols_tile(stage[s] + TB, rqt, tid);
-    store_rows_tile(stage[s] + 2 * TB, rdo, tid);
-    store_cols_tile(stage[s] + 3 * TB, rdot, tid);
-    const int which = tid >> 6, r = tid & 63;
-    if (which == 0) qpos_s[s][r] = rsi;
-    else if (which == 1) qbkt_s[s][r] = rsi;
-    else if (which == 2) lse_s[s][r] = rsc;
-    else del_s[s][r] = rsc;
   };
 
   int ci = next_chunk(2 * rng.x);
-  if (ci < 2 * rng.y) {
-    load(ci);
-    store(0);
+  int cn = ci < cend ? next_chunk(ci + 1) : cend;
+  int pos[2];
+  if (ci < cend) {
+    chunk_rows(ci, pos);
+    stage(ci, 0, pos);
   }
+  chunk_rows(cn, pos);
+  dma_wait();
   __syncthreads();
   int s = 0;
-  while (ci < 2 * rng.y) {
-    const int cn = next_chunk(ci + 1);
-    if (cn < 2 * rng.y) load(cn);
-    const uint8_t* Qr = stage[s];
-    const uint8_t* Qt = stage[s] + TB;
-    const uint8_t* Dr = stage[s] + 2 * TB;
-    const uint8_t* Dt = stage[s] + 3 * TB;
+  int4 qs_cur = ci < cend ? qstat(ci >> 1) : make_int4(0, 0, 0, 0);
+  while (ci < cend) {
+    const int cnn = cn < cend ? next_chunk(cn + 1) : cend;
+    const int4 qs = qs_cur;
+    if (cn < cend) qs_cur = qstat(cn >> 1);
+    int pos_nn[2];
+    chunk_rows(cnn, pos_nn);  // issued before the DMA: waiting for it never waits for the DMA
+    __builtin_amdgcn_sched_barrier(0);
+    if (cn < cend) stage(cn, s ^ 1, pos);
 
-    // S = Q K^T and dP = dO V^T: lane column = this lane's key, rows = queries
-    f32x4 S[4], dP[4];
+    // this wave's keys against the chunk's query tile: skip / no mask
+    const bool empty = !wk.any || wk.minpos > qs.y || (HASH && (wk.minb > qs.w || wk.maxb < qs.z));
+    if (!empty) {
+      const uint8_t* Qr = smem + s * 4 * TB;
+      const uint8_t* Qt = Qr + TB;
+      const uint8_t* Dr = Qr + 2 * TB;
+      const uint8_t* Dt = Qr + 3 * TB;
+      bool full = wk.all && wk.maxpos <= qs.x && ((ci >> 1) + 1) * BM <= p.Tq;
+      if (HASH) full = full && qs.z == qs.w && wk.minb == wk.maxb && wk.minb == qs.z;
+      // S = Q K^T (from the mask bias) and dP = dO V^T: rows = queries,
+      // column = this lane's key; element e of block qb is query
+      // 32 (qb >> 1) + 8 g + 4 (qb & 1) + e of the chunk
+      f32x4 S[4], dP[4];
+      if (full) {
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      S[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dP[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+        for (int qb = 0; qb < 4; ++qb) S[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        const bool buckets = HASH && !(qs.z == qs.w && wk.minb == wk.maxb);
 #pragma unroll
-    for (int ds = 0; ds < 2; ++ds)
+        for (int qb = 0; qb < 4; ++qb) {
+          const int qo = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);
+          const int4 qp4 = *reinterpret_cast<const int4*>(&qpos_s[s][qo]);
+          f32x4 c;
+          c[0] = bias_if_ge(qp4.x, kpos);
+          c[1] = bias_if_ge(qp4.y, kpos);
+          c[2] = bias_if_ge(qp4.z, kpos);
+          c[3] = bias_if_ge(qp4.w, kpos);
+          if (buckets) {
+            const int4 qb4 = *reinterpret_cast<const int4*>(&qbkt_s[s][qo]);
+            c[0] = keep_if_eq(c[0], qb4.x, kbkt);
+            c[1] = keep_if_eq(c[1], qb4.y, kbkt);
+            c[2] = keep_if_eq(c[2], qb4.z, kbkt);
+            c[3] = keep_if_eq(c[3], qb4.w, kbkt);
+          }
+          S[qb] = c;
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) dP[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+          S[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_row_op(Qr, qb, r16, ds * 4 + g), Kb[ds], S[qb], 0, 0, 0);
+          dP[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_row_op(Dr, qb, r16, ds * 4 + g), Vb[ds], dP[qb], 0, 0, 0);
+        }
+      // P = exp2(S c - lse2), dS = P (dP - Delta)
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
-        S[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_rows_op(Qr, qb, r16, ds * 4 + g), Kb[ds], S[qb], 0, 0, 0);
-        dP[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_rows_op(Dr, qb, r16, ds * 4 + g), Vb[ds], dP[qb], 0, 0, 0);
+        const int qo = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[s][qo]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&del_s[s][qo]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pe = __builtin_amdgcn_exp2f(fmaf(S[qb][e], p.c, -l4[e]));
+          S[qb][e] = pe;
+          dP[qb][e] = pe * (dP[qb][e] - d4[e]);
+        }
       }
-
-    const int4 qs = qst[ci >> 1];
-    bool full = kfull && ks.y <= qs.x && ((ci >> 1) + 1) * BM <= p.Tq;
-    if (HASH) full = full && ks.z == ks.w && qs.z == qs.w && ks.z == qs.z;
-    bf16x8 Pp[2], Sp[2];
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const int qo = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[s][qo]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&del_s[s][qo]);
-      int4 qp4 = make_int4(0, 0, 0, 0), qb4 = make_int4(0, 0, 0, 0);
-      if (!full) {
-        qp4 = *reinterpret_cast<const int4*>(&qpos_s[s][qo]);
-        if (HASH) qb4 = *reinterpret_cast<const int4*>(&qbkt_s[s][qo]);
-      }
-      f32x4 P, dS;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int qpe = e == 0 ? qp4.x : e == 1 ? qp4.y : e == 2 ? qp4.z : qp4.w;
-        const int qbe = e == 0 ? qb4.x : e == 1 ? qb4.y : e == 2 ? qb4.z : qb4.w;
-        const bool vis = full || (qpe >= kpos && (!HASH || qbe == kbkt));
-        const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(S[qb][e], p.c, -l4[e])) : 0.f;
-        P[e] = pe;
-        dS[e] = pe * (dP[qb][e] - d4[e]);
-      }
-      S[qb] = P;
-      dP[qb] = dS;
-    }
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      Pp[kc] = pack_bf16x8(S[2 * kc], S[2 * kc + 1]);
-      Sp[kc] = pack_bf16x8(dP[2 * kc], dP[2 * kc + 1]);
-    }
-    // dV^T += dO^T P,  dK^T += Q^T dS  (rows = dims, column = this lane's key)
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
+      bf16x8 Pp[2], Sp[2];
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        const int d = db * 16 + r16;
-        dVa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_cols_op(Dt, d, kc * 4 + g), Pp[kc], dVa[db], 0, 0, 0);
-        dKa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_cols_op(Qt, d, kc * 4 + g), Sp[kc], dKa[db], 0, 0, 0);
+        Pp[kc] = pack_bf16x8(S[2 * kc], S[2 * kc + 1]);
+        Sp[kc] = pack_bf16x8(dP[2 * kc], dP[2 * kc + 1]);
       }
+      // dV^T += dO^T P,  dK^T += Q^T dS  (rows = dims, column = this lane's key)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          dVa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_tr_op(Dt, db, kc, g, r16), Pp[kc], dVa[db], 0, 0, 0);
+          dKa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_tr_op(Qt, db, kc, g, r16), Sp[kc], dKa[db], 0, 0, 0);
+        }
+    }
 
-    if (cn < 2 * rng.y) store(s ^ 1);
+    dma_wait();
     __syncthreads();
     s ^= 1;
     ci = cn;
+    cn = cnn;
+    pos[0] = pos_nn[0];
+    pos[1] = pos_nn[1];
   }
 
   // ---- epilogue: stage dK (scaled) and dV in LDS, write whole rows ---------
-  float* tk = reinterpret_cast<float*>(&stage[0][0]);
+  float* tk = reinterpret_cast<float*>(smem);
   float* tv = tk + BN * HD;
   const int row = w * 16 + r16;
   stage_rows(tk, row, g, dKa, p.scale);
@@ -424,26 +444,40 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per 128-query tile, over the forward table's key tiles.
+// dQ: one workgroup per 128-query tile, over the forward table's key tiles;
+// wave w owns queries 32w .. 32w+31 (Q and dO rows in registers). Key tiles
+// are staged by DMA: K in the row layout (A operand of S^T = K Q^T) and in
+// the transposed-read layout (A operand of dQ^T += K^T dS^T), V in the row
+// layout (A operand of dP^T = V dO^T), with the keys' positions / buckets.
 // ---------------------------------------------------------------------------
 template <bool HASH, bool ZD>
 __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
-  __shared__ __align__(16) uint8_t stage[2][3 * TB];  // K rows, V rows, K^T
-  __shared__ __align__(16) int32_t kpos_s[2][BN];
-  __shared__ __align__(16) int32_t kbkt_s[2][BN];
-  __shared__ int32_t Qi[BM];
+  __shared__ __align__(16) uint8_t smem[2 * 3 * TB];  // 2 stages x (K rows, K tr, V rows); epilogue staging
+  __shared__ __align__(16) int32_t Kp[2][BN];
+  __shared__ __align__(16) int32_t Kb[2][BN];
+  __shared__ __align__(16) int4 Kst[kStatCap];
+  static_assert(2 * 3 * TB >= BM * HD * 4, "dQ staging does not fit");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int ws = __builtin_amdgcn_readfirstlane(w);
   const int BH = p.B * p.H;
   int qt, bh;
   map_work(blockIdx.x, BH, p.nQt, qt, bh, true);
   const int b = bh / p.H, h = bh - b * p.H;
-  const size_t rowbase = static_cast<size_t>(bh) * p.TqP;        // query side
-  const size_t kbase = static_cast<size_t>(bh) * p.TkP;          // key side
-  const size_t kcolbase = static_cast<size_t>(bh) * HD * p.TkP;
-  if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];
+  const size_t rowbase = static_cast<size_t>(bh) * p.TqP;  // query side
+  const size_t kbase = static_cast<size_t>(bh) * p.TkP;    // key side
+  const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
+  const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
+  const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
+  const bool kst_lds = rng.y - rng.x <= kStatCap;
+  if (kst_lds)
+    for (int i = tid; i < rng.y - rng.x; i += 256) Kst[i] = kst[rng.x + i];
+  __syncthreads();
+  auto kstat = [&](int j) { return uniform4(kst_lds ? Kst[j - rng.x] : kst[j]); };
 
+  const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;
+  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;
   const int q0 = qt * BM + w * 32;
   int qpos[2], qbkt[2];
   float ql2[2], qdl[2];
@@ -455,148 +489,160 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
     qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
     ql2[qb] = p.lse2[rowbase + row];
     qdl[qb] = p.delta[rowbase + row];
+    const size_t off = head0 + static_cast<size_t>(src_row(qpos[qb], p.T)) * rstride;
 #pragma unroll
     for (int ds = 0; ds < 2; ++ds) {
-      Qb[qb][ds] = *reinterpret_cast<const bf16x8*>(p.q_s + (rowbase + row) * HD + ds * 32 + g * 8);
-      Db[qb][ds] = *reinterpret_cast<const bf16x8*>(p.do_s + (rowbase + row) * HD + ds * 32 + g * 8);
+      Qb[qb][ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.q) + off + (ds * 32 + g * 8) * 2);
+      Db[qb][ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.dO) + off + (ds * 32 + g * 8) * 2);
     }
   }
+  const WaveRows wr = wave_rows(qpos, qbkt);
   f32x4 dQa[4][2];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) dQa[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
-  const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
-  const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
-  const bool qfull = (qt + 1) * BM <= p.Tq;
+  // ---- DMA staging of a key tile: wave w stages rows 16w .. 16w+15 --------
+  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + head0;
+  const uint8_t* vg = static_cast<const uint8_t*>(p.v) + head0;
+  const int32_t* kig = p.k_idx + kbase;
+  const int32_t* kbg = HASH ? p.k_bkt + kbase : nullptr;
+  uint32_t rch[2], tch[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * w + 8 * i + (lane >> 3), cp = lane & 7;
+    rch[i] = (cp ^ swz_k(row)) * 16;
+    tch[i] = swz_v(row, cp) * 16;
+  }
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t ldsp = lds_addr(&Kp[0][0]), ldsb = lds_addr(&Kb[0][0]);
+  auto tile_rows = [&](int j, int (&pos)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pos[i] = kig[min(j, p.nKt - 1) * BN + 16 * w + 8 * i + (lane >> 3)];
+  };
+  auto stage = [&](int j, int s, const int (&pos)[2]) {
+    const uint32_t base = lds0 + s * 3 * TB + ws * 2048;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t off = static_cast<uint32_t>(src_row(pos[i], p.T)) * rstride;
+      dma16(kg, off + rch[i], base + i * 1024);
+      dma16(kg, off + tch[i], base + TB + i * 1024);
+      dma16(vg, off + rch[i], base + 2 * TB + i * 1024);
+    }
+    if (ws == 0) dma4(kig + j * BN, lane * 4, ldsp + s * BN * 4);
+    else if (HASH && ws == 1) dma4(kbg + j * BN, lane * 4, ldsb + s * BN * 4);
+  };
   auto next_tile = [&](int j) {
-    while (j < rng.y && kst[j].x > qs.y) ++j;
+    if (HASH)
+      while (j < rng.y && kstat(j).x > qs.y) ++j;
     return j;
-  };
-  Tile2 rk, rv, rkt;
-  int ri = 0;
-  auto load = [&](int j) {
-    rk = load_rows_tile(p.k_s + (kbase + j * BN) * HD, tid);
-    rv = load_rows_tile(p.v_s + (kbase + j * BN) * HD, tid);
-    rkt = load_cols_tile(p.k_t + kcolbase + j * BN, p.TkP, tid);
-    if (tid < BN) ri = p.k_idx[kbase + j * BN + tid];
-    else if (HASH && tid < 2 * BN) ri = p.k_bkt[kbase + j * BN + tid - BN];
-  };
-  auto store = [&](int s) {
-    store_rows_tile(stage[s], rk, tid);
-    store_rows_tile(stage[s] + TB, rv, tid);
-    store_cols_tile(stage[s] + 2 * TB, rkt, tid);
-    if (tid < BN) kpos_s[s][tid] = ri;
-    else if (HASH && tid < 2 * BN) kbkt_s[s][tid - BN] = ri;
   };
 
   int j = next_tile(rng.x);
+  int jn = j < rng.y ? next_tile(j + 1) : rng.y;
+  int pos[2];
   if (j < rng.y) {
-    load(j);
-    store(0);
+    tile_rows(j, pos);
+    stage(j, 0, pos);
   }
+  tile_rows(jn, pos);
+  dma_wait();
   __syncthreads();
   int s = 0;
+  int4 ks_cur = j < rng.y ? kstat(j) : make_int4(0, 0, 0, 0);
   while (j < rng.y) {
-    const int jn = next_tile(j + 1);
-    if (jn < rng.y) load(jn);
-    const uint8_t* Kr = stage[s];
-    const uint8_t* Vr = stage[s] + TB;
-    const uint8_t* Kt = stage[s] + 2 * TB;
+    const int jnn = jn < rng.y ? next_tile(jn + 1) : rng.y;
+    const int4 ks = ks_cur;
+    if (jn < rng.y) ks_cur = kstat(jn);
+    int pos_nn[2];
+    tile_rows(jnn, pos_nn);
+    __builtin_amdgcn_sched_barrier(0);
+    if (jn < rng.y) stage(jn, s ^ 1, pos);
 
-    // S^T = K Q^T and dP^T = V dO^T: lane column = query, rows = keys
-    f32x4 S[4][2], dP[4][2];
+    if (!tile_empty_for<HASH>(ks, wr)) {
+      const uint8_t* Kr = smem + s * 3 * TB;
+      const uint8_t* Kt = Kr + TB;
+      const uint8_t* Vr = Kr + 2 * TB;
+      // S^T = K Q^T (from the mask bias) and dP^T = V dO^T: rows = keys,
+      // column = this lane's query
+      f32x4 S[4][2], dP[4][2];
+      if (tile_full_for<HASH>(ks, wr, j, p.Tk)) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dP[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        mask_bias<HASH>(S, ks, wr, Kp[s], Kb[s], qpos, qbkt, g);
       }
 #pragma unroll
-    for (int ds = 0; ds < 2; ++ds)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 ak = read_rows_op(Kr, kb, r16, ds * 4 + g);
-        const bf16x8 av = read_rows_op(Vr, kb, r16, ds * 4 + g);
+        for (int qb = 0; qb < 2; ++qb) dP[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, Qb[qb][ds], S[kb][qb], 0, 0, 0);
-          dP[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Db[qb][ds], dP[kb][qb], 0, 0, 0);
+      for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 ak = read_row_op(Kr, kb, r16, ds * 4 + g);
+          const bf16x8 av = read_row_op(Vr, kb, r16, ds * 4 + g);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, Qb[qb][ds], S[kb][qb], 0, 0, 0);
+            dP[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Db[qb][ds], dP[kb][qb], 0, 0, 0);
+          }
         }
-      }
-    const int4 ks = kst[j];
-    bool full = qfull && ks.y <= qs.x && (j + 1) * BN <= p.Tk;
-    if (HASH) full = full && ks.z == ks.w && qs.z == qs.w && ks.z == qs.z;
+      // dS^T = P^T (dP^T - Delta), P^T = exp2(S^T c - lse2)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int kbase = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1);
-      int4 kp4 = make_int4(0, 0, 0, 0), kb4 = make_int4(0, 0, 0, 0);
-      if (!full) {
-        kp4 = *reinterpret_cast<const int4*>(&kpos_s[s][kbase]);
-        if (HASH) kb4 = *reinterpret_cast<const int4*>(&kbkt_s[s][kbase]);
-      }
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][e], p.c, -ql2[qb]));
+            dP[kb][qb][e] = pe * (dP[kb][qb][e] - qdl[qb]);
+          }
+      // dQ^T += K^T dS^T (rows = dims, column = this lane's query)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kpe = e == 0 ? kp4.x : e == 1 ? kp4.y : e == 2 ? kp4.z : kp4.w;
-          const int kbe = e == 0 ? kb4.x : e == 1 ? kb4.y : e == 2 ? kb4.z : kb4.w;
-          const bool vis = full || (kpe <= qpos[qb] && (!HASH || kbe == qbkt[qb]));
-          const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(S[kb][qb][e], p.c, -ql2[qb])) : 0.f;
-          dP[kb][qb][e] = pe * (dP[kb][qb][e] - qdl[qb]);
+        for (int kc = 0; kc < 2; ++kc) {
+          const bf16x8 sp = pack_bf16x8(dP[2 * kc][qb], dP[2 * kc + 1][qb]);
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            dQa[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_tr_op(Kt, db, kc, g, r16), sp, dQa[db][qb], 0,
+                                                                 0, 0);
         }
     }
-    // dQ^T += K^T dS^T (rows = dims, column = this lane's query)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const bf16x8 sp = pack_bf16x8(dP[2 * kc][qb], dP[2 * kc + 1][qb]);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          dQa[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_cols_op(Kt, db * 16 + r16, kc * 4 + g), sp,
-                                                               dQa[db][qb], 0, 0, 0);
-      }
 
-    if (jn < rng.y) store(s ^ 1);
+    dma_wait();
     __syncthreads();
     s ^= 1;
     j = jn;
+    jn = jnn;
+    pos[0] = pos_nn[0];
+    pos[1] = pos_nn[1];
   }
 
   // ---- epilogue ------------------------------------------------------------
-  float* tq = reinterpret_cast<float*>(&stage[0][0]);
+  float* tq = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const f32x4 a[4] = {dQa[0][qb], dQa[1][qb], dQa[2][qb], dQa[3][qb]};
     stage_rows(tq, w * 32 + qb * 16 + r16, g, a, p.scale);
   }
   __syncthreads();
-  write_rows(tq, Qi, BM, p.dQ, p.T, p.H, b, h);
-  if constexpr (ZD) zero_unheld<BM>(p.q_idx + rowbase, Qi, qt, p.TqP, p.T, p.H, b, h, p.dQ, nullptr);
+  const int32_t* qi = p.q_idx + rowbase + qt * BM;  // this tile's index entries
+  write_rows(tq, qi, BM, p.dQ, p.T, p.H, b, h);
+  if constexpr (ZD) zero_unheld<BM>(p.q_idx + rowbase, qi, qt, p.TqP, p.T, p.H, b, h, p.dQ, nullptr);
 }
 
-// Workspace: v_s and k_t on the key side, q_t, do_s, do_t, lse2 and delta on
-// the query side.
-size_t ws_layout(int B, int H, int TqP, int TkP, size_t off[8]) {
-  const size_t bfq = static_cast<size_t>(B) * H * TqP * HD * 2;  // one bf16 (BH, TqP, D) tensor
-  const size_t bfk = static_cast<size_t>(B) * H * TkP * HD * 2;
+// Workspace: log2 LSE and Delta per sorted query row.
+size_t ws_layout(int B, int H, int TqP, size_t off[3]) {
   const size_t f = static_cast<size_t>(B) * H * TqP * 4;
-  size_t o = 0;
-  for (int i = 0; i < 5; ++i) {  // v_s, q_t, k_t, do_s, do_t
-    off[i] = o;
-    const size_t bf = (i == 0 || i == 2) ? bfk : bfq;
-    o += (bf + 255) & ~size_t(255);
-  }
-  off[5] = o;  // lse2
-  o += (f + 255) & ~size_t(255);
-  off[6] = o;  // delta
-  o += (f + 255) & ~size_t(255);
-  off[7] = o;
-  return o;
+  off[0] = 0;
+  off[1] = (f + 255) & ~size_t(255);
+  off[2] = off[1] + ((f + 255) & ~size_t(255));
+  return off[2];
 }
 
 template <bool HASH, bool ZD>
@@ -617,18 +663,18 @@ extern "C" {
 
 size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D) {
   if ((mode != SCFA_QK && mode != SCFA_HASH) || B < 1 || H < 1 || Tq < 1 || Tk < 1 || D != HD) return 0;
-  size_t off[8];
-  return ws_layout(B, H, pad_rows(Tq), pad_rows(Tk), off);
+  size_t off[3];
+  return ws_layout(B, H, pad_rows(Tq), off);
 }
 
-int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v_t, const int32_t* q_idx,
+int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
              const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
              const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
              const void* dO, int B, int H, int T, int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV,
              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (mode != SCFA_QK && mode != SCFA_HASH) return SCFA_ERR_INVALID;
-  if (!q || !k || !v_t || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !bwd_tab || !O || !lse || !dO ||
-      !dQ || !dK || !dV || !workspace)
+  if (!q || !k || !v || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !bwd_tab || !O || !lse || !dO || !dQ ||
+      !dK || !dV || !workspace)
     return SCFA_ERR_INVALID;
   if (mode == SCFA_HASH && (!q_bkt || !k_bkt)) return SCFA_ERR_INVALID;
   if (B < 1 || H < 1 || T < 1 || Tq < 1 || Tk < 1 || !(scale > 0.f) || !isfinite(scale)) return SCFA_ERR_INVALID;
@@ -636,19 +682,16 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
   if (D != HD || dtype_in != SCFA_BF16) return SCFA_ERR_UNSUPPORTED;
   if (mode == SCFA_QK && (Tq % SCFA_ROW_ALIGN || Tk != Tq)) return SCFA_ERR_INVALID;
   const int TqP = pad_rows(Tq), TkP = pad_rows(Tk);
-  size_t off[8];
-  if (workspace_bytes < ws_layout(B, H, TqP, TkP, off)) return SCFA_ERR_INVALID;
+  size_t off[3];
+  if (workspace_bytes < ws_layout(B, H, TqP, off)) return SCFA_ERR_INVALID;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   BwdParams p{};
-  p.q_s = static_cast<const uint16_t*>(q);
-  p.k_s = static_cast<const uint16_t*>(k);
-  p.v_s = reinterpret_cast<uint16_t*>(ws + off[0]);
-  p.q_t = reinterpret_cast<uint16_t*>(ws + off[1]);
-  p.k_t = reinterpret_cast<uint16_t*>(ws + off[2]);
-  p.do_s = reinterpret_cast<uint16_t*>(ws + off[3]);
-  p.do_t = reinterpret_cast<uint16_t*>(ws + off[4]);
-  p.lse2 = reinterpret_cast<float*>(ws + off[5]);
-  p.delta = reinterpret_cast<float*>(ws + off[6]);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.dO = dO;
+  p.lse2 = reinterpret_cast<float*>(ws + off[0]);
+  p.delta = reinterpret_cast<float*>(ws + off[1]);
   p.q_idx = q_idx;
   p.k_idx = k_idx;
   p.q_bkt = q_bkt;
@@ -671,23 +714,8 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
   p.nKt = TkP / BN;
   p.c = scale * kLog2e;
   p.scale = scale;
-  const int BH = B * H;
-  // preparation: transposes / row copies of the sorted operands, dO, Delta, LSE
-  hipLaunchKernelGGL(k_transpose<false>, dim3(TkP / 64, BH), dim3(256), 0, stream, static_cast<const uint16_t*>(v_t),
-                     const_cast<uint16_t*>(p.v_s), TkP);
-  SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_transpose<true>, dim3(TqP / 64, BH), dim3(256), 0, stream, p.q_s, const_cast<uint16_t*>(p.q_t),
-                     TqP);
-  SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_transpose<true>, dim3(TkP / 64, BH), dim3(256), 0, stream, p.k_s, const_cast<uint16_t*>(p.k_t),
-                     TkP);
-  SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_bwd_prep, dim3(TqP / 32, BH), dim3(256), 0, stream, static_cast<const uint16_t*>(dO), O, lse,
-                     q_idx, H, T, TqP, const_cast<uint16_t*>(p.do_s), const_cast<float*>(p.lse2),
-                     const_cast<float*>(p.delta));
-  SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_transpose<true>, dim3(TqP / 64, BH), dim3(256), 0, stream, p.do_s, const_cast<uint16_t*>(p.do_t),
-                     TqP);
+  hipLaunchKernelGGL(k_bwd_prep, dim3(TqP / 32, B * H), dim3(256), 0, stream, static_cast<const uint16_t*>(dO), O, lse,
+                     q_idx, H, T, TqP, const_cast<float*>(p.lse2), const_cast<float*>(p.delta));
   SCFA_RETURN_IF_LAUNCH_FAILED();
   if (mode == SCFA_HASH) return launch_bwd<true, false>(p, stream);
   return launch_bwd<false, true>(p, stream);

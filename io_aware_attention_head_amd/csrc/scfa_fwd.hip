@@ -50,7 +50,7 @@
 
 #include <math.h>
 
-#include "scfa_mfma.h"
+#include "scfa_stage.h"
 
 namespace scfa {
 namespace {
@@ -119,119 +119,6 @@ __device__ inline void pick_work(const FwdParams& p, int& qt, int& bh) {
       bh = x % BH;
     }
   }
-}
-
-// Extrema of this wave's real query rows (pad rows: position -1, their
-// results are never stored): a key tile is skipped by the whole wave when it
-// holds no pair visible to any of them, and unmasked when every pair is
-// visible to all of them. All 4 lane groups hold the same 2 x 16 rows.
-struct WaveRows {
-  int minpos, maxpos, minb, maxb;
-};
-
-__device__ inline WaveRows wave_rows(const int (&qpos)[2], const int (&qbkt)[2]) {
-  WaveRows s{kInt32Max, -1, kInt32Max, kInt32Min};
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    if (qpos[qb] >= 0) {
-      s.minpos = min(s.minpos, qpos[qb]);
-      s.maxpos = max(s.maxpos, qpos[qb]);
-      s.minb = min(s.minb, qbkt[qb]);
-      s.maxb = max(s.maxb, qbkt[qb]);
-    }
-  }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    s.minpos = min(s.minpos, __shfl_xor(s.minpos, o));
-    s.maxpos = max(s.maxpos, __shfl_xor(s.maxpos, o));
-    s.minb = min(s.minb, __shfl_xor(s.minb, o));
-    s.maxb = max(s.maxb, __shfl_xor(s.maxb, o));
-  }
-  // wave-uniform from here on: tile tests become scalar branches
-  s.minpos = __builtin_amdgcn_readfirstlane(s.minpos);
-  s.maxpos = __builtin_amdgcn_readfirstlane(s.maxpos);
-  s.minb = __builtin_amdgcn_readfirstlane(s.minb);
-  s.maxb = __builtin_amdgcn_readfirstlane(s.maxb);
-  return s;
-}
-
-template <bool HASH>
-__device__ inline bool tile_empty_for(const int4& ks, const WaveRows& wr) {
-  return ks.x > wr.maxpos || (HASH && (ks.w < wr.minb || ks.z > wr.maxb));
-}
-
-template <bool HASH>
-__device__ inline bool tile_full_for(const int4& ks, const WaveRows& wr, int j, int Tk) {
-  bool full = ks.y <= wr.minpos && (j + 1) * BN <= Tk;
-  if (HASH) full = full && ks.z == ks.w && wr.minb == wr.maxb && ks.z == wr.minb;
-  return full;
-}
-
-// The compares below go to VCC and are consumed at once, so a masked tile
-// holds no per-element lane masks in scalar registers (-inf comes from a
-// VGPR: VCC already takes the one scalar operand slot).
-// 0 if a >= b, else -inf.
-__device__ __forceinline__ float bias_if_ge(int a, int b) {
-  float r;
-  asm("v_cmp_ge_i32_e32 vcc, %1, %2\n\tv_cndmask_b32_e64 %0, %3, 0, vcc"
-      : "=v"(r)
-      : "v"(a), "v"(b), "v"(0xff800000u)
-      : "vcc");
-  return r;
-}
-// x if a == b, else -inf.
-__device__ __forceinline__ float keep_if_eq(float x, int a, int b) {
-  asm("v_cmp_eq_i32_e32 vcc, %1, %2\n\tv_cndmask_b32_e32 %0, %3, %0, vcc"
-      : "+v"(x)
-      : "v"(a), "v"(b), "v"(0xff800000u)
-      : "vcc");
-  return x;
-}
-
-// Mask bias of a tile: element e of block kb in lane group g (key
-// 32 (kb >> 1) + 8 g + 4 (kb & 1) + e of the tile) is 0 if that key is
-// visible to the lane's query, else -inf. BUCKETS: also compare buckets (not
-// needed when the tile and the wave's queries are all in one bucket: a tile
-// that is not skipped then has the queries' bucket).
-template <bool BUCKETS>
-__device__ inline void bias_tile(f32x4 (&C)[4][2], const int32_t* kp, const int32_t* kbk, const int (&qpos)[2],
-                                 const int (&qbkt)[2], int g) {
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int kbase = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1);
-    const int4 kp4 = *reinterpret_cast<const int4*>(&kp[kbase]);
-    int4 kb4 = make_int4(0, 0, 0, 0);
-    if (BUCKETS) kb4 = *reinterpret_cast<const int4*>(&kbk[kbase]);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qp = qpos[qb];
-      f32x4 c;
-      c[0] = bias_if_ge(qp, kp4.x);
-      c[1] = bias_if_ge(qp, kp4.y);
-      c[2] = bias_if_ge(qp, kp4.z);
-      c[3] = bias_if_ge(qp, kp4.w);
-      if (BUCKETS) {
-        const int qh = qbkt[qb];
-        c[0] = keep_if_eq(c[0], qh, kb4.x);
-        c[1] = keep_if_eq(c[1], qh, kb4.y);
-        c[2] = keep_if_eq(c[2], qh, kb4.z);
-        c[3] = keep_if_eq(c[3], qh, kb4.w);
-      }
-      C[kb][qb] = c;
-    }
-  }
-}
-
-// Mask bias of a tile that is not fully visible: positions only when the
-// tile's keys and the wave's real queries share one bucket (always so in QK
-// mode and in the bucket-aligned layout), positions and buckets otherwise.
-template <bool HASH>
-__device__ inline void mask_bias(f32x4 (&C)[4][2], const int4& ks, const WaveRows& wr, const int32_t* kp,
-                                 const int32_t* kbk, const int (&qpos)[2], const int (&qbkt)[2], int g) {
-  if (!HASH || (ks.z == ks.w && wr.minb == wr.maxb))
-    bias_tile<false>(C, kp, kbk, qpos, qbkt, g);
-  else
-    bias_tile<true>(C, kp, kbk, qpos, qbkt, g);
 }
 
 // Max (log2 units) of the 16 scores a lane holds for query column qb
@@ -333,36 +220,6 @@ __device__ inline void fwd_epilogue(const FwdParams& p, TOUT* ost, const int32_t
 // bf16 inputs.
 // ---------------------------------------------------------------------------
 
-// Global -> LDS DMA without registers: each lane's 16 (or 4) bytes land at
-// consecutive LDS addresses from the wave-uniform byte address `lds`; the
-// source is a wave-uniform base plus a per-lane 32-bit offset. Issued as
-// inline assembly so that the compiler does not order the LDS reads of the
-// other stage behind it; completion is awaited with dma_wait() before the
-// barrier that publishes the stage.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
-}
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt not waited on), as a builtin so that
-// the compiler knows every earlier vector-memory load has completed.
-__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0xF70); }
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  const __attribute__((address_space(3))) void* lp = (const __attribute__((address_space(3))) void*)p;
-  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)lp);
-}
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// Row of the original (B, T, H, D) tensors for an index entry: pads (and any
-// entry outside [0, T)) read token 0, whose values are finite.
-__device__ inline int src_row(int pos, int T) { return (pos >= 0 && pos < T) ? pos : 0; }
-
-// 16-byte chunk of row r of a staged V tile that holds chunk c: swizzled so
-// that the transposed operand reads (4 rows x 32 bytes per 16 lanes) use all
-// banks.
-__device__ inline int swz_v(int r, int c) { return c ^ (2 * (r & 3)); }
 
 // S^T += K Q^T for one staged key tile: 2 x 4 x 2 MFMAs over the two
 // 32-wide halves of D. K rows are read permuted (key_row) so that each
@@ -373,8 +230,7 @@ __device__ __forceinline__ void scores_bf16(f32x4 (&S)[4][2], const uint8_t* Ks,
   for (int ds = 0; ds < 2; ++ds)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const int row = key_row(kb, r16);
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[row * HD * 2 + (((ds * 4 + g) ^ swz_k(row)) * 16)]);
+      const bf16x8 a = read_row_op(Ks, kb, r16, ds * 4 + g);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
         S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Qb[qb][ds], S[kb][qb], 0, 0, 0);
@@ -574,23 +430,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       }
 
       // -- O^T += V^T P^T; row sums of the rounded weights ---------------------
-      // V^T operand of (db, kc): dims 16db + r16, keys 32kc + 8g + 0..7, as
-      // two transposed reads of 4 keys; source lane r16 of group g reads
-      // 4 dims of key 32kc + 8g + 4hh + r16 / 4.
+      // V^T operand of (db, kc): dims 16db + r16, keys 32kc + 8g + 0..7.
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-          v4i16 t[2];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int r = 32 * kc + 8 * g + 4 * hh + (r16 >> 2);
-            const int col = 16 * db + 4 * (r16 & 3);  // first of the 4 dims
-            const uint8_t* src = Vs + r * 128 + swz_v(r, col >> 3) * 16 + (col & 7) * 2;
-            t[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16*)(__attribute__((address_space(3))) void*)src);
-          }
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          const bf16x8 a = read_tr_op(Vs, db, kc, g, r16);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
             Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, P[qb][kc], Oacc[db][qb], 0, 0, 0);

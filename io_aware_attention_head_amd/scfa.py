@@ -268,11 +268,14 @@ def scfa_bwd_workspace_bytes(mode, B, H, Tq, Tk, D=64) -> int:
     return lib().scfa_bwd_workspace_bytes(mode, B, H, Tq, Tk, D)
 
 
-def scfa_bwd(mode, q, k, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, T, Tq, Tk, dQ,
+def scfa_bwd(mode, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, T, Tq, Tk, dQ,
              dK, dV, workspace, scale=None, stream=None):
-    B, H, Tp, D = q.shape
+    """q, k, v, dO: original (B,T,H,D) bf16 tensors (read through the index arrays)."""
+    B, Tq_, H, D = q.shape
+    if Tq_ != T:
+        raise ScfaError("q must be the original (B,T,H,D) tensor")
     scale = 1.0 / math.sqrt(D) if scale is None else scale
-    _check(lib().scfa_bwd(mode, _dt(q), _p(q), _p(k), _p(v_t), _p(q_idx), _p(k_idx), _p(q_bkt), _p(k_bkt), _p(qstats),
+    _check(lib().scfa_bwd(mode, _dt(q), _p(q), _p(k), _p(v), _p(q_idx), _p(k_idx), _p(q_bkt), _p(k_bkt), _p(qstats),
                           _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(O), _p(lse), _p(dO), B, H, T, Tq, Tk, D, scale,
                           _p(dQ), _p(dK), _p(dV), _p(workspace), workspace.numel() * workspace.element_size(),
                           _stream(stream, q)), "scfa_bwd")
@@ -286,9 +289,10 @@ def scfa_bwd(mode, q, k, v_t, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_ta
 class Prepared:
     """Index arrays of one attention call (head-major) and its operands.
 
-    The forward reads q_in, k_in, v_in (original (B,T,H,D) order) through
-    q_idx / k_idx. The backward reads gathered head-major copies q, k (rows)
-    and v_t (transposed), which gather_operands() fills on first use.
+    Forward and backward read q_in, k_in, v_in (original (B,T,H,D) order)
+    through q_idx / k_idx. Head-major copies q, k (rows) and v_t
+    (transposed) exist only on request (gather_operands(), or the compacted
+    rows of prepare_qk(rows=True)).
     Tq, Tk are the query / key rows as passed to the range table; the index
     arrays hold pad_rows(Tq) / pad_rows(Tk) rows per head."""
     mode: str
@@ -312,8 +316,8 @@ class Prepared:
 
 
 def gather_operands(pre: Prepared, stream=None) -> Prepared:
-    """Head-major copies of the operands in index order (pad rows zero), as
-    the backward kernels read them; a no-op for the ones already present."""
+    """Head-major copies of the operands in index order (pad rows zero); a
+    no-op for the ones already present."""
     B, H, D = pre.B, pre.H, pre.D
     TqP, TkP = pad_rows(pre.Tq), pad_rows(pre.Tk)
     if pre.q is None:
@@ -463,17 +467,16 @@ def forward(pre: Prepared, tab: Tables, out_dtype=torch.float32, scale=None, O=N
 
 
 def backward(pre: Prepared, tab: Tables, O, lse, dO, scale=None, grads=None, workspace=None, stream=None):
-    """Gradients w.r.t. the original-order q, k, v (fp32, (B,T,H,D)). Gathers
-    the head-major operands first if they are not there yet."""
+    """Gradients w.r.t. the original-order q, k, v (fp32, (B,T,H,D)); the
+    backward kernels read q, k, v and dO through the index arrays."""
     B, H, T, D = pre.B, pre.H, pre.T, pre.D
     mode = _table_mode(pre.mode)
-    gather_operands(pre, stream)
     if grads is None:
-        grads = tuple(_empty((B, T, H, D), torch.float32, pre.q) for _ in range(3))
+        grads = tuple(_empty((B, T, H, D), torch.float32, pre.q_in) for _ in range(3))
     if workspace is None:
-        workspace = _empty((scfa_bwd_workspace_bytes(mode, B, H, pre.Tq, pre.Tk, D),), torch.uint8, pre.q)
+        workspace = _empty((scfa_bwd_workspace_bytes(mode, B, H, pre.Tq, pre.Tk, D),), torch.uint8, pre.q_in)
     dQ, dK, dV = grads
-    scfa_bwd(mode, pre.q, pre.k, pre.v_t, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats, tab.fwd,
+    scfa_bwd(mode, pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats, tab.fwd,
              tab.bwd, O, lse, dO, T, pre.Tq, pre.Tk, dQ, dK, dV, workspace, scale, stream)
     return dQ, dK, dV
 
@@ -506,9 +509,9 @@ class Plan:
                  fixed compacted length Tc (default: pad_rows(T), which always
                  fits).
     mode "dense": tables -> forward on positions 0..T-1.
-    The forward gathers on load; backward() first gathers head-major copies
-    (gather stage). Each stage is a separate method so it can be timed on its
-    own.
+    Forward and backward read the operands through the index arrays (no
+    gathered copies). Each stage is a separate method so it can be timed on
+    its own.
     """
 
     def __init__(self, mode, B, H, T, D=64, dtype=torch.bfloat16, nb=16, Tc=None, out_dtype=torch.float32,
@@ -536,7 +539,6 @@ class Plan:
         else:
             self.Tq = self.Tk = pad_rows(T)
         TqP, TkP = pad_rows(self.Tq), pad_rows(self.Tk)
-        self.q_s = self.k_s = self.v_t = None  # gathered copies, allocated by gather()
         self.x = None  # operands of the last prepare()
         self.device = d
         self.q_idx, self.k_idx = e((B, H, TqP)), e((B, H, TkP))
@@ -586,17 +588,6 @@ class Plan:
         scfa_qk_compact(k, keep_k, self.cnt[1], self.choff[1], self.Tk, SCFA_K_PAD, None, self.k_idx,
                         self.dev_err, stream)
 
-    def gather(self, q, k, v, stream=None):
-        """Head-major copies in index order, for the backward."""
-        if self.q_s is None:
-            B, H, D = self.B, self.H, self.D
-            TqP, TkP = pad_rows(self.Tq), pad_rows(self.Tk)
-            e = lambda shape: torch.empty(shape, dtype=self.dtype, device=self.device)  # noqa: E731
-            self.q_s, self.k_s, self.v_t = e((B, H, TqP, D)), e((B, H, TkP, D)), e((B, H, D, TkP))
-        scfa_gather(q, self.q_idx, SCFA_ROWS, self.q_s, stream)
-        scfa_gather(k, self.k_idx, SCFA_ROWS, self.k_s, stream)
-        scfa_gather(v, self.k_idx, SCFA_COLS, self.v_t, stream)
-
     def tables(self, stream=None):
         """Tile statistics, forward ranges and the launch order (the backward
         table is built by backward())."""
@@ -610,10 +601,9 @@ class Plan:
 
     def backward(self, dO, stream=None):
         """Gradients of the last forward() w.r.t. q, k, v (fp32, original order):
-        gathers, then the backward kernels."""
+        the backward table, then the backward kernels."""
         if self.x is None:
             raise ScfaError("backward needs a prepared forward")
-        self.gather(self.x["q"], self.x["k"], self.x["v"], stream)
         scfa_bwd_table(self.tab.qstats, self.tab.kstats, self.tab.fwd, self.tab.bwd, stream)
         if self._grads is None:
             d = self.device
@@ -665,4 +655,4 @@ class Plan:
             raise ScfaError("call prepare() first")
         x = self.x
         return Prepared(self.mode, self.B, self.H, self.T, self.D, self.Tq, self.Tk, x["q"], x["k"], x["v"],
-                        self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.q_s, self.k_s, self.v_t)
+                        self.q_idx, self.k_idx, self.q_bkt, self.k_bkt)
