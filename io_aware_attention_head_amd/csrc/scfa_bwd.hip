@@ -16,8 +16,8 @@
 // MI355X design:
 //  * Three kernels, no atomics (deterministic): a preparation kernel (Delta
 //    and log2 LSE per sorted query row), dK/dV per 64-key tile (4 waves x 16
-//    keys, query chunks of 64), dQ per 128-query tile (4 waves x 32 queries,
-//    key tiles of 64).
+//    keys, query chunks of 32: 38 KB of LDS and 108 VGPRs, 4 waves per SIMD),
+//    dQ per 128-query tile (4 waves x 32 queries, key tiles of 64).
 //  * Operands are read from the original (B, T, H, D) tensors through the
 //    index arrays (gather fused into the loads, as in the forward): each
 //    lane's own rows straight into registers, the shared tiles by
@@ -46,7 +46,7 @@ namespace {
 
 constexpr int BM = SCFA_TILE_M;  // 128: dQ workgroup rows, table granularity
 constexpr int BN = SCFA_TILE_N;  // 64: dK/dV workgroup keys, table granularity
-constexpr int QC = 64;           // query chunk of the dK/dV loop
+constexpr int QC = 32;          // query chunk of the dK/dV loop
 constexpr int HD = 64;
 constexpr int TB = 64 * HD * 2;  // bytes of one 64 x 64 bf16 tile
 constexpr int kStatCap = 256;    // tile statistics of a range held in LDS
@@ -227,14 +227,15 @@ __device__ inline WaveKeys wave_keys(int kpos, int kbkt, int T) {
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per 64-key tile; wave w owns keys 16w .. 16w+15
 // (its K and V rows in registers, one key per lane column). Query chunks of
-// 64 rows are staged by DMA: Q and dO each in the row layout (A operands of
+// 32 rows are staged by DMA: Q and dO each in the row layout (A operands of
 // S = Q K^T and dP = dO V^T) and in the transposed-read layout (A operands of
 // dK^T += Q^T dS and dV^T += dO^T P), with their positions, buckets, log2
 // LSE and Delta.
 // ---------------------------------------------------------------------------
 template <bool HASH, bool ZD>
 __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
-  __shared__ __align__(16) uint8_t smem[2 * 4 * TB];  // 2 stages x (Q rows, Q tr, dO rows, dO tr); epilogue staging
+  constexpr int CB = QC * 128;  // bytes of one staged chunk copy (QC rows)
+  __shared__ __align__(16) uint8_t smem[2 * BN * HD * 4];  // 2 stages x 4 chunk copies; epilogue staging (32 KB)
   __shared__ __align__(16) int32_t qpos_s[2][QC];
   __shared__ __align__(16) int32_t qbkt_s[2][QC];
   __shared__ __align__(16) float lse_s[2][QC];
@@ -282,15 +283,14 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
     dKa[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- DMA staging of a query chunk: wave w stages rows 16w .. 16w+15 ------
+  // ---- DMA staging of a query chunk: wave w stages rows 8w .. 8w+7 --------
   const uint8_t* qg = static_cast<const uint8_t*>(p.q) + head0;
   const uint8_t* dg = static_cast<const uint8_t*>(p.dO) + head0;
-  uint32_t rch[2], tch[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 16 * w + 8 * i + (lane >> 3), cp = lane & 7;
-    rch[i] = (cp ^ swz_k(row)) * 16;  // row layout
-    tch[i] = swz_v(row, cp) * 16;     // transposed-read layout
+  uint32_t rch, tch;
+  {
+    const int row = 8 * w + (lane >> 3), cp = lane & 7;
+    rch = (cp ^ swz_k(row)) * 16;  // row layout
+    tch = swz_v(row, cp) * 16;     // transposed-read layout
   }
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t lds_small = ws == 0 ? lds_addr(&qpos_s[0][0])
@@ -301,32 +301,30 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
                           : ws == 1 ? static_cast<const void*>(HASH ? p.q_bkt + rowbase : p.q_idx + rowbase)
                           : ws == 2 ? static_cast<const void*>(p.lse2 + rowbase)
                                     : static_cast<const void*>(p.delta + rowbase);
-  const int nch = 2 * p.nQt;
-  auto chunk_rows = [&](int ci, int (&pos)[2]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) pos[i] = p.q_idx[rowbase + min(ci, nch - 1) * QC + 16 * w + 8 * i + (lane >> 3)];
+  constexpr int CPT = BM / QC;  // chunks per query tile
+  const int nch = CPT * p.nQt;
+  auto chunk_rows = [&](int ci, int (&pos)[2]) {  // pos[0]: the row this lane stages
+    pos[0] = p.q_idx[rowbase + min(ci, nch - 1) * QC + 8 * w + (lane >> 3)];
+    pos[1] = 0;
   };
   auto stage = [&](int ci, int s, const int (&pos)[2]) {
-    const uint32_t base = lds0 + s * 4 * TB + ws * 2048;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t off = static_cast<uint32_t>(src_row(pos[i], p.T)) * rstride;
-      dma16(qg, off + rch[i], base + i * 1024);
-      dma16(qg, off + tch[i], base + TB + i * 1024);
-      dma16(dg, off + rch[i], base + 2 * TB + i * 1024);
-      dma16(dg, off + tch[i], base + 3 * TB + i * 1024);
-    }
-    dma4(static_cast<const uint8_t*>(small_src) + ci * QC * 4, lane * 4, lds_small + s * QC * 4);
+    const uint32_t base = lds0 + s * 4 * CB + ws * 1024;
+    const uint32_t off = static_cast<uint32_t>(src_row(pos[0], p.T)) * rstride;
+    dma16(qg, off + rch, base);
+    dma16(qg, off + tch, base + CB);
+    dma16(dg, off + rch, base + 2 * CB);
+    dma16(dg, off + tch, base + 3 * CB);
+    if (lane < QC) dma4(static_cast<const uint8_t*>(small_src) + ci * QC * 4, lane * 4, lds_small + s * QC * 4);
   };
-  // chunk ci = 2 * query tile + half; skip tiles failing the causal test
+  // chunk ci = CPT * query tile + part; skip tiles failing the causal test
   const int4 ks = p.kstats[static_cast<size_t>(bh) * p.nKt + kt];
-  const int cend = 2 * rng.y;
+  const int cend = CPT * rng.y;
   auto next_chunk = [&](int ci) {
-    while (ci < cend && qstat(ci >> 1).y < ks.x) ci = (ci | 1) + 1;
+    while (ci < cend && qstat(ci / CPT).y < ks.x) ci = (ci / CPT + 1) * CPT;
     return ci;
   };
 
-  int ci = next_chunk(2 * rng.x);
+  int ci = next_chunk(CPT * rng.x);
   int cn = ci < cend ? next_chunk(ci + 1) : cend;
   int pos[2];
   if (ci < cend) {
@@ -337,11 +335,11 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
   dma_wait();
   __syncthreads();
   int s = 0;
-  int4 qs_cur = ci < cend ? qstat(ci >> 1) : make_int4(0, 0, 0, 0);
+  int4 qs_cur = ci < cend ? qstat(ci / CPT) : make_int4(0, 0, 0, 0);
   while (ci < cend) {
     const int cnn = cn < cend ? next_chunk(cn + 1) : cend;
     const int4 qs = qs_cur;
-    if (cn < cend) qs_cur = qstat(cn >> 1);
+    if (cn < cend) qs_cur = qstat(cn / CPT);
     int pos_nn[2];
     chunk_rows(cnn, pos_nn);  // issued before the DMA: waiting for it never waits for the DMA
     __builtin_amdgcn_sched_barrier(0);
@@ -350,24 +348,24 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
     // this wave's keys against the chunk's query tile: skip / no mask
     const bool empty = !wk.any || wk.minpos > qs.y || (HASH && (wk.minb > qs.w || wk.maxb < qs.z));
     if (!empty) {
-      const uint8_t* Qr = smem + s * 4 * TB;
-      const uint8_t* Qt = Qr + TB;
-      const uint8_t* Dr = Qr + 2 * TB;
-      const uint8_t* Dt = Qr + 3 * TB;
-      bool full = wk.all && wk.maxpos <= qs.x && ((ci >> 1) + 1) * BM <= p.Tq;
+      const uint8_t* Qr = smem + s * 4 * CB;
+      const uint8_t* Qt = Qr + CB;
+      const uint8_t* Dr = Qr + 2 * CB;
+      const uint8_t* Dt = Qr + 3 * CB;
+      bool full = wk.all && wk.maxpos <= qs.x && (ci / CPT + 1) * BM <= p.Tq;
       if (HASH) full = full && qs.z == qs.w && wk.minb == wk.maxb && wk.minb == qs.z;
       // S = Q K^T (from the mask bias) and dP = dO V^T: rows = queries,
       // column = this lane's key; element e of block qb is query
-      // 32 (qb >> 1) + 8 g + 4 (qb & 1) + e of the chunk
-      f32x4 S[4], dP[4];
+      // 8 g + 4 qb + e of the chunk
+      f32x4 S[2], dP[2];
       if (full) {
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) S[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < 2; ++qb) S[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
       } else {
         const bool buckets = HASH && !(qs.z == qs.w && wk.minb == wk.maxb);
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          const int qo = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);
+        for (int qb = 0; qb < 2; ++qb) {
+          const int qo = 8 * g + 4 * qb;
           const int4 qp4 = *reinterpret_cast<const int4*>(&qpos_s[s][qo]);
           f32x4 c;
           c[0] = bias_if_ge(qp4.x, kpos);
@@ -385,18 +383,18 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
         }
       }
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) dP[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < 2; ++qb) dP[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ds = 0; ds < 2; ++ds)
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
+        for (int qb = 0; qb < 2; ++qb) {
           S[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_row_op(Qr, qb, r16, ds * 4 + g), Kb[ds], S[qb], 0, 0, 0);
           dP[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_row_op(Dr, qb, r16, ds * 4 + g), Vb[ds], dP[qb], 0, 0, 0);
         }
       // P = exp2(S c - lse2), dS = P (dP - Delta)
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const int qo = 32 * (qb >> 1) + 8 * g + 4 * (qb & 1);
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qo = 8 * g + 4 * qb;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[s][qo]);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&del_s[s][qo]);
 #pragma unroll
@@ -406,20 +404,14 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
           dP[qb][e] = pe * (dP[qb][e] - d4[e]);
         }
       }
-      bf16x8 Pp[2], Sp[2];
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        Pp[kc] = pack_bf16x8(S[2 * kc], S[2 * kc + 1]);
-        Sp[kc] = pack_bf16x8(dP[2 * kc], dP[2 * kc + 1]);
-      }
+      const bf16x8 Pp = pack_bf16x8(S[0], S[1]);
+      const bf16x8 Sp = pack_bf16x8(dP[0], dP[1]);
       // dV^T += dO^T P,  dK^T += Q^T dS  (rows = dims, column = this lane's key)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          dVa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_tr_op(Dt, db, kc, g, r16), Pp[kc], dVa[db], 0, 0, 0);
-          dKa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_tr_op(Qt, db, kc, g, r16), Sp[kc], dKa[db], 0, 0, 0);
-        }
+      for (int db = 0; db < 4; ++db) {
+        dVa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_tr_op(Dt, db, 0, g, r16), Pp, dVa[db], 0, 0, 0);
+        dKa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_tr_op(Qt, db, 0, g, r16), Sp, dKa[db], 0, 0, 0);
+      }
     }
 
     dma_wait();
