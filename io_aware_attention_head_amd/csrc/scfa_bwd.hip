@@ -556,54 +556,57 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
       const uint8_t* Kr = smem + s * 3 * TB;
       const uint8_t* Kt = Kr + TB;
       const uint8_t* Vr = Kr + 2 * TB;
-      // S^T = K Q^T (from the mask bias) and dP^T = V dO^T: rows = keys,
-      // column = this lane's query
-      f32x4 S[4][2], dP[4][2];
-      if (tile_full_for<HASH>(ks, wr, j, p.Tk)) {
+      const bool full = tile_full_for<HASH>(ks, wr, j, p.Tk);
+      // Two halves of 32 keys (blocks 2 kc, 2 kc + 1), so that only half of
+      // the score tiles is live at a time. S^T = K Q^T (from the mask bias)
+      // and dP^T = V dO^T: rows = keys, column = this lane's query.
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+      for (int kc = 0; kc < 2; ++kc) {
+        f32x4 S[2][2], dP[2][2];
+        if (full) {
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      } else {
-        mask_bias<HASH>(S, ks, wr, Kp[s], Kb[s], qpos, qbkt, g);
-      }
+          for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) dP[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < 2; ++ds)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const bf16x8 ak = read_row_op(Kr, kb, r16, ds * 4 + g);
-          const bf16x8 av = read_row_op(Vr, kb, r16, ds * 4 + g);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, Qb[qb][ds], S[kb][qb], 0, 0, 0);
-            dP[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Db[qb][ds], dP[kb][qb], 0, 0, 0);
-          }
+            for (int qb = 0; qb < 2; ++qb) S[h2][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+          mask_bias_half<HASH>(S, ks, wr, Kp[s], Kb[s], qpos, qbkt, g, kc);
         }
-      // dS^T = P^T (dP^T - Delta), P^T = exp2(S^T c - lse2)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+          for (int qb = 0; qb < 2; ++qb) dP[h2][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float pe = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][e], p.c, -ql2[qb]));
-            dP[kb][qb][e] = pe * (dP[kb][qb][e] - qdl[qb]);
+        for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const bf16x8 ak = read_row_op(Kr, 2 * kc + h2, r16, ds * 4 + g);
+            const bf16x8 av = read_row_op(Vr, 2 * kc + h2, r16, ds * 4 + g);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              S[h2][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, Qb[qb][ds], S[h2][qb], 0, 0, 0);
+              dP[h2][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Db[qb][ds], dP[h2][qb], 0, 0, 0);
+            }
           }
-      // dQ^T += K^T dS^T (rows = dims, column = this lane's query)
+        // dS^T = P^T (dP^T - Delta), P^T = exp2(S^T c - lse2)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const bf16x8 sp = pack_bf16x8(dP[2 * kc][qb], dP[2 * kc + 1][qb]);
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float pe = __builtin_amdgcn_exp2f(fmaf(S[h2][qb][e], p.c, -ql2[qb]));
+              dP[h2][qb][e] = pe * (dP[h2][qb][e] - qdl[qb]);
+            }
+        // dQ^T += K^T dS^T (rows = dims, column = this lane's query)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const bf16x8 sp = pack_bf16x8(dP[0][qb], dP[1][qb]);
 #pragma unroll
           for (int db = 0; db < 4; ++db)
             dQa[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_tr_op(Kt, db, kc, g, r16), sp, dQa[db][qb], 0,
                                                                  0, 0);
         }
+      }
     }
 
     dma_wait();

@@ -171,6 +171,37 @@ __device__ inline void bias_tile(f32x4 (&C)[4][2], const int32_t* kp, const int3
   }
 }
 
+// The same bias for the 32 keys 32 kc .. 32 kc + 31 of the tile (blocks
+// 2 kc and 2 kc + 1 as C[0], C[1]).
+template <bool HASH>
+__device__ inline void mask_bias_half(f32x4 (&C)[2][2], const int4& ks, const WaveRows& wr, const int32_t* kp,
+                                      const int32_t* kbk, const int (&qpos)[2], const int (&qbkt)[2], int g, int kc) {
+  const bool buckets = HASH && !(ks.z == ks.w && wr.minb == wr.maxb);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int kbase = 32 * kc + 8 * g + 4 * h2;
+    const int4 kp4 = *reinterpret_cast<const int4*>(&kp[kbase]);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qp = qpos[qb];
+      f32x4 c;
+      c[0] = bias_if_ge(qp, kp4.x);
+      c[1] = bias_if_ge(qp, kp4.y);
+      c[2] = bias_if_ge(qp, kp4.z);
+      c[3] = bias_if_ge(qp, kp4.w);
+      if (buckets) {
+        const int4 kb4 = *reinterpret_cast<const int4*>(&kbk[kbase]);
+        const int qh = qbkt[qb];
+        c[0] = keep_if_eq(c[0], qh, kb4.x);
+        c[1] = keep_if_eq(c[1], qh, kb4.y);
+        c[2] = keep_if_eq(c[2], qh, kb4.z);
+        c[3] = keep_if_eq(c[3], qh, kb4.w);
+      }
+      C[h2][qb] = c;
+    }
+  }
+}
+
 // Mask bias of a tile that is not fully visible: positions only when the
 // tile's keys and the wave's real queries share one bucket (always so in QK
 // mode and in the bucket-aligned layout), positions and buckets otherwise.
