@@ -37,9 +37,7 @@
 //    registers one tile ahead, so DMA addresses never wait on a load.
 //  * The reference max moves only when a row's tile max exceeds it by more
 //    than 2^8 (lazy rescaling): probabilities stay <= 256 and the O rescale
-//    is rare. O is normalised by the sum of the bf16-rounded probabilities
-//    (an MFMA against a ones operand, consistent with the P V product); the
-//    LSE uses the fp32 row sum.
+//    is rare. O and the LSE use the fp32 row sum of the probabilities.
 //  * Per-wave tile tests from the extrema: a key tile holding no pair visible
 //    to any of the wave's 32 queries is skipped by that wave, and one whose
 //    pairs are all visible skips the mask.
@@ -301,11 +299,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) Oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};  // fp32 row sums (per lane: its 16 keys of each tile), for the LSE
-  f32x4 Lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};  // sums of the bf16 weights
-  bf16x8 ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = static_cast<__bf16>(1.0f);
+  float l[2] = {0.f, 0.f};  // fp32 row sums (per lane: its 16 keys of each tile)
 
   // ---- DMA staging of a key tile -----------------------------------------
   // Wave w stages rows 16w .. 16w+15 of the K and V tiles, 8 rows (1 KB) per
@@ -407,7 +401,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
           m[qb] = mnew;
 #pragma unroll
           for (int db = 0; db < 4; ++db) Oacc[db][qb] *= alpha;
-          Lacc[qb] *= alpha;
           l[qb] *= alpha;
         }
       }
@@ -429,7 +422,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         for (int kc = 0; kc < 2; ++kc) P[qb][kc] = pack_bf16x8(S[2 * kc][qb], S[2 * kc + 1][qb]);
       }
 
-      // -- O^T += V^T P^T; row sums of the rounded weights ---------------------
+      // -- O^T += V^T P^T ------------------------------------------------------
       // V^T operand of (db, kc): dims 16db + r16, keys 32kc + 8g + 0..7.
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -440,11 +433,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
           for (int qb = 0; qb < 2; ++qb)
             Oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, P[qb][kc], Oacc[db][qb], 0, 0, 0);
         }
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          Lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, P[qb][kc], Lacc[qb], 0, 0, 0);
     }
 
     dma_wait();
@@ -462,8 +450,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   for (int qb = 0; qb < 2; ++qb) {
     float lt = l[qb] + __shfl_xor(l[qb], 16);
     lt = lt + __shfl_xor(lt, 32);
-    const float lo = Lacc[qb][0];  // every row of the ones product holds the full sum
-    inv[qb] = lo > 0.f ? 1.f / lo : 0.f;
+    inv[qb] = lt > 0.f ? 1.f / lt : 0.f;
     const float muse = (m[qb] == -INFINITY) ? 0.f : m[qb];
     lse[qb] = lt > 0.f ? (muse + log2f(lt)) * kLn2 : -INFINITY;
   }
