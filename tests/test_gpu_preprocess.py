@@ -217,6 +217,54 @@ def test_tables_more_than_512_tiles(mode, T):
     assert ref["tiles"].sum() > 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_hash_bucket_near_ties(dtype):
+    """LSH buckets on inputs built to sit at or near ties, bit-exact against
+    the float64 definition: rotations with two equal columns (exact ties
+    between buckets 0 and 1 for every token), a column equal to minus another
+    (ties between a positive and a negative candidate), tokens whose two
+    largest projections differ by rounding only, and all-zero tokens (every
+    candidate equal). These are the tokens the float32 pass must hand to the
+    float64 one."""
+    need_gpu()
+    announce(f"hash bucket near ties {dtype}")
+    rng = np.random.default_rng(91)
+    B, T, H, D, nb = 1, 3000, 2, 64, 16
+    half = nb // 2
+    R = rng.standard_normal((H, D, half)).astype(np.float32)
+    R[0, :, 1] = R[0, :, 0]   # c_1 == c_0 exactly
+    R[1, :, 3] = -R[1, :, 2]  # -c_3 == c_2 exactly
+    x = rng.standard_normal((B, T, H, D))
+    for h in range(H):
+        for t in range(0, T, 3):  # every third token: two columns nearly tied as the largest
+            j1, j2 = rng.choice(half, 2, replace=False)
+            u = R[h, :, j1].astype(np.float64) - R[h, :, j2]
+            v = R[h, :, j1].astype(np.float64) + R[h, :, j2] + 0.1 * rng.standard_normal(D)
+            x[0, t, h] = v - (v @ u) / (u @ u) * u
+        x[0, 7::97, h] = 0.0  # all-zero tokens
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xt = torch.from_numpy(x.astype(np.float32)).to(tdt)
+    x64 = xt.double().numpy()
+    ref = oracle.hash_bucket(x64, R.astype(np.float64), nb)
+    d = torch.device("cuda:0")
+    got = torch.empty((B, H, T), dtype=torch.int32, device=d)
+    cnt = torch.empty(scfa.chunk_count_shape(B, H, T, nb), dtype=torch.int32, device=d)
+    scfa.scfa_hash_bucket_counts(xt.to(d), torch.from_numpy(R).to(d), nb, got, cnt)
+    got2 = torch.empty_like(got)
+    scfa.scfa_hash_bucket(xt.to(d), torch.from_numpy(R).to(d), nb, got2)
+    torch.cuda.synchronize()
+    g = got.cpu().numpy()
+    assert np.array_equal(g, ref), f"{int((g != ref).sum())} buckets differ"
+    assert torch.equal(got, got2)
+    assert np.array_equal(cnt.cpu().numpy(), chunk_counts_np(ref, nb))
+    # exact ties go to the first candidate: head 0 never picks 1 or 9 (tied
+    # with 0 and 8), head 1 never 10 or 11 (tied with 3 and 2); zero tokens
+    # pick 0
+    assert not np.isin(ref[0, 0], [1, half + 1]).any()
+    assert not np.isin(ref[0, 1], [half + 2, half + 3]).any()
+    assert (ref[:, :, 7::97] == 0).all()
+
+
 def chunk_counts_np(b_np, nb):
     """Tokens of each bucket among positions [256 c, 256 c + 256) of each head."""
     B, H, T = b_np.shape
