@@ -9,10 +9,13 @@
 //     counting sort by bucket, gather into the sorted order.
 //   * Tile extrema and the per-query-tile / per-key-tile range tables of
 //     Algorithms 1 and 2 and of the backward pass.
-// All of these are HBM-bandwidth or latency bound: they use 16-byte
-// coalesced accesses, wave64 ballots for the prefix sums, and no MFMA.
+// The LSH projection is bound by its float64 FMAs; the rest is HBM-bandwidth
+// or latency bound: 16-byte coalesced accesses, wave64 ballots for the
+// prefix sums, and no MFMA.
 
 #include <limits.h>
+
+#include <utility>
 
 #include "scfa_internal.h"
 
@@ -139,12 +142,14 @@ __global__ __launch_bounds__(256) void k_qk_compact(const uint8_t* __restrict__ 
 // LSH bucket. One workgroup per (256 tokens, head), one wave per 64 tokens.
 // A wave first copies its 64 rows into LDS with coalesced 16-byte loads
 // (consecutive lanes read consecutive 16 bytes of a row), then each lane
-// accumulates its own token's projections; R of the head sits in LDS as
-// float64 and is read as a wave-wide broadcast. A product of a bf16/fp32
-// input and an fp32 rotation is exact in float64, so a fused multiply-add
-// rounds exactly where a separate multiply and add would (only at the sum):
-// the accumulation matches the sequential definition
-// c_j = ((0 + x_0 R_0j) + x_1 R_1j) + ... bit for bit.
+// accumulates its own token's projections. R of the head reaches the
+// float64 FMA either from LDS as a wave-wide broadcast (k_hash_bucket) or,
+// up to nb = 32, from registers by a DPP row broadcast (k_hash_bucket_dpp,
+// which frees the kernel of the LDS reads that otherwise bound it). A
+// product of a bf16/fp32 input and an fp32 rotation is exact in float64, so
+// a fused multiply-add rounds exactly where a separate multiply and add
+// would (only at the sum): the accumulation matches the sequential
+// definition c_j = ((0 + x_0 R_0j) + x_1 R_1j) + ... bit for bit.
 // ---------------------------------------------------------------------------
 
 template <typename TIN>
@@ -217,6 +222,111 @@ __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* __restrict__ x, 
     if (threadIdx.x < 2 * HALF)
       counts[(static_cast<size_t>(bh) * gridDim.x + blockIdx.x) * (2 * HALF) + threadIdx.x] = hs[threadIdx.x];
   }
+}
+
+// acc += (lane K of this lane's 16-lane row of r) * x, in float64, with the
+// operand broadcast by DPP inside the FMA (row_newbcast).
+template <int K>
+__device__ __forceinline__ void fma_row_bcast(double& acc, double r, double x) {
+  asm("v_fmac_f64_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(r), "v"(x), "n"(K));
+}
+
+template <int HALF, int Q>
+__device__ __forceinline__ void fma_rq(double& acc, const double* Rv, double x) {
+  fma_row_bcast<Q % 16>(acc, Rv[Q / 16], x);
+}
+
+template <int HALF, int D0, int... J>
+__device__ __forceinline__ void fma_row_d(double* c, const double* Rv, double x, std::integer_sequence<int, J...>) {
+  (fma_rq<HALF, D0 * HALF + J>(c[J], Rv, x), ...);
+}
+
+template <typename TIN, int HALF, int I, int... E>
+__device__ __forceinline__ void fma_unit(double* c, const double* Rv, const u32x4 u, std::integer_sequence<int, E...>) {
+  constexpr int EPU = 16 / sizeof(TIN);
+  (fma_row_d<HALF, I * EPU + E>(c, Rv, static_cast<double>(unit_elem<TIN>(u, E)),
+                                std::make_integer_sequence<int, HALF>{}),
+   ...);
+}
+
+template <typename TIN, int HALF, int... I>
+__device__ __forceinline__ void fma_units(double* c, const double* Rv, const uint32_t* xr,
+                                          std::integer_sequence<int, I...>) {
+  constexpr int EPU = 16 / sizeof(TIN);
+  (fma_unit<TIN, HALF, I>(c, Rv, *reinterpret_cast<const u32x4*>(xr + I * 4), std::make_integer_sequence<int, EPU>{}),
+   ...);
+}
+
+// Same projection and argmax as k_hash_bucket, with the rotation held in
+// registers: flat entry q = d * HALF + j of the head's R sits in register
+// pair q / 16 of lane q % 16 of every 16-lane row, and reaches the FMA by a
+// row broadcast, so the inner loop is FMAs only. The accumulation order
+// (d = 0, 1, ..., 63 for each j, one rounding per FMA) is the same.
+template <typename TIN, int HALF>
+__global__ __launch_bounds__(256) void k_hash_bucket_dpp(const TIN* __restrict__ x, const float* __restrict__ R, int T,
+                                                         int H, int32_t* __restrict__ bucket,
+                                                         int32_t* __restrict__ counts) {
+  constexpr int D = 64;
+  constexpr int EPU = 16 / sizeof(TIN);
+  constexpr int NU = D / EPU;
+  constexpr int RPI = 64 / NU;
+  constexpr int LDW = NU * 4 + 4;
+  constexpr int NR = D * HALF / 16;  // register pairs holding R
+  __shared__ __align__(16) uint32_t xs[4][64 * LDW];
+  __shared__ int32_t hs[2 * HALF];
+  const int bh = blockIdx.y;
+  if (counts && threadIdx.x < 2 * HALF) hs[threadIdx.x] = 0;
+  const int b = bh / H, h = bh - b * H;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const float* Rh = R + static_cast<size_t>(h) * D * HALF;
+  double Rv[NR];
+#pragma unroll
+  for (int q = 0; q < NR; ++q) Rv[q] = static_cast<double>(Rh[16 * q + (lane & 15)]);
+  const int tw = blockIdx.x * 256 + w * 64;
+#pragma unroll
+  for (int k = 0; k < 64 / RPI; ++k) {
+    const int row = k * RPI + lane / NU, unit = lane % NU;
+    const int t = min(tw + row, T - 1);
+    const u32x4 v = reinterpret_cast<const u32x4*>(x + ((static_cast<size_t>(b) * T + t) * H + h) * D)[unit];
+    *reinterpret_cast<u32x4*>(&xs[w][row * LDW + unit * 4]) = v;
+  }
+  // A DPP source must be written at least two wait states before it is
+  // read; the asm (one per register pair) keeps the writes above the barrier.
+#pragma unroll
+  for (int q = 0; q < NR; ++q) asm volatile("s_nop 1" : "+v"(Rv[q]));
+  __syncthreads();
+  double c[HALF];
+#pragma unroll
+  for (int j = 0; j < HALF; ++j) c[j] = 0.0;
+  const uint32_t* xr = &xs[w][lane * LDW];
+  fma_units<TIN, HALF>(c, Rv, xr, std::make_integer_sequence<int, NU>{});
+  const int t = tw + lane;
+  int bp = 0, bn = 0;
+  double vp = c[0], vn = -c[0];
+#pragma unroll
+  for (int j = 1; j < HALF; ++j) {
+    if (c[j] > vp) { vp = c[j]; bp = j; }
+    if (-c[j] > vn) { vn = -c[j]; bn = j; }
+  }
+  const int v = (vn > vp) ? HALF + bn : bp;
+  if (t < T) bucket[static_cast<size_t>(bh) * T + t] = v;
+  if (counts) {
+    if (t < T) atomicAdd(&hs[v], 1);
+    __syncthreads();
+    if (threadIdx.x < 2 * HALF)
+      counts[(static_cast<size_t>(bh) * gridDim.x + blockIdx.x) * (2 * HALF) + threadIdx.x] = hs[threadIdx.x];
+  }
+}
+
+// Register-held rotation up to nb = 32 (at most 128 VGPRs of R); the LDS
+// broadcast kernel above it.
+template <typename TIN, int HALF>
+void bucket_launch(dim3 grid, hipStream_t stream, const TIN* x, const float* R, int T, int H, int32_t* bucket,
+                   int32_t* counts) {
+  if constexpr (HALF <= 16)
+    hipLaunchKernelGGL((k_hash_bucket_dpp<TIN, HALF>), grid, dim3(256), 0, stream, x, R, T, H, bucket, counts);
+  else
+    hipLaunchKernelGGL((k_hash_bucket<TIN, HALF>), grid, dim3(256), 0, stream, x, R, T, H, bucket, counts);
 }
 
 // ---------------------------------------------------------------------------
@@ -898,14 +1008,12 @@ static int launch_hash_bucket(int dtype, const void* x, const float* R, int B, i
   if (D != 64 || nb > 64) return SCFA_ERR_UNSUPPORTED;
   const dim3 grid(ceil_div(T, 256), B * H);
   const int half = nb / 2;
-#define SCFA_BUCKET_CASE(HALF)                                                                                  \
-  case HALF:                                                                                                    \
-    if (dtype == SCFA_BF16)                                                                                     \
-      hipLaunchKernelGGL((k_hash_bucket<uint16_t, HALF>), grid, dim3(256), 0, stream,                          \
-                         static_cast<const uint16_t*>(x), R, T, H, bucket, counts);                            \
-    else                                                                                                        \
-      hipLaunchKernelGGL((k_hash_bucket<float, HALF>), grid, dim3(256), 0, stream, static_cast<const float*>(x), \
-                         R, T, H, bucket, counts);                                                              \
+#define SCFA_BUCKET_CASE(HALF)                                                                               \
+  case HALF:                                                                                                 \
+    if (dtype == SCFA_BF16)                                                                                  \
+      bucket_launch<uint16_t, HALF>(grid, stream, static_cast<const uint16_t*>(x), R, T, H, bucket, counts); \
+    else                                                                                                     \
+      bucket_launch<float, HALF>(grid, stream, static_cast<const float*>(x), R, T, H, bucket, counts);       \
     break;
   switch (half) {
     SCFA_BUCKET_CASE(1)

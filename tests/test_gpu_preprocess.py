@@ -17,7 +17,8 @@ QK_CASES = [small("qk", 2, 3, 777, keep_p=0.6, seed=21), small("qk", 1, 2, 256, 
             small("qk", 1, 12, 2048, keep_p=0.5, seed=24)]
 HASH_CASES = [small("hash", 2, 3, 1000, nb=16, seed=31), small("hash", 1, 2, 1, nb=16, seed=32),
               small("hash", 1, 2, 333, dtype="f32", nb=8, seed=33), small("hash", 1, 4, 4096, nb=64, seed=34),
-              small("hash", 2, 2, 700, nb=2, seed=35)]
+              small("hash", 2, 2, 700, nb=2, seed=35), small("hash", 1, 2, 700, nb=32, seed=36),
+              small("hash", 1, 2, 500, dtype="f32", nb=24, seed=37), small("hash", 1, 3, 600, nb=6, seed=38)]
 
 
 def _tables_match(mode, pre, tab, Tq, Bm, Bn, q_bkt=None, k_bkt=None, Tk=None):
