@@ -137,6 +137,17 @@ int scfa_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int
 int scfa_hash_bucket_counts(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb,
                             int32_t* bucket, int32_t* chunk_counts, hipStream_t stream);
 
+/* scfa_hash_bucket_counts of the queries and of the keys in one launch (the
+ * two share R; grid dimension z selects the side): the same outputs, bit for
+ * bit, as two calls. Same definition and citation.
+ *  q, k                (B, T, H, D) of one dtype, device.
+ *  bucket_q, bucket_k  out (B, H, T) int32.
+ *  counts_q, counts_k  out chunk counts as in scfa_hash_bucket_counts.
+ * Argument errors as scfa_hash_bucket_counts (any NULL pointer: INVALID). */
+int scfa_hash_bucket_qk(int dtype, const void* q, const void* k, const float* R, int B, int T, int H, int D, int nb,
+                        int32_t* bucket_q, int32_t* bucket_k, int32_t* counts_q, int32_t* counts_k,
+                        hipStream_t stream);
+
 /* Bytes of device workspace scfa_hash_sort needs. */
 size_t scfa_hash_sort_workspace_bytes(int B, int H, int T, int nb);
 
@@ -191,6 +202,22 @@ int scfa_hash_segments(const int32_t* perm, const int32_t* offsets, int B, int H
 int scfa_hash_layout(const int32_t* bucket, const int32_t* chunk_counts, int B, int H, int T, int nb, int align,
                      int32_t pad_idx, int Tseg, int32_t* perm, int32_t* bucket_sorted, int32_t* offsets,
                      int32_t* idx_seg, int32_t* bkt_seg, int32_t* seg_offsets, int32_t* dev_err, hipStream_t stream);
+
+/* scfa_hash_layout of both sides in one launch (grid dimension z selects the
+ * side), with the attention's tiles: queries with align = SCFA_TILE_M and
+ * pad_idx = SCFA_Q_PAD into Tseg_q rows per head, keys with align =
+ * SCFA_TILE_N and pad_idx = SCFA_K_PAD into Tseg_k rows. The same outputs,
+ * bit for bit, as the two calls; the same citation.
+ *  *_q / *_k      the arguments of scfa_hash_layout for that side (every
+ *                 pointer required).
+ *  dev_err        shared by both sides (may be NULL).
+ * Argument errors as scfa_hash_layout; data errors of either side are OR-ed
+ * into dev_err. */
+int scfa_hash_layout_qk(const int32_t* bucket_q, const int32_t* bucket_k, const int32_t* counts_q,
+                        const int32_t* counts_k, int B, int H, int T, int nb, int Tseg_q, int Tseg_k, int32_t* perm_q,
+                        int32_t* perm_k, int32_t* bsorted_q, int32_t* bsorted_k, int32_t* offsets_q,
+                        int32_t* offsets_k, int32_t* idx_q, int32_t* idx_k, int32_t* bkt_q, int32_t* bkt_k,
+                        int32_t* seg_q, int32_t* seg_k, int32_t* dev_err, hipStream_t stream);
 
 /* Gather rows into head-major order: out row r of head (b, h) is
  * x[b, idx[b,h,r], h, :] when 0 <= idx < T, else zero.

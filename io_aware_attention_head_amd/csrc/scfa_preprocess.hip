@@ -167,8 +167,14 @@ __device__ inline float unit_elem<uint16_t>(const u32x4& u, int e) {
 }
 
 template <typename TIN, int HALF>
-__global__ __launch_bounds__(256) void k_hash_bucket(const TIN* __restrict__ x, const float* __restrict__ R, int T,
-                                                     int H, int32_t* __restrict__ bucket, int32_t* __restrict__ counts) {
+__global__ __launch_bounds__(256) void k_hash_bucket(const TIN* x, const TIN* x2, const float* __restrict__ R,
+                                                     int T, int H, int32_t* bucket, int32_t* bucket2, int32_t* counts,
+                                                     int32_t* counts2) {
+  if (blockIdx.z) {  // second side of a two-input launch
+    x = x2;
+    bucket = bucket2;
+    counts = counts2;
+  }
   constexpr int D = 64;
   constexpr int EPU = 16 / sizeof(TIN);  // elements per 16-byte unit
   constexpr int NU = D / EPU;            // units per row (8 bf16, 16 fp32)
@@ -263,9 +269,14 @@ __device__ __forceinline__ void fma_units(double* c, const double* Rv, const uin
 // row broadcast, so the inner loop is FMAs only. The accumulation order
 // (d = 0, 1, ..., 63 for each j, one rounding per FMA) is the same.
 template <typename TIN, int HALF>
-__global__ __launch_bounds__(256) void k_hash_bucket_dpp(const TIN* __restrict__ x, const float* __restrict__ R, int T,
-                                                         int H, int32_t* __restrict__ bucket,
-                                                         int32_t* __restrict__ counts) {
+__global__ __launch_bounds__(256) void k_hash_bucket_dpp(const TIN* x, const TIN* x2, const float* __restrict__ R,
+                                                         int T, int H, int32_t* bucket, int32_t* bucket2, int32_t* counts,
+                                                         int32_t* counts2) {
+  if (blockIdx.z) {  // second side of a two-input launch
+    x = x2;
+    bucket = bucket2;
+    counts = counts2;
+  }
   constexpr int D = 64;
   constexpr int EPU = 16 / sizeof(TIN);
   constexpr int NU = D / EPU;
@@ -321,19 +332,24 @@ __global__ __launch_bounds__(256) void k_hash_bucket_dpp(const TIN* __restrict__
 // Register-held rotation up to nb = 32 (at most 128 VGPRs of R); the LDS
 // broadcast kernel above it.
 template <typename TIN, int HALF>
-void bucket_launch(dim3 grid, hipStream_t stream, const TIN* x, const float* R, int T, int H, int32_t* bucket,
-                   int32_t* counts) {
+void bucket_launch(dim3 grid, hipStream_t stream, const void* x, const void* x2, const float* R, int T, int H,
+                   int32_t* bucket, int32_t* bucket2, int32_t* counts, int32_t* counts2) {
+  const TIN* a = static_cast<const TIN*>(x);
+  const TIN* a2 = static_cast<const TIN*>(x2);
   if constexpr (HALF <= 16)
-    hipLaunchKernelGGL((k_hash_bucket_dpp<TIN, HALF>), grid, dim3(256), 0, stream, x, R, T, H, bucket, counts);
+    hipLaunchKernelGGL((k_hash_bucket_dpp<TIN, HALF>), grid, dim3(256), 0, stream, a, a2, R, T, H, bucket, bucket2,
+                       counts, counts2);
   else
-    hipLaunchKernelGGL((k_hash_bucket<TIN, HALF>), grid, dim3(256), 0, stream, x, R, T, H, bucket, counts);
+    hipLaunchKernelGGL((k_hash_bucket<TIN, HALF>), grid, dim3(256), 0, stream, a, a2, R, T, H, bucket, bucket2,
+                       counts, counts2);
 }
 
 // ---------------------------------------------------------------------------
 // Stable counting sort by bucket: per-chunk histograms, then a scatter whose
 // workgroups each derive their own base from all chunk histograms of the
-// head (4 KB of L2 reads at nb = 16, 64 chunks) and whose in-chunk ranks
-// come from wave64 ballots.
+// head (4 KB of L2 reads at nb = 16, 64 chunks, all loads in flight at once
+// and summed by LDS atomics) and whose in-chunk ranks come from wave64
+// ballots.
 // ---------------------------------------------------------------------------
 
 constexpr int kSortChunk = 256;
@@ -358,20 +374,41 @@ __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ b
   if (threadIdx.x < nb) hist[(static_cast<size_t>(bh) * nC + c) * nb + threadIdx.x] = hs[threadIdx.x];
 }
 
-// Workgroup (chunk c, head bh). base[v] = (tokens of the head with bucket
-// < v) + (tokens of bucket v in chunks before c); the chunk-0 workgroup also
-// writes offsets. With align > 0 the same workgroup also places its tokens
-// in the bucket-aligned layout (bucket v's rows start at A_v) and writes the
-// pad rows of that layout that fall in rows [256 c, 256 c + 256). Chunks at or
-// beyond nC only write pad entries.
-__global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict__ bucket, int T, int Tp, int nb, int nC,
-                                                      const int32_t* __restrict__ hist, int32_t pad,
-                                                      int32_t* __restrict__ perm, int32_t* __restrict__ bsorted,
-                                                      int32_t* __restrict__ offsets, int align, int Tseg,
-                                                      int32_t* __restrict__ idx_seg, int32_t* __restrict__ bkt_seg,
-                                                      int32_t* __restrict__ seg_off, int32_t* dev_err) {
-  __shared__ int32_t part_tot[4][64];
-  __shared__ int32_t part_bef[4][64];
+// One side (queries or keys) of a sort / layout launch.
+struct SortSide {
+  const int32_t* bucket;  // (B, H, T)
+  const int32_t* hist;    // (B, H, nC, nb) chunk counts
+  int32_t pad;            // index of pad entries
+  int align;              // 0: sort only; else rows per bucket run multiple
+  int Tseg;               // rows per head of the aligned layout
+  int32_t* perm;
+  int32_t* bsorted;
+  int32_t* offsets;
+  int32_t* idx_seg;
+  int32_t* bkt_seg;
+  int32_t* seg_off;
+};
+
+// Workgroup (chunk c, head bh, side z: s0 or s1). base[v] = (tokens of the
+// head with bucket < v) + (tokens of bucket v in chunks before c); the
+// chunk-0 workgroup also writes offsets. With align > 0 the same workgroup
+// also places its tokens in the bucket-aligned layout (bucket v's rows start
+// at A_v) and writes the pad rows of that layout that fall in rows
+// [256 c, 256 c + 256). Chunks at or beyond nC only write pad entries.
+__global__ __launch_bounds__(256) void k_sort_scatter(const SortSide s0, const SortSide s1, int T, int Tp, int nb,
+                                                      int nC, int32_t* dev_err) {
+  const SortSide& sd = blockIdx.z ? s1 : s0;
+  const int32_t* __restrict__ bucket = sd.bucket;
+  const int32_t* __restrict__ hist = sd.hist;
+  const int32_t pad = sd.pad;
+  const int align = sd.align, Tseg = sd.Tseg;
+  int32_t* __restrict__ perm = sd.perm;
+  int32_t* __restrict__ bsorted = sd.bsorted;
+  int32_t* __restrict__ offsets = sd.offsets;
+  int32_t* __restrict__ idx_seg = sd.idx_seg;
+  int32_t* __restrict__ bkt_seg = sd.bkt_seg;
+  int32_t* __restrict__ seg_off = sd.seg_off;
+  __shared__ int32_t tot_a[64], bef_a[64];
   __shared__ int32_t base_s[64];
   __shared__ int32_t wcnt[4][64];
   __shared__ int32_t tot_s[64], off_s[65], aoff_s[65];
@@ -380,25 +417,41 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
   int32_t* pp = perm + static_cast<size_t>(bh) * Tp;
   int32_t* bp = bsorted + static_cast<size_t>(bh) * Tp;
   const int t = c * kSortChunk + threadIdx.x;
-  // per-bucket totals and the count before this chunk, lane = bucket
+  int v = -1;
+  if (c < nC && t < T) v = bucket[static_cast<size_t>(bh) * T + t];
+  if (w == 0) {
+    tot_a[lane] = 0;
+    bef_a[lane] = 0;
+  }
+  wcnt[w][lane] = 0;
+  __syncthreads();
+  // per-bucket totals and counts before this chunk: entry e = cc nb + v of the
+  // head's chunk histograms, 4 independent loads per thread in flight
   {
-    int tot = 0, bef = 0;
-    if (lane < nb) {
-      const int32_t* hp = hist + static_cast<size_t>(bh) * nC * nb + lane;
-      for (int cc = w; cc < nC; cc += 4) {
-        const int n = hp[static_cast<size_t>(cc) * nb];
-        tot += n;
-        bef += cc < c ? n : 0;
+    const int nE = nC * nb, eb = c * nb;
+    const int32_t* hp = hist + static_cast<size_t>(bh) * nE;
+    for (int e0 = 0; e0 < nE; e0 += 1024) {
+      int n[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = e0 + k * 256 + threadIdx.x;
+        n[k] = e < nE ? hp[e] : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = e0 + k * 256 + threadIdx.x;
+        if (n[k] != 0) {
+          const int bv = e % nb;
+          atomicAdd(&tot_a[bv], n[k]);
+          if (e < eb) atomicAdd(&bef_a[bv], n[k]);
+        }
       }
     }
-    part_tot[w][lane] = tot;
-    part_bef[w][lane] = bef;
-    wcnt[w][lane] = 0;
   }
   __syncthreads();
   if (w == 0) {
-    const int tot = part_tot[0][lane] + part_tot[1][lane] + part_tot[2][lane] + part_tot[3][lane];
-    const int bef = part_bef[0][lane] + part_bef[1][lane] + part_bef[2][lane] + part_bef[3][lane];
+    const int tot = lane < nb ? tot_a[lane] : 0;
+    const int bef = lane < nb ? bef_a[lane] : 0;
     int x = tot;  // inclusive scan over buckets
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -436,8 +489,6 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const int32_t* __restrict_
   }
   int32_t* ip = align > 0 ? idx_seg + static_cast<size_t>(bh) * Tseg : nullptr;
   int32_t* kp = align > 0 ? bkt_seg + static_cast<size_t>(bh) * Tseg : nullptr;
-  int v = -1;
-  if (c < nC && t < T) v = bucket[static_cast<size_t>(bh) * T + t];
   const bool valid = c < nC && t < T && v >= 0 && v < nb;
   if (c < nC && t < T && !valid) set_dev_err(dev_err, SCFA_DEVERR_BUCKET_RANGE);
   int my_rank = 0;
@@ -1000,20 +1051,22 @@ int scfa_qk_compact(int dtype, const void* x, const uint8_t* keep, const int32_t
   return SCFA_OK;
 }
 
-static int launch_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb,
-                              int32_t* bucket, int32_t* counts, hipStream_t stream) {
-  if (!x || !R || !bucket) return SCFA_ERR_INVALID;
+// nx = 1: side x only; nx = 2: sides x and x2 in one launch (grid z).
+static int launch_hash_bucket(int dtype, int nx, const void* x, const void* x2, const float* R, int B, int T, int H,
+                              int D, int nb, int32_t* bucket, int32_t* bucket2, int32_t* counts, int32_t* counts2,
+                              hipStream_t stream) {
+  if (!x || !R || !bucket || (nx == 2 && (!x2 || !bucket2))) return SCFA_ERR_INVALID;
   if (B < 1 || T < 1 || H < 1 || nb < 2 || nb % 2) return SCFA_ERR_INVALID;
   if (!dtype_ok(dtype)) return SCFA_ERR_INVALID;
   if (D != 64 || nb > 64) return SCFA_ERR_UNSUPPORTED;
-  const dim3 grid(ceil_div(T, 256), B * H);
+  const dim3 grid(ceil_div(T, 256), B * H, nx);
   const int half = nb / 2;
-#define SCFA_BUCKET_CASE(HALF)                                                                               \
-  case HALF:                                                                                                 \
-    if (dtype == SCFA_BF16)                                                                                  \
-      bucket_launch<uint16_t, HALF>(grid, stream, static_cast<const uint16_t*>(x), R, T, H, bucket, counts); \
-    else                                                                                                     \
-      bucket_launch<float, HALF>(grid, stream, static_cast<const float*>(x), R, T, H, bucket, counts);       \
+#define SCFA_BUCKET_CASE(HALF)                                                                                    \
+  case HALF:                                                                                                      \
+    if (dtype == SCFA_BF16)                                                                                       \
+      bucket_launch<uint16_t, HALF>(grid, stream, x, x2, R, T, H, bucket, bucket2, counts, counts2);              \
+    else                                                                                                          \
+      bucket_launch<float, HALF>(grid, stream, x, x2, R, T, H, bucket, bucket2, counts, counts2);                 \
     break;
   switch (half) {
     SCFA_BUCKET_CASE(1)
@@ -1038,13 +1091,20 @@ static int launch_hash_bucket(int dtype, const void* x, const float* R, int B, i
 
 int scfa_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb, int32_t* bucket,
                      hipStream_t stream) {
-  return launch_hash_bucket(dtype, x, R, B, T, H, D, nb, bucket, nullptr, stream);
+  return launch_hash_bucket(dtype, 1, x, nullptr, R, B, T, H, D, nb, bucket, nullptr, nullptr, nullptr, stream);
 }
 
 int scfa_hash_bucket_counts(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb,
                             int32_t* bucket, int32_t* chunk_counts, hipStream_t stream) {
   if (!chunk_counts) return SCFA_ERR_INVALID;
-  return launch_hash_bucket(dtype, x, R, B, T, H, D, nb, bucket, chunk_counts, stream);
+  return launch_hash_bucket(dtype, 1, x, nullptr, R, B, T, H, D, nb, bucket, nullptr, chunk_counts, nullptr, stream);
+}
+
+int scfa_hash_bucket_qk(int dtype, const void* q, const void* k, const float* R, int B, int T, int H, int D, int nb,
+                        int32_t* bucket_q, int32_t* bucket_k, int32_t* counts_q, int32_t* counts_k,
+                        hipStream_t stream) {
+  if (!counts_q || !counts_k) return SCFA_ERR_INVALID;
+  return launch_hash_bucket(dtype, 2, q, k, R, B, T, H, D, nb, bucket_q, bucket_k, counts_q, counts_k, stream);
 }
 
 size_t scfa_hash_sort_workspace_bytes(int B, int H, int T, int nb) {
@@ -1065,8 +1125,8 @@ int scfa_hash_sort(const int32_t* bucket, int B, int H, int T, int nb, int32_t p
   int32_t* hist = static_cast<int32_t*>(workspace);
   hipLaunchKernelGGL(k_sort_hist, dim3(nC, B * H), dim3(256), 0, stream, bucket, T, nb, nC, hist, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_sort_scatter, dim3(nCx, B * H), dim3(256), 0, stream, bucket, T, Tp, nb, nC, hist, pad_idx,
-                     perm, bucket_sorted, offsets, 0, 0, nullptr, nullptr, nullptr, dev_err);
+  const SortSide sd{bucket, hist, pad_idx, 0, 0, perm, bucket_sorted, offsets, nullptr, nullptr, nullptr};
+  hipLaunchKernelGGL(k_sort_scatter, dim3(nCx, B * H), dim3(256), 0, stream, sd, sd, T, Tp, nb, nC, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }
@@ -1106,8 +1166,33 @@ int scfa_hash_layout(const int32_t* bucket, const int32_t* chunk_counts, int B, 
   const int nC = ceil_div(T, kSortChunk);
   const int Tp = pad_rows(T);
   const int nW = ceil_div(align != 0 ? max(Tp, Tseg) : Tp, kSortChunk);
-  hipLaunchKernelGGL(k_sort_scatter, dim3(nW, B * H), dim3(256), 0, stream, bucket, T, Tp, nb, nC, chunk_counts,
-                     pad_idx, perm, bucket_sorted, offsets, align, Tseg, idx_seg, bkt_seg, seg_offsets, dev_err);
+  const SortSide sd{bucket,  chunk_counts, pad_idx, align,       Tseg,
+                    perm,    bucket_sorted, offsets, idx_seg, bkt_seg, seg_offsets};
+  hipLaunchKernelGGL(k_sort_scatter, dim3(nW, B * H), dim3(256), 0, stream, sd, sd, T, Tp, nb, nC, dev_err);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+int scfa_hash_layout_qk(const int32_t* bucket_q, const int32_t* bucket_k, const int32_t* counts_q,
+                        const int32_t* counts_k, int B, int H, int T, int nb, int Tseg_q, int Tseg_k, int32_t* perm_q,
+                        int32_t* perm_k, int32_t* bsorted_q, int32_t* bsorted_k, int32_t* offsets_q,
+                        int32_t* offsets_k, int32_t* idx_q, int32_t* idx_k, int32_t* bkt_q, int32_t* bkt_k,
+                        int32_t* seg_q, int32_t* seg_k, int32_t* dev_err, hipStream_t stream) {
+  if (!bucket_q || !bucket_k || !counts_q || !counts_k || !perm_q || !perm_k || !bsorted_q || !bsorted_k ||
+      !offsets_q || !offsets_k || !idx_q || !idx_k || !bkt_q || !bkt_k || !seg_q || !seg_k)
+    return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || T < 1 || nb < 1) return SCFA_ERR_INVALID;
+  if (nb > 64) return SCFA_ERR_UNSUPPORTED;
+  for (const int Tseg : {Tseg_q, Tseg_k})
+    if (Tseg < SCFA_ROW_ALIGN || Tseg % SCFA_ROW_ALIGN || Tseg < T) return SCFA_ERR_INVALID;
+  const int nC = ceil_div(T, kSortChunk);
+  const int Tp = pad_rows(T);
+  const int nW = ceil_div(max(Tp, max(Tseg_q, Tseg_k)), kSortChunk);
+  const SortSide sq{bucket_q, counts_q, SCFA_Q_PAD, SCFA_TILE_M, Tseg_q, perm_q, bsorted_q, offsets_q, idx_q, bkt_q,
+                    seg_q};
+  const SortSide sk{bucket_k, counts_k, SCFA_K_PAD, SCFA_TILE_N, Tseg_k, perm_k, bsorted_k, offsets_k, idx_k, bkt_k,
+                    seg_k};
+  hipLaunchKernelGGL(k_sort_scatter, dim3(nW, B * H, 2), dim3(256), 0, stream, sq, sk, T, Tp, nb, nC, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }

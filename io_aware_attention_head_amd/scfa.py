@@ -49,6 +49,8 @@ _SIGS = {
     "scfa_hash_segments": (_i, [_vp, _vp, _i, _i, _i, _i, _i, ctypes.c_int32, _i, _vp, _vp, _vp, _vp, _vp]),
     "scfa_hash_layout": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_hash_bucket_counts": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "scfa_hash_bucket_qk": (_i, [_i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "scfa_hash_layout_qk": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i] + [_vp] * 14),
     "scfa_bwd_table": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_gather": (_i, [_i, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "scfa_range_table": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -166,6 +168,15 @@ def scfa_hash_bucket_counts(x, R, nb, bucket, chunk_counts, stream=None):
                                          _stream(stream, x)), "scfa_hash_bucket_counts")
 
 
+def scfa_hash_bucket_qk(q, k, R, nb, bucket_q, bucket_k, counts_q, counts_k, stream=None):
+    """scfa_hash_bucket_counts of queries and keys in one launch."""
+    if q.shape != k.shape or q.dtype != k.dtype:
+        raise ScfaError("queries and keys must have the same shape and dtype")
+    B, T, H, D = q.shape
+    _check(lib().scfa_hash_bucket_qk(_dt(q), _p(q), _p(k), _p(R), B, T, H, D, nb, _p(bucket_q), _p(bucket_k),
+                                     _p(counts_q), _p(counts_k), _stream(stream, q)), "scfa_hash_bucket_qk")
+
+
 def scfa_hash_sort_workspace_bytes(B, H, T, nb) -> int:
     return lib().scfa_hash_sort_workspace_bytes(B, H, T, nb)
 
@@ -198,6 +209,19 @@ def scfa_hash_layout(bucket, chunk_counts, nb, align, pad_idx, perm, bucket_sort
     _check(lib().scfa_hash_layout(_p(bucket), _p(chunk_counts), B, H, T, nb, align, pad_idx, Tseg, _p(perm),
                                   _p(bucket_sorted), _p(offsets), _p(idx_seg), _p(bkt_seg), _p(seg_offsets),
                                   _p(dev_err), _stream(stream, bucket)), "scfa_hash_layout")
+
+
+def scfa_hash_layout_qk(bucket_q, bucket_k, counts_q, counts_k, nb, perm_q, perm_k, bs_q, bs_k, off_q, off_k, idx_q,
+                        idx_k, bkt_q, bkt_k, seg_q, seg_k, dev_err, stream=None):
+    """scfa_hash_layout of queries (query-tile alignment, query pads) and keys
+    (key-tile alignment, key pads) in one launch."""
+    B, H, T = bucket_q.shape
+    if bucket_k.shape != bucket_q.shape:
+        raise ScfaError("query and key buckets must have the same shape")
+    _check(lib().scfa_hash_layout_qk(_p(bucket_q), _p(bucket_k), _p(counts_q), _p(counts_k), B, H, T, nb,
+                                     idx_q.shape[-1], idx_k.shape[-1], _p(perm_q), _p(perm_k), _p(bs_q), _p(bs_k),
+                                     _p(off_q), _p(off_k), _p(idx_q), _p(idx_k), _p(bkt_q), _p(bkt_k), _p(seg_q),
+                                     _p(seg_k), _p(dev_err), _stream(stream, bucket_q)), "scfa_hash_layout_qk")
 
 
 def chunk_count_shape(B, H, T, nb):
@@ -569,16 +593,14 @@ class Plan:
 
     # -- stages ---------------------------------------------------------------
     def bucket(self, q, k, R, stream=None):
-        """LSH buckets and the chunk counts of the sort."""
-        scfa_hash_bucket_counts(q, R, self.nb, self.bq, self.cq, stream)
-        scfa_hash_bucket_counts(k, R, self.nb, self.bk, self.ck, stream)
+        """LSH buckets and the chunk counts of the sort (queries and keys in one launch)."""
+        scfa_hash_bucket_qk(q, k, R, self.nb, self.bq, self.bk, self.cq, self.ck, stream)
 
     def sort(self, stream=None):
-        """Stable sort by bucket and the bucket-aligned layout (one launch per side)."""
-        scfa_hash_layout(self.bq, self.cq, self.nb, SCFA_TILE_M, SCFA_Q_PAD, self.perm_q, self.bs_q, self.offq,
-                         self.q_idx, self.q_bkt, self.segq, self.dev_err, stream)
-        scfa_hash_layout(self.bk, self.ck, self.nb, SCFA_TILE_N, SCFA_K_PAD, self.perm_k, self.bs_k, self.offk,
-                         self.k_idx, self.k_bkt, self.segk, self.dev_err, stream)
+        """Stable sort by bucket and the bucket-aligned layout (both sides in one launch)."""
+        scfa_hash_layout_qk(self.bq, self.bk, self.cq, self.ck, self.nb, self.perm_q, self.perm_k, self.bs_q, self.bs_k,
+                            self.offq, self.offk, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.segq, self.segk,
+                            self.dev_err, stream)
 
     def compact(self, q, k, keep_q, keep_k, stream=None):
         scfa_qk_count(keep_q, self.cnt[0], self.mx[0], self.choff[0], stream)

@@ -97,6 +97,20 @@ def test_invalid_arguments_rejected_without_gpu():
     assert L.scfa_hash_layout(dummy, dummy, 1, 1, 300, 65, 0, -1, 0, dummy, dummy, dummy, null, null, null, null,
                               null) == scfa.SCFA_ERR_UNSUPPORTED
     assert L.scfa_hash_bucket_counts(0, dummy, dummy, 1, 8, 1, 64, 16, dummy, null, null) == scfa.SCFA_ERR_INVALID
+    # two-side entry points: missing counts, NULL key side, rows below T, nb above 64
+    assert L.scfa_hash_bucket_qk(0, dummy, dummy, dummy, 1, 8, 1, 64, 16, dummy, dummy, dummy, null,
+                                 null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_bucket_qk(0, dummy, null, dummy, 1, 8, 1, 64, 16, dummy, dummy, dummy, dummy,
+                                 null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_bucket_qk(0, dummy, dummy, dummy, 1, 8, 1, 32, 16, dummy, dummy, dummy, dummy,
+                                 null) == scfa.SCFA_ERR_UNSUPPORTED
+    qk_out = [dummy] * 13
+    assert L.scfa_hash_layout_qk(dummy, dummy, dummy, dummy, 1, 1, 300, 16, 256, 384, *qk_out,
+                                 null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_layout_qk(dummy, dummy, dummy, dummy, 1, 1, 300, 16, 384, 384, *qk_out[:-2], null, dummy,
+                                 null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_layout_qk(dummy, dummy, dummy, dummy, 1, 1, 300, 65, 384, 384, *qk_out,
+                                 null) == scfa.SCFA_ERR_UNSUPPORTED
     assert L.scfa_hash_segment_rows(16384, 16, 128) == 18432
     assert L.scfa_hash_segment_rows(16384, 16, 48) == 0
     # work order: bad sizes, NULL pointers
@@ -110,6 +124,8 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros(1, 8, 1, 64)
     with pytest.raises(scfa.ScfaError):
         scfa.scfa_gather(x, torch.zeros(1, 1, 128, dtype=torch.int32), scfa.SCFA_ROWS, torch.zeros(1, 1, 128, 64))
+    with pytest.raises(scfa.ScfaError):  # queries and keys of different shapes
+        scfa.scfa_hash_bucket_qk(x, torch.zeros(1, 9, 1, 64), torch.zeros(1, 64, 8), 16, *[None] * 4)
 
 
 def test_header_constants_match_binding():

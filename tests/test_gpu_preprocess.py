@@ -444,3 +444,37 @@ def test_full_size_preprocessing_bitexact(name):
     tab = scfa.build_tables(pre)
     torch.cuda.synchronize()
     _tables_match(mode, pre, tab, pre.Tq, scfa.SCFA_TILE_M, scfa.SCFA_TILE_N, pre.q_bkt, pre.k_bkt, pre.Tk)
+
+
+@pytest.mark.parametrize("w", [WORKLOADS["hash_bf16_t16384_nb16"], small("hash", 1, 2, 700, dtype="f32", nb=24, seed=81),
+                               small("hash", 2, 2, 1000, nb=64, seed=82), small("hash", 1, 3, 1, nb=16, seed=83)],
+                         ids=lambda w: w.name)
+def test_plan_two_side_launches_bitexact(w):
+    """The Plan's one-launch-per-stage entry points (queries and keys in one
+    grid): buckets, chunk counts, sort and both aligned layouts bit-exact
+    against the oracle, as the one-side entry points are."""
+    need_gpu()
+    announce(f"two-side preprocessing {w.name}")
+    x = make_inputs(w)
+    g = to_dev(x)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    plan = scfa.Plan("hash", w.B, w.H, w.T, w.D, dt, nb=w.nb)
+    plan.prepare(g)
+    torch.cuda.synchronize()
+    assert int(plan.dev_err.item()) == 0
+    bq, bk = oracle_buckets(w, x)
+    for b_, bg, cg, pg, bsg, og, ig, kg, sg, align, pad, Tseg in (
+            (bq, plan.bq, plan.cq, plan.perm_q, plan.bs_q, plan.offq, plan.q_idx, plan.q_bkt, plan.segq,
+             scfa.SCFA_TILE_M, oracle.Q_PAD, plan.Tq),
+            (bk, plan.bk, plan.ck, plan.perm_k, plan.bs_k, plan.offk, plan.k_idx, plan.k_bkt, plan.segk,
+             scfa.SCFA_TILE_N, oracle.K_PAD, plan.Tk)):
+        assert np.array_equal(bg.cpu().numpy(), b_)
+        assert np.array_equal(cg.cpu().numpy(), chunk_counts_np(b_, w.nb))
+        perm, bs, offs = oracle.hash_sort(b_, w.nb)
+        assert np.array_equal(pg.cpu().numpy()[:, :, :w.T], perm)
+        assert np.array_equal(bsg.cpu().numpy()[:, :, :w.T], bs)
+        assert np.array_equal(og.cpu().numpy(), offs)
+        ri, rb, ro = oracle.hash_segments(perm, offs, w.nb, align, pad, Tseg)
+        assert np.array_equal(ig.cpu().numpy()[:, :, :Tseg], ri)
+        assert np.array_equal(kg.cpu().numpy()[:, :, :Tseg], rb)
+        assert np.array_equal(sg.cpu().numpy(), ro)
