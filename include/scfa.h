@@ -210,6 +210,14 @@ int scfa_hash_layout(const int32_t* bucket, const int32_t* chunk_counts, int B, 
  * bit for bit, as the two calls; the same citation.
  *  *_q / *_k      the arguments of scfa_hash_layout for that side (every
  *                 pointer required).
+ *  qstats, kstats optional (both with tiles, or all three NULL): the tile
+ *                 statistics of the two aligned layouts, (B, H, Tseg_q /
+ *                 SCFA_TILE_M, 4) and (B, H, Tseg_k / SCFA_TILE_N, 4), the
+ *                 same values scfa_range_table computes from idx_q, bkt_q,
+ *                 idx_k, bkt_k in SCFA_HASH mode ("Kernel tiling logic for
+ *                 Hash-sparse (Algorithm 2)" extrema), written by the threads
+ *                 that place each tile's first and last token.
+ *  tiles          (B*H) int32: set to 0, ready for scfa_fwd_table.
  *  dev_err        shared by both sides (may be NULL).
  * Argument errors as scfa_hash_layout; data errors of either side are OR-ed
  * into dev_err. */
@@ -217,7 +225,8 @@ int scfa_hash_layout_qk(const int32_t* bucket_q, const int32_t* bucket_k, const 
                         const int32_t* counts_k, int B, int H, int T, int nb, int Tseg_q, int Tseg_k, int32_t* perm_q,
                         int32_t* perm_k, int32_t* bsorted_q, int32_t* bsorted_k, int32_t* offsets_q,
                         int32_t* offsets_k, int32_t* idx_q, int32_t* idx_k, int32_t* bkt_q, int32_t* bkt_k,
-                        int32_t* seg_q, int32_t* seg_k, int32_t* dev_err, hipStream_t stream);
+                        int32_t* seg_q, int32_t* seg_k, int32_t* qstats, int32_t* kstats, int32_t* tiles,
+                        int32_t* dev_err, hipStream_t stream);
 
 /* Gather rows into head-major order: out row r of head (b, h) is
  * x[b, idx[b,h,r], h, :] when 0 <= idx < T, else zero.
@@ -264,6 +273,16 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
  * scfa_range_table call (nQt, nKt as there): the same bwd_tab.              */
 int scfa_bwd_table(const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, int B, int H, int nQt, int nKt,
                    int32_t* bwd_tab, hipStream_t stream);
+
+/* The forward range table from tile statistics: the second half of
+ * scfa_range_table (same rules, same citation), for statistics that another
+ * call produced (scfa_hash_layout_qk).
+ *  qstats, kstats  (B, H, nQt, 4), (B, H, nKt, 4) as scfa_range_table's.
+ *  fwd_tab         out (B, H, nQt, 2).
+ *  tiles           (B*H) int32, zero on entry: the processed-tile count is
+ *                  added to it. */
+int scfa_fwd_table(int mode, const int32_t* qstats, const int32_t* kstats, int B, int H, int nQt, int nKt,
+                   int32_t* fwd_tab, int32_t* tiles, hipStream_t stream);
 
 /* Launch order of the attention workgroups for one range table (the
  * forward table for the forward and dQ kernels, the backward table for the

@@ -387,6 +387,8 @@ struct SortSide {
   int32_t* idx_seg;
   int32_t* bkt_seg;
   int32_t* seg_off;
+  int32_t* stats;  // optional: (B, H, Tseg / align, 4) statistics of the aligned layout's tiles
+  int32_t* tiles;  // optional: (B*H) processed-tile counters, zeroed here
 };
 
 // Workgroup (chunk c, head bh, side z: s0 or s1). base[v] = (tokens of the
@@ -408,6 +410,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const SortSide s0, const S
   int32_t* __restrict__ idx_seg = sd.idx_seg;
   int32_t* __restrict__ bkt_seg = sd.bkt_seg;
   int32_t* __restrict__ seg_off = sd.seg_off;
+  int32_t* __restrict__ stats = align > 0 ? sd.stats : nullptr;
   __shared__ int32_t tot_a[64], bef_a[64];
   __shared__ int32_t base_s[64];
   __shared__ int32_t wcnt[4][64];
@@ -466,6 +469,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const SortSide s0, const S
     if (c == 0) {
       if (lane < nb) offsets[static_cast<size_t>(bh) * (nb + 1) + lane] = off;
       if (lane == 63) offsets[static_cast<size_t>(bh) * (nb + 1) + nb] = x;  // all tokens
+      if (lane == 0 && sd.tiles) sd.tiles[bh] = 0;
     }
     if (align > 0) {
       const int a = ((tot + align - 1) / align) * align;  // aligned rows of bucket `lane`
@@ -513,6 +517,23 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const SortSide s0, const S
       if (r < Tseg) {
         ip[r] = t;
         kp[r] = v;
+        if (stats) {
+          // Tile statistics [min pos, max pos, min bucket, max bucket]: the
+          // tile's rows are one bucket's tokens in ascending position, then
+          // pad rows (pad sorts below every position for queries, above for
+          // keys). The tile's first row writes the minimum and the bucket,
+          // its last real row the maximum.
+          const int r0 = r - r % align;
+          const int run_end = aoff_s[v] + tot_s[v];  // first row after bucket v's tokens
+          const bool has_pad = r0 + align > run_end;
+          int32_t* st = stats + (static_cast<size_t>(bh) * (Tseg / align) + r / align) * 4;
+          if (r == r0) {
+            st[0] = has_pad ? min(t, pad) : t;
+            st[2] = v;
+            st[3] = v;
+          }
+          if (r == min(r0 + align, run_end) - 1) st[1] = has_pad ? max(t, pad) : t;
+        }
       }
     }
   }
@@ -529,6 +550,9 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const SortSide s0, const S
     if (a == nb || t - aoff_s[a] >= tot_s[a]) {
       ip[t] = pad;
       kp[t] = a;
+      if (stats && a == nb && t % align == 0)  // a tile after the last bucket: pad rows only
+        *reinterpret_cast<int4*>(stats + (static_cast<size_t>(bh) * (Tseg / align) + t / align) * 4) =
+            make_int4(pad, pad, nb, nb);
     }
   }
 }
@@ -1125,7 +1149,7 @@ int scfa_hash_sort(const int32_t* bucket, int B, int H, int T, int nb, int32_t p
   int32_t* hist = static_cast<int32_t*>(workspace);
   hipLaunchKernelGGL(k_sort_hist, dim3(nC, B * H), dim3(256), 0, stream, bucket, T, nb, nC, hist, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  const SortSide sd{bucket, hist, pad_idx, 0, 0, perm, bucket_sorted, offsets, nullptr, nullptr, nullptr};
+  const SortSide sd{bucket, hist, pad_idx, 0, 0, perm, bucket_sorted, offsets, nullptr, nullptr, nullptr, nullptr, nullptr};
   hipLaunchKernelGGL(k_sort_scatter, dim3(nCx, B * H), dim3(256), 0, stream, sd, sd, T, Tp, nb, nC, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
@@ -1166,8 +1190,8 @@ int scfa_hash_layout(const int32_t* bucket, const int32_t* chunk_counts, int B, 
   const int nC = ceil_div(T, kSortChunk);
   const int Tp = pad_rows(T);
   const int nW = ceil_div(align != 0 ? max(Tp, Tseg) : Tp, kSortChunk);
-  const SortSide sd{bucket,  chunk_counts, pad_idx, align,       Tseg,
-                    perm,    bucket_sorted, offsets, idx_seg, bkt_seg, seg_offsets};
+  const SortSide sd{bucket, chunk_counts, pad_idx, align,       Tseg,    perm,    bucket_sorted,
+                    offsets, idx_seg,      bkt_seg, seg_offsets, nullptr, nullptr};
   hipLaunchKernelGGL(k_sort_scatter, dim3(nW, B * H), dim3(256), 0, stream, sd, sd, T, Tp, nb, nC, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
@@ -1177,10 +1201,12 @@ int scfa_hash_layout_qk(const int32_t* bucket_q, const int32_t* bucket_k, const 
                         const int32_t* counts_k, int B, int H, int T, int nb, int Tseg_q, int Tseg_k, int32_t* perm_q,
                         int32_t* perm_k, int32_t* bsorted_q, int32_t* bsorted_k, int32_t* offsets_q,
                         int32_t* offsets_k, int32_t* idx_q, int32_t* idx_k, int32_t* bkt_q, int32_t* bkt_k,
-                        int32_t* seg_q, int32_t* seg_k, int32_t* dev_err, hipStream_t stream) {
+                        int32_t* seg_q, int32_t* seg_k, int32_t* qstats, int32_t* kstats, int32_t* tiles,
+                        int32_t* dev_err, hipStream_t stream) {
   if (!bucket_q || !bucket_k || !counts_q || !counts_k || !perm_q || !perm_k || !bsorted_q || !bsorted_k ||
       !offsets_q || !offsets_k || !idx_q || !idx_k || !bkt_q || !bkt_k || !seg_q || !seg_k)
     return SCFA_ERR_INVALID;
+  if (!((qstats && kstats && tiles) || (!qstats && !kstats && !tiles))) return SCFA_ERR_INVALID;
   if (B < 1 || H < 1 || T < 1 || nb < 1) return SCFA_ERR_INVALID;
   if (nb > 64) return SCFA_ERR_UNSUPPORTED;
   for (const int Tseg : {Tseg_q, Tseg_k})
@@ -1189,9 +1215,9 @@ int scfa_hash_layout_qk(const int32_t* bucket_q, const int32_t* bucket_k, const 
   const int Tp = pad_rows(T);
   const int nW = ceil_div(max(Tp, max(Tseg_q, Tseg_k)), kSortChunk);
   const SortSide sq{bucket_q, counts_q, SCFA_Q_PAD, SCFA_TILE_M, Tseg_q, perm_q, bsorted_q, offsets_q, idx_q, bkt_q,
-                    seg_q};
+                    seg_q,    qstats,   tiles};
   const SortSide sk{bucket_k, counts_k, SCFA_K_PAD, SCFA_TILE_N, Tseg_k, perm_k, bsorted_k, offsets_k, idx_k, bkt_k,
-                    seg_k};
+                    seg_k,    kstats,   nullptr};
   hipLaunchKernelGGL(k_sort_scatter, dim3(nW, B * H, 2), dim3(256), 0, stream, sq, sk, T, Tp, nb, nC, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
@@ -1248,6 +1274,17 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
                        nKt, bwd_tab);
     SCFA_RETURN_IF_LAUNCH_FAILED();
   }
+  return SCFA_OK;
+}
+
+int scfa_fwd_table(int mode, const int32_t* qstats, const int32_t* kstats, int B, int H, int nQt, int nKt,
+                   int32_t* fwd_tab, int32_t* tiles, hipStream_t stream) {
+  if (mode != SCFA_DENSE && mode != SCFA_QK && mode != SCFA_HASH) return SCFA_ERR_INVALID;
+  if (!qstats || !kstats || !fwd_tab || !tiles) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || nQt < 1 || nKt < 1) return SCFA_ERR_INVALID;
+  hipLaunchKernelGGL(k_fwd_table, dim3(ceil_div(nQt, kTabWaves), B * H), dim3(64 * kTabWaves), 0, stream, mode, qstats,
+                     kstats, nQt, nKt, fwd_tab, tiles);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }
 

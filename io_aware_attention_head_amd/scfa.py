@@ -50,7 +50,8 @@ _SIGS = {
     "scfa_hash_layout": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_hash_bucket_counts": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "scfa_hash_bucket_qk": (_i, [_i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
-    "scfa_hash_layout_qk": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i] + [_vp] * 14),
+    "scfa_hash_layout_qk": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i] + [_vp] * 17),
+    "scfa_fwd_table": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]),
     "scfa_bwd_table": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_gather": (_i, [_i, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "scfa_range_table": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -212,16 +213,26 @@ def scfa_hash_layout(bucket, chunk_counts, nb, align, pad_idx, perm, bucket_sort
 
 
 def scfa_hash_layout_qk(bucket_q, bucket_k, counts_q, counts_k, nb, perm_q, perm_k, bs_q, bs_k, off_q, off_k, idx_q,
-                        idx_k, bkt_q, bkt_k, seg_q, seg_k, dev_err, stream=None):
+                        idx_k, bkt_q, bkt_k, seg_q, seg_k, dev_err, qstats=None, kstats=None, tiles=None, stream=None):
     """scfa_hash_layout of queries (query-tile alignment, query pads) and keys
-    (key-tile alignment, key pads) in one launch."""
+    (key-tile alignment, key pads) in one launch; optionally also the tile
+    statistics of both layouts and a zeroed processed-tile counter."""
     B, H, T = bucket_q.shape
     if bucket_k.shape != bucket_q.shape:
         raise ScfaError("query and key buckets must have the same shape")
     _check(lib().scfa_hash_layout_qk(_p(bucket_q), _p(bucket_k), _p(counts_q), _p(counts_k), B, H, T, nb,
                                      idx_q.shape[-1], idx_k.shape[-1], _p(perm_q), _p(perm_k), _p(bs_q), _p(bs_k),
                                      _p(off_q), _p(off_k), _p(idx_q), _p(idx_k), _p(bkt_q), _p(bkt_k), _p(seg_q),
-                                     _p(seg_k), _p(dev_err), _stream(stream, bucket_q)), "scfa_hash_layout_qk")
+                                     _p(seg_k), _p(qstats), _p(kstats), _p(tiles), _p(dev_err),
+                                     _stream(stream, bucket_q)), "scfa_hash_layout_qk")
+
+
+def scfa_fwd_table(mode, qstats, kstats, fwd_tab, tiles, stream=None):
+    """Forward range table from tile statistics (tiles must be zero on entry)."""
+    B, H, nQt, _ = qstats.shape
+    nKt = kstats.shape[2]
+    _check(lib().scfa_fwd_table(mode, _p(qstats), _p(kstats), B, H, nQt, nKt, _p(fwd_tab), _p(tiles),
+                                _stream(stream, qstats)), "scfa_fwd_table")
 
 
 def chunk_count_shape(B, H, T, nb):
@@ -597,10 +608,12 @@ class Plan:
         scfa_hash_bucket_qk(q, k, R, self.nb, self.bq, self.bk, self.cq, self.ck, stream)
 
     def sort(self, stream=None):
-        """Stable sort by bucket and the bucket-aligned layout (both sides in one launch)."""
+        """Stable sort by bucket, the bucket-aligned layout and its tile
+        statistics (both sides in one launch)."""
+        t = self.tab
         scfa_hash_layout_qk(self.bq, self.bk, self.cq, self.ck, self.nb, self.perm_q, self.perm_k, self.bs_q, self.bs_k,
                             self.offq, self.offk, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.segq, self.segk,
-                            self.dev_err, stream)
+                            self.dev_err, t.qstats, t.kstats, t.tiles, stream)
 
     def compact(self, q, k, keep_q, keep_k, stream=None):
         scfa_qk_count(keep_q, self.cnt[0], self.mx[0], self.choff[0], stream)
@@ -611,11 +624,16 @@ class Plan:
                         self.dev_err, stream)
 
     def tables(self, stream=None):
-        """Tile statistics, forward ranges and the launch order (the backward
-        table is built by backward())."""
+        """Forward ranges and the launch order, after the tile statistics
+        (computed here, or in hash mode by sort(), which also zeroes the
+        processed-tile counter that this call adds to); the backward table is
+        built by backward()."""
         t = self.tab
-        scfa_range_table(_table_mode(self.mode), self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H, self.Tq,
-                         self.Tk, t.Bm, t.Bn, t.qstats, t.kstats, t.fwd, None, t.tiles, stream)
+        if self.mode == "hash":  # the tile statistics come from the layout launch
+            scfa_fwd_table(SCFA_HASH, t.qstats, t.kstats, t.fwd, t.tiles, stream)
+        else:
+            scfa_range_table(_table_mode(self.mode), self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H,
+                             self.Tq, self.Tk, t.Bm, t.Bn, t.qstats, t.kstats, t.fwd, None, t.tiles, stream)
         scfa_work_order(t.fwd, t.kstats.shape[2], t.fwd_order, stream)
 
     def forward(self, stream=None):

@@ -104,13 +104,20 @@ def test_invalid_arguments_rejected_without_gpu():
                                  null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_hash_bucket_qk(0, dummy, dummy, dummy, 1, 8, 1, 32, 16, dummy, dummy, dummy, dummy,
                                  null) == scfa.SCFA_ERR_UNSUPPORTED
-    qk_out = [dummy] * 13
+    qk_out = [dummy] * 12 + [null] * 3 + [dummy]  # layouts, no statistics, dev_err
     assert L.scfa_hash_layout_qk(dummy, dummy, dummy, dummy, 1, 1, 300, 16, 256, 384, *qk_out,
                                  null) == scfa.SCFA_ERR_INVALID
-    assert L.scfa_hash_layout_qk(dummy, dummy, dummy, dummy, 1, 1, 300, 16, 384, 384, *qk_out[:-2], null, dummy,
-                                 null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_layout_qk(dummy, dummy, dummy, dummy, 1, 1, 300, 16, 384, 384, *qk_out[:11], null,
+                                 *qk_out[12:], null) == scfa.SCFA_ERR_INVALID
+    # statistics: all three or none
+    assert L.scfa_hash_layout_qk(dummy, dummy, dummy, dummy, 1, 1, 300, 16, 384, 384, *qk_out[:12], dummy, null, null,
+                                 dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_hash_layout_qk(dummy, dummy, dummy, dummy, 1, 1, 300, 65, 384, 384, *qk_out,
                                  null) == scfa.SCFA_ERR_UNSUPPORTED
+    # forward table from statistics: bad mode, NULL counter, bad sizes
+    assert L.scfa_fwd_table(7, dummy, dummy, 1, 1, 2, 2, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_fwd_table(2, dummy, dummy, 1, 1, 2, 2, dummy, null, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_fwd_table(2, dummy, dummy, 1, 1, 0, 2, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_hash_segment_rows(16384, 16, 128) == 18432
     assert L.scfa_hash_segment_rows(16384, 16, 48) == 0
     # work order: bad sizes, NULL pointers

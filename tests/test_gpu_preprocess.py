@@ -478,3 +478,9 @@ def test_plan_two_side_launches_bitexact(w):
         assert np.array_equal(ig.cpu().numpy()[:, :, :Tseg], ri)
         assert np.array_equal(kg.cpu().numpy()[:, :, :Tseg], rb)
         assert np.array_equal(sg.cpu().numpy(), ro)
+    # tile statistics from the layout launch and the forward table built on
+    # them: the same as the tables built from the index arrays
+    ref = scfa.build_tables(plan.prepared())
+    torch.cuda.synchronize()
+    for name in ("qstats", "kstats", "fwd", "tiles"):
+        assert torch.equal(getattr(plan.tab, name), getattr(ref, name)), name
