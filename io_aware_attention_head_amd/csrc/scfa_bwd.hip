@@ -15,9 +15,12 @@
 //
 // MI355X design:
 //  * Three kernels, no atomics (deterministic): a preparation kernel (Delta
-//    and log2 LSE per sorted query row), dK/dV per 64-key tile (4 waves x 16
-//    keys, query chunks of 32: 38 KB of LDS and 108 VGPRs, 4 waves per SIMD),
-//    dQ per 128-query tile (4 waves x 32 queries, key tiles of 64).
+//    and log2 LSE per sorted query row), dK/dV, dQ per 128-query tile
+//    (4 waves x 32 queries, key tiles of 64). dK/dV runs per pair of 64-key
+//    tiles (4 waves x 32 keys, query chunks of 32: 38 KB of LDS, 3 waves per
+//    SIMD; each Q / dO operand read from LDS serves two 16-key blocks) for
+//    the long ranges of QK and dense attention, and per 64-key tile (4 waves
+//    x 16 keys, 4 waves per SIMD) for the short ranges of the hash layout.
 //  * Operands are read from the original (B, T, H, D) tensors through the
 //    index arrays (gather fused into the loads, as in the forward): each
 //    lane's own rows straight into registers, the shared tiles by
@@ -232,8 +235,17 @@ __device__ inline WaveKeys wave_keys(int kpos, int kbkt, int T) {
 // dK^T += Q^T dS and dV^T += dO^T P), with their positions, buckets, log2
 // LSE and Delta.
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// dK, dV for short query ranges (the hash layout's): one workgroup per 64-key
+// tile; wave w owns keys 16w .. 16w+15
+// (its K and V rows in registers, one key per lane column). Query chunks of
+// 32 rows are staged by DMA: Q and dO each in the row layout (A operands of
+// S = Q K^T and dP = dO V^T) and in the transposed-read layout (A operands of
+// dK^T += Q^T dS and dV^T += dO^T P), with their positions, buckets, log2
+// LSE and Delta.
+// ---------------------------------------------------------------------------
 template <bool HASH, bool ZD>
-__global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
+__global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   constexpr int CB = QC * 128;  // bytes of one staged chunk copy (QC rows)
   __shared__ __align__(16) uint8_t smem[2 * BN * HD * 4];  // 2 stages x 4 chunk copies; epilogue staging (32 KB)
   __shared__ __align__(16) int32_t qpos_s[2][QC];
@@ -433,6 +445,304 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
   write_rows(tk, Ki, BN, p.dK, p.T, p.H, b, h);
   write_rows(tv, Ki, BN, p.dV, p.T, p.H, b, h);
   if constexpr (ZD) zero_unheld<BN>(p.k_idx + kbase, Ki, kt, p.TkP, p.T, p.H, b, h, p.dK, p.dV);
+}
+
+// Extrema of this wave's 32 keys (two blocks of 16; lane column r16 in each).
+__device__ inline WaveKeys wave_keys2(const int (&kpos)[2], const int (&kbkt)[2], int T) {
+  int mn = kInt32Max, mx = kInt32Min, mnb = kInt32Max, mxb = kInt32Min, nreal = 0;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const bool real = kpos[kb] >= 0 && kpos[kb] < T;
+    if (real) {
+      mn = min(mn, kpos[kb]);
+      mx = max(mx, kpos[kb]);
+      mnb = min(mnb, kbkt[kb]);
+      mxb = max(mxb, kbkt[kb]);
+      ++nreal;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    mn = min(mn, __shfl_xor(mn, o));
+    mx = max(mx, __shfl_xor(mx, o));
+    mnb = min(mnb, __shfl_xor(mnb, o));
+    mxb = max(mxb, __shfl_xor(mxb, o));
+    nreal += __shfl_xor(nreal, o);
+  }
+  WaveKeys k;
+  k.minpos = __builtin_amdgcn_readfirstlane(mn);
+  k.maxpos = __builtin_amdgcn_readfirstlane(mx);
+  k.minb = __builtin_amdgcn_readfirstlane(mnb);
+  k.maxb = __builtin_amdgcn_readfirstlane(mxb);
+  nreal = __builtin_amdgcn_readfirstlane(nreal);
+  k.any = nreal > 0;
+  k.all = nreal == 32;
+  return k;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV for long query ranges (QK and dense): one workgroup per pair of
+// 64-key tiles (2 kt, 2 kt + 1); wave w
+// owns keys 32w .. 32w+31 of the pair (waves 0-1 the first tile, 2-3 the
+// second), over the union of the two tiles' query ranges from the backward
+// table in chunks of 32 queries. The chunk's Q and dO operands read from LDS
+// serve both 16-key blocks of a wave. Each query chunk's 32 rows are staged
+// by DMA: Q and dO each in the row layout (A operands of S = Q K^T and
+// dP = dO V^T) and in the transposed-read layout (A operands of
+// dK^T += Q^T dS and dV^T += dO^T P), with their positions, buckets, log2
+// LSE and Delta.
+// ---------------------------------------------------------------------------
+template <bool HASH, bool ZD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_bwd_dkdv(BwdParams p) {
+  constexpr int CB = QC * 128;  // bytes of one staged chunk copy (QC rows)
+  constexpr int KR = 2 * BN;    // keys of a workgroup
+  __shared__ __align__(16) uint8_t smem[2 * BN * HD * 4];  // 2 stages x 4 chunk copies; epilogue staging (32 KB)
+  __shared__ __align__(16) int32_t qpos_s[2][QC];
+  __shared__ __align__(16) int32_t qbkt_s[2][QC];
+  __shared__ __align__(16) float lse_s[2][QC];
+  __shared__ __align__(16) float del_s[2][QC];
+  __shared__ __align__(16) int4 Qst[kStatCap];
+  __shared__ int32_t Ki[KR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int ws = __builtin_amdgcn_readfirstlane(w);
+  const int BH = p.B * p.H;
+  const int nKp = (p.nKt + 1) / 2;
+  int kp, bh;
+  map_work(blockIdx.x, BH, nKp, kp, bh, false);  // early key tiles see the most queries
+  const int kt0 = 2 * kp;
+  const bool has1 = kt0 + 1 < p.nKt;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const size_t rowbase = static_cast<size_t>(bh) * p.TqP;  // query side
+  const size_t kbase = static_cast<size_t>(bh) * p.TkP;    // key side
+  const int2 rng0 = p.bwd_tab[static_cast<size_t>(bh) * p.nKt + kt0];
+  const int2 rng1 = has1 ? p.bwd_tab[static_cast<size_t>(bh) * p.nKt + kt0 + 1] : make_int2(0, 0);
+  const int4 ks0 = p.kstats[static_cast<size_t>(bh) * p.nKt + kt0];
+  const int4 ks1 = has1 ? p.kstats[static_cast<size_t>(bh) * p.nKt + kt0 + 1] : make_int4(0, 0, 0, 0);
+  const bool e0 = rng0.y <= rng0.x, e1 = rng1.y <= rng1.x;
+  const int lo = e0 ? rng1.x : (e1 ? rng0.x : min(rng0.x, rng1.x));
+  const int hi = e0 ? (e1 ? lo : rng1.y) : (e1 ? rng0.y : max(rng0.y, rng1.y));
+  const int4* qst = p.qstats + static_cast<size_t>(bh) * p.nQt;
+  const bool qst_lds = hi - lo <= kStatCap;
+  if (qst_lds)
+    for (int i = tid; i < hi - lo; i += 256) Qst[i] = qst[lo + i];
+  if (tid < KR) Ki[tid] = (tid < BN || has1) ? p.k_idx[kbase + kt0 * BN + tid] : SCFA_K_PAD;
+  __syncthreads();
+  auto qstat = [&](int i) { return uniform4(qst_lds ? Qst[i - lo] : qst[i]); };
+
+  const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
+  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;
+  int kpos[2], kbkt[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int r = w * 32 + kb * 16 + r16;  // this lane's key of block kb
+    kpos[kb] = Ki[r];
+    kbkt[kb] = HASH ? ((r < BN || has1) ? p.k_bkt[kbase + kt0 * BN + r] : 0) : 0;
+  }
+  const WaveKeys wk = wave_keys2(kpos, kbkt, p.T);
+  bf16x8 Kb[2][2], Vb[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const size_t off = head0 + static_cast<size_t>(src_row(kpos[kb], p.T)) * rstride;
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      Kb[kb][ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.k) + off + (ds * 32 + g * 8) * 2);
+      Vb[kb][ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.v) + off + (ds * 32 + g * 8) * 2);
+    }
+  }
+  f32x4 dVa[2][4], dKa[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      dVa[kb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dKa[kb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // ---- DMA staging of a query chunk: wave w stages rows 8w .. 8w+7 --------
+  const uint8_t* qg = static_cast<const uint8_t*>(p.q) + head0;
+  const uint8_t* dg = static_cast<const uint8_t*>(p.dO) + head0;
+  uint32_t rch, tch;
+  {
+    const int row = 8 * w + (lane >> 3), cp = lane & 7;
+    rch = (cp ^ swz_k(row)) * 16;  // row layout
+    tch = swz_v(row, cp) * 16;     // transposed-read layout
+  }
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t lds_small = ws == 0 ? lds_addr(&qpos_s[0][0])
+                             : ws == 1 ? lds_addr(&qbkt_s[0][0])
+                             : ws == 2 ? lds_addr(&lse_s[0][0])
+                                       : lds_addr(&del_s[0][0]);
+  const void* small_src = ws == 0 ? static_cast<const void*>(p.q_idx + rowbase)
+                          : ws == 1 ? static_cast<const void*>(HASH ? p.q_bkt + rowbase : p.q_idx + rowbase)
+                          : ws == 2 ? static_cast<const void*>(p.lse2 + rowbase)
+                                    : static_cast<const void*>(p.delta + rowbase);
+  constexpr int CPT = BM / QC;  // chunks per query tile
+  const int nch = CPT * p.nQt;
+  auto chunk_rows = [&](int ci, int (&pos)[2]) {  // pos[0]: the row this lane stages
+    pos[0] = p.q_idx[rowbase + min(ci, nch - 1) * QC + 8 * w + (lane >> 3)];
+    pos[1] = 0;
+  };
+  auto stage = [&](int ci, int s, const int (&pos)[2]) {
+    const uint32_t base = lds0 + s * 4 * CB + ws * 1024;
+    const uint32_t off = static_cast<uint32_t>(src_row(pos[0], p.T)) * rstride;
+    dma16(qg, off + rch, base);
+    dma16(qg, off + tch, base + CB);
+    dma16(dg, off + rch, base + 2 * CB);
+    dma16(dg, off + tch, base + 3 * CB);
+    if (lane < QC) dma4(static_cast<const uint8_t*>(small_src) + ci * QC * 4, lane * 4, lds_small + s * QC * 4);
+  };
+  // chunk ci = CPT * query tile + part: query tiles in either tile's range
+  // that pass that tile's causal test
+  const int cend = CPT * hi;
+  auto needed = [&](int t) {
+    const int qy = qstat(t).y;
+    return (t >= rng0.x && t < rng0.y && qy >= ks0.x) || (t >= rng1.x && t < rng1.y && qy >= ks1.x);
+  };
+  auto next_chunk = [&](int ci) {
+    while (ci < cend && !needed(ci / CPT)) ci = (ci / CPT + 1) * CPT;
+    return ci;
+  };
+
+  int ci = next_chunk(CPT * lo);
+  int cn = ci < cend ? next_chunk(ci + 1) : cend;
+  int pos[2];
+  if (ci < cend) {
+    chunk_rows(ci, pos);
+    stage(ci, 0, pos);
+  }
+  chunk_rows(cn, pos);
+  dma_wait();
+  __syncthreads();
+  int s = 0;
+  int4 qs_cur = ci < cend ? qstat(ci / CPT) : make_int4(0, 0, 0, 0);
+  while (ci < cend) {
+    const int cnn = cn < cend ? next_chunk(cn + 1) : cend;
+    const int4 qs = qs_cur;
+    if (cn < cend) qs_cur = qstat(cn / CPT);
+    int pos_nn[2];
+    chunk_rows(cnn, pos_nn);  // issued before the DMA: waiting for it never waits for the DMA
+    __builtin_amdgcn_sched_barrier(0);
+    if (cn < cend) stage(cn, s ^ 1, pos);
+
+    // this wave's keys against the chunk's query tile: skip / no mask
+    const bool empty = !wk.any || wk.minpos > qs.y || (HASH && (wk.minb > qs.w || wk.maxb < qs.z));
+    if (!empty) {
+      const uint8_t* Qr = smem + s * 4 * CB;
+      const uint8_t* Qt = Qr + CB;
+      const uint8_t* Dr = Qr + 2 * CB;
+      const uint8_t* Dt = Qr + 3 * CB;
+      bool full = wk.all && wk.maxpos <= qs.x && (ci / CPT + 1) * BM <= p.Tq;
+      if (HASH) full = full && qs.z == qs.w && wk.minb == wk.maxb && wk.minb == qs.z;
+      // S = Q K^T (from the mask bias) and dP = dO V^T: rows = queries,
+      // column = this lane's key of block kb; element e of block qb is
+      // query 8 g + 4 qb + e of the chunk
+      f32x4 S[2][2], dP[2][2];
+      if (full) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        const bool buckets = HASH && !(qs.z == qs.w && wk.minb == wk.maxb);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int qo = 8 * g + 4 * qb;
+          const int4 qp4 = *reinterpret_cast<const int4*>(&qpos_s[s][qo]);
+          const int4 qb4 = *reinterpret_cast<const int4*>(&qbkt_s[s][qo]);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            f32x4 c;
+            c[0] = bias_if_ge(qp4.x, kpos[kb]);
+            c[1] = bias_if_ge(qp4.y, kpos[kb]);
+            c[2] = bias_if_ge(qp4.z, kpos[kb]);
+            c[3] = bias_if_ge(qp4.w, kpos[kb]);
+            if (buckets) {
+              c[0] = keep_if_eq(c[0], qb4.x, kbkt[kb]);
+              c[1] = keep_if_eq(c[1], qb4.y, kbkt[kb]);
+              c[2] = keep_if_eq(c[2], qb4.z, kbkt[kb]);
+              c[3] = keep_if_eq(c[3], qb4.w, kbkt[kb]);
+            }
+            S[kb][qb] = c;
+          }
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) dP[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const bf16x8 qa = read_row_op(Qr, qb, r16, ds * 4 + g);
+          const bf16x8 da = read_row_op(Dr, qb, r16, ds * 4 + g);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            S[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, Kb[kb][ds], S[kb][qb], 0, 0, 0);
+            dP[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, Vb[kb][ds], dP[kb][qb], 0, 0, 0);
+          }
+        }
+      // P = exp2(S c - lse2), dS = P (dP - Delta)
+      bf16x8 Pp[2], Sp[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qo = 8 * g + 4 * qb;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[s][qo]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&del_s[s][qo]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][e], p.c, -l4[e]));
+            S[kb][qb][e] = pe;
+            dP[kb][qb][e] = pe * (dP[kb][qb][e] - d4[e]);
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        Pp[kb] = pack_bf16x8(S[kb][0], S[kb][1]);
+        Sp[kb] = pack_bf16x8(dP[kb][0], dP[kb][1]);
+      }
+      // dV^T += dO^T P,  dK^T += Q^T dS  (rows = dims, column = this lane's key)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 dt = read_tr_op(Dt, db, 0, g, r16);
+        const bf16x8 qt = read_tr_op(Qt, db, 0, g, r16);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          dVa[kb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dt, Pp[kb], dVa[kb][db], 0, 0, 0);
+          dKa[kb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt, Sp[kb], dKa[kb][db], 0, 0, 0);
+        }
+      }
+    }
+
+    dma_wait();
+    __syncthreads();
+    s ^= 1;
+    ci = cn;
+    cn = cnn;
+    pos[0] = pos_nn[0];
+    pos[1] = pos_nn[1];
+  }
+
+  // ---- epilogue: stage dK (scaled), then dV, in LDS; write whole rows ------
+  float* tg = reinterpret_cast<float*>(smem);  // 128 rows x 64 fp32 = 32 KB
+  const int nrows = has1 ? KR : BN;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) stage_rows(tg, w * 32 + kb * 16 + r16, g, dKa[kb], p.scale);
+  __syncthreads();
+  write_rows(tg, Ki, nrows, p.dK, p.T, p.H, b, h);
+  __syncthreads();
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) stage_rows(tg, w * 32 + kb * 16 + r16, g, dVa[kb], 1.f);
+  __syncthreads();
+  write_rows(tg, Ki, nrows, p.dV, p.T, p.H, b, h);
+  if constexpr (ZD) {
+    zero_unheld<BN>(p.k_idx + kbase, Ki, kt0, p.TkP, p.T, p.H, b, h, p.dK, p.dV);
+    if (has1) zero_unheld<BN>(p.k_idx + kbase, Ki + BN, kt0 + 1, p.TkP, p.T, p.H, b, h, p.dK, p.dV);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -642,7 +952,12 @@ size_t ws_layout(int B, int H, int TqP, size_t off[3]) {
 
 template <bool HASH, bool ZD>
 int launch_bwd(const BwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((k_bwd_dkdv<HASH, ZD>), dim3(p.nKt * p.B * p.H), dim3(256), 0, stream, p);
+  // hash ranges are short (one bucket's query tiles): more, smaller
+  // workgroups keep the CUs busier than sharing each chunk between two tiles
+  if constexpr (HASH)
+    hipLaunchKernelGGL((k_bwd_dkdv64<HASH, ZD>), dim3(p.nKt * p.B * p.H), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_bwd_dkdv<HASH, ZD>), dim3((p.nKt + 1) / 2 * p.B * p.H), dim3(256), 0, stream, p);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   hipLaunchKernelGGL((k_bwd_dq<HASH, ZD>), dim3(p.nQt * p.B * p.H), dim3(256), 0, stream, p);
   SCFA_RETURN_IF_LAUNCH_FAILED();
