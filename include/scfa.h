@@ -23,7 +23,9 @@
  *    outputs are then unspecified, but no access leaves its buffer.
  *  - Layouts: user tensors are (B, T, H, D) row-major ("3.2 Big-Picture
  *    Architecture", items 2 and 4); per-head index arrays are (B, H, n);
- *    compacted / sorted tensors are head-major.
+ *    compacted / sorted tensors are head-major. The attention calls address
+ *    rows inside one batch entry's T x H x D block with 32-bit byte offsets:
+ *    a block of 4 GiB or more returns SCFA_ERR_UNSUPPORTED.
  *  - Row buffers of compacted / sorted tensors hold Tpad = SCFA_PAD(n) rows,
  *    n = valid rows (Tc for QK compaction, T for hash sorting). Rows
  *    beyond n are zero; their index entries are the pads (-1 query,

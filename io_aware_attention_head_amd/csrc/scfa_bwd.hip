@@ -990,6 +990,8 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
   if (B < 1 || H < 1 || T < 1 || Tq < 1 || Tk < 1 || !(scale > 0.f) || !isfinite(scale)) return SCFA_ERR_INVALID;
   if (!dtype_ok(dtype_in)) return SCFA_ERR_INVALID;
   if (D != HD || dtype_in != SCFA_BF16) return SCFA_ERR_UNSUPPORTED;
+  // row offsets within one batch entry's (T, H, D) block are 32-bit
+  if (static_cast<uint64_t>(T) * H * D * 2 > 0xFFFFFFFFull) return SCFA_ERR_UNSUPPORTED;
   if (mode == SCFA_QK && (Tq % SCFA_ROW_ALIGN || Tk != Tq)) return SCFA_ERR_INVALID;
   const int TqP = pad_rows(Tq), TkP = pad_rows(Tk);
   size_t off[3];

@@ -637,6 +637,8 @@ int check_common(int dtype_in, int dtype_out, int B, int H, int T, int D, float 
   if (B < 1 || H < 1 || T < 1) return SCFA_ERR_INVALID;
   if (!(scale > 0.f) || !isfinite(scale)) return SCFA_ERR_INVALID;
   if (D != HD) return SCFA_ERR_UNSUPPORTED;
+  // row offsets within one batch entry's (T, H, D) block are 32-bit
+  if (static_cast<uint64_t>(T) * H * D * dtype_size(dtype_in) > 0xFFFFFFFFull) return SCFA_ERR_UNSUPPORTED;
   return SCFA_OK;
 }
 

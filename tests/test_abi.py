@@ -76,6 +76,9 @@ def test_invalid_arguments_rejected_without_gpu():
                                 null) == scfa.SCFA_ERR_UNSUPPORTED
     assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 120, 64, ctypes.c_float(0.125), dummy, dummy,
                                 null) == scfa.SCFA_ERR_INVALID
+    # one batch entry's T x H x D block of 4 GiB or more (32-bit row offsets)
+    assert L.scfa_qk_sparse_fwd(*args, 1, 64, 1 << 20, 1 << 20, 64, ctypes.c_float(0.125), dummy, dummy,
+                                null) == scfa.SCFA_ERR_UNSUPPORTED
     hargs = [0, 1] + [dummy] * 10
     # hash forward: a NULL table is rejected
     assert L.scfa_hash_sparse_fwd(*hargs[:-1], null, null, 1, 1, 8, 8, 8, 64, ctypes.c_float(0.125), dummy, dummy,
