@@ -152,3 +152,22 @@ def test_bwd_full_size(name):
             ref_v = dO[b, has, h].sum(axis=0)
             assert np.abs(dV[b, :, h].sum(axis=0) - ref_v).max() <= 2e-2 * (np.abs(ref_v).max() + 1)
             assert (dQ[b, ~has, h] == 0).all()
+
+
+def test_bwd_long_ranges():
+    """One bucket (R = 0) at T = 33000: every key tile's query range spans
+    258 query tiles and every query tile's key range up to 516 key tiles, so
+    both backward kernels read the tile statistics from global memory (more
+    than their LDS copy holds) and the forward does too (more than 512 key
+    tiles); one head against the oracle."""
+    need_gpu()
+    w = small("hash", 1, 1, 33000, nb=2, seed=76, grad=True)
+    announce("bwd long ranges hash nb=2 T=33000")
+    x = make_inputs(w)
+    x["R"].zero_()  # a single bucket: causal attention over all 33000 tokens
+    g, pre, tab, O, lse, grads = _run(w, x)
+    assert tab.fwd.shape[2] > 256 and tab.kstats.shape[2] > 512
+    heads = [(0, 0)]
+    ref = _oracle_bwd(w, x, heads=heads)
+    rels = _check(grads, ref, heads=heads)
+    print(f"long ranges: rel dQ {rels[0]:.2e} dK {rels[1]:.2e} dV {rels[2]:.2e}")

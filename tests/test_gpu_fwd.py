@@ -208,6 +208,22 @@ def test_fwd_full_size(name):
     assert int(nvis.sum()) == int(ref.sum())
 
 
+def test_fwd_long_ranges():
+    """Dense causal at T = 33000 (516 key tiles): query tiles whose key range
+    exceeds the 512 tile statistics the kernel copies to LDS read them from
+    global memory; sampled rows of every head against the oracle."""
+    need_gpu()
+    w = small("dense", 1, 2, 33000, seed=65)
+    announce("fwd long ranges dense T=33000")
+    x = make_inputs(w)
+    _, pre, tab, O, lse = run_pipeline(w, x)
+    assert tab.kstats.shape[2] > 512
+    rows = _sampled_rows(w.T, 96, 8)
+    Or, Lr = oracle_fwd(w, x, rows=rows)
+    err, lerr = check_fwd(w, O, lse, Or, Lr, rows=rows)
+    print(f"long ranges: sampled max-abs {err:.2e}  lse {lerr:.2e}")
+
+
 def test_fwd_deterministic():
     need_gpu()
     announce("fwd determinism")
