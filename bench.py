@@ -52,6 +52,10 @@ def _parse():
     ap.add_argument("--fwd-only", action="store_true", help="only launch the forward kernel in the timed loop "
                                                             "(for counter collection)")
     ap.add_argument("--no-train", action="store_true", help="skip the backward (training) figures")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line: the isolated sweeps of the explainer's runtime figures "
+                         "(hash nb x T, QK keep x T; forward and forward+backward against dense causal), one JSON "
+                         "line per point")
     return ap.parse_args()
 
 
@@ -188,6 +192,64 @@ def _stress_figures(w, x, K, dense_fwd_ms):
             "speedup_vs_dense_causal_fwd": round(dense_fwd_ms / fms, 3)}
 
 
+def _time_ms(fn, K):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(K):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / K
+
+
+def _sweep(K):
+    """Isolated runtime sweeps in the manner of the explainer's figures
+    ("Experimental Results": hash-sparse runtime against nb and T, QK-sparse
+    against the drop rate and T) at B=1, H=12, D=64, bf16: for each point the
+    preprocessing + forward (eager launches), the forward kernel, the
+    backward, and the same kernels run dense-causal on the same shape. One
+    JSON line per point; the dense twin is timed once per T."""
+    import torch
+    import io_aware_attention_head_amd.scfa as scfa
+    from io_aware_attention_head_amd.inputs import make_inputs, small
+
+    dense = {}
+    for T in (1024, 2048, 4096, 8192, 16384):
+        wd = small("dense", 1, 12, T, seed=90, grad=True)
+        xd = {k: v.to("cuda:0") for k, v in make_inputs(wd).items()}
+        pd = scfa.Plan("dense", 1, 12, T, 64, torch.bfloat16)
+        pd.run(xd)
+        dense[T] = {"fwd_ms": _time_ms(pd.forward, K), "bwd_ms": _time_ms(lambda: pd.backward(xd["dO"]), K)}
+        del pd, xd
+        torch.cuda.empty_cache()
+    points = [("hash", nb, None, T) for nb in (2, 4, 8, 16, 32, 64) for T in (1024, 2048, 4096, 8192, 16384)]
+    points += [("qk", 16, keep, T) for keep in (0.7, 0.5, 0.3) for T in (1024, 2048, 4096, 8192, 16384)]
+    for mode, nb, keep, T in points:
+        w = small(mode, 1, 12, T, nb=nb, keep_p=keep if keep is not None else 0.7, seed=91, grad=True)
+        x = {k: v.to("cuda:0") for k, v in make_inputs(w).items()}
+        pl = scfa.Plan(mode, 1, 12, T, 64, torch.bfloat16, nb=nb)
+        pl.run(x)
+        pairs = int(pl.count_visible().sum().item())
+        step = _time_ms(lambda: pl.run(x), K)
+        fwd = _time_ms(pl.forward, K)
+        bwd = _time_ms(lambda: pl.backward(x["dO"]), K)
+        d = dense[T]
+        rec = {"sweep": "hash_nb_T" if mode == "hash" else "qk_keep_T", "mode": mode, "T": T, "B": 1, "H": 12,
+               "D": 64, "visible_pairs": pairs, "prep_fwd_ms_eager": round(step, 4), "fwd_kernel_ms": round(fwd, 4),
+               "bwd_ms": round(bwd, 4), "fwd_tflops": round(4 * 64 * pairs / (fwd * 1e-3) / 1e12, 1),
+               "dense_fwd_ms": round(d["fwd_ms"], 4), "dense_bwd_ms": round(d["bwd_ms"], 4),
+               "speedup_fwd": round(d["fwd_ms"] / fwd, 3), "speedup_fwd_bwd": round((d["fwd_ms"] + d["bwd_ms"]) /
+                                                                                 (fwd + bwd), 3),
+               "speedup_prep_fwd": round(d["fwd_ms"] / step, 3)}
+        rec["nb" if mode == "hash" else "keep"] = nb if mode == "hash" else keep
+        print(json.dumps(rec), flush=True)
+        del pl, x
+        torch.cuda.empty_cache()
+
+
 def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -198,6 +260,9 @@ def main():
     import torch
     if args.copy_calibration:
         _copy_calibration()
+        return
+    if args.sweep:
+        _sweep(args.steps)
         return
     import io_aware_attention_head_amd.scfa as scfa
     from io_aware_attention_head_amd.inputs import WORKLOADS, make_inputs
