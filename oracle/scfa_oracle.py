@@ -26,6 +26,9 @@ Readings of points the pages leave open (each one is also listed in the design doc):
     each product and each sum separately rounded; bucket = first index of the
     maximum of [c ; -c].
   * Sort key: (bucket ascending, position ascending).
+  * Hashing combined with within-bucket dropping (the explainer's follow-up
+    idea): in hash mode with keep masks a pair is visible iff both tokens
+    share a bucket, both are kept and the key does not come after the query.
   * Tile tables: see range_tables().
 
 Pins: every function here is checked by tests/test_oracle_*.py against brute
@@ -312,6 +315,13 @@ def _vis_rows(mode: str, rows: np.ndarray, T: int, kq, kk, bq, bk) -> np.ndarray
         vis &= (kq[rows] != 0)[:, None] & (kk != 0)[None, :]
     elif mode == "hash":
         vis &= bq[rows][:, None] == bk[None, :]
+        # hashing combined with within-bucket dropping (the explainer's
+        # follow-up, "Combined hashing and within-bucket dropping"): a pair
+        # must also have both tokens kept
+        if kq is not None:
+            vis &= (kq[rows] != 0)[:, None]
+        if kk is not None:
+            vis &= (kk != 0)[None, :]
     elif mode != "dense":
         raise ValueError(mode)
     return vis
@@ -326,7 +336,8 @@ def attention_fwd(mode: str, q, k, v, keep_q=None, keep_k=None, bkt_q=None, bkt_
                   rows: Optional[np.ndarray] = None, block: int = 512):
     """Explicit masked-softmax causal attention in original token order.
 
-    q, k, v: (B, T, H, D) float64. keep_q/keep_k: (B, T, H) (qk mode).
+    q, k, v: (B, T, H, D) float64. keep_q/keep_k: (B, T, H) (qk mode; in
+    hash mode optional, for hashing combined with within-bucket dropping).
     bkt_q/bkt_k: (B, H, T) bucket ids (hash mode).
     heads: optional list of (b, h) to compute (others left at 0 / -inf).
     rows: optional query positions to compute (others left at 0 / -inf).
@@ -449,9 +460,11 @@ def visible_pairs(mode: str, T: int, B: int, H: int, keep_q=None, keep_k=None, b
             else:
                 tot = 0
                 bq, bk = bkt_q[b, h], bkt_k[b, h]
+                kq = np.ones(T, bool) if keep_q is None else keep_q[b, :, h] != 0
+                kk = np.ones(T, bool) if keep_k is None else keep_k[b, :, h] != 0
                 for val in np.union1d(np.unique(bq), np.unique(bk)):
-                    kin = np.cumsum(bk == val)
-                    tot += int(kin[bq == val].sum())
+                    kin = np.cumsum((bk == val) & kk)
+                    tot += int(kin[(bq == val) & kq].sum())
                 out[b, h] = tot
     return out
 

@@ -20,13 +20,23 @@ def _np64(t):
     return t.to(torch.float64).numpy()
 
 
+def _omode(mode):
+    """Oracle mode of a test mode ("hash_keep": hash with keep masks)."""
+    return "hash" if mode == "hash_keep" else mode
+
+
+def _keeps(mode, kq, kk):
+    """Keep masks the oracle gets: QK and hash_keep only."""
+    return (kq, kk) if mode in ("qk", "hash_keep") else (None, None)
+
+
 def _case(mode, T, H=2, D=16, seed=0, keep_p=0.6, nb=4, B=1):
-    w = small(mode, B, H, T, D, dtype="bf16", keep_p=keep_p, nb=nb, seed=seed)
+    w = small(_omode(mode), B, H, T, D, dtype="bf16", keep_p=keep_p, nb=nb, seed=seed)
     x = make_inputs(w)
     q, k, v = _np64(x["q"]), _np64(x["k"]), _np64(x["v"])
     kq, kk = x["keep_q"].numpy(), x["keep_k"].numpy()
     bq = bk = None
-    if mode == "hash":
+    if _omode(mode) == "hash":
         bq = oracle.hash_bucket(q, x["R"].double().numpy(), nb)
         bk = oracle.hash_bucket(k, x["R"].double().numpy(), nb)
     return w, x, q, k, v, kq, kk, bq, bk
@@ -43,9 +53,9 @@ def _brute_fwd(mode, q, k, v, kq, kk, bq, bk):
             for i in range(T):
                 vis = []
                 for j in range(i + 1):
-                    if mode == "qk" and not (kq[b, i, h] and kk[b, j, h]):
+                    if mode in ("qk", "hash_keep") and not (kq[b, i, h] and kk[b, j, h]):
                         continue
-                    if mode == "hash" and bq[b, h, i] != bk[b, h, j]:
+                    if mode in ("hash", "hash_keep") and bq[b, h, i] != bk[b, h, j]:
                         continue
                     vis.append(j)
                 if not vis:
@@ -60,11 +70,11 @@ def _brute_fwd(mode, q, k, v, kq, kk, bq, bk):
     return O, L
 
 
-@pytest.mark.parametrize("mode", ["dense", "qk", "hash"])
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash", "hash_keep"])
 @pytest.mark.parametrize("T,seed", [(1, 0), (7, 1), (33, 2), (64, 3)])
 def test_fwd_matches_pairwise_brute_force(mode, T, seed):
     _, _, q, k, v, kq, kk, bq, bk = _case(mode, T, seed=seed)
-    O, L = oracle.attention_fwd(mode, q, k, v, kq, kk, bq, bk)
+    O, L = oracle.attention_fwd(_omode(mode), q, k, v, *_keeps(mode, kq, kk), bq, bk)
     Ob, Lb = _brute_fwd(mode, q, k, v, kq, kk, bq, bk)
     np.testing.assert_allclose(O, Ob, atol=1e-12, rtol=0)
     assert np.array_equal(np.isinf(L), np.isinf(Lb))
@@ -74,7 +84,7 @@ def test_fwd_matches_pairwise_brute_force(mode, T, seed):
 
 def test_fwd_brute_force_full_head_dim():
     _, _, q, k, v, kq, kk, bq, bk = _case("hash", 24, H=1, D=64, seed=9, nb=2)
-    O, L = oracle.attention_fwd("hash", q, k, v, kq, kk, bq, bk)
+    O, L = oracle.attention_fwd("hash", q, k, v, bkt_q=bq, bkt_k=bk)
     Ob, Lb = _brute_fwd("hash", q, k, v, kq, kk, bq, bk)
     np.testing.assert_allclose(O, Ob, atol=1e-12, rtol=0)
 
@@ -230,15 +240,15 @@ def test_hand_worked_qk_example():
 
 
 def _loss(mode, q, k, v, dO, kq, kk, bq, bk):
-    O, _ = oracle.attention_fwd(mode, q, k, v, kq, kk, bq, bk)
+    O, _ = oracle.attention_fwd(_omode(mode), q, k, v, *_keeps(mode, kq, kk), bq, bk)
     return float((O * dO).sum())
 
 
-@pytest.mark.parametrize("mode", ["dense", "qk", "hash"])
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash", "hash_keep"])
 def test_bwd_central_finite_differences(mode):
     _, x, q, k, v, kq, kk, bq, bk = _case(mode, 10, H=1, D=4, seed=13, keep_p=0.6, nb=2)
     dO = _np64(x["dO"])
-    grads = oracle.attention_bwd(mode, q, k, v, dO, kq, kk, bq, bk)
+    grads = oracle.attention_bwd(_omode(mode), q, k, v, dO, *_keeps(mode, kq, kk), bq, bk)
     eps = 1e-6
     for which, g in zip(range(3), grads):
         args = [q.copy(), k.copy(), v.copy()]
@@ -302,3 +312,40 @@ def test_negative_control_flipped_keep_bit_changes_row():
     O2, _ = oracle.attention_fwd("qk", q, k, v, kq, kk2)
     assert np.abs(O2[0, 3:, 0] - O[0, 3:, 0]).max(axis=1).min() > 0
     np.testing.assert_array_equal(O2[0, :3, 0], O[0, :3, 0])
+
+
+def test_hash_with_keep_all_kept_equals_hash():
+    """Hashing combined with within-bucket dropping, nothing dropped: plain
+    hash-sparse attention, to the bit."""
+    _, _, q, k, v, kq, kk, bq, bk = _case("hash", 60, H=2, D=16, seed=21, nb=8)
+    ones = np.ones_like(kq)
+    O1, L1 = oracle.attention_fwd("hash", q, k, v, ones, ones, bq, bk)
+    O2, L2 = oracle.attention_fwd("hash", q, k, v, bkt_q=bq, bkt_k=bk)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_hash_with_keep_single_bucket_equals_qk():
+    """One bucket (R = 0) with keep masks: QK-drop attention (the QK path is
+    pinned on its own against brute force and SDPA)."""
+    _, _, q, k, v, kq, kk, _, _ = _case("qk", 70, H=2, D=16, seed=22, keep_p=0.5)
+    R0 = np.zeros((2, 16, 4))
+    bq, bk = oracle.hash_bucket(q, R0, 8), oracle.hash_bucket(k, R0, 8)
+    O1, L1 = oracle.attention_fwd("hash", q, k, v, kq, kk, bq, bk)
+    O2, L2 = oracle.attention_fwd("qk", q, k, v, kq, kk)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    g1 = oracle.attention_bwd("hash", q, k, v, q, kq, kk, bq, bk)
+    g2 = oracle.attention_bwd("qk", q, k, v, q, kq, kk)
+    for a, b in zip(g1, g2):
+        assert np.array_equal(a, b)
+
+
+def test_hash_with_keep_dropped_rows_and_gradients_are_zero():
+    _, x, q, k, v, kq, kk, bq, bk = _case("hash_keep", 48, H=2, D=16, seed=23, keep_p=0.5, nb=4)
+    O, L = oracle.attention_fwd("hash", q, k, v, kq, kk, bq, bk)
+    dropped_q = kq.transpose(0, 2, 1) == 0  # (B, H, T)
+    assert np.isneginf(L[dropped_q]).all()
+    assert (O.transpose(0, 2, 1, 3)[dropped_q] == 0).all()
+    dQ, dK, dV = oracle.attention_bwd("hash", q, k, v, _np64(x["dO"]), kq, kk, bq, bk)
+    dropped_k = kk == 0  # (B, T, H)
+    assert (dK[dropped_k] == 0).all() and (dV[dropped_k] == 0).all()
+    assert (dQ[kq == 0] == 0).all()

@@ -172,25 +172,27 @@ def test_gather_rows():
     assert (g[0, 1, 2] == 0).all() and (g[0, 2, 1] == x[0, 3, 2]).all()
 
 
-@pytest.mark.parametrize("mode", ["dense", "qk", "hash"])
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash", "hash_keep"])
 def test_visible_pairs_brute_force(mode):
-    w = small(mode, 2, 2, 45, 16, keep_p=0.6, nb=4, seed=7)
+    omode = "hash" if mode == "hash_keep" else mode
+    w = small(omode, 2, 2, 45, 16, keep_p=0.6, nb=4, seed=7)
     x = make_inputs(w)
     kq, kk = x["keep_q"].numpy(), x["keep_k"].numpy()
     bq = bk = None
-    if mode == "hash":
+    if omode == "hash":
         R = x["R"].double().numpy()
         bq = oracle.hash_bucket(x["q"].double().numpy(), R, 4)
         bk = oracle.hash_bucket(x["k"].double().numpy(), R, 4)
-    got = oracle.visible_pairs(mode, 45, 2, 2, kq, kk, bq, bk)
+    keeps = (kq, kk) if mode in ("qk", "hash_keep") else (None, None)
+    got = oracle.visible_pairs(omode, 45, 2, 2, *keeps, bq, bk)
     for b in range(2):
         for h in range(2):
             n = 0
             for i in range(45):
                 for j in range(i + 1):
-                    if mode == "qk" and not (kq[b, i, h] and kk[b, j, h]):
+                    if mode in ("qk", "hash_keep") and not (kq[b, i, h] and kk[b, j, h]):
                         continue
-                    if mode == "hash" and bq[b, h, i] != bk[b, h, j]:
+                    if omode == "hash" and bq[b, h, i] != bk[b, h, j]:
                         continue
                     n += 1
             assert got[b, h] == n
