@@ -143,12 +143,23 @@ int scfa_hash_bucket_counts(int dtype, const void* x, const float* R, int B, int
  * two share R; grid dimension z selects the side): the same outputs, bit for
  * bit, as two calls. Same definition and citation.
  *  q, k                (B, T, H, D) of one dtype, device.
+ *  keep_q, keep_k      optional (B, T, H) uint8 keep masks, both or neither:
+ *                      hashing combined with within-bucket dropping (the SCFA
+ *                      explainer's follow-up idea of a mask that is both
+ *                      hash-based and drop-based). A dropped query takes
+ *                      bucket nb and a dropped key bucket nb + 1, which match
+ *                      nothing, so the rest of the hash path (sort and layout
+ *                      with nb + 2 buckets, tables, attention, backward) runs
+ *                      unchanged: dropped queries output zero with LSE -inf,
+ *                      dropped keys are seen by no query. nb <= 62.
  *  bucket_q, bucket_k  out (B, H, T) int32.
- *  counts_q, counts_k  out chunk counts as in scfa_hash_bucket_counts.
- * Argument errors as scfa_hash_bucket_counts (any NULL pointer: INVALID). */
-int scfa_hash_bucket_qk(int dtype, const void* q, const void* k, const float* R, int B, int T, int H, int D, int nb,
-                        int32_t* bucket_q, int32_t* bucket_k, int32_t* counts_q, int32_t* counts_k,
-                        hipStream_t stream);
+ *  counts_q, counts_k  out chunk counts as in scfa_hash_bucket_counts, with
+ *                      nb + 2 buckets per chunk when keep masks are given.
+ * Argument errors as scfa_hash_bucket_counts (any NULL pointer other than
+ * the keep masks, or only one keep mask: INVALID). */
+int scfa_hash_bucket_qk(int dtype, const void* q, const void* k, const float* R, const uint8_t* keep_q,
+                        const uint8_t* keep_k, int B, int T, int H, int D, int nb, int32_t* bucket_q, int32_t* bucket_k,
+                        int32_t* counts_q, int32_t* counts_k, hipStream_t stream);
 
 /* Bytes of device workspace scfa_hash_sort needs. */
 size_t scfa_hash_sort_workspace_bytes(int B, int H, int T, int nb);

@@ -169,11 +169,12 @@ __device__ inline float unit_elem<uint16_t>(const u32x4& u, int e) {
 template <typename TIN, int HALF>
 __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* x, const TIN* x2, const float* __restrict__ R,
                                                      int T, int H, int32_t* bucket, int32_t* bucket2, int32_t* counts,
-                                                     int32_t* counts2) {
+                                                     int32_t* counts2, const uint8_t* keep, const uint8_t* keep2, int nbo) {
   if (blockIdx.z) {  // second side of a two-input launch
     x = x2;
     bucket = bucket2;
     counts = counts2;
+    keep = keep2;
   }
   constexpr int D = 64;
   constexpr int EPU = 16 / sizeof(TIN);  // elements per 16-byte unit
@@ -182,9 +183,9 @@ __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* x, const TIN* x2
   constexpr int LDW = NU * 4 + 4;        // LDS row stride in 32-bit words (+16 bytes)
   __shared__ double Rs[D * HALF];
   __shared__ __align__(16) uint32_t xs[4][64 * LDW];
-  __shared__ int32_t hs[2 * HALF];  // bucket counts of this workgroup's 256 tokens
+  __shared__ int32_t hs[2 * HALF + 2];  // nbo <= 2 HALF + 2 counted buckets  // bucket counts of this workgroup's 256 tokens
   const int bh = blockIdx.y;
-  if (counts && threadIdx.x < 2 * HALF) hs[threadIdx.x] = 0;
+  if (counts && threadIdx.x < nbo) hs[threadIdx.x] = 0;
   const int b = bh / H, h = bh - b * H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < D * HALF; i += 256) Rs[i] = static_cast<double>(R[static_cast<size_t>(h) * D * HALF + i]);
@@ -220,13 +221,16 @@ __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* x, const TIN* x2
     if (c[j] > vp) { vp = c[j]; bp = j; }
     if (-c[j] > vn) { vn = -c[j]; bn = j; }
   }
-  const int v = (vn > vp) ? HALF + bn : bp;
+  int v = (vn > vp) ? HALF + bn : bp;
+  // a dropped token (hashing with within-bucket dropping) takes a bucket of
+  // its own side that matches nothing: nb for queries, nb + 1 for keys
+  if (keep && t < T && keep[(static_cast<size_t>(b) * T + t) * H + h] == 0) v = 2 * HALF + blockIdx.z;
   if (t < T) bucket[static_cast<size_t>(bh) * T + t] = v;
   if (counts) {  // the chunk histogram of the stable sort (chunk = this workgroup)
     if (t < T) atomicAdd(&hs[v], 1);
     __syncthreads();
-    if (threadIdx.x < 2 * HALF)
-      counts[(static_cast<size_t>(bh) * gridDim.x + blockIdx.x) * (2 * HALF) + threadIdx.x] = hs[threadIdx.x];
+    if (threadIdx.x < nbo)
+      counts[(static_cast<size_t>(bh) * gridDim.x + blockIdx.x) * nbo + threadIdx.x] = hs[threadIdx.x];
   }
 }
 
@@ -271,11 +275,12 @@ __device__ __forceinline__ void fma_units(double* c, const double* Rv, const uin
 template <typename TIN, int HALF>
 __global__ __launch_bounds__(256) void k_hash_bucket_dpp(const TIN* x, const TIN* x2, const float* __restrict__ R,
                                                          int T, int H, int32_t* bucket, int32_t* bucket2, int32_t* counts,
-                                                         int32_t* counts2) {
+                                                         int32_t* counts2, const uint8_t* keep, const uint8_t* keep2, int nbo) {
   if (blockIdx.z) {  // second side of a two-input launch
     x = x2;
     bucket = bucket2;
     counts = counts2;
+    keep = keep2;
   }
   constexpr int D = 64;
   constexpr int EPU = 16 / sizeof(TIN);
@@ -284,9 +289,9 @@ __global__ __launch_bounds__(256) void k_hash_bucket_dpp(const TIN* x, const TIN
   constexpr int LDW = NU * 4 + 4;
   constexpr int NR = D * HALF / 16;  // register pairs holding R
   __shared__ __align__(16) uint32_t xs[4][64 * LDW];
-  __shared__ int32_t hs[2 * HALF];
+  __shared__ int32_t hs[2 * HALF + 2];  // nbo <= 2 HALF + 2 counted buckets
   const int bh = blockIdx.y;
-  if (counts && threadIdx.x < 2 * HALF) hs[threadIdx.x] = 0;
+  if (counts && threadIdx.x < nbo) hs[threadIdx.x] = 0;
   const int b = bh / H, h = bh - b * H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const float* Rh = R + static_cast<size_t>(h) * D * HALF;
@@ -319,13 +324,16 @@ __global__ __launch_bounds__(256) void k_hash_bucket_dpp(const TIN* x, const TIN
     if (c[j] > vp) { vp = c[j]; bp = j; }
     if (-c[j] > vn) { vn = -c[j]; bn = j; }
   }
-  const int v = (vn > vp) ? HALF + bn : bp;
+  int v = (vn > vp) ? HALF + bn : bp;
+  // a dropped token (hashing with within-bucket dropping) takes a bucket of
+  // its own side that matches nothing: nb for queries, nb + 1 for keys
+  if (keep && t < T && keep[(static_cast<size_t>(b) * T + t) * H + h] == 0) v = 2 * HALF + blockIdx.z;
   if (t < T) bucket[static_cast<size_t>(bh) * T + t] = v;
   if (counts) {
     if (t < T) atomicAdd(&hs[v], 1);
     __syncthreads();
-    if (threadIdx.x < 2 * HALF)
-      counts[(static_cast<size_t>(bh) * gridDim.x + blockIdx.x) * (2 * HALF) + threadIdx.x] = hs[threadIdx.x];
+    if (threadIdx.x < nbo)
+      counts[(static_cast<size_t>(bh) * gridDim.x + blockIdx.x) * nbo + threadIdx.x] = hs[threadIdx.x];
   }
 }
 
@@ -333,15 +341,17 @@ __global__ __launch_bounds__(256) void k_hash_bucket_dpp(const TIN* x, const TIN
 // broadcast kernel above it.
 template <typename TIN, int HALF>
 void bucket_launch(dim3 grid, hipStream_t stream, const void* x, const void* x2, const float* R, int T, int H,
-                   int32_t* bucket, int32_t* bucket2, int32_t* counts, int32_t* counts2) {
+                   int32_t* bucket, int32_t* bucket2, int32_t* counts, int32_t* counts2, const uint8_t* keep,
+                   const uint8_t* keep2) {
   const TIN* a = static_cast<const TIN*>(x);
   const TIN* a2 = static_cast<const TIN*>(x2);
+  const int nbo = 2 * HALF + (keep ? 2 : 0);
   if constexpr (HALF <= 16)
     hipLaunchKernelGGL((k_hash_bucket_dpp<TIN, HALF>), grid, dim3(256), 0, stream, a, a2, R, T, H, bucket, bucket2,
-                       counts, counts2);
+                       counts, counts2, keep, keep2, nbo);
   else
     hipLaunchKernelGGL((k_hash_bucket<TIN, HALF>), grid, dim3(256), 0, stream, a, a2, R, T, H, bucket, bucket2,
-                       counts, counts2);
+                       counts, counts2, keep, keep2, nbo);
 }
 
 // ---------------------------------------------------------------------------
@@ -1075,22 +1085,26 @@ int scfa_qk_compact(int dtype, const void* x, const uint8_t* keep, const int32_t
   return SCFA_OK;
 }
 
-// nx = 1: side x only; nx = 2: sides x and x2 in one launch (grid z).
+// nx = 1: side x only; nx = 2: sides x and x2 in one launch (grid z);
+// keep / keep2: optional keep masks of the two sides (both or neither).
 static int launch_hash_bucket(int dtype, int nx, const void* x, const void* x2, const float* R, int B, int T, int H,
                               int D, int nb, int32_t* bucket, int32_t* bucket2, int32_t* counts, int32_t* counts2,
-                              hipStream_t stream) {
+                              const uint8_t* keep, const uint8_t* keep2, hipStream_t stream) {
   if (!x || !R || !bucket || (nx == 2 && (!x2 || !bucket2))) return SCFA_ERR_INVALID;
+  if ((keep != nullptr) != (keep2 != nullptr) || (keep && nx != 2)) return SCFA_ERR_INVALID;
   if (B < 1 || T < 1 || H < 1 || nb < 2 || nb % 2) return SCFA_ERR_INVALID;
   if (!dtype_ok(dtype)) return SCFA_ERR_INVALID;
-  if (D != 64 || nb > 64) return SCFA_ERR_UNSUPPORTED;
+  if (D != 64 || nb > (keep ? 62 : 64)) return SCFA_ERR_UNSUPPORTED;
   const dim3 grid(ceil_div(T, 256), B * H, nx);
   const int half = nb / 2;
-#define SCFA_BUCKET_CASE(HALF)                                                                                    \
-  case HALF:                                                                                                      \
-    if (dtype == SCFA_BF16)                                                                                       \
-      bucket_launch<uint16_t, HALF>(grid, stream, x, x2, R, T, H, bucket, bucket2, counts, counts2);              \
-    else                                                                                                          \
-      bucket_launch<float, HALF>(grid, stream, x, x2, R, T, H, bucket, bucket2, counts, counts2);                 \
+#define SCFA_BUCKET_CASE(HALF)                                                                         \
+  case HALF:                                                                                           \
+    if (dtype == SCFA_BF16)                                                                            \
+      bucket_launch<uint16_t, HALF>(grid, stream, x, x2, R, T, H, bucket, bucket2, counts, counts2, keep, \
+                                    keep2);                                                            \
+    else                                                                                               \
+      bucket_launch<float, HALF>(grid, stream, x, x2, R, T, H, bucket, bucket2, counts, counts2, keep,    \
+                                 keep2);                                                               \
     break;
   switch (half) {
     SCFA_BUCKET_CASE(1)
@@ -1115,20 +1129,23 @@ static int launch_hash_bucket(int dtype, int nx, const void* x, const void* x2, 
 
 int scfa_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb, int32_t* bucket,
                      hipStream_t stream) {
-  return launch_hash_bucket(dtype, 1, x, nullptr, R, B, T, H, D, nb, bucket, nullptr, nullptr, nullptr, stream);
+  return launch_hash_bucket(dtype, 1, x, nullptr, R, B, T, H, D, nb, bucket, nullptr, nullptr, nullptr, nullptr,
+                            nullptr, stream);
 }
 
 int scfa_hash_bucket_counts(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb,
                             int32_t* bucket, int32_t* chunk_counts, hipStream_t stream) {
   if (!chunk_counts) return SCFA_ERR_INVALID;
-  return launch_hash_bucket(dtype, 1, x, nullptr, R, B, T, H, D, nb, bucket, nullptr, chunk_counts, nullptr, stream);
+  return launch_hash_bucket(dtype, 1, x, nullptr, R, B, T, H, D, nb, bucket, nullptr, chunk_counts, nullptr, nullptr,
+                            nullptr, stream);
 }
 
-int scfa_hash_bucket_qk(int dtype, const void* q, const void* k, const float* R, int B, int T, int H, int D, int nb,
-                        int32_t* bucket_q, int32_t* bucket_k, int32_t* counts_q, int32_t* counts_k,
-                        hipStream_t stream) {
+int scfa_hash_bucket_qk(int dtype, const void* q, const void* k, const float* R, const uint8_t* keep_q,
+                        const uint8_t* keep_k, int B, int T, int H, int D, int nb, int32_t* bucket_q, int32_t* bucket_k,
+                        int32_t* counts_q, int32_t* counts_k, hipStream_t stream) {
   if (!counts_q || !counts_k) return SCFA_ERR_INVALID;
-  return launch_hash_bucket(dtype, 2, q, k, R, B, T, H, D, nb, bucket_q, bucket_k, counts_q, counts_k, stream);
+  return launch_hash_bucket(dtype, 2, q, k, R, B, T, H, D, nb, bucket_q, bucket_k, counts_q, counts_k, keep_q, keep_k,
+                            stream);
 }
 
 size_t scfa_hash_sort_workspace_bytes(int B, int H, int T, int nb) {

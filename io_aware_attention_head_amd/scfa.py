@@ -49,7 +49,7 @@ _SIGS = {
     "scfa_hash_segments": (_i, [_vp, _vp, _i, _i, _i, _i, _i, ctypes.c_int32, _i, _vp, _vp, _vp, _vp, _vp]),
     "scfa_hash_layout": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_hash_bucket_counts": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
-    "scfa_hash_bucket_qk": (_i, [_i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "scfa_hash_bucket_qk": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "scfa_hash_layout_qk": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i] + [_vp] * 17),
     "scfa_fwd_table": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]),
     "scfa_bwd_table": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
@@ -169,13 +169,18 @@ def scfa_hash_bucket_counts(x, R, nb, bucket, chunk_counts, stream=None):
                                          _stream(stream, x)), "scfa_hash_bucket_counts")
 
 
-def scfa_hash_bucket_qk(q, k, R, nb, bucket_q, bucket_k, counts_q, counts_k, stream=None):
-    """scfa_hash_bucket_counts of queries and keys in one launch."""
+def scfa_hash_bucket_qk(q, k, R, nb, bucket_q, bucket_k, counts_q, counts_k, stream=None, keep_q=None, keep_k=None):
+    """scfa_hash_bucket_counts of queries and keys in one launch; with keep
+    masks, dropped queries take bucket nb and dropped keys bucket nb + 1
+    (chunk counts then have nb + 2 buckets)."""
     if q.shape != k.shape or q.dtype != k.dtype:
         raise ScfaError("queries and keys must have the same shape and dtype")
+    if (keep_q is None) != (keep_k is None):
+        raise ScfaError("give both keep masks or neither")
     B, T, H, D = q.shape
-    _check(lib().scfa_hash_bucket_qk(_dt(q), _p(q), _p(k), _p(R), B, T, H, D, nb, _p(bucket_q), _p(bucket_k),
-                                     _p(counts_q), _p(counts_k), _stream(stream, q)), "scfa_hash_bucket_qk")
+    _check(lib().scfa_hash_bucket_qk(_dt(q), _p(q), _p(k), _p(R), _p(keep_q), _p(keep_k), B, T, H, D, nb,
+                                     _p(bucket_q), _p(bucket_k), _p(counts_q), _p(counts_k), _stream(stream, q)),
+           "scfa_hash_bucket_qk")
 
 
 def scfa_hash_sort_workspace_bytes(B, H, T, nb) -> int:
@@ -408,26 +413,34 @@ def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, rows: bool = F
                     extra={"count_q": cq, "count_k": ck, "max_q": mq, "max_k": mk, "dev_err": dev_err})
 
 
-def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None) -> Prepared:
+def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None, keep_q=None, keep_k=None) -> Prepared:
     """Hash-sparse preprocessing: LSH buckets of Q and K, stable counting sort
     per head and (aligned=True) the bucket-aligned layout in one launch per
-    side (query buckets
-    start at multiples of the query tile, key buckets at multiples of the key
-    tile). The operands stay in original order (gathered on load)."""
+    side (query buckets start at multiples of the query tile, key buckets at
+    multiples of the key tile). The operands stay in original order (gathered
+    on load). With keep masks (hashing combined with within-bucket dropping)
+    the buckets come from the two-side launch, dropped queries in bucket nb and
+    dropped keys in bucket nb + 1, and the sort has nb + 2 buckets."""
     B, T, H, D = q.shape
     dev = q
     i32 = torch.int32
     Tp = pad_rows(T)
+    nbs = nb if keep_q is None and keep_k is None else nb + 2  # buckets of the sort
     bq, bk = _empty((B, H, T), i32, dev), _empty((B, H, T), i32, dev)
-    cq, ck = _empty(chunk_count_shape(B, H, T, nb), i32, dev), _empty(chunk_count_shape(B, H, T, nb), i32, dev)
-    scfa_hash_bucket_counts(q, R, nb, bq, cq, stream)
-    scfa_hash_bucket_counts(k, R, nb, bk, ck, stream)
+    cq, ck = _empty(chunk_count_shape(B, H, T, nbs), i32, dev), _empty(chunk_count_shape(B, H, T, nbs), i32, dev)
+    if nbs == nb:
+        scfa_hash_bucket_counts(q, R, nb, bq, cq, stream)
+        scfa_hash_bucket_counts(k, R, nb, bk, ck, stream)
+    else:
+        scfa_hash_bucket_qk(q, k, R, nb, bq, bk, cq, ck, stream, keep_q, keep_k)
+    nb = nbs
     dev_err = torch.zeros((1,), dtype=i32, device=q.device)
     perm_q, perm_k = _empty((B, H, Tp), i32, dev), _empty((B, H, Tp), i32, dev)
     bs_q, bs_k = _empty((B, H, Tp), i32, dev), _empty((B, H, Tp), i32, dev)
     offq, offk = _empty((B, H, nb + 1), i32, dev), _empty((B, H, nb + 1), i32, dev)
-    extra = {"bucket_q": bq, "bucket_k": bk, "chunk_counts_q": cq, "chunk_counts_k": ck, "perm_q": perm_q, "perm_k": perm_k, "sorted_bkt_q": bs_q,
-             "sorted_bkt_k": bs_k, "offsets_q": offq, "offsets_k": offk, "dev_err": dev_err}
+    extra = {"bucket_q": bq, "bucket_k": bk, "chunk_counts_q": cq, "chunk_counts_k": ck, "perm_q": perm_q,
+             "perm_k": perm_k, "sorted_bkt_q": bs_q, "sorted_bkt_k": bs_k, "offsets_q": offq, "offsets_k": offk,
+             "dev_err": dev_err, "sort_buckets": nb}
     if aligned:
         Tq = scfa_hash_segment_rows(T, nb, SCFA_TILE_M)
         Tk = scfa_hash_segment_rows(T, nb, SCFA_TILE_N)
@@ -540,6 +553,9 @@ class Plan:
     """Preallocated pipeline for one shape and mode.
 
     mode "hash": bucket -> sort -> bucket-aligned layout -> tables -> forward.
+    mode "hash_drop": hash with the keep masks of the inputs as well (hashing
+                 combined with within-bucket dropping: dropped queries and
+                 keys take buckets nb and nb + 1, which match nothing).
     mode "qk":   count -> compact (index arrays) -> tables -> forward, with a
                  fixed compacted length Tc (default: pad_rows(T), which always
                  fits).
@@ -551,9 +567,15 @@ class Plan:
 
     def __init__(self, mode, B, H, T, D=64, dtype=torch.bfloat16, nb=16, Tc=None, out_dtype=torch.float32,
                  device="cuda", scale=None):
+        self.drop = mode == "hash_drop"
+        if self.drop:
+            mode = "hash"
+            if nb > 62:
+                raise ScfaError("hash_drop supports nb <= 62")
         if mode not in MODE_IDS:
             raise ScfaError(f"unknown mode {mode}")
         self.mode, self.B, self.H, self.T, self.D, self.nb = mode, B, H, T, D, nb
+        self.nbs = nb + 2 if self.drop else nb  # buckets of the sort and layout
         self.dtype, self.out_dtype = dtype, out_dtype
         self.scale = 1.0 / math.sqrt(D) if scale is None else scale
         d = torch.device(device)
@@ -569,8 +591,8 @@ class Plan:
             self.mx = [e((1,)), e((1,))]
             self.choff = [e((B, H, nC)), e((B, H, nC))]
         elif mode == "hash":
-            self.Tq = scfa_hash_segment_rows(T, nb, SCFA_TILE_M)
-            self.Tk = scfa_hash_segment_rows(T, nb, SCFA_TILE_N)
+            self.Tq = scfa_hash_segment_rows(T, self.nbs, SCFA_TILE_M)
+            self.Tk = scfa_hash_segment_rows(T, self.nbs, SCFA_TILE_N)
         else:
             self.Tq = self.Tk = pad_rows(T)
         TqP, TkP = pad_rows(self.Tq), pad_rows(self.Tk)
@@ -584,10 +606,11 @@ class Plan:
             self.bq, self.bk = e((B, H, T)), e((B, H, T))
             self.perm_q, self.perm_k = e((B, H, Tp)), e((B, H, Tp))
             self.bs_q, self.bs_k = e((B, H, Tp)), e((B, H, Tp))
-            self.offq, self.offk = e((B, H, nb + 1)), e((B, H, nb + 1))
-            self.segq, self.segk = e((B, H, nb + 1)), e((B, H, nb + 1))
+            nbs = self.nbs
+            self.offq, self.offk = e((B, H, nbs + 1)), e((B, H, nbs + 1))
+            self.segq, self.segk = e((B, H, nbs + 1)), e((B, H, nbs + 1))
             self.q_bkt, self.k_bkt = e((B, H, TqP)), e((B, H, TkP))
-            self.cq, self.ck = e(chunk_count_shape(B, H, T, nb)), e(chunk_count_shape(B, H, T, nb))
+            self.cq, self.ck = e(chunk_count_shape(B, H, T, nbs)), e(chunk_count_shape(B, H, T, nbs))
         if mode == "dense":
             ar = torch.arange(TqP, dtype=i32, device=d)
             self.q_idx.copy_(torch.where(ar < T, ar, torch.full_like(ar, SCFA_Q_PAD)).expand(B, H, TqP))
@@ -603,15 +626,19 @@ class Plan:
         self._bws = None
 
     # -- stages ---------------------------------------------------------------
-    def bucket(self, q, k, R, stream=None):
-        """LSH buckets and the chunk counts of the sort (queries and keys in one launch)."""
-        scfa_hash_bucket_qk(q, k, R, self.nb, self.bq, self.bk, self.cq, self.ck, stream)
+    def bucket(self, q, k, R, stream=None, keep_q=None, keep_k=None):
+        """LSH buckets and the chunk counts of the sort (queries and keys in
+        one launch); the keep masks are required in hash_drop mode."""
+        if self.drop and (keep_q is None or keep_k is None):
+            raise ScfaError("hash_drop needs the keep masks")
+        scfa_hash_bucket_qk(q, k, R, self.nb, self.bq, self.bk, self.cq, self.ck, stream,
+                            keep_q if self.drop else None, keep_k if self.drop else None)
 
     def sort(self, stream=None):
         """Stable sort by bucket, the bucket-aligned layout and its tile
         statistics (both sides in one launch)."""
         t = self.tab
-        scfa_hash_layout_qk(self.bq, self.bk, self.cq, self.ck, self.nb, self.perm_q, self.perm_k, self.bs_q, self.bs_k,
+        scfa_hash_layout_qk(self.bq, self.bk, self.cq, self.ck, self.nbs, self.perm_q, self.perm_k, self.bs_q, self.bs_k,
                             self.offq, self.offk, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.segq, self.segk,
                             self.dev_err, t.qstats, t.kstats, t.tiles, stream)
 
@@ -663,7 +690,10 @@ class Plan:
     def prepare(self, x: dict, stream=None):
         """All preprocessing stages for inputs x (q, k, v, keep_q, keep_k, R)."""
         if self.mode == "hash":
-            self.bucket(x["q"], x["k"], x["R"], stream)
+            if self.drop:
+                self.bucket(x["q"], x["k"], x["R"], stream, x["keep_q"], x["keep_k"])
+            else:
+                self.bucket(x["q"], x["k"], x["R"], stream)
             self.sort(stream)
         elif self.mode == "qk":
             self.compact(x["q"], x["k"], x["keep_q"], x["keep_k"], stream)

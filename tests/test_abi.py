@@ -101,11 +101,16 @@ def test_invalid_arguments_rejected_without_gpu():
                               null) == scfa.SCFA_ERR_UNSUPPORTED
     assert L.scfa_hash_bucket_counts(0, dummy, dummy, 1, 8, 1, 64, 16, dummy, null, null) == scfa.SCFA_ERR_INVALID
     # two-side entry points: missing counts, NULL key side, rows below T, nb above 64
-    assert L.scfa_hash_bucket_qk(0, dummy, dummy, dummy, 1, 8, 1, 64, 16, dummy, dummy, dummy, null,
+    assert L.scfa_hash_bucket_qk(0, dummy, dummy, dummy, null, null, 1, 8, 1, 64, 16, dummy, dummy, dummy, null,
                                  null) == scfa.SCFA_ERR_INVALID
-    assert L.scfa_hash_bucket_qk(0, dummy, null, dummy, 1, 8, 1, 64, 16, dummy, dummy, dummy, dummy,
+    assert L.scfa_hash_bucket_qk(0, dummy, null, dummy, null, null, 1, 8, 1, 64, 16, dummy, dummy, dummy, dummy,
                                  null) == scfa.SCFA_ERR_INVALID
-    assert L.scfa_hash_bucket_qk(0, dummy, dummy, dummy, 1, 8, 1, 32, 16, dummy, dummy, dummy, dummy,
+    assert L.scfa_hash_bucket_qk(0, dummy, dummy, dummy, null, null, 1, 8, 1, 32, 16, dummy, dummy, dummy, dummy,
+                                 null) == scfa.SCFA_ERR_UNSUPPORTED
+    # keep masks: both or neither; nb + 2 sort buckets must fit 64
+    assert L.scfa_hash_bucket_qk(0, dummy, dummy, dummy, dummy, null, 1, 8, 1, 64, 16, dummy, dummy, dummy, dummy,
+                                 null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_hash_bucket_qk(0, dummy, dummy, dummy, dummy, dummy, 1, 8, 1, 64, 64, dummy, dummy, dummy, dummy,
                                  null) == scfa.SCFA_ERR_UNSUPPORTED
     qk_out = [dummy] * 12 + [null] * 3 + [dummy]  # layouts, no statistics, dev_err
     assert L.scfa_hash_layout_qk(dummy, dummy, dummy, dummy, 1, 1, 300, 16, 256, 384, *qk_out,
@@ -136,6 +141,8 @@ def test_python_binding_rejects_host_tensors():
         scfa.scfa_gather(x, torch.zeros(1, 1, 128, dtype=torch.int32), scfa.SCFA_ROWS, torch.zeros(1, 1, 128, 64))
     with pytest.raises(scfa.ScfaError):  # queries and keys of different shapes
         scfa.scfa_hash_bucket_qk(x, torch.zeros(1, 9, 1, 64), torch.zeros(1, 64, 8), 16, *[None] * 4)
+    with pytest.raises(scfa.ScfaError):  # one keep mask without the other
+        scfa.scfa_hash_bucket_qk(x, x, torch.zeros(1, 64, 8), 16, *[None] * 4, keep_q=torch.ones(1, 8, 1))
 
 
 def test_header_constants_match_binding():

@@ -1,0 +1,129 @@
+"""GPU parity of hashing combined with within-bucket dropping (the
+explainer's follow-up mask: a pair is visible iff both tokens share a bucket,
+both are kept and the key does not come after the query) against the float64
+oracle, through the C ABI. Dropped queries take bucket nb and dropped keys
+bucket nb + 1, so the sort, layout, tables, attention and backward are the
+hash path's own."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import io_aware_attention_head_amd.scfa as scfa
+from io_aware_attention_head_amd.inputs import WORKLOADS, make_inputs, small
+from gpu_util import TOL_GRAD, announce, check_fwd, f64, need_gpu, oracle_buckets, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    small("hash", 2, 3, 1000, nb=16, keep_p=0.6, seed=101, grad=True),
+    small("hash", 1, 2, 513, dtype="f32", nb=4, keep_p=0.5, seed=102),
+    small("hash", 1, 2, 300, nb=2, keep_p=0.3, seed=103, grad=True),
+    small("hash", 1, 3, 2000, nb=48, keep_p=0.7, seed=104),
+]
+
+
+def _prepare(w, x):
+    g = to_dev(x)
+    pre = scfa.prepare_hash(g["q"], g["k"], g["v"], g["R"], w.nb, keep_q=g["keep_q"], keep_k=g["keep_k"])
+    torch.cuda.synchronize()
+    return g, pre
+
+
+def _oracle_fwd(w, x, rows=None, heads=None):
+    bq, bk = oracle_buckets(w, x)
+    return oracle.attention_fwd("hash", f64(x["q"]), f64(x["k"]), f64(x["v"]), x["keep_q"].numpy(),
+                                x["keep_k"].numpy(), bq, bk, rows=rows, heads=heads)
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_hash_drop_buckets_and_forward(w):
+    """Buckets (the oracle's for kept tokens, nb / nb + 1 for dropped ones),
+    chunk counts over nb + 2 buckets, the visible-pair count and every output
+    row of the forward."""
+    need_gpu()
+    announce(f"hash+drop {w.name}")
+    x = make_inputs(w)
+    g, pre = _prepare(w, x)
+    assert int(pre.extra["dev_err"].item()) == 0
+    bq, bk = oracle_buckets(w, x)
+    kq = x["keep_q"].numpy().transpose(0, 2, 1) != 0  # (B, H, T)
+    kk = x["keep_k"].numpy().transpose(0, 2, 1) != 0
+    exp_q = np.where(kq, bq, w.nb)
+    exp_k = np.where(kk, bk, w.nb + 1)
+    assert np.array_equal(pre.extra["bucket_q"].cpu().numpy(), exp_q)
+    assert np.array_equal(pre.extra["bucket_k"].cpu().numpy(), exp_k)
+    for got, ref in ((pre.extra["chunk_counts_q"], exp_q), (pre.extra["chunk_counts_k"], exp_k)):
+        B, H, T = ref.shape
+        nC = (T + 255) // 256
+        cnt = np.zeros((B, H, nC, w.nb + 2), dtype=np.int32)
+        for c in range(nC):
+            for v in range(w.nb + 2):
+                cnt[:, :, c, v] = (ref[:, :, 256 * c:256 * (c + 1)] == v).sum(-1)
+        assert np.array_equal(got.cpu().numpy(), cnt)
+    tab = scfa.build_tables(pre)
+    O, lse = scfa.forward(pre, tab)
+    torch.cuda.synchronize()
+    Or, Lr = _oracle_fwd(w, x)
+    err, lerr = check_fwd(w, O, lse, Or, Lr)
+    print(f"{w.name}: max-abs {err:.2e}  lse {lerr:.2e}")
+    pairs = scfa.count_visible(pre).cpu().numpy()
+    ref = oracle.visible_pairs("hash", w.T, w.B, w.H, x["keep_q"].numpy(), x["keep_k"].numpy(), bq, bk)
+    assert np.array_equal(pairs, ref)
+    # dropped queries: zero rows, LSE -inf
+    Og, Lg = O.cpu().numpy(), lse.cpu().numpy()
+    assert np.isneginf(Lg[~kq]).all()
+    assert (Og.transpose(0, 2, 1, 3)[~kq] == 0).all()
+
+
+@pytest.mark.parametrize("w", [c for c in CASES if c.grad], ids=lambda w: w.name)
+def test_hash_drop_backward(w):
+    need_gpu()
+    announce(f"hash+drop bwd {w.name}")
+    x = make_inputs(w)
+    g, pre = _prepare(w, x)
+    tab = scfa.build_tables(pre)
+    O, lse = scfa.forward(pre, tab)
+    grads = scfa.backward(pre, tab, O, lse, g["dO"])
+    torch.cuda.synchronize()
+    bq, bk = oracle_buckets(w, x)
+    ref = oracle.attention_bwd("hash", f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["dO"]), x["keep_q"].numpy(),
+                               x["keep_k"].numpy(), bq, bk)
+    for name, got, r in zip(("dQ", "dK", "dV"), grads, ref):
+        gn = f64(got)
+        rel = float(np.linalg.norm(gn - r) / np.linalg.norm(r))
+        assert rel <= TOL_GRAD, f"{name} relative Frobenius error {rel:.3e}"
+    dropped_k = x["keep_k"].numpy() == 0  # (B, T, H)
+    assert (f64(grads[1])[dropped_k] == 0).all() and (f64(grads[2])[dropped_k] == 0).all()
+    assert (f64(grads[0])[x["keep_q"].numpy() == 0] == 0).all()
+
+
+def test_hash_drop_plan_full_size():
+    """The benchmark shape (B=2, H=12, T=16384, nb=16) with keep 0.7 through a
+    Plan in hash_drop mode, graph-captured: sampled rows of every head against
+    the oracle, the pair count, and bit-equal graph replays."""
+    need_gpu()
+    base = WORKLOADS["hash_bf16_t16384_nb16"]
+    w = small("hash", base.B, base.H, base.T, nb=base.nb, keep_p=0.7, seed=105)
+    announce("hash+drop plan full size")
+    x = make_inputs(w)
+    g = to_dev(x)
+    plan = scfa.Plan("hash_drop", w.B, w.H, w.T, w.D, torch.bfloat16, nb=w.nb)
+    plan.run(g)
+    torch.cuda.synchronize()
+    assert int(plan.dev_err.item()) == 0
+    O_ref, l_ref = plan.O.clone(), plan.lse.clone()
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([rng.choice(w.T, 160, replace=False), [0, w.T - 1]]))
+    Or, Lr = _oracle_fwd(w, x, rows=rows)
+    check_fwd(w, plan.O, plan.lse, Or, Lr, rows=rows)
+    bq, bk = oracle_buckets(w, x)
+    ref = oracle.visible_pairs("hash", w.T, w.B, w.H, x["keep_q"].numpy(), x["keep_k"].numpy(), bq, bk)
+    assert np.array_equal(plan.count_visible().cpu().numpy(), ref)
+    graph = plan.capture(g)
+    for _ in range(2):
+        plan.O.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.O, O_ref) and torch.equal(plan.lse, l_ref)
