@@ -42,8 +42,9 @@ def _case(mode, T, H=2, D=16, seed=0, keep_p=0.6, nb=4, B=1):
     return w, x, q, k, v, kq, kk, bq, bk
 
 
-def _brute_fwd(mode, q, k, v, kq, kk, bq, bk):
-    """Pairwise enumeration with Python scalars and math.exp."""
+def _brute_fwd(mode, q, k, v, kq, kk, bq, bk, strict=False):
+    """Pairwise enumeration with Python scalars and math.exp (strict: keys
+    j < i only)."""
     B, T, H, D = q.shape
     tau = 1.0 / math.sqrt(D)
     O = np.zeros_like(q)
@@ -52,7 +53,7 @@ def _brute_fwd(mode, q, k, v, kq, kk, bq, bk):
         for h in range(H):
             for i in range(T):
                 vis = []
-                for j in range(i + 1):
+                for j in range(i if strict else i + 1):
                     if mode in ("qk", "hash_keep") and not (kq[b, i, h] and kk[b, j, h]):
                         continue
                     if mode in ("hash", "hash_keep") and bq[b, h, i] != bk[b, h, j]:
@@ -285,9 +286,9 @@ def test_negative_control_strict_mask_is_caught(monkeypatch):
     _, _, q, k, v, kq, kk, bq, bk = _case("qk", 33, seed=15)
     orig = so._vis_rows
 
-    def strict(mode, rows, T, kq_, kk_, bq_, bk_):
-        vis = orig(mode, rows, T, kq_, kk_, bq_, bk_)
-        return vis & (np.arange(T)[None, :] < rows[:, None])  # '>' instead of '>='
+    def strict(mode, rows, T, kq_, kk_, bq_, bk_, strict_=False):
+        vis = orig(mode, rows, T, kq_, kk_, bq_, bk_, strict_)
+        return vis & (np.arange(T)[None, :] < rows[:, None])  # '>' planted where '>=' is asked for
 
     monkeypatch.setattr(so, "_vis_rows", strict)
     O, _ = so.attention_fwd("qk", q, k, v, kq, kk)
@@ -349,3 +350,60 @@ def test_hash_with_keep_dropped_rows_and_gradients_are_zero():
     dropped_k = kk == 0  # (B, T, H)
     assert (dK[dropped_k] == 0).all() and (dV[dropped_k] == 0).all()
     assert (dQ[kq == 0] == 0).all()
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash", "hash_keep"])
+@pytest.mark.parametrize("T,seed", [(1, 30), (9, 31), (40, 32)])
+def test_strict_matches_pairwise_brute_force(mode, T, seed):
+    """The explainer's '>' variant of the causal test (a key strictly before
+    the query) against pairwise enumeration over j < i."""
+    _, _, q, k, v, kq, kk, bq, bk = _case(mode, T, seed=seed)
+    O, L = oracle.attention_fwd(_omode(mode), q, k, v, *_keeps(mode, kq, kk), bq, bk, strict=True)
+    Ob, Lb = _brute_fwd(mode, q, k, v, kq, kk, bq, bk, strict=True)
+    np.testing.assert_allclose(O, Ob, atol=1e-12, rtol=0)
+    assert np.array_equal(np.isinf(L), np.isinf(Lb))
+    fin = np.isfinite(Lb)
+    np.testing.assert_allclose(L[fin], Lb[fin], atol=1e-12, rtol=0)
+    assert np.isneginf(L[:, :, 0]).all() and (O[:, 0] == 0).all()  # the first token sees nothing
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash"])
+def test_strict_equals_inclusive_on_shifted_sequence(mode):
+    """Query i strictly after key j is query i - 1 of the sequence whose
+    queries start one token later: strict(q, k, v)[1:] = causal(q[1:], k[:-1],
+    v[:-1]) with the keep masks / buckets shifted alike (forward and the
+    query gradient; keys and values of the last token get nothing)."""
+    _, x, q, k, v, kq, kk, bq, bk = _case(mode, 57, H=2, D=16, seed=33)
+    keeps = _keeps(mode, kq, kk)
+    O, L = oracle.attention_fwd(mode, q, k, v, *keeps, bq, bk, strict=True)
+    sk = (None, None) if keeps[0] is None else (kq[:, 1:], kk[:, :-1])
+    sb = (None, None) if bq is None else (bq[:, :, 1:], bk[:, :, :-1])
+    O2, L2 = oracle.attention_fwd(mode, q[:, 1:], k[:, :-1], v[:, :-1], *sk, *sb)
+    np.testing.assert_allclose(O[:, 1:], O2, atol=1e-13, rtol=0)
+    assert np.array_equal(np.isinf(L[:, :, 1:]), np.isinf(L2))
+    fin = np.isfinite(L2)
+    np.testing.assert_allclose(L[:, :, 1:][fin], L2[fin], atol=1e-13, rtol=0)
+    dO = _np64(x["dO"])
+    dQ, dK, dV = oracle.attention_bwd(mode, q, k, v, dO, *keeps, bq, bk, strict=True)
+    dQ2, dK2, dV2 = oracle.attention_bwd(mode, q[:, 1:], k[:, :-1], v[:, :-1], dO[:, 1:], *sk, *sb)
+    np.testing.assert_allclose(dQ[:, 1:], dQ2, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dK[:, :-1], dK2, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dV[:, :-1], dV2, atol=1e-12, rtol=0)
+    assert (dQ[:, 0] == 0).all() and (dK[:, -1] == 0).all() and (dV[:, -1] == 0).all()
+
+
+def test_strict_bwd_central_finite_differences():
+    _, x, q, k, v, kq, kk, bq, bk = _case("qk", 10, H=1, D=4, seed=34, keep_p=0.7)
+    dO = _np64(x["dO"])
+    grads = oracle.attention_bwd("qk", q, k, v, dO, kq, kk, strict=True)
+    eps = 1e-6
+    loss = lambda a: float((oracle.attention_fwd("qk", a[0], a[1], a[2], kq, kk, strict=True)[0] * dO).sum())  # noqa: E731
+    for which, g in zip(range(3), grads):
+        num = np.zeros_like(g)
+        for idx in np.ndindex(*g.shape):
+            a = [q.copy(), k.copy(), v.copy()]
+            a[which][idx] += eps
+            lp = loss(a)
+            a[which][idx] -= 2 * eps
+            num[idx] = (lp - loss(a)) / (2 * eps)
+        assert np.abs(num - g).max() <= 1e-6 * max(1.0, np.abs(num).max())
