@@ -62,6 +62,12 @@ extern "C" {
 #define SCFA_DENSE 0 /* causal attention, positions 0..T-1 */
 #define SCFA_QK 1    /* QK-drop: compacted keys/queries      */
 #define SCFA_HASH 2  /* hash-sparse: bucket-sorted           */
+/* Flag OR-ed into a mode (or passed as `flags`): strict causality, a key is
+ * visible only strictly before its query (k_pos < q_pos), the explainer's
+ * '>' variant of the causal test ("Design choice: >= vs >"); a query then
+ * never attends to itself. Every call of one forward/backward pass must
+ * agree on it (tables, attention, backward, pair count). */
+#define SCFA_STRICT 16
 
 #define SCFA_ROWS 0 /* (B, H, Tpad, D): one row per token           */
 #define SCFA_COLS 1 /* (B, H, D, Tpad): transposed, one row per dim */
@@ -285,7 +291,7 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
 /* The backward table alone, from the statistics and forward table of a
  * scfa_range_table call (nQt, nKt as there): the same bwd_tab.              */
 int scfa_bwd_table(const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, int B, int H, int nQt, int nKt,
-                   int32_t* bwd_tab, hipStream_t stream);
+                   int32_t* bwd_tab, int flags, hipStream_t stream);
 
 /* The forward range table from tile statistics: the second half of
  * scfa_range_table (same rules, same citation), for statistics that another
@@ -332,6 +338,8 @@ int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, con
  * key visible iff k_pos <= q_pos (QK), and same bucket (hash); scores are
  * scale * q.k. A query with no visible key -- and, in QK mode, a dropped
  * query -- gets O = 0 and LSE = -inf.
+ *  flags         0 or SCFA_STRICT (k_pos < q_pos; the tables must have been
+ *                built with the same flag).
  *  dtype_in      SCFA_BF16 / SCFA_F32 of q, k, v.
  *  dtype_out     SCFA_F32 / SCFA_BF16 of O.
  *  q, k, v       (B, T, H, D) the ORIGINAL, unpermuted tensors (D = 64).
@@ -355,7 +363,7 @@ int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, con
 int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v,
                        const int32_t* q_idx, const int32_t* k_idx, const int32_t* qstats, const int32_t* kstats,
                        const int32_t* fwd_tab, const int32_t* order, int B, int H, int T, int Tc, int D, float scale,
-                       void* O, float* lse, hipStream_t stream);
+                       int flags, void* O, float* lse, hipStream_t stream);
 
 /* Hash-sparse: as above, with the sorted (or bucket-aligned) index arrays
  * and
@@ -366,7 +374,7 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
 int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v,
                          const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
                          const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, const int32_t* order,
-                         int B, int H, int T, int Tq, int Tk, int D, float scale, void* O, float* lse,
+                         int B, int H, int T, int Tq, int Tk, int D, float scale, int flags, void* O, float* lse,
                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------

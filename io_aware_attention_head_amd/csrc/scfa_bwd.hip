@@ -78,6 +78,7 @@ struct BwdParams {
   int nQt, nKt;
   float c;      // scale * log2(e)
   float scale;  // score scale
+  int strict;   // 1: a key is visible only strictly before its query
 };
 
 // ---------------------------------------------------------------------------
@@ -203,9 +204,11 @@ struct WaveKeys {
   bool any, all;
 };
 
-__device__ inline WaveKeys wave_keys(int kpos, int kbkt, int T) {
+// st = 1 (strict causality): the extrema are of position + 1, the smallest
+// query position that sees the key.
+__device__ inline WaveKeys wave_keys(int kpos, int kbkt, int T, int st) {
   const bool real = kpos >= 0 && kpos < T;
-  int mn = real ? kpos : kInt32Max, mx = real ? kpos : kInt32Min;
+  int mn = real ? kpos + st : kInt32Max, mx = real ? kpos + st : kInt32Min;
   int mnb = real ? kbkt : kInt32Max, mxb = real ? kbkt : kInt32Min;
   int nreal = real ? 1 : 0;
 #pragma unroll
@@ -278,7 +281,10 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   const int krow = kt * BN + w * 16 + r16;  // this lane's key
   const int kpos = p.k_idx[kbase + krow];
   const int kbkt = HASH ? p.k_bkt[kbase + krow] : 0;
-  const WaveKeys wk = wave_keys(kpos, kbkt, p.T);
+  // the smallest query position that sees this key (kpos + 1 when strict):
+  // masks and tile tests compare queries against it
+  const int kcmp = kpos + p.strict;
+  const WaveKeys wk = wave_keys(kpos, kbkt, p.T, p.strict);
   bf16x8 Kb[2], Vb[2];
   {
     const size_t off = head0 + static_cast<size_t>(src_row(kpos, p.T)) * rstride;
@@ -332,7 +338,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   const int4 ks = p.kstats[static_cast<size_t>(bh) * p.nKt + kt];
   const int cend = CPT * rng.y;
   auto next_chunk = [&](int ci) {
-    while (ci < cend && qstat(ci / CPT).y < ks.x) ci = (ci / CPT + 1) * CPT;
+    while (ci < cend && qstat(ci / CPT).y < ks.x + p.strict) ci = (ci / CPT + 1) * CPT;
     return ci;
   };
 
@@ -380,10 +386,10 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
           const int qo = 8 * g + 4 * qb;
           const int4 qp4 = *reinterpret_cast<const int4*>(&qpos_s[s][qo]);
           f32x4 c;
-          c[0] = bias_if_ge(qp4.x, kpos);
-          c[1] = bias_if_ge(qp4.y, kpos);
-          c[2] = bias_if_ge(qp4.z, kpos);
-          c[3] = bias_if_ge(qp4.w, kpos);
+          c[0] = bias_if_ge(qp4.x, kcmp);
+          c[1] = bias_if_ge(qp4.y, kcmp);
+          c[2] = bias_if_ge(qp4.z, kcmp);
+          c[3] = bias_if_ge(qp4.w, kcmp);
           if (buckets) {
             const int4 qb4 = *reinterpret_cast<const int4*>(&qbkt_s[s][qo]);
             c[0] = keep_if_eq(c[0], qb4.x, kbkt);
@@ -448,14 +454,14 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
 }
 
 // Extrema of this wave's 32 keys (two blocks of 16; lane column r16 in each).
-__device__ inline WaveKeys wave_keys2(const int (&kpos)[2], const int (&kbkt)[2], int T) {
+__device__ inline WaveKeys wave_keys2(const int (&kpos)[2], const int (&kbkt)[2], int T, int st) {
   int mn = kInt32Max, mx = kInt32Min, mnb = kInt32Max, mxb = kInt32Min, nreal = 0;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const bool real = kpos[kb] >= 0 && kpos[kb] < T;
     if (real) {
-      mn = min(mn, kpos[kb]);
-      mx = max(mx, kpos[kb]);
+      mn = min(mn, kpos[kb] + st);
+      mx = max(mx, kpos[kb] + st);
       mnb = min(mnb, kbkt[kb]);
       mxb = max(mxb, kbkt[kb]);
       ++nreal;
@@ -540,7 +546,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     kpos[kb] = Ki[r];
     kbkt[kb] = HASH ? ((r < BN || has1) ? p.k_bkt[kbase + kt0 * BN + r] : 0) : 0;
   }
-  const WaveKeys wk = wave_keys2(kpos, kbkt, p.T);
+  const WaveKeys wk = wave_keys2(kpos, kbkt, p.T, p.strict);
+  // the smallest query position that sees each key (kpos + 1 when strict)
+  const int kcmp[2] = {kpos[0] + p.strict, kpos[1] + p.strict};
   bf16x8 Kb[2][2], Vb[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -598,7 +606,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int cend = CPT * hi;
   auto needed = [&](int t) {
     const int qy = qstat(t).y;
-    return (t >= rng0.x && t < rng0.y && qy >= ks0.x) || (t >= rng1.x && t < rng1.y && qy >= ks1.x);
+    return (t >= rng0.x && t < rng0.y && qy >= ks0.x + p.strict) ||
+           (t >= rng1.x && t < rng1.y && qy >= ks1.x + p.strict);
   };
   auto next_chunk = [&](int ci) {
     while (ci < cend && !needed(ci / CPT)) ci = (ci / CPT + 1) * CPT;
@@ -654,10 +663,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
             f32x4 c;
-            c[0] = bias_if_ge(qp4.x, kpos[kb]);
-            c[1] = bias_if_ge(qp4.y, kpos[kb]);
-            c[2] = bias_if_ge(qp4.z, kpos[kb]);
-            c[3] = bias_if_ge(qp4.w, kpos[kb]);
+            c[0] = bias_if_ge(qp4.x, kcmp[kb]);
+            c[1] = bias_if_ge(qp4.y, kcmp[kb]);
+            c[2] = bias_if_ge(qp4.z, kcmp[kb]);
+            c[3] = bias_if_ge(qp4.w, kcmp[kb]);
             if (buckets) {
               c[0] = keep_if_eq(c[0], qb4.x, kbkt[kb]);
               c[1] = keep_if_eq(c[1], qb4.y, kbkt[kb]);
@@ -798,7 +807,9 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
       Db[qb][ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.dO) + off + (ds * 32 + g * 8) * 2);
     }
   }
-  const WaveRows wr = wave_rows(qpos, qbkt);
+  const WaveRows wr = wave_rows(qpos, qbkt, p.strict);
+  // positions the masks compare keys against: the largest visible key position
+  const int qcmp[2] = {qpos[0] - p.strict, qpos[1] - p.strict};
   f32x4 dQa[4][2];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -837,7 +848,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   };
   auto next_tile = [&](int j) {
     if (HASH)
-      while (j < rng.y && kstat(j).x > qs.y) ++j;
+      while (j < rng.y && kstat(j).x + p.strict > qs.y) ++j;
     return j;
   };
 
@@ -879,7 +890,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) S[h2][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         } else {
-          mask_bias_half<HASH>(S, ks, wr, Kp[s], Kb[s], qpos, qbkt, g, kc);
+          mask_bias_half<HASH>(S, ks, wr, Kp[s], Kb[s], qcmp, qbkt, g, kc);
         }
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
@@ -972,6 +983,7 @@ using namespace scfa;
 extern "C" {
 
 size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D) {
+  mode &= ~SCFA_STRICT;
   if ((mode != SCFA_QK && mode != SCFA_HASH) || B < 1 || H < 1 || Tq < 1 || Tk < 1 || D != HD) return 0;
   size_t off[3];
   return ws_layout(B, H, pad_rows(Tq), off);
@@ -982,6 +994,8 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
              const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
              const void* dO, int B, int H, int T, int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV,
              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int strict = strict_of(mode);
+  mode &= ~SCFA_STRICT;
   if (mode != SCFA_QK && mode != SCFA_HASH) return SCFA_ERR_INVALID;
   if (!q || !k || !v || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !bwd_tab || !O || !lse || !dO || !dQ ||
       !dK || !dV || !workspace)
@@ -998,6 +1012,7 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
   if (workspace_bytes < ws_layout(B, H, TqP, off)) return SCFA_ERR_INVALID;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   BwdParams p{};
+  p.strict = strict;
   p.q = q;
   p.k = k;
   p.v = v;

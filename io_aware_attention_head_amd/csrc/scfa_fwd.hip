@@ -78,7 +78,8 @@ struct FwdParams {
   int TqPad;  // rows per head of the query-side index arrays (q_idx, q_bkt)
   int TkPad;  // rows per head of the key-side index arrays (k_idx, k_bkt)
   int nQt, nKt;
-  float c;  // scale * log2(e)
+  float c;     // scale * log2(e)
+  int strict;  // 1: a key is visible only strictly before its query
 };
 
 template <typename TOUT>
@@ -283,7 +284,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     qpos[qb] = p.q_idx[rowbase + row];
     qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
   }
-  const WaveRows wr = wave_rows(qpos, qbkt);
+  const WaveRows wr = wave_rows(qpos, qbkt, p.strict);
+  // positions the masks compare keys against: the largest visible key position
+  const int qcmp[2] = {qpos[0] - p.strict, qpos[1] - p.strict};
   bf16x8 Qb[2][2];  // [qb][ds]
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   // every tile of a QK range passes it)
   auto next_tile = [&](int j) {
     if (HASH)
-      while (j < rng.y && kstat(j).x > qs.y) ++j;
+      while (j < rng.y && kstat(j).x + p.strict > qs.y) ++j;
     return j;
   };
 
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
           for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         scores_bf16(S, Ks, Qb, r16, g);
       } else {
-        mask_bias<HASH>(S, ks, wr, Kp[s], Kb[s], qpos, qbkt, g);
+        mask_bias<HASH>(S, ks, wr, Kp[s], Kb[s], qcmp, qbkt, g);
         scores_bf16(S, Ks, Qb, r16, g);
       }
 
@@ -493,7 +496,9 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
     qpos[qb] = p.q_idx[rowbase + row];
     qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
   }
-  const WaveRows wr = wave_rows(qpos, qbkt);
+  const WaveRows wr = wave_rows(qpos, qbkt, p.strict);
+  // positions the masks compare keys against: the largest visible key position
+  const int qcmp[2] = {qpos[0] - p.strict, qpos[1] - p.strict};
   float Qf[2][16];  // [qb][t], d = 16g + t
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -522,7 +527,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
   const int32_t* kbg = HASH ? p.k_bkt + kbase : nullptr;
 
   for (int j = rng.x; j < rng.y; ++j) {
-    if (kst[j].x > qs.y) continue;  // causal extremum test (uniform)
+    if (kst[j].x + p.strict > qs.y) continue;  // causal extremum test (uniform)
     __syncthreads();  // previous tile no longer read
     // K and V rows of the tile (16 chunks of 16 bytes per row), through k_idx
 #pragma unroll
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
-      mask_bias<HASH>(S, kst[j], wr, Kp, Kb, qpos, qbkt, g);
+      mask_bias<HASH>(S, kst[j], wr, Kp, Kb, qcmp, qbkt, g);
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -652,8 +657,9 @@ extern "C" {
 int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v,
                        const int32_t* q_idx, const int32_t* k_idx, const int32_t* qstats, const int32_t* kstats,
                        const int32_t* fwd_tab, const int32_t* order, int B, int H, int T, int Tc, int D, float scale,
-                       void* O, float* lse, hipStream_t stream) {
+                       int flags, void* O, float* lse, hipStream_t stream) {
   if (!q || !k || !v || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !O || !lse) return SCFA_ERR_INVALID;
+  if (flags & ~SCFA_STRICT) return SCFA_ERR_INVALID;
   const int st = check_common(dtype_in, dtype_out, B, H, T, D, scale);
   if (st != SCFA_OK) return st;
   if (Tc < SCFA_ROW_ALIGN || Tc % SCFA_ROW_ALIGN) return SCFA_ERR_INVALID;
@@ -680,16 +686,18 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
   p.nQt = Tc / BM;
   p.nKt = Tc / BN;
   p.c = scale * 1.44269504088896340736f;
+  p.strict = strict_of(flags);
   return dispatch_fwd<false, true>(dtype_in, dtype_out, p, stream);
 }
 
 int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v,
                          const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
                          const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, const int32_t* order,
-                         int B, int H, int T, int Tq, int Tk, int D, float scale, void* O, float* lse,
+                         int B, int H, int T, int Tq, int Tk, int D, float scale, int flags, void* O, float* lse,
                          hipStream_t stream) {
   if (!q || !k || !v || !q_idx || !k_idx || !q_bkt || !k_bkt || !qstats || !kstats || !fwd_tab || !O || !lse)
     return SCFA_ERR_INVALID;
+  if (flags & ~SCFA_STRICT) return SCFA_ERR_INVALID;
   const int st = check_common(dtype_in, dtype_out, B, H, T, D, scale);
   if (st != SCFA_OK) return st;
   if (Tq < 1 || Tk < 1) return SCFA_ERR_INVALID;
@@ -716,6 +724,7 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
   p.nQt = p.TqPad / BM;
   p.nKt = p.TkPad / BN;
   p.c = scale * 1.44269504088896340736f;
+  p.strict = strict_of(flags);
   return dispatch_fwd<true, false>(dtype_in, dtype_out, p, stream);
 }
 

@@ -24,6 +24,9 @@ inline int pad_rows(int n) { return SCFA_PAD(n); }
 
 inline bool dtype_ok(int dt) { return dt == SCFA_BF16 || dt == SCFA_F32; }
 inline int dtype_size(int dt) { return dt == SCFA_BF16 ? 2 : 4; }
+// Offset added to key positions in every causal comparison: 1 for the strict
+// variant (a key strictly before its query), else 0.
+inline int strict_of(int mode_or_flags) { return (mode_or_flags & SCFA_STRICT) ? 1 : 0; }
 
 // Number of lanes below this one whose bit is set in `mask` (wave64).
 __device__ inline int lanes_below(uint64_t mask) {

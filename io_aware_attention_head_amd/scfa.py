@@ -23,6 +23,7 @@ SCFA_OK, SCFA_ERR_INVALID, SCFA_ERR_UNSUPPORTED, SCFA_ERR_HIP = 0, -1, -2, -3
 SCFA_DEVERR_COUNT_EXCEEDS_TC, SCFA_DEVERR_BUCKET_RANGE, SCFA_DEVERR_SEGMENT_OVERFLOW = 1, 2, 4
 SCFA_BF16, SCFA_F32 = 0, 1
 SCFA_DENSE, SCFA_QK, SCFA_HASH = 0, 1, 2
+SCFA_STRICT = 16  # flag: a key is visible only strictly before its query
 SCFA_ROWS, SCFA_COLS = 0, 1
 SCFA_Q_PAD, SCFA_K_PAD = -1, 1_000_000_000
 SCFA_ROW_ALIGN = 128
@@ -52,15 +53,15 @@ _SIGS = {
     "scfa_hash_bucket_qk": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "scfa_hash_layout_qk": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i] + [_vp] * 17),
     "scfa_fwd_table": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]),
-    "scfa_bwd_table": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "scfa_bwd_table": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _vp]),
     "scfa_gather": (_i, [_i, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "scfa_range_table": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_count_visible": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_work_order": (_i, [_vp, _i, _i, _i, _i, _vp, _vp]),
-    "scfa_qk_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp,
-                                _vp, _vp]),
+    "scfa_qk_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                                _vp, _vp, _vp]),
     "scfa_hash_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
-                                  _i, _f, _vp, _vp, _vp]),
+                                  _i, _f, _i, _vp, _vp, _vp]),
     "scfa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "scfa_bwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                       _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -259,10 +260,10 @@ def scfa_range_table(mode, q_idx, k_idx, q_bkt, k_bkt, B, H, Tq, Tk, Bm, Bn, qst
            "scfa_range_table")
 
 
-def scfa_bwd_table(qstats, kstats, fwd_tab, bwd_tab, stream=None):
+def scfa_bwd_table(qstats, kstats, fwd_tab, bwd_tab, stream=None, flags=0):
     B, H, nQt = fwd_tab.shape[:3]
     nKt = bwd_tab.shape[2]
-    _check(lib().scfa_bwd_table(_p(qstats), _p(kstats), _p(fwd_tab), B, H, nQt, nKt, _p(bwd_tab),
+    _check(lib().scfa_bwd_table(_p(qstats), _p(kstats), _p(fwd_tab), B, H, nQt, nKt, _p(bwd_tab), flags,
                                 _stream(stream, fwd_tab)), "scfa_bwd_table")
 
 
@@ -277,7 +278,7 @@ def scfa_work_order(tab, span, order, stream=None):
 
 
 def scfa_qk_sparse_fwd(q, k, v, q_idx, k_idx, qstats, kstats, fwd_tab, T, O, lse, scale=None, stream=None,
-                       order=None):
+                       order=None, flags=0):
     """q, k, v: original (B,T,H,D) tensors; q_idx, k_idx (B,H,Tc) compacted."""
     B, Tq_, H, D = q.shape
     if Tq_ != T:
@@ -285,12 +286,12 @@ def scfa_qk_sparse_fwd(q, k, v, q_idx, k_idx, qstats, kstats, fwd_tab, T, O, lse
     Tc = q_idx.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(lib().scfa_qk_sparse_fwd(_dt(q), _dt(O), _p(q), _p(k), _p(v), _p(q_idx), _p(k_idx), _p(qstats),
-                                    _p(kstats), _p(fwd_tab), _p(order), B, H, T, Tc, D, scale, _p(O), _p(lse),
+                                    _p(kstats), _p(fwd_tab), _p(order), B, H, T, Tc, D, scale, flags, _p(O), _p(lse),
                                     _stream(stream, q)), "scfa_qk_sparse_fwd")
 
 
 def scfa_hash_sparse_fwd(q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, T, O, lse, scale=None,
-                         stream=None, order=None, Tq=None, Tk=None):
+                         stream=None, order=None, Tq=None, Tk=None, flags=0):
     """q, k, v: original (B,T,H,D) tensors. Tq / Tk: query / key rows as
     passed to the range table (default: T)."""
     B, Tq_, H, D = q.shape
@@ -301,7 +302,7 @@ def scfa_hash_sparse_fwd(q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fw
     Tk = T if Tk is None else Tk
     _check(lib().scfa_hash_sparse_fwd(_dt(q), _dt(O), _p(q), _p(k), _p(v), _p(q_idx), _p(k_idx), _p(q_bkt),
                                       _p(k_bkt), _p(qstats), _p(kstats), _p(fwd_tab), _p(order), B, H, T, Tq, Tk, D,
-                                      scale, _p(O), _p(lse), _stream(stream, q)), "scfa_hash_sparse_fwd")
+                                      scale, flags, _p(O), _p(lse), _stream(stream, q)), "scfa_hash_sparse_fwd")
 
 
 def scfa_bwd_workspace_bytes(mode, B, H, Tq, Tk, D=64) -> int:
@@ -353,6 +354,7 @@ class Prepared:
     k: Optional[torch.Tensor] = None  # (B,H,pad(Tk),D) rows
     v_t: Optional[torch.Tensor] = None  # (B,H,D,pad(Tk)) transposed
     extra: dict = dataclasses.field(default_factory=dict)
+    strict: bool = False  # keys strictly before the query (SCFA_STRICT)
 
 
 def gather_operands(pre: Prepared, stream=None) -> Prepared:
@@ -388,7 +390,8 @@ def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
-def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, rows: bool = False, stream=None) -> Prepared:
+def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, rows: bool = False, stream=None,
+               strict: bool = False) -> Prepared:
     """QK-drop preprocessing: counts and the compacted index arrays (with
     rows=True also the compacted Q and K rows). Reads the max kept count back
     to the host once (to size Tc) unless Tc is given."""
@@ -410,10 +413,11 @@ def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, rows: bool = F
     scfa_qk_compact(q, keep_q, cq, oq, Tc, SCFA_Q_PAD, q_c, q_idx, dev_err, stream)
     scfa_qk_compact(k, keep_k, ck, ok, Tc, SCFA_K_PAD, k_c, k_idx, dev_err, stream)
     return Prepared("qk", B, H, T, D, Tc, Tc, q, k, v, q_idx, k_idx, q=q_c, k=k_c,
-                    extra={"count_q": cq, "count_k": ck, "max_q": mq, "max_k": mk, "dev_err": dev_err})
+                    extra={"count_q": cq, "count_k": ck, "max_q": mq, "max_k": mk, "dev_err": dev_err}, strict=strict)
 
 
-def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None, keep_q=None, keep_k=None) -> Prepared:
+def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None, keep_q=None, keep_k=None,
+                 strict: bool = False) -> Prepared:
     """Hash-sparse preprocessing: LSH buckets of Q and K, stable counting sort
     per head and (aligned=True) the bucket-aligned layout in one launch per
     side (query buckets start at multiples of the query tile, key buckets at
@@ -455,10 +459,10 @@ def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None, keep_q=
         scfa_hash_layout(bk, ck, nb, 0, SCFA_K_PAD, perm_k, bs_k, offk, dev_err=dev_err, stream=stream)
         Tq = Tk = T
         q_idx, k_idx, q_bkt, k_bkt = perm_q, perm_k, bs_q, bs_k
-    return Prepared("hash", B, H, T, D, Tq, Tk, q, k, v, q_idx, k_idx, q_bkt, k_bkt, extra=extra)
+    return Prepared("hash", B, H, T, D, Tq, Tk, q, k, v, q_idx, k_idx, q_bkt, k_bkt, extra=extra, strict=strict)
 
 
-def prepare_dense(q, k, v, stream=None) -> Prepared:
+def prepare_dense(q, k, v, stream=None, strict: bool = False) -> Prepared:
     """Dense causal attention on the same kernel: positions 0..T-1 for both
     queries and keys (the QK path with nothing dropped)."""
     B, T, H, D = q.shape
@@ -466,11 +470,15 @@ def prepare_dense(q, k, v, stream=None) -> Prepared:
     ar = torch.arange(Tp, dtype=torch.int32, device=q.device)
     q_idx = torch.where(ar < T, ar, torch.full_like(ar, SCFA_Q_PAD)).expand(B, H, Tp).contiguous()
     k_idx = torch.where(ar < T, ar, torch.full_like(ar, SCFA_K_PAD)).expand(B, H, Tp).contiguous()
-    return Prepared("dense", B, H, T, D, Tp, Tp, q, k, v, q_idx, k_idx)
+    return Prepared("dense", B, H, T, D, Tp, Tp, q, k, v, q_idx, k_idx, strict=strict)
 
 
 def _table_mode(mode: str) -> int:
     return SCFA_HASH if mode == "hash" else SCFA_QK
+
+
+def _flags(pre: "Prepared") -> int:
+    return SCFA_STRICT if pre.strict else 0
 
 
 def build_tables(pre: Prepared, Bm: int = SCFA_TILE_M, Bn: int = SCFA_TILE_N, stream=None) -> Tables:
@@ -483,8 +491,8 @@ def build_tables(pre: Prepared, Bm: int = SCFA_TILE_M, Bn: int = SCFA_TILE_N, st
     d = pre.q_idx
     t = Tables(_empty((B, H, nQt, 4), i32, d), _empty((B, H, nKt, 4), i32, d), _empty((B, H, nQt, 2), i32, d),
                _empty((B, H, nKt, 2), i32, d), _empty((B, H), i32, d), Bm, Bn)
-    scfa_range_table(_table_mode(pre.mode), pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, B, H, pre.Tq, pre.Tk, Bm, Bn,
-                     t.qstats, t.kstats, t.fwd, t.bwd, t.tiles, stream)
+    scfa_range_table(_table_mode(pre.mode) | _flags(pre), pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, B, H, pre.Tq,
+                     pre.Tk, Bm, Bn, t.qstats, t.kstats, t.fwd, t.bwd, t.tiles, stream)
     t.fwd_order = _empty((B * H * nQt,), i32, d)
     scfa_work_order(t.fwd, nKt, t.fwd_order, stream)
     return t
@@ -492,8 +500,8 @@ def build_tables(pre: Prepared, Bm: int = SCFA_TILE_M, Bn: int = SCFA_TILE_N, st
 
 def count_visible(pre: Prepared, stream=None) -> torch.Tensor:
     pairs = _empty((pre.B, pre.H), torch.int64, pre.q_idx)
-    scfa_count_visible(_table_mode(pre.mode), pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, pre.B, pre.H, pre.Tq, pre.Tk,
-                       pairs, stream)
+    scfa_count_visible(_table_mode(pre.mode) | _flags(pre), pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, pre.B, pre.H,
+                       pre.Tq, pre.Tk, pairs, stream)
     return pairs
 
 
@@ -507,10 +515,11 @@ def forward(pre: Prepared, tab: Tables, out_dtype=torch.float32, scale=None, O=N
         lse = _empty((B, H, T), torch.float32, pre.q_in)
     if pre.mode == "hash":
         scfa_hash_sparse_fwd(pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats,
-                             tab.fwd, T, O, lse, scale, stream, order=tab.fwd_order, Tq=pre.Tq, Tk=pre.Tk)
+                             tab.fwd, T, O, lse, scale, stream, order=tab.fwd_order, Tq=pre.Tq, Tk=pre.Tk,
+                             flags=_flags(pre))
     else:
         scfa_qk_sparse_fwd(pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx, tab.qstats, tab.kstats, tab.fwd, T, O, lse,
-                           scale, stream, order=tab.fwd_order)
+                           scale, stream, order=tab.fwd_order, flags=_flags(pre))
     return O, lse
 
 
@@ -524,7 +533,7 @@ def backward(pre: Prepared, tab: Tables, O, lse, dO, scale=None, grads=None, wor
     if workspace is None:
         workspace = _empty((scfa_bwd_workspace_bytes(mode, B, H, pre.Tq, pre.Tk, D),), torch.uint8, pre.q_in)
     dQ, dK, dV = grads
-    scfa_bwd(mode, pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats, tab.fwd,
+    scfa_bwd(mode | _flags(pre), pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats, tab.fwd,
              tab.bwd, O, lse, dO, T, pre.Tq, pre.Tk, dQ, dK, dV, workspace, scale, stream)
     return dQ, dK, dV
 
@@ -566,7 +575,7 @@ class Plan:
     """
 
     def __init__(self, mode, B, H, T, D=64, dtype=torch.bfloat16, nb=16, Tc=None, out_dtype=torch.float32,
-                 device="cuda", scale=None):
+                 device="cuda", scale=None, strict=False):
         self.drop = mode == "hash_drop"
         if self.drop:
             mode = "hash"
@@ -576,6 +585,8 @@ class Plan:
             raise ScfaError(f"unknown mode {mode}")
         self.mode, self.B, self.H, self.T, self.D, self.nb = mode, B, H, T, D, nb
         self.nbs = nb + 2 if self.drop else nb  # buckets of the sort and layout
+        self.strict = bool(strict)  # keys strictly before the query (SCFA_STRICT)
+        self.flags = SCFA_STRICT if self.strict else 0
         self.dtype, self.out_dtype = dtype, out_dtype
         self.scale = 1.0 / math.sqrt(D) if scale is None else scale
         d = torch.device(device)
@@ -657,10 +668,10 @@ class Plan:
         built by backward()."""
         t = self.tab
         if self.mode == "hash":  # the tile statistics come from the layout launch
-            scfa_fwd_table(SCFA_HASH, t.qstats, t.kstats, t.fwd, t.tiles, stream)
+            scfa_fwd_table(SCFA_HASH | self.flags, t.qstats, t.kstats, t.fwd, t.tiles, stream)
         else:
-            scfa_range_table(_table_mode(self.mode), self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H,
-                             self.Tq, self.Tk, t.Bm, t.Bn, t.qstats, t.kstats, t.fwd, None, t.tiles, stream)
+            scfa_range_table(_table_mode(self.mode) | self.flags, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B,
+                             self.H, self.Tq, self.Tk, t.Bm, t.Bn, t.qstats, t.kstats, t.fwd, None, t.tiles, stream)
         scfa_work_order(t.fwd, t.kstats.shape[2], t.fwd_order, stream)
 
     def forward(self, stream=None):
@@ -671,7 +682,7 @@ class Plan:
         the backward table, then the backward kernels."""
         if self.x is None:
             raise ScfaError("backward needs a prepared forward")
-        scfa_bwd_table(self.tab.qstats, self.tab.kstats, self.tab.fwd, self.tab.bwd, stream)
+        scfa_bwd_table(self.tab.qstats, self.tab.kstats, self.tab.fwd, self.tab.bwd, stream, self.flags)
         if self._grads is None:
             d = self.device
             self._grads = tuple(torch.empty((self.B, self.T, self.H, self.D), dtype=torch.float32, device=d)
@@ -683,8 +694,8 @@ class Plan:
         return backward(self.prepared(), self.tab, self.O, self.lse, dO, self.scale, self._grads, self._bws, stream)
 
     def count_visible(self, stream=None):
-        scfa_count_visible(_table_mode(self.mode), self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H,
-                           self.Tq, self.Tk, self.pairs, stream)
+        scfa_count_visible(_table_mode(self.mode) | self.flags, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B,
+                           self.H, self.Tq, self.Tk, self.pairs, stream)
         return self.pairs
 
     def prepare(self, x: dict, stream=None):
@@ -725,4 +736,4 @@ class Plan:
             raise ScfaError("call prepare() first")
         x = self.x
         return Prepared(self.mode, self.B, self.H, self.T, self.D, self.Tq, self.Tk, x["q"], x["k"], x["v"],
-                        self.q_idx, self.k_idx, self.q_bkt, self.k_bkt)
+                        self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, strict=self.strict)

@@ -71,17 +71,26 @@ def test_invalid_arguments_rejected_without_gpu():
                               null) == scfa.SCFA_ERR_INVALID
     # forward: bad scale, D, Tc (the launch order may be NULL)
     args = [0, 1] + [dummy] * 8 + [null]
-    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 64, ctypes.c_float(0.0), dummy, dummy, null) == scfa.SCFA_ERR_INVALID
-    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 128, ctypes.c_float(0.125), dummy, dummy,
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 64, ctypes.c_float(0.0), 0, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 128, ctypes.c_float(0.125), 0, dummy, dummy,
                                 null) == scfa.SCFA_ERR_UNSUPPORTED
-    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 120, 64, ctypes.c_float(0.125), dummy, dummy,
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 120, 64, ctypes.c_float(0.125), 0, dummy, dummy,
                                 null) == scfa.SCFA_ERR_INVALID
     # one batch entry's T x H x D block of 4 GiB or more (32-bit row offsets)
-    assert L.scfa_qk_sparse_fwd(*args, 1, 64, 1 << 20, 1 << 20, 64, ctypes.c_float(0.125), dummy, dummy,
+    assert L.scfa_qk_sparse_fwd(*args, 1, 64, 1 << 20, 1 << 20, 64, ctypes.c_float(0.125), 0, dummy, dummy,
                                 null) == scfa.SCFA_ERR_UNSUPPORTED
+    # flags other than SCFA_STRICT
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 64, ctypes.c_float(0.125), 4, dummy, dummy,
+                                null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_bwd_table(dummy, dummy, dummy, 1, 1, 2, 2, dummy, 3, null) == scfa.SCFA_ERR_INVALID
+    # a mode with the strict flag is accepted where a mode is (argument errors still caught)
+    assert L.scfa_range_table(2 | scfa.SCFA_STRICT, dummy, dummy, null, null, 1, 1, 8, 8, 128, 64, dummy, dummy,
+                              dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_range_table(7 | scfa.SCFA_STRICT, dummy, dummy, dummy, dummy, 1, 1, 8, 8, 128, 64, dummy, dummy,
+                              dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
     hargs = [0, 1] + [dummy] * 10
     # hash forward: a NULL table is rejected
-    assert L.scfa_hash_sparse_fwd(*hargs[:-1], null, null, 1, 1, 8, 8, 8, 64, ctypes.c_float(0.125), dummy, dummy,
+    assert L.scfa_hash_sparse_fwd(*hargs[:-1], null, null, 1, 1, 8, 8, 8, 64, ctypes.c_float(0.125), 0, dummy, dummy,
                                   null) == scfa.SCFA_ERR_INVALID
     # bucket-aligned layout: bad alignment, rows below T, size helper
     assert L.scfa_hash_segments(dummy, dummy, 1, 1, 100, 16, 48, -1, 128, dummy, dummy, dummy, null,
@@ -147,6 +156,6 @@ def test_python_binding_rejects_host_tensors():
 
 def test_header_constants_match_binding():
     txt = open(HEADER).read()
-    for name in ("SCFA_TILE_M", "SCFA_TILE_N", "SCFA_ROW_ALIGN", "SCFA_COUNT_CHUNK", "SCFA_K_PAD"):
+    for name in ("SCFA_TILE_M", "SCFA_TILE_N", "SCFA_ROW_ALIGN", "SCFA_COUNT_CHUNK", "SCFA_K_PAD", "SCFA_STRICT"):
         m = re.search(rf"#define {name} \(?(-?\d+)\)?", txt)
         assert m and int(m.group(1)) == getattr(scfa, name), name
