@@ -29,6 +29,9 @@ Readings of points the pages leave open (each one is also listed in the design doc):
   * strict=True (every attention function): the explainer's '>' variant of
     the causal test, a key strictly before the query; a query then never
     sees itself, and the first token of a sequence sees nothing.
+  * noncausal=True: no position test (bidirectional attention over the
+    kept / same-bucket tokens); a tile holds a visible pair iff it holds a
+    real key (position below the key pad).
   * Hashing combined with within-bucket dropping (the explainer's follow-up
     idea): in hash mode with keep masks a pair is visible iff both tokens
     share a bucket, both are kept and the key does not come after the query.
@@ -224,7 +227,8 @@ def tile_stats(pos: np.ndarray, bkt: Optional[np.ndarray], tile: int) -> np.ndar
 
 
 def range_tables(mode: str, q_idx: np.ndarray, k_idx: np.ndarray, q_bkt: Optional[np.ndarray],
-                 k_bkt: Optional[np.ndarray], Bm: int, Bn: int, strict: bool = False) -> dict:
+                 k_bkt: Optional[np.ndarray], Bm: int, Bn: int, strict: bool = False,
+                 noncausal: bool = False) -> dict:
     """Forward and backward tile ranges and the processed tile set.
 
     q_idx: (B, H, Tq), k_idx: (B, H, Tk) original positions (with pads);
@@ -254,7 +258,17 @@ def range_tables(mode: str, q_idx: np.ndarray, k_idx: np.ndarray, q_bkt: Optiona
     ks = tile_stats(k_idx, k_bkt if use_b else None, Bn)
     B, H, nQt, _ = qs.shape
     nKt = ks.shape[2]
-    sh = 1 if strict else 0  # key tile minimum + sh <= query tile maximum
+    sh = 1 if strict else 0
+
+    def reach(kmin, qmax):
+        """Tile-level position test. Causal: the key tile's smallest position
+        (+1 when strict) does not exceed the query tile's largest. Without
+        causality: the query tile holds a real query (largest position not
+        the pad -1) and the key tile a real key (smallest below the pad)."""
+        if noncausal:
+            return (kmin < K_PAD) & (qmax >= 0)
+        return kmin + sh <= qmax
+
     fwd = np.zeros((B, H, nQt, 2), dtype=np.int32)
     P = np.zeros((B, H, nQt, nKt), dtype=bool)
     for b in range(B):
@@ -266,7 +280,7 @@ def range_tables(mode: str, q_idx: np.ndarray, k_idx: np.ndarray, q_bkt: Optiona
                     # Algorithm 1: end = number of key tiles whose minimum
                     # position does not exceed the query tile's maximum.
                     start = 0
-                    end = int((kmin + sh <= qmax).sum())
+                    end = int(reach(kmin, qmax).sum())
                 else:
                     qminb, qmaxb = qs[b, h, i, 2], qs[b, h, i, 3]
                     kminb, kmaxb = ks[b, h, :, 2], ks[b, h, :, 3]
@@ -282,11 +296,11 @@ def range_tables(mode: str, q_idx: np.ndarray, k_idx: np.ndarray, q_bkt: Optiona
                     # that passes the causal extremum test.
                     end = start
                     for j in range(start, eh):
-                        if kmin[j] + sh <= qmax:
+                        if reach(kmin[j], qmax):
                             end = j + 1
                 fwd[b, h, i] = (start, end)
                 for j in range(start, end):
-                    if kmin[j] + sh <= qmax:
+                    if reach(kmin[j], qmax):
                         P[b, h, i, j] = True
     bwd = np.zeros((B, H, nKt, 2), dtype=np.int32)
     for b in range(B):
@@ -311,12 +325,18 @@ def range_tables(mode: str, q_idx: np.ndarray, k_idx: np.ndarray, q_bkt: Optiona
 # vector ("3.2 Big-Picture Architecture", item 4).
 # ---------------------------------------------------------------------------
 
-def _vis_rows(mode: str, rows: np.ndarray, T: int, kq, kk, bq, bk, strict: bool = False) -> np.ndarray:
+def _vis_rows(mode: str, rows: np.ndarray, T: int, kq, kk, bq, bk, strict: bool = False,
+              noncausal: bool = False) -> np.ndarray:
     """Visibility of query rows `rows` (original positions) against all keys
     of one head (strict: a key strictly before the query, the explainer's
-    '>' variant of the causal test). Returns (len(rows), T) bool."""
+    '>' variant of the causal test; noncausal: no position test at all, the
+    bidirectional attention the explainer mentions as an extension).
+    Returns (len(rows), T) bool."""
     j = np.arange(T)
-    vis = (j[None, :] < rows[:, None]) if strict else (j[None, :] <= rows[:, None])
+    if noncausal:
+        vis = np.ones((len(rows), T), dtype=bool)
+    else:
+        vis = (j[None, :] < rows[:, None]) if strict else (j[None, :] <= rows[:, None])
     if mode == "qk":
         vis &= (kq[rows] != 0)[:, None] & (kk != 0)[None, :]
     elif mode == "hash":
@@ -339,13 +359,15 @@ def _heads(B: int, H: int, heads):
 
 def attention_fwd(mode: str, q, k, v, keep_q=None, keep_k=None, bkt_q=None, bkt_k=None,
                   scale: Optional[float] = None, heads: Optional[Sequence[Tuple[int, int]]] = None,
-                  rows: Optional[np.ndarray] = None, block: int = 512, strict: bool = False):
+                  rows: Optional[np.ndarray] = None, block: int = 512, strict: bool = False,
+                  noncausal: bool = False):
     """Explicit masked-softmax causal attention in original token order.
 
     q, k, v: (B, T, H, D) float64. keep_q/keep_k: (B, T, H) (qk mode; in
     hash mode optional, for hashing combined with within-bucket dropping).
     bkt_q/bkt_k: (B, H, T) bucket ids (hash mode).
-    strict: keys strictly before the query (the explainer's '>' variant).
+    strict: keys strictly before the query (the explainer's '>' variant);
+    noncausal: no position test (bidirectional).
     heads: optional list of (b, h) to compute (others left at 0 / -inf).
     rows: optional query positions to compute (others left at 0 / -inf).
     Returns O (B, T, H, D) float64 and LSE (B, H, T) float64.
@@ -368,7 +390,7 @@ def attention_fwd(mode: str, q, k, v, keep_q=None, keep_k=None, bkt_q=None, bkt_
         Kh, Vh = k[b, :, h], v[b, :, h]
         for s0 in range(0, len(all_rows), block):
             r = all_rows[s0:s0 + block]
-            vis = _vis_rows(mode, r, T, kq, kk, bq, bk, strict)
+            vis = _vis_rows(mode, r, T, kq, kk, bq, bk, strict, noncausal)
             S = tau * (q[b, r, h] @ Kh.T)
             S = np.where(vis, S, NEG_INF)
             has = vis.any(axis=1)
@@ -385,7 +407,7 @@ def attention_fwd(mode: str, q, k, v, keep_q=None, keep_k=None, bkt_q=None, bkt_
 
 def attention_bwd(mode: str, q, k, v, dO, keep_q=None, keep_k=None, bkt_q=None, bkt_k=None,
                   scale: Optional[float] = None, heads: Optional[Sequence[Tuple[int, int]]] = None,
-                  block: int = 512, strict: bool = False):
+                  block: int = 512, strict: bool = False, noncausal: bool = False):
     """Gradients of L = sum(O * dO) w.r.t. the original-order q, k, v.
 
     With P_ij = exp(s_ij - LSE_i) on visible pairs (0 elsewhere):
@@ -406,7 +428,7 @@ def attention_bwd(mode: str, q, k, v, dO, keep_q=None, keep_k=None, bkt_q=None, 
     dV = np.zeros_like(v)
     for b, h in _heads(B, H, heads):
         O, LSE = attention_fwd(mode, q, k, v, keep_q, keep_k, bkt_q, bkt_k, tau, heads=[(b, h)], block=block,
-                               strict=strict)
+                               strict=strict, noncausal=noncausal)
         kq = None if keep_q is None else keep_q[b, :, h]
         kk = None if keep_k is None else keep_k[b, :, h]
         bq = None if bkt_q is None else bkt_q[b, h]
@@ -414,7 +436,7 @@ def attention_bwd(mode: str, q, k, v, dO, keep_q=None, keep_k=None, bkt_q=None, 
         Qh, Kh, Vh = q[b, :, h], k[b, :, h], v[b, :, h]
         for s0 in range(0, T, block):
             r = np.arange(s0, min(T, s0 + block))
-            vis = _vis_rows(mode, r, T, kq, kk, bq, bk, strict)
+            vis = _vis_rows(mode, r, T, kq, kk, bq, bk, strict, noncausal)
             lse = LSE[b, h, r]
             has = np.isfinite(lse)
             S = tau * (Qh[r] @ Kh.T)
@@ -455,18 +477,20 @@ def attention_rows(q, k, v, q_pos, k_pos, q_bkt=None, k_bkt=None, scale: Optiona
 
 
 def visible_pairs(mode: str, T: int, B: int, H: int, keep_q=None, keep_k=None, bkt_q=None, bkt_k=None,
-                  strict: bool = False) -> np.ndarray:
+                  strict: bool = False, noncausal: bool = False) -> np.ndarray:
     """Exact number of visible (query, key) pairs per (b, h). -> (B, H) int64."""
     out = np.zeros((B, H), dtype=np.int64)
     sh = 1 if strict else 0
 
-    def upto(c):  # counts over key positions <= i (strict: < i) from an inclusive cumsum
+    def upto(c):  # counts over key positions <= i (strict: < i; noncausal: all) from an inclusive cumsum
+        if noncausal:
+            return np.full_like(c, c[-1])
         return c if not strict else np.concatenate([[0], c[:-1]])
 
     for b in range(B):
         for h in range(H):
             if mode == "dense":
-                out[b, h] = T * (T + 1) // 2 - sh * T
+                out[b, h] = T * T if noncausal else T * (T + 1) // 2 - sh * T
             elif mode == "qk":
                 kk = (keep_k[b, :, h] != 0).astype(np.int64)
                 before = upto(np.cumsum(kk))  # kept keys at positions <= i (strict: < i)

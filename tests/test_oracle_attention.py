@@ -42,9 +42,9 @@ def _case(mode, T, H=2, D=16, seed=0, keep_p=0.6, nb=4, B=1):
     return w, x, q, k, v, kq, kk, bq, bk
 
 
-def _brute_fwd(mode, q, k, v, kq, kk, bq, bk, strict=False):
+def _brute_fwd(mode, q, k, v, kq, kk, bq, bk, strict=False, noncausal=False):
     """Pairwise enumeration with Python scalars and math.exp (strict: keys
-    j < i only)."""
+    j < i only; noncausal: every key j)."""
     B, T, H, D = q.shape
     tau = 1.0 / math.sqrt(D)
     O = np.zeros_like(q)
@@ -53,7 +53,7 @@ def _brute_fwd(mode, q, k, v, kq, kk, bq, bk, strict=False):
         for h in range(H):
             for i in range(T):
                 vis = []
-                for j in range(i if strict else i + 1):
+                for j in range(T if noncausal else (i if strict else i + 1)):
                     if mode in ("qk", "hash_keep") and not (kq[b, i, h] and kk[b, j, h]):
                         continue
                     if mode in ("hash", "hash_keep") and bq[b, h, i] != bk[b, h, j]:
@@ -286,8 +286,8 @@ def test_negative_control_strict_mask_is_caught(monkeypatch):
     _, _, q, k, v, kq, kk, bq, bk = _case("qk", 33, seed=15)
     orig = so._vis_rows
 
-    def strict(mode, rows, T, kq_, kk_, bq_, bk_, strict_=False):
-        vis = orig(mode, rows, T, kq_, kk_, bq_, bk_, strict_)
+    def strict(mode, rows, T, kq_, kk_, bq_, bk_, strict_=False, noncausal_=False):
+        vis = orig(mode, rows, T, kq_, kk_, bq_, bk_, strict_, noncausal_)
         return vis & (np.arange(T)[None, :] < rows[:, None])  # '>' planted where '>=' is asked for
 
     monkeypatch.setattr(so, "_vis_rows", strict)
@@ -398,6 +398,76 @@ def test_strict_bwd_central_finite_differences():
     grads = oracle.attention_bwd("qk", q, k, v, dO, kq, kk, strict=True)
     eps = 1e-6
     loss = lambda a: float((oracle.attention_fwd("qk", a[0], a[1], a[2], kq, kk, strict=True)[0] * dO).sum())  # noqa: E731
+    for which, g in zip(range(3), grads):
+        num = np.zeros_like(g)
+        for idx in np.ndindex(*g.shape):
+            a = [q.copy(), k.copy(), v.copy()]
+            a[which][idx] += eps
+            lp = loss(a)
+            a[which][idx] -= 2 * eps
+            num[idx] = (lp - loss(a)) / (2 * eps)
+        assert np.abs(num - g).max() <= 1e-6 * max(1.0, np.abs(num).max())
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash", "hash_keep"])
+@pytest.mark.parametrize("T,seed", [(1, 40), (9, 41), (40, 42)])
+def test_noncausal_matches_pairwise_brute_force(mode, T, seed):
+    """Bidirectional attention (no position test) against pairwise
+    enumeration over every key."""
+    _, _, q, k, v, kq, kk, bq, bk = _case(mode, T, seed=seed)
+    O, L = oracle.attention_fwd(_omode(mode), q, k, v, *_keeps(mode, kq, kk), bq, bk, noncausal=True)
+    Ob, Lb = _brute_fwd(mode, q, k, v, kq, kk, bq, bk, noncausal=True)
+    np.testing.assert_allclose(O, Ob, atol=1e-12, rtol=0)
+    assert np.array_equal(np.isinf(L), np.isinf(Lb))
+    fin = np.isfinite(Lb)
+    np.testing.assert_allclose(L[fin], Lb[fin], atol=1e-12, rtol=0)
+
+
+def test_noncausal_dense_equals_library_attention():
+    """Dense bidirectional attention is plain softmax(tau Q K^T) V: torch's
+    scaled_dot_product_attention without a mask, in float64 on the CPU."""
+    _, x, q, k, v, _, _, _, _ = _case("dense", 70, H=3, D=16, seed=43)
+    O, L = oracle.attention_fwd("dense", q, k, v, noncausal=True)
+    t = lambda a: torch.from_numpy(a).permute(0, 2, 1, 3)  # noqa: E731  (B, H, T, D)
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=False)
+    np.testing.assert_allclose(O, ref.permute(0, 2, 1, 3).numpy(), atol=1e-12, rtol=0)
+    s = torch.einsum("bhid,bhjd->bhij", t(q), t(k)) / math.sqrt(16)
+    np.testing.assert_allclose(L, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash"])
+def test_noncausal_is_permutation_equivariant(mode):
+    """Without a position test, reordering the tokens (q, k, v, keep bits and
+    buckets alike) reorders O, LSE and every gradient the same way; the
+    causal result has no such symmetry."""
+    _, x, q, k, v, kq, kk, bq, bk = _case(mode, 37, H=2, D=16, seed=44)
+    keeps = _keeps(mode, kq, kk)
+    dO = _np64(x["dO"])
+    perm = np.random.default_rng(45).permutation(37)
+    pk = (None, None) if keeps[0] is None else (kq[:, perm], kk[:, perm])
+    pb = (None, None) if bq is None else (bq[:, :, perm], bk[:, :, perm])
+    O, L = oracle.attention_fwd(mode, q, k, v, *keeps, bq, bk, noncausal=True)
+    O2, L2 = oracle.attention_fwd(mode, q[:, perm], k[:, perm], v[:, perm], *pk, *pb, noncausal=True)
+    np.testing.assert_allclose(O2, O[:, perm], atol=1e-13, rtol=0)
+    assert np.array_equal(np.isinf(L2), np.isinf(L[:, :, perm]))
+    fin = np.isfinite(L2)
+    np.testing.assert_allclose(L2[fin], L[:, :, perm][fin], atol=1e-13, rtol=0)
+    g = oracle.attention_bwd(mode, q, k, v, dO, *keeps, bq, bk, noncausal=True)
+    g2 = oracle.attention_bwd(mode, q[:, perm], k[:, perm], v[:, perm], dO[:, perm], *pk, *pb, noncausal=True)
+    for a, b in zip(g, g2):
+        np.testing.assert_allclose(b, a[:, perm], atol=1e-12, rtol=0)
+    Oc, _ = oracle.attention_fwd(mode, q[:, perm], k[:, perm], v[:, perm], *pk, *pb)
+    Oc0, _ = oracle.attention_fwd(mode, q, k, v, *keeps, bq, bk)
+    assert np.abs(Oc - Oc0[:, perm]).max() > 1e-3
+
+
+def test_noncausal_bwd_central_finite_differences():
+    _, x, q, k, v, kq, kk, bq, bk = _case("hash_keep", 10, H=1, D=4, seed=46, keep_p=0.8, nb=2)
+    dO = _np64(x["dO"])
+    grads = oracle.attention_bwd("hash", q, k, v, dO, kq, kk, bq, bk, noncausal=True)
+    eps = 1e-6
+    loss = lambda a: float((oracle.attention_fwd("hash", a[0], a[1], a[2], kq, kk, bq, bk,  # noqa: E731
+                                                 noncausal=True)[0] * dO).sum())
     for which, g in zip(range(3), grads):
         num = np.zeros_like(g)
         for idx in np.ndindex(*g.shape):

@@ -172,9 +172,9 @@ def test_gather_rows():
     assert (g[0, 1, 2] == 0).all() and (g[0, 2, 1] == x[0, 3, 2]).all()
 
 
-@pytest.mark.parametrize("strict", [False, True])
+@pytest.mark.parametrize("strict,noncausal", [(False, False), (True, False), (False, True)])
 @pytest.mark.parametrize("mode", ["dense", "qk", "hash", "hash_keep"])
-def test_visible_pairs_brute_force(mode, strict):
+def test_visible_pairs_brute_force(mode, strict, noncausal):
     omode = "hash" if mode == "hash_keep" else mode
     w = small(omode, 2, 2, 45, 16, keep_p=0.6, nb=4, seed=7)
     x = make_inputs(w)
@@ -185,12 +185,12 @@ def test_visible_pairs_brute_force(mode, strict):
         bq = oracle.hash_bucket(x["q"].double().numpy(), R, 4)
         bk = oracle.hash_bucket(x["k"].double().numpy(), R, 4)
     keeps = (kq, kk) if mode in ("qk", "hash_keep") else (None, None)
-    got = oracle.visible_pairs(omode, 45, 2, 2, *keeps, bq, bk, strict=strict)
+    got = oracle.visible_pairs(omode, 45, 2, 2, *keeps, bq, bk, strict=strict, noncausal=noncausal)
     for b in range(2):
         for h in range(2):
             n = 0
             for i in range(45):
-                for j in range(i if strict else i + 1):
+                for j in range(45 if noncausal else (i if strict else i + 1)):
                     if mode in ("qk", "hash_keep") and not (kq[b, i, h] and kk[b, j, h]):
                         continue
                     if omode == "hash" and bq[b, h, i] != bk[b, h, j]:
@@ -198,4 +198,6 @@ def test_visible_pairs_brute_force(mode, strict):
                     n += 1
             assert got[b, h] == n
     if mode == "dense":
-        assert (got == (45 * 44 // 2 if strict else 45 * 46 // 2)).all()
+        assert (got == (45 * 45 if noncausal else 45 * 44 // 2 if strict else 45 * 46 // 2)).all()
+    if mode == "qk" and noncausal:  # every kept query sees every kept key
+        assert (got == (kq != 0).sum(axis=1) * (kk != 0).sum(axis=1)).all()

@@ -34,14 +34,19 @@ def _sorted_domain(mode, T, seed, keep_p=0.6, nb=16, B=1, H=2, Tc=None):
     return qp, kp, qb, kb
 
 
-def _tiles_with_visible_pair(qi, ki, qb, kb, Bm, Bn, strict=False):
+def _tiles_with_visible_pair(qi, ki, qb, kb, Bm, Bn, strict=False, noncausal=False):
     B, H, Tq = qi.shape
     Tk = ki.shape[-1]
     nQt, nKt = -(-Tq // Bm), -(-Tk // Bn)
     out = np.zeros((B, H, nQt, nKt), dtype=bool)
     for b in range(B):
         for h in range(H):
-            before = (ki[b, h][None, :] < qi[b, h][:, None]) if strict else (ki[b, h][None, :] <= qi[b, h][:, None])
+            if noncausal:
+                before = np.broadcast_to(ki[b, h][None, :] != oracle.K_PAD, (len(qi[b, h]), Tk))
+            elif strict:
+                before = ki[b, h][None, :] < qi[b, h][:, None]
+            else:
+                before = ki[b, h][None, :] <= qi[b, h][:, None]
             vis = before & (qi[b, h][:, None] >= 0)
             if qb is not None:
                 vis &= qb[b, h][:, None] == kb[b, h][None, :]
@@ -51,14 +56,14 @@ def _tiles_with_visible_pair(qi, ki, qb, kb, Bm, Bn, strict=False):
     return out
 
 
-@pytest.mark.parametrize("strict", [False, True])
+@pytest.mark.parametrize("strict,noncausal", [(False, False), (True, False), (False, True)])
 @pytest.mark.parametrize("Bm,Bn", [(64, 64), (64, 128), (128, 64), (128, 128), (16, 32)])
 @pytest.mark.parametrize("mode,T,seed", [("dense", 300, 0), ("qk", 512, 1), ("qk", 333, 2), ("hash", 700, 3),
                                          ("hash", 129, 4)])
-def test_coverage_and_exactness(mode, T, seed, Bm, Bn, strict):
+def test_coverage_and_exactness(mode, T, seed, Bm, Bn, strict, noncausal):
     qi, ki, qb, kb = _sorted_domain(mode, T, seed)
-    tab = oracle.range_tables(mode, qi, ki, qb, kb, Bm, Bn, strict=strict)
-    need = _tiles_with_visible_pair(qi, ki, qb, kb, Bm, Bn, strict)
+    tab = oracle.range_tables(mode, qi, ki, qb, kb, Bm, Bn, strict=strict, noncausal=noncausal)
+    need = _tiles_with_visible_pair(qi, ki, qb, kb, Bm, Bn, strict, noncausal)
     P = tab["P"]
     assert not (need & ~P).any(), "a tile holding a visible pair is skipped"
     if mode in ("qk", "dense"):
