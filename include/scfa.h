@@ -68,6 +68,15 @@ extern "C" {
  * never attends to itself. Every call of one forward/backward pass must
  * agree on it (tables, attention, backward, pair count). */
 #define SCFA_STRICT 16
+/* Flag OR-ed into a mode (or passed as `flags`): no causal test, every kept
+ * (QK) or same-bucket (hash) key is visible to every query -- bidirectional
+ * attention, which the explainer names as untested ("Critical Assessment",
+ * "Additional Weaknesses and Missing Experiments": causal attention only).
+ * Every original position must lie below 2^28 (the attention entry points
+ * check T; the table and pair-count calls rely on the caller). It excludes
+ * SCFA_STRICT (SCFA_ERR_INVALID when both are set), and every call of one
+ * pass must agree on it, as for SCFA_STRICT. */
+#define SCFA_NONCAUSAL 32
 
 #define SCFA_ROWS 0 /* (B, H, Tpad, D): one row per token           */
 #define SCFA_COLS 1 /* (B, H, D, Tpad): transposed, one row per dim */
@@ -267,10 +276,12 @@ int scfa_gather(int dtype, int layout, const void* x, const int32_t* idx, int B,
  * positions 0..T-1).
  *
  * A tile pair (i, j) is PROCESSED iff j is in fwd range of i and
- * kstats[j].minpos <= qstats[i].maxpos. bwd range of j = [min, max+1) of
- * the processed i (or [0, 0)).
+ * kstats[j].minpos <= qstats[i].maxpos (minpos + 1 with SCFA_STRICT; with
+ * SCFA_NONCAUSAL: tile i holds a real query and tile j a real key). bwd
+ * range of j = [min, max+1) of the processed i (or [0, 0)).
  *  mode          SCFA_DENSE (q_idx, k_idx ignored, may be NULL), SCFA_QK,
- *                SCFA_HASH (q_bkt, k_bkt required).
+ *                SCFA_HASH (q_bkt, k_bkt required); OR-ed with at most one
+ *                of SCFA_STRICT, SCFA_NONCAUSAL.
  *  q_idx, q_bkt  (B, H, SCFA_PAD(Tq)); k_idx, k_bkt (B, H, SCFA_PAD(Tk)).
  *  Tq, Tk        valid rows (extrema are taken over rows < Tq / < Tk).
  *  Bm, Bn        tile sizes, each 16, 32, 64 or 128. The attention kernels
@@ -289,7 +300,8 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
                      int32_t* kstats, int32_t* fwd_tab, int32_t* bwd_tab, int32_t* tiles, hipStream_t stream);
 
 /* The backward table alone, from the statistics and forward table of a
- * scfa_range_table call (nQt, nKt as there): the same bwd_tab.              */
+ * scfa_range_table call (nQt, nKt as there): the same bwd_tab. flags: the
+ * SCFA_STRICT / SCFA_NONCAUSAL bit of that call (0 for none).             */
 int scfa_bwd_table(const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, int B, int H, int nQt, int nKt,
                    int32_t* bwd_tab, int flags, hipStream_t stream);
 
@@ -322,7 +334,9 @@ int scfa_work_order(const int32_t* tab, int B, int H, int ntiles, int span, int3
 
 /* Exact number of visible (query, key) pairs per head, from the sorted /
  * compacted index arrays (a query row r < Tq with position p >= 0 sees the
- * key rows s < Tk with k_idx[s] <= p, and equal bucket in hash mode).
+ * key rows s < Tk with k_idx[s] <= p, and equal bucket in hash mode; the
+ * mode may carry SCFA_STRICT, k_idx[s] < p, or SCFA_NONCAUSAL, every key row
+ * with a real position).
  *  pairs out (B, H) int64.                                                  */
 int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt,
                        const int32_t* k_bkt, int B, int H, int Tq, int Tk, int64_t* pairs, hipStream_t stream);
@@ -338,8 +352,9 @@ int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, con
  * key visible iff k_pos <= q_pos (QK), and same bucket (hash); scores are
  * scale * q.k. A query with no visible key -- and, in QK mode, a dropped
  * query -- gets O = 0 and LSE = -inf.
- *  flags         0 or SCFA_STRICT (k_pos < q_pos; the tables must have been
- *                built with the same flag).
+ *  flags         0, SCFA_STRICT (k_pos < q_pos) or SCFA_NONCAUSAL (no
+ *                position test); the tables must have been built with the
+ *                same flag.
  *  dtype_in      SCFA_BF16 / SCFA_F32 of q, k, v.
  *  dtype_out     SCFA_F32 / SCFA_BF16 of O.
  *  q, k, v       (B, T, H, D) the ORIGINAL, unpermuted tensors (D = 64).
@@ -387,7 +402,8 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
  * dK = scale dS^T Q. Keep masks and buckets are constants.
  *
  *  mode          SCFA_QK (also dense: QK rule on positions 0..T-1) or
- *                SCFA_HASH.
+ *                SCFA_HASH, OR-ed with the forward call's SCFA_STRICT or
+ *                SCFA_NONCAUSAL.
  *  dtype_in      SCFA_BF16 (the only backward build; fp32 returns
  *                SCFA_ERR_UNSUPPORTED).
  *  q, k, v       (B, T, H, D) the original tensors of the forward call,

@@ -78,7 +78,7 @@ struct BwdParams {
   int nQt, nKt;
   float c;      // scale * log2(e)
   float scale;  // score scale
-  int strict;   // 1: a key is visible only strictly before its query
+  Reach rc;     // position test (causal, strict or non-causal)
 };
 
 // ---------------------------------------------------------------------------
@@ -204,11 +204,11 @@ struct WaveKeys {
   bool any, all;
 };
 
-// st = 1 (strict causality): the extrema are of position + 1, the smallest
-// query position that sees the key.
-__device__ inline WaveKeys wave_keys(int kpos, int kbkt, int T, int st) {
+// The extrema are of k_reach(position), the smallest query position that
+// sees the key.
+__device__ inline WaveKeys wave_keys(int kpos, int kbkt, int T, const Reach& rc) {
   const bool real = kpos >= 0 && kpos < T;
-  int mn = real ? kpos + st : kInt32Max, mx = real ? kpos + st : kInt32Min;
+  int mn = real ? k_reach(rc, kpos) : kInt32Max, mx = real ? k_reach(rc, kpos) : kInt32Min;
   int mnb = real ? kbkt : kInt32Max, mxb = real ? kbkt : kInt32Min;
   int nreal = real ? 1 : 0;
 #pragma unroll
@@ -283,8 +283,8 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   const int kbkt = HASH ? p.k_bkt[kbase + krow] : 0;
   // the smallest query position that sees this key (kpos + 1 when strict):
   // masks and tile tests compare queries against it
-  const int kcmp = kpos + p.strict;
-  const WaveKeys wk = wave_keys(kpos, kbkt, p.T, p.strict);
+  const int kcmp = k_reach(p.rc, kpos);
+  const WaveKeys wk = wave_keys(kpos, kbkt, p.T, p.rc);
   bf16x8 Kb[2], Vb[2];
   {
     const size_t off = head0 + static_cast<size_t>(src_row(kpos, p.T)) * rstride;
@@ -336,9 +336,10 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   };
   // chunk ci = CPT * query tile + part; skip tiles failing the causal test
   const int4 ks = p.kstats[static_cast<size_t>(bh) * p.nKt + kt];
+  const int kreach = k_reach(p.rc, ks.x);  // smallest query position that sees a key of the tile
   const int cend = CPT * rng.y;
   auto next_chunk = [&](int ci) {
-    while (ci < cend && qstat(ci / CPT).y < ks.x + p.strict) ci = (ci / CPT + 1) * CPT;
+    while (ci < cend && qstat(ci / CPT).y < kreach) ci = (ci / CPT + 1) * CPT;
     return ci;
   };
 
@@ -454,14 +455,14 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
 }
 
 // Extrema of this wave's 32 keys (two blocks of 16; lane column r16 in each).
-__device__ inline WaveKeys wave_keys2(const int (&kpos)[2], const int (&kbkt)[2], int T, int st) {
+__device__ inline WaveKeys wave_keys2(const int (&kpos)[2], const int (&kbkt)[2], int T, const Reach& rc) {
   int mn = kInt32Max, mx = kInt32Min, mnb = kInt32Max, mxb = kInt32Min, nreal = 0;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const bool real = kpos[kb] >= 0 && kpos[kb] < T;
     if (real) {
-      mn = min(mn, kpos[kb] + st);
-      mx = max(mx, kpos[kb] + st);
+      mn = min(mn, k_reach(rc, kpos[kb]));
+      mx = max(mx, k_reach(rc, kpos[kb]));
       mnb = min(mnb, kbkt[kb]);
       mxb = max(mxb, kbkt[kb]);
       ++nreal;
@@ -526,6 +527,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int2 rng1 = has1 ? p.bwd_tab[static_cast<size_t>(bh) * p.nKt + kt0 + 1] : make_int2(0, 0);
   const int4 ks0 = p.kstats[static_cast<size_t>(bh) * p.nKt + kt0];
   const int4 ks1 = has1 ? p.kstats[static_cast<size_t>(bh) * p.nKt + kt0 + 1] : make_int4(0, 0, 0, 0);
+  // smallest query position that sees a key of each tile
+  const int kreach0 = k_reach(p.rc, ks0.x), kreach1 = k_reach(p.rc, ks1.x);
   const bool e0 = rng0.y <= rng0.x, e1 = rng1.y <= rng1.x;
   const int lo = e0 ? rng1.x : (e1 ? rng0.x : min(rng0.x, rng1.x));
   const int hi = e0 ? (e1 ? lo : rng1.y) : (e1 ? rng0.y : max(rng0.y, rng1.y));
@@ -546,9 +549,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     kpos[kb] = Ki[r];
     kbkt[kb] = HASH ? ((r < BN || has1) ? p.k_bkt[kbase + kt0 * BN + r] : 0) : 0;
   }
-  const WaveKeys wk = wave_keys2(kpos, kbkt, p.T, p.strict);
+  const WaveKeys wk = wave_keys2(kpos, kbkt, p.T, p.rc);
   // the smallest query position that sees each key (kpos + 1 when strict)
-  const int kcmp[2] = {kpos[0] + p.strict, kpos[1] + p.strict};
+  const int kcmp[2] = {k_reach(p.rc, kpos[0]), k_reach(p.rc, kpos[1])};
   bf16x8 Kb[2][2], Vb[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -606,8 +609,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int cend = CPT * hi;
   auto needed = [&](int t) {
     const int qy = qstat(t).y;
-    return (t >= rng0.x && t < rng0.y && qy >= ks0.x + p.strict) ||
-           (t >= rng1.x && t < rng1.y && qy >= ks1.x + p.strict);
+    return (t >= rng0.x && t < rng0.y && qy >= kreach0) || (t >= rng1.x && t < rng1.y && qy >= kreach1);
   };
   auto next_chunk = [&](int ci) {
     while (ci < cend && !needed(ci / CPT)) ci = (ci / CPT + 1) * CPT;
@@ -780,6 +782,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   const size_t kbase = static_cast<size_t>(bh) * p.TkP;    // key side
   const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
+  const int qreach = q_reach(p.rc, qs.y);  // largest key position a query of the tile may see
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
   const bool kst_lds = rng.y - rng.x <= kStatCap;
   if (kst_lds)
@@ -807,9 +810,9 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
       Db[qb][ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.dO) + off + (ds * 32 + g * 8) * 2);
     }
   }
-  const WaveRows wr = wave_rows(qpos, qbkt, p.strict);
+  const WaveRows wr = wave_rows(qpos, qbkt, p.rc);
   // positions the masks compare keys against: the largest visible key position
-  const int qcmp[2] = {qpos[0] - p.strict, qpos[1] - p.strict};
+  const int qcmp[2] = {q_reach(p.rc, qpos[0]), q_reach(p.rc, qpos[1])};
   f32x4 dQa[4][2];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -848,7 +851,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   };
   auto next_tile = [&](int j) {
     if (HASH)
-      while (j < rng.y && kstat(j).x + p.strict > qs.y) ++j;
+      while (j < rng.y && kstat(j).x > qreach) ++j;
     return j;
   };
 
@@ -983,7 +986,7 @@ using namespace scfa;
 extern "C" {
 
 size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D) {
-  mode &= ~SCFA_STRICT;
+  if (!flags_ok(take_flags(mode))) return 0;
   if ((mode != SCFA_QK && mode != SCFA_HASH) || B < 1 || H < 1 || Tq < 1 || Tk < 1 || D != HD) return 0;
   size_t off[3];
   return ws_layout(B, H, pad_rows(Tq), off);
@@ -994,9 +997,8 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
              const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
              const void* dO, int B, int H, int T, int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV,
              void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const int strict = strict_of(mode);
-  mode &= ~SCFA_STRICT;
-  if (mode != SCFA_QK && mode != SCFA_HASH) return SCFA_ERR_INVALID;
+  const int flags = take_flags(mode);
+  if (!flags_ok(flags) || (mode != SCFA_QK && mode != SCFA_HASH)) return SCFA_ERR_INVALID;
   if (!q || !k || !v || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !bwd_tab || !O || !lse || !dO || !dQ ||
       !dK || !dV || !workspace)
     return SCFA_ERR_INVALID;
@@ -1006,13 +1008,14 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
   if (D != HD || dtype_in != SCFA_BF16) return SCFA_ERR_UNSUPPORTED;
   // row offsets within one batch entry's (T, H, D) block are 32-bit
   if (static_cast<uint64_t>(T) * H * D * 2 > 0xFFFFFFFFull) return SCFA_ERR_UNSUPPORTED;
+  if ((flags & SCFA_NONCAUSAL) && T > kPosLimit) return SCFA_ERR_UNSUPPORTED;
   if (mode == SCFA_QK && (Tq % SCFA_ROW_ALIGN || Tk != Tq)) return SCFA_ERR_INVALID;
   const int TqP = pad_rows(Tq), TkP = pad_rows(Tk);
   size_t off[3];
   if (workspace_bytes < ws_layout(B, H, TqP, off)) return SCFA_ERR_INVALID;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   BwdParams p{};
-  p.strict = strict;
+  p.rc = reach_of(flags);
   p.q = q;
   p.k = k;
   p.v = v;

@@ -79,7 +79,7 @@ struct FwdParams {
   int TkPad;  // rows per head of the key-side index arrays (k_idx, k_bkt)
   int nQt, nKt;
   float c;     // scale * log2(e)
-  int strict;  // 1: a key is visible only strictly before its query
+  Reach rc;  // position test (causal, strict or non-causal)
 };
 
 template <typename TOUT>
@@ -260,6 +260,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const size_t kbase = static_cast<size_t>(bh) * p.TkPad;    // key side
   const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
+  const int qreach = q_reach(p.rc, qs.y);  // largest key position a query of the tile may see
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
   if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];  // visible after the first barrier
   const bool kst_lds = rng.y - rng.x <= kKstCap;
@@ -284,9 +285,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     qpos[qb] = p.q_idx[rowbase + row];
     qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
   }
-  const WaveRows wr = wave_rows(qpos, qbkt, p.strict);
+  const WaveRows wr = wave_rows(qpos, qbkt, p.rc);
   // positions the masks compare keys against: the largest visible key position
-  const int qcmp[2] = {qpos[0] - p.strict, qpos[1] - p.strict};
+  const int qcmp[2] = {q_reach(p.rc, qpos[0]), q_reach(p.rc, qpos[1])};
   bf16x8 Qb[2][2];  // [qb][ds]
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   // every tile of a QK range passes it)
   auto next_tile = [&](int j) {
     if (HASH)
-      while (j < rng.y && kstat(j).x + p.strict > qs.y) ++j;
+      while (j < rng.y && kstat(j).x > qreach) ++j;
     return j;
   };
 
@@ -483,6 +484,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
   const size_t kbase = static_cast<size_t>(bh) * p.TkPad;    // key side
   const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
+  const int qreach = q_reach(p.rc, qs.y);  // largest key position a query of the tile may see
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
   if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];
   const size_t rstride = static_cast<size_t>(p.H) * HD;                 // floats between token rows
@@ -496,9 +498,9 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
     qpos[qb] = p.q_idx[rowbase + row];
     qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
   }
-  const WaveRows wr = wave_rows(qpos, qbkt, p.strict);
+  const WaveRows wr = wave_rows(qpos, qbkt, p.rc);
   // positions the masks compare keys against: the largest visible key position
-  const int qcmp[2] = {qpos[0] - p.strict, qpos[1] - p.strict};
+  const int qcmp[2] = {q_reach(p.rc, qpos[0]), q_reach(p.rc, qpos[1])};
   float Qf[2][16];  // [qb][t], d = 16g + t
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -527,7 +529,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
   const int32_t* kbg = HASH ? p.k_bkt + kbase : nullptr;
 
   for (int j = rng.x; j < rng.y; ++j) {
-    if (kst[j].x + p.strict > qs.y) continue;  // causal extremum test (uniform)
+    if (kst[j].x > qreach) continue;  // causal extremum test (uniform)
     __syncthreads();  // previous tile no longer read
     // K and V rows of the tile (16 chunks of 16 bytes per row), through k_idx
 #pragma unroll
@@ -659,9 +661,10 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
                        const int32_t* fwd_tab, const int32_t* order, int B, int H, int T, int Tc, int D, float scale,
                        int flags, void* O, float* lse, hipStream_t stream) {
   if (!q || !k || !v || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !O || !lse) return SCFA_ERR_INVALID;
-  if (flags & ~SCFA_STRICT) return SCFA_ERR_INVALID;
+  if (!flags_ok(flags)) return SCFA_ERR_INVALID;
   const int st = check_common(dtype_in, dtype_out, B, H, T, D, scale);
   if (st != SCFA_OK) return st;
+  if ((flags & SCFA_NONCAUSAL) && T > kPosLimit) return SCFA_ERR_UNSUPPORTED;
   if (Tc < SCFA_ROW_ALIGN || Tc % SCFA_ROW_ALIGN) return SCFA_ERR_INVALID;
   FwdParams p{};
   p.q = q;
@@ -686,7 +689,7 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
   p.nQt = Tc / BM;
   p.nKt = Tc / BN;
   p.c = scale * 1.44269504088896340736f;
-  p.strict = strict_of(flags);
+  p.rc = reach_of(flags);
   return dispatch_fwd<false, true>(dtype_in, dtype_out, p, stream);
 }
 
@@ -697,9 +700,10 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
                          hipStream_t stream) {
   if (!q || !k || !v || !q_idx || !k_idx || !q_bkt || !k_bkt || !qstats || !kstats || !fwd_tab || !O || !lse)
     return SCFA_ERR_INVALID;
-  if (flags & ~SCFA_STRICT) return SCFA_ERR_INVALID;
+  if (!flags_ok(flags)) return SCFA_ERR_INVALID;
   const int st = check_common(dtype_in, dtype_out, B, H, T, D, scale);
   if (st != SCFA_OK) return st;
+  if ((flags & SCFA_NONCAUSAL) && T > kPosLimit) return SCFA_ERR_UNSUPPORTED;
   if (Tq < 1 || Tk < 1) return SCFA_ERR_INVALID;
   FwdParams p{};
   p.q = q;
@@ -724,7 +728,7 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
   p.nQt = p.TqPad / BM;
   p.nKt = p.TkPad / BN;
   p.c = scale * 1.44269504088896340736f;
-  p.strict = strict_of(flags);
+  p.rc = reach_of(flags);
   return dispatch_fwd<true, false>(dtype_in, dtype_out, p, stream);
 }
 

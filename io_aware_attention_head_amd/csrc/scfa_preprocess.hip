@@ -756,8 +756,9 @@ constexpr int kTabRegChunks = 8;  // register path for up to 512 tiles
 // One query tile's range [start, end) and processed-tile count (one wave).
 // ks: the head's key-tile statistics (global memory or LDS).
 __device__ void fwd_table_row(int mode, const int4 qs, const int4* ks, int nKt, int2* __restrict__ fwd_row, int lane,
-                              int32_t& cnt_out, int st) {
+                              int32_t& cnt_out, const Reach rc) {
   const int nch = (nKt + 63) / 64;
+  const int qreach = q_reach(rc, qs.y);  // largest key position a query of the tile may see
   // per chunk: a = tile below the query buckets, e = tile above them, c = causal test passes
   uint64_t A[kTabRegChunks], E[kTabRegChunks], C[kTabRegChunks];
   auto chunk_masks = [&](int ch, uint64_t& a, uint64_t& e, uint64_t& c) {
@@ -766,7 +767,7 @@ __device__ void fwd_table_row(int mode, const int4 qs, const int4* ks, int nKt, 
     if (j < nKt) k = ks[j];
     a = __ballot(j < nKt && k.w < qs.z);
     e = __ballot(j < nKt && k.z > qs.w);
-    c = __ballot(j < nKt && k.x + st <= qs.y);
+    c = __ballot(j < nKt && k.x <= qreach);
   };
   int start = 0, end = 0, cnt = 0;
   if (nch <= kTabRegChunks) {
@@ -830,7 +831,7 @@ __device__ void fwd_table_row(int mode, const int4 qs, const int4* ks, int nKt, 
       end = start;
       for (int j0 = start & ~63; j0 < eh; j0 += 64) {
         const int j = j0 + lane;
-        const uint64_t m = __ballot(j >= start && j < eh && ks[j].x + st <= qs.y);
+        const uint64_t m = __ballot(j >= start && j < eh && ks[j].x <= qreach);
         if (m) {
           end = j0 + 64 - __clzll(static_cast<long long>(m));
           cnt += __popcll(m);
@@ -851,7 +852,7 @@ constexpr int kTabWaves = 16;
 __global__ __launch_bounds__(64 * kTabWaves) void k_fwd_table(int mode, const int32_t* __restrict__ qstats,
                                                               const int32_t* __restrict__ kstats, int nQt, int nKt,
                                                               int32_t* __restrict__ fwd, int32_t* __restrict__ tiles,
-                                                              int st) {
+                                                              const Reach rc) {
   __shared__ int32_t wcnt[kTabWaves];
   const int bh = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -860,7 +861,7 @@ __global__ __launch_bounds__(64 * kTabWaves) void k_fwd_table(int mode, const in
   if (i < nQt)
     fwd_table_row(mode, reinterpret_cast<const int4*>(qstats)[static_cast<size_t>(bh) * nQt + i],
                   reinterpret_cast<const int4*>(kstats) + static_cast<size_t>(bh) * nKt, nKt,
-                  reinterpret_cast<int2*>(fwd) + static_cast<size_t>(bh) * nQt + i, lane, wcnt[w], st);
+                  reinterpret_cast<int2*>(fwd) + static_cast<size_t>(bh) * nQt + i, lane, wcnt[w], rc);
   __syncthreads();
   if (threadIdx.x == 0) {
     int sum = 0;
@@ -874,12 +875,13 @@ __global__ __launch_bounds__(64 * kTabWaves) void k_fwd_table(int mode, const in
 // holds query tiles l, l+64, ... (loads issued up front).
 __global__ __launch_bounds__(256) void k_bwd_table(const int32_t* __restrict__ qstats, const int32_t* __restrict__ kstats,
                                                    const int32_t* __restrict__ fwd, int nQt, int nKt,
-                                                   int32_t* __restrict__ bwd, int st) {
+                                                   int32_t* __restrict__ bwd, const Reach rc) {
   const int bh = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (j >= nKt) return;
-  const int kmin = reinterpret_cast<const int4*>(kstats)[static_cast<size_t>(bh) * nKt + j].x;
+  // smallest query position that sees a key of the tile
+  const int kreach = k_reach(rc, reinterpret_cast<const int4*>(kstats)[static_cast<size_t>(bh) * nKt + j].x);
   const int4* qs = reinterpret_cast<const int4*>(qstats) + static_cast<size_t>(bh) * nQt;
   const int2* ft = reinterpret_cast<const int2*>(fwd) + static_cast<size_t>(bh) * nQt;
   const int nch = (nQt + 63) / 64;
@@ -888,7 +890,7 @@ __global__ __launch_bounds__(256) void k_bwd_table(const int32_t* __restrict__ q
     bool hit = false;
     if (i < nQt) {
       const int2 r = ft[i];
-      hit = j >= r.x && j < r.y && kmin + st <= qs[i].y;
+      hit = j >= r.x && j < r.y && kreach <= qs[i].y;
     }
     return __ballot(hit);
   };
@@ -985,17 +987,17 @@ __global__ __launch_bounds__(256) void k_count_visible(int mode, const int32_t* 
                                                        const int32_t* __restrict__ k_idx,
                                                        const int32_t* __restrict__ q_bkt,
                                                        const int32_t* __restrict__ k_bkt, int Tq, int Tk, int TqP,
-                                                       int TkP, int64_t* __restrict__ pairs, int st) {
+                                                       int TkP, int64_t* __restrict__ pairs, const Reach rc) {
   __shared__ long long part[4];
   const int bh = blockIdx.y;
   const int r = blockIdx.x * 256 + threadIdx.x;
   long long n = 0;
   if (r < Tq) {
     if (mode == SCFA_DENSE) {
-      n = min(r + 1 - st, Tk);
+      n = min(static_cast<long long>(q_reach(rc, r)) + 1, static_cast<long long>(Tk));
     } else {
       const int p0 = q_idx[static_cast<size_t>(bh) * TqP + r];
-      const int p = p0 - st;  // keys at positions <= p are visible
+      const int p = q_reach(rc, p0);  // keys at positions <= p are visible
       const int32_t* kp = k_idx + static_cast<size_t>(bh) * TkP;
       if (p0 >= 0) {
         if (mode == SCFA_QK) {
@@ -1273,9 +1275,9 @@ int scfa_gather(int dtype, int layout, const void* x, const int32_t* idx, int B,
 int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
                      int B, int H, int Tq, int Tk, int Bm, int Bn, int32_t* qstats, int32_t* kstats, int32_t* fwd_tab,
                      int32_t* bwd_tab, int32_t* tiles, hipStream_t stream) {
-  const int st = strict_of(mode);
-  mode &= ~SCFA_STRICT;
-  if (mode != SCFA_DENSE && mode != SCFA_QK && mode != SCFA_HASH) return SCFA_ERR_INVALID;
+  const int flags = take_flags(mode);
+  if (!flags_ok(flags) || (mode != SCFA_DENSE && mode != SCFA_QK && mode != SCFA_HASH)) return SCFA_ERR_INVALID;
+  const Reach rc = reach_of(flags);
   if (!qstats || !kstats || !fwd_tab || !tiles) return SCFA_ERR_INVALID;
   if (mode != SCFA_DENSE && (!q_idx || !k_idx)) return SCFA_ERR_INVALID;
   if (mode == SCFA_HASH && (!q_bkt || !k_bkt)) return SCFA_ERR_INVALID;
@@ -1288,11 +1290,11 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
                      Tk, TqP, TkP, Bm, Bn, nQt, nKt, qstats, kstats, tiles);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   hipLaunchKernelGGL(k_fwd_table, dim3(ceil_div(nQt, kTabWaves), B * H), dim3(64 * kTabWaves), 0, stream, mode, qstats,
-                     kstats, nQt, nKt, fwd_tab, tiles, st);
+                     kstats, nQt, nKt, fwd_tab, tiles, rc);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   if (bwd_tab) {
     hipLaunchKernelGGL(k_bwd_table, dim3(ceil_div(nKt, 4), B * H), dim3(256), 0, stream, qstats, kstats, fwd_tab, nQt,
-                       nKt, bwd_tab, st);
+                       nKt, bwd_tab, rc);
     SCFA_RETURN_IF_LAUNCH_FAILED();
   }
   return SCFA_OK;
@@ -1300,13 +1302,13 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
 
 int scfa_fwd_table(int mode, const int32_t* qstats, const int32_t* kstats, int B, int H, int nQt, int nKt,
                    int32_t* fwd_tab, int32_t* tiles, hipStream_t stream) {
-  const int st = strict_of(mode);
-  mode &= ~SCFA_STRICT;
-  if (mode != SCFA_DENSE && mode != SCFA_QK && mode != SCFA_HASH) return SCFA_ERR_INVALID;
+  const int flags = take_flags(mode);
+  if (!flags_ok(flags) || (mode != SCFA_DENSE && mode != SCFA_QK && mode != SCFA_HASH)) return SCFA_ERR_INVALID;
+  const Reach rc = reach_of(flags);
   if (!qstats || !kstats || !fwd_tab || !tiles) return SCFA_ERR_INVALID;
   if (B < 1 || H < 1 || nQt < 1 || nKt < 1) return SCFA_ERR_INVALID;
   hipLaunchKernelGGL(k_fwd_table, dim3(ceil_div(nQt, kTabWaves), B * H), dim3(64 * kTabWaves), 0, stream, mode, qstats,
-                     kstats, nQt, nKt, fwd_tab, tiles, st);
+                     kstats, nQt, nKt, fwd_tab, tiles, rc);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }
@@ -1314,9 +1316,9 @@ int scfa_fwd_table(int mode, const int32_t* qstats, const int32_t* kstats, int B
 int scfa_bwd_table(const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, int B, int H, int nQt, int nKt,
                    int32_t* bwd_tab, int flags, hipStream_t stream) {
   if (!qstats || !kstats || !fwd_tab || !bwd_tab) return SCFA_ERR_INVALID;
-  if (B < 1 || H < 1 || nQt < 1 || nKt < 1 || (flags & ~SCFA_STRICT)) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || nQt < 1 || nKt < 1 || !flags_ok(flags)) return SCFA_ERR_INVALID;
   hipLaunchKernelGGL(k_bwd_table, dim3(ceil_div(nKt, 4), B * H), dim3(256), 0, stream, qstats, kstats, fwd_tab, nQt, nKt,
-                     bwd_tab, strict_of(flags));
+                     bwd_tab, reach_of(flags));
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }
@@ -1335,9 +1337,9 @@ int scfa_work_order(const int32_t* tab, int B, int H, int ntiles, int span, int3
 
 int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
                        int B, int H, int Tq, int Tk, int64_t* pairs, hipStream_t stream) {
-  const int st = strict_of(mode);
-  mode &= ~SCFA_STRICT;
-  if (mode != SCFA_DENSE && mode != SCFA_QK && mode != SCFA_HASH) return SCFA_ERR_INVALID;
+  const int flags = take_flags(mode);
+  if (!flags_ok(flags) || (mode != SCFA_DENSE && mode != SCFA_QK && mode != SCFA_HASH)) return SCFA_ERR_INVALID;
+  const Reach rc = reach_of(flags);
   if (!pairs) return SCFA_ERR_INVALID;
   if (mode != SCFA_DENSE && (!q_idx || !k_idx)) return SCFA_ERR_INVALID;
   if (mode == SCFA_HASH && (!q_bkt || !k_bkt)) return SCFA_ERR_INVALID;
@@ -1345,7 +1347,7 @@ int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, con
   hipLaunchKernelGGL(k_zero_i64, dim3(ceil_div(B * H, 256)), dim3(256), 0, stream, pairs, B * H);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   hipLaunchKernelGGL(k_count_visible, dim3(ceil_div(Tq, 256), B * H), dim3(256), 0, stream, mode, q_idx, k_idx, q_bkt,
-                     k_bkt, Tq, Tk, pad_rows(Tq), pad_rows(Tk), pairs, st);
+                     k_bkt, Tq, Tk, pad_rows(Tq), pad_rows(Tk), pairs, rc);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }

@@ -98,16 +98,15 @@ struct WaveRows {
   int minpos, maxpos, minb, maxb;
 };
 
-// st = 1 (strict causality): the extrema are of position - 1, the largest
-// key position each query may see, so that every tile test compares keys
-// against them unchanged.
-__device__ inline WaveRows wave_rows(const int (&qpos)[2], const int (&qbkt)[2], int st) {
-  WaveRows s{kInt32Max, -1 - st, kInt32Max, kInt32Min};
+// The extrema are of q_reach(position), the largest key position each query
+// may see, so that every tile test compares keys against them unchanged.
+__device__ inline WaveRows wave_rows(const int (&qpos)[2], const int (&qbkt)[2], const Reach& rc) {
+  WaveRows s{kInt32Max, q_reach(rc, -1), kInt32Max, kInt32Min};
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     if (qpos[qb] >= 0) {
-      s.minpos = min(s.minpos, qpos[qb] - st);
-      s.maxpos = max(s.maxpos, qpos[qb] - st);
+      s.minpos = min(s.minpos, q_reach(rc, qpos[qb]));
+      s.maxpos = max(s.maxpos, q_reach(rc, qpos[qb]));
       s.minb = min(s.minb, qbkt[qb]);
       s.maxb = max(s.maxb, qbkt[qb]);
     }

@@ -24,6 +24,7 @@ SCFA_DEVERR_COUNT_EXCEEDS_TC, SCFA_DEVERR_BUCKET_RANGE, SCFA_DEVERR_SEGMENT_OVER
 SCFA_BF16, SCFA_F32 = 0, 1
 SCFA_DENSE, SCFA_QK, SCFA_HASH = 0, 1, 2
 SCFA_STRICT = 16  # flag: a key is visible only strictly before its query
+SCFA_NONCAUSAL = 32  # flag: no causal test (bidirectional attention)
 SCFA_ROWS, SCFA_COLS = 0, 1
 SCFA_Q_PAD, SCFA_K_PAD = -1, 1_000_000_000
 SCFA_ROW_ALIGN = 128
@@ -355,6 +356,7 @@ class Prepared:
     v_t: Optional[torch.Tensor] = None  # (B,H,D,pad(Tk)) transposed
     extra: dict = dataclasses.field(default_factory=dict)
     strict: bool = False  # keys strictly before the query (SCFA_STRICT)
+    noncausal: bool = False  # no causal test (SCFA_NONCAUSAL)
 
 
 def gather_operands(pre: Prepared, stream=None) -> Prepared:
@@ -391,7 +393,7 @@ def _empty(shape, dtype, like):
 
 
 def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, rows: bool = False, stream=None,
-               strict: bool = False) -> Prepared:
+               strict: bool = False, noncausal: bool = False) -> Prepared:
     """QK-drop preprocessing: counts and the compacted index arrays (with
     rows=True also the compacted Q and K rows). Reads the max kept count back
     to the host once (to size Tc) unless Tc is given."""
@@ -413,11 +415,12 @@ def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, rows: bool = F
     scfa_qk_compact(q, keep_q, cq, oq, Tc, SCFA_Q_PAD, q_c, q_idx, dev_err, stream)
     scfa_qk_compact(k, keep_k, ck, ok, Tc, SCFA_K_PAD, k_c, k_idx, dev_err, stream)
     return Prepared("qk", B, H, T, D, Tc, Tc, q, k, v, q_idx, k_idx, q=q_c, k=k_c,
-                    extra={"count_q": cq, "count_k": ck, "max_q": mq, "max_k": mk, "dev_err": dev_err}, strict=strict)
+                    extra={"count_q": cq, "count_k": ck, "max_q": mq, "max_k": mk, "dev_err": dev_err}, strict=strict,
+                    noncausal=noncausal)
 
 
 def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None, keep_q=None, keep_k=None,
-                 strict: bool = False) -> Prepared:
+                 strict: bool = False, noncausal: bool = False) -> Prepared:
     """Hash-sparse preprocessing: LSH buckets of Q and K, stable counting sort
     per head and (aligned=True) the bucket-aligned layout in one launch per
     side (query buckets start at multiples of the query tile, key buckets at
@@ -459,10 +462,11 @@ def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None, keep_q=
         scfa_hash_layout(bk, ck, nb, 0, SCFA_K_PAD, perm_k, bs_k, offk, dev_err=dev_err, stream=stream)
         Tq = Tk = T
         q_idx, k_idx, q_bkt, k_bkt = perm_q, perm_k, bs_q, bs_k
-    return Prepared("hash", B, H, T, D, Tq, Tk, q, k, v, q_idx, k_idx, q_bkt, k_bkt, extra=extra, strict=strict)
+    return Prepared("hash", B, H, T, D, Tq, Tk, q, k, v, q_idx, k_idx, q_bkt, k_bkt, extra=extra, strict=strict,
+                    noncausal=noncausal)
 
 
-def prepare_dense(q, k, v, stream=None, strict: bool = False) -> Prepared:
+def prepare_dense(q, k, v, stream=None, strict: bool = False, noncausal: bool = False) -> Prepared:
     """Dense causal attention on the same kernel: positions 0..T-1 for both
     queries and keys (the QK path with nothing dropped)."""
     B, T, H, D = q.shape
@@ -470,7 +474,7 @@ def prepare_dense(q, k, v, stream=None, strict: bool = False) -> Prepared:
     ar = torch.arange(Tp, dtype=torch.int32, device=q.device)
     q_idx = torch.where(ar < T, ar, torch.full_like(ar, SCFA_Q_PAD)).expand(B, H, Tp).contiguous()
     k_idx = torch.where(ar < T, ar, torch.full_like(ar, SCFA_K_PAD)).expand(B, H, Tp).contiguous()
-    return Prepared("dense", B, H, T, D, Tp, Tp, q, k, v, q_idx, k_idx, strict=strict)
+    return Prepared("dense", B, H, T, D, Tp, Tp, q, k, v, q_idx, k_idx, strict=strict, noncausal=noncausal)
 
 
 def _table_mode(mode: str) -> int:
@@ -478,7 +482,9 @@ def _table_mode(mode: str) -> int:
 
 
 def _flags(pre: "Prepared") -> int:
-    return SCFA_STRICT if pre.strict else 0
+    if pre.strict and pre.noncausal:
+        raise ScfaError("strict and noncausal exclude each other")
+    return (SCFA_STRICT if pre.strict else 0) | (SCFA_NONCAUSAL if pre.noncausal else 0)
 
 
 def build_tables(pre: Prepared, Bm: int = SCFA_TILE_M, Bn: int = SCFA_TILE_N, stream=None) -> Tables:
@@ -575,7 +581,7 @@ class Plan:
     """
 
     def __init__(self, mode, B, H, T, D=64, dtype=torch.bfloat16, nb=16, Tc=None, out_dtype=torch.float32,
-                 device="cuda", scale=None, strict=False):
+                 device="cuda", scale=None, strict=False, noncausal=False):
         self.drop = mode == "hash_drop"
         if self.drop:
             mode = "hash"
@@ -586,7 +592,10 @@ class Plan:
         self.mode, self.B, self.H, self.T, self.D, self.nb = mode, B, H, T, D, nb
         self.nbs = nb + 2 if self.drop else nb  # buckets of the sort and layout
         self.strict = bool(strict)  # keys strictly before the query (SCFA_STRICT)
-        self.flags = SCFA_STRICT if self.strict else 0
+        self.noncausal = bool(noncausal)  # no causal test (SCFA_NONCAUSAL)
+        if self.strict and self.noncausal:
+            raise ScfaError("strict and noncausal exclude each other")
+        self.flags = (SCFA_STRICT if self.strict else 0) | (SCFA_NONCAUSAL if self.noncausal else 0)
         self.dtype, self.out_dtype = dtype, out_dtype
         self.scale = 1.0 / math.sqrt(D) if scale is None else scale
         d = torch.device(device)
@@ -736,4 +745,5 @@ class Plan:
             raise ScfaError("call prepare() first")
         x = self.x
         return Prepared(self.mode, self.B, self.H, self.T, self.D, self.Tq, self.Tk, x["q"], x["k"], x["v"],
-                        self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, strict=self.strict)
+                        self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, strict=self.strict,
+                        noncausal=self.noncausal)

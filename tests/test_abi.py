@@ -79,10 +79,20 @@ def test_invalid_arguments_rejected_without_gpu():
     # one batch entry's T x H x D block of 4 GiB or more (32-bit row offsets)
     assert L.scfa_qk_sparse_fwd(*args, 1, 64, 1 << 20, 1 << 20, 64, ctypes.c_float(0.125), 0, dummy, dummy,
                                 null) == scfa.SCFA_ERR_UNSUPPORTED
-    # flags other than SCFA_STRICT
+    # flags other than SCFA_STRICT / SCFA_NONCAUSAL, and the two together
     assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 64, ctypes.c_float(0.125), 4, dummy, dummy,
                                 null) == scfa.SCFA_ERR_INVALID
+    both = scfa.SCFA_STRICT | scfa.SCFA_NONCAUSAL
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 64, ctypes.c_float(0.125), both, dummy, dummy,
+                                null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_bwd_table(dummy, dummy, dummy, 1, 1, 2, 2, dummy, 3, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_bwd_table(dummy, dummy, dummy, 1, 1, 2, 2, dummy, both, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_range_table(1 | both, dummy, dummy, null, null, 1, 1, 8, 8, 128, 64, dummy, dummy, dummy, dummy,
+                              dummy, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_count_visible(1 | both, dummy, dummy, null, null, 1, 1, 8, 8, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_bwd_workspace_bytes(1 | both, 1, 1, 128, 128, 64) == 0
+    assert L.scfa_bwd_workspace_bytes(1 | scfa.SCFA_NONCAUSAL, 1, 1, 128, 128, 64) == \
+        L.scfa_bwd_workspace_bytes(1, 1, 1, 128, 128, 64) > 0
     # a mode with the strict flag is accepted where a mode is (argument errors still caught)
     assert L.scfa_range_table(2 | scfa.SCFA_STRICT, dummy, dummy, null, null, 1, 1, 8, 8, 128, 64, dummy, dummy,
                               dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
@@ -156,6 +166,12 @@ def test_python_binding_rejects_host_tensors():
 
 def test_header_constants_match_binding():
     txt = open(HEADER).read()
-    for name in ("SCFA_TILE_M", "SCFA_TILE_N", "SCFA_ROW_ALIGN", "SCFA_COUNT_CHUNK", "SCFA_K_PAD", "SCFA_STRICT"):
+    for name in ("SCFA_TILE_M", "SCFA_TILE_N", "SCFA_ROW_ALIGN", "SCFA_COUNT_CHUNK", "SCFA_K_PAD", "SCFA_STRICT",
+                 "SCFA_NONCAUSAL"):
         m = re.search(rf"#define {name} \(?(-?\d+)\)?", txt)
         assert m and int(m.group(1)) == getattr(scfa, name), name
+
+
+def test_plan_rejects_strict_with_noncausal():
+    with pytest.raises(scfa.ScfaError):
+        scfa.Plan("hash", 1, 1, 128, strict=True, noncausal=True, device="cpu")

@@ -97,8 +97,8 @@ def test_strict_backward(w):
 
 def test_strict_plan_full_size_graph():
     """The benchmark workload, strict, through a graph-captured Plan: sampled
-    rows of every head against the oracle, the pair count, bit-equal
-    replays, and the backward of two heads."""
+    rows of every head against the oracle, the pair count and bit-equal
+    replays."""
     need_gpu()
     w = WORKLOADS["hash_bf16_t16384_nb16"]
     announce("strict plan full size")
