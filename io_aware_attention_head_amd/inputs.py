@@ -39,6 +39,11 @@ class Workload:
     nb: int = 16         # number of LSH buckets (hash mode)
     seed: int = 0
     grad: bool = False   # also draw dO and run the backward
+    Tk: int = 0          # key/value length when it differs from T (0: T)
+
+    @property
+    def T_kv(self) -> int:
+        return self.Tk if self.Tk else self.T
 
 
 # The five workloads: a small fp32 QK case, a dense-causal sanity case, QK-drop
@@ -68,9 +73,10 @@ def _torch_dtype(name: str) -> torch.dtype:
 def make_inputs(w: Workload, keep_override: Optional[float] = None) -> dict:
     """Draw the inputs of workload ``w`` on the CPU.
 
-    Returns a dict of CPU tensors: q, k, v (B,T,H,D) in the workload dtype;
-    keep_q, keep_k (B,T,H) uint8 (1 = kept); R (H,D,nb/2) float32; dO
-    (B,T,H,D) in the workload dtype. In dense mode the keep masks are all ones.
+    Returns a dict of CPU tensors: q (B,T,H,D), k, v (B,Tk,H,D) in the
+    workload dtype; keep_q (B,T,H), keep_k (B,Tk,H) uint8 (1 = kept); R
+    (H,D,nb/2) float32; dO (B,T,H,D) in the workload dtype. In dense mode the
+    keep masks are all ones. Tk is the workload's key length (T unless set).
     """
     if w.mode not in MODES:
         raise ValueError(f"unknown mode {w.mode!r}")
@@ -78,12 +84,13 @@ def make_inputs(w: Workload, keep_override: Optional[float] = None) -> dict:
         raise ValueError("nb must be even")
     g = torch.Generator().manual_seed(w.seed)
     shape = (w.B, w.T, w.H, w.D)
+    kshape = (w.B, w.T_kv, w.H, w.D)
     q = torch.randn(shape, generator=g)
-    k = torch.randn(shape, generator=g)
-    v = torch.randn(shape, generator=g)
+    k = torch.randn(kshape, generator=g)
+    v = torch.randn(kshape, generator=g)
     p = w.keep_p if keep_override is None else keep_override
     keep_q = (torch.rand((w.B, w.T, w.H), generator=g) < p).to(torch.uint8)
-    keep_k = (torch.rand((w.B, w.T, w.H), generator=g) < p).to(torch.uint8)
+    keep_k = (torch.rand((w.B, w.T_kv, w.H), generator=g) < p).to(torch.uint8)
     R = torch.randn((w.H, w.D, w.nb // 2), generator=g)
     dO = torch.randn(shape, generator=g)
     if w.mode == "dense":
@@ -97,6 +104,9 @@ def make_inputs(w: Workload, keep_override: Optional[float] = None) -> dict:
 
 
 def small(mode: str, B: int, H: int, T: int, D: int = 64, dtype: str = "bf16", keep_p: float = 0.7,
-          nb: int = 16, seed: int = 0, grad: bool = False) -> Workload:
-    """A named ad-hoc workload for tests (edge cases, ragged shapes)."""
-    return Workload(f"{mode}_{dtype}_B{B}H{H}T{T}D{D}_s{seed}", mode, B, H, T, D, dtype, keep_p, nb, seed, grad)
+          nb: int = 16, seed: int = 0, grad: bool = False, Tk: int = 0) -> Workload:
+    """A named ad-hoc workload for tests (edge cases, ragged shapes); Tk: a
+    key/value length other than T."""
+    tk = f"Tk{Tk}" if Tk and Tk != T else ""
+    return Workload(f"{mode}_{dtype}_B{B}H{H}T{T}{tk}D{D}_s{seed}", mode, B, H, T, D, dtype, keep_p, nb, seed, grad,
+                    Tk if Tk != T else 0)

@@ -32,6 +32,11 @@ Readings of points the pages leave open (each one is also listed in the design doc):
   * noncausal=True: no position test (bidirectional attention over the
     kept / same-bucket tokens); a tile holds a visible pair iff it holds a
     real key (position below the key pad).
+  * Separate query and key lengths (the explainer's decision tensors of
+    lengths T_Q and T_KV): queries at positions 0..T_Q-1, keys at
+    0..T_KV-1, compared unchanged by the causal test. With T_KV > T_Q the
+    keys after the last query are never visible (unless noncausal); with
+    T_Q > T_KV the queries at T_KV and beyond see every key.
   * Hashing combined with within-bucket dropping (the explainer's follow-up
     idea): in hash mode with keep masks a pair is visible iff both tokens
     share a bucket, both are kept and the key does not come after the query.
@@ -327,7 +332,7 @@ def range_tables(mode: str, q_idx: np.ndarray, k_idx: np.ndarray, q_bkt: Optiona
 
 def _vis_rows(mode: str, rows: np.ndarray, T: int, kq, kk, bq, bk, strict: bool = False,
               noncausal: bool = False) -> np.ndarray:
-    """Visibility of query rows `rows` (original positions) against all keys
+    """Visibility of query rows `rows` (original positions) against all T keys
     of one head (strict: a key strictly before the query, the explainer's
     '>' variant of the causal test; noncausal: no position test at all, the
     bidirectional attention the explainer mentions as an extension).
@@ -363,14 +368,17 @@ def attention_fwd(mode: str, q, k, v, keep_q=None, keep_k=None, bkt_q=None, bkt_
                   noncausal: bool = False):
     """Explicit masked-softmax causal attention in original token order.
 
-    q, k, v: (B, T, H, D) float64. keep_q/keep_k: (B, T, H) (qk mode; in
-    hash mode optional, for hashing combined with within-bucket dropping).
-    bkt_q/bkt_k: (B, H, T) bucket ids (hash mode).
+    q: (B, Tq, H, D), k, v: (B, Tk, H, D) float64; Tq and Tk may differ (the
+    explainer's decision tensors have lengths T_Q and T_KV): queries sit at
+    positions 0..Tq-1 and keys at 0..Tk-1, and the causal test compares
+    these positions unchanged. keep_q (B, Tq, H) / keep_k (B, Tk, H) (qk
+    mode; in hash mode optional, for hashing combined with within-bucket
+    dropping). bkt_q (B, H, Tq) / bkt_k (B, H, Tk) bucket ids (hash mode).
     strict: keys strictly before the query (the explainer's '>' variant);
     noncausal: no position test (bidirectional).
     heads: optional list of (b, h) to compute (others left at 0 / -inf).
     rows: optional query positions to compute (others left at 0 / -inf).
-    Returns O (B, T, H, D) float64 and LSE (B, H, T) float64.
+    Returns O (B, Tq, H, D) float64 and LSE (B, H, Tq) float64.
     For a row with n visible keys: O = sum_j softmax_j v_j, LSE = m + ln sum
     exp(s - m); with n = 0: O = 0, LSE = -inf.
     """
@@ -378,6 +386,7 @@ def attention_fwd(mode: str, q, k, v, keep_q=None, keep_k=None, bkt_q=None, bkt_
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     B, T, H, D = q.shape
+    Tk = k.shape[1]
     tau = 1.0 / math.sqrt(D) if scale is None else scale
     O = np.zeros((B, T, H, v.shape[-1]))
     LSE = np.full((B, H, T), NEG_INF)
@@ -390,7 +399,7 @@ def attention_fwd(mode: str, q, k, v, keep_q=None, keep_k=None, bkt_q=None, bkt_
         Kh, Vh = k[b, :, h], v[b, :, h]
         for s0 in range(0, len(all_rows), block):
             r = all_rows[s0:s0 + block]
-            vis = _vis_rows(mode, r, T, kq, kk, bq, bk, strict, noncausal)
+            vis = _vis_rows(mode, r, Tk, kq, kk, bq, bk, strict, noncausal)
             S = tau * (q[b, r, h] @ Kh.T)
             S = np.where(vis, S, NEG_INF)
             has = vis.any(axis=1)
@@ -414,14 +423,15 @@ def attention_bwd(mode: str, q, k, v, dO, keep_q=None, keep_k=None, bkt_q=None, 
       dV_j = sum_i P_ij dO_i;   dP_ij = dO_i . v_j;   Delta_i = dO_i . O_i;
       dS_ij = P_ij (dP_ij - Delta_i);   dQ_i = tau sum_j dS_ij k_j;
       dK_j = tau sum_i dS_ij q_i.
-    Keep masks and buckets are constants. Returns dQ, dK, dV (B, T, H, D)
-    float64 (zero for heads not in `heads`).
+    Keep masks and buckets are constants. Returns dQ (shaped like q) and dK,
+    dV (shaped like k) float64 (zero for heads not in `heads`).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     dO = np.asarray(dO, np.float64)
     B, T, H, D = q.shape
+    Tk = k.shape[1]
     tau = 1.0 / math.sqrt(D) if scale is None else scale
     dQ = np.zeros_like(q)
     dK = np.zeros_like(k)
@@ -436,7 +446,7 @@ def attention_bwd(mode: str, q, k, v, dO, keep_q=None, keep_k=None, bkt_q=None, 
         Qh, Kh, Vh = q[b, :, h], k[b, :, h], v[b, :, h]
         for s0 in range(0, T, block):
             r = np.arange(s0, min(T, s0 + block))
-            vis = _vis_rows(mode, r, T, kq, kk, bq, bk, strict, noncausal)
+            vis = _vis_rows(mode, r, Tk, kq, kk, bq, bk, strict, noncausal)
             lse = LSE[b, h, r]
             has = np.isfinite(lse)
             S = tau * (Qh[r] @ Kh.T)
@@ -477,29 +487,36 @@ def attention_rows(q, k, v, q_pos, k_pos, q_bkt=None, k_bkt=None, scale: Optiona
 
 
 def visible_pairs(mode: str, T: int, B: int, H: int, keep_q=None, keep_k=None, bkt_q=None, bkt_k=None,
-                  strict: bool = False, noncausal: bool = False) -> np.ndarray:
-    """Exact number of visible (query, key) pairs per (b, h). -> (B, H) int64."""
+                  strict: bool = False, noncausal: bool = False, Tk: Optional[int] = None) -> np.ndarray:
+    """Exact number of visible (query, key) pairs per (b, h), T queries and
+    Tk keys (default T). -> (B, H) int64."""
+    Tk = T if Tk is None else Tk
     out = np.zeros((B, H), dtype=np.int64)
     sh = 1 if strict else 0
+    qpos = np.arange(T)
 
-    def upto(c):  # counts over key positions <= i (strict: < i; noncausal: all) from an inclusive cumsum
+    def upto(c):
+        """Per query position i < T: the count c holds (inclusive cumsum over
+        the Tk key positions) at key positions <= i (strict: < i;
+        noncausal: all)."""
         if noncausal:
-            return np.full_like(c, c[-1])
-        return c if not strict else np.concatenate([[0], c[:-1]])
+            return np.full(T, c[-1])
+        last = np.minimum(qpos - sh, Tk - 1)  # last visible key position
+        return np.where(last >= 0, c[np.maximum(last, 0)], 0)
 
     for b in range(B):
         for h in range(H):
             if mode == "dense":
-                out[b, h] = T * T if noncausal else T * (T + 1) // 2 - sh * T
+                out[b, h] = int(upto(np.arange(1, Tk + 1)).sum())
             elif mode == "qk":
                 kk = (keep_k[b, :, h] != 0).astype(np.int64)
-                before = upto(np.cumsum(kk))  # kept keys at positions <= i (strict: < i)
+                before = upto(np.cumsum(kk))  # kept keys visible to query position i
                 out[b, h] = int(before[keep_q[b, :, h] != 0].sum())
             else:
                 tot = 0
                 bq, bk = bkt_q[b, h], bkt_k[b, h]
                 kq = np.ones(T, bool) if keep_q is None else keep_q[b, :, h] != 0
-                kk = np.ones(T, bool) if keep_k is None else keep_k[b, :, h] != 0
+                kk = np.ones(Tk, bool) if keep_k is None else keep_k[b, :, h] != 0
                 for val in np.union1d(np.unique(bq), np.unique(bk)):
                     kin = upto(np.cumsum((bk == val) & kk))
                     tot += int(kin[(bq == val) & kq].sum())

@@ -30,8 +30,8 @@ def _keeps(mode, kq, kk):
     return (kq, kk) if mode in ("qk", "hash_keep") else (None, None)
 
 
-def _case(mode, T, H=2, D=16, seed=0, keep_p=0.6, nb=4, B=1):
-    w = small(_omode(mode), B, H, T, D, dtype="bf16", keep_p=keep_p, nb=nb, seed=seed)
+def _case(mode, T, H=2, D=16, seed=0, keep_p=0.6, nb=4, B=1, Tk=0):
+    w = small(_omode(mode), B, H, T, D, dtype="bf16", keep_p=keep_p, nb=nb, seed=seed, Tk=Tk)
     x = make_inputs(w)
     q, k, v = _np64(x["q"]), _np64(x["k"]), _np64(x["v"])
     kq, kk = x["keep_q"].numpy(), x["keep_k"].numpy()
@@ -46,6 +46,7 @@ def _brute_fwd(mode, q, k, v, kq, kk, bq, bk, strict=False, noncausal=False):
     """Pairwise enumeration with Python scalars and math.exp (strict: keys
     j < i only; noncausal: every key j)."""
     B, T, H, D = q.shape
+    Tk = k.shape[1]
     tau = 1.0 / math.sqrt(D)
     O = np.zeros_like(q)
     L = np.full((B, H, T), -math.inf)
@@ -53,7 +54,7 @@ def _brute_fwd(mode, q, k, v, kq, kk, bq, bk, strict=False, noncausal=False):
         for h in range(H):
             for i in range(T):
                 vis = []
-                for j in range(T if noncausal else (i if strict else i + 1)):
+                for j in range(Tk if noncausal else min(Tk, i if strict else i + 1)):
                     if mode in ("qk", "hash_keep") and not (kq[b, i, h] and kk[b, j, h]):
                         continue
                     if mode in ("hash", "hash_keep") and bq[b, h, i] != bk[b, h, j]:
@@ -468,6 +469,85 @@ def test_noncausal_bwd_central_finite_differences():
     eps = 1e-6
     loss = lambda a: float((oracle.attention_fwd("hash", a[0], a[1], a[2], kq, kk, bq, bk,  # noqa: E731
                                                  noncausal=True)[0] * dO).sum())
+    for which, g in zip(range(3), grads):
+        num = np.zeros_like(g)
+        for idx in np.ndindex(*g.shape):
+            a = [q.copy(), k.copy(), v.copy()]
+            a[which][idx] += eps
+            lp = loss(a)
+            a[which][idx] -= 2 * eps
+            num[idx] = (lp - loss(a)) / (2 * eps)
+        assert np.abs(num - g).max() <= 1e-6 * max(1.0, np.abs(num).max())
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash", "hash_keep"])
+@pytest.mark.parametrize("T,Tk,seed", [(9, 23, 50), (23, 9, 51), (1, 5, 52), (5, 1, 53)])
+@pytest.mark.parametrize("variant", ["causal", "strict", "noncausal"])
+def test_separate_lengths_match_pairwise_brute_force(mode, T, Tk, seed, variant):
+    """T_Q != T_KV: queries at 0..T-1, keys at 0..Tk-1, against pairwise
+    enumeration."""
+    _, _, q, k, v, kq, kk, bq, bk = _case(mode, T, seed=seed, Tk=Tk)
+    assert q.shape[1] == T and k.shape[1] == Tk and v.shape[1] == Tk
+    flags = {"strict": variant == "strict", "noncausal": variant == "noncausal"}
+    O, L = oracle.attention_fwd(_omode(mode), q, k, v, *_keeps(mode, kq, kk), bq, bk, **flags)
+    Ob, Lb = _brute_fwd(mode, q, k, v, kq, kk, bq, bk, **flags)
+    np.testing.assert_allclose(O, Ob, atol=1e-12, rtol=0)
+    assert np.array_equal(np.isinf(L), np.isinf(Lb))
+    fin = np.isfinite(Lb)
+    np.testing.assert_allclose(L[fin], Lb[fin], atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash"])
+def test_longer_keys_reduce_to_the_square_case(mode):
+    """Tk > Tq, causal: the keys after the last query are never visible, so
+    the result equals the square case on the first Tq keys, and those keys
+    get no gradient."""
+    _, x, q, k, v, kq, kk, bq, bk = _case(mode, 31, H=2, D=16, seed=54, Tk=50)
+    keeps = _keeps(mode, kq, kk)
+    sk = (None, None) if keeps[0] is None else (kq, kk[:, :31])
+    sb = (None, None) if bq is None else (bq, bk[:, :, :31])
+    O, L = oracle.attention_fwd(mode, q, k, v, *keeps, bq, bk)
+    O2, L2 = oracle.attention_fwd(mode, q, k[:, :31], v[:, :31], *sk, *sb)
+    np.testing.assert_allclose(O, O2, atol=1e-13, rtol=0)
+    assert np.array_equal(np.isinf(L), np.isinf(L2))
+    np.testing.assert_allclose(L[np.isfinite(L)], L2[np.isfinite(L2)], atol=1e-13, rtol=0)
+    dO = _np64(x["dO"])
+    dQ, dK, dV = oracle.attention_bwd(mode, q, k, v, dO, *keeps, bq, bk)
+    dQ2, dK2, dV2 = oracle.attention_bwd(mode, q, k[:, :31], v[:, :31], dO, *sk, *sb)
+    np.testing.assert_allclose(dQ, dQ2, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(dK[:, :31], dK2, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(dV[:, :31], dV2, atol=1e-13, rtol=0)
+    assert (dK[:, 31:] == 0).all() and (dV[:, 31:] == 0).all()
+
+
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash"])
+def test_longer_queries_split_into_square_and_bidirectional(mode):
+    """Tq > Tk, causal: the first Tk queries give the square case; every
+    later query sees every key, as in the non-causal result."""
+    _, x, q, k, v, kq, kk, bq, bk = _case(mode, 50, H=2, D=16, seed=55, Tk=31)
+    keeps = _keeps(mode, kq, kk)
+    O, L = oracle.attention_fwd(mode, q, k, v, *keeps, bq, bk)
+    sk = (None, None) if keeps[0] is None else (kq[:, :31], kk)
+    sb = (None, None) if bq is None else (bq[:, :, :31], bk)
+    O2, L2 = oracle.attention_fwd(mode, q[:, :31], k, v, *sk, *sb)
+    np.testing.assert_allclose(O[:, :31], O2, atol=1e-13, rtol=0)
+    assert np.array_equal(np.isinf(L[:, :, :31]), np.isinf(L2))
+    np.testing.assert_allclose(L[:, :, :31][np.isfinite(L2)], L2[np.isfinite(L2)], atol=1e-13, rtol=0)
+    On, Ln = oracle.attention_fwd(mode, q, k, v, *keeps, bq, bk, noncausal=True)
+    np.testing.assert_allclose(O[:, 31:], On[:, 31:], atol=1e-13, rtol=0)
+    assert np.array_equal(np.isinf(L[:, :, 31:]), np.isinf(Ln[:, :, 31:]))
+    fin = np.isfinite(Ln[:, :, 31:])
+    np.testing.assert_allclose(L[:, :, 31:][fin], Ln[:, :, 31:][fin], atol=1e-13, rtol=0)
+
+
+def test_separate_lengths_bwd_central_finite_differences():
+    _, x, q, k, v, kq, kk, bq, bk = _case("qk", 7, H=1, D=4, seed=56, keep_p=0.8, Tk=11)
+    dO = _np64(x["dO"])
+    assert dO.shape == q.shape
+    grads = oracle.attention_bwd("qk", q, k, v, dO, kq, kk, strict=True)
+    assert grads[1].shape == k.shape and grads[2].shape == v.shape
+    eps = 1e-6
+    loss = lambda a: float((oracle.attention_fwd("qk", a[0], a[1], a[2], kq, kk, strict=True)[0] * dO).sum())  # noqa: E731
     for which, g in zip(range(3), grads):
         num = np.zeros_like(g)
         for idx in np.ndindex(*g.shape):

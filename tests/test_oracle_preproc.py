@@ -201,3 +201,35 @@ def test_visible_pairs_brute_force(mode, strict, noncausal):
         assert (got == (45 * 45 if noncausal else 45 * 44 // 2 if strict else 45 * 46 // 2)).all()
     if mode == "qk" and noncausal:  # every kept query sees every kept key
         assert (got == (kq != 0).sum(axis=1) * (kk != 0).sum(axis=1)).all()
+
+
+@pytest.mark.parametrize("T,Tk", [(45, 70), (70, 45), (1, 9), (9, 1)])
+@pytest.mark.parametrize("strict,noncausal", [(False, False), (True, False), (False, True)])
+@pytest.mark.parametrize("mode", ["dense", "qk", "hash", "hash_keep"])
+def test_visible_pairs_separate_lengths_brute_force(mode, strict, noncausal, T, Tk):
+    omode = "hash" if mode == "hash_keep" else mode
+    w = small(omode, 2, 2, T, 16, keep_p=0.6, nb=4, seed=8, Tk=Tk)
+    x = make_inputs(w)
+    kq, kk = x["keep_q"].numpy(), x["keep_k"].numpy()
+    bq = bk = None
+    if omode == "hash":
+        R = x["R"].double().numpy()
+        bq = oracle.hash_bucket(x["q"].double().numpy(), R, 4)
+        bk = oracle.hash_bucket(x["k"].double().numpy(), R, 4)
+    keeps = (kq, kk) if mode in ("qk", "hash_keep") else (None, None)
+    got = oracle.visible_pairs(omode, T, 2, 2, *keeps, bq, bk, strict=strict, noncausal=noncausal, Tk=Tk)
+    for b in range(2):
+        for h in range(2):
+            n = 0
+            for i in range(T):
+                for j in range(Tk):
+                    if not noncausal and (j >= i if strict else j > i):
+                        continue
+                    if mode in ("qk", "hash_keep") and not (kq[b, i, h] and kk[b, j, h]):
+                        continue
+                    if omode == "hash" and bq[b, h, i] != bk[b, h, j]:
+                        continue
+                    n += 1
+            assert got[b, h] == n
+    if mode == "dense" and not strict and not noncausal:
+        assert (got == sum(min(i + 1, Tk) for i in range(T))).all()

@@ -175,3 +175,34 @@ def test_qk_end_is_a_prefix_and_pad_tiles_are_empty():
                 assert (ks[b, h, :e, 0] <= qmax).all() and (ks[b, h, e:, 0] > qmax).all()
                 if qmax < 0:
                     assert e == 0
+
+
+@pytest.mark.parametrize("variant", ["causal", "strict", "noncausal"])
+@pytest.mark.parametrize("mode,T,Tk,seed", [("dense", 300, 170, 20), ("dense", 170, 300, 21), ("qk", 500, 260, 22),
+                                             ("qk", 260, 500, 23), ("hash", 400, 700, 24), ("hash", 700, 400, 25)])
+def test_coverage_and_exactness_separate_lengths(mode, T, Tk, seed, variant):
+    """T_Q != T_KV: the same coverage and exactness rules on index arrays of
+    different lengths."""
+    w = small(mode, 1, 2, T, 16, keep_p=0.6, nb=8, seed=seed, Tk=Tk)
+    x = make_inputs(w)
+    if mode == "dense":
+        qi = np.broadcast_to(np.arange(T, dtype=np.int32), (1, 2, T)).copy()
+        ki = np.broadcast_to(np.arange(Tk, dtype=np.int32), (1, 2, Tk)).copy()
+        qb = kb = None
+    elif mode == "qk":
+        _, qi = oracle.qk_compact(None, x["keep_q"].numpy(), T, oracle.Q_PAD)
+        _, ki = oracle.qk_compact(None, x["keep_k"].numpy(), Tk, oracle.K_PAD)
+        qb = kb = None
+    else:
+        R = x["R"].double().numpy()
+        qi, qb, _ = oracle.hash_sort(oracle.hash_bucket(x["q"].double().numpy(), R, 8), 8)
+        ki, kb, _ = oracle.hash_sort(oracle.hash_bucket(x["k"].double().numpy(), R, 8), 8)
+    flags = {"strict": variant == "strict", "noncausal": variant == "noncausal"}
+    for Bm, Bn in ((128, 64), (64, 128)):
+        tab = oracle.range_tables(mode, qi, ki, qb, kb, Bm, Bn, **flags)
+        need = _tiles_with_visible_pair(qi, ki, qb, kb, Bm, Bn, **flags)
+        P = tab["P"]
+        assert P.shape[2:] == (-(-qi.shape[-1] // Bm), -(-ki.shape[-1] // Bn))
+        assert not (need & ~P).any(), "a tile holding a visible pair is skipped"
+        if mode in ("qk", "dense"):
+            assert (need == P).all(), "QK/dense processed set must be exact"
