@@ -157,7 +157,9 @@ int scfa_hash_bucket_counts(int dtype, const void* x, const float* R, int B, int
 /* scfa_hash_bucket_counts of the queries and of the keys in one launch (the
  * two share R; grid dimension z selects the side): the same outputs, bit for
  * bit, as two calls. Same definition and citation.
- *  q, k                (B, T, H, D) of one dtype, device.
+ *  q, k                (B, T, H, D) of one dtype, device: one length T for
+ *                      both (queries and keys of different lengths take
+ *                      scfa_hash_bucket_counts per side, without keep masks).
  *  keep_q, keep_k      optional (B, T, H) uint8 keep masks, both or neither:
  *                      hashing combined with within-bucket dropping (the SCFA
  *                      explainer's follow-up idea of a mask that is both
@@ -237,7 +239,8 @@ int scfa_hash_layout(const int32_t* bucket, const int32_t* chunk_counts, int B, 
  * SCFA_TILE_N and pad_idx = SCFA_K_PAD into Tseg_k rows. The same outputs,
  * bit for bit, as the two calls; the same citation.
  *  *_q / *_k      the arguments of scfa_hash_layout for that side (every
- *                 pointer required).
+ *                 pointer required); both sides have T tokens (different
+ *                 lengths take scfa_hash_layout per side).
  *  qstats, kstats optional (both with tiles, or all three NULL): the tile
  *                 statistics of the two aligned layouts, (B, H, Tseg_q /
  *                 SCFA_TILE_M, 4) and (B, H, Tseg_k / SCFA_TILE_N, 4), the
@@ -357,11 +360,12 @@ int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, con
  *                same flag.
  *  dtype_in      SCFA_BF16 / SCFA_F32 of q, k, v.
  *  dtype_out     SCFA_F32 / SCFA_BF16 of O.
- *  q, k, v       (B, T, H, D) the ORIGINAL, unpermuted tensors (D = 64).
- *                The gather of the preprocessing is fused into the loads:
- *                row r of a head reads token q_idx[r] (k_idx[r] for k and
- *                v); pad entries (any index outside [0, T)) read token 0,
- *                whose values must be finite.
+ *  q             (B, T, H, D) and k, v (B, T_kv, H, D): the ORIGINAL,
+ *                unpermuted tensors (D = 64). The gather of the
+ *                preprocessing is fused into the loads: row r of a head
+ *                reads token q_idx[r] of q (k_idx[r] of k and v); pad
+ *                entries (any index outside [0, T) / [0, T_kv)) read token
+ *                0, whose values must be finite.
  *  q_idx, k_idx  (B, H, Tpad) original positions with pads.
  *  q_bkt, k_bkt  (B, H, Tpad) sorted bucket ids (hash only).
  *  qstats, kstats, fwd_tab   from scfa_range_table with Bm = SCFA_TILE_M,
@@ -369,7 +373,12 @@ int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, con
  *  order         (B*H*nQt) launch order from scfa_work_order on fwd_tab, or
  *                NULL (then query tiles run in descending index order). Any
  *                permutation gives the same results; only the schedule moves.
- *  T             original sequence length (rows of O and LSE).
+ *  T             original query length (rows of O and LSE).
+ *  T_kv          original key/value length; T_kv != T follows the
+ *                explainer's separate decision-tensor lengths T_Q and T_KV
+ *                ("QK-Sparse Attention: Compaction and Index-Guided
+ *                Tiling"): query and key positions both count from 0 and the
+ *                position test compares them unchanged.
  *  Tc            QK: compacted length (multiple of 128); Tpad = Tc.
  *  scale         score scale, normally 1/sqrt(D).
  *  O             out (B, T, H, D), every row written.
@@ -377,8 +386,8 @@ int scfa_count_visible(int mode, const int32_t* q_idx, const int32_t* k_idx, con
  *                written (-inf for rows without a visible key).           */
 int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v,
                        const int32_t* q_idx, const int32_t* k_idx, const int32_t* qstats, const int32_t* kstats,
-                       const int32_t* fwd_tab, const int32_t* order, int B, int H, int T, int Tc, int D, float scale,
-                       int flags, void* O, float* lse, hipStream_t stream);
+                       const int32_t* fwd_tab, const int32_t* order, int B, int H, int T, int T_kv, int Tc, int D,
+                       float scale, int flags, void* O, float* lse, hipStream_t stream);
 
 /* Hash-sparse: as above, with the sorted (or bucket-aligned) index arrays
  * and
@@ -389,8 +398,8 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
 int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v,
                          const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
                          const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, const int32_t* order,
-                         int B, int H, int T, int Tq, int Tk, int D, float scale, int flags, void* O, float* lse,
-                         hipStream_t stream);
+                         int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale, int flags, void* O,
+                         float* lse, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Backward attention (recomputation from the saved LSE).
@@ -406,20 +415,22 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
  *                SCFA_NONCAUSAL.
  *  dtype_in      SCFA_BF16 (the only backward build; fp32 returns
  *                SCFA_ERR_UNSUPPORTED).
- *  q, k, v       (B, T, H, D) the original tensors of the forward call,
- *                read through q_idx / k_idx like the forward (pad entries
- *                read token 0).
+ *  q             (B, T, H, D), k, v (B, T_kv, H, D): the original tensors
+ *                of the forward call, read through q_idx / k_idx like the
+ *                forward (pad entries read token 0).
  *  q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab
  *                exactly the index arrays and tables of the forward call.
  *  bwd_tab       the backward table of the same call (scfa_range_table or
  *                scfa_bwd_table).
  *  O             (B, T, H, D) fp32 forward output;  lse (B, H, T) fp32.
  *  dO            (B, T, H, D) upstream gradient, dtype_in.
- *  T             original sequence length; Tq, Tk query / key rows as
+ *  T, T_kv       original query and key/value lengths, as in the forward;
+ *  Tq, Tk        query / key rows as
  *                passed to scfa_range_table (Tc and Tc for QK; T and T for the
  *                sorted hash order, Tseg_q and Tseg_k for the bucket-aligned
  *                layout); the buffers hold SCFA_PAD(Tq) / SCFA_PAD(Tk) rows.
- *  dQ, dK, dV    out (B, T, H, D) fp32 in original order, every row
+ *  dQ            out (B, T, H, D), dK, dV out (B, T_kv, H, D): fp32 in
+ *                original order, every row
  *                written (zero for dropped tokens and tokens without any
  *                visible pair).
  *  workspace     device scratch of scfa_bwd_workspace_bytes() bytes (Delta
@@ -430,8 +441,8 @@ size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D);
 int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
              const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
              const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
-             const void* dO, int B, int H, int T, int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV,
-             void* workspace, size_t workspace_bytes, hipStream_t stream);
+             const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale, float* dQ, float* dK,
+             float* dV, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -73,6 +73,7 @@ struct BwdParams {
   float* dK;
   float* dV;
   int B, H, T;
+  int Tkv;       // tokens of the original k and v tensors (B, Tkv, H, D); T is that of q, dO
   int Tq, Tk;    // valid query / key rows (as passed to the range table)
   int TqP, TkP;  // rows per head of the query-side / key-side index arrays
   int nQt, nKt;
@@ -277,17 +278,18 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   auto qstat = [&](int i) { return uniform4(qst_lds ? Qst[i - rng.x] : qst[i]); };
 
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
-  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;
+  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;     // token 0 of this head in q, dO
+  const size_t khead0 = (static_cast<size_t>(b) * p.Tkv * p.H + h) * HD * 2;  // and in k, v
   const int krow = kt * BN + w * 16 + r16;  // this lane's key
   const int kpos = p.k_idx[kbase + krow];
   const int kbkt = HASH ? p.k_bkt[kbase + krow] : 0;
   // the smallest query position that sees this key (kpos + 1 when strict):
   // masks and tile tests compare queries against it
   const int kcmp = k_reach(p.rc, kpos);
-  const WaveKeys wk = wave_keys(kpos, kbkt, p.T, p.rc);
+  const WaveKeys wk = wave_keys(kpos, kbkt, p.Tkv, p.rc);
   bf16x8 Kb[2], Vb[2];
   {
-    const size_t off = head0 + static_cast<size_t>(src_row(kpos, p.T)) * rstride;
+    const size_t off = khead0 + static_cast<size_t>(src_row(kpos, p.Tkv)) * rstride;
 #pragma unroll
     for (int ds = 0; ds < 2; ++ds) {
       Kb[ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.k) + off + (ds * 32 + g * 8) * 2);
@@ -449,9 +451,9 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   stage_rows(tk, row, g, dKa, p.scale);
   stage_rows(tv, row, g, dVa, 1.f);
   __syncthreads();
-  write_rows(tk, Ki, BN, p.dK, p.T, p.H, b, h);
-  write_rows(tv, Ki, BN, p.dV, p.T, p.H, b, h);
-  if constexpr (ZD) zero_unheld<BN>(p.k_idx + kbase, Ki, kt, p.TkP, p.T, p.H, b, h, p.dK, p.dV);
+  write_rows(tk, Ki, BN, p.dK, p.Tkv, p.H, b, h);
+  write_rows(tv, Ki, BN, p.dV, p.Tkv, p.H, b, h);
+  if constexpr (ZD) zero_unheld<BN>(p.k_idx + kbase, Ki, kt, p.TkP, p.Tkv, p.H, b, h, p.dK, p.dV);
 }
 
 // Extrema of this wave's 32 keys (two blocks of 16; lane column r16 in each).
@@ -541,7 +543,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   auto qstat = [&](int i) { return uniform4(qst_lds ? Qst[i - lo] : qst[i]); };
 
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
-  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;
+  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;     // token 0 of this head in q, dO
+  const size_t khead0 = (static_cast<size_t>(b) * p.Tkv * p.H + h) * HD * 2;  // and in k, v
   int kpos[2], kbkt[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -549,13 +552,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     kpos[kb] = Ki[r];
     kbkt[kb] = HASH ? ((r < BN || has1) ? p.k_bkt[kbase + kt0 * BN + r] : 0) : 0;
   }
-  const WaveKeys wk = wave_keys2(kpos, kbkt, p.T, p.rc);
+  const WaveKeys wk = wave_keys2(kpos, kbkt, p.Tkv, p.rc);
   // the smallest query position that sees each key (kpos + 1 when strict)
   const int kcmp[2] = {k_reach(p.rc, kpos[0]), k_reach(p.rc, kpos[1])};
   bf16x8 Kb[2][2], Vb[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const size_t off = head0 + static_cast<size_t>(src_row(kpos[kb], p.T)) * rstride;
+    const size_t off = khead0 + static_cast<size_t>(src_row(kpos[kb], p.Tkv)) * rstride;
 #pragma unroll
     for (int ds = 0; ds < 2; ++ds) {
       Kb[kb][ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.k) + off + (ds * 32 + g * 8) * 2);
@@ -744,15 +747,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) stage_rows(tg, w * 32 + kb * 16 + r16, g, dKa[kb], p.scale);
   __syncthreads();
-  write_rows(tg, Ki, nrows, p.dK, p.T, p.H, b, h);
+  write_rows(tg, Ki, nrows, p.dK, p.Tkv, p.H, b, h);
   __syncthreads();
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) stage_rows(tg, w * 32 + kb * 16 + r16, g, dVa[kb], 1.f);
   __syncthreads();
-  write_rows(tg, Ki, nrows, p.dV, p.T, p.H, b, h);
+  write_rows(tg, Ki, nrows, p.dV, p.Tkv, p.H, b, h);
   if constexpr (ZD) {
-    zero_unheld<BN>(p.k_idx + kbase, Ki, kt0, p.TkP, p.T, p.H, b, h, p.dK, p.dV);
-    if (has1) zero_unheld<BN>(p.k_idx + kbase, Ki + BN, kt0 + 1, p.TkP, p.T, p.H, b, h, p.dK, p.dV);
+    zero_unheld<BN>(p.k_idx + kbase, Ki, kt0, p.TkP, p.Tkv, p.H, b, h, p.dK, p.dV);
+    if (has1) zero_unheld<BN>(p.k_idx + kbase, Ki + BN, kt0 + 1, p.TkP, p.Tkv, p.H, b, h, p.dK, p.dV);
   }
 }
 
@@ -791,7 +794,8 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   auto kstat = [&](int j) { return uniform4(kst_lds ? Kst[j - rng.x] : kst[j]); };
 
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;
-  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;
+  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;     // token 0 of this head in q, dO
+  const size_t khead0 = (static_cast<size_t>(b) * p.Tkv * p.H + h) * HD * 2;  // and in k, v
   const int q0 = qt * BM + w * 32;
   int qpos[2], qbkt[2];
   float ql2[2], qdl[2];
@@ -820,8 +824,8 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
     for (int qb = 0; qb < 2; ++qb) dQa[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- DMA staging of a key tile: wave w stages rows 16w .. 16w+15 --------
-  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + head0;
-  const uint8_t* vg = static_cast<const uint8_t*>(p.v) + head0;
+  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + khead0;
+  const uint8_t* vg = static_cast<const uint8_t*>(p.v) + khead0;
   const int32_t* kig = p.k_idx + kbase;
   const int32_t* kbg = HASH ? p.k_bkt + kbase : nullptr;
   uint32_t rch[2], tch[2];
@@ -841,7 +845,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
     const uint32_t base = lds0 + s * 3 * TB + ws * 2048;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t off = static_cast<uint32_t>(src_row(pos[i], p.T)) * rstride;
+      const uint32_t off = static_cast<uint32_t>(src_row(pos[i], p.Tkv)) * rstride;
       dma16(kg, off + rch[i], base + i * 1024);
       dma16(kg, off + tch[i], base + TB + i * 1024);
       dma16(vg, off + rch[i], base + 2 * TB + i * 1024);
@@ -995,7 +999,8 @@ size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D) {
 int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
              const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
              const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
-             const void* dO, int B, int H, int T, int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV,
+             const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale, float* dQ, float* dK,
+             float* dV,
              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int flags = take_flags(mode);
   if (!flags_ok(flags) || (mode != SCFA_QK && mode != SCFA_HASH)) return SCFA_ERR_INVALID;
@@ -1003,12 +1008,13 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
       !dK || !dV || !workspace)
     return SCFA_ERR_INVALID;
   if (mode == SCFA_HASH && (!q_bkt || !k_bkt)) return SCFA_ERR_INVALID;
-  if (B < 1 || H < 1 || T < 1 || Tq < 1 || Tk < 1 || !(scale > 0.f) || !isfinite(scale)) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || T < 1 || T_kv < 1 || Tq < 1 || Tk < 1 || !(scale > 0.f) || !isfinite(scale))
+    return SCFA_ERR_INVALID;
   if (!dtype_ok(dtype_in)) return SCFA_ERR_INVALID;
   if (D != HD || dtype_in != SCFA_BF16) return SCFA_ERR_UNSUPPORTED;
   // row offsets within one batch entry's (T, H, D) block are 32-bit
-  if (static_cast<uint64_t>(T) * H * D * 2 > 0xFFFFFFFFull) return SCFA_ERR_UNSUPPORTED;
-  if ((flags & SCFA_NONCAUSAL) && T > kPosLimit) return SCFA_ERR_UNSUPPORTED;
+  if (static_cast<uint64_t>(max(T, T_kv)) * H * D * 2 > 0xFFFFFFFFull) return SCFA_ERR_UNSUPPORTED;
+  if ((flags & SCFA_NONCAUSAL) && max(T, T_kv) > kPosLimit) return SCFA_ERR_UNSUPPORTED;
   if (mode == SCFA_QK && (Tq % SCFA_ROW_ALIGN || Tk != Tq)) return SCFA_ERR_INVALID;
   const int TqP = pad_rows(Tq), TkP = pad_rows(Tk);
   size_t off[3];
@@ -1036,6 +1042,7 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
   p.B = B;
   p.H = H;
   p.T = T;
+  p.Tkv = T_kv;
   p.Tq = Tq;
   p.Tk = Tk;
   p.TqP = TqP;

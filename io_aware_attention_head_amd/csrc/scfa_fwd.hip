@@ -74,6 +74,7 @@ struct FwdParams {
   void* O;
   float* lse;
   int B, H, T;
+  int Tkv;   // tokens of the original k and v tensors (B, Tkv, H, D)
   int Tk;    // valid key rows (extrema/ragged test)
   int TqPad;  // rows per head of the query-side index arrays (q_idx, q_bkt)
   int TkPad;  // rows per head of the key-side index arrays (k_idx, k_bkt)
@@ -274,7 +275,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                      __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
   };
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
-  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;  // token 0 of this head
+  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;     // token 0 of this head in q
+  const size_t khead0 = (static_cast<size_t>(b) * p.Tkv * p.H + h) * HD * 2;  // and in k, v
 
   // ---- queries of this wave: B operand, positions, buckets --------------
   const int q0 = qt * BM + w * 32;
@@ -309,8 +311,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   // Wave w stages rows 16w .. 16w+15 of the K and V tiles, 8 rows (1 KB) per
   // instruction: lane l writes chunk position l % 8 of row 16w + 8i + l / 8
   // and reads the chunk of that row's token that the swizzle puts there.
-  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + head0;
-  const uint8_t* vg = static_cast<const uint8_t*>(p.v) + head0;
+  const uint8_t* kg = static_cast<const uint8_t*>(p.k) + khead0;
+  const uint8_t* vg = static_cast<const uint8_t*>(p.v) + khead0;
   const int32_t* kig = p.k_idx + kbase;
   const int32_t* kbg = HASH ? p.k_bkt + kbase : nullptr;
   uint32_t kch[2], vch[2];
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const uint32_t ks = lds0 + s * TB + ws * 2048, vs = lds0 + (2 + s) * TB + ws * 2048;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t off = static_cast<uint32_t>(src_row(pos[i], p.T)) * rstride;
+      const uint32_t off = static_cast<uint32_t>(src_row(pos[i], p.Tkv)) * rstride;
       dma16(kg, off + kch[i], ks + i * 1024);
       dma16(vg, off + vch[i], vs + i * 1024);
     }
@@ -488,7 +490,8 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
   if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];
   const size_t rstride = static_cast<size_t>(p.H) * HD;                 // floats between token rows
-  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD;  // token 0 of this head
+  const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD;     // token 0 of this head in q
+  const size_t khead0 = (static_cast<size_t>(b) * p.Tkv * p.H + h) * HD;  // and in k, v
 
   const int q0 = qt * BM + w * 32;
   int qpos[2], qbkt[2];
@@ -523,8 +526,8 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
   float m[2] = {-INFINITY, -INFINITY};
   float l[2] = {0.f, 0.f};
 
-  const float* kg = static_cast<const float*>(p.k) + head0;
-  const float* vg = static_cast<const float*>(p.v) + head0;
+  const float* kg = static_cast<const float*>(p.k) + khead0;
+  const float* vg = static_cast<const float*>(p.v) + khead0;
   const int32_t* kig = p.k_idx + kbase;
   const int32_t* kbg = HASH ? p.k_bkt + kbase : nullptr;
 
@@ -535,7 +538,7 @@ __global__ __launch_bounds__(256) void k_fwd_f32(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = tid + 256 * i, row = u >> 4, ch = u & 15;
-      const size_t off = src_row(kig[j * BN + row], p.T) * rstride + ch * 4;
+      const size_t off = src_row(kig[j * BN + row], p.Tkv) * rstride + ch * 4;
       const float4 kr = *reinterpret_cast<const float4*>(kg + off);
       const float4 vr = *reinterpret_cast<const float4*>(vg + off);
       *reinterpret_cast<float4*>(Ks + row * HD * 4 + ((ch ^ swz_k(row)) * 16)) = kr;
@@ -639,13 +642,13 @@ int dispatch_fwd(int dtype_in, int dtype_out, const FwdParams& p, hipStream_t st
   return SCFA_OK;
 }
 
-int check_common(int dtype_in, int dtype_out, int B, int H, int T, int D, float scale) {
+int check_common(int dtype_in, int dtype_out, int B, int H, int T, int T_kv, int D, float scale) {
   if (!dtype_ok(dtype_in) || !dtype_ok(dtype_out)) return SCFA_ERR_INVALID;
-  if (B < 1 || H < 1 || T < 1) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || T < 1 || T_kv < 1) return SCFA_ERR_INVALID;
   if (!(scale > 0.f) || !isfinite(scale)) return SCFA_ERR_INVALID;
   if (D != HD) return SCFA_ERR_UNSUPPORTED;
   // row offsets within one batch entry's (T, H, D) block are 32-bit
-  if (static_cast<uint64_t>(T) * H * D * dtype_size(dtype_in) > 0xFFFFFFFFull) return SCFA_ERR_UNSUPPORTED;
+  if (static_cast<uint64_t>(max(T, T_kv)) * H * D * dtype_size(dtype_in) > 0xFFFFFFFFull) return SCFA_ERR_UNSUPPORTED;
   return SCFA_OK;
 }
 
@@ -658,13 +661,14 @@ extern "C" {
 
 int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v,
                        const int32_t* q_idx, const int32_t* k_idx, const int32_t* qstats, const int32_t* kstats,
-                       const int32_t* fwd_tab, const int32_t* order, int B, int H, int T, int Tc, int D, float scale,
+                       const int32_t* fwd_tab, const int32_t* order, int B, int H, int T, int T_kv, int Tc, int D,
+                       float scale,
                        int flags, void* O, float* lse, hipStream_t stream) {
   if (!q || !k || !v || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !O || !lse) return SCFA_ERR_INVALID;
   if (!flags_ok(flags)) return SCFA_ERR_INVALID;
-  const int st = check_common(dtype_in, dtype_out, B, H, T, D, scale);
+  const int st = check_common(dtype_in, dtype_out, B, H, T, T_kv, D, scale);
   if (st != SCFA_OK) return st;
-  if ((flags & SCFA_NONCAUSAL) && T > kPosLimit) return SCFA_ERR_UNSUPPORTED;
+  if ((flags & SCFA_NONCAUSAL) && max(T, T_kv) > kPosLimit) return SCFA_ERR_UNSUPPORTED;
   if (Tc < SCFA_ROW_ALIGN || Tc % SCFA_ROW_ALIGN) return SCFA_ERR_INVALID;
   FwdParams p{};
   p.q = q;
@@ -683,6 +687,7 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
   p.B = B;
   p.H = H;
   p.T = T;
+  p.Tkv = T_kv;
   p.Tk = Tc;
   p.TqPad = Tc;
   p.TkPad = Tc;
@@ -696,14 +701,15 @@ int scfa_qk_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k
 int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void* k, const void* v,
                          const int32_t* q_idx, const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt,
                          const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, const int32_t* order,
-                         int B, int H, int T, int Tq, int Tk, int D, float scale, int flags, void* O, float* lse,
+                         int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale, int flags, void* O,
+                         float* lse,
                          hipStream_t stream) {
   if (!q || !k || !v || !q_idx || !k_idx || !q_bkt || !k_bkt || !qstats || !kstats || !fwd_tab || !O || !lse)
     return SCFA_ERR_INVALID;
   if (!flags_ok(flags)) return SCFA_ERR_INVALID;
-  const int st = check_common(dtype_in, dtype_out, B, H, T, D, scale);
+  const int st = check_common(dtype_in, dtype_out, B, H, T, T_kv, D, scale);
   if (st != SCFA_OK) return st;
-  if ((flags & SCFA_NONCAUSAL) && T > kPosLimit) return SCFA_ERR_UNSUPPORTED;
+  if ((flags & SCFA_NONCAUSAL) && max(T, T_kv) > kPosLimit) return SCFA_ERR_UNSUPPORTED;
   if (Tq < 1 || Tk < 1) return SCFA_ERR_INVALID;
   FwdParams p{};
   p.q = q;
@@ -722,6 +728,7 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
   p.B = B;
   p.H = H;
   p.T = T;
+  p.Tkv = T_kv;
   p.Tk = Tk;
   p.TqPad = pad_rows(Tq);
   p.TkPad = pad_rows(Tk);

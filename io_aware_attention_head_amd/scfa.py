@@ -59,13 +59,13 @@ _SIGS = {
     "scfa_range_table": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_count_visible": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_work_order": (_i, [_vp, _i, _i, _i, _i, _vp, _vp]),
-    "scfa_qk_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+    "scfa_qk_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                                 _vp, _vp, _vp]),
     "scfa_hash_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
-                                  _i, _f, _i, _vp, _vp, _vp]),
+                                  _i, _i, _f, _i, _vp, _vp, _vp]),
     "scfa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "scfa_bwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
-                      _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
+                      _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 _LIB = None
@@ -278,32 +278,41 @@ def scfa_work_order(tab, span, order, stream=None):
     _check(lib().scfa_work_order(_p(tab), B, H, n, span, _p(order), _stream(stream, tab)), "scfa_work_order")
 
 
+def _kv_len(q, k, v) -> int:
+    """Tokens of the original k and v tensors (B, T_kv, H, D)."""
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
+        raise ScfaError("k and v must be (B, T_kv, H, D) with the B, H, D of q")
+    return k.shape[1]
+
+
 def scfa_qk_sparse_fwd(q, k, v, q_idx, k_idx, qstats, kstats, fwd_tab, T, O, lse, scale=None, stream=None,
                        order=None, flags=0):
-    """q, k, v: original (B,T,H,D) tensors; q_idx, k_idx (B,H,Tc) compacted."""
+    """q: original (B,T,H,D), k, v: original (B,T_kv,H,D) tensors; q_idx,
+    k_idx (B,H,Tc) compacted."""
     B, Tq_, H, D = q.shape
     if Tq_ != T:
         raise ScfaError("q must be the original (B,T,H,D) tensor")
     Tc = q_idx.shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(lib().scfa_qk_sparse_fwd(_dt(q), _dt(O), _p(q), _p(k), _p(v), _p(q_idx), _p(k_idx), _p(qstats),
-                                    _p(kstats), _p(fwd_tab), _p(order), B, H, T, Tc, D, scale, flags, _p(O), _p(lse),
-                                    _stream(stream, q)), "scfa_qk_sparse_fwd")
+                                    _p(kstats), _p(fwd_tab), _p(order), B, H, T, _kv_len(q, k, v), Tc, D, scale, flags,
+                                    _p(O), _p(lse), _stream(stream, q)), "scfa_qk_sparse_fwd")
 
 
 def scfa_hash_sparse_fwd(q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, T, O, lse, scale=None,
                          stream=None, order=None, Tq=None, Tk=None, flags=0):
-    """q, k, v: original (B,T,H,D) tensors. Tq / Tk: query / key rows as
-    passed to the range table (default: T)."""
+    """q: original (B,T,H,D), k, v: original (B,T_kv,H,D) tensors. Tq / Tk:
+    query / key rows as passed to the range table (default: T, T_kv)."""
     B, Tq_, H, D = q.shape
     if Tq_ != T:
         raise ScfaError("q must be the original (B,T,H,D) tensor")
+    T_kv = _kv_len(q, k, v)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     Tq = T if Tq is None else Tq
-    Tk = T if Tk is None else Tk
+    Tk = T_kv if Tk is None else Tk
     _check(lib().scfa_hash_sparse_fwd(_dt(q), _dt(O), _p(q), _p(k), _p(v), _p(q_idx), _p(k_idx), _p(q_bkt),
-                                      _p(k_bkt), _p(qstats), _p(kstats), _p(fwd_tab), _p(order), B, H, T, Tq, Tk, D,
-                                      scale, flags, _p(O), _p(lse), _stream(stream, q)), "scfa_hash_sparse_fwd")
+                                      _p(k_bkt), _p(qstats), _p(kstats), _p(fwd_tab), _p(order), B, H, T, T_kv, Tq, Tk,
+                                      D, scale, flags, _p(O), _p(lse), _stream(stream, q)), "scfa_hash_sparse_fwd")
 
 
 def scfa_bwd_workspace_bytes(mode, B, H, Tq, Tk, D=64) -> int:
@@ -312,13 +321,15 @@ def scfa_bwd_workspace_bytes(mode, B, H, Tq, Tk, D=64) -> int:
 
 def scfa_bwd(mode, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, T, Tq, Tk, dQ,
              dK, dV, workspace, scale=None, stream=None):
-    """q, k, v, dO: original (B,T,H,D) bf16 tensors (read through the index arrays)."""
+    """q, dO: original (B,T,H,D), k, v: original (B,T_kv,H,D) bf16 tensors
+    (read through the index arrays)."""
     B, Tq_, H, D = q.shape
     if Tq_ != T:
         raise ScfaError("q must be the original (B,T,H,D) tensor")
+    T_kv = _kv_len(q, k, v)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(lib().scfa_bwd(mode, _dt(q), _p(q), _p(k), _p(v), _p(q_idx), _p(k_idx), _p(q_bkt), _p(k_bkt), _p(qstats),
-                          _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(O), _p(lse), _p(dO), B, H, T, Tq, Tk, D, scale,
+                          _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(O), _p(lse), _p(dO), B, H, T, T_kv, Tq, Tk, D, scale,
                           _p(dQ), _p(dK), _p(dV), _p(workspace), workspace.numel() * workspace.element_size(),
                           _stream(stream, q)), "scfa_bwd")
 
@@ -398,12 +409,14 @@ def prepare_qk(q, k, v, keep_q, keep_k, Tc: Optional[int] = None, rows: bool = F
     rows=True also the compacted Q and K rows). Reads the max kept count back
     to the host once (to size Tc) unless Tc is given."""
     B, T, H, D = q.shape
+    T_kv = _kv_len(q, k, v)
     dev = q
     i32 = torch.int32
-    nC = (T + SCFA_COUNT_CHUNK - 1) // SCFA_COUNT_CHUNK
+    nCq = (T + SCFA_COUNT_CHUNK - 1) // SCFA_COUNT_CHUNK
+    nCk = (T_kv + SCFA_COUNT_CHUNK - 1) // SCFA_COUNT_CHUNK
     cq, ck = _empty((B, H), i32, dev), _empty((B, H), i32, dev)
     mq, mk = _empty((1,), i32, dev), _empty((1,), i32, dev)
-    oq, ok = _empty((B, H, nC), i32, dev), _empty((B, H, nC), i32, dev)
+    oq, ok = _empty((B, H, nCq), i32, dev), _empty((B, H, nCk), i32, dev)
     scfa_qk_count(keep_q, cq, mq, oq, stream)
     scfa_qk_count(keep_k, ck, mk, ok, stream)
     if Tc is None:
@@ -429,12 +442,15 @@ def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None, keep_q=
     the buckets come from the two-side launch, dropped queries in bucket nb and
     dropped keys in bucket nb + 1, and the sort has nb + 2 buckets."""
     B, T, H, D = q.shape
+    T_kv = _kv_len(q, k, v)
     dev = q
     i32 = torch.int32
-    Tp = pad_rows(T)
+    Tp, Tkp = pad_rows(T), pad_rows(T_kv)
     nbs = nb if keep_q is None and keep_k is None else nb + 2  # buckets of the sort
-    bq, bk = _empty((B, H, T), i32, dev), _empty((B, H, T), i32, dev)
-    cq, ck = _empty(chunk_count_shape(B, H, T, nbs), i32, dev), _empty(chunk_count_shape(B, H, T, nbs), i32, dev)
+    if nbs != nb and T_kv != T:
+        raise ScfaError("hashing with dropping needs queries and keys of one length")
+    bq, bk = _empty((B, H, T), i32, dev), _empty((B, H, T_kv), i32, dev)
+    cq, ck = _empty(chunk_count_shape(B, H, T, nbs), i32, dev), _empty(chunk_count_shape(B, H, T_kv, nbs), i32, dev)
     if nbs == nb:
         scfa_hash_bucket_counts(q, R, nb, bq, cq, stream)
         scfa_hash_bucket_counts(k, R, nb, bk, ck, stream)
@@ -442,15 +458,15 @@ def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None, keep_q=
         scfa_hash_bucket_qk(q, k, R, nb, bq, bk, cq, ck, stream, keep_q, keep_k)
     nb = nbs
     dev_err = torch.zeros((1,), dtype=i32, device=q.device)
-    perm_q, perm_k = _empty((B, H, Tp), i32, dev), _empty((B, H, Tp), i32, dev)
-    bs_q, bs_k = _empty((B, H, Tp), i32, dev), _empty((B, H, Tp), i32, dev)
+    perm_q, perm_k = _empty((B, H, Tp), i32, dev), _empty((B, H, Tkp), i32, dev)
+    bs_q, bs_k = _empty((B, H, Tp), i32, dev), _empty((B, H, Tkp), i32, dev)
     offq, offk = _empty((B, H, nb + 1), i32, dev), _empty((B, H, nb + 1), i32, dev)
     extra = {"bucket_q": bq, "bucket_k": bk, "chunk_counts_q": cq, "chunk_counts_k": ck, "perm_q": perm_q,
              "perm_k": perm_k, "sorted_bkt_q": bs_q, "sorted_bkt_k": bs_k, "offsets_q": offq, "offsets_k": offk,
              "dev_err": dev_err, "sort_buckets": nb}
     if aligned:
         Tq = scfa_hash_segment_rows(T, nb, SCFA_TILE_M)
-        Tk = scfa_hash_segment_rows(T, nb, SCFA_TILE_N)
+        Tk = scfa_hash_segment_rows(T_kv, nb, SCFA_TILE_N)
         q_idx, q_bkt = _empty((B, H, Tq), i32, dev), _empty((B, H, Tq), i32, dev)
         k_idx, k_bkt = _empty((B, H, Tk), i32, dev), _empty((B, H, Tk), i32, dev)
         sq, sk = _empty((B, H, nb + 1), i32, dev), _empty((B, H, nb + 1), i32, dev)
@@ -460,20 +476,22 @@ def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None, keep_q=
     else:
         scfa_hash_layout(bq, cq, nb, 0, SCFA_Q_PAD, perm_q, bs_q, offq, dev_err=dev_err, stream=stream)
         scfa_hash_layout(bk, ck, nb, 0, SCFA_K_PAD, perm_k, bs_k, offk, dev_err=dev_err, stream=stream)
-        Tq = Tk = T
+        Tq, Tk = T, T_kv
         q_idx, k_idx, q_bkt, k_bkt = perm_q, perm_k, bs_q, bs_k
     return Prepared("hash", B, H, T, D, Tq, Tk, q, k, v, q_idx, k_idx, q_bkt, k_bkt, extra=extra, strict=strict,
                     noncausal=noncausal)
 
 
 def prepare_dense(q, k, v, stream=None, strict: bool = False, noncausal: bool = False) -> Prepared:
-    """Dense causal attention on the same kernel: positions 0..T-1 for both
-    queries and keys (the QK path with nothing dropped)."""
+    """Dense causal attention on the same kernel: positions 0..T-1 for the
+    queries and 0..T_kv-1 for the keys (the QK path with nothing dropped;
+    both index arrays padded to one length, as the QK path's compacted ones)."""
     B, T, H, D = q.shape
-    Tp = pad_rows(T)
+    T_kv = _kv_len(q, k, v)
+    Tp = pad_rows(max(T, T_kv))
     ar = torch.arange(Tp, dtype=torch.int32, device=q.device)
     q_idx = torch.where(ar < T, ar, torch.full_like(ar, SCFA_Q_PAD)).expand(B, H, Tp).contiguous()
-    k_idx = torch.where(ar < T, ar, torch.full_like(ar, SCFA_K_PAD)).expand(B, H, Tp).contiguous()
+    k_idx = torch.where(ar < T_kv, ar, torch.full_like(ar, SCFA_K_PAD)).expand(B, H, Tp).contiguous()
     return Prepared("dense", B, H, T, D, Tp, Tp, q, k, v, q_idx, k_idx, strict=strict, noncausal=noncausal)
 
 
@@ -535,7 +553,8 @@ def backward(pre: Prepared, tab: Tables, O, lse, dO, scale=None, grads=None, wor
     B, H, T, D = pre.B, pre.H, pre.T, pre.D
     mode = _table_mode(pre.mode)
     if grads is None:
-        grads = tuple(_empty((B, T, H, D), torch.float32, pre.q_in) for _ in range(3))
+        T_kv = pre.k_in.shape[1]
+        grads = tuple(_empty((B, n, H, D), torch.float32, pre.q_in) for n in (T, T_kv, T_kv))
     if workspace is None:
         workspace = _empty((scfa_bwd_workspace_bytes(mode, B, H, pre.Tq, pre.Tk, D),), torch.uint8, pre.q_in)
     dQ, dK, dV = grads
@@ -575,14 +594,21 @@ class Plan:
                  fixed compacted length Tc (default: pad_rows(T), which always
                  fits).
     mode "dense": tables -> forward on positions 0..T-1.
+    T_kv: key/value length when it differs from the query length T (keys at
+    positions 0..T_kv-1); hash mode then runs the one-side bucket and layout
+    launches per side and builds the tile statistics with the tables.
     Forward and backward read the operands through the index arrays (no
     gathered copies). Each stage is a separate method so it can be timed on
     its own.
     """
 
     def __init__(self, mode, B, H, T, D=64, dtype=torch.bfloat16, nb=16, Tc=None, out_dtype=torch.float32,
-                 device="cuda", scale=None, strict=False, noncausal=False):
+                 device="cuda", scale=None, strict=False, noncausal=False, T_kv=None):
         self.drop = mode == "hash_drop"
+        self.T_kv = T if T_kv is None else T_kv
+        self.two_side = self.T_kv == T  # queries and keys bucketed and laid out in one launch each
+        if self.drop and not self.two_side:
+            raise ScfaError("hash_drop needs queries and keys of one length")
         if self.drop:
             mode = "hash"
             if nb > 62:
@@ -601,20 +627,21 @@ class Plan:
         d = torch.device(device)
         i32 = torch.int32
         e = lambda shape, dt=i32: torch.empty(shape, dtype=dt, device=d)  # noqa: E731
+        Tkv = self.T_kv
         if mode == "qk":
-            Tc = Tc if Tc is not None else pad_rows(T)
+            Tc = Tc if Tc is not None else pad_rows(max(T, Tkv))
             if Tc % SCFA_ROW_ALIGN:
                 raise ScfaError("Tc must be a multiple of 128")
             self.Tq = self.Tk = Tc
-            nC = (T + SCFA_COUNT_CHUNK - 1) // SCFA_COUNT_CHUNK
+            nC = [(n + SCFA_COUNT_CHUNK - 1) // SCFA_COUNT_CHUNK for n in (T, Tkv)]
             self.cnt = [e((B, H)), e((B, H))]
             self.mx = [e((1,)), e((1,))]
-            self.choff = [e((B, H, nC)), e((B, H, nC))]
+            self.choff = [e((B, H, nC[0])), e((B, H, nC[1]))]
         elif mode == "hash":
             self.Tq = scfa_hash_segment_rows(T, self.nbs, SCFA_TILE_M)
-            self.Tk = scfa_hash_segment_rows(T, self.nbs, SCFA_TILE_N)
+            self.Tk = scfa_hash_segment_rows(Tkv, self.nbs, SCFA_TILE_N)
         else:
-            self.Tq = self.Tk = pad_rows(T)
+            self.Tq = self.Tk = pad_rows(max(T, Tkv))
         TqP, TkP = pad_rows(self.Tq), pad_rows(self.Tk)
         self.x = None  # operands of the last prepare()
         self.device = d
@@ -622,19 +649,19 @@ class Plan:
         self.q_bkt = self.k_bkt = None
         self.dev_err = torch.zeros((1,), dtype=i32, device=d)
         if mode == "hash":
-            Tp = pad_rows(T)
-            self.bq, self.bk = e((B, H, T)), e((B, H, T))
-            self.perm_q, self.perm_k = e((B, H, Tp)), e((B, H, Tp))
-            self.bs_q, self.bs_k = e((B, H, Tp)), e((B, H, Tp))
+            Tp, Tkp = pad_rows(T), pad_rows(Tkv)
+            self.bq, self.bk = e((B, H, T)), e((B, H, Tkv))
+            self.perm_q, self.perm_k = e((B, H, Tp)), e((B, H, Tkp))
+            self.bs_q, self.bs_k = e((B, H, Tp)), e((B, H, Tkp))
             nbs = self.nbs
             self.offq, self.offk = e((B, H, nbs + 1)), e((B, H, nbs + 1))
             self.segq, self.segk = e((B, H, nbs + 1)), e((B, H, nbs + 1))
             self.q_bkt, self.k_bkt = e((B, H, TqP)), e((B, H, TkP))
-            self.cq, self.ck = e(chunk_count_shape(B, H, T, nbs)), e(chunk_count_shape(B, H, T, nbs))
+            self.cq, self.ck = e(chunk_count_shape(B, H, T, nbs)), e(chunk_count_shape(B, H, Tkv, nbs))
         if mode == "dense":
             ar = torch.arange(TqP, dtype=i32, device=d)
             self.q_idx.copy_(torch.where(ar < T, ar, torch.full_like(ar, SCFA_Q_PAD)).expand(B, H, TqP))
-            self.k_idx.copy_(torch.where(ar < T, ar, torch.full_like(ar, SCFA_K_PAD)).expand(B, H, TkP))
+            self.k_idx.copy_(torch.where(ar < Tkv, ar, torch.full_like(ar, SCFA_K_PAD)).expand(B, H, TkP))
         Bm, Bn = SCFA_TILE_M, SCFA_TILE_N
         nQt, nKt = TqP // Bm, TkP // Bn
         self.tab = Tables(e((B, H, nQt, 4)), e((B, H, nKt, 4)), e((B, H, nQt, 2)), e((B, H, nKt, 2)), e((B, H)), Bm, Bn,
@@ -651,6 +678,10 @@ class Plan:
         one launch); the keep masks are required in hash_drop mode."""
         if self.drop and (keep_q is None or keep_k is None):
             raise ScfaError("hash_drop needs the keep masks")
+        if not self.two_side:  # queries and keys of different lengths: one launch per side
+            scfa_hash_bucket_counts(q, R, self.nb, self.bq, self.cq, stream)
+            scfa_hash_bucket_counts(k, R, self.nb, self.bk, self.ck, stream)
+            return
         scfa_hash_bucket_qk(q, k, R, self.nb, self.bq, self.bk, self.cq, self.ck, stream,
                             keep_q if self.drop else None, keep_k if self.drop else None)
 
@@ -658,6 +689,12 @@ class Plan:
         """Stable sort by bucket, the bucket-aligned layout and its tile
         statistics (both sides in one launch)."""
         t = self.tab
+        if not self.two_side:  # one launch per side; tables() computes the tile statistics
+            scfa_hash_layout(self.bq, self.cq, self.nbs, SCFA_TILE_M, SCFA_Q_PAD, self.perm_q, self.bs_q, self.offq,
+                             self.q_idx, self.q_bkt, self.segq, self.dev_err, stream)
+            scfa_hash_layout(self.bk, self.ck, self.nbs, SCFA_TILE_N, SCFA_K_PAD, self.perm_k, self.bs_k, self.offk,
+                             self.k_idx, self.k_bkt, self.segk, self.dev_err, stream)
+            return
         scfa_hash_layout_qk(self.bq, self.bk, self.cq, self.ck, self.nbs, self.perm_q, self.perm_k, self.bs_q, self.bs_k,
                             self.offq, self.offk, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.segq, self.segk,
                             self.dev_err, t.qstats, t.kstats, t.tiles, stream)
@@ -676,7 +713,7 @@ class Plan:
         processed-tile counter that this call adds to); the backward table is
         built by backward()."""
         t = self.tab
-        if self.mode == "hash":  # the tile statistics come from the layout launch
+        if self.mode == "hash" and self.two_side:  # the tile statistics come from the layout launch
             scfa_fwd_table(SCFA_HASH | self.flags, t.qstats, t.kstats, t.fwd, t.tiles, stream)
         else:
             scfa_range_table(_table_mode(self.mode) | self.flags, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B,
@@ -694,8 +731,8 @@ class Plan:
         scfa_bwd_table(self.tab.qstats, self.tab.kstats, self.tab.fwd, self.tab.bwd, stream, self.flags)
         if self._grads is None:
             d = self.device
-            self._grads = tuple(torch.empty((self.B, self.T, self.H, self.D), dtype=torch.float32, device=d)
-                                for _ in range(3))
+            self._grads = tuple(torch.empty((self.B, n, self.H, self.D), dtype=torch.float32, device=d)
+                                for n in (self.T, self.T_kv, self.T_kv))
             self._bws = torch.empty((scfa_bwd_workspace_bytes(_table_mode(self.mode), self.B, self.H, self.Tq, self.Tk,
                                                               self.D),), dtype=torch.uint8, device=d)
         if self.out_dtype != torch.float32:

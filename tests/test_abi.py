@@ -71,19 +71,24 @@ def test_invalid_arguments_rejected_without_gpu():
                               null) == scfa.SCFA_ERR_INVALID
     # forward: bad scale, D, Tc (the launch order may be NULL)
     args = [0, 1] + [dummy] * 8 + [null]
-    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 64, ctypes.c_float(0.0), 0, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
-    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 128, ctypes.c_float(0.125), 0, dummy, dummy,
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 8, 128, 64, ctypes.c_float(0.0), 0, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 8, 128, 128, ctypes.c_float(0.125), 0, dummy, dummy,
                                 null) == scfa.SCFA_ERR_UNSUPPORTED
-    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 120, 64, ctypes.c_float(0.125), 0, dummy, dummy,
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 8, 120, 64, ctypes.c_float(0.125), 0, dummy, dummy,
                                 null) == scfa.SCFA_ERR_INVALID
     # one batch entry's T x H x D block of 4 GiB or more (32-bit row offsets)
-    assert L.scfa_qk_sparse_fwd(*args, 1, 64, 1 << 20, 1 << 20, 64, ctypes.c_float(0.125), 0, dummy, dummy,
+    assert L.scfa_qk_sparse_fwd(*args, 1, 64, 1 << 20, 1 << 20, 1 << 20, 64, ctypes.c_float(0.125), 0, dummy, dummy,
+                                null) == scfa.SCFA_ERR_UNSUPPORTED
+    # separate key/value length: zero is rejected, and so is a k/v block of 4 GiB or more
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 0, 128, 64, ctypes.c_float(0.125), 0, dummy, dummy,
+                                null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_qk_sparse_fwd(*args, 1, 64, 8, 1 << 20, 128, 64, ctypes.c_float(0.125), 0, dummy, dummy,
                                 null) == scfa.SCFA_ERR_UNSUPPORTED
     # flags other than SCFA_STRICT / SCFA_NONCAUSAL, and the two together
-    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 64, ctypes.c_float(0.125), 4, dummy, dummy,
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 8, 128, 64, ctypes.c_float(0.125), 4, dummy, dummy,
                                 null) == scfa.SCFA_ERR_INVALID
     both = scfa.SCFA_STRICT | scfa.SCFA_NONCAUSAL
-    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 128, 64, ctypes.c_float(0.125), both, dummy, dummy,
+    assert L.scfa_qk_sparse_fwd(*args, 1, 1, 8, 8, 128, 64, ctypes.c_float(0.125), both, dummy, dummy,
                                 null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_bwd_table(dummy, dummy, dummy, 1, 1, 2, 2, dummy, 3, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_bwd_table(dummy, dummy, dummy, 1, 1, 2, 2, dummy, both, null) == scfa.SCFA_ERR_INVALID
@@ -100,7 +105,7 @@ def test_invalid_arguments_rejected_without_gpu():
                               dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
     hargs = [0, 1] + [dummy] * 10
     # hash forward: a NULL table is rejected
-    assert L.scfa_hash_sparse_fwd(*hargs[:-1], null, null, 1, 1, 8, 8, 8, 64, ctypes.c_float(0.125), 0, dummy, dummy,
+    assert L.scfa_hash_sparse_fwd(*hargs[:-1], null, null, 1, 1, 8, 8, 8, 8, 64, ctypes.c_float(0.125), 0, dummy, dummy,
                                   null) == scfa.SCFA_ERR_INVALID
     # bucket-aligned layout: bad alignment, rows below T, size helper
     assert L.scfa_hash_segments(dummy, dummy, 1, 1, 100, 16, 48, -1, 128, dummy, dummy, dummy, null,
