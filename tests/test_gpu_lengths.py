@@ -25,6 +25,11 @@ CASES = [
     (small("hash", 2, 3, 1000, nb=16, seed=136, grad=True, Tk=1500), "causal"),
     (small("hash", 2, 3, 1500, nb=8, seed=137, grad=True, Tk=1000), "noncausal"),
     (small("hash", 1, 2, 200, nb=4, dtype="f32", seed=138, Tk=900), "strict"),
+    # extremes: one query against many keys, many queries against one key
+    (small("dense", 1, 2, 1, seed=140, Tk=257), "causal"),
+    (small("qk", 1, 2, 257, keep_p=0.7, seed=141, Tk=1), "causal"),
+    (small("hash", 1, 2, 3, nb=4, seed=142, Tk=700), "noncausal"),
+    (small("hash", 1, 2, 700, nb=4, seed=143, Tk=1), "causal"),
 ]
 
 
