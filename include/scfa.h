@@ -159,7 +159,9 @@ int scfa_hash_bucket_counts(int dtype, const void* x, const float* R, int B, int
  * bit, as two calls. Same definition and citation.
  *  q, k                (B, T, H, D) of one dtype, device: one length T for
  *                      both (queries and keys of different lengths take
- *                      scfa_hash_bucket_counts per side, without keep masks).
+ *                      scfa_hash_bucket_counts per side, or
+ *                      scfa_hash_bucket_counts_drop per side with keep
+ *                      masks).
  *  keep_q, keep_k      optional (B, T, H) uint8 keep masks, both or neither:
  *                      hashing combined with within-bucket dropping (the SCFA
  *                      explainer's follow-up idea of a mask that is both
@@ -177,6 +179,25 @@ int scfa_hash_bucket_counts(int dtype, const void* x, const float* R, int B, int
 int scfa_hash_bucket_qk(int dtype, const void* q, const void* k, const float* R, const uint8_t* keep_q,
                         const uint8_t* keep_k, int B, int T, int H, int D, int nb, int32_t* bucket_q, int32_t* bucket_k,
                         int32_t* counts_q, int32_t* counts_k, hipStream_t stream);
+
+/* One side of scfa_hash_bucket_qk with its keep mask, for queries and keys of
+ * different lengths (the SCFA explainer's decision tensors have lengths T_Q
+ * and T_KV) combined with within-bucket dropping: the explainer's follow-up
+ * idea of a mask that is both hash-based and drop-based. Kept tokens take
+ * the scfa_hash_bucket bucket; a dropped token takes bucket nb + side, which
+ * matches nothing on the other side. Bit for bit the same bucket and counts
+ * as the corresponding side of scfa_hash_bucket_qk when the lengths agree.
+ *  x             (B, T, H, D) bf16 or fp32, device: the queries (side 0) or
+ *                the keys (side 1), T their own length.
+ *  keep          (B, T, H) uint8, device, nonzero = kept; required.
+ *  side          0 (queries: dropped -> nb) or 1 (keys: dropped -> nb + 1).
+ *  bucket        out (B, H, T) int32.
+ *  chunk_counts  out (B, H, ceil(T / 256), nb + 2) int32 (input of
+ *                scfa_hash_layout with nb + 2 buckets).
+ * Errors: NULL pointer, side not 0 or 1, bad sizes -> SCFA_ERR_INVALID;
+ * D != 64 or nb > 62 -> SCFA_ERR_UNSUPPORTED. Asynchronous on `stream`. */
+int scfa_hash_bucket_counts_drop(int dtype, const void* x, const float* R, const uint8_t* keep, int side, int B, int T,
+                                 int H, int D, int nb, int32_t* bucket, int32_t* chunk_counts, hipStream_t stream);
 
 /* Bytes of device workspace scfa_hash_sort needs. */
 size_t scfa_hash_sort_workspace_bytes(int B, int H, int T, int nb);

@@ -169,7 +169,8 @@ __device__ inline float unit_elem<uint16_t>(const u32x4& u, int e) {
 template <typename TIN, int HALF>
 __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* x, const TIN* x2, const float* __restrict__ R,
                                                      int T, int H, int32_t* bucket, int32_t* bucket2, int32_t* counts,
-                                                     int32_t* counts2, const uint8_t* keep, const uint8_t* keep2, int nbo) {
+                                                     int32_t* counts2, const uint8_t* keep, const uint8_t* keep2, int nbo,
+                                                     int side0) {
   if (blockIdx.z) {  // second side of a two-input launch
     x = x2;
     bucket = bucket2;
@@ -223,8 +224,9 @@ __global__ __launch_bounds__(256) void k_hash_bucket(const TIN* x, const TIN* x2
   }
   int v = (vn > vp) ? HALF + bn : bp;
   // a dropped token (hashing with within-bucket dropping) takes a bucket of
-  // its own side that matches nothing: nb for queries, nb + 1 for keys
-  if (keep && t < T && keep[(static_cast<size_t>(b) * T + t) * H + h] == 0) v = 2 * HALF + blockIdx.z;
+  // its own side (side0 + blockIdx.z: 0 queries, 1 keys) that matches
+  // nothing: nb for queries, nb + 1 for keys
+  if (keep && t < T && keep[(static_cast<size_t>(b) * T + t) * H + h] == 0) v = 2 * HALF + side0 + blockIdx.z;
   if (t < T) bucket[static_cast<size_t>(bh) * T + t] = v;
   if (counts) {  // the chunk histogram of the stable sort (chunk = this workgroup)
     if (t < T) atomicAdd(&hs[v], 1);
@@ -275,7 +277,8 @@ __device__ __forceinline__ void fma_units(double* c, const double* Rv, const uin
 template <typename TIN, int HALF>
 __global__ __launch_bounds__(256) void k_hash_bucket_dpp(const TIN* x, const TIN* x2, const float* __restrict__ R,
                                                          int T, int H, int32_t* bucket, int32_t* bucket2, int32_t* counts,
-                                                         int32_t* counts2, const uint8_t* keep, const uint8_t* keep2, int nbo) {
+                                                         int32_t* counts2, const uint8_t* keep, const uint8_t* keep2, int nbo,
+                                                     int side0) {
   if (blockIdx.z) {  // second side of a two-input launch
     x = x2;
     bucket = bucket2;
@@ -326,8 +329,9 @@ __global__ __launch_bounds__(256) void k_hash_bucket_dpp(const TIN* x, const TIN
   }
   int v = (vn > vp) ? HALF + bn : bp;
   // a dropped token (hashing with within-bucket dropping) takes a bucket of
-  // its own side that matches nothing: nb for queries, nb + 1 for keys
-  if (keep && t < T && keep[(static_cast<size_t>(b) * T + t) * H + h] == 0) v = 2 * HALF + blockIdx.z;
+  // its own side (side0 + blockIdx.z: 0 queries, 1 keys) that matches
+  // nothing: nb for queries, nb + 1 for keys
+  if (keep && t < T && keep[(static_cast<size_t>(b) * T + t) * H + h] == 0) v = 2 * HALF + side0 + blockIdx.z;
   if (t < T) bucket[static_cast<size_t>(bh) * T + t] = v;
   if (counts) {
     if (t < T) atomicAdd(&hs[v], 1);
@@ -342,16 +346,16 @@ __global__ __launch_bounds__(256) void k_hash_bucket_dpp(const TIN* x, const TIN
 template <typename TIN, int HALF>
 void bucket_launch(dim3 grid, hipStream_t stream, const void* x, const void* x2, const float* R, int T, int H,
                    int32_t* bucket, int32_t* bucket2, int32_t* counts, int32_t* counts2, const uint8_t* keep,
-                   const uint8_t* keep2) {
+                   const uint8_t* keep2, int side0) {
   const TIN* a = static_cast<const TIN*>(x);
   const TIN* a2 = static_cast<const TIN*>(x2);
   const int nbo = 2 * HALF + (keep ? 2 : 0);
   if constexpr (HALF <= 16)
     hipLaunchKernelGGL((k_hash_bucket_dpp<TIN, HALF>), grid, dim3(256), 0, stream, a, a2, R, T, H, bucket, bucket2,
-                       counts, counts2, keep, keep2, nbo);
+                       counts, counts2, keep, keep2, nbo, side0);
   else
     hipLaunchKernelGGL((k_hash_bucket<TIN, HALF>), grid, dim3(256), 0, stream, a, a2, R, T, H, bucket, bucket2,
-                       counts, counts2, keep, keep2, nbo);
+                       counts, counts2, keep, keep2, nbo, side0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1093,9 +1097,12 @@ int scfa_qk_compact(int dtype, const void* x, const uint8_t* keep, const int32_t
 // keep / keep2: optional keep masks of the two sides (both or neither).
 static int launch_hash_bucket(int dtype, int nx, const void* x, const void* x2, const float* R, int B, int T, int H,
                               int D, int nb, int32_t* bucket, int32_t* bucket2, int32_t* counts, int32_t* counts2,
-                              const uint8_t* keep, const uint8_t* keep2, hipStream_t stream) {
+                              const uint8_t* keep, const uint8_t* keep2, int side0, hipStream_t stream) {
   if (!x || !R || !bucket || (nx == 2 && (!x2 || !bucket2))) return SCFA_ERR_INVALID;
-  if ((keep != nullptr) != (keep2 != nullptr) || (keep && nx != 2)) return SCFA_ERR_INVALID;
+  // keep masks: both sides or neither in a two-side launch; one side's mask
+  // (keep2 unused) in a one-side launch
+  if (nx == 2 ? (keep != nullptr) != (keep2 != nullptr) : keep2 != nullptr) return SCFA_ERR_INVALID;
+  if (side0 != 0 && (nx != 1 || !keep)) return SCFA_ERR_INVALID;
   if (B < 1 || T < 1 || H < 1 || nb < 2 || nb % 2) return SCFA_ERR_INVALID;
   if (!dtype_ok(dtype)) return SCFA_ERR_INVALID;
   if (D != 64 || nb > (keep ? 62 : 64)) return SCFA_ERR_UNSUPPORTED;
@@ -1105,10 +1112,10 @@ static int launch_hash_bucket(int dtype, int nx, const void* x, const void* x2, 
   case HALF:                                                                                           \
     if (dtype == SCFA_BF16)                                                                            \
       bucket_launch<uint16_t, HALF>(grid, stream, x, x2, R, T, H, bucket, bucket2, counts, counts2, keep, \
-                                    keep2);                                                            \
+                                    keep2, side0);                                                     \
     else                                                                                               \
       bucket_launch<float, HALF>(grid, stream, x, x2, R, T, H, bucket, bucket2, counts, counts2, keep,    \
-                                 keep2);                                                               \
+                                 keep2, side0);                                                        \
     break;
   switch (half) {
     SCFA_BUCKET_CASE(1)
@@ -1134,14 +1141,21 @@ static int launch_hash_bucket(int dtype, int nx, const void* x, const void* x2, 
 int scfa_hash_bucket(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb, int32_t* bucket,
                      hipStream_t stream) {
   return launch_hash_bucket(dtype, 1, x, nullptr, R, B, T, H, D, nb, bucket, nullptr, nullptr, nullptr, nullptr,
-                            nullptr, stream);
+                            nullptr, 0, stream);
 }
 
 int scfa_hash_bucket_counts(int dtype, const void* x, const float* R, int B, int T, int H, int D, int nb,
                             int32_t* bucket, int32_t* chunk_counts, hipStream_t stream) {
   if (!chunk_counts) return SCFA_ERR_INVALID;
   return launch_hash_bucket(dtype, 1, x, nullptr, R, B, T, H, D, nb, bucket, nullptr, chunk_counts, nullptr, nullptr,
-                            nullptr, stream);
+                            nullptr, 0, stream);
+}
+
+int scfa_hash_bucket_counts_drop(int dtype, const void* x, const float* R, const uint8_t* keep, int side, int B, int T,
+                                 int H, int D, int nb, int32_t* bucket, int32_t* chunk_counts, hipStream_t stream) {
+  if (!chunk_counts || !keep || (side != 0 && side != 1)) return SCFA_ERR_INVALID;
+  return launch_hash_bucket(dtype, 1, x, nullptr, R, B, T, H, D, nb, bucket, nullptr, chunk_counts, nullptr, keep,
+                            nullptr, side, stream);
 }
 
 int scfa_hash_bucket_qk(int dtype, const void* q, const void* k, const float* R, const uint8_t* keep_q,
@@ -1149,7 +1163,7 @@ int scfa_hash_bucket_qk(int dtype, const void* q, const void* k, const float* R,
                         int32_t* counts_q, int32_t* counts_k, hipStream_t stream) {
   if (!counts_q || !counts_k) return SCFA_ERR_INVALID;
   return launch_hash_bucket(dtype, 2, q, k, R, B, T, H, D, nb, bucket_q, bucket_k, counts_q, counts_k, keep_q, keep_k,
-                            stream);
+                            0, stream);
 }
 
 size_t scfa_hash_sort_workspace_bytes(int B, int H, int T, int nb) {

@@ -51,6 +51,7 @@ _SIGS = {
     "scfa_hash_segments": (_i, [_vp, _vp, _i, _i, _i, _i, _i, ctypes.c_int32, _i, _vp, _vp, _vp, _vp, _vp]),
     "scfa_hash_layout": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_hash_bucket_counts": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "scfa_hash_bucket_counts_drop": (_i, [_i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "scfa_hash_bucket_qk": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "scfa_hash_layout_qk": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i] + [_vp] * 17),
     "scfa_fwd_table": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]),
@@ -169,6 +170,16 @@ def scfa_hash_bucket_counts(x, R, nb, bucket, chunk_counts, stream=None):
     B, T, H, D = x.shape
     _check(lib().scfa_hash_bucket_counts(_dt(x), _p(x), _p(R), B, T, H, D, nb, _p(bucket), _p(chunk_counts),
                                          _stream(stream, x)), "scfa_hash_bucket_counts")
+
+
+def scfa_hash_bucket_counts_drop(x, R, keep, side, nb, bucket, chunk_counts, stream=None):
+    """One side with its keep mask (side 0: queries, dropped -> nb; side 1:
+    keys, dropped -> nb + 1); chunk counts over nb + 2 buckets."""
+    B, T, H, D = x.shape
+    if keep is None or tuple(keep.shape) != (B, T, H):
+        raise ScfaError("keep must be (B, T, H) for the side's own length T")
+    _check(lib().scfa_hash_bucket_counts_drop(_dt(x), _p(x), _p(R), _p(keep), side, B, T, H, D, nb, _p(bucket),
+                                              _p(chunk_counts), _stream(stream, x)), "scfa_hash_bucket_counts_drop")
 
 
 def scfa_hash_bucket_qk(q, k, R, nb, bucket_q, bucket_k, counts_q, counts_k, stream=None, keep_q=None, keep_k=None):
@@ -439,23 +450,27 @@ def prepare_hash(q, k, v, R, nb: int, aligned: bool = True, stream=None, keep_q=
     side (query buckets start at multiples of the query tile, key buckets at
     multiples of the key tile). The operands stay in original order (gathered
     on load). With keep masks (hashing combined with within-bucket dropping)
-    the buckets come from the two-side launch, dropped queries in bucket nb and
-    dropped keys in bucket nb + 1, and the sort has nb + 2 buckets."""
+    dropped queries take bucket nb and dropped keys bucket nb + 1 (two-side
+    launch, or one launch per side when the lengths differ), and the sort has
+    nb + 2 buckets."""
     B, T, H, D = q.shape
     T_kv = _kv_len(q, k, v)
     dev = q
     i32 = torch.int32
     Tp, Tkp = pad_rows(T), pad_rows(T_kv)
-    nbs = nb if keep_q is None and keep_k is None else nb + 2  # buckets of the sort
-    if nbs != nb and T_kv != T:
-        raise ScfaError("hashing with dropping needs queries and keys of one length")
+    if (keep_q is None) != (keep_k is None):
+        raise ScfaError("give both keep masks or neither")
+    nbs = nb if keep_q is None else nb + 2  # buckets of the sort
     bq, bk = _empty((B, H, T), i32, dev), _empty((B, H, T_kv), i32, dev)
     cq, ck = _empty(chunk_count_shape(B, H, T, nbs), i32, dev), _empty(chunk_count_shape(B, H, T_kv, nbs), i32, dev)
     if nbs == nb:
         scfa_hash_bucket_counts(q, R, nb, bq, cq, stream)
         scfa_hash_bucket_counts(k, R, nb, bk, ck, stream)
-    else:
+    elif T_kv == T:
         scfa_hash_bucket_qk(q, k, R, nb, bq, bk, cq, ck, stream, keep_q, keep_k)
+    else:  # two lengths: one launch per side
+        scfa_hash_bucket_counts_drop(q, R, keep_q, 0, nb, bq, cq, stream)
+        scfa_hash_bucket_counts_drop(k, R, keep_k, 1, nb, bk, ck, stream)
     nb = nbs
     dev_err = torch.zeros((1,), dtype=i32, device=q.device)
     perm_q, perm_k = _empty((B, H, Tp), i32, dev), _empty((B, H, Tkp), i32, dev)
@@ -607,8 +622,6 @@ class Plan:
         self.drop = mode == "hash_drop"
         self.T_kv = T if T_kv is None else T_kv
         self.two_side = self.T_kv == T  # queries and keys bucketed and laid out in one launch each
-        if self.drop and not self.two_side:
-            raise ScfaError("hash_drop needs queries and keys of one length")
         if self.drop:
             mode = "hash"
             if nb > 62:
@@ -679,8 +692,12 @@ class Plan:
         if self.drop and (keep_q is None or keep_k is None):
             raise ScfaError("hash_drop needs the keep masks")
         if not self.two_side:  # queries and keys of different lengths: one launch per side
-            scfa_hash_bucket_counts(q, R, self.nb, self.bq, self.cq, stream)
-            scfa_hash_bucket_counts(k, R, self.nb, self.bk, self.ck, stream)
+            if self.drop:
+                scfa_hash_bucket_counts_drop(q, R, keep_q, 0, self.nb, self.bq, self.cq, stream)
+                scfa_hash_bucket_counts_drop(k, R, keep_k, 1, self.nb, self.bk, self.ck, stream)
+            else:
+                scfa_hash_bucket_counts(q, R, self.nb, self.bq, self.cq, stream)
+                scfa_hash_bucket_counts(k, R, self.nb, self.bk, self.ck, stream)
             return
         scfa_hash_bucket_qk(q, k, R, self.nb, self.bq, self.bk, self.cq, self.ck, stream,
                             keep_q if self.drop else None, keep_k if self.drop else None)

@@ -55,6 +55,15 @@ def test_invalid_arguments_rejected_without_gpu():
     # odd nb / unsupported nb
     assert L.scfa_hash_bucket(0, dummy, dummy, 1, 8, 1, 64, 15, dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_hash_bucket(0, dummy, dummy, 1, 8, 1, 64, 128, dummy, null) == scfa.SCFA_ERR_UNSUPPORTED
+    # one-side bucket launch with a keep mask: the mask and the counts are
+    # required, side is 0 or 1, nb + 2 buckets must fit 64
+    drop = L.scfa_hash_bucket_counts_drop
+    assert drop(0, dummy, dummy, null, 0, 1, 8, 1, 64, 16, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert drop(0, dummy, dummy, dummy, 0, 1, 8, 1, 64, 16, dummy, null, null) == scfa.SCFA_ERR_INVALID
+    assert drop(0, dummy, dummy, dummy, 2, 1, 8, 1, 64, 16, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert drop(0, dummy, dummy, dummy, -1, 1, 8, 1, 64, 16, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert drop(0, dummy, dummy, dummy, 1, 1, 0, 1, 64, 16, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert drop(0, dummy, dummy, dummy, 1, 1, 8, 1, 64, 64, dummy, dummy, null) == scfa.SCFA_ERR_UNSUPPORTED
     # bad dtype
     assert L.scfa_gather(7, 0, dummy, dummy, 1, 8, 1, 64, 128, dummy, null) == scfa.SCFA_ERR_INVALID
     # bad layout

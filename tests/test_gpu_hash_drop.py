@@ -1,7 +1,8 @@
 """GPU parity of hashing combined with within-bucket dropping (the
 explainer's follow-up mask: a pair is visible iff both tokens share a bucket,
 both are kept and the key does not come after the query) against the float64
-oracle, through the C ABI. Dropped queries take bucket nb and dropped keys
+oracle, through the C ABI, with queries and keys of one length (two-side
+bucket launch) and of different lengths (one launch per side). Dropped queries take bucket nb and dropped keys
 bucket nb + 1, so the sort, layout, tables, attention and backward are the
 hash path's own."""
 import numpy as np
@@ -20,6 +21,10 @@ CASES = [
     small("hash", 1, 2, 513, dtype="f32", nb=4, keep_p=0.5, seed=102),
     small("hash", 1, 2, 300, nb=2, keep_p=0.3, seed=103, grad=True),
     small("hash", 1, 3, 2000, nb=48, keep_p=0.7, seed=104),
+    # queries and keys of different lengths (one bucket launch per side)
+    small("hash", 2, 3, 900, nb=16, keep_p=0.6, seed=106, grad=True, Tk=1400),
+    small("hash", 1, 2, 1300, nb=8, keep_p=0.5, seed=107, grad=True, Tk=600),
+    small("hash", 1, 2, 257, dtype="f32", nb=4, keep_p=0.4, seed=108, Tk=800),
 ]
 
 
@@ -68,8 +73,17 @@ def test_hash_drop_buckets_and_forward(w):
     err, lerr = check_fwd(w, O, lse, Or, Lr)
     print(f"{w.name}: max-abs {err:.2e}  lse {lerr:.2e}")
     pairs = scfa.count_visible(pre).cpu().numpy()
-    ref = oracle.visible_pairs("hash", w.T, w.B, w.H, x["keep_q"].numpy(), x["keep_k"].numpy(), bq, bk)
+    ref = oracle.visible_pairs("hash", w.T, w.B, w.H, x["keep_q"].numpy(), x["keep_k"].numpy(), bq, bk,
+                               Tk=w.T_kv)
     assert np.array_equal(pairs, ref)
+    if w.T_kv == w.T:  # the one-side launches give the two-side launch's bits
+        for side, name, keep in ((0, "q", g["keep_q"]), (1, "k", g["keep_k"])):
+            b1 = torch.empty_like(pre.extra["bucket_" + name])
+            c1 = torch.empty_like(pre.extra["chunk_counts_" + name])
+            scfa.scfa_hash_bucket_counts_drop(g[name], g["R"], keep, side, w.nb, b1, c1)
+            torch.cuda.synchronize()
+            assert torch.equal(b1, pre.extra["bucket_" + name])
+            assert torch.equal(c1, pre.extra["chunk_counts_" + name])
     # dropped queries: zero rows, LSE -inf
     Og, Lg = O.cpu().numpy(), lse.cpu().numpy()
     assert np.isneginf(Lg[~kq]).all()
@@ -96,6 +110,37 @@ def test_hash_drop_backward(w):
     dropped_k = x["keep_k"].numpy() == 0  # (B, T, H)
     assert (f64(grads[1])[dropped_k] == 0).all() and (f64(grads[2])[dropped_k] == 0).all()
     assert (f64(grads[0])[x["keep_q"].numpy() == 0] == 0).all()
+
+
+@pytest.mark.parametrize("T,Tk", [(8192, 16384), (16384, 4096)])
+def test_hash_drop_plan_lengths(T, Tk):
+    """Plans in hash_drop mode with T_kv != T (one bucket and layout launch
+    per side, statistics built with the tables), graph-captured: sampled rows
+    of every head against the oracle, the pair count, bit-equal replays."""
+    need_gpu()
+    w = small("hash", 2, 4, T, nb=16, keep_p=0.6, seed=109, Tk=Tk)
+    announce(f"hash+drop plan T={T} Tk={Tk}")
+    x = make_inputs(w)
+    g = to_dev(x)
+    plan = scfa.Plan("hash_drop", w.B, w.H, w.T, w.D, torch.bfloat16, nb=w.nb, T_kv=Tk)
+    plan.run(g)
+    torch.cuda.synchronize()
+    assert int(plan.dev_err.item()) == 0
+    O_ref, l_ref = plan.O.clone(), plan.lse.clone()
+    rng = np.random.default_rng(10)
+    rows = np.unique(np.concatenate([rng.choice(T, 96, replace=False), [0, T - 1, min(T, Tk) - 1]]))
+    Or, Lr = _oracle_fwd(w, x, rows=rows)
+    check_fwd(w, plan.O, plan.lse, Or, Lr, rows=rows)
+    bq, bk = oracle_buckets(w, x)
+    ref = oracle.visible_pairs("hash", T, w.B, w.H, x["keep_q"].numpy(), x["keep_k"].numpy(), bq, bk, Tk=Tk)
+    assert np.array_equal(plan.count_visible().cpu().numpy(), ref)
+    graph = plan.capture(g)
+    for _ in range(2):
+        plan.O.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.O, O_ref) and torch.equal(plan.lse, l_ref)
 
 
 def test_hash_drop_plan_full_size():
