@@ -263,17 +263,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
   const int qreach = q_reach(p.rc, qs.y);  // largest key position a query of the tile may see
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
-  if (tid < BM) Qi[tid] = p.q_idx[rowbase + qt * BM + tid];  // visible after the first barrier
-  const bool kst_lds = rng.y - rng.x <= kKstCap;
-  if (kst_lds)
-    for (int i = tid; i < rng.y - rng.x; i += 256) Kst[i] = kst[rng.x + i];
-  __syncthreads();
-  // statistics of key tile j, rng.x <= j < rng.y
-  auto kstat = [&](int j) -> int4 {
-    const int4 v = kst_lds ? Kst[j - rng.x] : kst[j];
-    return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
-                     __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
-  };
+  // index entries of the tile (to LDS at the first barrier; loaded here with
+  // the table so the stores wait on nothing later)
+  const int qi_v = tid < BM ? p.q_idx[rowbase + qt * BM + tid] : 0;
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
   const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;     // token 0 of this head in q
   const size_t khead0 = (static_cast<size_t>(b) * p.Tkv * p.H + h) * HD * 2;  // and in k, v
@@ -287,6 +279,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     qpos[qb] = p.q_idx[rowbase + row];
     qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
   }
+  const bool kst_lds = rng.y - rng.x <= kKstCap;
+  static_assert(kKstCap <= 2 * 256, "statistics copy: two entries per thread");
+  const int nks = kst_lds ? rng.y - rng.x : 0;  // entries copied to LDS
+  int4 kst_a = make_int4(0, 0, 0, 0), kst_b = make_int4(0, 0, 0, 0);
+  if (tid < nks) kst_a = kst[rng.x + tid];
+  if (tid + 256 < nks) kst_b = kst[rng.x + tid + 256];
+  // statistics of key tile j, rng.x <= j < rng.y
+  auto kstat = [&](int j) -> int4 {
+    const int4 v = kst_lds ? Kst[j - rng.x] : kst[j];
+    return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                     __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
+  };
   const WaveRows wr = wave_rows(qpos, qbkt, p.rc);
   // positions the masks compare keys against: the largest visible key position
   const int qcmp[2] = {q_reach(p.rc, qpos[0]), q_reach(p.rc, qpos[1])};
@@ -349,13 +353,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     return j;
   };
 
-  int j = next_tile(rng.x);
-  int jn = j < rng.y ? next_tile(j + 1) : rng.y;
+  // The first tile of the range is staged before the statistics reach LDS
+  // (a tile failing the causal extremum test is skipped by every wave's own
+  // test), so the table, query and key loads form as short a chain as
+  // possible; the tiles after it are chosen from the statistics.
+  int j = rng.x < rng.y ? rng.x : rng.y;
   int pos[2];
   if (j < rng.y) {
     tile_rows(j, pos);
     stage_tile(j, 0, pos);
   }
+  if (tid < BM) Qi[tid] = qi_v;
+  if (tid < nks) Kst[tid] = kst_a;
+  if (tid + 256 < nks) Kst[tid + 256] = kst_b;
+  __syncthreads();  // Qi and the statistics
+  int jn = j < rng.y ? next_tile(j + 1) : rng.y;
   tile_rows(jn, pos);  // rows of the next tile, used by the first iteration
   dma_wait();
   __syncthreads();
