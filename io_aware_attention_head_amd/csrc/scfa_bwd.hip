@@ -271,10 +271,14 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   const int2 rng = p.bwd_tab[static_cast<size_t>(bh) * p.nKt + kt];
   const int4* qst = p.qstats + static_cast<size_t>(bh) * p.nQt;
   const bool qst_lds = rng.y - rng.x <= kStatCap;
-  if (qst_lds)
-    for (int i = tid; i < rng.y - rng.x; i += 256) Qst[i] = qst[rng.x + i];
-  if (tid < BN) Ki[tid] = p.k_idx[kbase + kt * BN + tid];
-  __syncthreads();
+  // statistics of the range and the tile's key entries: loaded here, stored
+  // to LDS at the first barrier (after the first chunk's DMA), so the key and
+  // query loads do not wait
+  static_assert(kStatCap <= 256, "statistics copy: one entry per thread");
+  const int nqs = qst_lds ? rng.y - rng.x : 0;
+  int4 qst_a = make_int4(0, 0, 0, 0);
+  if (tid < nqs) qst_a = qst[rng.x + tid];
+  const int ki_v = tid < BN ? p.k_idx[kbase + kt * BN + tid] : 0;
   auto qstat = [&](int i) { return uniform4(qst_lds ? Qst[i - rng.x] : qst[i]); };
 
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
@@ -345,13 +349,19 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
     return ci;
   };
 
-  int ci = next_chunk(CPT * rng.x);
-  int cn = ci < cend ? next_chunk(ci + 1) : cend;
+  // The first chunk of the range is staged before the statistics reach LDS
+  // (a chunk failing the causal extremum test is skipped by every wave's own
+  // test); the chunks after it are chosen from the statistics.
+  int ci = CPT * rng.x < cend ? CPT * rng.x : cend;
   int pos[2];
   if (ci < cend) {
     chunk_rows(ci, pos);
     stage(ci, 0, pos);
   }
+  if (tid < nqs) Qst[tid] = qst_a;
+  if (tid < BN) Ki[tid] = ki_v;
+  __syncthreads();  // the statistics and the key entries
+  int cn = ci < cend ? next_chunk(ci + 1) : cend;
   chunk_rows(cn, pos);
   dma_wait();
   __syncthreads();
@@ -788,9 +798,12 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   const int qreach = q_reach(p.rc, qs.y);  // largest key position a query of the tile may see
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
   const bool kst_lds = rng.y - rng.x <= kStatCap;
-  if (kst_lds)
-    for (int i = tid; i < rng.y - rng.x; i += 256) Kst[i] = kst[rng.x + i];
-  __syncthreads();
+  // statistics of the range: loaded here, stored to LDS at the first barrier
+  // (after the first tile's DMA), so the query and key loads do not wait
+  static_assert(kStatCap <= 256, "statistics copy: one entry per thread");
+  const int nks = kst_lds ? rng.y - rng.x : 0;
+  int4 kst_a = make_int4(0, 0, 0, 0);
+  if (tid < nks) kst_a = kst[rng.x + tid];
   auto kstat = [&](int j) { return uniform4(kst_lds ? Kst[j - rng.x] : kst[j]); };
 
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;
@@ -859,13 +872,18 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
     return j;
   };
 
-  int j = next_tile(rng.x);
-  int jn = j < rng.y ? next_tile(j + 1) : rng.y;
+  // The first tile of the range is staged before the statistics reach LDS
+  // (a tile failing the causal extremum test is skipped by every wave's own
+  // test); the tiles after it are chosen from the statistics.
+  int j = rng.x < rng.y ? rng.x : rng.y;
   int pos[2];
   if (j < rng.y) {
     tile_rows(j, pos);
     stage(j, 0, pos);
   }
+  if (tid < nks) Kst[tid] = kst_a;
+  __syncthreads();  // the statistics
+  int jn = j < rng.y ? next_tile(j + 1) : rng.y;
   tile_rows(jn, pos);
   dma_wait();
   __syncthreads();
