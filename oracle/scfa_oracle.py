@@ -43,8 +43,9 @@ Readings of points the pages leave open (each one is also listed in the design doc):
   * Tile tables: see range_tables().
 
 Pins: every function here is checked by tests/test_oracle_*.py against brute
-force, closed forms, invariants or library routines ("Oracle
-pins"). Parity pinned for all functions.
+force, closed forms, invariants, library routines or numbers the pages print
+(the FLOP counts flops_fwd and flops_bwd against the teaching page's
+per-product inventory). Parity pinned for all functions.
 """
 from __future__ import annotations
 
@@ -532,6 +533,8 @@ def flops_fwd(pairs: int, D: int) -> int:
 
 
 def flops_bwd(pairs: int, D: int) -> int:
-    """Algorithmic backward FLOPs per visible pair: recompute S (2D), dP (2D),
-    dV (2D), dQ (2D), dK (2D) = 10*D."""
+    """Algorithmic backward FLOPs per visible pair: the five products of the
+    recomputation backward (the scores S again, dP, dV, dQ, dK), each costing
+    2*D per pair as the teaching page's per-product inventory counts Q K^T
+    (section on compute/memory arithmetic): 10*D."""
     return 10 * D * int(pairs)

@@ -259,3 +259,43 @@ def test_graph_replay_matches_eager(mode):
         plan.run(x)  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(plan.O, O_ref)
+
+
+@pytest.mark.parametrize("name", ["hash_bf16_t16384_nb16", "qk_bf16_t8192_keep0.7", "qk_bf16_t8192_keep0.5"])
+def test_plan_full_size_graph(name):
+    """The benchmark's own timed path: a Plan of the workload (preprocessing,
+    tables, launch order and forward), run eagerly and as replays of its HIP
+    graph. Sampled rows of every head against the oracle (O max-abs, LSE,
+    the -inf pattern), the visible-pair count against the oracle's, and
+    every replay bit-equal to the eager run."""
+    need_gpu()
+    w = WORKLOADS[name]
+    announce(f"plan full size graph {name}")
+    x = make_inputs(w)
+    g = to_dev(x)
+    plan = scfa.Plan(w.mode, w.B, w.H, w.T, w.D, torch.bfloat16, nb=w.nb)
+    plan.run(g)
+    torch.cuda.synchronize()
+    assert int(plan.dev_err.item()) == 0
+    O_ref, l_ref = plan.O.clone(), plan.lse.clone()
+    rows = _sampled_rows(w.T, 160, 12)
+    buckets = oracle_buckets(w, x) if w.mode == "hash" else None
+    Or, Lr = oracle_fwd(w, x, rows=rows, buckets=buckets)
+    err, lerr = check_fwd(w, plan.O, plan.lse, Or, Lr, rows=rows)
+    print(f"{name} plan: sampled max-abs {err:.2e}  lse {lerr:.2e}")
+    if w.mode == "hash":
+        ref = oracle.visible_pairs("hash", w.T, w.B, w.H, bkt_q=buckets[0], bkt_k=buckets[1])
+    else:
+        ref = oracle.visible_pairs("qk", w.T, w.B, w.H, x["keep_q"].numpy(), x["keep_k"].numpy())
+    assert np.array_equal(plan.count_visible().cpu().numpy(), ref)
+    graph = plan.capture(g)
+    for rep in range(3):
+        plan.O.fill_(float("nan"))
+        plan.lse.fill_(0.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.O, O_ref) and torch.equal(plan.lse, l_ref), f"replay {rep}"
+        plan.run(g)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(plan.O, O_ref)

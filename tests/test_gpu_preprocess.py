@@ -238,14 +238,20 @@ def test_hash_bucket_near_ties(dtype):
     x = rng.standard_normal((B, T, H, D))
     for h in range(H):
         for t in range(0, T, 3):  # every third token: two columns nearly tied as the largest
-            j1, j2 = rng.choice(half, 2, replace=False)
-            u = R[h, :, j1].astype(np.float64) - R[h, :, j2]
+            # two columns whose difference is nonzero (head 0 has two equal
+            # columns: that pair is tied for every token already)
+            while True:
+                j1, j2 = rng.choice(half, 2, replace=False)
+                u = R[h, :, j1].astype(np.float64) - R[h, :, j2]
+                if u @ u > 0:
+                    break
             v = R[h, :, j1].astype(np.float64) + R[h, :, j2] + 0.1 * rng.standard_normal(D)
             x[0, t, h] = v - (v @ u) / (u @ u) * u
         x[0, 7::97, h] = 0.0  # all-zero tokens
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     xt = torch.from_numpy(x.astype(np.float32)).to(tdt)
     x64 = xt.double().numpy()
+    assert np.isfinite(x64).all()
     ref = oracle.hash_bucket(x64, R.astype(np.float64), nb)
     d = torch.device("cuda:0")
     got = torch.empty((B, H, T), dtype=torch.int32, device=d)

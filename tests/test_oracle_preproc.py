@@ -25,6 +25,14 @@ def test_pages_constants_match_oracle():
     fi = g["flop_inventory"]
     pairs = fi["N"] * fi["N"]  # dense, non-causal square
     assert oracle.flops_fwd(pairs, fi["d_h"]) == fi["qk_flops"] + fi["av_flops"]
+    # The backward by recomputation evaluates five products of the same
+    # (N x d)(d x N) or (N x N)(N x d) shape over the same pairs: the scores
+    # Q K^T again, dP = dO V^T, dV = P^T dO, dQ = dS K and dK = dS^T Q. Each
+    # costs what the inventory gives for Q K^T (d_h = d_v here).
+    assert fi["d_h"] == fi["d_v"]
+    assert oracle.flops_bwd(pairs, fi["d_h"]) == 5 * fi["qk_flops"]
+    # forward + backward per visible pair: 14 * D
+    assert oracle.flops_fwd(1, 64) + oracle.flops_bwd(1, 64) == 14 * 64
     w = WORKLOADS["hash_bf16_t16384_nb16"]
     assert w.H == g["lm_shape"]["heads"] and w.D == g["lm_shape"]["head_dim"] and w.nb == g["lm_shape"]["nb"]
 
