@@ -49,6 +49,7 @@ extern "C" {
 #define SCFA_ERR_INVALID (-1)     /* bad argument (NULL, size, range)          */
 #define SCFA_ERR_UNSUPPORTED (-2) /* valid but not built (e.g. D != 64)        */
 #define SCFA_ERR_HIP (-3)         /* a HIP launch/runtime call failed          */
+#define SCFA_ERR_TOO_LARGE (-4)   /* beyond the static scratch of a no-allocation entry point */
 
 /* ---- device error bits (OR-ed into *dev_err) -------------------------- */
 #define SCFA_DEVERR_COUNT_EXCEEDS_TC 1 /* a head keeps more tokens than Tc     */
@@ -464,6 +465,34 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
              const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
              const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale, float* dQ, float* dK,
              float* dV, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Backward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving or training
+ * loops, harnesses that forbid hipMalloc). Same arguments, kernels and
+ * results as scfa_bwd, bit for bit; the workspace (log2 LSE and Delta per
+ * sorted query row, 8 bytes per row of B * H * SCFA_PAD(Tq)) lives in a
+ * static device array of SCFA_NOALLOC_SCRATCH_BYTES that each device holds
+ * for the life of the process. The call allocates nothing: no hipMalloc,
+ * no hipFree, no allocating library routine.
+ *  stream        must belong to the current device (else
+ *                SCFA_ERR_INVALID); the first call on a device looks the
+ *                array's address up on that device.
+ * Errors: as scfa_bwd; a problem whose workspace exceeds the array
+ * (B * H * SCFA_PAD(Tq) above about 2 million rows) -> SCFA_ERR_TOO_LARGE,
+ * before anything is enqueued.
+ * Every call on one device shares that device's array: calls that overlap
+ * in time on one device (two streams, or two host threads) race and give
+ * wrong gradients; calls in one stream order are safe. The array keeps the
+ * last call's contents; every row a call reads it writes first, so nothing
+ * needs clearing. */
+#define SCFA_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+
+int scfa_bwd_noalloc(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
+                     const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
+                     const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O,
+                     const float* lse, const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale,
+                     float* dQ, float* dK, float* dV, hipStream_t stream);
 
 #ifdef __cplusplus
 }

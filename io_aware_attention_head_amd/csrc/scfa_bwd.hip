@@ -42,6 +42,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "scfa_stage.h"
 
 namespace scfa {
@@ -1000,30 +1002,50 @@ int launch_bwd(const BwdParams& p, hipStream_t stream) {
   return SCFA_OK;
 }
 
-}  // namespace
-}  // namespace scfa
+// Scratch of scfa_bwd_noalloc (log2 LSE and Delta of the sorted query
+// rows), in place of a caller-supplied workspace. Each device holds its own
+// copy for the life of the process; host code reaches it only through the
+// address hipGetSymbolAddress returns for that device (the array's name is
+// a host-side stand-in, not a device address). The preparation kernel
+// writes every row it covers before the other kernels read it, so nothing
+// has to be cleared between calls.
+__device__ __align__(256) uint8_t scratch[SCFA_NOALLOC_SCRATCH_BYTES];
 
-using namespace scfa;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[kMaxDevices] = {};
 
-extern "C" {
-
-size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D) {
-  if (!flags_ok(take_flags(mode))) return 0;
-  if ((mode != SCFA_QK && mode != SCFA_HASH) || B < 1 || H < 1 || Tq < 1 || Tk < 1 || D != HD) return 0;
-  size_t off[3];
-  return ws_layout(B, H, pad_rows(Tq), off);
+// Device address of `scratch` on the device of `stream`, looked up once per
+// device (with that device current, as it must be for the calls on it).
+int scratch_of_stream(hipStream_t stream, uint8_t** out) {
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return SCFA_ERR_HIP;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) return SCFA_ERR_HIP;
+  if (dev != cur) return SCFA_ERR_INVALID;  // the stream must belong to the current device
+  if (dev < 0 || dev >= kMaxDevices) return SCFA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SCFA_ERR_HIP;
+    g_scratch[dev] = static_cast<uint8_t*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return SCFA_OK;
 }
 
-int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
-             const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
-             const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
-             const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale, float* dQ, float* dK,
-             float* dV,
-             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Shared body of scfa_bwd and scfa_bwd_noalloc: argument checks, then the
+// preparation, dK/dV and dQ kernels with the workspace of log2 LSE and
+// Delta: `ws` (ws_bytes bytes) from the caller, or with `noalloc` the
+// device's static scratch (after every argument check).
+int bwd_run(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
+            const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
+            const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
+            const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale, float* dQ, float* dK,
+            float* dV, uint8_t* ws, size_t ws_bytes, bool noalloc, hipStream_t stream) {
   const int flags = take_flags(mode);
   if (!flags_ok(flags) || (mode != SCFA_QK && mode != SCFA_HASH)) return SCFA_ERR_INVALID;
   if (!q || !k || !v || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !bwd_tab || !O || !lse || !dO || !dQ ||
-      !dK || !dV || !workspace)
+      !dK || !dV || (!noalloc && !ws))
     return SCFA_ERR_INVALID;
   if (mode == SCFA_HASH && (!q_bkt || !k_bkt)) return SCFA_ERR_INVALID;
   if (B < 1 || H < 1 || T < 1 || T_kv < 1 || Tq < 1 || Tk < 1 || !(scale > 0.f) || !isfinite(scale))
@@ -1036,8 +1058,13 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
   if (mode == SCFA_QK && (Tq % SCFA_ROW_ALIGN || Tk != Tq)) return SCFA_ERR_INVALID;
   const int TqP = pad_rows(Tq), TkP = pad_rows(Tk);
   size_t off[3];
-  if (workspace_bytes < ws_layout(B, H, TqP, off)) return SCFA_ERR_INVALID;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (noalloc) {
+    if (ws_layout(B, H, TqP, off) > SCFA_NOALLOC_SCRATCH_BYTES) return SCFA_ERR_TOO_LARGE;
+    const int st = scratch_of_stream(stream, &ws);
+    if (st != SCFA_OK) return st;
+  } else if (ws_bytes < ws_layout(B, H, TqP, off)) {
+    return SCFA_ERR_INVALID;
+  }
   BwdParams p{};
   p.rc = reach_of(flags);
   p.q = q;
@@ -1074,6 +1101,40 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
   SCFA_RETURN_IF_LAUNCH_FAILED();
   if (mode == SCFA_HASH) return launch_bwd<true, false>(p, stream);
   return launch_bwd<false, true>(p, stream);
+}
+
+
+}  // namespace
+}  // namespace scfa
+
+using namespace scfa;
+
+extern "C" {
+
+size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D) {
+  if (!flags_ok(take_flags(mode))) return 0;
+  if ((mode != SCFA_QK && mode != SCFA_HASH) || B < 1 || H < 1 || Tq < 1 || Tk < 1 || D != HD) return 0;
+  size_t off[3];
+  return ws_layout(B, H, pad_rows(Tq), off);
+}
+
+int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
+             const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
+             const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
+             const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale, float* dQ, float* dK,
+             float* dV, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_run(mode, dtype_in, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, B,
+                 H, T, T_kv, Tq, Tk, D, scale, dQ, dK, dV, static_cast<uint8_t*>(workspace), workspace_bytes, false,
+                 stream);
+}
+
+int scfa_bwd_noalloc(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
+                     const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
+                     const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O,
+                     const float* lse, const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale,
+                     float* dQ, float* dK, float* dV, hipStream_t stream) {
+  return bwd_run(mode, dtype_in, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, B,
+                 H, T, T_kv, Tq, Tk, D, scale, dQ, dK, dV, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

@@ -1054,6 +1054,7 @@ const char* scfa_status_string(int status) {
     case SCFA_ERR_INVALID: return "SCFA_ERR_INVALID: invalid argument";
     case SCFA_ERR_UNSUPPORTED: return "SCFA_ERR_UNSUPPORTED: configuration not built";
     case SCFA_ERR_HIP: return "SCFA_ERR_HIP: HIP launch or runtime error";
+    case SCFA_ERR_TOO_LARGE: return "SCFA_ERR_TOO_LARGE: problem exceeds the static scratch of a no-allocation entry point";
     default: return "SCFA: unknown status";
   }
 }

@@ -19,7 +19,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libscfa.so")
 
-SCFA_OK, SCFA_ERR_INVALID, SCFA_ERR_UNSUPPORTED, SCFA_ERR_HIP = 0, -1, -2, -3
+SCFA_OK, SCFA_ERR_INVALID, SCFA_ERR_UNSUPPORTED, SCFA_ERR_HIP, SCFA_ERR_TOO_LARGE = 0, -1, -2, -3, -4
+SCFA_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 SCFA_DEVERR_COUNT_EXCEEDS_TC, SCFA_DEVERR_BUCKET_RANGE, SCFA_DEVERR_SEGMENT_OVERFLOW = 1, 2, 4
 SCFA_BF16, SCFA_F32 = 0, 1
 SCFA_DENSE, SCFA_QK, SCFA_HASH = 0, 1, 2
@@ -67,6 +68,8 @@ _SIGS = {
     "scfa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "scfa_bwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                       _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "scfa_bwd_noalloc": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                              _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp]),
 }
 
 _LIB = None
@@ -343,6 +346,21 @@ def scfa_bwd(mode, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab,
                           _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(O), _p(lse), _p(dO), B, H, T, T_kv, Tq, Tk, D, scale,
                           _p(dQ), _p(dK), _p(dV), _p(workspace), workspace.numel() * workspace.element_size(),
                           _stream(stream, q)), "scfa_bwd")
+
+
+def scfa_bwd_noalloc(mode, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, T, Tq,
+                     Tk, dQ, dK, dV, scale=None, stream=None):
+    """scfa_bwd without a workspace argument: the library's static per-device
+    scratch holds it (for callers that cannot allocate)."""
+    B, Tq_, H, D = q.shape
+    if Tq_ != T:
+        raise ScfaError("q must be the original (B,T,H,D) tensor")
+    T_kv = _kv_len(q, k, v)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(lib().scfa_bwd_noalloc(mode, _dt(q), _p(q), _p(k), _p(v), _p(q_idx), _p(k_idx), _p(q_bkt), _p(k_bkt),
+                                  _p(qstats), _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(O), _p(lse), _p(dO), B, H, T,
+                                  T_kv, Tq, Tk, D, scale, _p(dQ), _p(dK), _p(dV), _stream(stream, q)),
+           "scfa_bwd_noalloc")
 
 
 # ---------------------------------------------------------------------------

@@ -189,3 +189,28 @@ def test_header_constants_match_binding():
 def test_plan_rejects_strict_with_noncausal():
     with pytest.raises(scfa.ScfaError):
         scfa.Plan("hash", 1, 1, 128, strict=True, noncausal=True, device="cpu")
+
+
+def test_bwd_noalloc_rejects_without_gpu():
+    """The no-allocation backward checks its arguments and the size of its
+    static scratch before it touches the device."""
+    L = scfa.lib()
+    null = None
+    d = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    f = L.scfa_bwd_noalloc
+    ptrs = [d] * 14  # q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO
+
+    def call(mode, ps, B, H, T, Tq, Tk, D=64, dtype=scfa.SCFA_BF16, scale=0.125):
+        return f(mode, dtype, *ps, B, H, T, T, Tq, Tk, D, scale, d, d, d, null)
+
+    # NULL operand, NULL gradient, bad mode, fp32, D != 64
+    assert call(scfa.SCFA_HASH, [null] + ptrs[1:], 1, 1, 256, 256, 256) == scfa.SCFA_ERR_INVALID
+    assert f(scfa.SCFA_HASH, 0, *ptrs, 1, 1, 256, 256, 256, 256, 64, 0.125, null, d, d, null) == scfa.SCFA_ERR_INVALID
+    assert call(7, ptrs, 1, 1, 256, 256, 256) == scfa.SCFA_ERR_INVALID
+    assert call(scfa.SCFA_HASH, ptrs, 1, 1, 256, 256, 256, dtype=scfa.SCFA_F32) == scfa.SCFA_ERR_UNSUPPORTED
+    assert call(scfa.SCFA_HASH, ptrs, 1, 1, 256, 256, 256, D=32) == scfa.SCFA_ERR_UNSUPPORTED
+    # workspace beyond the static scratch: 8 bytes per query row of B*H*pad(Tq)
+    rows_max = scfa.SCFA_NOALLOC_SCRATCH_BYTES // 8
+    assert call(scfa.SCFA_QK, ptrs, 1, 17, 131072, 131072, 131072) == scfa.SCFA_ERR_TOO_LARGE
+    assert 17 * 131072 > rows_max
+    assert scfa.scfa_status_string(scfa.SCFA_ERR_TOO_LARGE).startswith("SCFA_ERR_TOO_LARGE")

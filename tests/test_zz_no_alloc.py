@@ -1,0 +1,70 @@
+"""The no-allocation backward (scfa_bwd_noalloc, static per-device scratch)
+against scfa_bwd with a caller workspace, through the C ABI: bit-equal
+gradients on two calls in a row, the second on a smaller problem, in hash
+and QK mode; a problem beyond the scratch is rejected before launch."""
+import numpy as np
+import pytest
+import torch
+
+import io_aware_attention_head_amd.scfa as scfa
+from io_aware_attention_head_amd.inputs import make_inputs, small
+from gpu_util import TOL_GRAD, announce, f64, need_gpu, oracle_buckets, run_pipeline
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(w):
+    x = make_inputs(w)
+    g, pre, tab, O, lse = run_pipeline(w, x)
+    ref = scfa.backward(pre, tab, O, lse, g["dO"])  # caller workspace (scfa_bwd)
+    ref = tuple(t.clone() for t in ref)
+    mode = scfa._table_mode(pre.mode) | scfa._flags(pre)
+    got = tuple(torch.full_like(t, float("nan")) for t in ref)
+    scfa.scfa_bwd_noalloc(mode, pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats,
+                          tab.kstats, tab.fwd, tab.bwd, O, lse, g["dO"], pre.T, pre.Tq, pre.Tk, *got)
+    torch.cuda.synchronize()
+    return x, ref, got
+
+
+@pytest.mark.parametrize("mode", ["hash", "qk"])
+def test_bwd_noalloc_matches_bwd(mode):
+    need_gpu()
+    sizes = [(2, 3, 3000), (1, 2, 700)]  # second call smaller than the first
+    for i, (B, H, T) in enumerate(sizes):
+        announce(f"bwd noalloc {mode} call {i} B={B} H={H} T={T}")
+        w = small(mode, B, H, T, nb=16, keep_p=0.6, seed=81 + i, grad=True)
+        x, ref, got = _both(w)
+        for name, a, b in zip(("dQ", "dK", "dV"), ref, got):
+            assert torch.equal(a, b), f"call {i}: {name} differs from scfa_bwd"
+        # and within the gradient tolerance of the oracle on one head
+        import oracle
+        q, k, v, dO = (f64(x[n]) for n in ("q", "k", "v", "dO"))
+        if mode == "hash":
+            bq, bk = oracle_buckets(w, x)
+            r = oracle.attention_bwd("hash", q, k, v, dO, bkt_q=bq, bkt_k=bk, heads=[(0, 0)])
+        else:
+            r = oracle.attention_bwd("qk", q, k, v, dO, x["keep_q"].numpy(), x["keep_k"].numpy(), heads=[(0, 0)])
+        for name, t, rr in zip(("dQ", "dK", "dV"), got, r):
+            gs, rs = f64(t)[0, :, 0], rr[0, :, 0]
+            rel = float(np.linalg.norm(gs - rs) / np.linalg.norm(rs))
+            assert rel <= TOL_GRAD, f"call {i}: {name} relative Frobenius error {rel:.3e}"
+
+
+def test_bwd_noalloc_too_large_rejected():
+    need_gpu()
+    announce("bwd noalloc too large")
+    w = small("qk", 1, 1, 300, keep_p=0.6, seed=83, grad=True)
+    x = make_inputs(w)
+    g, pre, tab, O, lse = run_pipeline(w, x)
+    dQ, dK, dV = (torch.zeros((1, 300, 1, 64), dtype=torch.float32, device="cuda") for _ in range(3))
+    # claim a query length whose workspace exceeds the scratch: rejected on
+    # the host before any launch, outputs untouched
+    big = scfa.SCFA_NOALLOC_SCRATCH_BYTES // 8 + 128
+    L = scfa.lib()
+    st = L.scfa_bwd_noalloc(scfa.SCFA_QK, scfa.SCFA_BF16, *(scfa._p(t) for t in (
+        pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx)), None, None, *(scfa._p(t) for t in (
+            tab.qstats, tab.kstats, tab.fwd, tab.bwd, O, lse, g["dO"])), 1, 1, 300, 300, scfa.pad_rows(big),
+        scfa.pad_rows(big), 64, 0.125, scfa._p(dQ), scfa._p(dK), scfa._p(dV), None)
+    assert st == scfa.SCFA_ERR_TOO_LARGE
+    torch.cuda.synchronize()
+    assert (dQ == 0).all() and (dK == 0).all() and (dV == 0).all()
