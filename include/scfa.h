@@ -444,6 +444,15 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
  *                exactly the index arrays and tables of the forward call.
  *  bwd_tab       the backward table of the same call (scfa_range_table or
  *                scfa_bwd_table).
+ *  fwd_order     launch order of the dQ workgroups: scfa_work_order on
+ *                fwd_tab (the forward call's order), or NULL (then query
+ *                tiles run in descending index order).
+ *  bwd_order     launch order of the dK/dV workgroups of the hash mode (one
+ *                workgroup per key tile): scfa_work_order on bwd_tab with
+ *                span = query tiles per head, or NULL (key tiles in index
+ *                order). QK mode runs pairs of key tiles in index order
+ *                and does not read it. Any permutation gives the same
+ *                results; only the schedule moves.
  *  O             (B, T, H, D) fp32 forward output;  lse (B, H, T) fp32.
  *  dO            (B, T, H, D) upstream gradient, dtype_in.
  *  T, T_kv       original query and key/value lengths, as in the forward;
@@ -462,9 +471,10 @@ size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D);
 
 int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
              const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
-             const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
-             const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale, float* dQ, float* dK,
-             float* dV, void* workspace, size_t workspace_bytes, hipStream_t stream);
+             const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const int32_t* fwd_order,
+             const int32_t* bwd_order, const float* O, const float* lse, const void* dO, int B, int H, int T, int T_kv,
+             int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV, void* workspace,
+             size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Backward without a workspace argument, for callers that cannot allocate
@@ -490,9 +500,9 @@ int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v
 
 int scfa_bwd_noalloc(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
                      const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
-                     const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O,
-                     const float* lse, const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale,
-                     float* dQ, float* dK, float* dV, hipStream_t stream);
+                     const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const int32_t* fwd_order,
+                     const int32_t* bwd_order, const float* O, const float* lse, const void* dO, int B, int H, int T,
+                     int T_kv, int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -54,7 +54,10 @@ constexpr int BN = SCFA_TILE_N;  // 64: dK/dV workgroup keys, table granularity
 constexpr int QC = 32;          // query chunk of the dK/dV loop
 constexpr int HD = 64;
 constexpr int TB = 64 * HD * 2;  // bytes of one 64 x 64 bf16 tile
-constexpr int kStatCap = 256;    // tile statistics of a range held in LDS
+constexpr int kStatCap = 256;    // tile statistics of a range held in LDS (dK/dV)
+// ... and in the dQ kernel: 128 entries keep its LDS at 52 KB, so that three
+// workgroups fit a compute unit (VGPRs allow three waves per SIMD)
+constexpr int kStatCapQ = 128;
 
 struct BwdParams {
   const void* q;   // (B, T, H, D) bf16, original order, as are k, v, dO
@@ -71,6 +74,8 @@ struct BwdParams {
   const int4* kstats;
   const int2* fwd_tab;
   const int2* bwd_tab;
+  const int32_t* q_order;  // launch order of the dQ workgroups (over fwd_tab items), or null
+  const int32_t* k_order;  // launch order of the dK/dV workgroups (over bwd_tab items), or null
   float* dQ;
   float* dK;
   float* dV;
@@ -195,6 +200,18 @@ __device__ inline void map_work(int x, int BH, int ntiles, int& tile, int& bh, b
   tile = reverse ? ntiles - 1 - t : t;
 }
 
+// Work item of workgroup x: from a launch order (item = bh * ntiles + tile,
+// longest range first) when one is given, else the default mapping.
+__device__ inline void pick_item(const int32_t* order, int x, int BH, int ntiles, int& tile, int& bh, bool reverse) {
+  if (order) {
+    const int it = order[x];
+    bh = it / ntiles;
+    tile = it - bh * ntiles;
+  } else {
+    map_work(x, BH, ntiles, tile, bh, reverse);
+  }
+}
+
 __device__ __forceinline__ int4 uniform4(const int4& v) {
   return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
                    __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
@@ -266,7 +283,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   const int ws = __builtin_amdgcn_readfirstlane(w);
   const int BH = p.B * p.H;
   int kt, bh;
-  map_work(blockIdx.x, BH, p.nKt, kt, bh, false);  // early key tiles see the most queries
+  pick_item(p.k_order, blockIdx.x, BH, p.nKt, kt, bh, false);  // longest ranges first
   const int b = bh / p.H, h = bh - b * p.H;
   const size_t rowbase = static_cast<size_t>(bh) * p.TqP;  // query side
   const size_t kbase = static_cast<size_t>(bh) * p.TkP;    // key side
@@ -783,7 +800,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   __shared__ __align__(16) uint8_t smem[2 * 3 * TB];  // 2 stages x (K rows, K tr, V rows); epilogue staging
   __shared__ __align__(16) int32_t Kp[2][BN];
   __shared__ __align__(16) int32_t Kb[2][BN];
-  __shared__ __align__(16) int4 Kst[kStatCap];
+  __shared__ __align__(16) int4 Kst[kStatCapQ];
   static_assert(2 * 3 * TB >= BM * HD * 4, "dQ staging does not fit");
 
   const int tid = threadIdx.x;
@@ -791,7 +808,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   const int ws = __builtin_amdgcn_readfirstlane(w);
   const int BH = p.B * p.H;
   int qt, bh;
-  map_work(blockIdx.x, BH, p.nQt, qt, bh, true);
+  pick_item(p.q_order, blockIdx.x, BH, p.nQt, qt, bh, true);
   const int b = bh / p.H, h = bh - b * p.H;
   const size_t rowbase = static_cast<size_t>(bh) * p.TqP;  // query side
   const size_t kbase = static_cast<size_t>(bh) * p.TkP;    // key side
@@ -799,10 +816,10 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
   const int qreach = q_reach(p.rc, qs.y);  // largest key position a query of the tile may see
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
-  const bool kst_lds = rng.y - rng.x <= kStatCap;
+  const bool kst_lds = rng.y - rng.x <= kStatCapQ;
   // statistics of the range: loaded here, stored to LDS at the first barrier
   // (after the first tile's DMA), so the query and key loads do not wait
-  static_assert(kStatCap <= 256, "statistics copy: one entry per thread");
+  static_assert(kStatCapQ <= 256, "statistics copy: one entry per thread");
   const int nks = kst_lds ? rng.y - rng.x : 0;
   int4 kst_a = make_int4(0, 0, 0, 0);
   if (tid < nks) kst_a = kst[rng.x + tid];
@@ -1039,9 +1056,10 @@ int scratch_of_stream(hipStream_t stream, uint8_t** out) {
 // device's static scratch (after every argument check).
 int bwd_run(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
             const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
-            const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
-            const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale, float* dQ, float* dK,
-            float* dV, uint8_t* ws, size_t ws_bytes, bool noalloc, hipStream_t stream) {
+            const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const int32_t* fwd_order,
+            const int32_t* bwd_order, const float* O, const float* lse, const void* dO, int B, int H, int T, int T_kv,
+            int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV, uint8_t* ws, size_t ws_bytes,
+            bool noalloc, hipStream_t stream) {
   const int flags = take_flags(mode);
   if (!flags_ok(flags) || (mode != SCFA_QK && mode != SCFA_HASH)) return SCFA_ERR_INVALID;
   if (!q || !k || !v || !q_idx || !k_idx || !qstats || !kstats || !fwd_tab || !bwd_tab || !O || !lse || !dO || !dQ ||
@@ -1081,6 +1099,8 @@ int bwd_run(int mode, int dtype_in, const void* q, const void* k, const void* v,
   p.kstats = reinterpret_cast<const int4*>(kstats);
   p.fwd_tab = reinterpret_cast<const int2*>(fwd_tab);
   p.bwd_tab = reinterpret_cast<const int2*>(bwd_tab);
+  p.q_order = fwd_order;
+  p.k_order = bwd_order;
   p.dQ = dQ;
   p.dK = dK;
   p.dV = dV;
@@ -1120,21 +1140,22 @@ size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D) {
 
 int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
              const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
-             const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O, const float* lse,
-             const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale, float* dQ, float* dK,
-             float* dV, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return bwd_run(mode, dtype_in, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, B,
-                 H, T, T_kv, Tq, Tk, D, scale, dQ, dK, dV, static_cast<uint8_t*>(workspace), workspace_bytes, false,
-                 stream);
+             const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const int32_t* fwd_order,
+             const int32_t* bwd_order, const float* O, const float* lse, const void* dO, int B, int H, int T, int T_kv,
+             int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV, void* workspace,
+             size_t workspace_bytes, hipStream_t stream) {
+  return bwd_run(mode, dtype_in, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, fwd_order,
+                 bwd_order, O, lse, dO, B, H, T, T_kv, Tq, Tk, D, scale, dQ, dK, dV, static_cast<uint8_t*>(workspace),
+                 workspace_bytes, false, stream);
 }
 
 int scfa_bwd_noalloc(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
                      const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
-                     const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const float* O,
-                     const float* lse, const void* dO, int B, int H, int T, int T_kv, int Tq, int Tk, int D, float scale,
-                     float* dQ, float* dK, float* dV, hipStream_t stream) {
-  return bwd_run(mode, dtype_in, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, B,
-                 H, T, T_kv, Tq, Tk, D, scale, dQ, dK, dV, nullptr, 0, true, stream);
+                     const int32_t* kstats, const int32_t* fwd_tab, const int32_t* bwd_tab, const int32_t* fwd_order,
+                     const int32_t* bwd_order, const float* O, const float* lse, const void* dO, int B, int H, int T,
+                     int T_kv, int Tq, int Tk, int D, float scale, float* dQ, float* dK, float* dV, hipStream_t stream) {
+  return bwd_run(mode, dtype_in, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, fwd_order,
+                 bwd_order, O, lse, dO, B, H, T, T_kv, Tq, Tk, D, scale, dQ, dK, dV, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

@@ -66,10 +66,8 @@ _SIGS = {
     "scfa_hash_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                   _i, _i, _f, _i, _vp, _vp, _vp]),
     "scfa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
-    "scfa_bwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
-                      _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "scfa_bwd_noalloc": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
-                              _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp]),
+    "scfa_bwd": (_i, [_i, _i] + [_vp] * 16 + [_i] * 7 + [_f, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "scfa_bwd_noalloc": (_i, [_i, _i] + [_vp] * 16 + [_i] * 7 + [_f, _vp, _vp, _vp, _vp]),
 }
 
 _LIB = None
@@ -334,22 +332,23 @@ def scfa_bwd_workspace_bytes(mode, B, H, Tq, Tk, D=64) -> int:
 
 
 def scfa_bwd(mode, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, T, Tq, Tk, dQ,
-             dK, dV, workspace, scale=None, stream=None):
+             dK, dV, workspace, scale=None, stream=None, fwd_order=None, bwd_order=None):
     """q, dO: original (B,T,H,D), k, v: original (B,T_kv,H,D) bf16 tensors
-    (read through the index arrays)."""
+    (read through the index arrays); fwd_order / bwd_order: optional launch
+    orders from scfa_work_order."""
     B, Tq_, H, D = q.shape
     if Tq_ != T:
         raise ScfaError("q must be the original (B,T,H,D) tensor")
     T_kv = _kv_len(q, k, v)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(lib().scfa_bwd(mode, _dt(q), _p(q), _p(k), _p(v), _p(q_idx), _p(k_idx), _p(q_bkt), _p(k_bkt), _p(qstats),
-                          _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(O), _p(lse), _p(dO), B, H, T, T_kv, Tq, Tk, D, scale,
-                          _p(dQ), _p(dK), _p(dV), _p(workspace), workspace.numel() * workspace.element_size(),
-                          _stream(stream, q)), "scfa_bwd")
+                          _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(fwd_order), _p(bwd_order), _p(O), _p(lse), _p(dO), B,
+                          H, T, T_kv, Tq, Tk, D, scale, _p(dQ), _p(dK), _p(dV), _p(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream, q)), "scfa_bwd")
 
 
 def scfa_bwd_noalloc(mode, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO, T, Tq,
-                     Tk, dQ, dK, dV, scale=None, stream=None):
+                     Tk, dQ, dK, dV, scale=None, stream=None, fwd_order=None, bwd_order=None):
     """scfa_bwd without a workspace argument: the library's static per-device
     scratch holds it (for callers that cannot allocate)."""
     B, Tq_, H, D = q.shape
@@ -358,8 +357,9 @@ def scfa_bwd_noalloc(mode, q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, 
     T_kv = _kv_len(q, k, v)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(lib().scfa_bwd_noalloc(mode, _dt(q), _p(q), _p(k), _p(v), _p(q_idx), _p(k_idx), _p(q_bkt), _p(k_bkt),
-                                  _p(qstats), _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(O), _p(lse), _p(dO), B, H, T,
-                                  T_kv, Tq, Tk, D, scale, _p(dQ), _p(dK), _p(dV), _stream(stream, q)),
+                                  _p(qstats), _p(kstats), _p(fwd_tab), _p(bwd_tab), _p(fwd_order), _p(bwd_order),
+                                  _p(O), _p(lse), _p(dO), B, H, T, T_kv, Tq, Tk, D, scale, _p(dQ), _p(dK), _p(dV),
+                                  _stream(stream, q)),
            "scfa_bwd_noalloc")
 
 
@@ -426,6 +426,7 @@ class Tables:
     Bm: int
     Bn: int
     fwd_order: Optional[torch.Tensor] = None  # launch order of the forward / dQ workgroups
+    bwd_order: Optional[torch.Tensor] = None  # launch order of the dK/dV workgroups (hash mode)
 
 
 def _empty(shape, dtype, like):
@@ -552,6 +553,8 @@ def build_tables(pre: Prepared, Bm: int = SCFA_TILE_M, Bn: int = SCFA_TILE_N, st
                      pre.Tk, Bm, Bn, t.qstats, t.kstats, t.fwd, t.bwd, t.tiles, stream)
     t.fwd_order = _empty((B * H * nQt,), i32, d)
     scfa_work_order(t.fwd, nKt, t.fwd_order, stream)
+    t.bwd_order = _empty((B * H * nKt,), i32, d)
+    scfa_work_order(t.bwd, nQt, t.bwd_order, stream)
     return t
 
 
@@ -591,8 +594,9 @@ def backward(pre: Prepared, tab: Tables, O, lse, dO, scale=None, grads=None, wor
     if workspace is None:
         workspace = _empty((scfa_bwd_workspace_bytes(mode, B, H, pre.Tq, pre.Tk, D),), torch.uint8, pre.q_in)
     dQ, dK, dV = grads
-    scfa_bwd(mode | _flags(pre), pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats, tab.kstats, tab.fwd,
-             tab.bwd, O, lse, dO, T, pre.Tq, pre.Tk, dQ, dK, dV, workspace, scale, stream)
+    scfa_bwd(mode | _flags(pre), pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats,
+             tab.kstats, tab.fwd, tab.bwd, O, lse, dO, T, pre.Tq, pre.Tk, dQ, dK, dV, workspace, scale, stream,
+             fwd_order=tab.fwd_order, bwd_order=tab.bwd_order)
     return dQ, dK, dV
 
 
@@ -696,7 +700,7 @@ class Plan:
         Bm, Bn = SCFA_TILE_M, SCFA_TILE_N
         nQt, nKt = TqP // Bm, TkP // Bn
         self.tab = Tables(e((B, H, nQt, 4)), e((B, H, nKt, 4)), e((B, H, nQt, 2)), e((B, H, nKt, 2)), e((B, H)), Bm, Bn,
-                          e((B * H * nQt,)))
+                          e((B * H * nQt,)), e((B * H * nKt,)) if mode == "hash" else None)
         self.O = e((B, T, H, D), out_dtype)
         self.lse = e((B, H, T), torch.float32)
         self.pairs = e((B, H), torch.int64)
@@ -764,6 +768,8 @@ class Plan:
         if self.x is None:
             raise ScfaError("backward needs a prepared forward")
         scfa_bwd_table(self.tab.qstats, self.tab.kstats, self.tab.fwd, self.tab.bwd, stream, self.flags)
+        if self.mode == "hash":  # one dK/dV workgroup per key tile: longest query ranges first
+            scfa_work_order(self.tab.bwd, self.tab.fwd.shape[2], self.tab.bwd_order, stream)
         if self._grads is None:
             d = self.device
             self._grads = tuple(torch.empty((self.B, n, self.H, self.D), dtype=torch.float32, device=d)

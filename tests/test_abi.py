@@ -198,7 +198,9 @@ def test_bwd_noalloc_rejects_without_gpu():
     null = None
     d = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     f = L.scfa_bwd_noalloc
-    ptrs = [d] * 14  # q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, O, lse, dO
+    # q, k, v, q_idx, k_idx, q_bkt, k_bkt, qstats, kstats, fwd_tab, bwd_tab, fwd_order, bwd_order (optional),
+    # O, lse, dO
+    ptrs = [d] * 11 + [null, null] + [d] * 3
 
     def call(mode, ps, B, H, T, Tq, Tk, D=64, dtype=scfa.SCFA_BF16, scale=0.125):
         return f(mode, dtype, *ps, B, H, T, T, Tq, Tk, D, scale, d, d, d, null)

@@ -21,7 +21,8 @@ def _both(w):
     mode = scfa._table_mode(pre.mode) | scfa._flags(pre)
     got = tuple(torch.full_like(t, float("nan")) for t in ref)
     scfa.scfa_bwd_noalloc(mode, pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx, pre.q_bkt, pre.k_bkt, tab.qstats,
-                          tab.kstats, tab.fwd, tab.bwd, O, lse, g["dO"], pre.T, pre.Tq, pre.Tk, *got)
+                          tab.kstats, tab.fwd, tab.bwd, O, lse, g["dO"], pre.T, pre.Tq, pre.Tk, *got,
+                          fwd_order=tab.fwd_order, bwd_order=tab.bwd_order)
     torch.cuda.synchronize()
     return x, ref, got
 
@@ -63,7 +64,8 @@ def test_bwd_noalloc_too_large_rejected():
     L = scfa.lib()
     st = L.scfa_bwd_noalloc(scfa.SCFA_QK, scfa.SCFA_BF16, *(scfa._p(t) for t in (
         pre.q_in, pre.k_in, pre.v_in, pre.q_idx, pre.k_idx)), None, None, *(scfa._p(t) for t in (
-            tab.qstats, tab.kstats, tab.fwd, tab.bwd, O, lse, g["dO"])), 1, 1, 300, 300, scfa.pad_rows(big),
+            tab.qstats, tab.kstats, tab.fwd, tab.bwd)), None, None, *(scfa._p(t) for t in (O, lse, g["dO"])), 1, 1,
+        300, 300, scfa.pad_rows(big),
         scfa.pad_rows(big), 64, 0.125, scfa._p(dQ), scfa._p(dK), scfa._p(dV), None)
     assert st == scfa.SCFA_ERR_TOO_LARGE
     torch.cuda.synchronize()
