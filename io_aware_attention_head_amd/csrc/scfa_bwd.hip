@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   int4 qst_a = make_int4(0, 0, 0, 0);
   if (tid < nqs) qst_a = qst[rng.x + tid];
   const int ki_v = tid < BN ? p.k_idx[kbase + kt * BN + tid] : 0;
-  auto qstat = [&](int i) { return uniform4(qst_lds ? Qst[i - rng.x] : qst[i]); };
+  auto qstat = [&](int i) { return uniform4(stat_entry(qst_lds, Qst, i - rng.x, qst, i)); };
 
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
   const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;     // token 0 of this head in q, dO
@@ -569,7 +569,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     for (int i = tid; i < hi - lo; i += 256) Qst[i] = qst[lo + i];
   if (tid < KR) Ki[tid] = (tid < BN || has1) ? p.k_idx[kbase + kt0 * BN + tid] : SCFA_K_PAD;
   __syncthreads();
-  auto qstat = [&](int i) { return uniform4(qst_lds ? Qst[i - lo] : qst[i]); };
+  auto qstat = [&](int i) { return uniform4(stat_entry(qst_lds, Qst, i - lo, qst, i)); };
 
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
   const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;     // token 0 of this head in q, dO
@@ -823,7 +823,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   const int nks = kst_lds ? rng.y - rng.x : 0;
   int4 kst_a = make_int4(0, 0, 0, 0);
   if (tid < nks) kst_a = kst[rng.x + tid];
-  auto kstat = [&](int j) { return uniform4(kst_lds ? Kst[j - rng.x] : kst[j]); };
+  auto kstat = [&](int j) { return uniform4(stat_entry(kst_lds, Kst, j - rng.x, kst, j)); };
 
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;
   const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;     // token 0 of this head in q, dO

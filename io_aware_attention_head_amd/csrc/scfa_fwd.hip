@@ -35,9 +35,12 @@
 //  * K and V tiles are staged by global-to-LDS DMA (no registers), double
 //    buffered; the key positions of the tile after next are prefetched into
 //    registers one tile ahead, so DMA addresses never wait on a load.
-//  * The reference max moves only when a row's tile max exceeds it by more
-//    than 2^8 (lazy rescaling): probabilities stay <= 256 and the O rescale
-//    is rare. O and the LSE use the fp32 row sum of the probabilities.
+//  * Speculative reference max: a tile's weights are exponentiated against
+//    the current reference without looking at the tile's max; the row max is
+//    taken only for a row's first tile with a visible key, or when some weight
+//    exceeds 2^64 (then the weights are recomputed), so the O rescale is rare
+//    and the per-tile max reduction is gone. O and the LSE use the fp32 row
+//    sum of the probabilities. (The fp32 kernel keeps an exact running max.)
 //  * Per-wave tile tests from the extrema: a key tile holding no pair visible
 //    to any of the wave's 32 queries is skipped by that wave, and one whose
 //    pairs are all visible skips the mask.
@@ -57,7 +60,10 @@ constexpr int BM = SCFA_TILE_M;  // 128 query rows per workgroup
 constexpr int BN = SCFA_TILE_N;  // 64 keys per tile
 constexpr int HD = 64;           // head dimension
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLazy = 8.0f;  // log2 headroom before the reference max moves
+// Largest lane sum of 16 weights accepted against a reference max (bf16
+// kernel): weights up to 2^64 keep O, the row sums and their bf16 copies far
+// from the fp32 range limits.
+constexpr float kSpecCap = 18446744073709551616.0f;  // 2^64
 
 struct FwdParams {
   const void* q;  // (B, T, H, D) original order, as are k and v
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   if (tid + 256 < nks) kst_b = kst[rng.x + tid + 256];
   // statistics of key tile j, rng.x <= j < rng.y
   auto kstat = [&](int j) -> int4 {
-    const int4 v = kst_lds ? Kst[j - rng.x] : kst[j];
+    const int4 v = stat_entry(kst_lds, Kst, j - rng.x, kst, j);
     return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
                      __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
   };
@@ -403,42 +409,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         scores_bf16(S, Ks, Qb, r16, g);
       }
 
-      // -- online softmax, lazy reference max ---------------------------------
-      // Each lane tests its own 16 scores per query against the shared
-      // reference; only when some lane is more than 2^kLazy above it is the
-      // row max taken across the lane groups and the reference moved.
-      float lmx[2];
+      // -- online softmax, speculative reference ------------------------------
+      // The weights are exponentiated against the current reference max
+      // without looking at this tile's max; the row max is taken only while a
+      // row of the wave has no reference yet (its first tile with a visible
+      // key) or when some weight of the tile exceeds 2^kSpec (a lane's sum of
+      // its 16 weights above 2^kSpec, or not finite); then the reference
+      // moves to the row max and the weights are recomputed.
+      bf16x8 P[2][2];
+      float ls[2];
+      auto expo = [&](int qb, float muse) {
+        float sum = 0.f;
+        f32x4 t[4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) lmx[qb] = lane_max_scaled(S, qb, p.c);
-      if (__ballot(lmx[0] > m[0] + kLazy || lmx[1] > m[1] + kLazy)) {
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            t[kb][e] = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][e], p.c, -muse));
+            sum += t[kb][e];
+          }
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) P[qb][kc] = pack_bf16x8(t[2 * kc], t[2 * kc + 1]);
+        return sum;
+      };
+      bool need_max = __ballot(m[0] == -INFINITY || m[1] == -INFINITY) != 0;
+      if (!need_max) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) ls[qb] = expo(qb, m[qb]);
+        need_max = __ballot(!(ls[0] <= kSpecCap) || !(ls[1] <= kSpecCap)) != 0;
+      }
+      if (need_max) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const float mnew = fmaxf(m[qb], group_max(lmx[qb]));
+          const float mnew = fmaxf(m[qb], row_max_scaled(S, qb, p.c));
           const float muse = (mnew == -INFINITY) ? 0.f : mnew;
           const float alpha = __builtin_amdgcn_exp2f(m[qb] - muse);  // 1 when unchanged, 0 from -inf
           m[qb] = mnew;
 #pragma unroll
           for (int db = 0; db < 4; ++db) Oacc[db][qb] *= alpha;
           l[qb] *= alpha;
+          ls[qb] = expo(qb, muse);
         }
       }
-      bf16x8 P[2][2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float muse = (m[qb] == -INFINITY) ? 0.f : m[qb];
-        float ls = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][e], p.c, -muse));
-            S[kb][qb][e] = pv;
-            ls += pv;
-          }
-        l[qb] += ls;
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) P[qb][kc] = pack_bf16x8(S[2 * kc][qb], S[2 * kc + 1][qb]);
-      }
+      for (int qb = 0; qb < 2; ++qb) l[qb] += ls[qb];
 
       // -- O^T += V^T P^T ------------------------------------------------------
       // V^T operand of (db, kc): dims 16db + r16, keys 32kc + 8g + 0..7.

@@ -29,6 +29,26 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
+// Tile statistics entry of a range: from its LDS copy when the range fits
+// the copy, else from global memory. The two reads stay two loads in two
+// branches (pointers of their own address spaces, and a scheduling barrier
+// that makes the branches differ): folded into one load of a selected
+// pointer they become a flat load, which waits on every outstanding memory
+// operation (the K/V DMA included) instead of the LDS alone.
+__device__ __forceinline__ int4 stat_entry(bool in_lds, const int4* lds_copy, int li, const int4* glob, int gi) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(3))) i32x4 lds_i32x4;
+  typedef const __attribute__((address_space(1))) i32x4 glb_i32x4;
+  i32x4 v;
+  if (in_lds) {
+    v = *(lds_i32x4*)(lds_copy + li);
+  } else {
+    v = *(glb_i32x4*)(glob + gi);
+    __builtin_amdgcn_sched_barrier(0);  // the branches differ: no common load to sink
+  }
+  return make_int4(v[0], v[1], v[2], v[3]);
+}
+
 // Row of the original (B, T, H, D) tensors for an index entry: pads (and any
 // entry outside [0, T)) read token 0, whose values are finite.
 __device__ inline int src_row(int pos, int T) { return (pos >= 0 && pos < T) ? pos : 0; }

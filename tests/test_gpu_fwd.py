@@ -299,3 +299,30 @@ def test_plan_full_size_graph(name):
         plan.run(g)  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(plan.O, O_ref)
+
+
+@pytest.mark.parametrize("mode", ["dense", "hash", "qk"])
+def test_fwd_reference_moves(mode):
+    """Keys whose scale grows with their position, so that each later key
+    tile scores far above the earlier ones: the forward's reference max (taken
+    on a row's first visible tile) must move whenever a tile's weights would
+    exceed 2^64, many times per row. O, LSE and the -inf pattern against the
+    oracle on every row (hash with R = 0: one bucket; values halved, see
+    below)."""
+    need_gpu()
+    announce(f"fwd reference moves {mode}")
+    w = small(mode, 1, 2, 1500, nb=16, keep_p=0.8, seed=66)
+    x = make_inputs(w)
+    ramp = torch.linspace(1.0, 40.0, w.T).view(1, w.T, 1, 1)
+    x["k"] = (x["k"].float() * ramp).to(torch.bfloat16)
+    # Nearly one-hot rows: the bf16 rounding of the dominant weight alone can
+    # move O by 2^-9 |v|, so v is halved (exactly) to keep that under 1e-2.
+    x["v"] = x["v"] * 0.5
+    if mode == "hash":
+        x["R"].zero_()
+    _, pre, tab, O, lse = run_pipeline(w, x)
+    Or, Lr = oracle_fwd(w, x)
+    s = f64(x["q"])[0, :, 0] @ f64(x["k"])[0, :, 0].T * 0.125 * 1.4426950408889634
+    assert s.max() - s[:, :64].max() > 64  # later keys exceed the first tile's reference by more than 2^64
+    err, lerr = check_fwd(w, O, lse, Or, Lr)
+    print(f"reference moves {mode}: max-abs {err:.2e}  lse {lerr:.2e}")
