@@ -490,3 +490,5 @@ def test_plan_two_side_launches_bitexact(w):
     torch.cuda.synchronize()
     for name in ("qstats", "kstats", "fwd", "tiles"):
         assert torch.equal(getattr(plan.tab, name), getattr(ref, name)), name
+    # the Plan's launch order over its forward table
+    check_order(plan.tab.fwd_order.cpu().numpy(), plan.tab.fwd.cpu().numpy())
