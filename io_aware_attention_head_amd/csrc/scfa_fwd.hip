@@ -43,7 +43,9 @@
 //    sum of the probabilities. (The fp32 kernel keeps an exact running max.)
 //  * Per-wave tile tests from the extrema: a key tile holding no pair visible
 //    to any of the wave's 32 queries is skipped by that wave, and one whose
-//    pairs are all visible skips the mask.
+//    pairs are all visible skips the mask. The tests of 64 key tiles at a time
+//    are taken at once (one tile per lane) and kept as wave-uniform bit masks,
+//    so the tile loop reads no statistics.
 //  * Work order: a launch order (longest query tiles first, XCD-aware) from
 //    scfa_work_order, or descending query-tile index.
 //  * float32 inputs use v_mfma_f32_16x16x4_f32 in a single-buffered kernel
@@ -252,11 +254,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   __shared__ __align__(16) int32_t Kp[2][BN];
   __shared__ __align__(16) int32_t Kb[2][BN];
   __shared__ int32_t Qi[BM];
-  // statistics of the key tiles of this workgroup's range (ranges longer
-  // than kKstCap read them from global memory instead)
-  constexpr int kKstCap = 512;
-  __shared__ __align__(16) int4 Kst[kKstCap];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
   const int ws = __builtin_amdgcn_readfirstlane(w);
@@ -269,7 +266,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
   const int qreach = q_reach(p.rc, qs.y);  // largest key position a query of the tile may see
   const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
-  // index entries of the tile (to LDS at the first barrier; loaded here with
+  // index entries of the tile (to LDS before the first barrier; loaded here with
   // the table so the stores wait on nothing later)
   const int qi_v = tid < BM ? p.q_idx[rowbase + qt * BM + tid] : 0;
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
@@ -285,18 +282,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     qpos[qb] = p.q_idx[rowbase + row];
     qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
   }
-  const bool kst_lds = rng.y - rng.x <= kKstCap;
-  static_assert(kKstCap <= 2 * 256, "statistics copy: two entries per thread");
-  const int nks = kst_lds ? rng.y - rng.x : 0;  // entries copied to LDS
-  int4 kst_a = make_int4(0, 0, 0, 0), kst_b = make_int4(0, 0, 0, 0);
-  if (tid < nks) kst_a = kst[rng.x + tid];
-  if (tid + 256 < nks) kst_b = kst[rng.x + tid + 256];
-  // statistics of key tile j, rng.x <= j < rng.y
-  auto kstat = [&](int j) -> int4 {
-    const int4 v = stat_entry(kst_lds, Kst, j - rng.x, kst, j);
-    return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
-                     __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
+  // Tile tests in windows of 64 key tiles of the range (window k: tiles
+  // rng.x + 64 k ...), as wave-uniform bit masks; lane i loads the statistics
+  // of tile i of a window. cw_* is the window of the current tile; pre_* holds
+  // the statistics of one more window (the next one, prefetched, or the one a
+  // search for the next tile reached).
+  auto load_stats = [&](int wb) -> int4 {
+    int4 v = make_int4(0, 0, 0, 0);
+    if (wb + lane < rng.y) v = kst[wb + lane];
+    return v;
   };
+  const int4 st0 = load_stats(rng.x);
+  int pre_wb = rng.y - rng.x > 64 ? rng.x + 64 : -1;
+  int4 pre_st = pre_wb >= 0 ? load_stats(pre_wb) : make_int4(0, 0, 0, 0);
+  bool pre_pass_ok = false;
+  uint64_t pre_pass = 0;
   const WaveRows wr = wave_rows(qpos, qbkt, p.rc);
   // positions the masks compare keys against: the largest visible key position
   const int qcmp[2] = {q_reach(p.rc, qpos[0]), q_reach(p.rc, qpos[1])};
@@ -351,46 +351,75 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     else if (HASH && ws == 1) dma4(kbg + j * BN, lane * 4, ldsb + s * BN * 4);
   };
 
-  // first tile from j on that passes the causal extremum test (hash ranges;
-  // every tile of a QK range passes it)
-  auto next_tile = [&](int j) {
-    if (HASH)
-      while (j < rng.y && kstat(j).x > qreach) ++j;
-    return j;
+  int cw_wb = rng.x;
+  TileMasks cw = tile_masks<HASH>(st0, rng.x + lane, rng.y, qreach, wr, p.Tk);
+  auto fetch_pre = [&](int wb) {
+    if (pre_wb != wb) {
+      pre_wb = wb;
+      pre_st = load_stats(wb);
+      pre_pass_ok = false;
+    }
+  };
+  // first tile from `from` on that passes the workgroup's causal extremum
+  // test (every tile of a QK range passes it), or rng.y
+  auto find_next = [&](int from) -> int {
+    if (!HASH) return min(from, rng.y);
+    if (from >= rng.y) return rng.y;
+    {  // the current window (from >= cw_wb: tiles are visited in order)
+      const int o = from - cw_wb;
+      if (o < 64) {
+        const uint64_t m = cw.pass & (~0ull << o);
+        if (m) return cw_wb + static_cast<int>(__builtin_ctzll(m));
+        from = cw_wb + 64;
+      }
+    }
+    while (from < rng.y) {  // later windows
+      const int wb = rng.x + ((from - rng.x) & ~63);
+      fetch_pre(wb);
+      if (!pre_pass_ok) {
+        pre_pass = __ballot(wb + lane < rng.y && pre_st.x <= qreach);
+        pre_pass_ok = true;
+      }
+      const uint64_t m = pre_pass & (~0ull << (from - wb));
+      if (m) return wb + static_cast<int>(__builtin_ctzll(m));
+      from = wb + 64;
+    }
+    return rng.y;
   };
 
-  // The first tile of the range is staged before the statistics reach LDS
-  // (a tile failing the causal extremum test is skipped by every wave's own
-  // test), so the table, query and key loads form as short a chain as
-  // possible; the tiles after it are chosen from the statistics.
+  // The first tile of the range is staged at once (a tile failing the causal
+  // extremum test is skipped by every wave's own test), so the table, query
+  // and key loads form as short a chain as possible.
   int j = rng.x < rng.y ? rng.x : rng.y;
   int pos[2];
   if (j < rng.y) {
     tile_rows(j, pos);
     stage_tile(j, 0, pos);
   }
-  if (tid < BM) Qi[tid] = qi_v;
-  if (tid < nks) Kst[tid] = kst_a;
-  if (tid + 256 < nks) Kst[tid + 256] = kst_b;
-  __syncthreads();  // Qi and the statistics
-  int jn = j < rng.y ? next_tile(j + 1) : rng.y;
+  if (tid < BM) Qi[tid] = qi_v;  // published by the barriers below
+  int jn = j < rng.y ? find_next(j + 1) : rng.y;
   tile_rows(jn, pos);  // rows of the next tile, used by the first iteration
   dma_wait();
   __syncthreads();
   int s = 0;
-  int4 ks_cur = j < rng.y ? kstat(j) : make_int4(0, 0, 0, 0);
   while (j < rng.y) {
-    const int jnn = jn < rng.y ? next_tile(jn + 1) : rng.y;
-    // small loads (statistics, and the rows of the tile after next) are
-    // issued before the DMA, so that waiting for them never waits for it
-    const int4 ks = ks_cur;
-    if (jn < rng.y) ks_cur = kstat(jn);
+    if (j - cw_wb >= 64) {  // the window of tile j, and a prefetch of the one after it
+      const int wb = rng.x + ((j - rng.x) & ~63);
+      fetch_pre(wb);
+      cw_wb = wb;
+      cw = tile_masks<HASH>(pre_st, wb + lane, rng.y, qreach, wr, p.Tk);
+      if (wb + 64 < rng.y) fetch_pre(wb + 64);
+    }
+    const int jnn = jn < rng.y ? find_next(jn + 1) : rng.y;
+    // the rows of the tile after next are loaded before the DMA, so that
+    // waiting for them never waits for it
     int pos_nn[2];
     tile_rows(jnn, pos_nn);
     __builtin_amdgcn_sched_barrier(0);
     if (jn < rng.y) stage_tile(jn, s ^ 1, pos);
 
-    if (!tile_empty_for<HASH>(ks, wr)) {
+    const int bit = j - cw_wb;
+    if (!((cw.empty >> bit) & 1)) {
       const uint8_t* Ks = smem + s * TB;
       const uint8_t* Vs = smem + (2 + s) * TB;
       // -- S^T = K Q^T ------------------------------------------------------
@@ -398,17 +427,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       // mask bias (0 or -inf), so masked scores come out of the MFMAs as
       // -inf; both branches define S afresh.
       f32x4 S[4][2];
-      if (tile_full_for<HASH>(ks, wr, j, p.Tk)) {
+      if ((cw.full >> bit) & 1) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         scores_bf16(S, Ks, Qb, r16, g);
       } else {
-        mask_bias<HASH>(S, ks, wr, Kp[s], Kb[s], qcmp, qbkt, g);
+        if (HASH && ((cw.mixed >> bit) & 1))
+          bias_tile<true>(S, Kp[s], Kb[s], qcmp, qbkt, g);
+        else
+          bias_tile<false>(S, Kp[s], Kb[s], qcmp, qbkt, g);
         scores_bf16(S, Ks, Qb, r16, g);
       }
-
       // -- online softmax, speculative reference ------------------------------
       // The weights are exponentiated against the current reference max
       // without looking at this tile's max; the row max is taken only while a

@@ -224,6 +224,27 @@ __device__ inline void mask_bias_half(f32x4 (&C)[2][2], const int4& ks, const Wa
   }
 }
 
+// Tile tests of up to 64 consecutive key tiles of a range, as wave-uniform
+// bit masks (bit i: key tile jj - lane + i), from the statistics of tile jj
+// held by each lane.
+struct TileMasks {
+  uint64_t pass;   // passes the workgroup's causal extremum test (hash ranges)
+  uint64_t empty;  // holds no pair visible to the wave's queries
+  uint64_t full;   // every pair visible to them: no mask
+  uint64_t mixed;  // keys or queries span buckets: the mask compares buckets
+};
+
+template <bool HASH>
+__device__ inline TileMasks tile_masks(const int4& st, int jj, int jend, int qreach, const WaveRows& wr, int Tk) {
+  const bool valid = jj < jend;
+  TileMasks m;
+  m.pass = __ballot(valid && (!HASH || st.x <= qreach));
+  m.empty = __ballot(valid && tile_empty_for<HASH>(st, wr));
+  m.full = __ballot(valid && tile_full_for<HASH>(st, wr, jj, Tk));
+  m.mixed = HASH ? static_cast<uint64_t>(__ballot(valid && !(st.z == st.w && wr.minb == wr.maxb))) : 0ull;
+  return m;
+}
+
 // Mask bias of a tile that is not fully visible: positions only when the
 // tile's keys and the wave's real queries share one bucket (always so in QK
 // mode and in the bucket-aligned layout), positions and buckets otherwise.
