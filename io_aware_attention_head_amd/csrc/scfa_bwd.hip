@@ -35,8 +35,10 @@
 //    lets P and dS feed the next MFMA directly as B operands.
 //  * Masks are accumulator biases (0 / -inf) built with VCC-only selects;
 //    tiles proven fully visible by the extrema skip them, and each wave
-//    skips chunks holding no pair visible to its rows. The tile statistics
-//    of a workgroup's range are staged in LDS once.
+//    skips chunks holding no pair visible to its rows. The dQ and hash dK/dV
+//    kernels take these tests for 64 tiles of their range at once and keep
+//    them as wave-uniform bit masks; the tile-pair dK/dV kernel stages the
+//    statistics of its range in LDS once.
 //  * Gradients are staged in LDS and written as whole rows at the original
 //    token positions; QK-drop zeroes the rows of dropped tokens.
 
@@ -54,10 +56,7 @@ constexpr int BN = SCFA_TILE_N;  // 64: dK/dV workgroup keys, table granularity
 constexpr int QC = 32;          // query chunk of the dK/dV loop
 constexpr int HD = 64;
 constexpr int TB = 64 * HD * 2;  // bytes of one 64 x 64 bf16 tile
-constexpr int kStatCap = 256;    // tile statistics of a range held in LDS (dK/dV)
-// ... and in the dQ kernel: 128 entries keep its LDS at 52 KB, so that three
-// workgroups fit a compute unit (VGPRs allow three waves per SIMD)
-constexpr int kStatCapQ = 128;
+constexpr int kStatCap = 256;    // tile statistics of a range held in LDS (dK/dV of tile pairs)
 
 struct BwdParams {
   const void* q;   // (B, T, H, D) bf16, original order, as are k, v, dO
@@ -275,7 +274,6 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   __shared__ __align__(16) int32_t qbkt_s[2][QC];
   __shared__ __align__(16) float lse_s[2][QC];
   __shared__ __align__(16) float del_s[2][QC];
-  __shared__ __align__(16) int4 Qst[kStatCap];
   __shared__ int32_t Ki[BN];
 
   const int tid = threadIdx.x;
@@ -288,17 +286,9 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   const size_t rowbase = static_cast<size_t>(bh) * p.TqP;  // query side
   const size_t kbase = static_cast<size_t>(bh) * p.TkP;    // key side
   const int2 rng = p.bwd_tab[static_cast<size_t>(bh) * p.nKt + kt];
-  const int4* qst = p.qstats + static_cast<size_t>(bh) * p.nQt;
-  const bool qst_lds = rng.y - rng.x <= kStatCap;
-  // statistics of the range and the tile's key entries: loaded here, stored
-  // to LDS at the first barrier (after the first chunk's DMA), so the key and
-  // query loads do not wait
-  static_assert(kStatCap <= 256, "statistics copy: one entry per thread");
-  const int nqs = qst_lds ? rng.y - rng.x : 0;
-  int4 qst_a = make_int4(0, 0, 0, 0);
-  if (tid < nqs) qst_a = qst[rng.x + tid];
-  const int ki_v = tid < BN ? p.k_idx[kbase + kt * BN + tid] : 0;
-  auto qstat = [&](int i) { return uniform4(stat_entry(qst_lds, Qst, i - rng.x, qst, i)); };
+  // tests of the range's query tiles, 64 tiles per window
+  TileWalk<true> walk(p.qstats + static_cast<size_t>(bh) * p.nQt, rng.x, rng.y, lane);
+  const int ki_v = tid < BN ? p.k_idx[kbase + kt * BN + tid] : 0;  // the tile's key entries
 
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;  // bytes between token rows
   const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;     // token 0 of this head in q, dO
@@ -359,51 +349,61 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
     dma16(dg, off + tch, base + 3 * CB);
     if (lane < QC) dma4(static_cast<const uint8_t*>(small_src) + ci * QC * 4, lane * 4, lds_small + s * QC * 4);
   };
-  // chunk ci = CPT * query tile + part; skip tiles failing the causal test
+  // chunk ci = CPT * query tile + part; tiles failing the causal test are
+  // skipped
   const int4 ks = p.kstats[static_cast<size_t>(bh) * p.nKt + kt];
   const int kreach = k_reach(p.rc, ks.x);  // smallest query position that sees a key of the tile
   const int cend = CPT * rng.y;
-  auto next_chunk = [&](int ci) {
-    while (ci < cend && qstat(ci / CPT).y < kreach) ci = (ci / CPT + 1) * CPT;
-    return ci;
+  // query tile ii (statistics qs) against this wave's keys
+  auto tests = [&](const int4& qs, int ii) {
+    const bool valid = ii < rng.y;
+    bool full = wk.all && wk.maxpos <= qs.x && (ii + 1) * BM <= p.Tq;
+    if (HASH) full = full && qs.z == qs.w && wk.minb == wk.maxb && wk.minb == qs.z;
+    TileMasks m;
+    m.pass = __ballot(valid && qs.y >= kreach);
+    m.empty = __ballot(valid && (!wk.any || wk.minpos > qs.y || (HASH && (wk.minb > qs.w || wk.maxb < qs.z))));
+    m.full = __ballot(valid && full);
+    m.mixed = HASH ? static_cast<uint64_t>(__ballot(valid && !(qs.z == qs.w && wk.minb == wk.maxb))) : 0ull;
+    return m;
+  };
+  walk.first(tests);
+  // first chunk at or after c whose query tile passes the causal test
+  auto next_chunk = [&](int c) {
+    if (c >= cend) return cend;
+    const int t = c / CPT, t2 = walk.next(t, tests);
+    return t2 == t ? c : (t2 < rng.y ? CPT * t2 : cend);
   };
 
-  // The first chunk of the range is staged before the statistics reach LDS
-  // (a chunk failing the causal extremum test is skipped by every wave's own
-  // test); the chunks after it are chosen from the statistics.
+  // The first chunk of the range is staged at once (a chunk failing the
+  // causal extremum test is skipped by every wave's own test).
   int ci = CPT * rng.x < cend ? CPT * rng.x : cend;
   int pos[2];
   if (ci < cend) {
     chunk_rows(ci, pos);
     stage(ci, 0, pos);
   }
-  if (tid < nqs) Qst[tid] = qst_a;
-  if (tid < BN) Ki[tid] = ki_v;
-  __syncthreads();  // the statistics and the key entries
+  if (tid < BN) Ki[tid] = ki_v;  // published by the barriers below
   int cn = ci < cend ? next_chunk(ci + 1) : cend;
   chunk_rows(cn, pos);
   dma_wait();
   __syncthreads();
   int s = 0;
-  int4 qs_cur = ci < cend ? qstat(ci / CPT) : make_int4(0, 0, 0, 0);
   while (ci < cend) {
+    walk.enter(ci / CPT, tests);
     const int cnn = cn < cend ? next_chunk(cn + 1) : cend;
-    const int4 qs = qs_cur;
-    if (cn < cend) qs_cur = qstat(cn / CPT);
     int pos_nn[2];
     chunk_rows(cnn, pos_nn);  // issued before the DMA: waiting for it never waits for the DMA
     __builtin_amdgcn_sched_barrier(0);
     if (cn < cend) stage(cn, s ^ 1, pos);
 
     // this wave's keys against the chunk's query tile: skip / no mask
-    const bool empty = !wk.any || wk.minpos > qs.y || (HASH && (wk.minb > qs.w || wk.maxb < qs.z));
-    if (!empty) {
+    const int qt = ci / CPT;
+    if (!walk.has(walk.cw.empty, qt)) {
       const uint8_t* Qr = smem + s * 4 * CB;
       const uint8_t* Qt = Qr + CB;
       const uint8_t* Dr = Qr + 2 * CB;
       const uint8_t* Dt = Qr + 3 * CB;
-      bool full = wk.all && wk.maxpos <= qs.x && (ci / CPT + 1) * BM <= p.Tq;
-      if (HASH) full = full && qs.z == qs.w && wk.minb == wk.maxb && wk.minb == qs.z;
+      const bool full = walk.has(walk.cw.full, qt);
       // S = Q K^T (from the mask bias) and dP = dO V^T: rows = queries,
       // column = this lane's key; element e of block qb is query
       // 8 g + 4 qb + e of the chunk
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) S[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
       } else {
-        const bool buckets = HASH && !(qs.z == qs.w && wk.minb == wk.maxb);
+        const bool buckets = HASH && walk.has(walk.cw.mixed, qt);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           const int qo = 8 * g + 4 * qb;
@@ -800,7 +800,6 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   __shared__ __align__(16) uint8_t smem[2 * 3 * TB];  // 2 stages x (K rows, K tr, V rows); epilogue staging
   __shared__ __align__(16) int32_t Kp[2][BN];
   __shared__ __align__(16) int32_t Kb[2][BN];
-  __shared__ __align__(16) int4 Kst[kStatCapQ];
   static_assert(2 * 3 * TB >= BM * HD * 4, "dQ staging does not fit");
 
   const int tid = threadIdx.x;
@@ -815,15 +814,8 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   const int2 rng = p.fwd_tab[static_cast<size_t>(bh) * p.nQt + qt];
   const int4 qs = p.qstats[static_cast<size_t>(bh) * p.nQt + qt];
   const int qreach = q_reach(p.rc, qs.y);  // largest key position a query of the tile may see
-  const int4* kst = p.kstats + static_cast<size_t>(bh) * p.nKt;
-  const bool kst_lds = rng.y - rng.x <= kStatCapQ;
-  // statistics of the range: loaded here, stored to LDS at the first barrier
-  // (after the first tile's DMA), so the query and key loads do not wait
-  static_assert(kStatCapQ <= 256, "statistics copy: one entry per thread");
-  const int nks = kst_lds ? rng.y - rng.x : 0;
-  int4 kst_a = make_int4(0, 0, 0, 0);
-  if (tid < nks) kst_a = kst[rng.x + tid];
-  auto kstat = [&](int j) { return uniform4(stat_entry(kst_lds, Kst, j - rng.x, kst, j)); };
+  // tile tests of the range, 64 key tiles per window
+  TileWalk<HASH> walk(p.kstats + static_cast<size_t>(bh) * p.nKt, rng.x, rng.y, lane);
 
   const uint32_t rstride = static_cast<uint32_t>(p.H) * HD * 2;
   const size_t head0 = (static_cast<size_t>(b) * p.T * p.H + h) * HD * 2;     // token 0 of this head in q, dO
@@ -885,43 +877,36 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
     if (ws == 0) dma4(kig + j * BN, lane * 4, ldsp + s * BN * 4);
     else if (HASH && ws == 1) dma4(kbg + j * BN, lane * 4, ldsb + s * BN * 4);
   };
-  auto next_tile = [&](int j) {
-    if (HASH)
-      while (j < rng.y && kstat(j).x > qreach) ++j;
-    return j;
-  };
+  auto tests = [&](const int4& st, int jj) { return key_tile_masks<HASH>(st, jj, rng.y, qreach, wr, p.Tk); };
+  walk.first(tests);
 
-  // The first tile of the range is staged before the statistics reach LDS
-  // (a tile failing the causal extremum test is skipped by every wave's own
-  // test); the tiles after it are chosen from the statistics.
+  // The first tile of the range is staged at once (a tile failing the causal
+  // extremum test is skipped by every wave's own test).
   int j = rng.x < rng.y ? rng.x : rng.y;
   int pos[2];
   if (j < rng.y) {
     tile_rows(j, pos);
     stage(j, 0, pos);
   }
-  if (tid < nks) Kst[tid] = kst_a;
-  __syncthreads();  // the statistics
-  int jn = j < rng.y ? next_tile(j + 1) : rng.y;
+  int jn = j < rng.y ? walk.next(j + 1, tests) : rng.y;
   tile_rows(jn, pos);
   dma_wait();
   __syncthreads();
   int s = 0;
-  int4 ks_cur = j < rng.y ? kstat(j) : make_int4(0, 0, 0, 0);
   while (j < rng.y) {
-    const int jnn = jn < rng.y ? next_tile(jn + 1) : rng.y;
-    const int4 ks = ks_cur;
-    if (jn < rng.y) ks_cur = kstat(jn);
+    walk.enter(j, tests);
+    const int jnn = jn < rng.y ? walk.next(jn + 1, tests) : rng.y;
     int pos_nn[2];
     tile_rows(jnn, pos_nn);
     __builtin_amdgcn_sched_barrier(0);
     if (jn < rng.y) stage(jn, s ^ 1, pos);
 
-    if (!tile_empty_for<HASH>(ks, wr)) {
+    if (!walk.has(walk.cw.empty, j)) {
       const uint8_t* Kr = smem + s * 3 * TB;
       const uint8_t* Kt = Kr + TB;
       const uint8_t* Vr = Kr + 2 * TB;
-      const bool full = tile_full_for<HASH>(ks, wr, j, p.Tk);
+      const bool full = walk.has(walk.cw.full, j);
+      const bool buckets = HASH && walk.has(walk.cw.mixed, j);
       // Two halves of 32 keys (blocks 2 kc, 2 kc + 1), so that only half of
       // the score tiles is live at a time. S^T = K Q^T (from the mask bias)
       // and dP^T = V dO^T: rows = keys, column = this lane's query.
@@ -934,7 +919,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) S[h2][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         } else {
-          mask_bias_half<HASH>(S, ks, wr, Kp[s], Kb[s], qcmp, qbkt, g, kc);
+          mask_bias_half(S, buckets, Kp[s], Kb[s], qcmp, qbkt, g, kc);
         }
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)

@@ -282,21 +282,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     qpos[qb] = p.q_idx[rowbase + row];
     qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
   }
-  // Tile tests in windows of 64 key tiles of the range (window k: tiles
-  // rng.x + 64 k ...), as wave-uniform bit masks; lane i loads the statistics
-  // of tile i of a window. cw_* is the window of the current tile; pre_* holds
-  // the statistics of one more window (the next one, prefetched, or the one a
-  // search for the next tile reached).
-  auto load_stats = [&](int wb) -> int4 {
-    int4 v = make_int4(0, 0, 0, 0);
-    if (wb + lane < rng.y) v = kst[wb + lane];
-    return v;
-  };
-  const int4 st0 = load_stats(rng.x);
-  int pre_wb = rng.y - rng.x > 64 ? rng.x + 64 : -1;
-  int4 pre_st = pre_wb >= 0 ? load_stats(pre_wb) : make_int4(0, 0, 0, 0);
-  bool pre_pass_ok = false;
-  uint64_t pre_pass = 0;
+  TileWalk<HASH> walk(kst, rng.x, rng.y, lane);  // tile tests of the range, 64 tiles per window
   const WaveRows wr = wave_rows(qpos, qbkt, p.rc);
   // positions the masks compare keys against: the largest visible key position
   const int qcmp[2] = {q_reach(p.rc, qpos[0]), q_reach(p.rc, qpos[1])};
@@ -351,41 +337,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     else if (HASH && ws == 1) dma4(kbg + j * BN, lane * 4, ldsb + s * BN * 4);
   };
 
-  int cw_wb = rng.x;
-  TileMasks cw = tile_masks<HASH>(st0, rng.x + lane, rng.y, qreach, wr, p.Tk);
-  auto fetch_pre = [&](int wb) {
-    if (pre_wb != wb) {
-      pre_wb = wb;
-      pre_st = load_stats(wb);
-      pre_pass_ok = false;
-    }
-  };
-  // first tile from `from` on that passes the workgroup's causal extremum
-  // test (every tile of a QK range passes it), or rng.y
-  auto find_next = [&](int from) -> int {
-    if (!HASH) return min(from, rng.y);
-    if (from >= rng.y) return rng.y;
-    {  // the current window (from >= cw_wb: tiles are visited in order)
-      const int o = from - cw_wb;
-      if (o < 64) {
-        const uint64_t m = cw.pass & (~0ull << o);
-        if (m) return cw_wb + static_cast<int>(__builtin_ctzll(m));
-        from = cw_wb + 64;
-      }
-    }
-    while (from < rng.y) {  // later windows
-      const int wb = rng.x + ((from - rng.x) & ~63);
-      fetch_pre(wb);
-      if (!pre_pass_ok) {
-        pre_pass = __ballot(wb + lane < rng.y && pre_st.x <= qreach);
-        pre_pass_ok = true;
-      }
-      const uint64_t m = pre_pass & (~0ull << (from - wb));
-      if (m) return wb + static_cast<int>(__builtin_ctzll(m));
-      from = wb + 64;
-    }
-    return rng.y;
-  };
+  auto tests = [&](const int4& st, int jj) { return key_tile_masks<HASH>(st, jj, rng.y, qreach, wr, p.Tk); };
+  walk.first(tests);
 
   // The first tile of the range is staged at once (a tile failing the causal
   // extremum test is skipped by every wave's own test), so the table, query
@@ -397,20 +350,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     stage_tile(j, 0, pos);
   }
   if (tid < BM) Qi[tid] = qi_v;  // published by the barriers below
-  int jn = j < rng.y ? find_next(j + 1) : rng.y;
+  int jn = j < rng.y ? walk.next(j + 1, tests) : rng.y;
   tile_rows(jn, pos);  // rows of the next tile, used by the first iteration
   dma_wait();
   __syncthreads();
   int s = 0;
   while (j < rng.y) {
-    if (j - cw_wb >= 64) {  // the window of tile j, and a prefetch of the one after it
-      const int wb = rng.x + ((j - rng.x) & ~63);
-      fetch_pre(wb);
-      cw_wb = wb;
-      cw = tile_masks<HASH>(pre_st, wb + lane, rng.y, qreach, wr, p.Tk);
-      if (wb + 64 < rng.y) fetch_pre(wb + 64);
-    }
-    const int jnn = jn < rng.y ? find_next(jn + 1) : rng.y;
+    walk.enter(j, tests);
+    const int jnn = jn < rng.y ? walk.next(jn + 1, tests) : rng.y;
     // the rows of the tile after next are loaded before the DMA, so that
     // waiting for them never waits for it
     int pos_nn[2];
@@ -418,8 +365,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     __builtin_amdgcn_sched_barrier(0);
     if (jn < rng.y) stage_tile(jn, s ^ 1, pos);
 
-    const int bit = j - cw_wb;
-    if (!((cw.empty >> bit) & 1)) {
+    if (!walk.has(walk.cw.empty, j)) {
       const uint8_t* Ks = smem + s * TB;
       const uint8_t* Vs = smem + (2 + s) * TB;
       // -- S^T = K Q^T ------------------------------------------------------
@@ -427,14 +373,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       // mask bias (0 or -inf), so masked scores come out of the MFMAs as
       // -inf; both branches define S afresh.
       f32x4 S[4][2];
-      if ((cw.full >> bit) & 1) {
+      if (walk.has(walk.cw.full, j)) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) S[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         scores_bf16(S, Ks, Qb, r16, g);
       } else {
-        if (HASH && ((cw.mixed >> bit) & 1))
+        if (HASH && walk.has(walk.cw.mixed, j))
           bias_tile<true>(S, Kp[s], Kb[s], qcmp, qbkt, g);
         else
           bias_tile<false>(S, Kp[s], Kb[s], qcmp, qbkt, g);

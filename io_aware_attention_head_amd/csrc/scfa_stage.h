@@ -195,10 +195,10 @@ __device__ inline void bias_tile(f32x4 (&C)[4][2], const int32_t* kp, const int3
 
 // The same bias for the 32 keys 32 kc .. 32 kc + 31 of the tile (blocks
 // 2 kc and 2 kc + 1 as C[0], C[1]).
-template <bool HASH>
-__device__ inline void mask_bias_half(f32x4 (&C)[2][2], const int4& ks, const WaveRows& wr, const int32_t* kp,
-                                      const int32_t* kbk, const int (&qpos)[2], const int (&qbkt)[2], int g, int kc) {
-  const bool buckets = HASH && !(ks.z == ks.w && wr.minb == wr.maxb);
+// buckets: also compare buckets (the tile's keys or the wave's queries span
+// more than one bucket).
+__device__ inline void mask_bias_half(f32x4 (&C)[2][2], bool buckets, const int32_t* kp, const int32_t* kbk,
+                                      const int (&qpos)[2], const int (&qbkt)[2], int g, int kc) {
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
     const int kbase = 32 * kc + 8 * g + 4 * h2;
@@ -224,18 +224,96 @@ __device__ inline void mask_bias_half(f32x4 (&C)[2][2], const int4& ks, const Wa
   }
 }
 
-// Tile tests of up to 64 consecutive key tiles of a range, as wave-uniform
-// bit masks (bit i: key tile jj - lane + i), from the statistics of tile jj
-// held by each lane.
+// Tests of up to 64 consecutive tiles of a range, as wave-uniform bit masks
+// (bit i: tile i of the window).
 struct TileMasks {
   uint64_t pass;   // passes the workgroup's causal extremum test (hash ranges)
-  uint64_t empty;  // holds no pair visible to the wave's queries
+  uint64_t empty;  // holds no pair visible to the wave's rows
   uint64_t full;   // every pair visible to them: no mask
-  uint64_t mixed;  // keys or queries span buckets: the mask compares buckets
+  uint64_t mixed;  // tile or wave rows span buckets: the mask compares buckets
 };
 
+// Walk over a range [beg, end) of tiles whose tests are kept as bit masks, 64
+// tiles per window (window k: tiles beg + 64 k, ...). Lane i loads the
+// statistics of tile i of a window, and `tests(stats, tile)` turns them into
+// the window's masks (ballots; tiles at or past `end` must test false). `cw`
+// holds the masks of the window of the current tile; `pre` the statistics of
+// one more window: the next one, prefetched, or the one that a search for the
+// next passing tile reached. SKIP: tiles failing `pass` are not visited.
+template <bool SKIP>
+struct TileWalk {
+  const int4* stats;
+  int beg, end, lane;
+  int cw_wb, pre_wb;
+  int4 st0, pre_st;
+  bool pre_ok;
+  TileMasks cw, pre;
+
+  // Issues the loads of the first window (and of the second one).
+  __device__ TileWalk(const int4* st, int b, int e, int l)
+      : stats(st), beg(b), end(e), lane(l), cw_wb(b), pre_ok(false) {
+    st0 = load(beg);
+    pre_wb = end - beg > 64 ? beg + 64 : -1;
+    pre_st = pre_wb >= 0 ? load(pre_wb) : make_int4(0, 0, 0, 0);
+  }
+  __device__ int4 load(int wb) const {
+    int4 v = make_int4(0, 0, 0, 0);
+    if (wb + lane < end) v = stats[wb + lane];
+    return v;
+  }
+  // Masks of the first window (waits for its statistics).
+  template <class Tests>
+  __device__ void first(Tests&& tests) {
+    cw = tests(st0, beg + lane);
+  }
+  __device__ void fetch(int wb) {
+    if (pre_wb != wb) {
+      pre_wb = wb;
+      pre_st = load(wb);
+      pre_ok = false;
+    }
+  }
+  // First tile at or after `from` (>= the current tile) to visit, or end.
+  template <class Tests>
+  __device__ int next(int from, Tests&& tests) {
+    if (!SKIP) return min(from, end);
+    if (from >= end) return end;
+    const int o = from - cw_wb;
+    if (o < 64) {
+      const uint64_t m = cw.pass & (~0ull << o);
+      if (m) return cw_wb + static_cast<int>(__builtin_ctzll(m));
+      from = cw_wb + 64;
+    }
+    while (from < end) {  // later windows
+      const int wb = beg + ((from - beg) & ~63);
+      fetch(wb);
+      if (!pre_ok) {
+        pre = tests(pre_st, wb + lane);
+        pre_ok = true;
+      }
+      const uint64_t m = pre.pass & (~0ull << (from - wb));
+      if (m) return wb + static_cast<int>(__builtin_ctzll(m));
+      from = wb + 64;
+    }
+    return end;
+  }
+  // Makes the window of tile j current (and prefetches the one after it).
+  template <class Tests>
+  __device__ void enter(int j, Tests&& tests) {
+    if (j - cw_wb < 64) return;
+    const int wb = beg + ((j - beg) & ~63);
+    fetch(wb);
+    cw = pre_ok ? pre : tests(pre_st, wb + lane);
+    cw_wb = wb;
+    if (wb + 64 < end) fetch(wb + 64);
+  }
+  __device__ bool has(uint64_t m, int j) const { return (m >> (j - cw_wb)) & 1; }
+};
+
+// Tests of key tiles (statistics st of tile jj, range end jend) against a
+// wave's query rows.
 template <bool HASH>
-__device__ inline TileMasks tile_masks(const int4& st, int jj, int jend, int qreach, const WaveRows& wr, int Tk) {
+__device__ inline TileMasks key_tile_masks(const int4& st, int jj, int jend, int qreach, const WaveRows& wr, int Tk) {
   const bool valid = jj < jend;
   TileMasks m;
   m.pass = __ballot(valid && (!HASH || st.x <= qreach));
