@@ -466,7 +466,8 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
  *                visible pair).
  *  workspace     device scratch of scfa_bwd_workspace_bytes() bytes (Delta
  *                and log2 LSE per sorted query row).
- * Launches 3 kernels on `stream`; no atomics, results are deterministic.  */
+ * Launches 2 kernels on `stream` (dQ, which also fills the workspace,
+ * then dK/dV); no atomics, results are deterministic.                      */
 size_t scfa_bwd_workspace_bytes(int mode, int B, int H, int Tq, int Tk, int D);
 
 int scfa_bwd(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,

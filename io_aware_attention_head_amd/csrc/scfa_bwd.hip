@@ -14,9 +14,10 @@
 // NaN-safe softmax carried to the backward).
 //
 // MI355X design:
-//  * Three kernels, no atomics (deterministic): a preparation kernel (Delta
-//    and log2 LSE per sorted query row), dK/dV, dQ per 128-query tile
-//    (4 waves x 32 queries, key tiles of 64). dK/dV runs per pair of 64-key
+//  * Two kernels, no atomics (deterministic): dQ per 128-query tile (4 waves
+//    x 32 queries, key tiles of 64), which also computes Delta and log2 LSE
+//    of its rows from O, dO and the LSE and leaves them in the workspace,
+//    then dK/dV, which reads them. dK/dV runs per pair of 64-key
 //    tiles (4 waves x 32 keys, query chunks of 32: 38 KB of LDS, 3 waves per
 //    SIMD; each Q / dO operand read from LDS serves two 16-key blocks) for
 //    the long ranges of QK and dense attention, and per 64-key tile (4 waves
@@ -63,8 +64,10 @@ struct BwdParams {
   const void* k;
   const void* v;
   const void* dO;
-  const float* lse2;   // (BH, TqP) sorted query rows: log2 LSE, +inf when no visible key / pad row
-  const float* delta;  // (BH, TqP)
+  const float* O;      // (B, T, H, D) forward output, original order
+  const float* lse;    // (B*H, T) forward natural-log LSE, original order
+  float* lse2;         // (BH, TqP) sorted query rows: log2 LSE, +inf when no visible key / pad row (written by dQ)
+  float* delta;        // (BH, TqP) Delta = dO . O per sorted query row (written by dQ)
   const int32_t* q_idx;
   const int32_t* k_idx;
   const int32_t* q_bkt;
@@ -87,43 +90,6 @@ struct BwdParams {
   float scale;  // score scale
   Reach rc;     // position test (causal, strict or non-causal)
 };
-
-// ---------------------------------------------------------------------------
-// Preparation: Delta = dO . O and log2 LSE per sorted query row.
-// 8 threads per row (8 dims each), 32 rows per workgroup.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_bwd_prep(const uint16_t* __restrict__ dO, const float* __restrict__ O,
-                                                  const float* __restrict__ lse, const int32_t* __restrict__ q_idx,
-                                                  int H, int T, int Tp, float* __restrict__ lse2,
-                                                  float* __restrict__ delta) {
-  const int bh = blockIdx.y;
-  const int b = bh / H, h = bh - b * H;
-  const int r = blockIdx.x * 32 + (threadIdx.x >> 3);
-  const int part = threadIdx.x & 7;
-  const int qp = q_idx[static_cast<size_t>(bh) * Tp + r];
-  const bool valid = qp >= 0 && qp < T;
-  float s = 0.f;
-  if (valid) {
-    const size_t row = (static_cast<size_t>(b) * T + qp) * H + h;
-    const u32x4 dv = *reinterpret_cast<const u32x4*>(dO + row * HD + part * 8);
-    const f32x4 o0 = *reinterpret_cast<const f32x4*>(O + row * HD + part * 8);
-    const f32x4 o1 = *reinterpret_cast<const f32x4*>(O + row * HD + part * 8 + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = __uint_as_float(dv[i] << 16), hi = __uint_as_float(dv[i] & 0xffff0000u);
-      s += lo * (i < 2 ? o0[2 * i] : o1[2 * i - 4]) + hi * (i < 2 ? o0[2 * i + 1] : o1[2 * i - 3]);
-    }
-  }
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 4);
-  if (part == 0) {
-    const size_t o = static_cast<size_t>(bh) * Tp + r;
-    delta[o] = valid ? s : 0.f;
-    const float l = valid ? lse[static_cast<size_t>(bh) * T + qp] : -INFINITY;
-    lse2[o] = (l == -INFINITY) ? INFINITY : l * kLog2e;
-  }
-}
 
 // Zero the gradient rows of the tokens a tile owns but does not hold
 // (QK-drop: dropped tokens). Tile `tile` of `rows` rows of the index array
@@ -829,13 +795,42 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
     const int row = q0 + qb * 16 + r16;
     qpos[qb] = p.q_idx[rowbase + row];
     qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
-    ql2[qb] = p.lse2[rowbase + row];
-    qdl[qb] = p.delta[rowbase + row];
     const size_t off = head0 + static_cast<size_t>(src_row(qpos[qb], p.T)) * rstride;
 #pragma unroll
     for (int ds = 0; ds < 2; ++ds) {
       Qb[qb][ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.q) + off + (ds * 32 + g * 8) * 2);
       Db[qb][ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.dO) + off + (ds * 32 + g * 8) * 2);
+    }
+  }
+  // Delta = dO . O and log2 LSE of this wave's rows (the four lane groups
+  // hold 16 dims each of a row), written to the workspace for dK/dV, which
+  // runs after this kernel. Rows without a visible key (LSE = -inf) and pad
+  // rows get log2 LSE = +inf, so exp2(s - lse2) = 0 there.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qp = qpos[qb];
+    const bool valid = qp >= 0 && qp < p.T;
+    const float* orow = p.O + ((static_cast<size_t>(b) * p.T + src_row(qp, p.T)) * p.H + h) * HD;
+    float dot = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 2; ++ds) {
+      const f32x4 o0 = *reinterpret_cast<const f32x4*>(orow + ds * 32 + g * 8);
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(orow + ds * 32 + g * 8 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot = fmaf(static_cast<float>(Db[qb][ds][e]), o0[e], dot);
+        dot = fmaf(static_cast<float>(Db[qb][ds][4 + e]), o1[e], dot);
+      }
+    }
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    const float l = valid ? p.lse[static_cast<size_t>(bh) * p.T + qp] : -INFINITY;
+    qdl[qb] = valid ? dot : 0.f;
+    ql2[qb] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    if (g == 0) {
+      const size_t r = rowbase + q0 + qb * 16 + r16;
+      p.lse2[r] = ql2[qb];
+      p.delta[r] = qdl[qb];
     }
   }
   const WaveRows wr = wave_rows(qpos, qbkt, p.rc);
@@ -992,14 +987,16 @@ size_t ws_layout(int B, int H, int TqP, size_t off[3]) {
 
 template <bool HASH, bool ZD>
 int launch_bwd(const BwdParams& p, hipStream_t stream) {
+  // dQ first: it also writes Delta and log2 LSE of every sorted query row,
+  // which dK/dV reads
+  hipLaunchKernelGGL((k_bwd_dq<HASH, ZD>), dim3(p.nQt * p.B * p.H), dim3(256), 0, stream, p);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
   // hash ranges are short (one bucket's query tiles): more, smaller
   // workgroups keep the CUs busier than sharing each chunk between two tiles
   if constexpr (HASH)
     hipLaunchKernelGGL((k_bwd_dkdv64<HASH, ZD>), dim3(p.nKt * p.B * p.H), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((k_bwd_dkdv<HASH, ZD>), dim3((p.nKt + 1) / 2 * p.B * p.H), dim3(256), 0, stream, p);
-  SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL((k_bwd_dq<HASH, ZD>), dim3(p.nQt * p.B * p.H), dim3(256), 0, stream, p);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }
@@ -1074,6 +1071,8 @@ int bwd_run(int mode, int dtype_in, const void* q, const void* k, const void* v,
   p.k = k;
   p.v = v;
   p.dO = dO;
+  p.O = O;
+  p.lse = lse;
   p.lse2 = reinterpret_cast<float*>(ws + off[0]);
   p.delta = reinterpret_cast<float*>(ws + off[1]);
   p.q_idx = q_idx;
@@ -1101,9 +1100,6 @@ int bwd_run(int mode, int dtype_in, const void* q, const void* k, const void* v,
   p.nKt = TkP / BN;
   p.c = scale * kLog2e;
   p.scale = scale;
-  hipLaunchKernelGGL(k_bwd_prep, dim3(TqP / 32, B * H), dim3(256), 0, stream, static_cast<const uint16_t*>(dO), O, lse,
-                     q_idx, H, T, TqP, const_cast<float*>(p.lse2), const_cast<float*>(p.delta));
-  SCFA_RETURN_IF_LAUNCH_FAILED();
   if (mode == SCFA_HASH) return launch_bwd<true, false>(p, stream);
   return launch_bwd<false, true>(p, stream);
 }

@@ -236,25 +236,23 @@ struct TileMasks {
 // Walk over a range [beg, end) of tiles whose tests are kept as bit masks, 64
 // tiles per window (window k: tiles beg + 64 k, ...). Lane i loads the
 // statistics of tile i of a window, and `tests(stats, tile)` turns them into
-// the window's masks (ballots; tiles at or past `end` must test false). `cw`
-// holds the masks of the window of the current tile; `pre` the statistics of
-// one more window: the next one, prefetched, or the one that a search for the
-// next passing tile reached. SKIP: tiles failing `pass` are not visited.
+// the window's masks (ballots; tiles at or past `end` must test false); `cw`
+// holds the masks of the window of the current tile.
+// SKIP: tiles failing `pass` are not visited, and a window is loaded when the
+// walk reaches it (hash ranges are short). Otherwise every tile is visited
+// and the statistics of the window after the current one are prefetched.
 template <bool SKIP>
 struct TileWalk {
   const int4* stats;
   int beg, end, lane;
-  int cw_wb, pre_wb;
-  int4 st0, pre_st;
-  bool pre_ok;
-  TileMasks cw, pre;
+  int cw_wb;
+  int4 st0, nx_st;
+  TileMasks cw;
 
   // Issues the loads of the first window (and of the second one).
-  __device__ TileWalk(const int4* st, int b, int e, int l)
-      : stats(st), beg(b), end(e), lane(l), cw_wb(b), pre_ok(false) {
+  __device__ TileWalk(const int4* st, int b, int e, int l) : stats(st), beg(b), end(e), lane(l), cw_wb(b) {
     st0 = load(beg);
-    pre_wb = end - beg > 64 ? beg + 64 : -1;
-    pre_st = pre_wb >= 0 ? load(pre_wb) : make_int4(0, 0, 0, 0);
+    if (!SKIP) nx_st = end - beg > 64 ? load(beg + 64) : make_int4(0, 0, 0, 0);
   }
   __device__ int4 load(int wb) const {
     int4 v = make_int4(0, 0, 0, 0);
@@ -265,13 +263,6 @@ struct TileWalk {
   template <class Tests>
   __device__ void first(Tests&& tests) {
     cw = tests(st0, beg + lane);
-  }
-  __device__ void fetch(int wb) {
-    if (pre_wb != wb) {
-      pre_wb = wb;
-      pre_st = load(wb);
-      pre_ok = false;
-    }
   }
   // First tile at or after `from` (>= the current tile) to visit, or end.
   template <class Tests>
@@ -286,26 +277,24 @@ struct TileWalk {
     }
     while (from < end) {  // later windows
       const int wb = beg + ((from - beg) & ~63);
-      fetch(wb);
-      if (!pre_ok) {
-        pre = tests(pre_st, wb + lane);
-        pre_ok = true;
-      }
-      const uint64_t m = pre.pass & (~0ull << (from - wb));
+      const uint64_t m = tests(load(wb), wb + lane).pass & (~0ull << (from - wb));
       if (m) return wb + static_cast<int>(__builtin_ctzll(m));
       from = wb + 64;
     }
     return end;
   }
-  // Makes the window of tile j current (and prefetches the one after it).
+  // Makes the window of tile j current.
   template <class Tests>
   __device__ void enter(int j, Tests&& tests) {
     if (j - cw_wb < 64) return;
     const int wb = beg + ((j - beg) & ~63);
-    fetch(wb);
-    cw = pre_ok ? pre : tests(pre_st, wb + lane);
+    if (SKIP) {
+      cw = tests(load(wb), wb + lane);
+    } else {  // tiles are visited in turn: wb is the window after cw
+      cw = tests(nx_st, wb + lane);
+      if (wb + 64 < end) nx_st = load(wb + 64);
+    }
     cw_wb = wb;
-    if (wb + 64 < end) fetch(wb + 64);
   }
   __device__ bool has(uint64_t m, int j) const { return (m >> (j - cw_wb)) & 1; }
 };
