@@ -239,7 +239,7 @@ def _grad_identities(plan, dO):
 def _train_one(name, K):
     """Forward + backward of one training workload and of its dense-causal
     twin (same kernels, positions 0..T-1): the recomputation backward
-    (backward table, Delta, dK/dV and dQ kernels) timed after a forward with
+    (backward table, dQ (with Delta) and dK/dV kernels. timed after a forward with
     HIP events, the forward kernel timed on its own."""
     import torch
     import io_aware_attention_head_amd.scfa as scfa
@@ -527,7 +527,7 @@ def _sweep(K):
 
 def _bwd_only(K):
     """The backward of the hash training workload in a timed loop (for
-    counter collection): backward table, Delta, dK/dV and dQ kernels."""
+    counter collection): backward table, dQ (with Delta) and dK/dV kernels."""
     import torch
     import io_aware_attention_head_amd.scfa as scfa
     from io_aware_attention_head_amd.inputs import WORKLOADS, make_inputs
