@@ -26,9 +26,10 @@
 //    index arrays (gather fused into the loads, as in the forward): each
 //    lane's own rows straight into registers, the shared tiles by
 //    global-to-LDS DMA, double buffered. A tile needed both as row operand
-//    and transposed (Q and dO for dK/dV, K for dQ) is staged twice, once in
-//    the row layout and once in the layout of the transposed reads
-//    (ds_read_b64_tr_b16); no transposed copy exists in memory.
+//    and transposed (Q and dO for dK/dV, K for dQ) is staged once, in the
+//    layout of the row reads, which the transposed reads
+//    (ds_read_b64_tr_b16) also read at full speed; no transposed copy exists
+//    in memory.
 //  * All six products are v_mfma_f32_16x16x32_bf16. The score-like tiles
 //    (S, dP) are laid out so that each lane owns one column (a key in dK/dV,
 //    a query in dQ) and 4 rows per 16x16 block; their A-operand rows are
@@ -216,26 +217,17 @@ __device__ inline WaveKeys wave_keys(int kpos, int kbkt, int T, const Reach& rc)
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per 64-key tile; wave w owns keys 16w .. 16w+15
-// (its K and V rows in registers, one key per lane column). Query chunks of
-// 32 rows are staged by DMA: Q and dO each in the row layout (A operands of
-// S = Q K^T and dP = dO V^T) and in the transposed-read layout (A operands of
-// dK^T += Q^T dS and dV^T += dO^T P), with their positions, buckets, log2
-// LSE and Delta.
-// ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
 // dK, dV for short query ranges (the hash layout's): one workgroup per 64-key
-// tile; wave w owns keys 16w .. 16w+15
-// (its K and V rows in registers, one key per lane column). Query chunks of
-// 32 rows are staged by DMA: Q and dO each in the row layout (A operands of
-// S = Q K^T and dP = dO V^T) and in the transposed-read layout (A operands of
-// dK^T += Q^T dS and dV^T += dO^T P), with their positions, buckets, log2
-// LSE and Delta.
+// tile; wave w owns keys 16w .. 16w+15 (its K and V rows in registers, one
+// key per lane column). Query chunks of 32 rows are staged by DMA: Q and dO
+// once each, read as rows (A operands of S = Q K^T and dP = dO V^T) and
+// transposed (A operands of dK^T += Q^T dS and dV^T += dO^T P), with their
+// positions, buckets, log2 LSE and Delta.
 // ---------------------------------------------------------------------------
 template <bool HASH, bool ZD>
 __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   constexpr int CB = QC * 128;  // bytes of one staged chunk copy (QC rows)
-  __shared__ __align__(16) uint8_t smem[2 * BN * HD * 4];  // 2 stages x 4 chunk copies; epilogue staging (32 KB)
+  __shared__ __align__(16) uint8_t smem[2 * BN * HD * 4];  // 2 stages x (Q, dO) chunks; epilogue staging (32 KB)
   __shared__ __align__(16) int32_t qpos_s[2][QC];
   __shared__ __align__(16) int32_t qbkt_s[2][QC];
   __shared__ __align__(16) float lse_s[2][QC];
@@ -285,11 +277,10 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
   // ---- DMA staging of a query chunk: wave w stages rows 8w .. 8w+7 --------
   const uint8_t* qg = static_cast<const uint8_t*>(p.q) + head0;
   const uint8_t* dg = static_cast<const uint8_t*>(p.dO) + head0;
-  uint32_t rch, tch;
+  uint32_t rch;  // swz_k layout: serves the row and the transposed reads
   {
     const int row = 8 * w + (lane >> 3), cp = lane & 7;
-    rch = (cp ^ swz_k(row)) * 16;  // row layout
-    tch = swz_v(row, cp) * 16;     // transposed-read layout
+    rch = (cp ^ swz_k(row)) * 16;
   }
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t lds_small = ws == 0 ? lds_addr(&qpos_s[0][0])
@@ -307,12 +298,10 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
     pos[1] = 0;
   };
   auto stage = [&](int ci, int s, const int (&pos)[2]) {
-    const uint32_t base = lds0 + s * 4 * CB + ws * 1024;
+    const uint32_t base = lds0 + s * 2 * CB + ws * 1024;
     const uint32_t off = static_cast<uint32_t>(src_row(pos[0], p.T)) * rstride;
     dma16(qg, off + rch, base);
-    dma16(qg, off + tch, base + CB);
-    dma16(dg, off + rch, base + 2 * CB);
-    dma16(dg, off + tch, base + 3 * CB);
+    dma16(dg, off + rch, base + CB);
     if (lane < QC) dma4(static_cast<const uint8_t*>(small_src) + ci * QC * 4, lane * 4, lds_small + s * QC * 4);
   };
   // chunk ci = CPT * query tile + part; tiles failing the causal test are
@@ -365,10 +354,10 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
     // this wave's keys against the chunk's query tile: skip / no mask
     const int qt = ci / CPT;
     if (!walk.has(walk.cw.empty, qt)) {
-      const uint8_t* Qr = smem + s * 4 * CB;
-      const uint8_t* Qt = Qr + CB;
-      const uint8_t* Dr = Qr + 2 * CB;
-      const uint8_t* Dt = Qr + 3 * CB;
+      const uint8_t* Qr = smem + s * 2 * CB;
+      const uint8_t* Qt = Qr;
+      const uint8_t* Dr = Qr + CB;
+      const uint8_t* Dt = Dr;
       const bool full = walk.has(walk.cw.full, qt);
       // S = Q K^T (from the mask bias) and dP = dO V^T: rows = queries,
       // column = this lane's key; element e of block qb is query
@@ -491,16 +480,15 @@ __device__ inline WaveKeys wave_keys2(const int (&kpos)[2], const int (&kbkt)[2]
 // second), over the union of the two tiles' query ranges from the backward
 // table in chunks of 32 queries. The chunk's Q and dO operands read from LDS
 // serve both 16-key blocks of a wave. Each query chunk's 32 rows are staged
-// by DMA: Q and dO each in the row layout (A operands of S = Q K^T and
-// dP = dO V^T) and in the transposed-read layout (A operands of
-// dK^T += Q^T dS and dV^T += dO^T P), with their positions, buckets, log2
-// LSE and Delta.
+// by DMA: Q and dO once each, read as rows (A operands of S = Q K^T and
+// dP = dO V^T) and transposed (A operands of dK^T += Q^T dS and
+// dV^T += dO^T P), with their positions, buckets, log2 LSE and Delta.
 // ---------------------------------------------------------------------------
 template <bool HASH, bool ZD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_bwd_dkdv(BwdParams p) {
   constexpr int CB = QC * 128;  // bytes of one staged chunk copy (QC rows)
   constexpr int KR = 2 * BN;    // keys of a workgroup
-  __shared__ __align__(16) uint8_t smem[2 * BN * HD * 4];  // 2 stages x 4 chunk copies; epilogue staging (32 KB)
+  __shared__ __align__(16) uint8_t smem[2 * BN * HD * 4];  // 2 stages x (Q, dO) chunks; epilogue staging (32 KB)
   __shared__ __align__(16) int32_t qpos_s[2][QC];
   __shared__ __align__(16) int32_t qbkt_s[2][QC];
   __shared__ __align__(16) float lse_s[2][QC];
@@ -572,11 +560,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   // ---- DMA staging of a query chunk: wave w stages rows 8w .. 8w+7 --------
   const uint8_t* qg = static_cast<const uint8_t*>(p.q) + head0;
   const uint8_t* dg = static_cast<const uint8_t*>(p.dO) + head0;
-  uint32_t rch, tch;
+  uint32_t rch;  // swz_k layout: serves the row and the transposed reads
   {
     const int row = 8 * w + (lane >> 3), cp = lane & 7;
-    rch = (cp ^ swz_k(row)) * 16;  // row layout
-    tch = swz_v(row, cp) * 16;     // transposed-read layout
+    rch = (cp ^ swz_k(row)) * 16;
   }
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t lds_small = ws == 0 ? lds_addr(&qpos_s[0][0])
@@ -594,12 +581,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     pos[1] = 0;
   };
   auto stage = [&](int ci, int s, const int (&pos)[2]) {
-    const uint32_t base = lds0 + s * 4 * CB + ws * 1024;
+    const uint32_t base = lds0 + s * 2 * CB + ws * 1024;
     const uint32_t off = static_cast<uint32_t>(src_row(pos[0], p.T)) * rstride;
     dma16(qg, off + rch, base);
-    dma16(qg, off + tch, base + CB);
-    dma16(dg, off + rch, base + 2 * CB);
-    dma16(dg, off + tch, base + 3 * CB);
+    dma16(dg, off + rch, base + CB);
     if (lane < QC) dma4(static_cast<const uint8_t*>(small_src) + ci * QC * 4, lane * 4, lds_small + s * QC * 4);
   };
   // chunk ci = CPT * query tile + part: query tiles in either tile's range
@@ -638,10 +623,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     // this wave's keys against the chunk's query tile: skip / no mask
     const bool empty = !wk.any || wk.minpos > qs.y || (HASH && (wk.minb > qs.w || wk.maxb < qs.z));
     if (!empty) {
-      const uint8_t* Qr = smem + s * 4 * CB;
-      const uint8_t* Qt = Qr + CB;
-      const uint8_t* Dr = Qr + 2 * CB;
-      const uint8_t* Dt = Qr + 3 * CB;
+      const uint8_t* Qr = smem + s * 2 * CB;
+      const uint8_t* Qt = Qr;
+      const uint8_t* Dr = Qr + CB;
+      const uint8_t* Dt = Dr;
       bool full = wk.all && wk.maxpos <= qs.x && (ci / CPT + 1) * BM <= p.Tq;
       if (HASH) full = full && qs.z == qs.w && wk.minb == wk.maxb && wk.minb == qs.z;
       // S = Q K^T (from the mask bias) and dP = dO V^T: rows = queries,
@@ -757,16 +742,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per 128-query tile, over the forward table's key tiles;
 // wave w owns queries 32w .. 32w+31 (Q and dO rows in registers). Key tiles
-// are staged by DMA: K in the row layout (A operand of S^T = K Q^T) and in
-// the transposed-read layout (A operand of dQ^T += K^T dS^T), V in the row
-// layout (A operand of dP^T = V dO^T), with the keys' positions / buckets.
+// are staged by DMA: K once, read as rows (A operand of S^T = K Q^T) and
+// transposed (A operand of dQ^T += K^T dS^T), and V (A operand of
+// dP^T = V dO^T), with the keys' positions / buckets.
 // ---------------------------------------------------------------------------
 template <bool HASH, bool ZD>
 __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
-  __shared__ __align__(16) uint8_t smem[2 * 3 * TB];  // 2 stages x (K rows, K tr, V rows); epilogue staging
+  __shared__ __align__(16) uint8_t smem[2 * 2 * TB];  // 2 stages x (K, V); epilogue staging
   __shared__ __align__(16) int32_t Kp[2][BN];
   __shared__ __align__(16) int32_t Kb[2][BN];
-  static_assert(2 * 3 * TB >= BM * HD * 4, "dQ staging does not fit");
+  static_assert(2 * 2 * TB >= BM * HD * 4, "dQ staging does not fit");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
@@ -847,12 +832,11 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   const uint8_t* vg = static_cast<const uint8_t*>(p.v) + khead0;
   const int32_t* kig = p.k_idx + kbase;
   const int32_t* kbg = HASH ? p.k_bkt + kbase : nullptr;
-  uint32_t rch[2], tch[2];
+  uint32_t rch[2];  // swz_k layout: serves the row and the transposed reads
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 16 * w + 8 * i + (lane >> 3), cp = lane & 7;
     rch[i] = (cp ^ swz_k(row)) * 16;
-    tch[i] = swz_v(row, cp) * 16;
   }
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t ldsp = lds_addr(&Kp[0][0]), ldsb = lds_addr(&Kb[0][0]);
@@ -861,13 +845,12 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
     for (int i = 0; i < 2; ++i) pos[i] = kig[min(j, p.nKt - 1) * BN + 16 * w + 8 * i + (lane >> 3)];
   };
   auto stage = [&](int j, int s, const int (&pos)[2]) {
-    const uint32_t base = lds0 + s * 3 * TB + ws * 2048;
+    const uint32_t base = lds0 + s * 2 * TB + ws * 2048;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t off = static_cast<uint32_t>(src_row(pos[i], p.Tkv)) * rstride;
       dma16(kg, off + rch[i], base + i * 1024);
-      dma16(kg, off + tch[i], base + TB + i * 1024);
-      dma16(vg, off + rch[i], base + 2 * TB + i * 1024);
+      dma16(vg, off + rch[i], base + TB + i * 1024);
     }
     if (ws == 0) dma4(kig + j * BN, lane * 4, ldsp + s * BN * 4);
     else if (HASH && ws == 1) dma4(kbg + j * BN, lane * 4, ldsb + s * BN * 4);
@@ -897,9 +880,9 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
     if (jn < rng.y) stage(jn, s ^ 1, pos);
 
     if (!walk.has(walk.cw.empty, j)) {
-      const uint8_t* Kr = smem + s * 3 * TB;
-      const uint8_t* Kt = Kr + TB;
-      const uint8_t* Vr = Kr + 2 * TB;
+      const uint8_t* Kr = smem + s * 2 * TB;
+      const uint8_t* Kt = Kr;
+      const uint8_t* Vr = Kr + TB;
       const bool full = walk.has(walk.cw.full, j);
       const bool buckets = HASH && walk.has(walk.cw.mixed, j);
       // Two halves of 32 keys (blocks 2 kc, 2 kc + 1), so that only half of

@@ -29,9 +29,9 @@
 //    to bf16; K rows are permuted when loaded as the A operand so that each
 //    lane's 8 probabilities cover 8 CONSECUTIVE keys. The V^T operand is
 //    read from the row-major V tile with the LDS transpose read
-//    (ds_read_b64_tr_b16: 16 lanes exchange a 16 x 4 block of 16-bit values)
-//    from a layout whose 16-byte chunks are XOR-swizzled by row so that these
-//    reads are free of bank conflicts.
+//    (ds_read_b64_tr_b16: 16 lanes exchange a 16 x 4 block of 16-bit values).
+//    K and V tiles share one layout whose 16-byte chunks are XOR-swizzled by
+//    row, which keeps the K row reads free of bank conflicts.
 //  * K and V tiles are staged by global-to-LDS DMA (no registers), double
 //    buffered; the key positions of the tile after next are prefetched into
 //    registers one tile ahead, so DMA addresses never wait on a load.
@@ -311,12 +311,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const uint8_t* vg = static_cast<const uint8_t*>(p.v) + khead0;
   const int32_t* kig = p.k_idx + kbase;
   const int32_t* kbg = HASH ? p.k_bkt + kbase : nullptr;
-  uint32_t kch[2], vch[2];
+  uint32_t kch[2];  // K and V tiles share the swz_k layout
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 16 * w + 8 * i + (lane >> 3), cp = lane & 7;
     kch[i] = (cp ^ swz_k(row)) * 16;
-    vch[i] = swz_v(row, cp) * 16;  // swz_v is its own inverse
   }
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t ldsp = lds_addr(&Kp[0][0]), ldsb = lds_addr(&Kb[0][0]);
@@ -331,7 +330,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     for (int i = 0; i < 2; ++i) {
       const uint32_t off = static_cast<uint32_t>(src_row(pos[i], p.Tkv)) * rstride;
       dma16(kg, off + kch[i], ks + i * 1024);
-      dma16(vg, off + vch[i], vs + i * 1024);
+      dma16(vg, off + kch[i], vs + i * 1024);
     }
     if (ws == 0) dma4(kig + j * BN, lane * 4, ldsp + s * BN * 4);
     else if (HASH && ws == 1) dma4(kbg + j * BN, lane * 4, ldsb + s * BN * 4);

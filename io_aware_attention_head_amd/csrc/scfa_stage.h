@@ -53,23 +53,21 @@ __device__ __forceinline__ int4 stat_entry(bool in_lds, const int4* lds_copy, in
 // entry outside [0, T)) read token 0, whose values are finite.
 __device__ inline int src_row(int pos, int T) { return (pos >= 0 && pos < T) ? pos : 0; }
 
-// 16-byte chunk of row r of a staged V tile that holds chunk c: swizzled so
-// that the transposed operand reads (4 rows x 32 bytes per 16 lanes) use all
-// banks.
-__device__ inline int swz_v(int r, int c) { return c ^ (2 * (r & 3)); }
-
 // Transposed A operand (16 x 32, bf16) from a row-major 64 x 64 tile stored
-// with the swz_v layout: operand row = column 16 db + r16 of the tile, k =
-// tile rows 32 kc + 8 g .. 32 kc + 8 g + 7, as two ds_read_b64_tr_b16 of 4
-// rows each (within a 16-lane group, source lane r16 reads 4 columns of tile
-// row 32 kc + 8 g + 4 hh + r16 / 4).
+// with the swz_k layout (the layout of the row operand reads, so that one
+// staged copy of a tile serves both kinds of read): operand row = column
+// 16 db + r16 of the tile, k = tile rows 32 kc + 8 g .. 32 kc + 8 g + 7, as
+// two ds_read_b64_tr_b16 of 4 rows each (within a 16-lane group, source lane
+// r16 reads 4 columns of tile row 32 kc + 8 g + 4 hh + r16 / 4). Measured on
+// gfx950, these reads run as fast from the swz_k layout as from any other
+// XOR layout of the 16-byte chunks, while the row reads need swz_k.
 __device__ __forceinline__ bf16x8 read_tr_op(const uint8_t* tile, int db, int kc, int g, int r16) {
   v4i16 t[2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const int r = 32 * kc + 8 * g + 4 * hh + (r16 >> 2);
     const int col = 16 * db + 4 * (r16 & 3);  // first of the 4 columns
-    const uint8_t* src = tile + r * 128 + swz_v(r, col >> 3) * 16 + (col & 7) * 2;
+    const uint8_t* src = tile + r * 128 + (((col >> 3) ^ swz_k(r)) * 16) + (col & 7) * 2;
     t[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) v4i16*)(__attribute__((address_space(3))) void*)src);
   }
