@@ -226,12 +226,14 @@ __device__ inline WaveKeys wave_keys(int kpos, int kbkt, int T, const Reach& rc)
 // ---------------------------------------------------------------------------
 template <bool HASH, bool ZD>
 __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
-  constexpr int CB = QC * 128;  // bytes of one staged chunk copy (QC rows)
+  constexpr int CQ = 2 * QC;     // query rows of a staged chunk, processed in two halves of QC
+  constexpr int CB = CQ * 128;   // bytes of one staged chunk copy
   __shared__ __align__(16) uint8_t smem[2 * BN * HD * 4];  // 2 stages x (Q, dO) chunks; epilogue staging (32 KB)
-  __shared__ __align__(16) int32_t qpos_s[2][QC];
-  __shared__ __align__(16) int32_t qbkt_s[2][QC];
-  __shared__ __align__(16) float lse_s[2][QC];
-  __shared__ __align__(16) float del_s[2][QC];
+  static_assert(2 * 2 * CB <= 2 * BN * HD * 4, "chunk staging does not fit");
+  __shared__ __align__(16) int32_t qpos_s[2][CQ];
+  __shared__ __align__(16) int32_t qbkt_s[2][CQ];
+  __shared__ __align__(16) float lse_s[2][CQ];
+  __shared__ __align__(16) float del_s[2][CQ];
   __shared__ int32_t Ki[BN];
 
   const int tid = threadIdx.x;
@@ -274,13 +276,14 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
     dKa[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- DMA staging of a query chunk: wave w stages rows 8w .. 8w+7 --------
+  // ---- DMA staging of a query chunk: wave w stages rows 16w .. 16w+15 ------
   const uint8_t* qg = static_cast<const uint8_t*>(p.q) + head0;
   const uint8_t* dg = static_cast<const uint8_t*>(p.dO) + head0;
-  uint32_t rch;  // swz_k layout: serves the row and the transposed reads
-  {
-    const int row = 8 * w + (lane >> 3), cp = lane & 7;
-    rch = (cp ^ swz_k(row)) * 16;
+  uint32_t rch[2];  // swz_k layout: serves the row and the transposed reads
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * w + 8 * i + (lane >> 3), cp = lane & 7;
+    rch[i] = (cp ^ swz_k(row)) * 16;
   }
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t lds_small = ws == 0 ? lds_addr(&qpos_s[0][0])
@@ -291,18 +294,22 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
                           : ws == 1 ? static_cast<const void*>(HASH ? p.q_bkt + rowbase : p.q_idx + rowbase)
                           : ws == 2 ? static_cast<const void*>(p.lse2 + rowbase)
                                     : static_cast<const void*>(p.delta + rowbase);
-  constexpr int CPT = BM / QC;  // chunks per query tile
+  constexpr int CPT = BM / CQ;  // chunks per query tile
   const int nch = CPT * p.nQt;
-  auto chunk_rows = [&](int ci, int (&pos)[2]) {  // pos[0]: the row this lane stages
-    pos[0] = p.q_idx[rowbase + min(ci, nch - 1) * QC + 8 * w + (lane >> 3)];
-    pos[1] = 0;
+  auto chunk_rows = [&](int ci, int (&pos)[2]) {  // the two rows this lane stages
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pos[i] = p.q_idx[rowbase + min(ci, nch - 1) * CQ + 16 * w + 8 * i + (lane >> 3)];
   };
   auto stage = [&](int ci, int s, const int (&pos)[2]) {
-    const uint32_t base = lds0 + s * 2 * CB + ws * 1024;
-    const uint32_t off = static_cast<uint32_t>(src_row(pos[0], p.T)) * rstride;
-    dma16(qg, off + rch, base);
-    dma16(dg, off + rch, base + CB);
-    if (lane < QC) dma4(static_cast<const uint8_t*>(small_src) + ci * QC * 4, lane * 4, lds_small + s * QC * 4);
+    const uint32_t base = lds0 + s * 2 * CB + ws * 2048;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t off = static_cast<uint32_t>(src_row(pos[i], p.T)) * rstride;
+      dma16(qg, off + rch[i], base + i * 1024);
+      dma16(dg, off + rch[i], base + CB + i * 1024);
+    }
+    static_assert(CQ == 64, "one 4-byte entry per lane");
+    dma4(static_cast<const uint8_t*>(small_src) + ci * CQ * 4, lane * 4, lds_small + s * CQ * 4);
   };
   // chunk ci = CPT * query tile + part; tiles failing the causal test are
   // skipped
@@ -355,67 +362,79 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
     const int qt = ci / CPT;
     if (!walk.has(walk.cw.empty, qt)) {
       const uint8_t* Qr = smem + s * 2 * CB;
-      const uint8_t* Qt = Qr;
       const uint8_t* Dr = Qr + CB;
-      const uint8_t* Dt = Dr;
       const bool full = walk.has(walk.cw.full, qt);
-      // S = Q K^T (from the mask bias) and dP = dO V^T: rows = queries,
-      // column = this lane's key; element e of block qb is query
-      // 8 g + 4 qb + e of the chunk
-      f32x4 S[2], dP[2];
-      if (full) {
+      const bool buckets = HASH && walk.has(walk.cw.mixed, qt);
+      // the chunk's two halves of QC queries (rows 32 hq .. 32 hq + 31)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) S[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      } else {
-        const bool buckets = HASH && walk.has(walk.cw.mixed, qt);
+      for (int hq = 0; hq < 2; ++hq) {
+        // S = Q K^T (from the mask bias) and dP = dO V^T: rows = queries,
+        // column = this lane's key; element e of block qb is query
+        // 32 hq + 8 g + 4 qb + e of the chunk. Both branches define S afresh
+        // (a fully visible chunk starts the accumulators at zero).
+        f32x4 S[2], dP[2];
+        auto scores = [&]() {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int qo = 8 * g + 4 * qb;
-          const int4 qp4 = *reinterpret_cast<const int4*>(&qpos_s[s][qo]);
-          f32x4 c;
-          c[0] = bias_if_ge(qp4.x, kcmp);
-          c[1] = bias_if_ge(qp4.y, kcmp);
-          c[2] = bias_if_ge(qp4.z, kcmp);
-          c[3] = bias_if_ge(qp4.w, kcmp);
-          if (buckets) {
-            const int4 qb4 = *reinterpret_cast<const int4*>(&qbkt_s[s][qo]);
-            c[0] = keep_if_eq(c[0], qb4.x, kbkt);
-            c[1] = keep_if_eq(c[1], qb4.y, kbkt);
-            c[2] = keep_if_eq(c[2], qb4.z, kbkt);
-            c[3] = keep_if_eq(c[3], qb4.w, kbkt);
+          for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              S[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_row_op(Qr, 2 * hq + qb, r16, ds * 4 + g), Kb[ds],
+                                                              S[qb], 0, 0, 0);
+        };
+        if (full) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) S[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          scores();
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const int qo = 32 * hq + 8 * g + 4 * qb;
+            const int4 qp4 = *reinterpret_cast<const int4*>(&qpos_s[s][qo]);
+            f32x4 c;
+            c[0] = bias_if_ge(qp4.x, kcmp);
+            c[1] = bias_if_ge(qp4.y, kcmp);
+            c[2] = bias_if_ge(qp4.z, kcmp);
+            c[3] = bias_if_ge(qp4.w, kcmp);
+            if (buckets) {
+              const int4 qb4 = *reinterpret_cast<const int4*>(&qbkt_s[s][qo]);
+              c[0] = keep_if_eq(c[0], qb4.x, kbkt);
+              c[1] = keep_if_eq(c[1], qb4.y, kbkt);
+              c[2] = keep_if_eq(c[2], qb4.z, kbkt);
+              c[3] = keep_if_eq(c[3], qb4.w, kbkt);
+            }
+            S[qb] = c;
           }
-          S[qb] = c;
+          scores();
         }
-      }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) dP[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < 2; ++qb) dP[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ds = 0; ds < 2; ++ds)
+        for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            dP[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_row_op(Dr, 2 * hq + qb, r16, ds * 4 + g), Vb[ds],
+                                                             dP[qb], 0, 0, 0);
+        // P = exp2(S c - lse2), dS = P (dP - Delta)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          S[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_row_op(Qr, qb, r16, ds * 4 + g), Kb[ds], S[qb], 0, 0, 0);
-          dP[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_row_op(Dr, qb, r16, ds * 4 + g), Vb[ds], dP[qb], 0, 0, 0);
+          const int qo = 32 * hq + 8 * g + 4 * qb;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[s][qo]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&del_s[s][qo]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(fmaf(S[qb][e], p.c, -l4[e]));
+            S[qb][e] = pe;
+            dP[qb][e] = pe * (dP[qb][e] - d4[e]);
+          }
         }
-      // P = exp2(S c - lse2), dS = P (dP - Delta)
+        const bf16x8 Pp = pack_bf16x8(S[0], S[1]);
+        const bf16x8 Sp = pack_bf16x8(dP[0], dP[1]);
+        // dV^T += dO^T P,  dK^T += Q^T dS  (rows = dims, column = this lane's key)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int qo = 8 * g + 4 * qb;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[s][qo]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&del_s[s][qo]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(S[qb][e], p.c, -l4[e]));
-          S[qb][e] = pe;
-          dP[qb][e] = pe * (dP[qb][e] - d4[e]);
+        for (int db = 0; db < 4; ++db) {
+          dVa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_tr_op(Dr, db, hq, g, r16), Pp, dVa[db], 0, 0, 0);
+          dKa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_tr_op(Qr, db, hq, g, r16), Sp, dKa[db], 0, 0, 0);
         }
-      }
-      const bf16x8 Pp = pack_bf16x8(S[0], S[1]);
-      const bf16x8 Sp = pack_bf16x8(dP[0], dP[1]);
-      // dV^T += dO^T P,  dK^T += Q^T dS  (rows = dims, column = this lane's key)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        dVa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_tr_op(Dt, db, 0, g, r16), Pp, dVa[db], 0, 0, 0);
-        dKa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(read_tr_op(Qt, db, 0, g, r16), Sp, dKa[db], 0, 0, 0);
       }
     }
 
