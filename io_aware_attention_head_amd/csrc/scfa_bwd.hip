@@ -909,31 +909,37 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
       // and dP^T = V dO^T: rows = keys, column = this lane's query.
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
+        // both branches define S afresh: a fully visible tile starts the
+        // score accumulators at zero, others at the mask bias
         f32x4 S[2][2], dP[2][2];
+        auto products = [&]() {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) dP[h2][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ds = 0; ds < 2; ++ds)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const bf16x8 ak = read_row_op(Kr, 2 * kc + h2, r16, ds * 4 + g);
+              const bf16x8 av = read_row_op(Vr, 2 * kc + h2, r16, ds * 4 + g);
+#pragma unroll
+              for (int qb = 0; qb < 2; ++qb) {
+                S[h2][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, Qb[qb][ds], S[h2][qb], 0, 0, 0);
+                dP[h2][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Db[qb][ds], dP[h2][qb], 0, 0, 0);
+              }
+            }
+        };
         if (full) {
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) S[h2][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          products();
         } else {
           mask_bias_half(S, buckets, Kp[s], Kb[s], qcmp, qbkt, g, kc);
+          products();
         }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) dP[h2][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < 2; ++ds)
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const bf16x8 ak = read_row_op(Kr, 2 * kc + h2, r16, ds * 4 + g);
-            const bf16x8 av = read_row_op(Vr, 2 * kc + h2, r16, ds * 4 + g);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-              S[h2][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, Qb[qb][ds], S[h2][qb], 0, 0, 0);
-              dP[h2][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, Db[qb][ds], dP[h2][qb], 0, 0, 0);
-            }
-          }
         // dS^T = P^T (dP^T - Delta), P^T = exp2(S^T c - lse2)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
