@@ -357,6 +357,28 @@ int scfa_fwd_table(int mode, const int32_t* qstats, const int32_t* kstats, int B
  *  order   out (B*H*ntiles) int32, a permutation of the items.             */
 int scfa_work_order(const int32_t* tab, int B, int H, int ntiles, int span, int32_t* order, hipStream_t stream);
 
+/* The forward range table and its launch order in one call: the results of
+ * scfa_fwd_table followed by scfa_work_order(fwd_tab, ..., span = nKt, ...),
+ * for hash-mode statistics of the bucket-aligned layout (as
+ * scfa_hash_layout_qk writes them). One launch: the group's key-tile
+ * statistics are held in LDS, and where a head's key tiles are in layout
+ * order (one bucket per tile, buckets and, within a bucket, smallest
+ * positions non-decreasing) the range rules (explainer 3.4, Algorithm 2)
+ * become binary searches; other statistics are scanned tile by tile with
+ * the same rules, so any statistics give scfa_fwd_table's table. Groups too
+ * large for LDS fall back to the two separate launches.
+ *  mode            SCFA_HASH, optionally OR-ed with SCFA_STRICT or
+ *                  SCFA_NONCAUSAL (other modes: SCFA_ERR_INVALID).
+ *  qstats, kstats  (B, H, nQt, 4), (B, H, nKt, 4).
+ *  fwd_tab         out (B, H, nQt, 2).
+ *  tiles           (B*H) int32, zero on entry: the processed-tile count is
+ *                  added to it.
+ *  order           out (B*H*nQt) int32, as scfa_work_order (items of equal
+ *                  length in an unspecified order).
+ *  nKt             1..16383.                                              */
+int scfa_fwd_table_order(int mode, const int32_t* qstats, const int32_t* kstats, int B, int H, int nQt, int nKt,
+                         int32_t* fwd_tab, int32_t* tiles, int32_t* order, hipStream_t stream);
+
 /* Exact number of visible (query, key) pairs per head, from the sorted /
  * compacted index arrays (a query row r < Tq with position p >= 0 sees the
  * key rows s < Tk with k_idx[s] <= p, and equal bucket in hash mode; the

@@ -368,6 +368,7 @@ void bucket_launch(dim3 grid, hipStream_t stream, const void* x, const void* x2,
 
 constexpr int kSortChunk = 256;
 constexpr int kMaxOrderSpan = 16383;  // length bins of k_work_order fit in 64 KB of LDS
+constexpr size_t kTableOrderLds = 60 * 1024;  // dynamic LDS of k_fwd_table_order (within the default 64 KB)
 
 __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ bucket, int T, int nb, int nC,
                                                    int32_t* __restrict__ hist, int32_t* dev_err) {
@@ -979,6 +980,140 @@ __global__ __launch_bounds__(1024) void k_work_order(const int2* __restrict__ ta
 }
 
 // ---------------------------------------------------------------------------
+// Forward ranges and launch order in one launch, for tile statistics of the
+// bucket-aligned layout (hash mode). One workgroup per group of heads (the
+// groups of k_work_order). The group's key-tile statistics go to LDS. Where
+// a head's key tiles are in the layout's order (each tile one bucket,
+// buckets non-decreasing, and within a bucket non-decreasing smallest
+// positions; this holds for every layout scfa_hash_layout_qk writes), the
+// rules of Algorithm 2 reduce to searches: start = first key tile whose
+// bucket reaches the query tile's, stop = first tile past its bucket, and
+// the tiles passing the causal test are a prefix of [start, stop), found by
+// a binary search. Otherwise (or for a query tile spanning buckets) the
+// thread scans the head's tiles one by one with the same rules. The ranges
+// are then counting-sorted by length as in k_work_order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_fwd_table_order(const int4* __restrict__ qstats,
+                                                          const int4* __restrict__ kstats, int BH, int nQt, int nKt,
+                                                          int G, int2* __restrict__ fwd, int32_t* __restrict__ tiles,
+                                                          int32_t* __restrict__ order, const Reach rc) {
+  extern __shared__ int4 lds4[];
+  const int g = blockIdx.x;
+  const int hpg = BH / G;
+  const int n = hpg * nQt;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nbins = nKt + 1;  // bin nKt - len
+  int4* ks = lds4;                                               // hpg * nKt key-tile statistics
+  int32_t* bins = reinterpret_cast<int32_t*>(ks + hpg * nKt);    // nbins
+  int32_t* lens = bins + nbins;                                  // n range lengths
+  __shared__ int32_t ordered[64];                                // per head of the group: tiles in layout order
+  __shared__ int32_t cnt_s[64];                                  // per head: processed tiles
+  __shared__ int32_t wsum[16];
+  for (int i = tid; i < hpg * nKt; i += 1024) {
+    const int hl = i / nKt, j = i - hl * nKt;
+    ks[i] = kstats[static_cast<size_t>(g + hl * G) * nKt + j];
+  }
+  for (int i = tid; i < nbins; i += 1024) bins[i] = 0;
+  if (tid < hpg) {
+    ordered[tid] = 1;
+    cnt_s[tid] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < hpg * nKt; i += 1024) {
+    const int hl = i / nKt, j = i - hl * nKt;
+    const int4 a = ks[i];
+    bool ok = a.z == a.w;
+    if (j + 1 < nKt) {
+      const int4 c = ks[i + 1];
+      ok = ok && (a.w < c.z || (a.w == c.z && a.x <= c.x));
+    }
+    if (!ok) ordered[hl] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) {
+    const int hl = i / nQt, t = i - hl * nQt;
+    const int bh = g + hl * G;
+    const int4 qs = qstats[static_cast<size_t>(bh) * nQt + t];
+    const int qreach = q_reach(rc, qs.y);
+    const int4* k = ks + hl * nKt;
+    int start, end, cnt;
+    if (ordered[hl] && qs.z == qs.w) {
+      // first tile whose bucket is >= the query bucket, first tile past it
+      int lo = 0, hi = nKt;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (k[mid].w < qs.z) lo = mid + 1; else hi = mid;
+      }
+      start = lo;
+      hi = nKt;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (k[mid].z <= qs.w) lo = mid + 1; else hi = mid;
+      }
+      const int stop = lo;
+      // tiles of [start, stop) passing the causal test: a prefix
+      lo = start;
+      hi = stop;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (k[mid].x <= qreach) lo = mid + 1; else hi = mid;
+      }
+      cnt = lo - start;
+      end = lo;
+    } else {
+      start = 0;
+      for (int j = 0; j < nKt; ++j) start += k[j].w < qs.z;
+      int stop = nKt;
+      for (int j = start; j < nKt; ++j)
+        if (k[j].z > qs.w) {
+          stop = j;
+          break;
+        }
+      end = start;
+      cnt = 0;
+      for (int j = start; j < stop; ++j)
+        if (k[j].x <= qreach) {
+          end = j + 1;
+          ++cnt;
+        }
+    }
+    fwd[static_cast<size_t>(bh) * nQt + t] = make_int2(start, end);
+    const int len = min(max(end - start, 0), nKt);
+    lens[i] = len;
+    atomicAdd(&bins[nKt - len], 1);
+    if (cnt) atomicAdd(&cnt_s[hl], cnt);
+  }
+  __syncthreads();
+  if (tid < hpg && cnt_s[tid]) atomicAdd(&tiles[g + tid * G], cnt_s[tid]);
+  // exclusive scan of the bins (as k_work_order)
+  const int per = (nbins + 1023) / 1024;
+  const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
+  int sacc = 0;
+  for (int q = b0; q < b1; ++q) sacc += bins[q];
+  int x = sacc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int pre = x - sacc;
+  for (int q = 0; q < w; ++q) pre += wsum[q];
+  for (int q = b0; q < b1; ++q) {
+    const int c = bins[q];
+    bins[q] = pre;
+    pre += c;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) {
+    const int hl = i / nQt, t = i - hl * nQt;
+    const int slot = atomicAdd(&bins[nKt - lens[i]], 1);
+    order[static_cast<size_t>(slot) * G + g] = (g + hl * G) * nQt + t;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Exact visible-pair count (binary searches in the sorted key arrays).
 // ---------------------------------------------------------------------------
 
@@ -1346,6 +1481,28 @@ int scfa_work_order(const int32_t* tab, int B, int H, int ntiles, int span, int3
   const size_t lds = static_cast<size_t>(span + 1) * sizeof(int32_t);
   hipLaunchKernelGGL(k_work_order, dim3(G), dim3(1024), lds, stream, reinterpret_cast<const int2*>(tab), BH, ntiles,
                      span, G, order);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+int scfa_fwd_table_order(int mode, const int32_t* qstats, const int32_t* kstats, int B, int H, int nQt, int nKt,
+                         int32_t* fwd_tab, int32_t* tiles, int32_t* order, hipStream_t stream) {
+  const int flags = take_flags(mode);
+  if (!flags_ok(flags) || mode != SCFA_HASH) return SCFA_ERR_INVALID;
+  if (!qstats || !kstats || !fwd_tab || !tiles || !order) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || nQt < 1 || nKt < 1 || nKt > kMaxOrderSpan) return SCFA_ERR_INVALID;
+  const int BH = B * H;
+  const int G = (BH % 8 == 0) ? 8 : 1;
+  const int hpg = BH / G;
+  const size_t lds = static_cast<size_t>(hpg) * nKt * sizeof(int4) + static_cast<size_t>(nKt + 1 + hpg * nQt) * 4;
+  if (hpg > 64 || lds > kTableOrderLds) {  // too large for one workgroup's LDS: the two launches
+    const int st = scfa_fwd_table(mode | flags, qstats, kstats, B, H, nQt, nKt, fwd_tab, tiles, stream);
+    if (st != SCFA_OK) return st;
+    return scfa_work_order(fwd_tab, B, H, nQt, nKt, order, stream);
+  }
+  hipLaunchKernelGGL(k_fwd_table_order, dim3(G), dim3(1024), lds, stream, reinterpret_cast<const int4*>(qstats),
+                     reinterpret_cast<const int4*>(kstats), BH, nQt, nKt, G, reinterpret_cast<int2*>(fwd_tab), tiles,
+                     order, reach_of(flags));
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }

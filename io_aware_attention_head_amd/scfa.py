@@ -61,6 +61,7 @@ _SIGS = {
     "scfa_range_table": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_count_visible": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_work_order": (_i, [_vp, _i, _i, _i, _i, _vp, _vp]),
+    "scfa_fwd_table_order": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "scfa_qk_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                                 _vp, _vp, _vp]),
     "scfa_hash_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
@@ -252,6 +253,15 @@ def scfa_fwd_table(mode, qstats, kstats, fwd_tab, tiles, stream=None):
     nKt = kstats.shape[2]
     _check(lib().scfa_fwd_table(mode, _p(qstats), _p(kstats), B, H, nQt, nKt, _p(fwd_tab), _p(tiles),
                                 _stream(stream, qstats)), "scfa_fwd_table")
+
+
+def scfa_fwd_table_order(mode, qstats, kstats, fwd_tab, tiles, order, stream=None):
+    """Forward range table and its launch order in one launch (hash mode,
+    statistics of the bucket-aligned layout; tiles must be zero on entry)."""
+    B, H, nQt, _ = qstats.shape
+    nKt = kstats.shape[2]
+    _check(lib().scfa_fwd_table_order(mode, _p(qstats), _p(kstats), B, H, nQt, nKt, _p(fwd_tab), _p(tiles), _p(order),
+                                      _stream(stream, qstats)), "scfa_fwd_table_order")
 
 
 def chunk_count_shape(B, H, T, nb):
@@ -749,14 +759,14 @@ class Plan:
     def tables(self, stream=None):
         """Forward ranges and the launch order, after the tile statistics
         (computed here, or in hash mode by sort(), which also zeroes the
-        processed-tile counter that this call adds to); the backward table is
-        built by backward()."""
+        processed-tile counter that this call adds to; both then come from
+        one launch); the backward table is built by backward()."""
         t = self.tab
         if self.mode == "hash" and self.two_side:  # the tile statistics come from the layout launch
-            scfa_fwd_table(SCFA_HASH | self.flags, t.qstats, t.kstats, t.fwd, t.tiles, stream)
-        else:
-            scfa_range_table(_table_mode(self.mode) | self.flags, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B,
-                             self.H, self.Tq, self.Tk, t.Bm, t.Bn, t.qstats, t.kstats, t.fwd, None, t.tiles, stream)
+            scfa_fwd_table_order(SCFA_HASH | self.flags, t.qstats, t.kstats, t.fwd, t.tiles, t.fwd_order, stream)
+            return
+        scfa_range_table(_table_mode(self.mode) | self.flags, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B,
+                         self.H, self.Tq, self.Tk, t.Bm, t.Bn, t.qstats, t.kstats, t.fwd, None, t.tiles, stream)
         scfa_work_order(t.fwd, t.kstats.shape[2], t.fwd_order, stream)
 
     def forward(self, stream=None):

@@ -492,3 +492,66 @@ def test_plan_two_side_launches_bitexact(w):
         assert torch.equal(getattr(plan.tab, name), getattr(ref, name)), name
     # the Plan's launch order over its forward table
     check_order(plan.tab.fwd_order.cpu().numpy(), plan.tab.fwd.cpu().numpy())
+
+
+def _layout_stats(rng, BH, nQt, nKt, nb):
+    """Tile statistics shaped like the bucket-aligned layout's: every tile one
+    bucket, buckets non-decreasing, positions ascending within a bucket, pad
+    tiles (bucket nb) at the end of each side."""
+    qs = np.empty((BH, nQt, 4), np.int32)
+    ks = np.empty((BH, nKt, 4), np.int32)
+    for st, n, pad, rows in ((qs, nQt, oracle.Q_PAD, scfa.SCFA_TILE_M), (ks, nKt, oracle.K_PAD, scfa.SCFA_TILE_N)):
+        for h in range(BH):
+            nreal = int(rng.integers(max(1, n // 2), n + 1))
+            bk = np.sort(rng.integers(0, nb, nreal))
+            pos = np.empty(nreal, np.int64)
+            for v in range(nb):  # positions ascend within each bucket
+                m = bk == v
+                pos[m] = np.sort(rng.integers(0, 50 * n * rows, int(m.sum())))
+            st[h, :nreal, 0] = pos
+            st[h, :nreal, 1] = pos + rng.integers(0, 3 * rows, nreal)
+            st[h, :nreal, 2] = bk
+            st[h, :nreal, 3] = bk
+            st[h, nreal:] = (pad, pad, nb, nb)
+    return qs, ks
+
+
+@pytest.mark.parametrize("case", [(2, 12, 144, 272, 16, 0), (1, 3, 20, 40, 8, 0), (2, 4, 64, 130, 4, scfa.SCFA_STRICT),
+                                  (1, 8, 30, 70, 6, scfa.SCFA_NONCAUSAL), (1, 3, 40, 1300, 16, 0),
+                                  (1, 5, 9, 2, 2, 0)],
+                         ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("kind", ["layout", "random"])
+def test_fwd_table_order_matches_two_launches(case, kind):
+    """The one-launch forward table and order against scfa_fwd_table followed
+    by scfa_work_order: the same table and tile count, bit for bit, and a
+    valid longest-first order, on statistics shaped like the aligned layout's
+    (the searched path) and on random statistics (the tile-by-tile path);
+    (1, 3, 40, 1300) is too large for one workgroup's LDS (the two-launch
+    fallback inside the call)."""
+    need_gpu()
+    B, H, nQt, nKt, nb, flags = case
+    announce(f"fwd table + order {kind} {case}")
+    rng = np.random.default_rng(sum(case) + (7 if kind == "random" else 0))
+    if kind == "layout":
+        qs, ks = _layout_stats(rng, B * H, nQt, nKt, nb)
+    else:
+        qs = rng.integers(-5, 4000, (B * H, nQt, 4)).astype(np.int32)
+        ks = rng.integers(-5, 4000, (B * H, nKt, 4)).astype(np.int32)
+        qs[..., 2:] = np.sort(rng.integers(0, nb, (B * H, nQt, 2)), axis=-1)
+        ks[..., 2:] = np.sort(rng.integers(0, nb, (B * H, nKt, 2)), axis=-1)
+    dev = torch.device("cuda:0")
+    qst = torch.from_numpy(qs).reshape(B, H, nQt, 4).to(dev)
+    kst = torch.from_numpy(ks).reshape(B, H, nKt, 4).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    mode = scfa.SCFA_HASH | flags
+    ref_tab, ref_tiles, ref_order = (torch.empty((B, H, nQt, 2), **i32), torch.zeros((B, H), **i32),
+                                     torch.empty((B * H * nQt,), **i32))
+    scfa.scfa_fwd_table(mode, qst, kst, ref_tab, ref_tiles)
+    scfa.scfa_work_order(ref_tab, nKt, ref_order)
+    tab, tiles, order = (torch.empty((B, H, nQt, 2), **i32), torch.zeros((B, H), **i32),
+                         torch.empty((B * H * nQt,), **i32))
+    scfa.scfa_fwd_table_order(mode, qst, kst, tab, tiles, order)
+    torch.cuda.synchronize()
+    assert torch.equal(tab, ref_tab)
+    assert torch.equal(tiles, ref_tiles)
+    check_order(order.cpu().numpy(), tab.cpu().numpy())
