@@ -114,21 +114,28 @@ __device__ void zero_unheld(const int32_t* idx_bh, const int32_t* ti, int tile, 
     lo = 0;
     hi = T - 1;
   }
-  for (int base = lo; base <= hi; base += 16) {
-    const int pos = base + (tid >> 4);
-    const int u = tid & 15;
-    if (pos <= hi) {
-      int a = 0, z = nreal;
-      while (a < z) {
-        const int mid = (a + z) >> 1;
-        if (ti[mid] < pos) a = mid + 1; else z = mid;
-      }
-      if (!(a < nreal && ti[a] == pos)) {
-        const size_t o = ((static_cast<size_t>(b) * T + pos) * H + h) * HD;
+  // 256 positions per pass, one per thread: the tile's real entries in the
+  // pass's window are flagged in LDS, and each thread zeroes the whole rows of
+  // its position when that is not flagged
+  __shared__ uint8_t held_w[256];
+  for (int base = lo; base <= hi; base += 256) {
+    held_w[tid] = 0;
+    __syncthreads();
+    if (tid < nreal) {
+      const int d = ti[tid] - base;
+      if (d >= 0 && d < 256) held_w[d] = 1;
+    }
+    __syncthreads();
+    const int pos = base + tid;
+    if (pos <= hi && !held_w[tid]) {
+      const size_t o = ((static_cast<size_t>(b) * T + pos) * H + h) * HD;
+#pragma unroll
+      for (int u = 0; u < HD / 4; ++u) {
         reinterpret_cast<f32x4*>(out0 + o)[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (out1) reinterpret_cast<f32x4*>(out1 + o)[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
+    __syncthreads();  // held_w is cleared for the next pass
   }
 }
 

@@ -203,23 +203,27 @@ __device__ inline void fwd_epilogue(const FwdParams& p, TOUT* ost, const int32_t
       lo = 0;
       hi = p.T - 1;
     }
+    // 256 positions per pass, one per thread: the tile's kept positions in
+    // the pass's window are flagged in LDS, and each thread writes the whole
+    // row of its position when that is not flagged
     constexpr int UPR = HD * sizeof(TOUT) / 16;  // 16-byte units per output row
-    constexpr int RPI = 256 / UPR;               // rows per iteration
-    for (int base = lo; base <= hi; base += RPI) {
-      const int pos = base + tid / UPR;
-      const int u = tid % UPR;
-      if (pos <= hi) {
-        int a = 0, z = nreal;  // binary search pos among the tile's kept positions
-        while (a < z) {
-          const int mid = (a + z) >> 1;
-          if (Qi[mid] < pos) a = mid + 1; else z = mid;
-        }
-        if (!(a < nreal && Qi[a] == pos)) {
-          TOUT* orow = O + ((static_cast<size_t>(b) * p.T + pos) * p.H + h) * HD;
-          reinterpret_cast<uint4*>(orow)[u] = make_uint4(0, 0, 0, 0);
-          if (u == 0) p.lse[static_cast<size_t>(bh) * p.T + pos] = -INFINITY;
-        }
+    __shared__ uint8_t kept_w[256];
+    for (int base = lo; base <= hi; base += 256) {
+      kept_w[tid] = 0;
+      __syncthreads();
+      if (tid < nreal) {
+        const int d = Qi[tid] - base;
+        if (d >= 0 && d < 256) kept_w[d] = 1;
       }
+      __syncthreads();
+      const int pos = base + tid;
+      if (pos <= hi && !kept_w[tid]) {
+        uint4* orow = reinterpret_cast<uint4*>(O + ((static_cast<size_t>(b) * p.T + pos) * p.H + h) * HD);
+#pragma unroll
+        for (int u = 0; u < UPR; ++u) orow[u] = make_uint4(0, 0, 0, 0);
+        p.lse[static_cast<size_t>(bh) * p.T + pos] = -INFINITY;
+      }
+      __syncthreads();  // kept_w is cleared for the next pass
     }
   }
 }
