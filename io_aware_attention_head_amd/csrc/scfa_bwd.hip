@@ -801,17 +801,29 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   int qpos[2], qbkt[2];
   float ql2[2], qdl[2];
   bf16x8 Qb[2][2], Db[2][2];
+  // O and the LSE of the same rows, for Delta: loaded with Q and dO (all
+  // loads of the rows in flight together, before any store)
+  f32x4 Ov[2][2][2];  // [qb][ds][half]
+  float lraw[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int row = q0 + qb * 16 + r16;
     qpos[qb] = p.q_idx[rowbase + row];
     qbkt[qb] = HASH ? p.q_bkt[rowbase + row] : 0;
-    const size_t off = head0 + static_cast<size_t>(src_row(qpos[qb], p.T)) * rstride;
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qp = qpos[qb];
+    const size_t off = head0 + static_cast<size_t>(src_row(qp, p.T)) * rstride;
+    const float* orow = p.O + ((static_cast<size_t>(b) * p.T + src_row(qp, p.T)) * p.H + h) * HD;
 #pragma unroll
     for (int ds = 0; ds < 2; ++ds) {
       Qb[qb][ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.q) + off + (ds * 32 + g * 8) * 2);
       Db[qb][ds] = *reinterpret_cast<const bf16x8*>(static_cast<const uint8_t*>(p.dO) + off + (ds * 32 + g * 8) * 2);
+      Ov[qb][ds][0] = *reinterpret_cast<const f32x4*>(orow + ds * 32 + g * 8);
+      Ov[qb][ds][1] = *reinterpret_cast<const f32x4*>(orow + ds * 32 + g * 8 + 4);
     }
+    lraw[qb] = p.lse[static_cast<size_t>(bh) * p.T + src_row(qp, p.T)];
   }
   // Delta = dO . O and log2 LSE of this wave's rows (the four lane groups
   // hold 16 dims each of a row), written to the workspace for dK/dV, which
@@ -821,24 +833,23 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
   for (int qb = 0; qb < 2; ++qb) {
     const int qp = qpos[qb];
     const bool valid = qp >= 0 && qp < p.T;
-    const float* orow = p.O + ((static_cast<size_t>(b) * p.T + src_row(qp, p.T)) * p.H + h) * HD;
     float dot = 0.f;
 #pragma unroll
-    for (int ds = 0; ds < 2; ++ds) {
-      const f32x4 o0 = *reinterpret_cast<const f32x4*>(orow + ds * 32 + g * 8);
-      const f32x4 o1 = *reinterpret_cast<const f32x4*>(orow + ds * 32 + g * 8 + 4);
+    for (int ds = 0; ds < 2; ++ds)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        dot = fmaf(static_cast<float>(Db[qb][ds][e]), o0[e], dot);
-        dot = fmaf(static_cast<float>(Db[qb][ds][4 + e]), o1[e], dot);
+        dot = fmaf(static_cast<float>(Db[qb][ds][e]), Ov[qb][ds][0][e], dot);
+        dot = fmaf(static_cast<float>(Db[qb][ds][4 + e]), Ov[qb][ds][1][e], dot);
       }
-    }
     dot += __shfl_xor(dot, 16);
     dot += __shfl_xor(dot, 32);
-    const float l = valid ? p.lse[static_cast<size_t>(bh) * p.T + qp] : -INFINITY;
+    const float l = valid ? lraw[qb] : -INFINITY;
     qdl[qb] = valid ? dot : 0.f;
     ql2[qb] = (l == -INFINITY) ? INFINITY : l * kLog2e;
-    if (g == 0) {
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
       const size_t r = rowbase + q0 + qb * 16 + r16;
       p.lse2[r] = ql2[qb];
       p.delta[r] = qdl[qb];
