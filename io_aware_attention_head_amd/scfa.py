@@ -437,6 +437,7 @@ class Tables:
     Bn: int
     fwd_order: Optional[torch.Tensor] = None  # launch order of the forward / dQ workgroups
     bwd_order: Optional[torch.Tensor] = None  # launch order of the dK/dV workgroups (hash mode)
+    bwd_ready: bool = True  # bwd (and bwd_order) hold the ranges of the current forward tables
 
 
 def _empty(shape, dtype, like):
@@ -596,6 +597,8 @@ def forward(pre: Prepared, tab: Tables, out_dtype=torch.float32, scale=None, O=N
 def backward(pre: Prepared, tab: Tables, O, lse, dO, scale=None, grads=None, workspace=None, stream=None):
     """Gradients w.r.t. the original-order q, k, v (fp32, (B,T,H,D)); the
     backward kernels read q, k, v and dO through the index arrays."""
+    if not tab.bwd_ready:  # the dK/dV kernel reads bwd (and bwd_order)
+        raise ScfaError("the backward table of these tables is not built (a plan builds it in its backward())")
     B, H, T, D = pre.B, pre.H, pre.T, pre.D
     mode = _table_mode(pre.mode)
     if grads is None:
@@ -710,7 +713,7 @@ class Plan:
         Bm, Bn = SCFA_TILE_M, SCFA_TILE_N
         nQt, nKt = TqP // Bm, TkP // Bn
         self.tab = Tables(e((B, H, nQt, 4)), e((B, H, nKt, 4)), e((B, H, nQt, 2)), e((B, H, nKt, 2)), e((B, H)), Bm, Bn,
-                          e((B * H * nQt,)), e((B * H * nKt,)) if mode == "hash" else None)
+                          e((B * H * nQt,)), e((B * H * nKt,)) if mode == "hash" else None, bwd_ready=False)
         self.O = e((B, T, H, D), out_dtype)
         self.lse = e((B, H, T), torch.float32)
         self.pairs = e((B, H), torch.int64)
@@ -762,6 +765,7 @@ class Plan:
         processed-tile counter that this call adds to; both then come from
         one launch); the backward table is built by backward()."""
         t = self.tab
+        t.bwd_ready = False  # new forward ranges: backward() rebuilds the backward table
         if self.mode == "hash" and self.two_side:  # the tile statistics come from the layout launch
             scfa_fwd_table_order(SCFA_HASH | self.flags, t.qstats, t.kstats, t.fwd, t.tiles, t.fwd_order, stream)
             return
@@ -777,17 +781,18 @@ class Plan:
         the backward table, then the backward kernels."""
         if self.x is None:
             raise ScfaError("backward needs a prepared forward")
+        if self.out_dtype != torch.float32:
+            raise ScfaError("backward needs the fp32 forward output")
         scfa_bwd_table(self.tab.qstats, self.tab.kstats, self.tab.fwd, self.tab.bwd, stream, self.flags)
         if self.mode == "hash":  # one dK/dV workgroup per key tile: longest query ranges first
             scfa_work_order(self.tab.bwd, self.tab.fwd.shape[2], self.tab.bwd_order, stream)
+        self.tab.bwd_ready = True
         if self._grads is None:
             d = self.device
             self._grads = tuple(torch.empty((self.B, n, self.H, self.D), dtype=torch.float32, device=d)
                                 for n in (self.T, self.T_kv, self.T_kv))
             self._bws = torch.empty((scfa_bwd_workspace_bytes(_table_mode(self.mode), self.B, self.H, self.Tq, self.Tk,
                                                               self.D),), dtype=torch.uint8, device=d)
-        if self.out_dtype != torch.float32:
-            raise ScfaError("backward needs the fp32 forward output")
         return backward(self.prepared(), self.tab, self.O, self.lse, dO, self.scale, self._grads, self._bws, stream)
 
     def count_visible(self, stream=None):

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import io_aware_attention_head_amd.scfa as scfa
 
@@ -214,6 +215,7 @@ def test_bwd_noalloc_rejects_without_gpu():
     assert call(scfa.SCFA_HASH, [null] + ptrs[1:], 1, 1, 256, 256, 256) == scfa.SCFA_ERR_INVALID
     assert f(scfa.SCFA_HASH, 0, *ptrs, 1, 1, 256, 256, 256, 256, 64, 0.125, null, d, d, null) == scfa.SCFA_ERR_INVALID
     assert call(7, ptrs, 1, 1, 256, 256, 256) == scfa.SCFA_ERR_INVALID
+    assert call(scfa.SCFA_HASH | 64, ptrs, 1, 1, 256, 256, 256) == scfa.SCFA_ERR_INVALID
     assert call(scfa.SCFA_HASH, ptrs, 1, 1, 256, 256, 256, dtype=scfa.SCFA_F32) == scfa.SCFA_ERR_UNSUPPORTED
     assert call(scfa.SCFA_HASH, ptrs, 1, 1, 256, 256, 256, D=32) == scfa.SCFA_ERR_UNSUPPORTED
     # workspace beyond the static scratch: 8 bytes per query row of B*H*pad(Tq)
@@ -221,3 +223,15 @@ def test_bwd_noalloc_rejects_without_gpu():
     assert call(scfa.SCFA_QK, ptrs, 1, 17, 131072, 131072, 131072) == scfa.SCFA_ERR_TOO_LARGE
     assert 17 * 131072 > rows_max
     assert scfa.scfa_status_string(scfa.SCFA_ERR_TOO_LARGE).startswith("SCFA_ERR_TOO_LARGE")
+
+
+def test_plan_tables_need_backward_table_before_dkdv():
+    """A plan's tables carry no backward ranges until the plan's backward()
+    builds them: a backward on them is refused on the host (its dK/dV kernel
+    would read unwritten ranges)."""
+    plan = scfa.Plan("hash", 1, 2, 300, device="cpu")
+    q = torch.zeros(1, 300, 2, 64, dtype=torch.bfloat16)
+    plan.x = dict(q=q, k=q, v=q, R=torch.zeros(64, 8))
+    assert not plan.tab.bwd_ready
+    with pytest.raises(scfa.ScfaError, match="backward table"):
+        scfa.backward(plan.prepared(), plan.tab, plan.O, plan.lse, q)

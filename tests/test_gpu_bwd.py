@@ -126,6 +126,33 @@ def test_bwd_deterministic_and_fp32_unsupported():
         scfa.backward(pref, tabf, Of, lsef, gf["dO"])
 
 
+@pytest.mark.parametrize("mode", ["hash", "qk"])
+def test_plan_backward_matches_call(mode):
+    """A plan's backward (backward table, launch order, kernels) equals one
+    backward call on the tables it built, bit for bit, and rewrites every
+    gradient row when called again; before its first backward the plan's
+    tables are refused."""
+    need_gpu()
+    announce(f"plan backward {mode}")
+    w = small(mode, 2, 3, 1500, nb=16, keep_p=0.6, seed=80, grad=True)
+    g = {k: v.to("cuda:0") for k, v in make_inputs(w).items()}
+    plan = scfa.Plan(mode, w.B, w.H, w.T, w.D, torch.bfloat16, nb=w.nb)
+    plan.run(g)
+    with pytest.raises(scfa.ScfaError):
+        scfa.backward(plan.prepared(), plan.tab, plan.O, plan.lse, g["dO"])
+    first = tuple(t.clone() for t in plan.backward(g["dO"]))
+    ref = scfa.backward(plan.prepared(), plan.tab, plan.O, plan.lse, g["dO"])
+    torch.cuda.synchronize()
+    for a, b in zip(first, ref):
+        assert torch.equal(a, b)
+    for t in plan._grads:
+        t.fill_(float("nan"))
+    got = plan.backward(g["dO"])
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
+
+
 def _check_tiles(grads, ref, pre, heads):
     """Per-tile check of the gradients: dQ over each 128-query tile and dK, dV
     over each 64-key tile of the kernels' layout (rows of q_idx / k_idx), so
