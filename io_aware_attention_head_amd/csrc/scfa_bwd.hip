@@ -380,6 +380,15 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
         // 32 hq + 8 g + 4 qb + e of the chunk. Both branches define S afresh
         // (a fully visible chunk starts the accumulators at zero).
         f32x4 S[2], dP[2];
+        // log2 LSE and Delta of the half's queries, read before the products
+        // so that the exponentials do not wait for LDS
+        f32x4 l4[2], d4[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int qo = 32 * hq + 8 * g + 4 * qb;
+          l4[qb] = *reinterpret_cast<const f32x4*>(&lse_s[s][qo]);
+          d4[qb] = *reinterpret_cast<const f32x4*>(&del_s[s][qo]);
+        }
         auto scores = [&]() {
 #pragma unroll
           for (int ds = 0; ds < 2; ++ds)
@@ -413,8 +422,9 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
           }
           scores();
         }
+        // dP - Delta straight from the MFMAs: the accumulators start at -Delta
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) dP[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < 2; ++qb) dP[qb] = -d4[qb];
 #pragma unroll
         for (int ds = 0; ds < 2; ++ds)
 #pragma unroll
@@ -424,14 +434,11 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv64(BwdParams p) {
         // P = exp2(S c - lse2), dS = P (dP - Delta)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const int qo = 32 * hq + 8 * g + 4 * qb;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[s][qo]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&del_s[s][qo]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float pe = __builtin_amdgcn_exp2f(fmaf(S[qb][e], p.c, -l4[e]));
+            const float pe = __builtin_amdgcn_exp2f(fmaf(S[qb][e], p.c, -l4[qb][e]));
             S[qb][e] = pe;
-            dP[qb][e] = pe * (dP[qb][e] - d4[e]);
+            dP[qb][e] = pe * dP[qb][e];
           }
         }
         const bf16x8 Pp = pack_bf16x8(S[0], S[1]);
@@ -688,10 +695,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
           }
         }
       }
+      // dP - Delta straight from the MFMAs: the accumulators start at -Delta
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < 2; ++qb) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&del_s[s][8 * g + 4 * qb]);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) dP[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 2; ++kb) dP[kb][qb] = -d4;
+      }
 #pragma unroll
       for (int ds = 0; ds < 2; ++ds)
 #pragma unroll
@@ -710,14 +720,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       for (int qb = 0; qb < 2; ++qb) {
         const int qo = 8 * g + 4 * qb;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[s][qo]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&del_s[s][qo]);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float pe = __builtin_amdgcn_exp2f(fmaf(S[kb][qb][e], p.c, -l4[e]));
             S[kb][qb][e] = pe;
-            dP[kb][qb][e] = pe * (dP[kb][qb][e] - d4[e]);
+            dP[kb][qb][e] = pe * dP[kb][qb][e];
           }
       }
 #pragma unroll
@@ -773,7 +782,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 // dP^T = V dO^T), with the keys' positions / buckets.
 // ---------------------------------------------------------------------------
 template <bool HASH, bool ZD>
-__global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_bwd_dq(BwdParams p) {
   __shared__ __align__(16) uint8_t smem[2 * 2 * TB];  // 2 stages x (K, V); epilogue staging
   __shared__ __align__(16) int32_t Kp[2][BN];
   __shared__ __align__(16) int32_t Kb[2][BN];
@@ -931,10 +940,11 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
         // score accumulators at zero, others at the mask bias
         f32x4 S[2][2], dP[2][2];
         auto products = [&]() {
+          // dP^T - Delta straight from the MFMAs: the accumulators start at -Delta
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) dP[h2][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int qb = 0; qb < 2; ++qb) dP[h2][qb] = f32x4{-qdl[qb], -qdl[qb], -qdl[qb], -qdl[qb]};
 #pragma unroll
           for (int ds = 0; ds < 2; ++ds)
 #pragma unroll
@@ -966,7 +976,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float pe = __builtin_amdgcn_exp2f(fmaf(S[h2][qb][e], p.c, -ql2[qb]));
-              dP[h2][qb][e] = pe * (dP[h2][qb][e] - qdl[qb]);
+              dP[h2][qb][e] = pe * dP[h2][qb][e];
             }
         // dQ^T += K^T dS^T (rows = dims, column = this lane's query)
 #pragma unroll
