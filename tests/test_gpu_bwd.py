@@ -108,6 +108,33 @@ def test_bwd_hash_single_bucket_equals_dense():
     _check(gd, ref)
 
 
+@pytest.mark.parametrize("case", ["T1", "T2", "last_bucket_only", "skewed", "nb64_short"])
+def test_bwd_hash_edge_cases(case):
+    """Hash-mode gradients against the oracle where buckets and tiles are
+    degenerate: one and two tokens, every token in the last bucket, most
+    tokens in two buckets, and nb = 64 buckets over 300 tokens (most buckets
+    hold a handful of tokens or none, so tiles are mostly pad rows)."""
+    need_gpu()
+    announce(f"bwd hash edge {case}")
+    T = {"T1": 1, "T2": 2, "nb64_short": 300}.get(case, 900)
+    nb = 64 if case == "nb64_short" else 16
+    w = small("hash", 1, 3, T, nb=nb, seed=81, grad=True)
+    x = make_inputs(w)
+    if case == "last_bucket_only":
+        x["R"].zero_()
+        x["R"][:, :, nb // 2 - 1] = 1.0
+        x["q"] = (-x["q"].float().abs() - 0.01).to(torch.bfloat16)
+        x["k"] = (-x["k"].float().abs() - 0.01).to(torch.bfloat16)
+    elif case == "skewed":
+        x["R"][:, :, 0] += 3.0
+    _, pre, tab, O, lse, grads = _run(w, x)
+    buckets = oracle_buckets(w, x)
+    if case == "last_bucket_only":
+        assert (buckets[0] == nb - 1).all() and (buckets[1] == nb - 1).all()
+    rels = _check(grads, _oracle_bwd(w, x, buckets=buckets))
+    print(f"{case}: rel dQ {rels[0]:.2e} dK {rels[1]:.2e} dV {rels[2]:.2e}")
+
+
 def test_bwd_deterministic_and_fp32_unsupported():
     need_gpu()
     announce("bwd determinism")
