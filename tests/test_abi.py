@@ -235,3 +235,16 @@ def test_plan_tables_need_backward_table_before_dkdv():
     assert not plan.tab.bwd_ready
     with pytest.raises(scfa.ScfaError, match="backward table"):
         scfa.backward(plan.prepared(), plan.tab, plan.O, plan.lse, q)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more (flag or WORLD_SIZE) it exits
+    with status 2 and a message, before it imports torch or touches a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *argv], capture_output=True, text=True,
+                           env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 2
+        assert "one GPU only" in r.stderr
