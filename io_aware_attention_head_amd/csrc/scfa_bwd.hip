@@ -1041,9 +1041,9 @@ int launch_bwd(const BwdParams& p, hipStream_t stream) {
 // rows), in place of a caller-supplied workspace. Each device holds its own
 // copy for the life of the process; host code reaches it only through the
 // address hipGetSymbolAddress returns for that device (the array's name is
-// a host-side stand-in, not a device address). The preparation kernel
-// writes every row it covers before the other kernels read it, so nothing
-// has to be cleared between calls.
+// a host-side stand-in, not a device address). The dQ kernel writes every
+// row of it before the dK/dV kernel reads it, so nothing has to be cleared
+// between calls.
 __device__ __align__(256) uint8_t scratch[SCFA_NOALLOC_SCRATCH_BYTES];
 
 constexpr int kMaxDevices = 64;
@@ -1069,8 +1069,8 @@ int scratch_of_stream(hipStream_t stream, uint8_t** out) {
 }
 
 // Shared body of scfa_bwd and scfa_bwd_noalloc: argument checks, then the
-// preparation, dK/dV and dQ kernels with the workspace of log2 LSE and
-// Delta: `ws` (ws_bytes bytes) from the caller, or with `noalloc` the
+// dQ kernel (which fills the workspace of log2 LSE and Delta) and the dK/dV
+// kernel: `ws` (ws_bytes bytes) from the caller, or with `noalloc` the
 // device's static scratch (after every argument check).
 int bwd_run(int mode, int dtype_in, const void* q, const void* k, const void* v, const int32_t* q_idx,
             const int32_t* k_idx, const int32_t* q_bkt, const int32_t* k_bkt, const int32_t* qstats,
