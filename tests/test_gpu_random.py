@@ -37,6 +37,25 @@ def _cases(n=96, seed=2024):
 CASES = _cases()
 
 
+def _long_cases(n=8, seed=4048):
+    """Longer sequences (ranges beyond one 64-tile window of the tile tests),
+    one or two heads."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        mode = ["dense", "qk", "hash", "hash_drop"][i % 4]
+        variant = ["causal", "strict", "noncausal"][int(rng.integers(0, 3))]
+        T = int(rng.integers(4100, 6000))
+        Tk = int(rng.integers(4100, 6000)) if rng.random() < 0.4 else T
+        nb = int(rng.choice([2, 4]))  # few buckets: long ranges
+        keep = float(rng.choice([0.7, 0.9]))
+        out.append((mode, variant, 1, int(rng.integers(1, 3)), T, Tk, nb, keep, "bf16", 700 + i))
+    return out
+
+
+CASES = CASES + _long_cases()
+
+
 def _ids(c):
     mode, variant, B, H, T, Tk, nb, keep, dtype, seed = c
     return f"{mode}-{variant}-B{B}H{H}T{T}Tk{Tk}-nb{nb}-p{keep}-{dtype}-s{seed}"
