@@ -316,7 +316,9 @@ int scfa_gather(int dtype, int layout, const void* x, const int32_t* idx, int B,
  *                hash).
  *  kstats out (B, H, nKt, 4), nKt = SCFA_PAD(Tk)/Bn; a tile with no valid
  *                row holds [K_PAD, K_PAD, INT32_MAX, INT32_MAX].
- *  fwd_tab out (B, H, nQt, 2) [start, end).
+ *  fwd_tab out (B, H, nQt, 2) [start, end), or NULL (then bwd_tab must be
+ *                NULL too) for the statistics alone, with tiles zeroed:
+ *                scfa_fwd_table_order then builds the ranges and the order.
  *  bwd_tab out (B, H, nKt, 2), or NULL to skip it (a forward-only call;
  *                scfa_bwd_table builds it later from the same statistics).
  *  tiles   out (B, H) int32: number of processed tile pairs.               */
@@ -358,17 +360,17 @@ int scfa_fwd_table(int mode, const int32_t* qstats, const int32_t* kstats, int B
 int scfa_work_order(const int32_t* tab, int B, int H, int ntiles, int span, int32_t* order, hipStream_t stream);
 
 /* The forward range table and its launch order in one call: the results of
- * scfa_fwd_table followed by scfa_work_order(fwd_tab, ..., span = nKt, ...),
- * for hash-mode statistics of the bucket-aligned layout (as
- * scfa_hash_layout_qk writes them). One launch: the group's key-tile
- * statistics are held in LDS, and where a head's key tiles are in layout
- * order (one bucket per tile, buckets and, within a bucket, smallest
- * positions non-decreasing) the range rules (explainer 3.4, Algorithm 2)
- * become binary searches; other statistics are scanned tile by tile with
- * the same rules, so any statistics give scfa_fwd_table's table. Groups too
- * large for LDS fall back to the two separate launches.
- *  mode            SCFA_HASH, optionally OR-ed with SCFA_STRICT or
- *                  SCFA_NONCAUSAL (other modes: SCFA_ERR_INVALID).
+ * scfa_fwd_table followed by scfa_work_order(fwd_tab, ..., span = nKt, ...).
+ * One launch: the group's key-tile statistics are held in LDS, and where a
+ * head's key tiles are in layout order (one bucket per tile, buckets and,
+ * within a bucket, smallest positions non-decreasing: the hash layout of
+ * scfa_hash_layout_qk, and the compacted or dense rows of the QK and dense
+ * modes) the range rules (explainer 3.4, Algorithms 1 and 2) become binary
+ * searches; other statistics are scanned tile by tile with the same rules,
+ * so any statistics give scfa_fwd_table's table. Groups too large for LDS
+ * fall back to the two separate launches.
+ *  mode            SCFA_DENSE, SCFA_QK or SCFA_HASH, optionally OR-ed with
+ *                  SCFA_STRICT or SCFA_NONCAUSAL.
  *  qstats, kstats  (B, H, nQt, 4), (B, H, nKt, 4).
  *  fwd_tab         out (B, H, nQt, 2).
  *  tiles           (B*H) int32, zero on entry: the processed-tile count is

@@ -980,20 +980,21 @@ __global__ __launch_bounds__(1024) void k_work_order(const int2* __restrict__ ta
 }
 
 // ---------------------------------------------------------------------------
-// Forward ranges and launch order in one launch, for tile statistics of the
-// bucket-aligned layout (hash mode). One workgroup per group of heads (the
-// groups of k_work_order). The group's key-tile statistics go to LDS. Where
-// a head's key tiles are in the layout's order (each tile one bucket,
+// Forward ranges and launch order in one launch. One workgroup per group of
+// heads (the groups of k_work_order). The group's key-tile statistics go to
+// LDS. Where a head's key tiles are in layout order (each tile one bucket,
 // buckets non-decreasing, and within a bucket non-decreasing smallest
-// positions; this holds for every layout scfa_hash_layout_qk writes), the
-// rules of Algorithm 2 reduce to searches: start = first key tile whose
-// bucket reaches the query tile's, stop = first tile past its bucket, and
-// the tiles passing the causal test are a prefix of [start, stop), found by
-// a binary search. Otherwise (or for a query tile spanning buckets) the
-// thread scans the head's tiles one by one with the same rules. The ranges
-// are then counting-sorted by length as in k_work_order.
+// positions: every layout scfa_hash_layout_qk writes, and the compacted or
+// dense rows of the QK and dense modes, whose buckets are all 0), the rules
+// reduce to binary searches. Hash (Algorithm 2): start = first key tile
+// whose bucket reaches the query tile's, stop = first tile past its bucket,
+// and the tiles passing the causal test are a prefix of [start, stop). QK and
+// dense (Algorithm 1): end = the prefix of key tiles the query tile reaches.
+// Otherwise (or for a hash query tile spanning buckets) the thread scans the
+// head's tiles one by one with the same rules. The ranges are then
+// counting-sorted by length as in k_work_order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_fwd_table_order(const int4* __restrict__ qstats,
+__global__ __launch_bounds__(1024) void k_fwd_table_order(int mode, const int4* __restrict__ qstats,
                                                           const int4* __restrict__ kstats, int BH, int nQt, int nKt,
                                                           int G, int2* __restrict__ fwd, int32_t* __restrict__ tiles,
                                                           int32_t* __restrict__ order, const Reach rc) {
@@ -1037,7 +1038,24 @@ __global__ __launch_bounds__(1024) void k_fwd_table_order(const int4* __restrict
     const int qreach = q_reach(rc, qs.y);
     const int4* k = ks + hl * nKt;
     int start, end, cnt;
-    if (ordered[hl] && qs.z == qs.w) {
+    if (mode != SCFA_HASH) {
+      // Algorithm 1: key tiles [0, end), end = the tiles whose smallest
+      // position the query tile reaches (a prefix where smallest positions
+      // are in order, else counted one by one)
+      start = 0;
+      cnt = 0;
+      if (ordered[hl]) {
+        int lo = 0, hi = nKt;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (k[mid].x <= qreach) lo = mid + 1; else hi = mid;
+        }
+        cnt = lo;
+      } else {
+        for (int j = 0; j < nKt; ++j) cnt += k[j].x <= qreach;
+      }
+      end = cnt;
+    } else if (ordered[hl] && qs.z == qs.w) {
       // first tile whose bucket is >= the query bucket, first tile past it
       int lo = 0, hi = nKt;
       while (lo < hi) {
@@ -1428,7 +1446,7 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
   const int flags = take_flags(mode);
   if (!flags_ok(flags) || (mode != SCFA_DENSE && mode != SCFA_QK && mode != SCFA_HASH)) return SCFA_ERR_INVALID;
   const Reach rc = reach_of(flags);
-  if (!qstats || !kstats || !fwd_tab || !tiles) return SCFA_ERR_INVALID;
+  if (!qstats || !kstats || !tiles || (!fwd_tab && bwd_tab)) return SCFA_ERR_INVALID;
   if (mode != SCFA_DENSE && (!q_idx || !k_idx)) return SCFA_ERR_INVALID;
   if (mode == SCFA_HASH && (!q_bkt || !k_bkt)) return SCFA_ERR_INVALID;
   if (B < 1 || H < 1 || Tq < 1 || Tk < 1) return SCFA_ERR_INVALID;
@@ -1439,6 +1457,7 @@ int scfa_range_table(int mode, const int32_t* q_idx, const int32_t* k_idx, const
   hipLaunchKernelGGL(k_tile_stats, dim3(nQt + nKt, B * H), dim3(64), 0, stream, mode, q_idx, k_idx, q_bkt, k_bkt, Tq,
                      Tk, TqP, TkP, Bm, Bn, nQt, nKt, qstats, kstats, tiles);
   SCFA_RETURN_IF_LAUNCH_FAILED();
+  if (!fwd_tab) return SCFA_OK;  // statistics only (scfa_fwd_table_order builds the ranges)
   hipLaunchKernelGGL(k_fwd_table, dim3(ceil_div(nQt, kTabWaves), B * H), dim3(64 * kTabWaves), 0, stream, mode, qstats,
                      kstats, nQt, nKt, fwd_tab, tiles, rc);
   SCFA_RETURN_IF_LAUNCH_FAILED();
@@ -1488,7 +1507,7 @@ int scfa_work_order(const int32_t* tab, int B, int H, int ntiles, int span, int3
 int scfa_fwd_table_order(int mode, const int32_t* qstats, const int32_t* kstats, int B, int H, int nQt, int nKt,
                          int32_t* fwd_tab, int32_t* tiles, int32_t* order, hipStream_t stream) {
   const int flags = take_flags(mode);
-  if (!flags_ok(flags) || mode != SCFA_HASH) return SCFA_ERR_INVALID;
+  if (!flags_ok(flags) || (mode != SCFA_DENSE && mode != SCFA_QK && mode != SCFA_HASH)) return SCFA_ERR_INVALID;
   if (!qstats || !kstats || !fwd_tab || !tiles || !order) return SCFA_ERR_INVALID;
   if (B < 1 || H < 1 || nQt < 1 || nKt < 1 || nKt > kMaxOrderSpan) return SCFA_ERR_INVALID;
   const int BH = B * H;
@@ -1500,7 +1519,7 @@ int scfa_fwd_table_order(int mode, const int32_t* qstats, const int32_t* kstats,
     if (st != SCFA_OK) return st;
     return scfa_work_order(fwd_tab, B, H, nQt, nKt, order, stream);
   }
-  hipLaunchKernelGGL(k_fwd_table_order, dim3(G), dim3(1024), lds, stream, reinterpret_cast<const int4*>(qstats),
+  hipLaunchKernelGGL(k_fwd_table_order, dim3(G), dim3(1024), lds, stream, mode, reinterpret_cast<const int4*>(qstats),
                      reinterpret_cast<const int4*>(kstats), BH, nQt, nKt, G, reinterpret_cast<int2*>(fwd_tab), tiles,
                      order, reach_of(flags));
   SCFA_RETURN_IF_LAUNCH_FAILED();

@@ -256,8 +256,8 @@ def scfa_fwd_table(mode, qstats, kstats, fwd_tab, tiles, stream=None):
 
 
 def scfa_fwd_table_order(mode, qstats, kstats, fwd_tab, tiles, order, stream=None):
-    """Forward range table and its launch order in one launch (hash mode,
-    statistics of the bucket-aligned layout; tiles must be zero on entry)."""
+    """Forward range table and its launch order in one launch (tiles must be
+    zero on entry)."""
     B, H, nQt, _ = qstats.shape
     nKt = kstats.shape[2]
     _check(lib().scfa_fwd_table_order(mode, _p(qstats), _p(kstats), B, H, nQt, nKt, _p(fwd_tab), _p(tiles), _p(order),
@@ -766,12 +766,11 @@ class Plan:
         one launch); the backward table is built by backward()."""
         t = self.tab
         t.bwd_ready = False  # new forward ranges: backward() rebuilds the backward table
-        if self.mode == "hash" and self.two_side:  # the tile statistics come from the layout launch
-            scfa_fwd_table_order(SCFA_HASH | self.flags, t.qstats, t.kstats, t.fwd, t.tiles, t.fwd_order, stream)
-            return
-        scfa_range_table(_table_mode(self.mode) | self.flags, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B,
-                         self.H, self.Tq, self.Tk, t.Bm, t.Bn, t.qstats, t.kstats, t.fwd, None, t.tiles, stream)
-        scfa_work_order(t.fwd, t.kstats.shape[2], t.fwd_order, stream)
+        mode = _table_mode(self.mode) | self.flags
+        if not (self.mode == "hash" and self.two_side):  # else the tile statistics come from the layout launch
+            scfa_range_table(mode, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H, self.Tq, self.Tk,
+                             t.Bm, t.Bn, t.qstats, t.kstats, None, None, t.tiles, stream)  # statistics only
+        scfa_fwd_table_order(mode, t.qstats, t.kstats, t.fwd, t.tiles, t.fwd_order, stream)
 
     def forward(self, stream=None):
         forward(self.prepared(), self.tab, self.out_dtype, self.scale, self.O, self.lse, stream)

@@ -166,8 +166,12 @@ def test_invalid_arguments_rejected_without_gpu():
     assert L.scfa_work_order(dummy, 1, 1, 0, 8, dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_work_order(dummy, 1, 1, 8, 16384, dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_work_order(null, 1, 1, 8, 8, dummy, null) == scfa.SCFA_ERR_INVALID
-    # forward table and order in one launch: hash mode only, NULL outputs, bad sizes
-    assert L.scfa_fwd_table_order(1, dummy, dummy, 1, 1, 2, 2, dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    # forward table and order in one launch: bad mode, NULL outputs, bad sizes
+    assert L.scfa_fwd_table_order(7, dummy, dummy, 1, 1, 2, 2, dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_fwd_table_order(3, dummy, dummy, 1, 1, 2, 2, dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    # range table: statistics only (no forward table) cannot ask for a backward table
+    assert L.scfa_range_table(1, dummy, dummy, null, null, 1, 1, 8, 8, 128, 64, dummy, dummy, null, dummy, dummy,
+                              null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_fwd_table_order(2, dummy, dummy, 1, 1, 2, 2, dummy, dummy, null, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_fwd_table_order(2, dummy, dummy, 1, 1, 2, 16384, dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_fwd_table_order(2 | 48, dummy, dummy, 1, 1, 2, 2, dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID

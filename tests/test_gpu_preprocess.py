@@ -452,6 +452,58 @@ def test_full_size_preprocessing_bitexact(name):
     _tables_match(mode, pre, tab, pre.Tq, scfa.SCFA_TILE_M, scfa.SCFA_TILE_N, pre.q_bkt, pre.k_bkt, pre.Tk)
 
 
+def _qk_stats(rng, BH, nQt, nKt, ordered=True):
+    """Tile statistics shaped like the QK and dense modes' (buckets 0): real
+    tiles with ascending positions, then pad tiles; or, unordered, real tiles
+    with random positions."""
+    qs = np.empty((BH, nQt, 4), np.int32)
+    ks = np.empty((BH, nKt, 4), np.int32)
+    for st, n, pad, zw, rows in ((qs, nQt, oracle.Q_PAD, (2**31 - 1, -2**31), scfa.SCFA_TILE_M),
+                                 (ks, nKt, oracle.K_PAD, (2**31 - 1, 2**31 - 1), scfa.SCFA_TILE_N)):
+        for h in range(BH):
+            nreal = int(rng.integers(1, n + 1))
+            lo = np.sort(rng.integers(0, 40 * n * rows, nreal)) if ordered else rng.integers(0, 40 * n * rows, nreal)
+            st[h, :nreal, 0] = lo
+            st[h, :nreal, 1] = lo + rng.integers(0, 3 * rows, nreal)
+            st[h, :nreal, 2:] = 0
+            st[h, nreal:] = (pad, pad, zw[0], zw[1])
+    return qs, ks
+
+
+@pytest.mark.parametrize("case", [(1, 12, 64, 128, scfa.SCFA_QK), (2, 12, 64, 128, scfa.SCFA_QK | scfa.SCFA_STRICT),
+                                  (2, 4, 33, 70, scfa.SCFA_QK | scfa.SCFA_NONCAUSAL), (1, 3, 40, 1300, scfa.SCFA_QK),
+                                  (1, 2, 16, 32, scfa.SCFA_DENSE), (1, 5, 9, 1, scfa.SCFA_QK)],
+                         ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("kind", ["ordered", "random"])
+def test_fwd_table_order_qk_matches_two_launches(case, kind):
+    """The one-launch forward table and order in the QK and dense modes
+    (Algorithm 1) against scfa_fwd_table followed by scfa_work_order: the
+    same table and tile count bit for bit and a valid longest-first order,
+    on position-ordered statistics (the searched path) and on unordered ones
+    (the tile-by-tile count); (1, 3, 40, 1300) takes the two-launch
+    fallback."""
+    need_gpu()
+    B, H, nQt, nKt, mode = case
+    announce(f"fwd table + order qk {kind} {case}")
+    rng = np.random.default_rng(sum(case) + (5 if kind == "random" else 2))
+    qs, ks = _qk_stats(rng, B * H, nQt, nKt, ordered=(kind == "ordered"))
+    dev = torch.device("cuda:0")
+    qst = torch.from_numpy(qs).reshape(B, H, nQt, 4).to(dev)
+    kst = torch.from_numpy(ks).reshape(B, H, nKt, 4).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    ref_tab, ref_tiles, ref_order = (torch.empty((B, H, nQt, 2), **i32), torch.zeros((B, H), **i32),
+                                     torch.empty((B * H * nQt,), **i32))
+    scfa.scfa_fwd_table(mode, qst, kst, ref_tab, ref_tiles)
+    scfa.scfa_work_order(ref_tab, nKt, ref_order)
+    tab, tiles, order = (torch.empty((B, H, nQt, 2), **i32), torch.zeros((B, H), **i32),
+                         torch.empty((B * H * nQt,), **i32))
+    scfa.scfa_fwd_table_order(mode, qst, kst, tab, tiles, order)
+    torch.cuda.synchronize()
+    assert torch.equal(tab, ref_tab)
+    assert torch.equal(tiles, ref_tiles)
+    check_order(order.cpu().numpy(), tab.cpu().numpy())
+
+
 @pytest.mark.parametrize("w", [WORKLOADS["hash_bf16_t16384_nb16"], small("hash", 1, 2, 700, dtype="f32", nb=24, seed=81),
                                small("hash", 2, 2, 1000, nb=64, seed=82), small("hash", 1, 3, 1, nb=16, seed=83)],
                          ids=lambda w: w.name)
