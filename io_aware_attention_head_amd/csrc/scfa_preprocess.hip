@@ -26,9 +26,8 @@ namespace {
 // QK-drop: counts per 64-position chunk, then an exclusive scan per head.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void k_qk_chunk_counts(const uint8_t* __restrict__ keep, int T, int H, int nC,
-                                                         int32_t* __restrict__ chunk, int32_t* __restrict__ max_count) {
-  const int c = blockIdx.x, b = blockIdx.y;
+__device__ inline void qk_chunk_counts(const uint8_t* __restrict__ keep, int T, int H, int nC, int c, int b,
+                                       int32_t* __restrict__ chunk, int32_t* __restrict__ max_count) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (c == 0 && b == 0 && threadIdx.x == 0) *max_count = 0;
   const int t = c * SCFA_COUNT_CHUNK + lane;
@@ -39,10 +38,14 @@ __global__ __launch_bounds__(256) void k_qk_chunk_counts(const uint8_t* __restri
   }
 }
 
-__global__ __launch_bounds__(256) void k_qk_scan(int32_t* __restrict__ chunk, int nC, int32_t* __restrict__ count,
-                                                 int32_t* __restrict__ max_count) {
+__global__ __launch_bounds__(256) void k_qk_chunk_counts(const uint8_t* __restrict__ keep, int T, int H, int nC,
+                                                         int32_t* __restrict__ chunk, int32_t* __restrict__ max_count) {
+  qk_chunk_counts(keep, T, H, nC, blockIdx.x, blockIdx.y, chunk, max_count);
+}
+
+__device__ inline void qk_scan(int32_t* __restrict__ chunk, int nC, int bh, int32_t* __restrict__ count,
+                               int32_t* __restrict__ max_count) {
   __shared__ int32_t wsum[4];
-  const int bh = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int32_t* p = chunk + static_cast<size_t>(bh) * nC;
   int carry = 0;
@@ -70,16 +73,19 @@ __global__ __launch_bounds__(256) void k_qk_scan(int32_t* __restrict__ chunk, in
   }
 }
 
+__global__ __launch_bounds__(256) void k_qk_scan(int32_t* __restrict__ chunk, int nC, int32_t* __restrict__ count,
+                                                 int32_t* __restrict__ max_count) {
+  qk_scan(chunk, nC, blockIdx.x, count, max_count);
+}
+
 // One workgroup per (64-position chunk, batch), all heads: the keep bytes and
 // the input rows of the chunk are one contiguous block of memory.
 template <int ESZ>
-__global__ __launch_bounds__(256) void k_qk_compact(const uint8_t* __restrict__ x, const uint8_t* __restrict__ keep,
-                                                    const int32_t* __restrict__ count,
-                                                    const int32_t* __restrict__ chunk_off, int T, int H, int D, int Tc,
-                                                    int nC, int32_t pad, uint8_t* __restrict__ xc,
-                                                    int32_t* __restrict__ idx, int32_t* dev_err) {
+__device__ inline void qk_compact(const uint8_t* __restrict__ x, const uint8_t* __restrict__ keep,
+                                  const int32_t* __restrict__ count, const int32_t* __restrict__ chunk_off, int T,
+                                  int H, int D, int Tc, int nC, int c, int b, int32_t pad, uint8_t* __restrict__ xc,
+                                  int32_t* __restrict__ idx, int32_t* dev_err) {
   extern __shared__ int32_t rank[];  // [H][64]
-  const int c = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int h = w; h < H; h += 4) {
     const int bh = b * H + h;
@@ -136,6 +142,47 @@ __global__ __launch_bounds__(256) void k_qk_compact(const uint8_t* __restrict__ 
       reinterpret_cast<uint4*>(dst)[kk] = z;
     }
   }
+}
+
+template <int ESZ>
+__global__ __launch_bounds__(256) void k_qk_compact(const uint8_t* __restrict__ x, const uint8_t* __restrict__ keep,
+                                                    const int32_t* __restrict__ count,
+                                                    const int32_t* __restrict__ chunk_off, int T, int H, int D, int Tc,
+                                                    int nC, int32_t pad, uint8_t* __restrict__ xc,
+                                                    int32_t* __restrict__ idx, int32_t* dev_err) {
+  qk_compact<ESZ>(x, keep, count, chunk_off, T, H, D, Tc, nC, blockIdx.x, blockIdx.y, pad, xc, idx, dev_err);
+}
+
+// Queries and keys in one launch each (grid dimension z selects the side;
+// the grid covers the longer side, and the other side's extra workgroups
+// return at once): counts, prefix sums and index compaction, the same
+// outputs as the one-side kernels.
+struct QkSide {
+  const uint8_t* keep;
+  int T, nC, nCx, Tc;  // tokens, count chunks, compaction chunks (covering max(T, Tc)), compacted length
+  int32_t pad;
+  int32_t* chunk;
+  int32_t* count;
+  int32_t* max_count;
+  int32_t* idx;
+};
+
+__global__ __launch_bounds__(256) void k_qk_chunk_counts_qk(QkSide s0, QkSide s1, int H) {
+  const QkSide& s = blockIdx.z == 0 ? s0 : s1;
+  if (static_cast<int>(blockIdx.x) >= s.nC) return;
+  qk_chunk_counts(s.keep, s.T, H, s.nC, blockIdx.x, blockIdx.y, s.chunk, s.max_count);
+}
+
+__global__ __launch_bounds__(256) void k_qk_scan_qk(QkSide s0, QkSide s1) {
+  const QkSide& s = blockIdx.z == 0 ? s0 : s1;
+  qk_scan(s.chunk, s.nC, blockIdx.x, s.count, s.max_count);
+}
+
+__global__ __launch_bounds__(256) void k_qk_compact_qk(QkSide s0, QkSide s1, int H, int32_t* dev_err) {
+  const QkSide& s = blockIdx.z == 0 ? s0 : s1;
+  if (static_cast<int>(blockIdx.x) >= s.nCx) return;
+  qk_compact<2>(nullptr, s.keep, s.count, s.chunk, s.T, H, 64, s.Tc, s.nC, blockIdx.x, blockIdx.y, s.pad, nullptr,
+                s.idx, dev_err);
 }
 
 // ---------------------------------------------------------------------------
@@ -1222,6 +1269,42 @@ int scfa_qk_count(const uint8_t* keep, int B, int T, int H, int32_t* count, int3
   hipLaunchKernelGGL(k_qk_chunk_counts, dim3(nC, B), dim3(256), 0, stream, keep, T, H, nC, chunk_offsets, max_count);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   hipLaunchKernelGGL(k_qk_scan, dim3(B * H), dim3(256), 0, stream, chunk_offsets, nC, count, max_count);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+int scfa_qk_index_qk(const uint8_t* keep_q, const uint8_t* keep_k, int B, int T, int T_kv, int H, int Tq, int Tk,
+                     int32_t* count_q, int32_t* count_k, int32_t* max_count, int32_t* chunk_offsets_q,
+                     int32_t* chunk_offsets_k, int32_t* q_idx, int32_t* k_idx, int32_t* dev_err, hipStream_t stream) {
+  if (!keep_q || !keep_k || !count_q || !count_k || !max_count || !chunk_offsets_q || !chunk_offsets_k || !q_idx ||
+      !k_idx)
+    return SCFA_ERR_INVALID;
+  if (B < 1 || T < 1 || T_kv < 1 || H < 1 || H > 128) return SCFA_ERR_INVALID;
+  for (int tc : {Tq, Tk})
+    if (tc < SCFA_ROW_ALIGN || tc % SCFA_ROW_ALIGN) return SCFA_ERR_INVALID;
+  auto side = [&](const uint8_t* keep, int t, int tc, int32_t pad, int32_t* chunk, int32_t* count, int32_t* mx,
+                  int32_t* idx) {
+    QkSide sd;
+    sd.keep = keep;
+    sd.T = t;
+    sd.nC = ceil_div(t, SCFA_COUNT_CHUNK);
+    sd.nCx = ceil_div(t > tc ? t : tc, SCFA_COUNT_CHUNK);
+    sd.Tc = tc;
+    sd.pad = pad;
+    sd.chunk = chunk;
+    sd.count = count;
+    sd.max_count = mx;
+    sd.idx = idx;
+    return sd;
+  };
+  const QkSide sq = side(keep_q, T, Tq, SCFA_Q_PAD, chunk_offsets_q, count_q, max_count, q_idx);
+  const QkSide sk = side(keep_k, T_kv, Tk, SCFA_K_PAD, chunk_offsets_k, count_k, max_count + 1, k_idx);
+  hipLaunchKernelGGL(k_qk_chunk_counts_qk, dim3(max(sq.nC, sk.nC), B, 2), dim3(256), 0, stream, sq, sk, H);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  hipLaunchKernelGGL(k_qk_scan_qk, dim3(B * H, 1, 2), dim3(256), 0, stream, sq, sk);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  const size_t lds = static_cast<size_t>(H) * 64 * sizeof(int32_t);
+  hipLaunchKernelGGL(k_qk_compact_qk, dim3(max(sq.nCx, sk.nCx), B, 2), dim3(256), lds, stream, sq, sk, H, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }

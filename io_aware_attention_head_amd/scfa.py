@@ -62,6 +62,7 @@ _SIGS = {
     "scfa_count_visible": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_work_order": (_i, [_vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_fwd_table_order": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "scfa_qk_index_qk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_qk_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                                 _vp, _vp, _vp]),
     "scfa_hash_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
@@ -160,6 +161,19 @@ def scfa_qk_compact(x, keep, count, chunk_offsets, Tc, pad_idx, x_c, idx_c, dev_
     dt = _dt(x) if x is not None else SCFA_BF16
     _check(lib().scfa_qk_compact(dt, _p(x), _p(keep), _p(count), _p(chunk_offsets), B, T, H, D, Tc, pad_idx, _p(x_c),
                                  _p(idx_c), _p(dev_err), _stream(stream, keep)), "scfa_qk_compact")
+
+
+def scfa_qk_index_qk(keep_q, keep_k, Tq, Tk, count_q, count_k, max_count, chunk_offsets_q, chunk_offsets_k, q_idx,
+                     k_idx, dev_err=None, stream=None):
+    """Index compaction of the queries and of the keys in three launches
+    (counts, prefix sums, index arrays of both sides)."""
+    B, T, H = keep_q.shape
+    T_kv = keep_k.shape[1]
+    if keep_k.shape[0] != B or keep_k.shape[2] != H:
+        raise ScfaError("keep_q and keep_k must share B and H")
+    _check(lib().scfa_qk_index_qk(_p(keep_q), _p(keep_k), B, T, T_kv, H, Tq, Tk, _p(count_q), _p(count_k),
+                                  _p(max_count), _p(chunk_offsets_q), _p(chunk_offsets_k), _p(q_idx), _p(k_idx),
+                                  _p(dev_err), _stream(stream, keep_q)), "scfa_qk_index_qk")
 
 
 def scfa_hash_bucket(x, R, nb, bucket, stream=None):
@@ -683,7 +697,8 @@ class Plan:
             self.Tq = self.Tk = Tc
             nC = [(n + SCFA_COUNT_CHUNK - 1) // SCFA_COUNT_CHUNK for n in (T, Tkv)]
             self.cnt = [e((B, H)), e((B, H))]
-            self.mx = [e((1,)), e((1,))]
+            self.mx2 = e((2,))  # max counts of the query and key sides
+            self.mx = [self.mx2[0:1], self.mx2[1:2]]
             self.choff = [e((B, H, nC[0])), e((B, H, nC[1]))]
         elif mode == "hash":
             self.Tq = scfa_hash_segment_rows(T, self.nbs, SCFA_TILE_M)
@@ -752,12 +767,10 @@ class Plan:
                             self.dev_err, t.qstats, t.kstats, t.tiles, stream)
 
     def compact(self, q, k, keep_q, keep_k, stream=None):
-        scfa_qk_count(keep_q, self.cnt[0], self.mx[0], self.choff[0], stream)
-        scfa_qk_count(keep_k, self.cnt[1], self.mx[1], self.choff[1], stream)
-        scfa_qk_compact(q, keep_q, self.cnt[0], self.choff[0], self.Tq, SCFA_Q_PAD, None, self.q_idx,
-                        self.dev_err, stream)
-        scfa_qk_compact(k, keep_k, self.cnt[1], self.choff[1], self.Tk, SCFA_K_PAD, None, self.k_idx,
-                        self.dev_err, stream)
+        """Counts, prefix sums and index arrays of both sides (three launches;
+        the operands are read through the index arrays, no compacted copies)."""
+        scfa_qk_index_qk(keep_q, keep_k, self.Tq, self.Tk, self.cnt[0], self.cnt[1], self.mx2, self.choff[0],
+                         self.choff[1], self.q_idx, self.k_idx, self.dev_err, stream)
 
     def tables(self, stream=None):
         """Forward ranges and the launch order, after the tile statistics

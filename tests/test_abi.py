@@ -166,6 +166,20 @@ def test_invalid_arguments_rejected_without_gpu():
     assert L.scfa_work_order(dummy, 1, 1, 0, 8, dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_work_order(dummy, 1, 1, 8, 16384, dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_work_order(null, 1, 1, 8, 8, dummy, null) == scfa.SCFA_ERR_INVALID
+    # two-side QK index compaction: NULL pointers, compacted lengths not multiples of 128, too many heads
+    qk = [dummy] * 2 + [1, 8, 8, 2, 128, 128] + [dummy] * 7 + [null, null]
+    bad = list(qk)
+    bad[0] = null
+    assert L.scfa_qk_index_qk(*bad) == scfa.SCFA_ERR_INVALID
+    bad = list(qk)
+    bad[6] = 100
+    assert L.scfa_qk_index_qk(*bad) == scfa.SCFA_ERR_INVALID
+    bad = list(qk)
+    bad[5] = 129
+    assert L.scfa_qk_index_qk(*bad) == scfa.SCFA_ERR_INVALID
+    bad = list(qk)
+    bad[14] = null
+    assert L.scfa_qk_index_qk(*bad) == scfa.SCFA_ERR_INVALID
     # forward table and order in one launch: bad mode, NULL outputs, bad sizes
     assert L.scfa_fwd_table_order(7, dummy, dummy, 1, 1, 2, 2, dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_fwd_table_order(3, dummy, dummy, 1, 1, 2, 2, dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID

@@ -607,3 +607,39 @@ def test_fwd_table_order_matches_two_launches(case, kind):
     assert torch.equal(tab, ref_tab)
     assert torch.equal(tiles, ref_tiles)
     check_order(order.cpu().numpy(), tab.cpu().numpy())
+
+
+@pytest.mark.parametrize("case", [(2, 8192, 8192, 12, 0.5, 8192, 8192), (1, 300, 777, 3, 0.6, 384, 896),
+                                  (1, 1, 1, 2, 1.0, 128, 128), (2, 1000, 200, 5, 0.0, 1024, 256),
+                                  (1, 777, 300, 16, 0.9, 896, 384), (2, 100, 130, 4, 0.7, 512, 256)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_qk_index_two_sides_matches_one_side_calls(case):
+    """The two-side index compaction against scfa_qk_count and scfa_qk_compact
+    (index only) per side: counts, max counts, chunk offsets and index arrays
+    bit for bit, with compacted lengths above the kept counts and above T."""
+    need_gpu()
+    B, T, Tkv, H, p, Tq, Tk = case
+    announce(f"qk index two sides {case}")
+    g = torch.Generator().manual_seed(sum(case[:4]))
+    dev = torch.device("cuda:0")
+    keep_q = (torch.rand((B, T, H), generator=g) < p).to(torch.uint8).to(dev)
+    keep_k = (torch.rand((B, Tkv, H), generator=g) < p).to(torch.uint8).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    nCq, nCk = (T + 63) // 64, (Tkv + 63) // 64
+    ref = {"cq": torch.empty((B, H), **i32), "ck": torch.empty((B, H), **i32), "mq": torch.empty((1,), **i32),
+           "mk": torch.empty((1,), **i32), "oq": torch.empty((B, H, nCq), **i32), "ok": torch.empty((B, H, nCk), **i32),
+           "iq": torch.empty((B, H, Tq), **i32), "ik": torch.empty((B, H, Tk), **i32)}
+    scfa.scfa_qk_count(keep_q, ref["cq"], ref["mq"], ref["oq"])
+    scfa.scfa_qk_count(keep_k, ref["ck"], ref["mk"], ref["ok"])
+    scfa.scfa_qk_compact(None, keep_q, ref["cq"], ref["oq"], Tq, scfa.SCFA_Q_PAD, None, ref["iq"])
+    scfa.scfa_qk_compact(None, keep_k, ref["ck"], ref["ok"], Tk, scfa.SCFA_K_PAD, None, ref["ik"])
+    got = {k: torch.full_like(v, -7) for k, v in ref.items()}
+    mx = torch.full((2,), -7, **i32)
+    err = torch.zeros((1,), **i32)
+    scfa.scfa_qk_index_qk(keep_q, keep_k, Tq, Tk, got["cq"], got["ck"], mx, got["oq"], got["ok"], got["iq"], got["ik"],
+                          err)
+    torch.cuda.synchronize()
+    for name in ("cq", "ck", "oq", "ok", "iq", "ik"):
+        assert torch.equal(got[name], ref[name]), name
+    assert int(mx[0]) == int(ref["mq"][0]) and int(mx[1]) == int(ref["mk"][0])
+    assert int(err.item()) == 0
