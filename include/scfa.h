@@ -133,24 +133,27 @@ int scfa_qk_compact(int dtype, const void* x, const uint8_t* keep, const int32_t
                     const int32_t* chunk_offsets, int B, int T, int H, int D, int Tc, int32_t pad_idx,
                     void* x_c, int32_t* idx_c, int32_t* dev_err, hipStream_t stream);
 
-/* The index compaction of the queries and of the keys, three launches for
- * both sides (grid dimension z selects the side): the outputs of
- * scfa_qk_count on keep_q and on keep_k, then of scfa_qk_compact with
- * x = x_c = NULL (index only), pad_idx SCFA_Q_PAD for the queries and
- * SCFA_K_PAD for the keys, bit for bit. Same definition and citation.
+/* The index compaction of the queries and of the keys, two launches for
+ * both sides (grid dimension z selects the side): counts, max counts and
+ * index arrays bit for bit as scfa_qk_count on keep_q and on keep_k
+ * followed by scfa_qk_compact with x = x_c = NULL (index only), pad_idx
+ * SCFA_Q_PAD for the queries and SCFA_K_PAD for the keys. Same definition
+ * and citation. The second launch sums the chunk counts before each chunk
+ * itself, so no prefix-sum array is written.
  *  keep_q (B, T, H), keep_k (B, T_kv, H) uint8, nonzero = kept.
  *  Tq, Tk            compacted lengths of the two sides (multiples of
  *                    SCFA_ROW_ALIGN, each >= its side's max count).
  *  count_q, count_k  out (B, H) int32.
  *  max_count         out (2) int32: max over heads of the query side, then
  *                    of the key side.
- *  chunk_offsets_q   out (B, H, ceil(T/64)); chunk_offsets_k out
- *                    (B, H, ceil(T_kv/64)): as scfa_qk_count.
+ *  chunk_counts_q    workspace (B, H, ceil(T/64)) int32, chunk_counts_k
+ *                    (B, H, ceil(T_kv/64)): kept tokens per 64-position
+ *                    chunk (left there on return).
  *  q_idx, k_idx      out (B, H, Tq), (B, H, Tk) int32.
  *  dev_err           as scfa_qk_compact (may be NULL).                      */
 int scfa_qk_index_qk(const uint8_t* keep_q, const uint8_t* keep_k, int B, int T, int T_kv, int H, int Tq, int Tk,
-                     int32_t* count_q, int32_t* count_k, int32_t* max_count, int32_t* chunk_offsets_q,
-                     int32_t* chunk_offsets_k, int32_t* q_idx, int32_t* k_idx, int32_t* dev_err, hipStream_t stream);
+                     int32_t* count_q, int32_t* count_k, int32_t* max_count, int32_t* chunk_counts_q,
+                     int32_t* chunk_counts_k, int32_t* q_idx, int32_t* k_idx, int32_t* dev_err, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Hash-sparse preprocessing.

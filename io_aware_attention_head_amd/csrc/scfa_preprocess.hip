@@ -153,15 +153,16 @@ __global__ __launch_bounds__(256) void k_qk_compact(const uint8_t* __restrict__ 
   qk_compact<ESZ>(x, keep, count, chunk_off, T, H, D, Tc, nC, blockIdx.x, blockIdx.y, pad, xc, idx, dev_err);
 }
 
-// Queries and keys in one launch each (grid dimension z selects the side;
-// the grid covers the longer side, and the other side's extra workgroups
-// return at once): counts, prefix sums and index compaction, the same
-// outputs as the one-side kernels.
+// Queries and keys in two launches (grid dimension z selects the side; the
+// grid covers the longer side, and the other side's extra workgroups return
+// at once): the chunk counts, then the index arrays, whose workgroups sum
+// the chunk counts before their own chunk themselves (no scan launch). The
+// index arrays, counts and max counts equal those of the one-side calls.
 struct QkSide {
   const uint8_t* keep;
   int T, nC, nCx, Tc;  // tokens, count chunks, compaction chunks (covering max(T, Tc)), compacted length
   int32_t pad;
-  int32_t* chunk;
+  int32_t* chunk;  // per-chunk kept counts
   int32_t* count;
   int32_t* max_count;
   int32_t* idx;
@@ -173,16 +174,43 @@ __global__ __launch_bounds__(256) void k_qk_chunk_counts_qk(QkSide s0, QkSide s1
   qk_chunk_counts(s.keep, s.T, H, s.nC, blockIdx.x, blockIdx.y, s.chunk, s.max_count);
 }
 
-__global__ __launch_bounds__(256) void k_qk_scan_qk(QkSide s0, QkSide s1) {
+__global__ __launch_bounds__(256) void k_qk_index_qk(QkSide s0, QkSide s1, int H, int32_t* dev_err) {
   const QkSide& s = blockIdx.z == 0 ? s0 : s1;
-  qk_scan(s.chunk, s.nC, blockIdx.x, s.count, s.max_count);
-}
-
-__global__ __launch_bounds__(256) void k_qk_compact_qk(QkSide s0, QkSide s1, int H, int32_t* dev_err) {
-  const QkSide& s = blockIdx.z == 0 ? s0 : s1;
-  if (static_cast<int>(blockIdx.x) >= s.nCx) return;
-  qk_compact<2>(nullptr, s.keep, s.count, s.chunk, s.T, H, 64, s.Tc, s.nC, blockIdx.x, blockIdx.y, s.pad, nullptr,
-                s.idx, dev_err);
+  const int c = blockIdx.x, b = blockIdx.y;
+  if (c >= s.nCx) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int h = w; h < H; h += 4) {
+    const int bh = b * H + h;
+    // kept tokens before this chunk, and in the whole head
+    const int32_t* cc = s.chunk + static_cast<size_t>(bh) * s.nC;
+    int pre = 0, tot = 0;
+    for (int i = lane; i < s.nC; i += 64) {
+      const int v = cc[i];
+      tot += v;
+      pre += i < c ? v : 0;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      pre += __shfl_xor(pre, o);
+      tot += __shfl_xor(tot, o);
+    }
+    if (c < s.nC) {
+      const int t = c * SCFA_COUNT_CHUNK + lane;
+      const bool f = t < s.T && s.keep[(static_cast<size_t>(b) * s.T + t) * H + h] != 0;
+      const uint64_t m = __ballot(f);
+      if (f) {
+        const int r = pre + lanes_below(m);
+        if (r < s.Tc) s.idx[static_cast<size_t>(bh) * s.Tc + r] = t;
+        else set_dev_err(dev_err, SCFA_DEVERR_COUNT_EXCEEDS_TC);
+      }
+    }
+    const int pr = tot + c * SCFA_COUNT_CHUNK + lane;
+    if (pr < s.Tc) s.idx[static_cast<size_t>(bh) * s.Tc + pr] = s.pad;
+    if (c == 0 && lane == 0) {
+      s.count[bh] = tot;
+      atomicMax(s.max_count, tot);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1274,9 +1302,9 @@ int scfa_qk_count(const uint8_t* keep, int B, int T, int H, int32_t* count, int3
 }
 
 int scfa_qk_index_qk(const uint8_t* keep_q, const uint8_t* keep_k, int B, int T, int T_kv, int H, int Tq, int Tk,
-                     int32_t* count_q, int32_t* count_k, int32_t* max_count, int32_t* chunk_offsets_q,
-                     int32_t* chunk_offsets_k, int32_t* q_idx, int32_t* k_idx, int32_t* dev_err, hipStream_t stream) {
-  if (!keep_q || !keep_k || !count_q || !count_k || !max_count || !chunk_offsets_q || !chunk_offsets_k || !q_idx ||
+                     int32_t* count_q, int32_t* count_k, int32_t* max_count, int32_t* chunk_counts_q,
+                     int32_t* chunk_counts_k, int32_t* q_idx, int32_t* k_idx, int32_t* dev_err, hipStream_t stream) {
+  if (!keep_q || !keep_k || !count_q || !count_k || !max_count || !chunk_counts_q || !chunk_counts_k || !q_idx ||
       !k_idx)
     return SCFA_ERR_INVALID;
   if (B < 1 || T < 1 || T_kv < 1 || H < 1 || H > 128) return SCFA_ERR_INVALID;
@@ -1297,14 +1325,11 @@ int scfa_qk_index_qk(const uint8_t* keep_q, const uint8_t* keep_k, int B, int T,
     sd.idx = idx;
     return sd;
   };
-  const QkSide sq = side(keep_q, T, Tq, SCFA_Q_PAD, chunk_offsets_q, count_q, max_count, q_idx);
-  const QkSide sk = side(keep_k, T_kv, Tk, SCFA_K_PAD, chunk_offsets_k, count_k, max_count + 1, k_idx);
+  const QkSide sq = side(keep_q, T, Tq, SCFA_Q_PAD, chunk_counts_q, count_q, max_count, q_idx);
+  const QkSide sk = side(keep_k, T_kv, Tk, SCFA_K_PAD, chunk_counts_k, count_k, max_count + 1, k_idx);
   hipLaunchKernelGGL(k_qk_chunk_counts_qk, dim3(max(sq.nC, sk.nC), B, 2), dim3(256), 0, stream, sq, sk, H);
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_qk_scan_qk, dim3(B * H, 1, 2), dim3(256), 0, stream, sq, sk);
-  SCFA_RETURN_IF_LAUNCH_FAILED();
-  const size_t lds = static_cast<size_t>(H) * 64 * sizeof(int32_t);
-  hipLaunchKernelGGL(k_qk_compact_qk, dim3(max(sq.nCx, sk.nCx), B, 2), dim3(256), lds, stream, sq, sk, H, dev_err);
+  hipLaunchKernelGGL(k_qk_index_qk, dim3(max(sq.nCx, sk.nCx), B, 2), dim3(256), 0, stream, sq, sk, H, dev_err);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }

@@ -163,16 +163,16 @@ def scfa_qk_compact(x, keep, count, chunk_offsets, Tc, pad_idx, x_c, idx_c, dev_
                                  _p(idx_c), _p(dev_err), _stream(stream, keep)), "scfa_qk_compact")
 
 
-def scfa_qk_index_qk(keep_q, keep_k, Tq, Tk, count_q, count_k, max_count, chunk_offsets_q, chunk_offsets_k, q_idx,
+def scfa_qk_index_qk(keep_q, keep_k, Tq, Tk, count_q, count_k, max_count, chunk_counts_q, chunk_counts_k, q_idx,
                      k_idx, dev_err=None, stream=None):
-    """Index compaction of the queries and of the keys in three launches
-    (counts, prefix sums, index arrays of both sides)."""
+    """Index compaction of the queries and of the keys in two launches
+    (counts and index arrays of both sides; the chunk counts are workspace)."""
     B, T, H = keep_q.shape
     T_kv = keep_k.shape[1]
     if keep_k.shape[0] != B or keep_k.shape[2] != H:
         raise ScfaError("keep_q and keep_k must share B and H")
     _check(lib().scfa_qk_index_qk(_p(keep_q), _p(keep_k), B, T, T_kv, H, Tq, Tk, _p(count_q), _p(count_k),
-                                  _p(max_count), _p(chunk_offsets_q), _p(chunk_offsets_k), _p(q_idx), _p(k_idx),
+                                  _p(max_count), _p(chunk_counts_q), _p(chunk_counts_k), _p(q_idx), _p(k_idx),
                                   _p(dev_err), _stream(stream, keep_q)), "scfa_qk_index_qk")
 
 
@@ -767,8 +767,8 @@ class Plan:
                             self.dev_err, t.qstats, t.kstats, t.tiles, stream)
 
     def compact(self, q, k, keep_q, keep_k, stream=None):
-        """Counts, prefix sums and index arrays of both sides (three launches;
-        the operands are read through the index arrays, no compacted copies)."""
+        """Counts and index arrays of both sides (two launches; the operands
+        are read through the index arrays, no compacted copies)."""
         scfa_qk_index_qk(keep_q, keep_k, self.Tq, self.Tk, self.cnt[0], self.cnt[1], self.mx2, self.choff[0],
                          self.choff[1], self.q_idx, self.k_idx, self.dev_err, stream)
 

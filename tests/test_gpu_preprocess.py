@@ -615,8 +615,8 @@ def test_fwd_table_order_matches_two_launches(case, kind):
                          ids=lambda c: "x".join(map(str, c)))
 def test_qk_index_two_sides_matches_one_side_calls(case):
     """The two-side index compaction against scfa_qk_count and scfa_qk_compact
-    (index only) per side: counts, max counts, chunk offsets and index arrays
-    bit for bit, with compacted lengths above the kept counts and above T."""
+    (index only) per side: counts, max counts and index arrays bit for bit,
+    with compacted lengths above the kept counts and above T."""
     need_gpu()
     B, T, Tkv, H, p, Tq, Tk = case
     announce(f"qk index two sides {case}")
@@ -639,7 +639,7 @@ def test_qk_index_two_sides_matches_one_side_calls(case):
     scfa.scfa_qk_index_qk(keep_q, keep_k, Tq, Tk, got["cq"], got["ck"], mx, got["oq"], got["ok"], got["iq"], got["ik"],
                           err)
     torch.cuda.synchronize()
-    for name in ("cq", "ck", "oq", "ok", "iq", "ik"):
+    for name in ("cq", "ck", "iq", "ik"):
         assert torch.equal(got[name], ref[name]), name
     assert int(mx[0]) == int(ref["mq"][0]) and int(mx[1]) == int(ref["mk"][0])
     assert int(err.item()) == 0
