@@ -150,10 +150,19 @@ int scfa_qk_compact(int dtype, const void* x, const uint8_t* keep, const int32_t
  *                    (B, H, ceil(T_kv/64)): kept tokens per 64-position
  *                    chunk (left there on return).
  *  q_idx, k_idx      out (B, H, Tq), (B, H, Tk) int32.
+ *  qstats, kstats, tiles
+ *                    optional (all three or none): out (B, H, Tq/SCFA_TILE_M,
+ *                    4), (B, H, Tk/SCFA_TILE_N, 4) and (B, H) -- the tile
+ *                    statistics and zeroed processed-tile count that
+ *                    scfa_range_table(SCFA_QK, q_idx, k_idx, ..., Tq, Tk,
+ *                    SCFA_TILE_M, SCFA_TILE_N, ...) computes over these index
+ *                    arrays (every row, pads included), bit for bit, for
+ *                    scfa_fwd_table_order to take next.
  *  dev_err           as scfa_qk_compact (may be NULL).                      */
 int scfa_qk_index_qk(const uint8_t* keep_q, const uint8_t* keep_k, int B, int T, int T_kv, int H, int Tq, int Tk,
                      int32_t* count_q, int32_t* count_k, int32_t* max_count, int32_t* chunk_counts_q,
-                     int32_t* chunk_counts_k, int32_t* q_idx, int32_t* k_idx, int32_t* dev_err, hipStream_t stream);
+                     int32_t* chunk_counts_k, int32_t* q_idx, int32_t* k_idx, int32_t* qstats, int32_t* kstats,
+                     int32_t* tiles, int32_t* dev_err, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Hash-sparse preprocessing.

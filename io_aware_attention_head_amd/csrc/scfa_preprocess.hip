@@ -166,6 +166,8 @@ struct QkSide {
   int32_t* count;
   int32_t* max_count;
   int32_t* idx;
+  int32_t* stats;  // optional (B, H, Tc / bs, 4) tile statistics over all Tc rows
+  int bs;          // rows per tile of stats
 };
 
 __global__ __launch_bounds__(256) void k_qk_chunk_counts_qk(QkSide s0, QkSide s1, int H) {
@@ -174,7 +176,8 @@ __global__ __launch_bounds__(256) void k_qk_chunk_counts_qk(QkSide s0, QkSide s1
   qk_chunk_counts(s.keep, s.T, H, s.nC, blockIdx.x, blockIdx.y, s.chunk, s.max_count);
 }
 
-__global__ __launch_bounds__(256) void k_qk_index_qk(QkSide s0, QkSide s1, int H, int32_t* dev_err) {
+__global__ __launch_bounds__(256) void k_qk_index_qk(QkSide s0, QkSide s1, int H, int32_t* dev_err,
+                                                     int32_t* tiles) {
   const QkSide& s = blockIdx.z == 0 ? s0 : s1;
   const int c = blockIdx.x, b = blockIdx.y;
   if (c >= s.nCx) return;
@@ -194,21 +197,53 @@ __global__ __launch_bounds__(256) void k_qk_index_qk(QkSide s0, QkSide s1, int H
       pre += __shfl_xor(pre, o);
       tot += __shfl_xor(tot, o);
     }
+    // Tile statistics of the compacted rows (min and max position over all
+    // Tc rows of a tile, pads included; buckets 0), as k_tile_stats gives
+    // them: real rows come first in ascending position, then the pads, so
+    // the first row of a tile gives its minimum (the query pad -1 where the
+    // tile holds a pad) and its last real row, or a pad, its maximum. Each
+    // field has exactly one writer.
+    int32_t* st = s.stats ? s.stats + static_cast<size_t>(bh) * (s.Tc / s.bs) * 4 : nullptr;
+    const bool qside = s.pad == SCFA_Q_PAD;
     if (c < s.nC) {
       const int t = c * SCFA_COUNT_CHUNK + lane;
       const bool f = t < s.T && s.keep[(static_cast<size_t>(b) * s.T + t) * H + h] != 0;
       const uint64_t m = __ballot(f);
       if (f) {
         const int r = pre + lanes_below(m);
-        if (r < s.Tc) s.idx[static_cast<size_t>(bh) * s.Tc + r] = t;
-        else set_dev_err(dev_err, SCFA_DEVERR_COUNT_EXCEEDS_TC);
+        if (r < s.Tc) {
+          s.idx[static_cast<size_t>(bh) * s.Tc + r] = t;
+          if (st) {
+            const int i = r / s.bs;
+            const bool has_pad = tot < (i + 1) * s.bs;
+            if (r == i * s.bs) {  // first row: the minimum
+              st[4 * i + 0] = (qside && has_pad) ? SCFA_Q_PAD : t;
+              st[4 * i + 2] = 0;
+              st[4 * i + 3] = 0;
+            }
+            if (r == min((i + 1) * s.bs, tot) - 1)  // last real row: the maximum
+              st[4 * i + 1] = (!qside && has_pad) ? SCFA_K_PAD : t;
+          }
+        } else {
+          set_dev_err(dev_err, SCFA_DEVERR_COUNT_EXCEEDS_TC);
+        }
       }
     }
     const int pr = tot + c * SCFA_COUNT_CHUNK + lane;
-    if (pr < s.Tc) s.idx[static_cast<size_t>(bh) * s.Tc + pr] = s.pad;
+    if (pr < s.Tc) {
+      s.idx[static_cast<size_t>(bh) * s.Tc + pr] = s.pad;
+      if (st && pr % s.bs == 0) {  // a tile of pads only
+        const int i = pr / s.bs;
+        st[4 * i + 0] = s.pad;
+        st[4 * i + 1] = s.pad;
+        st[4 * i + 2] = 0;
+        st[4 * i + 3] = 0;
+      }
+    }
     if (c == 0 && lane == 0) {
       s.count[bh] = tot;
       atomicMax(s.max_count, tot);
+      if (tiles && blockIdx.z == 0) tiles[bh] = 0;  // the processed-tile count the range table adds to
     }
   }
 }
@@ -1303,15 +1338,17 @@ int scfa_qk_count(const uint8_t* keep, int B, int T, int H, int32_t* count, int3
 
 int scfa_qk_index_qk(const uint8_t* keep_q, const uint8_t* keep_k, int B, int T, int T_kv, int H, int Tq, int Tk,
                      int32_t* count_q, int32_t* count_k, int32_t* max_count, int32_t* chunk_counts_q,
-                     int32_t* chunk_counts_k, int32_t* q_idx, int32_t* k_idx, int32_t* dev_err, hipStream_t stream) {
+                     int32_t* chunk_counts_k, int32_t* q_idx, int32_t* k_idx, int32_t* qstats, int32_t* kstats,
+                     int32_t* tiles, int32_t* dev_err, hipStream_t stream) {
   if (!keep_q || !keep_k || !count_q || !count_k || !max_count || !chunk_counts_q || !chunk_counts_k || !q_idx ||
       !k_idx)
     return SCFA_ERR_INVALID;
+  if ((qstats == nullptr) != (kstats == nullptr) || (qstats == nullptr) != (tiles == nullptr)) return SCFA_ERR_INVALID;
   if (B < 1 || T < 1 || T_kv < 1 || H < 1 || H > 128) return SCFA_ERR_INVALID;
   for (int tc : {Tq, Tk})
     if (tc < SCFA_ROW_ALIGN || tc % SCFA_ROW_ALIGN) return SCFA_ERR_INVALID;
   auto side = [&](const uint8_t* keep, int t, int tc, int32_t pad, int32_t* chunk, int32_t* count, int32_t* mx,
-                  int32_t* idx) {
+                  int32_t* idx, int32_t* stats, int bs) {
     QkSide sd;
     sd.keep = keep;
     sd.T = t;
@@ -1323,13 +1360,17 @@ int scfa_qk_index_qk(const uint8_t* keep_q, const uint8_t* keep_k, int B, int T,
     sd.count = count;
     sd.max_count = mx;
     sd.idx = idx;
+    sd.stats = stats;
+    sd.bs = bs;
     return sd;
   };
-  const QkSide sq = side(keep_q, T, Tq, SCFA_Q_PAD, chunk_counts_q, count_q, max_count, q_idx);
-  const QkSide sk = side(keep_k, T_kv, Tk, SCFA_K_PAD, chunk_counts_k, count_k, max_count + 1, k_idx);
+  const QkSide sq = side(keep_q, T, Tq, SCFA_Q_PAD, chunk_counts_q, count_q, max_count, q_idx, qstats, SCFA_TILE_M);
+  const QkSide sk = side(keep_k, T_kv, Tk, SCFA_K_PAD, chunk_counts_k, count_k, max_count + 1, k_idx, kstats,
+                         SCFA_TILE_N);
   hipLaunchKernelGGL(k_qk_chunk_counts_qk, dim3(max(sq.nC, sk.nC), B, 2), dim3(256), 0, stream, sq, sk, H);
   SCFA_RETURN_IF_LAUNCH_FAILED();
-  hipLaunchKernelGGL(k_qk_index_qk, dim3(max(sq.nCx, sk.nCx), B, 2), dim3(256), 0, stream, sq, sk, H, dev_err);
+  hipLaunchKernelGGL(k_qk_index_qk, dim3(max(sq.nCx, sk.nCx), B, 2), dim3(256), 0, stream, sq, sk, H, dev_err,
+                     tiles);
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }

@@ -62,7 +62,7 @@ _SIGS = {
     "scfa_count_visible": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_work_order": (_i, [_vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_fwd_table_order": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
-    "scfa_qk_index_qk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "scfa_qk_index_qk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i] + [_vp] * 12),
     "scfa_qk_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                                 _vp, _vp, _vp]),
     "scfa_hash_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
@@ -164,16 +164,18 @@ def scfa_qk_compact(x, keep, count, chunk_offsets, Tc, pad_idx, x_c, idx_c, dev_
 
 
 def scfa_qk_index_qk(keep_q, keep_k, Tq, Tk, count_q, count_k, max_count, chunk_counts_q, chunk_counts_k, q_idx,
-                     k_idx, dev_err=None, stream=None):
+                     k_idx, dev_err=None, stream=None, qstats=None, kstats=None, tiles=None):
     """Index compaction of the queries and of the keys in two launches
-    (counts and index arrays of both sides; the chunk counts are workspace)."""
+    (counts and index arrays of both sides; the chunk counts are workspace),
+    optionally with the tile statistics of the attention tiles."""
     B, T, H = keep_q.shape
     T_kv = keep_k.shape[1]
     if keep_k.shape[0] != B or keep_k.shape[2] != H:
         raise ScfaError("keep_q and keep_k must share B and H")
     _check(lib().scfa_qk_index_qk(_p(keep_q), _p(keep_k), B, T, T_kv, H, Tq, Tk, _p(count_q), _p(count_k),
                                   _p(max_count), _p(chunk_counts_q), _p(chunk_counts_k), _p(q_idx), _p(k_idx),
-                                  _p(dev_err), _stream(stream, keep_q)), "scfa_qk_index_qk")
+                                  _p(qstats), _p(kstats), _p(tiles), _p(dev_err), _stream(stream, keep_q)),
+           "scfa_qk_index_qk")
 
 
 def scfa_hash_bucket(x, R, nb, bucket, stream=None):
@@ -767,22 +769,26 @@ class Plan:
                             self.dev_err, t.qstats, t.kstats, t.tiles, stream)
 
     def compact(self, q, k, keep_q, keep_k, stream=None):
-        """Counts and index arrays of both sides (two launches; the operands
-        are read through the index arrays, no compacted copies)."""
+        """Counts, index arrays and tile statistics of both sides (two
+        launches; the operands are read through the index arrays, no
+        compacted copies)."""
+        t = self.tab
         scfa_qk_index_qk(keep_q, keep_k, self.Tq, self.Tk, self.cnt[0], self.cnt[1], self.mx2, self.choff[0],
-                         self.choff[1], self.q_idx, self.k_idx, self.dev_err, stream)
+                         self.choff[1], self.q_idx, self.k_idx, self.dev_err, stream, t.qstats, t.kstats, t.tiles)
 
     def tables(self, stream=None):
         """Forward ranges and the launch order, after the tile statistics
-        (computed here, or in hash mode by sort(), which also zeroes the
-        processed-tile counter that this call adds to; both then come from
-        one launch); the backward table is built by backward()."""
+        (computed here, or by sort() in hash mode and by compact() in QK
+        mode, which also zero the processed-tile counter that this call adds
+        to); the backward table is built by backward()."""
         t = self.tab
         t.bwd_ready = False  # new forward ranges: backward() rebuilds the backward table
         mode = _table_mode(self.mode) | self.flags
-        if not (self.mode == "hash" and self.two_side):  # else the tile statistics come from the layout launch
+        # the tile statistics come from the layout launch (hash, one length)
+        # or from the compaction (QK); otherwise from a statistics-only call
+        if self.mode == "dense" or (self.mode == "hash" and not self.two_side):
             scfa_range_table(mode, self.q_idx, self.k_idx, self.q_bkt, self.k_bkt, self.B, self.H, self.Tq, self.Tk,
-                             t.Bm, t.Bn, t.qstats, t.kstats, None, None, t.tiles, stream)  # statistics only
+                             t.Bm, t.Bn, t.qstats, t.kstats, None, None, t.tiles, stream)
         scfa_fwd_table_order(mode, t.qstats, t.kstats, t.fwd, t.tiles, t.fwd_order, stream)
 
     def forward(self, stream=None):

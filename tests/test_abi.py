@@ -167,7 +167,7 @@ def test_invalid_arguments_rejected_without_gpu():
     assert L.scfa_work_order(dummy, 1, 1, 8, 16384, dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_work_order(null, 1, 1, 8, 8, dummy, null) == scfa.SCFA_ERR_INVALID
     # two-side QK index compaction: NULL pointers, compacted lengths not multiples of 128, too many heads
-    qk = [dummy] * 2 + [1, 8, 8, 2, 128, 128] + [dummy] * 7 + [null, null]
+    qk = [dummy] * 2 + [1, 8, 8, 2, 128, 128] + [dummy] * 7 + [null, null, null, null, null]
     bad = list(qk)
     bad[0] = null
     assert L.scfa_qk_index_qk(*bad) == scfa.SCFA_ERR_INVALID
@@ -179,6 +179,9 @@ def test_invalid_arguments_rejected_without_gpu():
     assert L.scfa_qk_index_qk(*bad) == scfa.SCFA_ERR_INVALID
     bad = list(qk)
     bad[14] = null
+    assert L.scfa_qk_index_qk(*bad) == scfa.SCFA_ERR_INVALID
+    bad = list(qk)
+    bad[15] = dummy  # statistics: all three outputs or none
     assert L.scfa_qk_index_qk(*bad) == scfa.SCFA_ERR_INVALID
     # forward table and order in one launch: bad mode, NULL outputs, bad sizes
     assert L.scfa_fwd_table_order(7, dummy, dummy, 1, 1, 2, 2, dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID

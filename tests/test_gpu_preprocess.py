@@ -633,13 +633,19 @@ def test_qk_index_two_sides_matches_one_side_calls(case):
     scfa.scfa_qk_count(keep_k, ref["ck"], ref["mk"], ref["ok"])
     scfa.scfa_qk_compact(None, keep_q, ref["cq"], ref["oq"], Tq, scfa.SCFA_Q_PAD, None, ref["iq"])
     scfa.scfa_qk_compact(None, keep_k, ref["ck"], ref["ok"], Tk, scfa.SCFA_K_PAD, None, ref["ik"])
+    # tile statistics of the attention tiles over every row of the index arrays
+    nQt, nKt = Tq // scfa.SCFA_TILE_M, Tk // scfa.SCFA_TILE_N
+    ref["qs"], ref["ks"] = torch.empty((B, H, nQt, 4), **i32), torch.empty((B, H, nKt, 4), **i32)
+    ref["tiles"] = torch.full((B, H), -7, **i32)
+    scfa.scfa_range_table(scfa.SCFA_QK, ref["iq"], ref["ik"], None, None, B, H, Tq, Tk, scfa.SCFA_TILE_M,
+                          scfa.SCFA_TILE_N, ref["qs"], ref["ks"], None, None, ref["tiles"])
     got = {k: torch.full_like(v, -7) for k, v in ref.items()}
     mx = torch.full((2,), -7, **i32)
     err = torch.zeros((1,), **i32)
     scfa.scfa_qk_index_qk(keep_q, keep_k, Tq, Tk, got["cq"], got["ck"], mx, got["oq"], got["ok"], got["iq"], got["ik"],
-                          err)
+                          err, qstats=got["qs"], kstats=got["ks"], tiles=got["tiles"])
     torch.cuda.synchronize()
-    for name in ("cq", "ck", "iq", "ik"):
+    for name in ("cq", "ck", "iq", "ik", "qs", "ks", "tiles"):
         assert torch.equal(got[name], ref[name]), name
     assert int(mx[0]) == int(ref["mq"][0]) and int(mx[1]) == int(ref["mk"][0])
     assert int(err.item()) == 0
