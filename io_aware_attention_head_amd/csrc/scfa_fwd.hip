@@ -435,11 +435,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       for (int qb = 0; qb < 2; ++qb) l[qb] += ls[qb];
 
       // -- O^T += V^T P^T ------------------------------------------------------
-      // V^T operand of (db, kc): dims 16db + r16, keys 32kc + 8g + 0..7.
+      // V^T operand of (db, kc): dims 16db + r16, keys 32kc + 8g + 0..7. The
+      // key halves are the outer loop, so the two MFMAs that accumulate into
+      // one O block are eight apart.
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
+        for (int db = 0; db < 4; ++db) {
           const bf16x8 a = read_tr_op(Vs, db, kc, g, r16);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
