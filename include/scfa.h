@@ -377,11 +377,12 @@ int scfa_fwd_table(int mode, const int32_t* qstats, const int32_t* kstats, int B
  * forward table for the forward and dQ kernels, the backward table for the
  * dK/dV kernel): the B*H*ntiles items (item = (b*H + h)*ntiles + tile) sorted
  * by range length (end - start), longest first, so that the longest tiles
- * start first and the short ones fill the tail. When B*H is a multiple of 8
- * the items are sorted within 8 groups of heads (head bh in group bh % 8)
- * and interleaved, order[slot*8 + g]: workgroup x runs on XCD x % 8, so each
- * XCD keeps to its own heads and their K/V tiles stay in its L2. Items of
- * equal length come in an unspecified order.
+ * start first and the short ones fill the tail. The items are sorted within
+ * G groups of heads (head bh in group bh % G) and interleaved,
+ * order[slot*G + g]: G = 8 when B*H is a multiple of 8 (workgroup x runs on
+ * XCD x % 8, so each XCD keeps to its own heads and their K/V tiles stay in
+ * its L2), else the largest divisor of B*H not above 8 (one workgroup builds
+ * each group). Items of equal length come in an unspecified order.
  *  tab     (B, H, ntiles, 2) [start, end) range table.
  *  ntiles  >= 1, tiles per head the table describes.
  *  span    1..16383, tiles per head its ranges index (key tiles for the
@@ -389,6 +390,27 @@ int scfa_fwd_table(int mode, const int32_t* qstats, const int32_t* kstats, int B
  *          are clamped to [0, span].
  *  order   out (B*H*ntiles) int32, a permutation of the items.             */
 int scfa_work_order(const int32_t* tab, int B, int H, int ntiles, int span, int32_t* order, hipStream_t stream);
+
+/* The backward table and the launch order of the dK/dV workgroups in one
+ * call: the results of scfa_bwd_table followed by scfa_work_order(bwd_tab,
+ * ..., ntiles = nKt, span = nQt, ...), for the backward kernels' tile
+ * ranges of the SCFA explainer, 3.4 "Backward Pass Design" (the same ranges
+ * with queries and keys swapped). One launch: the group's forward ranges and
+ * query extrema are held in LDS, and where a head's forward starts and ends
+ * are both non-decreasing (the aligned hash layout, the QK and dense modes)
+ * the query tiles whose range holds a key tile are found by two binary
+ * searches; other tables are scanned tile by tile with the same rule, so any
+ * table gives scfa_bwd_table's result. Groups too large for LDS fall back to
+ * the two separate launches.
+ *  qstats, kstats, fwd_tab   as for scfa_bwd_table.
+ *  bwd_tab         out (B, H, nKt, 2).
+ *  order           out (B*H*nKt) int32, as scfa_work_order (items of equal
+ *                  length in an unspecified order).
+ *  nQt             1..16383.
+ *  flags           the SCFA_STRICT / SCFA_NONCAUSAL bit of the tables (0
+ *                  for none).                                             */
+int scfa_bwd_table_order(const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, int B, int H, int nQt,
+                         int nKt, int32_t* bwd_tab, int32_t* order, int flags, hipStream_t stream);
 
 /* The forward range table and its launch order in one call: the results of
  * scfa_fwd_table followed by scfa_work_order(fwd_tab, ..., span = nKt, ...).

@@ -1035,9 +1035,11 @@ __global__ __launch_bounds__(256) void k_bwd_table(const int32_t* __restrict__ q
 // ---------------------------------------------------------------------------
 // Launch order of the attention workgroups: tiles sorted by range length,
 // longest first (a longest-processing-time-first schedule), within G groups
-// of heads. Workgroup x of an attention launch takes order[x]; the hardware
-// hands workgroup x to XCD x % 8, so with G = 8 each XCD works on its own
-// heads (their K/V stay in that XCD's L2). One workgroup per group:
+// of heads (head bh in group bh % G; G = 8 when B*H is a multiple of 8, else
+// the largest divisor of B*H not above 8). Workgroup x of an attention
+// launch takes order[x]; the hardware hands workgroup x to XCD x % 8, so with
+// G = 8 each XCD works on its own heads (their K/V stay in that XCD's L2).
+// One workgroup per group:
 // counting sort over the length bins in LDS. Items of equal length may come
 // in any order; every order gives the same attention results.
 // ---------------------------------------------------------------------------
@@ -1238,6 +1240,126 @@ __global__ __launch_bounds__(1024) void k_fwd_table_order(int mode, const int4* 
     const int hl = i / nQt, t = i - hl * nQt;
     const int slot = atomicAdd(&bins[nKt - lens[i]], 1);
     order[static_cast<size_t>(slot) * G + g] = (g + hl * G) * nQt + t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward ranges and their launch order in one launch (the results of
+// k_bwd_table and k_work_order over the backward table, span = nQt). One
+// workgroup per group of heads holds the group's forward ranges and query
+// extrema in LDS. Key tile j of a head is processed by the query tiles whose
+// forward range holds j and whose largest position reaches the tile's
+// smallest; the backward range runs from the first to one past the last of
+// them. Where a head's forward starts and ends are both non-decreasing over
+// its query tiles (every table of the aligned hash layout, the QK and the
+// dense modes), the tiles whose range holds j form one run, found by two
+// binary searches, and the reach test is taken from its two ends inward;
+// otherwise every query tile is tested. The ranges are then counting-sorted
+// by length as in k_work_order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_bwd_table_order(const int4* __restrict__ qstats,
+                                                          const int4* __restrict__ kstats,
+                                                          const int2* __restrict__ fwd, int BH, int nQt, int nKt,
+                                                          int G, int2* __restrict__ bwd, int32_t* __restrict__ order,
+                                                          const Reach rc) {
+  extern __shared__ int2 lds2[];
+  const int g = blockIdx.x;
+  const int hpg = BH / G;
+  const int n = hpg * nKt;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nbins = nQt + 1;  // bin nQt - len
+  int2* ft = lds2;                                            // hpg * nQt forward ranges
+  int32_t* qy = reinterpret_cast<int32_t*>(ft + hpg * nQt);  // hpg * nQt largest query positions
+  int32_t* bins = qy + hpg * nQt;                             // nbins
+  int32_t* lens = bins + nbins;                               // n range lengths
+  __shared__ int32_t mono[64];                                // per head of the group: starts and ends in order
+  __shared__ int32_t wsum[16];
+  for (int i = tid; i < hpg * nQt; i += 1024) {
+    const int hl = i / nQt, t = i - hl * nQt;
+    const size_t gi = static_cast<size_t>(g + hl * G) * nQt + t;
+    ft[i] = fwd[gi];
+    qy[i] = qstats[gi].y;
+  }
+  for (int i = tid; i < nbins; i += 1024) bins[i] = 0;
+  if (tid < hpg) mono[tid] = 1;
+  __syncthreads();
+  for (int i = tid; i < hpg * nQt; i += 1024) {
+    const int t = i % nQt;
+    if (t + 1 < nQt && (ft[i + 1].x < ft[i].x || ft[i + 1].y < ft[i].y)) mono[i / nQt] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) {
+    const int hl = i / nKt, j = i - hl * nKt;
+    const int bh = g + hl * G;
+    // smallest query position that sees a key of the tile
+    const int kreach = k_reach(rc, kstats[static_cast<size_t>(bh) * nKt + j].x);
+    const int2* f = ft + hl * nQt;
+    const int32_t* y = qy + hl * nQt;
+    int first = -1, last = -1;
+    if (mono[hl]) {
+      // tiles [lo, hi] are those with start <= j < end
+      int lo = 0, hi = nQt;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (f[mid].y <= j) lo = mid + 1; else hi = mid;
+      }
+      const int a = lo;
+      hi = nQt;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (f[mid].x <= j) lo = mid + 1; else hi = mid;
+      }
+      const int b = lo - 1;
+      for (int t = a; t <= b; ++t)
+        if (kreach <= y[t]) {
+          first = t;
+          break;
+        }
+      if (first >= 0)
+        for (int t = b; t >= first; --t)
+          if (kreach <= y[t]) {
+            last = t;
+            break;
+          }
+    } else {
+      for (int t = 0; t < nQt; ++t)
+        if (j >= f[t].x && j < f[t].y && kreach <= y[t]) {
+          if (first < 0) first = t;
+          last = t;
+        }
+    }
+    const int2 r = first < 0 ? make_int2(0, 0) : make_int2(first, last + 1);
+    bwd[static_cast<size_t>(bh) * nKt + j] = r;
+    const int len = min(r.y - r.x, nQt);
+    lens[i] = len;
+    atomicAdd(&bins[nQt - len], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the bins (as k_work_order)
+  const int per = (nbins + 1023) / 1024;
+  const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
+  int sacc = 0;
+  for (int q = b0; q < b1; ++q) sacc += bins[q];
+  int x = sacc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int yv = __shfl_up(x, o);
+    if (lane >= o) x += yv;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int pre = x - sacc;
+  for (int q = 0; q < w; ++q) pre += wsum[q];
+  for (int q = b0; q < b1; ++q) {
+    const int c = bins[q];
+    bins[q] = pre;
+    pre += c;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) {
+    const int hl = i / nKt, j = i - hl * nKt;
+    const int slot = atomicAdd(&bins[nQt - lens[i]], 1);
+    order[static_cast<size_t>(slot) * G + g] = (g + hl * G) * nKt + j;
   }
 }
 
@@ -1641,14 +1763,44 @@ int scfa_bwd_table(const int32_t* qstats, const int32_t* kstats, const int32_t* 
   return SCFA_OK;
 }
 
+// Groups of heads of a launch order: 8 when B*H is a multiple of 8 (one
+// group per XCD), else the largest divisor of B*H not above 8, so that
+// several workgroups share the building of the order.
+static int order_groups(int BH) {
+  if (BH % 8 == 0) return 8;
+  for (int g = 7; g > 1; --g)
+    if (BH % g == 0) return g;
+  return 1;
+}
+
 int scfa_work_order(const int32_t* tab, int B, int H, int ntiles, int span, int32_t* order, hipStream_t stream) {
   if (!tab || !order) return SCFA_ERR_INVALID;
   if (B < 1 || H < 1 || ntiles < 1 || span < 1 || span > kMaxOrderSpan) return SCFA_ERR_INVALID;
   const int BH = B * H;
-  const int G = (BH % 8 == 0) ? 8 : 1;
+  const int G = order_groups(BH);
   const size_t lds = static_cast<size_t>(span + 1) * sizeof(int32_t);
   hipLaunchKernelGGL(k_work_order, dim3(G), dim3(1024), lds, stream, reinterpret_cast<const int2*>(tab), BH, ntiles,
                      span, G, order);
+  SCFA_RETURN_IF_LAUNCH_FAILED();
+  return SCFA_OK;
+}
+
+int scfa_bwd_table_order(const int32_t* qstats, const int32_t* kstats, const int32_t* fwd_tab, int B, int H, int nQt,
+                         int nKt, int32_t* bwd_tab, int32_t* order, int flags, hipStream_t stream) {
+  if (!qstats || !kstats || !fwd_tab || !bwd_tab || !order) return SCFA_ERR_INVALID;
+  if (B < 1 || H < 1 || nQt < 1 || nKt < 1 || nQt > kMaxOrderSpan || !flags_ok(flags)) return SCFA_ERR_INVALID;
+  const int BH = B * H;
+  const int G = order_groups(BH);
+  const int hpg = BH / G;
+  const size_t lds = static_cast<size_t>(hpg) * nQt * (sizeof(int2) + 4) + static_cast<size_t>(nQt + 1 + hpg * nKt) * 4;
+  if (hpg > 64 || lds > kTableOrderLds) {  // too large for one workgroup's LDS: the two launches
+    const int st = scfa_bwd_table(qstats, kstats, fwd_tab, B, H, nQt, nKt, bwd_tab, flags, stream);
+    if (st != SCFA_OK) return st;
+    return scfa_work_order(bwd_tab, B, H, nKt, nQt, order, stream);
+  }
+  hipLaunchKernelGGL(k_bwd_table_order, dim3(G), dim3(1024), lds, stream, reinterpret_cast<const int4*>(qstats),
+                     reinterpret_cast<const int4*>(kstats), reinterpret_cast<const int2*>(fwd_tab), BH, nQt, nKt, G,
+                     reinterpret_cast<int2*>(bwd_tab), order, reach_of(flags));
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }
@@ -1660,7 +1812,7 @@ int scfa_fwd_table_order(int mode, const int32_t* qstats, const int32_t* kstats,
   if (!qstats || !kstats || !fwd_tab || !tiles || !order) return SCFA_ERR_INVALID;
   if (B < 1 || H < 1 || nQt < 1 || nKt < 1 || nKt > kMaxOrderSpan) return SCFA_ERR_INVALID;
   const int BH = B * H;
-  const int G = (BH % 8 == 0) ? 8 : 1;
+  const int G = order_groups(BH);
   const int hpg = BH / G;
   const size_t lds = static_cast<size_t>(hpg) * nKt * sizeof(int4) + static_cast<size_t>(nKt + 1 + hpg * nQt) * 4;
   if (hpg > 64 || lds > kTableOrderLds) {  // too large for one workgroup's LDS: the two launches

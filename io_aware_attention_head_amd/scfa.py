@@ -61,6 +61,7 @@ _SIGS = {
     "scfa_range_table": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "scfa_count_visible": (_i, [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "scfa_work_order": (_i, [_vp, _i, _i, _i, _i, _vp, _vp]),
+    "scfa_bwd_table_order": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _vp]),
     "scfa_fwd_table_order": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "scfa_qk_index_qk": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i] + [_vp] * 12),
     "scfa_qk_sparse_fwd": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
@@ -304,6 +305,14 @@ def scfa_bwd_table(qstats, kstats, fwd_tab, bwd_tab, stream=None, flags=0):
     nKt = bwd_tab.shape[2]
     _check(lib().scfa_bwd_table(_p(qstats), _p(kstats), _p(fwd_tab), B, H, nQt, nKt, _p(bwd_tab), flags,
                                 _stream(stream, fwd_tab)), "scfa_bwd_table")
+
+
+def scfa_bwd_table_order(qstats, kstats, fwd_tab, bwd_tab, order, stream=None, flags=0):
+    """scfa_bwd_table and scfa_work_order(bwd_tab, span = nQt) in one launch."""
+    B, H, nQt = fwd_tab.shape[:3]
+    nKt = bwd_tab.shape[2]
+    _check(lib().scfa_bwd_table_order(_p(qstats), _p(kstats), _p(fwd_tab), B, H, nQt, nKt, _p(bwd_tab), _p(order),
+                                      flags, _stream(stream, fwd_tab)), "scfa_bwd_table_order")
 
 
 def scfa_count_visible(mode, q_idx, k_idx, q_bkt, k_bkt, B, H, Tq, Tk, pairs, stream=None):
@@ -801,9 +810,11 @@ class Plan:
             raise ScfaError("backward needs a prepared forward")
         if self.out_dtype != torch.float32:
             raise ScfaError("backward needs the fp32 forward output")
-        scfa_bwd_table(self.tab.qstats, self.tab.kstats, self.tab.fwd, self.tab.bwd, stream, self.flags)
         if self.mode == "hash":  # one dK/dV workgroup per key tile: longest query ranges first
-            scfa_work_order(self.tab.bwd, self.tab.fwd.shape[2], self.tab.bwd_order, stream)
+            scfa_bwd_table_order(self.tab.qstats, self.tab.kstats, self.tab.fwd, self.tab.bwd, self.tab.bwd_order,
+                                 stream, self.flags)
+        else:
+            scfa_bwd_table(self.tab.qstats, self.tab.kstats, self.tab.fwd, self.tab.bwd, stream, self.flags)
         self.tab.bwd_ready = True
         if self._grads is None:
             d = self.device

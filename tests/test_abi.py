@@ -192,6 +192,13 @@ def test_invalid_arguments_rejected_without_gpu():
     assert L.scfa_fwd_table_order(2, dummy, dummy, 1, 1, 2, 2, dummy, dummy, null, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_fwd_table_order(2, dummy, dummy, 1, 1, 2, 16384, dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
     assert L.scfa_fwd_table_order(2 | 48, dummy, dummy, 1, 1, 2, 2, dummy, dummy, dummy, null) == scfa.SCFA_ERR_INVALID
+    # backward table and order in one launch: NULL inputs or outputs, bad sizes, bad flags
+    assert L.scfa_bwd_table_order(dummy, dummy, dummy, 1, 1, 2, 2, dummy, null, 0, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_bwd_table_order(dummy, dummy, null, 1, 1, 2, 2, dummy, dummy, 0, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_bwd_table_order(dummy, dummy, dummy, 1, 1, 16384, 2, dummy, dummy, 0, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_bwd_table_order(dummy, dummy, dummy, 1, 0, 2, 2, dummy, dummy, 0, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_bwd_table_order(dummy, dummy, dummy, 1, 1, 2, 2, dummy, dummy, both, null) == scfa.SCFA_ERR_INVALID
+    assert L.scfa_bwd_table_order(dummy, dummy, dummy, 1, 1, 2, 2, dummy, dummy, 3, null) == scfa.SCFA_ERR_INVALID
 
 
 def test_python_binding_rejects_host_tensors():

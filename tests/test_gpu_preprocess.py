@@ -47,13 +47,13 @@ def _tables_match(mode, pre, tab, Tq, Bm, Bn, q_bkt=None, k_bkt=None, Tk=None):
 
 def check_order(order, tab):
     """A launch order is a permutation of the (head, tile) items; within each
-    group of heads (bh % 8 when B*H is a multiple of 8) the range lengths do
-    not increase along the group's slots, and slot s of group g sits at
-    s*8 + g (workgroup x runs on XCD x % 8)."""
+    of the G groups of heads (bh % G; G = 8 when B*H is a multiple of 8,
+    else the largest divisor of B*H not above 8) the range lengths do not
+    increase along the group's slots, and slot s of group g sits at s*G + g."""
     B, H, n, _ = tab.shape
     BH = B * H
     assert sorted(order.tolist()) == list(range(BH * n))
-    G = 8 if BH % 8 == 0 else 1
+    G = 8 if BH % 8 == 0 else max(g for g in range(1, 8) if BH % g == 0)
     lens = (tab[..., 1] - tab[..., 0]).reshape(BH * n)
     for g in range(G):
         items = order[g::G]
@@ -649,3 +649,52 @@ def test_qk_index_two_sides_matches_one_side_calls(case):
         assert torch.equal(got[name], ref[name]), name
     assert int(mx[0]) == int(ref["mq"][0]) and int(mx[1]) == int(ref["mk"][0])
     assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("case", [(1, 12, 135, 272, 16, 0, "layout"), (2, 12, 144, 272, 16, 0, "layout"),
+                                  (1, 3, 20, 40, 8, scfa.SCFA_STRICT, "layout"),
+                                  (1, 8, 30, 70, 6, scfa.SCFA_NONCAUSAL, "layout"), (1, 1, 9, 2, 2, 0, "layout"),
+                                  (1, 12, 40, 80, 4, 0, "random"), (2, 4, 33, 70, 4, scfa.SCFA_STRICT, "random"),
+                                  (1, 5, 64, 128, 1, 0, "qk"), (2, 3, 33, 65, 1, scfa.SCFA_NONCAUSAL, "qk"),
+                                  (65, 8, 1, 2, 2, 0, "layout"), (1, 1, 3000, 6000, 16, 0, "layout")],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_bwd_table_order_matches_two_launches(case):
+    """The one-launch backward table and dK/dV launch order against
+    scfa_bwd_table followed by scfa_work_order (span = nQt): the same table
+    bit for bit and a valid longest-first order, on forward tables of
+    statistics shaped like the aligned hash layout and the QK mode (starts
+    and ends in order: the searched path) and of random statistics (the
+    tile-by-tile path); (65, 8, ...) and (1, 1, 3000, 6000, ...) are too
+    large for one workgroup (the two-launch fallback inside the call)."""
+    need_gpu()
+    B, H, nQt, nKt, nb, flags, kind = case
+    announce(f"bwd table + order {case}")
+    rng = np.random.default_rng(sum(case[:6]) + 11)
+    if kind == "layout":
+        qs, ks = _layout_stats(rng, B * H, nQt, nKt, nb)
+        mode = scfa.SCFA_HASH
+    elif kind == "qk":
+        qs, ks = _qk_stats(rng, B * H, nQt, nKt)
+        mode = scfa.SCFA_QK
+    else:
+        qs = rng.integers(-5, 4000, (B * H, nQt, 4)).astype(np.int32)
+        ks = rng.integers(-5, 4000, (B * H, nKt, 4)).astype(np.int32)
+        qs[..., 2:] = np.sort(rng.integers(0, nb, (B * H, nQt, 2)), axis=-1)
+        ks[..., 2:] = np.sort(rng.integers(0, nb, (B * H, nKt, 2)), axis=-1)
+        mode = scfa.SCFA_HASH
+    dev = torch.device("cuda:0")
+    qst = torch.from_numpy(qs).reshape(B, H, nQt, 4).to(dev)
+    kst = torch.from_numpy(ks).reshape(B, H, nKt, 4).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    fwd, tiles = torch.empty((B, H, nQt, 2), **i32), torch.zeros((B, H), **i32)
+    scfa.scfa_fwd_table(mode | flags, qst, kst, fwd, tiles)
+    ref_bwd, ref_order = torch.empty((B, H, nKt, 2), **i32), torch.empty((B * H * nKt,), **i32)
+    scfa.scfa_bwd_table(qst, kst, fwd, ref_bwd, flags=flags)
+    scfa.scfa_work_order(ref_bwd, nQt, ref_order)
+    bwd, order = torch.empty((B, H, nKt, 2), **i32), torch.empty((B * H * nKt,), **i32)
+    scfa.scfa_bwd_table_order(qst, kst, fwd, bwd, order, flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(bwd, ref_bwd)
+    if kind != "random":
+        assert int((bwd[..., 1] > bwd[..., 0]).sum()) > 0  # the tables hold work
+    check_order(order.cpu().numpy(), bwd.cpu().numpy())
