@@ -404,8 +404,13 @@ int scfa_work_order(const int32_t* tab, int B, int H, int ntiles, int span, int3
  * the two separate launches.
  *  qstats, kstats, fwd_tab   as for scfa_bwd_table.
  *  bwd_tab         out (B, H, nKt, 2).
- *  order           out (B*H*nKt) int32, as scfa_work_order (items of equal
- *                  length in an unspecified order).
+ *  order           out (B*H*nKt) int32, sorted as scfa_work_order (items of
+ *                  equal length in an unspecified order); when B*H is not a
+ *                  multiple of 8, in the 8 runs of consecutive items that
+ *                  scfa_fwd_table_order uses in SCFA_HASH mode (slot s of run
+ *                  k at order[s*8 + k]); problems too large for one workgroup
+ *                  per group or run take the two launches and
+ *                  scfa_work_order's groups.
  *  nQt             1..16383.
  *  flags           the SCFA_STRICT / SCFA_NONCAUSAL bit of the tables (0
  *                  for none).                                             */
@@ -428,8 +433,17 @@ int scfa_bwd_table_order(const int32_t* qstats, const int32_t* kstats, const int
  *  fwd_tab         out (B, H, nQt, 2).
  *  tiles           (B*H) int32, zero on entry: the processed-tile count is
  *                  added to it.
- *  order           out (B*H*nQt) int32, as scfa_work_order (items of equal
- *                  length in an unspecified order).
+ *  order           out (B*H*nQt) int32: the items sorted by range length,
+ *                  longest first, as scfa_work_order (items of equal length
+ *                  in an unspecified order), in scfa_work_order's groups of
+ *                  heads, except in SCFA_HASH mode when B*H is not a
+ *                  multiple of 8: then the N = B*H*nQt items (head-major)
+ *                  form 8 runs of consecutive items of equal count (the
+ *                  first N % 8 runs one item longer), each sorted on its
+ *                  own, with slot s of run k at order[s*8 + k], so that each
+ *                  XCD (workgroup x runs on XCD x % 8) works on about B*H/8
+ *                  heads. Problems too large for one workgroup per run take
+ *                  the two launches and scfa_work_order's groups.
  *  nKt             1..16383.                                              */
 int scfa_fwd_table_order(int mode, const int32_t* qstats, const int32_t* kstats, int B, int H, int nQt, int nKt,
                          int32_t* fwd_tab, int32_t* tiles, int32_t* order, hipStream_t stream);

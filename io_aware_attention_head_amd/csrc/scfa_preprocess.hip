@@ -1092,6 +1092,42 @@ __global__ __launch_bounds__(1024) void k_work_order(const int2* __restrict__ ta
 }
 
 // ---------------------------------------------------------------------------
+// Work of one workgroup of the one-launch table and order kernels, and where
+// its items go in the order. Groups: workgroup g takes the heads g, g + G,
+// g + 2G, ... (all their tiles) and its slot s goes to order[s * G + g].
+// Parts: the B*H*nT items (head-major) are cut into 8 runs of consecutive
+// items of equal count (the first N % 8 one item longer); workgroup k takes
+// run k, which may start or end inside a head, and its slot s goes to
+// order[s * 8 + k], so that every XCD (workgroup x runs on XCD x % 8) works
+// on about B*H / 8 heads, also when B*H is not a multiple of 8.
+// ---------------------------------------------------------------------------
+struct OrderSplit {
+  bool parts;
+  int k, G, nT;
+  int lo, n;  // parts: first item and item count of this workgroup; groups: n = items of the group
+  int bh0;    // parts: first head of the run
+  __device__ OrderSplit(bool parts_, int k_, int G_, int BH, int nT_) : parts(parts_), k(k_), G(G_), nT(nT_) {
+    if (parts) {
+      const int N = BH * nT, c = N / 8, r = N % 8;
+      lo = k * c + min(k, r);
+      n = c + (k < r ? 1 : 0);
+      bh0 = lo / nT;
+    } else {
+      lo = 0;
+      n = (BH / G) * nT;
+      bh0 = 0;
+    }
+  }
+  // heads whose tiles the workgroup reads (slot hl = 0 .. heads() - 1)
+  __device__ int heads() const { return parts ? (n ? (lo + n - 1) / nT - bh0 + 1 : 0) : n / nT; }
+  __device__ int head(int hl) const { return parts ? bh0 + hl : k + hl * G; }
+  // local item li: head slot and tile
+  __device__ int slot_of(int li) const { return parts ? (lo + li) / nT - bh0 : li / nT; }
+  __device__ int tile_of(int li) const { return parts ? (lo + li) % nT : li % nT; }
+  __device__ size_t pos(int s) const { return static_cast<size_t>(s) * G + k; }  // G = 8 for parts
+};
+
+// ---------------------------------------------------------------------------
 // Forward ranges and launch order in one launch. One workgroup per group of
 // heads (the groups of k_work_order). The group's key-tile statistics go to
 // LDS. Where a head's key tiles are in layout order (each tile one bucket,
@@ -1108,31 +1144,32 @@ __global__ __launch_bounds__(1024) void k_work_order(const int2* __restrict__ ta
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void k_fwd_table_order(int mode, const int4* __restrict__ qstats,
                                                           const int4* __restrict__ kstats, int BH, int nQt, int nKt,
-                                                          int G, int2* __restrict__ fwd, int32_t* __restrict__ tiles,
-                                                          int32_t* __restrict__ order, const Reach rc) {
+                                                          int G, bool parts, int2* __restrict__ fwd,
+                                                          int32_t* __restrict__ tiles, int32_t* __restrict__ order,
+                                                          const Reach rc) {
   extern __shared__ int4 lds4[];
-  const int g = blockIdx.x;
-  const int hpg = BH / G;
-  const int n = hpg * nQt;
+  const OrderSplit sp(parts, blockIdx.x, G, BH, nQt);
+  const int nh = sp.heads();
+  const int n = sp.n;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nbins = nKt + 1;  // bin nKt - len
-  int4* ks = lds4;                                               // hpg * nKt key-tile statistics
-  int32_t* bins = reinterpret_cast<int32_t*>(ks + hpg * nKt);    // nbins
+  int4* ks = lds4;                                               // nh * nKt key-tile statistics
+  int32_t* bins = reinterpret_cast<int32_t*>(ks + nh * nKt);     // nbins
   int32_t* lens = bins + nbins;                                  // n range lengths
-  __shared__ int32_t ordered[64];                                // per head of the group: tiles in layout order
+  __shared__ int32_t ordered[64];                                // per head: tiles in layout order
   __shared__ int32_t cnt_s[64];                                  // per head: processed tiles
   __shared__ int32_t wsum[16];
-  for (int i = tid; i < hpg * nKt; i += 1024) {
+  for (int i = tid; i < nh * nKt; i += 1024) {
     const int hl = i / nKt, j = i - hl * nKt;
-    ks[i] = kstats[static_cast<size_t>(g + hl * G) * nKt + j];
+    ks[i] = kstats[static_cast<size_t>(sp.head(hl)) * nKt + j];
   }
   for (int i = tid; i < nbins; i += 1024) bins[i] = 0;
-  if (tid < hpg) {
+  if (tid < nh) {
     ordered[tid] = 1;
     cnt_s[tid] = 0;
   }
   __syncthreads();
-  for (int i = tid; i < hpg * nKt; i += 1024) {
+  for (int i = tid; i < nh * nKt; i += 1024) {
     const int hl = i / nKt, j = i - hl * nKt;
     const int4 a = ks[i];
     bool ok = a.z == a.w;
@@ -1144,8 +1181,8 @@ __global__ __launch_bounds__(1024) void k_fwd_table_order(int mode, const int4* 
   }
   __syncthreads();
   for (int i = tid; i < n; i += 1024) {
-    const int hl = i / nQt, t = i - hl * nQt;
-    const int bh = g + hl * G;
+    const int hl = sp.slot_of(i), t = sp.tile_of(i);
+    const int bh = sp.head(hl);
     const int4 qs = qstats[static_cast<size_t>(bh) * nQt + t];
     const int qreach = q_reach(rc, qs.y);
     const int4* k = ks + hl * nKt;
@@ -1214,7 +1251,7 @@ __global__ __launch_bounds__(1024) void k_fwd_table_order(int mode, const int4* 
     if (cnt) atomicAdd(&cnt_s[hl], cnt);
   }
   __syncthreads();
-  if (tid < hpg && cnt_s[tid]) atomicAdd(&tiles[g + tid * G], cnt_s[tid]);
+  if (tid < nh && cnt_s[tid]) atomicAdd(&tiles[sp.head(tid)], cnt_s[tid]);
   // exclusive scan of the bins (as k_work_order)
   const int per = (nbins + 1023) / 1024;
   const int b0 = min(tid * per, nbins), b1 = min(b0 + per, nbins);
@@ -1237,9 +1274,8 @@ __global__ __launch_bounds__(1024) void k_fwd_table_order(int mode, const int4* 
   }
   __syncthreads();
   for (int i = tid; i < n; i += 1024) {
-    const int hl = i / nQt, t = i - hl * nQt;
     const int slot = atomicAdd(&bins[nKt - lens[i]], 1);
-    order[static_cast<size_t>(slot) * G + g] = (g + hl * G) * nQt + t;
+    order[sp.pos(slot)] = sp.head(sp.slot_of(i)) * nQt + sp.tile_of(i);
   }
 }
 
@@ -1260,37 +1296,37 @@ __global__ __launch_bounds__(1024) void k_fwd_table_order(int mode, const int4* 
 __global__ __launch_bounds__(1024) void k_bwd_table_order(const int4* __restrict__ qstats,
                                                           const int4* __restrict__ kstats,
                                                           const int2* __restrict__ fwd, int BH, int nQt, int nKt,
-                                                          int G, int2* __restrict__ bwd, int32_t* __restrict__ order,
-                                                          const Reach rc) {
+                                                          int G, bool parts, int2* __restrict__ bwd,
+                                                          int32_t* __restrict__ order, const Reach rc) {
   extern __shared__ int2 lds2[];
-  const int g = blockIdx.x;
-  const int hpg = BH / G;
-  const int n = hpg * nKt;
+  const OrderSplit sp(parts, blockIdx.x, G, BH, nKt);
+  const int nh = sp.heads();
+  const int n = sp.n;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nbins = nQt + 1;  // bin nQt - len
-  int2* ft = lds2;                                            // hpg * nQt forward ranges
-  int32_t* qy = reinterpret_cast<int32_t*>(ft + hpg * nQt);  // hpg * nQt largest query positions
-  int32_t* bins = qy + hpg * nQt;                             // nbins
-  int32_t* lens = bins + nbins;                               // n range lengths
-  __shared__ int32_t mono[64];                                // per head of the group: starts and ends in order
+  int2* ft = lds2;                                           // nh * nQt forward ranges
+  int32_t* qy = reinterpret_cast<int32_t*>(ft + nh * nQt);  // nh * nQt largest query positions
+  int32_t* bins = qy + nh * nQt;                             // nbins
+  int32_t* lens = bins + nbins;                              // n range lengths
+  __shared__ int32_t mono[64];                               // per head: starts and ends in order
   __shared__ int32_t wsum[16];
-  for (int i = tid; i < hpg * nQt; i += 1024) {
+  for (int i = tid; i < nh * nQt; i += 1024) {
     const int hl = i / nQt, t = i - hl * nQt;
-    const size_t gi = static_cast<size_t>(g + hl * G) * nQt + t;
+    const size_t gi = static_cast<size_t>(sp.head(hl)) * nQt + t;
     ft[i] = fwd[gi];
     qy[i] = qstats[gi].y;
   }
   for (int i = tid; i < nbins; i += 1024) bins[i] = 0;
-  if (tid < hpg) mono[tid] = 1;
+  if (tid < nh) mono[tid] = 1;
   __syncthreads();
-  for (int i = tid; i < hpg * nQt; i += 1024) {
+  for (int i = tid; i < nh * nQt; i += 1024) {
     const int t = i % nQt;
     if (t + 1 < nQt && (ft[i + 1].x < ft[i].x || ft[i + 1].y < ft[i].y)) mono[i / nQt] = 0;
   }
   __syncthreads();
   for (int i = tid; i < n; i += 1024) {
-    const int hl = i / nKt, j = i - hl * nKt;
-    const int bh = g + hl * G;
+    const int hl = sp.slot_of(i), j = sp.tile_of(i);
+    const int bh = sp.head(hl);
     // smallest query position that sees a key of the tile
     const int kreach = k_reach(rc, kstats[static_cast<size_t>(bh) * nKt + j].x);
     const int2* f = ft + hl * nQt;
@@ -1357,9 +1393,8 @@ __global__ __launch_bounds__(1024) void k_bwd_table_order(const int4* __restrict
   }
   __syncthreads();
   for (int i = tid; i < n; i += 1024) {
-    const int hl = i / nKt, j = i - hl * nKt;
     const int slot = atomicAdd(&bins[nQt - lens[i]], 1);
-    order[static_cast<size_t>(slot) * G + g] = (g + hl * G) * nKt + j;
+    order[sp.pos(slot)] = sp.head(sp.slot_of(i)) * nKt + sp.tile_of(i);
   }
 }
 
@@ -1773,6 +1808,33 @@ static int order_groups(int BH) {
   return 1;
 }
 
+// Work split of the one-launch table and order kernels: 8 runs of
+// consecutive items when `runs_ok` and B*H is not a multiple of 8 (the hash
+// modes, whose tiles carry similar work along a head; in the causal QK and
+// dense modes a run that ends inside a head would carry less work than one
+// that starts there), else the groups of scfa_work_order. heads / items:
+// the most heads and items one workgroup handles.
+struct OrderPlan {
+  bool parts;
+  int G, heads, items;
+};
+static OrderPlan order_plan(bool runs_ok, int BH, int nT) {
+  OrderPlan op;
+  op.parts = runs_ok && BH % 8 != 0;
+  if (op.parts) {
+    const long long N = static_cast<long long>(BH) * nT;
+    const int c1 = static_cast<int>((N + 7) / 8);
+    op.G = 8;
+    op.items = c1;
+    op.heads = min(BH, (c1 + nT - 1) / nT + 1);
+  } else {
+    op.G = order_groups(BH);
+    op.heads = BH / op.G;
+    op.items = op.heads * nT;
+  }
+  return op;
+}
+
 int scfa_work_order(const int32_t* tab, int B, int H, int ntiles, int span, int32_t* order, hipStream_t stream) {
   if (!tab || !order) return SCFA_ERR_INVALID;
   if (B < 1 || H < 1 || ntiles < 1 || span < 1 || span > kMaxOrderSpan) return SCFA_ERR_INVALID;
@@ -1790,17 +1852,17 @@ int scfa_bwd_table_order(const int32_t* qstats, const int32_t* kstats, const int
   if (!qstats || !kstats || !fwd_tab || !bwd_tab || !order) return SCFA_ERR_INVALID;
   if (B < 1 || H < 1 || nQt < 1 || nKt < 1 || nQt > kMaxOrderSpan || !flags_ok(flags)) return SCFA_ERR_INVALID;
   const int BH = B * H;
-  const int G = order_groups(BH);
-  const int hpg = BH / G;
-  const size_t lds = static_cast<size_t>(hpg) * nQt * (sizeof(int2) + 4) + static_cast<size_t>(nQt + 1 + hpg * nKt) * 4;
-  if (hpg > 64 || lds > kTableOrderLds) {  // too large for one workgroup's LDS: the two launches
+  const OrderPlan op = order_plan(true, BH, nKt);
+  const size_t lds = static_cast<size_t>(op.heads) * nQt * (sizeof(int2) + 4) +
+                     static_cast<size_t>(nQt + 1 + op.items) * 4;
+  if (op.heads > 64 || lds > kTableOrderLds) {  // too large for one workgroup's LDS: the two launches
     const int st = scfa_bwd_table(qstats, kstats, fwd_tab, B, H, nQt, nKt, bwd_tab, flags, stream);
     if (st != SCFA_OK) return st;
     return scfa_work_order(bwd_tab, B, H, nKt, nQt, order, stream);
   }
-  hipLaunchKernelGGL(k_bwd_table_order, dim3(G), dim3(1024), lds, stream, reinterpret_cast<const int4*>(qstats),
-                     reinterpret_cast<const int4*>(kstats), reinterpret_cast<const int2*>(fwd_tab), BH, nQt, nKt, G,
-                     reinterpret_cast<int2*>(bwd_tab), order, reach_of(flags));
+  hipLaunchKernelGGL(k_bwd_table_order, dim3(op.G), dim3(1024), lds, stream, reinterpret_cast<const int4*>(qstats),
+                     reinterpret_cast<const int4*>(kstats), reinterpret_cast<const int2*>(fwd_tab), BH, nQt, nKt, op.G,
+                     op.parts, reinterpret_cast<int2*>(bwd_tab), order, reach_of(flags));
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }
@@ -1812,17 +1874,16 @@ int scfa_fwd_table_order(int mode, const int32_t* qstats, const int32_t* kstats,
   if (!qstats || !kstats || !fwd_tab || !tiles || !order) return SCFA_ERR_INVALID;
   if (B < 1 || H < 1 || nQt < 1 || nKt < 1 || nKt > kMaxOrderSpan) return SCFA_ERR_INVALID;
   const int BH = B * H;
-  const int G = order_groups(BH);
-  const int hpg = BH / G;
-  const size_t lds = static_cast<size_t>(hpg) * nKt * sizeof(int4) + static_cast<size_t>(nKt + 1 + hpg * nQt) * 4;
-  if (hpg > 64 || lds > kTableOrderLds) {  // too large for one workgroup's LDS: the two launches
+  const OrderPlan op = order_plan(mode == SCFA_HASH, BH, nQt);
+  const size_t lds = static_cast<size_t>(op.heads) * nKt * sizeof(int4) + static_cast<size_t>(nKt + 1 + op.items) * 4;
+  if (op.heads > 64 || lds > kTableOrderLds) {  // too large for one workgroup's LDS: the two launches
     const int st = scfa_fwd_table(mode | flags, qstats, kstats, B, H, nQt, nKt, fwd_tab, tiles, stream);
     if (st != SCFA_OK) return st;
     return scfa_work_order(fwd_tab, B, H, nQt, nKt, order, stream);
   }
-  hipLaunchKernelGGL(k_fwd_table_order, dim3(G), dim3(1024), lds, stream, mode, reinterpret_cast<const int4*>(qstats),
-                     reinterpret_cast<const int4*>(kstats), BH, nQt, nKt, G, reinterpret_cast<int2*>(fwd_tab), tiles,
-                     order, reach_of(flags));
+  hipLaunchKernelGGL(k_fwd_table_order, dim3(op.G), dim3(1024), lds, stream, mode,
+                     reinterpret_cast<const int4*>(qstats), reinterpret_cast<const int4*>(kstats), BH, nQt, nKt, op.G,
+                     op.parts, reinterpret_cast<int2*>(fwd_tab), tiles, order, reach_of(flags));
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }

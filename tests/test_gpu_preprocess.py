@@ -45,21 +45,33 @@ def _tables_match(mode, pre, tab, Tq, Bm, Bn, q_bkt=None, k_bkt=None, Tk=None):
     return ref
 
 
-def check_order(order, tab):
-    """A launch order is a permutation of the (head, tile) items; within each
-    of the G groups of heads (bh % G; G = 8 when B*H is a multiple of 8,
-    else the largest divisor of B*H not above 8) the range lengths do not
-    increase along the group's slots, and slot s of group g sits at s*G + g."""
+def check_order(order, tab, layout="groups"):
+    """A launch order is a permutation of the (head, tile) items, longest range
+    first within each part, in one of two layouts:
+    groups: G groups of heads (head bh in group bh % G; G = 8 when B*H is a
+    multiple of 8, else the largest divisor of B*H not above 8), slot s of
+    group g at s*G + g;
+    runs: 8 runs of consecutive items of equal count (the first N % 8 one
+    longer), slot s of run k at s*8 + k."""
     B, H, n, _ = tab.shape
     BH = B * H
-    assert sorted(order.tolist()) == list(range(BH * n))
-    G = 8 if BH % 8 == 0 else max(g for g in range(1, 8) if BH % g == 0)
-    lens = (tab[..., 1] - tab[..., 0]).reshape(BH * n)
-    for g in range(G):
-        items = order[g::G]
-        assert ((items // n) % G == g).all()
-        ls = lens[items]
-        assert (np.diff(ls) <= 0).all()
+    N = BH * n
+    assert sorted(order.tolist()) == list(range(N))
+    lens = (tab[..., 1] - tab[..., 0]).reshape(N)
+    if layout == "groups":
+        G = 8 if BH % 8 == 0 else max(g for g in range(1, 8) if BH % g == 0)
+        for g in range(G):
+            items = order[g::G]
+            assert ((items // n) % G == g).all()
+            assert (np.diff(lens[items]) <= 0).all()
+    else:
+        c, r = divmod(N, 8)
+        for k in range(8):
+            lo, cnt = k * c + min(k, r), c + (1 if k < r else 0)
+            items = order[k::8]
+            assert len(items) == cnt
+            assert sorted(items.tolist()) == list(range(lo, lo + cnt))
+            assert (np.diff(lens[items]) <= 0).all()
 
 
 @pytest.mark.parametrize("w", QK_CASES, ids=lambda w: w.name)
@@ -471,7 +483,7 @@ def _qk_stats(rng, BH, nQt, nKt, ordered=True):
 
 
 @pytest.mark.parametrize("case", [(1, 12, 64, 128, scfa.SCFA_QK), (2, 12, 64, 128, scfa.SCFA_QK | scfa.SCFA_STRICT),
-                                  (2, 4, 33, 70, scfa.SCFA_QK | scfa.SCFA_NONCAUSAL), (1, 3, 40, 1300, scfa.SCFA_QK),
+                                  (2, 4, 33, 70, scfa.SCFA_QK | scfa.SCFA_NONCAUSAL), (1, 3, 40, 4000, scfa.SCFA_QK),
                                   (1, 2, 16, 32, scfa.SCFA_DENSE), (1, 5, 9, 1, scfa.SCFA_QK)],
                          ids=lambda c: "x".join(map(str, c)))
 @pytest.mark.parametrize("kind", ["ordered", "random"])
@@ -480,7 +492,7 @@ def test_fwd_table_order_qk_matches_two_launches(case, kind):
     (Algorithm 1) against scfa_fwd_table followed by scfa_work_order: the
     same table and tile count bit for bit and a valid longest-first order,
     on position-ordered statistics (the searched path) and on unordered ones
-    (the tile-by-tile count); (1, 3, 40, 1300) takes the two-launch
+    (the tile-by-tile count); (1, 3, 40, 4000) takes the two-launch
     fallback."""
     need_gpu()
     B, H, nQt, nKt, mode = case
@@ -543,7 +555,8 @@ def test_plan_two_side_launches_bitexact(w):
     for name in ("qstats", "kstats", "fwd", "tiles"):
         assert torch.equal(getattr(plan.tab, name), getattr(ref, name)), name
     # the Plan's launch order over its forward table
-    check_order(plan.tab.fwd_order.cpu().numpy(), plan.tab.fwd.cpu().numpy())
+    check_order(plan.tab.fwd_order.cpu().numpy(), plan.tab.fwd.cpu().numpy(),
+                "groups" if (w.B * w.H) % 8 == 0 else "runs")
 
 
 def _layout_stats(rng, BH, nQt, nKt, nb):
@@ -569,7 +582,7 @@ def _layout_stats(rng, BH, nQt, nKt, nb):
 
 
 @pytest.mark.parametrize("case", [(2, 12, 144, 272, 16, 0), (1, 3, 20, 40, 8, 0), (2, 4, 64, 130, 4, scfa.SCFA_STRICT),
-                                  (1, 8, 30, 70, 6, scfa.SCFA_NONCAUSAL), (1, 3, 40, 1300, 16, 0),
+                                  (1, 8, 30, 70, 6, scfa.SCFA_NONCAUSAL), (1, 3, 40, 4000, 16, 0), (1, 3, 40, 1300, 16, 0),
                                   (1, 5, 9, 2, 2, 0)],
                          ids=lambda c: "x".join(map(str, c)))
 @pytest.mark.parametrize("kind", ["layout", "random"])
@@ -578,8 +591,9 @@ def test_fwd_table_order_matches_two_launches(case, kind):
     by scfa_work_order: the same table and tile count, bit for bit, and a
     valid longest-first order, on statistics shaped like the aligned layout's
     (the searched path) and on random statistics (the tile-by-tile path);
-    (1, 3, 40, 1300) is too large for one workgroup's LDS (the two-launch
-    fallback inside the call)."""
+    (1, 3, 40, 4000) is too large for one workgroup's LDS (the two-launch
+    fallback inside the call, with scfa_work_order's groups); the other
+    cases with B*H not a multiple of 8 take the runs layout."""
     need_gpu()
     B, H, nQt, nKt, nb, flags = case
     announce(f"fwd table + order {kind} {case}")
@@ -606,7 +620,8 @@ def test_fwd_table_order_matches_two_launches(case, kind):
     torch.cuda.synchronize()
     assert torch.equal(tab, ref_tab)
     assert torch.equal(tiles, ref_tiles)
-    check_order(order.cpu().numpy(), tab.cpu().numpy())
+    fallback = nKt >= 4000  # too large for one workgroup: scfa_work_order's groups
+    check_order(order.cpu().numpy(), tab.cpu().numpy(), "groups" if fallback or (B * H) % 8 == 0 else "runs")
 
 
 @pytest.mark.parametrize("case", [(2, 8192, 8192, 12, 0.5, 8192, 8192), (1, 300, 777, 3, 0.6, 384, 896),
@@ -656,7 +671,8 @@ def test_qk_index_two_sides_matches_one_side_calls(case):
                                   (1, 8, 30, 70, 6, scfa.SCFA_NONCAUSAL, "layout"), (1, 1, 9, 2, 2, 0, "layout"),
                                   (1, 12, 40, 80, 4, 0, "random"), (2, 4, 33, 70, 4, scfa.SCFA_STRICT, "random"),
                                   (1, 5, 64, 128, 1, 0, "qk"), (2, 3, 33, 65, 1, scfa.SCFA_NONCAUSAL, "qk"),
-                                  (65, 8, 1, 2, 2, 0, "layout"), (1, 1, 3000, 6000, 16, 0, "layout")],
+                                  (65, 8, 1, 2, 2, 0, "layout"), (1, 1, 4000, 8000, 16, 0, "layout"),
+                                  (1, 1, 3000, 6000, 16, 0, "layout")],
                          ids=lambda c: "x".join(map(str, c)))
 def test_bwd_table_order_matches_two_launches(case):
     """The one-launch backward table and dK/dV launch order against
@@ -664,8 +680,10 @@ def test_bwd_table_order_matches_two_launches(case):
     bit for bit and a valid longest-first order, on forward tables of
     statistics shaped like the aligned hash layout and the QK mode (starts
     and ends in order: the searched path) and of random statistics (the
-    tile-by-tile path); (65, 8, ...) and (1, 1, 3000, 6000, ...) are too
-    large for one workgroup (the two-launch fallback inside the call)."""
+    tile-by-tile path); (65, 8, ...) and (1, 1, 4000, 8000, ...) are too
+    large for one workgroup (the two-launch fallback inside the call, with
+    scfa_work_order's groups); the other cases with B*H not a multiple of 8
+    take the runs layout."""
     need_gpu()
     B, H, nQt, nKt, nb, flags, kind = case
     announce(f"bwd table + order {case}")
@@ -697,4 +715,5 @@ def test_bwd_table_order_matches_two_launches(case):
     assert torch.equal(bwd, ref_bwd)
     if kind != "random":
         assert int((bwd[..., 1] > bwd[..., 0]).sum()) > 0  # the tables hold work
-    check_order(order.cpu().numpy(), bwd.cpu().numpy())
+    fallback = (B, H) == (65, 8) or nQt >= 4000  # too large for one workgroup: scfa_work_order's groups
+    check_order(order.cpu().numpy(), bwd.cpu().numpy(), "groups" if fallback or (B * H) % 8 == 0 else "runs")
