@@ -1095,19 +1095,19 @@ __global__ __launch_bounds__(1024) void k_work_order(const int2* __restrict__ ta
 // Work of one workgroup of the one-launch table and order kernels, and where
 // its items go in the order. Groups: workgroup g takes the heads g, g + G,
 // g + 2G, ... (all their tiles) and its slot s goes to order[s * G + g].
-// Parts: the B*H*nT items (head-major) are cut into 8 runs of consecutive
+// Runs: the B*H*nT items (head-major) are cut into 8 runs of consecutive
 // items of equal count (the first N % 8 one item longer); workgroup k takes
 // run k, which may start or end inside a head, and its slot s goes to
 // order[s * 8 + k], so that every XCD (workgroup x runs on XCD x % 8) works
 // on about B*H / 8 heads, also when B*H is not a multiple of 8.
 // ---------------------------------------------------------------------------
 struct OrderSplit {
-  bool parts;
+  bool runs;
   int k, G, nT;
-  int lo, n;  // parts: first item and item count of this workgroup; groups: n = items of the group
-  int bh0;    // parts: first head of the run
-  __device__ OrderSplit(bool parts_, int k_, int G_, int BH, int nT_) : parts(parts_), k(k_), G(G_), nT(nT_) {
-    if (parts) {
+  int lo, n;  // runs: first item and item count of this workgroup; groups: n = items of the group
+  int bh0;    // runs: first head of the run
+  __device__ OrderSplit(bool runs_, int k_, int G_, int BH, int nT_) : runs(runs_), k(k_), G(G_), nT(nT_) {
+    if (runs) {
       const int N = BH * nT, c = N / 8, r = N % 8;
       lo = k * c + min(k, r);
       n = c + (k < r ? 1 : 0);
@@ -1119,12 +1119,12 @@ struct OrderSplit {
     }
   }
   // heads whose tiles the workgroup reads (slot hl = 0 .. heads() - 1)
-  __device__ int heads() const { return parts ? (n ? (lo + n - 1) / nT - bh0 + 1 : 0) : n / nT; }
-  __device__ int head(int hl) const { return parts ? bh0 + hl : k + hl * G; }
+  __device__ int heads() const { return runs ? (n ? (lo + n - 1) / nT - bh0 + 1 : 0) : n / nT; }
+  __device__ int head(int hl) const { return runs ? bh0 + hl : k + hl * G; }
   // local item li: head slot and tile
-  __device__ int slot_of(int li) const { return parts ? (lo + li) / nT - bh0 : li / nT; }
-  __device__ int tile_of(int li) const { return parts ? (lo + li) % nT : li % nT; }
-  __device__ size_t pos(int s) const { return static_cast<size_t>(s) * G + k; }  // G = 8 for parts
+  __device__ int slot_of(int li) const { return runs ? (lo + li) / nT - bh0 : li / nT; }
+  __device__ int tile_of(int li) const { return runs ? (lo + li) % nT : li % nT; }
+  __device__ size_t pos(int s) const { return static_cast<size_t>(s) * G + k; }  // G = 8 for runs
 };
 
 // ---------------------------------------------------------------------------
@@ -1144,11 +1144,11 @@ struct OrderSplit {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void k_fwd_table_order(int mode, const int4* __restrict__ qstats,
                                                           const int4* __restrict__ kstats, int BH, int nQt, int nKt,
-                                                          int G, bool parts, int2* __restrict__ fwd,
+                                                          int G, bool runs, int2* __restrict__ fwd,
                                                           int32_t* __restrict__ tiles, int32_t* __restrict__ order,
                                                           const Reach rc) {
   extern __shared__ int4 lds4[];
-  const OrderSplit sp(parts, blockIdx.x, G, BH, nQt);
+  const OrderSplit sp(runs, blockIdx.x, G, BH, nQt);
   const int nh = sp.heads();
   const int n = sp.n;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1296,10 +1296,10 @@ __global__ __launch_bounds__(1024) void k_fwd_table_order(int mode, const int4* 
 __global__ __launch_bounds__(1024) void k_bwd_table_order(const int4* __restrict__ qstats,
                                                           const int4* __restrict__ kstats,
                                                           const int2* __restrict__ fwd, int BH, int nQt, int nKt,
-                                                          int G, bool parts, int2* __restrict__ bwd,
+                                                          int G, bool runs, int2* __restrict__ bwd,
                                                           int32_t* __restrict__ order, const Reach rc) {
   extern __shared__ int2 lds2[];
-  const OrderSplit sp(parts, blockIdx.x, G, BH, nKt);
+  const OrderSplit sp(runs, blockIdx.x, G, BH, nKt);
   const int nh = sp.heads();
   const int n = sp.n;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1815,13 +1815,13 @@ static int order_groups(int BH) {
 // that starts there), else the groups of scfa_work_order. heads / items:
 // the most heads and items one workgroup handles.
 struct OrderPlan {
-  bool parts;
+  bool runs;
   int G, heads, items;
 };
 static OrderPlan order_plan(bool runs_ok, int BH, int nT) {
   OrderPlan op;
-  op.parts = runs_ok && BH % 8 != 0;
-  if (op.parts) {
+  op.runs = runs_ok && BH % 8 != 0;
+  if (op.runs) {
     const long long N = static_cast<long long>(BH) * nT;
     const int c1 = static_cast<int>((N + 7) / 8);
     op.G = 8;
@@ -1862,7 +1862,7 @@ int scfa_bwd_table_order(const int32_t* qstats, const int32_t* kstats, const int
   }
   hipLaunchKernelGGL(k_bwd_table_order, dim3(op.G), dim3(1024), lds, stream, reinterpret_cast<const int4*>(qstats),
                      reinterpret_cast<const int4*>(kstats), reinterpret_cast<const int2*>(fwd_tab), BH, nQt, nKt, op.G,
-                     op.parts, reinterpret_cast<int2*>(bwd_tab), order, reach_of(flags));
+                     op.runs, reinterpret_cast<int2*>(bwd_tab), order, reach_of(flags));
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }
@@ -1883,7 +1883,7 @@ int scfa_fwd_table_order(int mode, const int32_t* qstats, const int32_t* kstats,
   }
   hipLaunchKernelGGL(k_fwd_table_order, dim3(op.G), dim3(1024), lds, stream, mode,
                      reinterpret_cast<const int4*>(qstats), reinterpret_cast<const int4*>(kstats), BH, nQt, nKt, op.G,
-                     op.parts, reinterpret_cast<int2*>(fwd_tab), tiles, order, reach_of(flags));
+                     op.runs, reinterpret_cast<int2*>(fwd_tab), tiles, order, reach_of(flags));
   SCFA_RETURN_IF_LAUNCH_FAILED();
   return SCFA_OK;
 }
