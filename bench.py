@@ -236,11 +236,42 @@ def _grad_identities(plan, dO):
     return ok
 
 
+def _backward_graph(plan, dO, name, mode):
+    """One HIP graph of plan.backward(dO) (backward table, dQ, dK/dV), checked
+    bit for bit against the eager call over three replays with eager work in
+    between; the backward allocates nothing after its first call and records
+    no memset."""
+    import torch
+    plan.backward(dO)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in plan._grads]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        plan.backward(dO)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.backward(dO)
+    for _ in range(3):
+        for t in plan._grads:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(plan._grads, ref)):
+            raise SystemExit(f"{name} ({mode}): the backward graph replay differs from the eager backward")
+        plan.backward(dO)  # eager work between the replays
+        torch.cuda.synchronize()
+    return graph
+
+
 def _train_one(name, K):
     """Forward + backward of one training workload and of its dense-causal
     twin (same kernels, positions 0..T-1): the recomputation backward
-    (backward table, dQ (with Delta) and dK/dV kernels. timed after a forward with
-    HIP events, the forward kernel timed on its own."""
+    (backward table, dQ (with Delta) and dK/dV kernels) timed after a forward
+    with HIP events as replays of one HIP graph (checked against the eager
+    call; the eager-launch time is reported beside it), the forward kernel
+    timed on its own."""
     import torch
     import io_aware_attention_head_amd.scfa as scfa
     from io_aware_attention_head_amd.inputs import WORKLOADS, make_inputs
@@ -261,12 +292,14 @@ def _train_one(name, K):
         if not _grad_identities(plan, xt["dO"]):
             raise SystemExit(f"{name} ({mode}): gradient identities fail; nothing timed")
         pairs = int(plan.count_visible().sum().item())
-        ms = _time_ms(lambda: plan.backward(xt["dO"]), K)
+        ms_eager = _time_ms(lambda: plan.backward(xt["dO"]), K)
+        graph = _backward_graph(plan, xt["dO"], name, mode)
+        ms = _time_ms(graph.replay, K)
         fms = _time_ms(plan.forward, K)
         tf = 10 * wt.D * pairs / (ms * 1e-3) / 1e12
         tfb = 14 * wt.D * pairs / ((ms + fms) * 1e-3) / 1e12
         key = "sparse" if mode == wt.mode else "dense"
-        res[key] = {"bwd_ms": round(ms, 5), "bwd_tflops": round(tf, 2),
+        res[key] = {"bwd_ms": round(ms, 5), "bwd_ms_eager_launches": round(ms_eager, 5), "bwd_tflops": round(tf, 2),
                     "pct_bf16_peak_bwd": round(100 * tf / PEAK_BF16_TFLOPS, 2), "visible_pairs": pairs,
                     "fwd_kernel_ms": round(fms, 5), "fwd_bwd_ms": round(ms + fms, 5),
                     "fwd_bwd_tflops": round(tfb, 2), "pct_bf16_peak_fwd_bwd": round(100 * tfb / PEAK_BF16_TFLOPS, 2)}

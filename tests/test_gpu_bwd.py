@@ -180,6 +180,41 @@ def test_plan_backward_matches_call(mode):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("mode", ["hash", "qk", "dense"])
+def test_plan_backward_graph_replay(mode):
+    """A plan's backward captured as one HIP graph (as the benchmark times
+    it): three replays, each into gradients first filled with NaN and with
+    an eager backward in between, equal the eager backward bit for bit."""
+    need_gpu()
+    announce(f"plan backward graph {mode}")
+    w = small("qk" if mode == "dense" else mode, 1, 3, 1300, nb=8, keep_p=0.6, seed=81, grad=True)
+    g = {k: v.to("cuda:0") for k, v in make_inputs(w).items()}
+    plan = scfa.Plan(mode, w.B, w.H, w.T, w.D, torch.bfloat16, nb=w.nb)
+    plan.run(g)
+    plan.backward(g["dO"])
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in plan._grads]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        plan.backward(g["dO"])
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.backward(g["dO"])
+    for _ in range(3):
+        for t in plan._grads:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(plan._grads, ref):
+            assert torch.equal(a, b)
+        plan.backward(g["dO"])
+        torch.cuda.synchronize()
+        for a, b in zip(plan._grads, ref):
+            assert torch.equal(a, b)
+
+
 def _check_tiles(grads, ref, pre, heads):
     """Per-tile check of the gradients: dQ over each 128-query tile and dK, dV
     over each 64-key tile of the kernels' layout (rows of q_idx / k_idx), so
