@@ -535,13 +535,14 @@ int scfa_hash_sparse_fwd(int dtype_in, int dtype_out, const void* q, const void*
  *                exactly the index arrays and tables of the forward call.
  *  bwd_tab       the backward table of the same call (scfa_range_table or
  *                scfa_bwd_table).
- *  fwd_order     launch order of the dQ workgroups: scfa_work_order on
- *                fwd_tab (the forward call's order), or NULL (then query
- *                tiles run in descending index order).
+ *  fwd_order     launch order of the dQ workgroups: scfa_work_order or
+ *                scfa_fwd_table_order on fwd_tab (the forward call's
+ *                order), or NULL (then query tiles run in descending index
+ *                order).
  *  bwd_order     launch order of the dK/dV workgroups of the hash mode (one
  *                workgroup per key tile): scfa_work_order on bwd_tab with
- *                span = query tiles per head, or NULL (key tiles in index
- *                order). QK mode runs pairs of key tiles in index order
+ *                span = query tiles per head, or the order of
+ *                scfa_bwd_table_order, or NULL (key tiles in index order). QK mode runs pairs of key tiles in index order
  *                and does not read it. Any permutation gives the same
  *                results; only the schedule moves.
  *  O             (B, T, H, D) fp32 forward output;  lse (B, H, T) fp32.
