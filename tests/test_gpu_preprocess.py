@@ -717,3 +717,19 @@ def test_bwd_table_order_matches_two_launches(case):
         assert int((bwd[..., 1] > bwd[..., 0]).sum()) > 0  # the tables hold work
     fallback = (B, H) == (65, 8) or nQt >= 4000  # too large for one workgroup: scfa_work_order's groups
     check_order(order.cpu().numpy(), bwd.cpu().numpy(), "groups" if fallback or (B * H) % 8 == 0 else "runs")
+
+
+def test_plan_orders_training_workload_runs():
+    """The hash training workload (B*H = 12, not a multiple of 8): the Plan's
+    forward order (forward and dQ) and its dK/dV order are longest-first
+    orders in 8 runs of consecutive items, one run per XCD."""
+    need_gpu()
+    w = WORKLOADS["train_hash_bf16_t16384_nb16"]
+    announce(f"plan orders {w.name}")
+    x = {k: v.to("cuda:0") for k, v in make_inputs(w).items()}
+    plan = scfa.Plan("hash", w.B, w.H, w.T, w.D, torch.bfloat16, nb=w.nb)
+    plan.run(x)
+    plan.backward(x["dO"])
+    torch.cuda.synchronize()
+    check_order(plan.tab.fwd_order.cpu().numpy(), plan.tab.fwd.cpu().numpy(), "runs")
+    check_order(plan.tab.bwd_order.cpu().numpy(), plan.tab.bwd.cpu().numpy(), "runs")
